@@ -1,0 +1,378 @@
+"""Pins of the fp64 oracle against facts fixed by the pages and by mathematics.
+
+Each test is chosen so that a plausible mistake in the oracle (a dropped term,
+a wrong sign or index, a transposed operand, a wrong pairing of RoPE dims, a
+wrong mask) fails at least one of them. No GPU needed.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp8, mask, mla
+from head_latent_attention_fwd_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def kimi_dims():
+    return mla.default_dims(7168, 1536, 512, 64)
+
+
+def dsv32_dims():
+    return mla.default_dims(7168, 1536, 512, 128)
+
+
+def small(seed=7, **over):
+    cfg = dict(name="t", mode="prefill", B=1, T=24, dim=96, q_lora_rank=32, kv_lora_rank=16,
+               n_heads=3, act="f32", weight="f32", topk=0)
+    cfg.update(over)
+    inp = synth.gen_prefill(cfg, seed)
+    d = mla.default_dims(cfg["dim"], cfg["q_lora_rank"], cfg["kv_lora_rank"], cfg["n_heads"])
+    return cfg, d, inp
+
+
+# --------------------------------------------------------------------------
+# parameter counts printed on the pages
+
+def test_parameter_counts_from_weight_shapes():
+    g = {k: v["value"] for k, v in json.load(open(os.path.join(GOLDEN, "param_counts.json"))).items()
+         if not k.startswith("_")}
+    ks = mla.weight_shapes(kimi_dims())
+    n = {k: mla.n_params(s) for k, s in ks.items()}
+    assert n["wq_a"] == g["query_down_projection"]
+    assert n["q_norm_w"] == g["query_latent_rmsnorm"]
+    assert n["wq_a"] + n["q_norm_w"] == g["query_compression_per_instance"]
+    assert 60 * (n["wq_a"] + n["q_norm_w"]) == g["query_compression_x60"]
+    assert n["wq_a"] + n["wq_b"] == g["low_rank_query_weights"]
+    assert ks["wq_b"][0] * ks["wq_a"][1] == g["full_rank_query_weights"]
+    assert n["wo"] == g["kimi_o_proj"] and 60 * n["wo"] == g["kimi_o_proj_x60"]
+    down = mla.n_params(mla.swiglu_shapes(7168, 2048)["down"])
+    assert down == g["kimi_shared_expert_down"] and 60 * down == g["kimi_shared_expert_down_x60"]
+    ds = mla.weight_shapes(dsv32_dims())
+    assert mla.n_params(ds["wo"]) == g["dsv32_wo"] and 58 * mla.n_params(ds["wo"]) == g["dsv32_wo_x58"]
+    # the generator draws the same shapes as the oracle expects
+    for cfg_i, dims in ((1, kimi_dims()), (3, dsv32_dims())):
+        for name, shape in synth.weight_shapes(synth.CONFIGS[cfg_i]):
+            assert tuple(shape) == tuple(mla.weight_shapes(dims)[name])
+
+
+def test_softmax_scale():
+    assert kimi_dims()["softmax_scale"] == pytest.approx(1.0 / np.sqrt(192.0), rel=1e-15)
+
+
+# --------------------------------------------------------------------------
+# e4m3 codec
+
+def test_e4m3_decode_matches_torch_for_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = fp8.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert (np.isnan(ours) == nan).all() and nan.sum() == 2
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.nanmax(ours) == 448.0 and ours[1] == 2.0 ** -9
+
+
+def test_e4m3_encode_roundtrip_all_finite_codes():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    assert np.array_equal(fp8.e4m3_encode(fp8.e4m3_decode(codes)), codes)
+
+
+def test_e4m3_encode_ties_to_even_and_saturation():
+    dec = fp8.e4m3_decode
+    enc = fp8.e4m3_encode
+    assert dec(enc(1.0 + 1 / 16)) == 1.0            # tie between 1 and 1.125 -> even mantissa 0
+    assert dec(enc(1.0 + 3 / 16)) == 1.25           # tie between 1.125 and 1.25 -> mantissa 2
+    assert dec(enc(2.0 ** -10)) == 0.0              # tie between 0 and 2^-9 -> 0
+    assert dec(enc(3 * 2.0 ** -10)) == 2 * 2.0 ** -9
+    for big in (448.0, 460.0, 464.0, 500.0, 1e6):
+        assert dec(enc(big)) == 448.0 and dec(enc(-big)) == -448.0
+    assert enc(-0.0) == 0x80 and enc(0.0) == 0x00
+
+
+def test_e4m3_encode_matches_torch_cast():
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.uniform(-448, 448, 20000), rng.normal(0, 0.01, 20000),
+                        rng.normal(0, 1, 20000)]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(fp8.e4m3_encode(v), ref)
+
+
+def test_quant_1x128_error_bound_and_max():
+    rng = np.random.default_rng(4)
+    a = rng.standard_normal((5, 384)) * np.array([1e-3, 1, 30, 1e4, 1])[:, None]
+    a[4, 128:256] = 0.0                             # an all-zero group
+    codes, s = fp8.quant_act_1x128(a)
+    assert s.shape == (5, 3) and s.dtype == np.float32
+    assert s[4, 1] == 0 and (codes[4, 128:256] == 0).all()
+    deq = fp8.e4m3_decode(codes).reshape(5, 3, 128) * s[:, :, None]
+    g = a.reshape(5, 3, 128)
+    # half an e4m3 ulp: 2^-4 relative in the normal range, 2^-10 * scale below it
+    assert (np.abs(deq - g) <= np.maximum(np.abs(g) * 2.0 ** -4, s[:, :, None] * 2.0 ** -10) * (1 + 1e-6)).all()
+    mx = np.abs(fp8.e4m3_decode(codes)).reshape(5, 3, 128).max(axis=2)
+    assert (mx[s > 0] == 448.0).all()
+
+
+def test_block128_quant_partial_edge_blocks():
+    rng = np.random.default_rng(5)
+    w = rng.standard_normal((576, 256)).astype(np.float32)
+    w[512:, 128:] *= 1e-3                           # a small partial block (64 rows)
+    codes, s = fp8.quant_weight_block128(w)
+    assert s.shape == (5, 2)
+    assert s[4, 1] == np.float32(np.abs(w[512:, 128:]).max()) / np.float32(448)
+    deq = fp8.e4m3_decode(codes) * np.repeat(np.repeat(s, 128, 0), 128, 1)[:576]
+    bound = np.maximum(np.abs(w) * 2.0 ** -4, np.repeat(np.repeat(s, 128, 0), 128, 1)[:576] * 2.0 ** -10)
+    assert (np.abs(deq - w) <= bound * (1 + 1e-6)).all()
+
+
+def test_fp8_linear_equals_dequantised_matmul():
+    rng = np.random.default_rng(6)
+    a = rng.standard_normal((7, 256))
+    w = (rng.standard_normal((200, 256)) / 16).astype(np.float32)
+    wc, ws = fp8.quant_weight_block128(w)
+    y = fp8.linear_fp8(a, wc, ws)
+    ac, as_ = fp8.quant_act_1x128(a)
+    A = fp8.e4m3_decode(ac) * np.repeat(as_, 128, axis=1)
+    W = fp8.e4m3_decode(wc) * np.repeat(np.repeat(ws, 128, 0), 128, 1)[:200, :256]
+    np.testing.assert_allclose(y, A @ W.T, rtol=1e-12, atol=1e-12)
+    assert np.abs(y - a @ w.T.astype(np.float64)).max() < 0.1 * np.abs(a @ w.T).max()
+
+
+# --------------------------------------------------------------------------
+# RMSNorm and RoPE
+
+def test_rmsnorm_invariants():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((6, 512)) * 3
+    eps = 1e-6
+    y = mla.rmsnorm(x, np.ones(512), eps)
+    ms = np.mean(x * x, axis=1)
+    np.testing.assert_allclose(np.mean(y * y, axis=1), ms / (ms + eps), rtol=1e-13)
+    g = rng.standard_normal(512)
+    np.testing.assert_allclose(mla.rmsnorm(x, g, eps), g * y, rtol=1e-13)
+    np.testing.assert_allclose(mla.rmsnorm(5 * x, g, 0.0), mla.rmsnorm(x, g, 0.0), rtol=1e-13)
+
+
+def test_rope_definition_values_and_invariants():
+    e = np.eye(64)
+    r = mla.rope(e, np.full(64, 1.0))
+    # dim 0 pairs with dim 32 and turns by exactly 1 rad at position 1
+    assert r[0, 0] == pytest.approx(np.cos(1.0), abs=1e-15)
+    assert r[0, 32] == pytest.approx(np.sin(1.0), abs=1e-15)
+    assert r[32, 0] == pytest.approx(-np.sin(1.0), abs=1e-15)
+    # dim 1's frequency is 10000^(-1/32); nothing leaks to other dims
+    f1 = 10000.0 ** (-1 / 32)
+    assert r[1, 1] == pytest.approx(np.cos(f1)) and r[1, 33] == pytest.approx(np.sin(f1))
+    assert abs(r[1]).sum() == pytest.approx(abs(np.cos(f1)) + abs(np.sin(f1)))
+    rng = np.random.default_rng(9)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    np.testing.assert_array_equal(mla.rope(q, 0.0), q)
+    assert np.linalg.norm(mla.rope(q, 777.0)) == pytest.approx(np.linalg.norm(q), rel=1e-13)
+    a = mla.rope(q, 123.0) @ mla.rope(k, 40.0)
+    b = mla.rope(q, 1123.0) @ mla.rope(k, 1040.0)
+    assert a == pytest.approx(b, rel=1e-10)
+
+
+# --------------------------------------------------------------------------
+# attention
+
+def test_softmax_rows_sum_to_one_and_row0_is_v0():
+    cfg, d, inp = small(T=20)
+    out, aux = mla.mla_prefill(inp["x"], inp["w"], d, return_aux=True)
+    for p in aux["p"]:
+        np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-12)
+    # query 0 sees only key 0: its attention output is v[0] exactly
+    entry = aux["cache"][0]
+    _, v = mla.up_project(entry[:, :d["kv_lora_rank"]], inp["w"], d)
+    q_nope, q_pe = mla.query_path(inp["x"][0, :1], inp["w"], d, np.array([0]))
+    o, p = mla.attend_row(q_nope[0], q_pe[0], *mla.up_project(entry[:, :16], inp["w"], d)[:1],
+                          entry[:, 16:], v, np.array([0]), d["softmax_scale"])
+    assert (p == 1.0).all() and np.array_equal(o, v[0])
+
+
+def test_masked_keys_contribute_exactly_zero():
+    rng = np.random.default_rng(10)
+    T, H = 30, 3
+    q_nope, q_pe = rng.standard_normal((H, 128)), rng.standard_normal((H, 64))
+    kn, kp, v = rng.standard_normal((T, H, 128)), rng.standard_normal((T, 64)), rng.standard_normal((T, H, 128))
+    live = np.array([0, 3, 4, 17, 20])
+    o1, p1 = mla.attend_row(q_nope, q_pe, kn, kp, v, live, 0.07)
+    dead = np.setdiff1d(np.arange(T), live)
+    kn[dead], kp[dead], v[dead] = 1e30, -1e30, 1e30
+    o2, p2 = mla.attend_row(q_nope, q_pe, kn, kp, v, live, 0.07)
+    assert np.array_equal(o1, o2) and np.array_equal(p1, p2)
+
+
+def test_live_keys_rule():
+    assert list(mla.live_keys(3)) == [0, 1, 2, 3]
+    assert list(mla.live_keys(5, [7, 1, -1, 5, 0, 1])) == [0, 1, 5]
+
+
+def _dense_matrix_prefill(x, w, d, topk=None):
+    """Second formulation: full [T, T] additive 0/-inf mask built by scattering the
+    picks, plus the causal mask, scores for all (s, t) pairs as one matrix."""
+    B, T, _ = x.shape
+    H, L = d["n_heads"], d["kv_lora_rank"]
+    out = np.zeros((B, T, d["dim"]))
+    for b in range(B):
+        cq = x[b].astype(np.float64) @ w["wq_a"].T.astype(np.float64)
+        ms = (cq ** 2).mean(1, keepdims=True)
+        q = (w["q_norm_w"] * cq / np.sqrt(ms + d["rms_eps"])) @ w["wq_b"].T.astype(np.float64)
+        q = q.reshape(T, H, 192)
+        kv = x[b].astype(np.float64) @ w["wkv_a"].T.astype(np.float64)
+        lat = kv[:, :L]
+        c = w["kv_norm_w"] * lat / np.sqrt((lat ** 2).mean(1, keepdims=True) + d["rms_eps"])
+        u = (c @ w["wkv_b"].T.astype(np.float64)).reshape(T, H, 256)
+        ang = np.arange(T)[:, None] * 10000.0 ** (-np.arange(32) / 32.0)
+        cs, sn = np.cos(ang), np.sin(ang)
+
+        def rot(z):  # z [T, ..., 64]
+            shp = (T,) + (1,) * (z.ndim - 2) + (32,)
+            a1, a2 = z[..., :32], z[..., 32:]
+            return np.concatenate([a1 * cs.reshape(shp) - a2 * sn.reshape(shp),
+                                   a2 * cs.reshape(shp) + a1 * sn.reshape(shp)], -1)
+        qf = np.concatenate([q[:, :, :128], rot(q[:, :, 128:])], -1)          # [T,H,192]
+        kf = np.concatenate([u[:, :, :128], np.repeat(rot(kv[:, L:])[:, None, :], H, 1)], -1)
+        msk = np.triu(np.full((T, T), -np.inf), 1)
+        if topk is not None:
+            sel = np.full((T, T), -np.inf)
+            for s in range(T):
+                sel[s, topk[b, s][topk[b, s] >= 0]] = 0.0
+            msk = msk + sel
+        sc = np.einsum("shd,thd->hst", qf, kf) * d["softmax_scale"] + msk[None]
+        sc = np.exp(sc - sc.max(-1, keepdims=True))
+        sc /= sc.sum(-1, keepdims=True)
+        o = np.einsum("hst,thd->shd", sc, u[:, :, 128:]).reshape(T, H * 128)
+        out[b] = o @ w["wo"].T.astype(np.float64)
+    return out
+
+
+def test_prefill_matches_dense_matrix_formulation():
+    cfg, d, inp = small(T=40, B=2)
+    ref = _dense_matrix_prefill(inp["x"], inp["w"], d)
+    np.testing.assert_allclose(mla.mla_prefill(inp["x"], inp["w"], d), ref, rtol=1e-11, atol=1e-11)
+
+
+def test_prefill_topk_matches_dense_matrix_formulation():
+    cfg, d, inp = small(T=48, topk=8, seed=11)
+    ref = _dense_matrix_prefill(inp["x"], inp["w"], d, inp["topk_idx"])
+    got = mla.mla_prefill(inp["x"], inp["w"], d, topk_idx=inp["topk_idx"])
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-11)
+
+
+def test_config0_matches_dense_matrix_formulation():
+    cfg = synth.CONFIGS[0]
+    inp = synth.gen_prefill(cfg, synth.seed_of(0))
+    d = mla.default_dims(cfg["dim"], cfg["q_lora_rank"], cfg["kv_lora_rank"], cfg["n_heads"])
+    ref = _dense_matrix_prefill(inp["x"], inp["w"], d)
+    np.testing.assert_allclose(mla.mla_prefill(inp["x"], inp["w"], d), ref, rtol=1e-11, atol=1e-11)
+
+
+def test_topk_covering_all_keys_equals_dense_causal():
+    cfg, d, inp = small(T=16, seed=12)
+    T = 16
+    full = np.broadcast_to(np.arange(T, dtype=np.int32), (1, T, T)).copy()
+    a = mla.mla_prefill(inp["x"], inp["w"], d)
+    b = mla.mla_prefill(inp["x"], inp["w"], d, topk_idx=full)
+    assert np.array_equal(a, b)
+
+
+def test_causality_future_tokens_do_not_matter():
+    cfg, d, inp = small(T=20, seed=13)
+    a = mla.mla_prefill(inp["x"], inp["w"], d)
+    x2 = inp["x"].copy()
+    x2[:, 12:] = 99.0
+    b = mla.mla_prefill(x2, inp["w"], d)
+    assert np.array_equal(a[:, :12], b[:, :12])
+    assert not np.allclose(a[:, 12:], b[:, 12:])
+
+
+def test_sampled_rows_equal_full_rows():
+    cfg, d, inp = small(T=33, seed=14)
+    a = mla.mla_prefill(inp["x"], inp["w"], d)
+    rows = np.array([0, 5, 32])
+    np.testing.assert_allclose(mla.mla_prefill(inp["x"], inp["w"], d, rows=rows), a[:, rows], rtol=1e-13, atol=1e-13)
+
+
+def test_head_permutation_invariance():
+    cfg, d, inp = small(T=12, seed=15)
+    w = dict(inp["w"])
+    H = d["n_heads"]
+    perm = np.array([2, 0, 1])
+    w["wq_b"] = w["wq_b"].reshape(H, 192, -1)[perm].reshape(H * 192, -1)
+    w["wkv_b"] = w["wkv_b"].reshape(H, 256, -1)[perm].reshape(H * 256, -1)
+    w["wo"] = w["wo"].reshape(w["wo"].shape[0], H, 128)[:, perm].reshape(w["wo"].shape[0], -1)
+    np.testing.assert_allclose(mla.mla_prefill(inp["x"], w, d), mla.mla_prefill(inp["x"], inp["w"], d),
+                               rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# decode
+
+def _tiny_decode(P=10, B=3, seed=16):
+    cfg = dict(name="t", mode="decode", B=B, cache_len=P, dim=96, q_lora_rank=32, kv_lora_rank=16,
+               n_heads=3, act="f32", weight="f32")
+    inp = synth.gen_decode(cfg, seed, max_len=P + 4)
+    d = mla.default_dims(96, 32, 16, 3)
+    return d, inp
+
+
+def test_absorbed_decode_equals_unabsorbed():
+    d, inp = _tiny_decode()
+    o1, e1 = mla.mla_decode(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"])
+    o2, e2 = mla.mla_decode_absorbed(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"])
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-12 * np.abs(o1).max())
+    assert np.array_equal(e1, e2)
+
+
+def test_decode_equals_last_row_of_prefill():
+    """Decoding token P against the cache that prefill makes for tokens 0..P-1
+    gives prefill's output row P."""
+    cfg, d, inp = small(T=13, seed=17)
+    out, aux = mla.mla_prefill(inp["x"], inp["w"], d, return_aux=True)
+    P = 12
+    cache = aux["cache"][0][None, :P]
+    x_new = inp["x"][:, P]
+    o1, entry = mla.mla_decode(x_new, inp["w"], d, cache, np.array([P]))
+    o2, _ = mla.mla_decode_absorbed(x_new, inp["w"], d, cache, np.array([P]))
+    np.testing.assert_allclose(o1[0], out[0, P], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(o2[0], out[0, P], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(entry[0], aux["cache"][0][P], rtol=1e-13, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# selection mask
+
+def test_topk_bitmask_brute_force():
+    rng = np.random.default_rng(18)
+    B, T, k = 2, 70, 9
+    idx = rng.integers(-1, T, size=(B, T, k)).astype(np.int32)
+    got = mask.topk_bitmask(idx, T)
+    for b in range(B):
+        for s in range(T):
+            bits = [(int(got[b, s, t // 32]) >> (t % 32)) & 1 for t in range(T)]
+            want = [1 if (t <= s and t in idx[b, s]) else 0 for t in range(T)]
+            assert bits == want
+    assert got.shape == (B, T, 3)
+
+
+def test_synthetic_topk_recipe():
+    rng = np.random.default_rng(19)
+    idx = synth.draw_topk(rng, 1, 40, 8)
+    for s in range(40):
+        row = idx[0, s]
+        live = row[row >= 0]
+        if s < 8:
+            assert list(live) == list(range(s + 1))
+        else:
+            assert len(live) == 8 and len(set(live)) == 8 and s in live
+            assert (np.diff(live) > 0).all() and live.max() == s
+
+
+def test_swiglu_oracle_special_case():
+    # gate = 0 gives silu(0) = 0, so the output is exactly 0
+    x = np.ones((2, 8))
+    assert not mla.swiglu_mlp(x, np.zeros((4, 8)), np.ones((4, 8)), np.ones((8, 4))).any()
