@@ -1,0 +1,423 @@
+// Host side of the C ABI declared in include/mla.h: argument checks,
+// workspace carving and the launch sequences of the prefill and decode paths.
+// Nothing here computes; every step is a kernel enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/mla.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MLA_OK;
+  return fail(MLA_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+#define LAUNCH(expr, what)                           \
+  do {                                               \
+    int rc_ = hip_check((expr), what);               \
+    if (rc_ != MLA_OK) return rc_;                   \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Bump allocator over the caller's workspace.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* p) : base((char*)p) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  }
+};
+
+int check_dims(const mla_dims* d) {
+  if (!d) return fail(MLA_INVALID_ARG, "dims is NULL");
+  if (d->dim <= 0 || d->q_lora_rank <= 0 || d->kv_lora_rank <= 0 || d->n_heads <= 0)
+    return fail(MLA_INVALID_ARG, "dims must be positive");
+  if (d->qk_nope_head_dim != 128 || d->qk_rope_head_dim != 64 || d->v_head_dim != 128)
+    return fail(MLA_UNSUPPORTED, "head dims must be 128/64/128 (got %d/%d/%d)", d->qk_nope_head_dim,
+                d->qk_rope_head_dim, d->v_head_dim);
+  if (d->dim % 8 || d->q_lora_rank % 8 || d->kv_lora_rank % 8)
+    return fail(MLA_UNSUPPORTED, "dim, q_lora_rank and kv_lora_rank must be multiples of 8");
+  if (!(d->softmax_scale > 0.f) || !(d->rms_eps >= 0.f)) return fail(MLA_INVALID_ARG, "bad softmax_scale/rms_eps");
+  return MLA_OK;
+}
+
+int check_weights(const mla_weights* w, int wdt) {
+  if (!w) return fail(MLA_INVALID_ARG, "weights is NULL");
+  if (w->weight_dtype != wdt) return fail(MLA_INVALID_ARG, "weights->weight_dtype mismatch");
+  if (!w->wq_a || !w->q_norm_w || !w->wq_b || !w->wkv_a || !w->kv_norm_w || !w->wkv_b || !w->wo)
+    return fail(MLA_INVALID_ARG, "a weight pointer is NULL");
+  if (wdt == MLA_E4M3 && (!w->wq_a_scale || !w->wq_b_scale || !w->wkv_a_scale || !w->wkv_b_scale || !w->wo_scale))
+    return fail(MLA_INVALID_ARG, "e4m3 weights need every block-scale pointer");
+  return MLA_OK;
+}
+
+struct PrefillWs {
+  void *cqkv, *cqn, *kvc, *q, *u, *attn, *mask, *aq, *as;
+};
+
+size_t prefill_layout(const mla_dims* d, int wdt, int adt, int B, int T, int topk, bool own_kvc, void* ws,
+                      PrefillWs* out) {
+  const size_t M = (size_t)B * T, H = d->n_heads, Dq = d->q_lora_rank, L = d->kv_lora_rank;
+  const size_t es = adt == MLA_F32 ? 4 : 2;
+  Carver c(ws);
+  PrefillWs p{};
+  p.cqkv = c.take(M * (Dq + L + 64) * es);
+  p.cqn = c.take(M * Dq * es);
+  p.kvc = own_kvc ? c.take(M * (L + 64) * es) : nullptr;
+  p.q = c.take(M * H * 192 * es);
+  p.u = c.take(M * H * 256 * es);
+  p.attn = c.take(M * H * 128 * es);
+  p.mask = topk > 0 ? c.take((size_t)B * T * ((T + 31) / 32) * 4) : nullptr;
+  if (wdt == MLA_E4M3) {
+    size_t kmax = d->dim;
+    if (Dq > kmax) kmax = Dq;
+    if (L > kmax) kmax = L;
+    if (H * 128 > kmax) kmax = H * 128;
+    p.aq = c.take(M * kmax);
+    p.as = c.take(M * (kmax / 128) * 4);
+  }
+  if (out) *out = p;
+  return c.off;
+}
+
+struct DecodeWs {
+  void *cqkv, *cqn, *entry, *q, *qlat, *olat, *o;
+};
+
+size_t decode_layout(const mla_dims* d, int B, void* ws, DecodeWs* out) {
+  const size_t H = d->n_heads, Dq = d->q_lora_rank, L = d->kv_lora_rank;
+  Carver c(ws);
+  DecodeWs p{};
+  p.cqkv = c.take((size_t)B * (Dq + L + 64) * 2);
+  p.cqn = c.take((size_t)B * Dq * 2);
+  p.entry = c.take((size_t)B * (L + 64) * 2);
+  p.q = c.take((size_t)B * H * 192 * 2);
+  p.qlat = c.take((size_t)B * H * 576 * 2);
+  p.olat = c.take((size_t)B * H * 512 * 2);
+  p.o = c.take((size_t)B * H * 128 * 2);
+  if (out) *out = p;
+  return c.off;
+}
+
+mla::GemmArgs gemm_args(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc, int cdt, int M,
+                        int N, int K) {
+  mla::GemmArgs g{};
+  g.A = A; g.lda = lda; g.W = W; g.ldw = ldw; g.W2 = nullptr; g.ldw2 = 0; g.n_split = N;
+  g.C = C; g.ldc = ldc; g.c_dtype = cdt; g.M = M; g.N = N; g.K = K; g.batch = 1; g.w_kn = false;
+  return g;
+}
+
+mla::NormRopeArgs norm_args(const void* in, int64_t ld_in, void* out, int64_t ld_out, int dt, int rows) {
+  mla::NormRopeArgs a{};
+  a.in = in; a.ld_in = ld_in; a.in_dtype = dt; a.out = out; a.ld_out = ld_out; a.out_dtype = dt; a.rows = rows;
+  a.pos_period = 1;
+  return a;
+}
+
+// y[M, N] = act[M, K] . W^T for the path's weight format; fp8 quantises act first.
+int project(const mla_weights* w, int wdt, int adt, const void* act, int64_t lda, const void* W, const float* Ws,
+            const void* W2, const float* W2s, int n_split, void* out, int64_t ldo, int M, int N, int K,
+            const PrefillWs* ws, hipStream_t s) {
+  (void)w;
+  if (wdt == MLA_E4M3) {
+    LAUNCH(mla::launch_quant_1x128(act, lda, adt, M, K, (uint8_t*)ws->aq, (float*)ws->as, s), "quant_e4m3_1x128");
+    mla::GemmFp8Args g{};
+    g.A = (const uint8_t*)ws->aq; g.a_scale = (const float*)ws->as;
+    g.W = (const uint8_t*)W; g.w_scale = Ws; g.W2 = (const uint8_t*)W2; g.w2_scale = W2s; g.n_split = n_split;
+    g.C = out; g.ldc = ldo; g.c_dtype = adt; g.M = M; g.N = N; g.K = K;
+    LAUNCH(mla::launch_gemm_fp8(g, s), "gemm_fp8_blockscaled");
+    return MLA_OK;
+  }
+  mla::GemmArgs g = gemm_args(act, lda, W, K, out, ldo, adt, M, N, K);
+  g.W2 = W2; g.ldw2 = K; g.n_split = n_split;
+  if (adt == MLA_F32) LAUNCH(mla::launch_gemm_f32(g, s), "gemm_f32");
+  else LAUNCH(mla::launch_gemm_bf16(g, s), "gemm_bf16");
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_version(void) { return "mla-gfx950 0.1.0"; }
+const char* mla_last_error(void) { return g_err.c_str(); }
+
+size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t weight_dtype, int32_t act_dtype, int32_t B, int32_t T,
+                                  int32_t topk) {
+  if (check_dims(dims) != MLA_OK || B <= 0 || T <= 0) return 0;
+  return prefill_layout(dims, weight_dtype, act_dtype, B, T, topk, true, nullptr, nullptr);
+}
+
+int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int32_t adt, int32_t B, int32_t T,
+                const float* rope_cos, const float* rope_sin, int32_t rope_len, const int32_t* topk_idx,
+                int32_t topk, void* out, void* kv_cache_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!w) return fail(MLA_INVALID_ARG, "weights is NULL");
+  const int wdt = w->weight_dtype;
+  if (!((adt == MLA_F32 && wdt == MLA_F32) || (adt == MLA_BF16 && (wdt == MLA_BF16 || wdt == MLA_E4M3))))
+    return fail(MLA_UNSUPPORTED, "supported (act, weight) dtypes: (F32, F32), (BF16, BF16), (BF16, E4M3)");
+  if ((rc = check_weights(w, wdt))) return rc;
+  if (!x || !out || !rope_cos || !rope_sin) return fail(MLA_INVALID_ARG, "x/out/rope tables must not be NULL");
+  if (B <= 0 || T <= 0) return fail(MLA_INVALID_ARG, "B and T must be positive");
+  if ((int64_t)B * T > (1LL << 30)) return fail(MLA_INVALID_ARG, "B*T too large");
+  if (rope_len < T) return fail(MLA_INVALID_ARG, "rope_len (%d) < T (%d)", rope_len, T);
+  if ((topk_idx == nullptr) != (topk <= 0)) return fail(MLA_INVALID_ARG, "topk_idx and topk > 0 go together");
+  const int H = d->n_heads, Dq = d->q_lora_rank, L = d->kv_lora_rank, dim = d->dim;
+  if (wdt == MLA_E4M3 && (dim % 128 || Dq % 128 || L % 128))
+    return fail(MLA_UNSUPPORTED, "e4m3 weights need dim, q_lora_rank, kv_lora_rank multiples of 128");
+  PrefillWs p;
+  const size_t need = prefill_layout(d, wdt, adt, B, T, topk, kv_cache_out == nullptr, ws, &p);
+  if (!ws || ws_bytes < need) return fail(MLA_INVALID_ARG, "workspace too small: need %zu bytes", need);
+  if ((uintptr_t)ws & 255) return fail(MLA_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const int M = B * T, NQKV = Dq + L + 64;
+  void* kvc = kv_cache_out ? kv_cache_out : p.kvc;
+
+  // joint down-projection: [c_q | latent | k_pe] = x . [Wq_a ; Wkv_a]^T
+  if ((rc = project(w, wdt, adt, x, dim, w->wq_a, w->wq_a_scale, w->wkv_a, w->wkv_a_scale, Dq, p.cqkv, NQKV, M, NQKV,
+                    dim, &p, s)))
+    return rc;
+  const size_t es = adt == MLA_F32 ? 4 : 2;
+  {  // q_norm
+    mla::NormRopeArgs a = norm_args(p.cqkv, NQKV, p.cqn, Dq, adt, M);
+    a.norm_dim = Dq; a.gamma = w->q_norm_w; a.eps = d->rms_eps;
+    LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(q)");
+  }
+  {  // kv_norm on the latent, RoPE on the shared key -> [c | k_pe]
+    mla::NormRopeArgs a = norm_args((const char*)p.cqkv + Dq * es, NQKV, kvc, L + 64, adt, M);
+    a.norm_dim = L; a.gamma = w->kv_norm_w; a.eps = d->rms_eps;
+    a.rope_off = L; a.rope_heads = 1; a.rope_stride = 64;
+    a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = rope_len; a.pos_period = T;
+    LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(kv)");
+  }
+  // q = c_q . Wq_b^T, then RoPE on each head's rotary slice
+  if ((rc = project(w, wdt, adt, p.cqn, Dq, w->wq_b, w->wq_b_scale, nullptr, nullptr, H * 192, p.q, H * 192, M,
+                    H * 192, Dq, &p, s)))
+    return rc;
+  {
+    mla::NormRopeArgs a = norm_args(p.q, H * 192, p.q, H * 192, adt, M);
+    a.rope_off = 128; a.rope_heads = H; a.rope_stride = 192;
+    a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = rope_len; a.pos_period = T;
+    LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(q_pe)");
+  }
+  // [k_nope | v] per head = c . Wkv_b^T
+  if ((rc = project(w, wdt, adt, kvc, L + 64, w->wkv_b, w->wkv_b_scale, nullptr, nullptr, H * 256, p.u, H * 256, M,
+                    H * 256, L, &p, s)))
+    return rc;
+  if (topk > 0) LAUNCH(mla::launch_topk_bitmask(topk_idx, B, T, topk, (uint32_t*)p.mask, s), "topk_to_bitmask");
+  mla::PrefillAttnArgs at{};
+  at.q = p.q; at.u = p.u; at.kv = kvc; at.ld_kv = L + 64; at.kpe_off = L;
+  at.mask = (const uint32_t*)p.mask; at.out = p.attn; at.B = B; at.T = T; at.H = H; at.scale = d->softmax_scale;
+  if (adt == MLA_F32) LAUNCH(mla::launch_prefill_attn_f32(at, s), "prefill_attn_f32");
+  else LAUNCH(mla::launch_prefill_attn_bf16(at, s), "prefill_attn");
+  // out = o . Wo^T
+  return project(w, wdt, adt, p.attn, H * 128, w->wo, w->wo_scale, nullptr, nullptr, dim, out, dim, M, dim, H * 128,
+                 &p, s);
+}
+
+size_t mla_decode_workspace_size(const mla_dims* dims, int32_t weight_dtype, int32_t B, int32_t max_len) {
+  if (check_dims(dims) != MLA_OK || B <= 0 || max_len <= 0 || weight_dtype != MLA_BF16) return 0;
+  return decode_layout(dims, B, nullptr, nullptr);
+}
+
+int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B, void* kv_cache, int32_t max_len,
+               const int32_t* cache_len, const float* rope_cos, const float* rope_sin, int32_t rope_len, void* out,
+               void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if ((rc = check_weights(w, MLA_BF16))) return rc;
+  if (d->kv_lora_rank != 512) return fail(MLA_UNSUPPORTED, "decode needs kv_lora_rank = 512");
+  if (d->n_heads % 64) return fail(MLA_UNSUPPORTED, "decode needs n_heads to be a multiple of 64");
+  if (!x || !kv_cache || !cache_len || !rope_cos || !rope_sin || !out)
+    return fail(MLA_INVALID_ARG, "x/kv_cache/cache_len/rope tables/out must not be NULL");
+  if (B <= 0 || max_len <= 0) return fail(MLA_INVALID_ARG, "B and max_len must be positive");
+  if (rope_len < max_len) return fail(MLA_INVALID_ARG, "rope_len (%d) < max_len (%d)", rope_len, max_len);
+  DecodeWs p;
+  const size_t need = decode_layout(d, B, ws, &p);
+  if (!ws || ws_bytes < need) return fail(MLA_INVALID_ARG, "workspace too small: need %zu bytes", need);
+  if ((uintptr_t)ws & 255) return fail(MLA_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const int H = d->n_heads, Dq = d->q_lora_rank, L = d->kv_lora_rank, dim = d->dim, NQKV = Dq + L + 64;
+
+  {
+    mla::GemmArgs g = gemm_args(x, dim, w->wq_a, dim, p.cqkv, NQKV, MLA_BF16, B, NQKV, dim);
+    g.W2 = w->wkv_a; g.ldw2 = dim; g.n_split = Dq;
+    LAUNCH(mla::launch_gemm_bf16(g, s), "gemm(q_a|kv_a)");
+  }
+  {
+    mla::NormRopeArgs a = norm_args(p.cqkv, NQKV, p.cqn, Dq, MLA_BF16, B);
+    a.norm_dim = Dq; a.gamma = w->q_norm_w; a.eps = d->rms_eps;
+    LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm(q)");
+  }
+  {
+    mla::NormRopeArgs a = norm_args((const uint16_t*)p.cqkv + Dq, NQKV, p.entry, L + 64, MLA_BF16, B);
+    a.norm_dim = L; a.gamma = w->kv_norm_w; a.eps = d->rms_eps;
+    a.rope_off = L; a.rope_heads = 1; a.rope_stride = 64;
+    a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = max_len; a.pos = cache_len;
+    LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(kv)");
+  }
+  {
+    mla::GemmArgs g = gemm_args(p.cqn, Dq, w->wq_b, Dq, p.q, H * 192, MLA_BF16, B, H * 192, Dq);
+    LAUNCH(mla::launch_gemm_bf16(g, s), "gemm(q_b)");
+  }
+  {  // q_lat[b, h, :512] = q_nope[b, h] . W_UK_h  (W_UK_h = Wkv_b rows [256h, 256h+128), read [K, N])
+    mla::GemmArgs g = gemm_args(p.q, H * 192, w->wkv_b, L, p.qlat, H * 576, MLA_BF16, B, L, 128);
+    g.batch = H; g.batch_a = 192; g.batch_w = 256 * (int64_t)L; g.batch_c = 576; g.w_kn = true;
+    LAUNCH(mla::launch_gemm_bf16(g, s), "gemm(absorb W_UK)");
+  }
+  LAUNCH(mla::launch_decode_append(p.entry, kv_cache, cache_len, B, max_len, p.q, p.qlat, H, rope_cos, rope_sin, s),
+         "decode_append");
+  {
+    mla::DecodeAttnArgs a{};
+    a.qlat = p.qlat; a.cache = kv_cache; a.cache_len = cache_len; a.olat = p.olat;
+    a.B = B; a.H = H; a.max_len = max_len; a.scale = d->softmax_scale;
+    LAUNCH(mla::launch_decode_attn(a, s), "decode_attn");
+  }
+  {  // o[b, h] = W_UV_h . o_lat[b, h]  (W_UV_h = Wkv_b rows [256h+128, 256h+256))
+    mla::GemmArgs g = gemm_args(p.olat, H * 512, (const uint16_t*)w->wkv_b + 128 * (int64_t)L, L, p.o, H * 128,
+                                MLA_BF16, B, 128, L);
+    g.batch = H; g.batch_a = 512; g.batch_w = 256 * (int64_t)L; g.batch_c = 128;
+    LAUNCH(mla::launch_gemm_bf16(g, s), "gemm(un-absorb W_UV)");
+  }
+  {
+    mla::GemmArgs g = gemm_args(p.o, H * 128, w->wo, H * 128, out, dim, MLA_BF16, B, dim, H * 128);
+    LAUNCH(mla::launch_gemm_bf16(g, s), "gemm(wo)");
+  }
+  return MLA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// building blocks
+
+int gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc, int32_t c_dtype,
+              int32_t M, int32_t N, int32_t K, void* stream) {
+  g_err.clear();
+  if (!A || !W || !C) return fail(MLA_INVALID_ARG, "NULL pointer");
+  if (M < 0 || N < 0 || K <= 0) return fail(MLA_INVALID_ARG, "bad sizes M=%d N=%d K=%d", M, N, K);
+  if (c_dtype != MLA_F32 && c_dtype != MLA_BF16) return fail(MLA_UNSUPPORTED, "c_dtype must be F32 or BF16");
+  if (K % 8 || lda % 8 || ldw % 8 || lda < K || ldw < K || ldc < N)
+    return fail(MLA_UNSUPPORTED, "need K, lda, ldw multiples of 8, lda/ldw >= K, ldc >= N");
+  if (((uintptr_t)A | (uintptr_t)W) & 15) return fail(MLA_UNSUPPORTED, "A and W must be 16-byte aligned");
+  if (M == 0 || N == 0) return MLA_OK;
+  mla::GemmArgs g = gemm_args(A, lda, W, ldw, C, ldc, c_dtype, M, N, K);
+  LAUNCH(mla::launch_gemm_bf16(g, (hipStream_t)stream), "gemm_bf16");
+  return MLA_OK;
+}
+
+int gemm_f32(const float* A, int64_t lda, const float* W, int64_t ldw, float* C, int64_t ldc, int32_t M, int32_t N,
+             int32_t K, void* stream) {
+  g_err.clear();
+  if (!A || !W || !C) return fail(MLA_INVALID_ARG, "NULL pointer");
+  if (M < 0 || N < 0 || K <= 0 || lda < K || ldw < K || ldc < N) return fail(MLA_INVALID_ARG, "bad sizes");
+  if (M == 0 || N == 0) return MLA_OK;
+  mla::GemmArgs g = gemm_args(A, lda, W, ldw, C, ldc, MLA_F32, M, N, K);
+  LAUNCH(mla::launch_gemm_f32(g, (hipStream_t)stream), "gemm_f32");
+  return MLA_OK;
+}
+
+int gemm_fp8_blockscaled(const uint8_t* Aq, const float* a_scale, const uint8_t* Wq, const float* w_scale, void* C,
+                         int64_t ldc, int32_t c_dtype, int32_t M, int32_t N, int32_t K, void* stream) {
+  g_err.clear();
+  if (!Aq || !a_scale || !Wq || !w_scale || !C) return fail(MLA_INVALID_ARG, "NULL pointer");
+  if (M < 0 || N < 0 || K <= 0 || ldc < N) return fail(MLA_INVALID_ARG, "bad sizes");
+  if (K % 128) return fail(MLA_UNSUPPORTED, "K must be a multiple of 128");
+  if (c_dtype != MLA_F32 && c_dtype != MLA_BF16) return fail(MLA_UNSUPPORTED, "c_dtype must be F32 or BF16");
+  if (((uintptr_t)Aq | (uintptr_t)Wq) & 15) return fail(MLA_UNSUPPORTED, "Aq and Wq must be 16-byte aligned");
+  if (M == 0 || N == 0) return MLA_OK;
+  mla::GemmFp8Args g{};
+  g.A = Aq; g.a_scale = a_scale; g.W = Wq; g.w_scale = w_scale; g.W2 = nullptr; g.w2_scale = nullptr; g.n_split = N;
+  g.C = C; g.ldc = ldc; g.c_dtype = c_dtype; g.M = M; g.N = N; g.K = K;
+  LAUNCH(mla::launch_gemm_fp8(g, (hipStream_t)stream), "gemm_fp8_blockscaled");
+  return MLA_OK;
+}
+
+int rmsnorm_rope(const void* in, int64_t ld_in, int32_t in_dtype, int32_t rows, int32_t norm_dim, const float* gamma,
+                 float eps, int32_t rope_off, int32_t rope_heads, int32_t rope_stride, const float* cos_tab,
+                 const float* sin_tab, int32_t rope_len, const int32_t* pos, int32_t pos_period, void* out,
+                 int64_t ld_out, int32_t out_dtype, void* stream) {
+  g_err.clear();
+  if (!in || !out) return fail(MLA_INVALID_ARG, "NULL in/out");
+  if ((in_dtype != MLA_F32 && in_dtype != MLA_BF16) || (out_dtype != MLA_F32 && out_dtype != MLA_BF16))
+    return fail(MLA_UNSUPPORTED, "dtypes must be F32 or BF16");
+  if (rows < 0 || norm_dim < 0 || rope_heads < 0) return fail(MLA_INVALID_ARG, "negative size");
+  if (norm_dim > 0 && !gamma) return fail(MLA_INVALID_ARG, "gamma is NULL");
+  if (rope_heads > 0) {
+    if (!cos_tab || !sin_tab || rope_len <= 0) return fail(MLA_INVALID_ARG, "rope tables missing");
+    if (!pos && (pos_period <= 0 || pos_period > rope_len)) return fail(MLA_INVALID_ARG, "bad pos_period");
+    if (rope_off < 0 || (rope_heads > 1 && rope_stride < 64)) return fail(MLA_INVALID_ARG, "bad rope layout");
+  }
+  int64_t span = norm_dim;
+  if (rope_heads > 0) {
+    int64_t e = rope_off + (int64_t)(rope_heads - 1) * rope_stride + 64;
+    if (e > span) span = e;
+  }
+  if (ld_in < span || ld_out < span) return fail(MLA_INVALID_ARG, "ld_in/ld_out shorter than the row span");
+  mla::NormRopeArgs a{};
+  a.in = in; a.ld_in = ld_in; a.in_dtype = in_dtype; a.out = out; a.ld_out = ld_out; a.out_dtype = out_dtype;
+  a.rows = rows; a.norm_dim = norm_dim; a.gamma = gamma; a.eps = eps;
+  a.rope_off = rope_off; a.rope_heads = rope_heads; a.rope_stride = rope_stride;
+  a.cos_tab = cos_tab; a.sin_tab = sin_tab; a.rope_len = rope_len; a.pos = pos; a.pos_period = pos_period > 0 ? pos_period : 1;
+  LAUNCH(mla::launch_rmsnorm_rope(a, (hipStream_t)stream), "rmsnorm_rope");
+  return MLA_OK;
+}
+
+int mla_rope_table(float* cos_tab, float* sin_tab, int32_t n_pos, float base, void* stream) {
+  g_err.clear();
+  if (!cos_tab || !sin_tab) return fail(MLA_INVALID_ARG, "NULL table");
+  if (n_pos <= 0 || !(base > 1.f)) return fail(MLA_INVALID_ARG, "bad n_pos/base");
+  LAUNCH(mla::launch_rope_table(cos_tab, sin_tab, n_pos, base, (hipStream_t)stream), "rope_table");
+  return MLA_OK;
+}
+
+int mla_quant_e4m3_1x128(const void* a, int64_t lda, int32_t a_dtype, int32_t M, int32_t K, uint8_t* q, float* scales,
+                         void* stream) {
+  g_err.clear();
+  if (!a || !q || !scales) return fail(MLA_INVALID_ARG, "NULL pointer");
+  if (M < 0 || K <= 0 || lda < K) return fail(MLA_INVALID_ARG, "bad sizes");
+  if (K % 128) return fail(MLA_UNSUPPORTED, "K must be a multiple of 128");
+  if (a_dtype != MLA_F32 && a_dtype != MLA_BF16) return fail(MLA_UNSUPPORTED, "a_dtype must be F32 or BF16");
+  LAUNCH(mla::launch_quant_1x128(a, lda, a_dtype, M, K, q, scales, (hipStream_t)stream), "quant_e4m3_1x128");
+  return MLA_OK;
+}
+
+int mla_quant_e4m3_block128(const float* w, int32_t N, int32_t K, uint8_t* q, float* scales, void* stream) {
+  g_err.clear();
+  if (!w || !q || !scales) return fail(MLA_INVALID_ARG, "NULL pointer");
+  if (N <= 0 || K <= 0) return fail(MLA_INVALID_ARG, "bad sizes");
+  LAUNCH(mla::launch_quant_block128(w, N, K, q, scales, (hipStream_t)stream), "quant_e4m3_block128");
+  return MLA_OK;
+}
+
+int mla_topk_to_bitmask(const int32_t* topk_idx, int32_t B, int32_t T, int32_t topk, uint32_t* mask, void* stream) {
+  g_err.clear();
+  if (!topk_idx || !mask) return fail(MLA_INVALID_ARG, "NULL pointer");
+  if (B <= 0 || T <= 0 || topk <= 0) return fail(MLA_INVALID_ARG, "bad sizes");
+  if (T > 65536 * 8) return fail(MLA_UNSUPPORTED, "T too large for the LDS row buffer");
+  LAUNCH(mla::launch_topk_bitmask(topk_idx, B, T, topk, mask, (hipStream_t)stream), "topk_to_bitmask");
+  return MLA_OK;
+}
+
+}  // extern "C"

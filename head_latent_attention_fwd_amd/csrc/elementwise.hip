@@ -1,0 +1,210 @@
+// Row-wise and element-wise kernels of the MLA path: RMSNorm + RoPE, the RoPE
+// table, e4m3 quantisation (activations 1x128, weights 128x128), the top-k
+// selection bitmask and the decode cache append.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+namespace {
+
+__device__ __forceinline__ float ld(const void* p, int dt, int64_t i) {
+  return dt == DT_F32 ? ((const float*)p)[i] : bf2f(((const uint16_t*)p)[i]);
+}
+__device__ __forceinline__ void st(void* p, int dt, int64_t i, float v) {
+  if (dt == DT_F32) ((float*)p)[i] = v;
+  else ((uint16_t*)p)[i] = f2bf(v);
+}
+
+__device__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t += red[i];
+  return t;
+}
+__device__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) t = fmaxf(t, red[i]);
+  return t;
+}
+
+// RMSNorm (gamma * x / sqrt(mean(x^2) + eps)) over the row prefix and rotate-half
+// RoPE on rope_heads 64-wide slices; one 256-thread block per row.
+__global__ __launch_bounds__(256) void rmsnorm_rope_kernel(NormRopeArgs a, int rope_len) {
+  __shared__ float red[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int64_t ib = (int64_t)row * a.ld_in, ob = (int64_t)row * a.ld_out;
+  if (a.norm_dim > 0) {
+    float ss = 0.f;
+    for (int i = tid; i < a.norm_dim; i += 256) {
+      float v = ld(a.in, a.in_dtype, ib + i);
+      ss = fmaf(v, v, ss);
+    }
+    ss = block_sum(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)a.norm_dim + a.eps);
+    for (int i = tid; i < a.norm_dim; i += 256)
+      st(a.out, a.out_dtype, ob + i, a.gamma[i] * (ld(a.in, a.in_dtype, ib + i) * r));
+  }
+  if (a.rope_heads > 0) {
+    const int pos = a.pos ? a.pos[row] : row % a.pos_period;
+    const bool ok = pos >= 0 && pos < rope_len;
+    for (int p = tid; p < a.rope_heads * 32; p += 256) {
+      const int h = p >> 5, d = p & 31;
+      const int64_t o = a.rope_off + (int64_t)h * a.rope_stride + d;
+      const float x1 = ld(a.in, a.in_dtype, ib + o), x2 = ld(a.in, a.in_dtype, ib + o + 32);
+      float c = 0.f, s = 0.f;
+      if (ok) { c = a.cos_tab[pos * 32 + d]; s = a.sin_tab[pos * 32 + d]; }
+      st(a.out, a.out_dtype, ob + o, x1 * c - x2 * s);
+      st(a.out, a.out_dtype, ob + o + 32, x2 * c + x1 * s);
+    }
+  }
+}
+
+__global__ void rope_table_kernel(float* c, float* s, int n_pos, double base) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_pos * 32) return;
+  const int p = i >> 5, d = i & 31;
+  const double th = (double)p * pow(base, -(double)d / 32.0);
+  c[i] = (float)cos(th);
+  s[i] = (float)sin(th);
+}
+
+__device__ __forceinline__ uint32_t to_e4m3x2(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// One wave per (row, 128-group): s = amax/448, q = e4m3(x / s).
+__global__ __launch_bounds__(256) void quant_1x128_kernel(const void* a, int64_t lda, int dt, int M, int K,
+                                                          uint8_t* q, float* scales) {
+  const int G = K / 128;
+  const int g = blockIdx.x * 4 + (threadIdx.x >> 6), m = blockIdx.y, lane = threadIdx.x & 63;
+  if (g >= G) return;
+  const int64_t base = (int64_t)m * lda + g * 128 + lane * 2;
+  const float v0 = ld(a, dt, base), v1 = ld(a, dt, base + 1);
+  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  const float s = amax / 448.0f;
+  uint32_t code = 0;
+  if (s != 0.f) code = to_e4m3x2(v0 / s, v1 / s);
+  *(uint16_t*)(q + (int64_t)m * K + g * 128 + lane * 2) = (uint16_t)code;
+  if (lane == 0) scales[(int64_t)m * G + g] = s;
+}
+
+// One block per 128x128 weight block.
+__global__ __launch_bounds__(256) void quant_block128_kernel(const float* w, int N, int K, uint8_t* q,
+                                                             float* scales) {
+  __shared__ float red[4];
+  const int nb = blockIdx.y, kb = blockIdx.x, tid = threadIdx.x;
+  const int n0 = nb * 128, k0 = kb * 128;
+  float amax = 0.f;
+  for (int e = tid; e < 128 * 128; e += 256) {
+    const int n = n0 + (e >> 7), k = k0 + (e & 127);
+    if (n < N && k < K) amax = fmaxf(amax, fabsf(w[(int64_t)n * K + k]));
+  }
+  amax = block_max(amax, red);
+  const float s = amax / 448.0f;
+  for (int e = tid * 2; e < 128 * 128; e += 512) {
+    const int n = n0 + (e >> 7), k = k0 + (e & 127);
+    if (n >= N || k >= K) continue;
+    const float v0 = w[(int64_t)n * K + k];
+    const float v1 = (k + 1 < K) ? w[(int64_t)n * K + k + 1] : 0.f;
+    const uint32_t code = s != 0.f ? to_e4m3x2(v0 / s, v1 / s) : 0u;
+    q[(int64_t)n * K + k] = (uint8_t)(code & 0xFF);
+    if (k + 1 < K) q[(int64_t)n * K + k + 1] = (uint8_t)(code >> 8);
+  }
+  if (tid == 0) scales[(int64_t)nb * ((K + 127) / 128) + kb] = s;
+}
+
+// One block per query row: OR the picks (t <= s) into LDS words, then store.
+__global__ __launch_bounds__(256) void topk_bitmask_kernel(const int32_t* idx, int T, int k, uint32_t* mask) {
+  extern __shared__ uint32_t words[];
+  const int s = blockIdx.x, b = blockIdx.y, W = (T + 31) / 32;
+  for (int i = threadIdx.x; i < W; i += 256) words[i] = 0u;
+  __syncthreads();
+  const int32_t* row = idx + ((int64_t)b * T + s) * k;
+  for (int j = threadIdx.x; j < k; j += 256) {
+    const int t = row[j];
+    if (t >= 0 && t <= s && t < T) atomicOr(&words[t >> 5], 1u << (t & 31));
+  }
+  __syncthreads();
+  uint32_t* out = mask + ((int64_t)b * T + s) * W;
+  for (int i = threadIdx.x; i < W; i += 256) out[i] = words[i];
+}
+
+// Decode: append the new [latent | k_pe] entry at slot cache_len[b] and write
+// the rotated query rope part into the latent-space query.
+__global__ __launch_bounds__(256) void decode_append_kernel(const uint16_t* entry, uint16_t* cache,
+                                                            const int32_t* cache_len, int max_len,
+                                                            const uint16_t* q, uint16_t* qlat, int H,
+                                                            const float* cos_tab, const float* sin_tab) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int P = cache_len[b];
+  const bool ok = P >= 0 && P < max_len;
+  if (ok) {
+    uint16_t* dst = cache + ((int64_t)b * max_len + P) * 576;
+    for (int i = tid; i < 576; i += 256) dst[i] = entry[(int64_t)b * 576 + i];
+  }
+  for (int p = tid; p < H * 32; p += 256) {
+    const int h = p >> 5, d = p & 31;
+    const uint16_t* src = q + ((int64_t)b * H + h) * 192 + 128;
+    uint16_t* o = qlat + ((int64_t)b * H + h) * 576 + 512;
+    const float x1 = bf2f(src[d]), x2 = bf2f(src[d + 32]);
+    float c = 0.f, s = 0.f;
+    if (ok) { c = cos_tab[P * 32 + d]; s = sin_tab[P * 32 + d]; }
+    o[d] = f2bf(x1 * c - x2 * s);
+    o[d + 32] = f2bf(x2 * c + x1 * s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm_rope(const NormRopeArgs& a, hipStream_t s) {
+  // Positions outside the table (only possible through a device pos array)
+  // give zero rotations instead of reading past it.
+  if (a.rows <= 0) return hipSuccess;
+  rmsnorm_rope_kernel<<<a.rows, 256, 0, s>>>(a, a.rope_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float* c, float* sn, int n_pos, float base, hipStream_t s) {
+  if (n_pos <= 0) return hipSuccess;
+  rope_table_kernel<<<(n_pos * 32 + 255) / 256, 256, 0, s>>>(c, sn, n_pos, (double)base);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_1x128(const void* a, int64_t lda, int a_dtype, int M, int K, uint8_t* q, float* scales,
+                              hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  dim3 grid((K / 128 + 3) / 4, M);
+  quant_1x128_kernel<<<grid, 256, 0, s>>>(a, lda, a_dtype, M, K, q, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_block128(const float* w, int N, int K, uint8_t* q, float* scales, hipStream_t s) {
+  dim3 grid((K + 127) / 128, (N + 127) / 128);
+  quant_block128_kernel<<<grid, 256, 0, s>>>(w, N, K, q, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_bitmask(const int32_t* idx, int B, int T, int k, uint32_t* mask, hipStream_t s) {
+  dim3 grid(T, B);
+  topk_bitmask_kernel<<<grid, 256, ((T + 31) / 32) * 4, s>>>(idx, T, k, mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_append(const void* entry, void* cache, const int32_t* cache_len, int B, int max_len,
+                                const void* q, void* qlat, int H, const float* cos_tab, const float* sin_tab,
+                                hipStream_t s) {
+  decode_append_kernel<<<B, 256, 0, s>>>((const uint16_t*)entry, (uint16_t*)cache, cache_len, max_len,
+                                         (const uint16_t*)q, (uint16_t*)qlat, H, cos_tab, sin_tab);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,76 @@
+// Internal launch interface between the host API (api.cpp) and the kernels.
+// Every launcher enqueues on the given stream and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
+
+// C[b][M, N] = A[b][M, K] . W[b]^T. W is [N, K] (K contiguous) unless w_kn, in
+// which case it is [K, N] (N contiguous). Rows n >= n_split of W come from W2
+// (row n - n_split), which lets one launch cover two stacked weight matrices.
+struct GemmArgs {
+  const void* A; int64_t lda; int64_t batch_a;
+  const void* W; int64_t ldw; int64_t batch_w;
+  const void* W2; int64_t ldw2; int n_split;
+  void* C; int64_t ldc; int64_t batch_c; int c_dtype;
+  int M, N, K, batch;
+  bool w_kn;
+};
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s);
+
+// Block-scaled e4m3 GEMM. W2/w2_scale as in GemmArgs (n_split multiple of 128).
+struct GemmFp8Args {
+  const uint8_t* A; const float* a_scale;          // [M, K], [M, K/128]
+  const uint8_t* W; const float* w_scale;          // [N, K], [ceil(N/128), K/128]
+  const uint8_t* W2; const float* w2_scale; int n_split;
+  void* C; int64_t ldc; int c_dtype;
+  int M, N, K;
+};
+hipError_t launch_gemm_fp8(const GemmFp8Args& g, hipStream_t s);
+
+struct NormRopeArgs {
+  const void* in; int64_t ld_in; int in_dtype;
+  void* out; int64_t ld_out; int out_dtype;
+  int rows, norm_dim; const float* gamma; float eps;
+  int rope_off, rope_heads, rope_stride;
+  const float* cos_tab; const float* sin_tab; int rope_len;
+  const int32_t* pos; int pos_period;
+};
+hipError_t launch_rmsnorm_rope(const NormRopeArgs& a, hipStream_t s);
+hipError_t launch_rope_table(float* c, float* sn, int n_pos, float base, hipStream_t s);
+hipError_t launch_quant_1x128(const void* a, int64_t lda, int a_dtype, int M, int K,
+                              uint8_t* q, float* scales, hipStream_t s);
+hipError_t launch_quant_block128(const float* w, int N, int K, uint8_t* q, float* scales, hipStream_t s);
+hipError_t launch_topk_bitmask(const int32_t* idx, int B, int T, int k, uint32_t* mask, hipStream_t s);
+
+// Prefill attention. q [B*T, H*192] (rope applied), u [B*T, H*256] = per head
+// [k_nope | v], kv [B*T, ld_kv] with the rotated shared key at kpe_off,
+// optional bitmask [B, T, ceil(T/32)], out [B*T, H*128].
+struct PrefillAttnArgs {
+  const void* q; const void* u; const void* kv; int64_t ld_kv; int kpe_off;
+  const uint32_t* mask; void* out;
+  int B, T, H; float scale;
+};
+hipError_t launch_prefill_attn_bf16(const PrefillAttnArgs& a, hipStream_t s);
+hipError_t launch_prefill_attn_f32(const PrefillAttnArgs& a, hipStream_t s);
+
+// Decode pieces.
+struct DecodeAttnArgs {
+  const void* qlat;      // [B, H, 576] bf16: absorbed query (512) | rotated q_pe (64)
+  const void* cache;     // [B, max_len, 576] bf16
+  const int32_t* cache_len;
+  void* olat;            // [B, H, 512] bf16
+  int B, H, max_len; float scale;
+};
+hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s);
+// Copies entry[b] ([576] bf16) to cache[b, cache_len[b]] and the rotated q_pe of
+// every head (q [B, H*192] at 128 + 192h) to qlat[b, h, 512:576].
+hipError_t launch_decode_append(const void* entry, void* cache, const int32_t* cache_len, int B,
+                                int max_len, const void* q, void* qlat, int H,
+                                const float* cos_tab, const float* sin_tab, hipStream_t s);
+
+}  // namespace mla

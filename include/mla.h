@@ -1,0 +1,215 @@
+/*
+ * mla.h — C ABI of the MI355X (gfx950) multi-head latent attention forward.
+ *
+ * What is computed follows the model-atlas pages on MLA:
+ *   "Kimi K2 · Query compression"            (query path, module init, parameter table)
+ *   "Kimi K2 · Output projection"            (Delta_attn = o W_O, [out, in] weights)
+ *   "Kimi K2 · Down projection"              (FP8 e4m3, 128 x 128 weight blocks, dynamic activations)
+ *   "DeepSeek-V3.2-Exp · Sparse attention"   (prefill: scores, top-k + causal mask, softmax, PV)
+ *   "DeepSeek-V3.2-Exp · Output projection"  (decode at p = 1000; softmax_scale from the MLA init)
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller. The library never
+ *    allocates device memory; scratch comes from a caller workspace whose size
+ *    the *_workspace_size queries return. Host-side structs are read during the
+ *    call only.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
+ *    enqueued asynchronously on it; no entry point synchronises.
+ *  - Matrices are row-major. Weights are [out, in] (K contiguous). Activations
+ *    are [rows, features] with rows = B*T and per-head features packed head-major.
+ *  - bf16 = bfloat16 storage, fp32 accumulation. e4m3 = OCP FP8 E4M3FN bytes.
+ *  - Return value: an mla_status. On failure nothing has been enqueued, except
+ *    MLA_HIP_ERROR from a launch, after which the stream's contents are
+ *    unspecified. mla_last_error() gives a thread-local message.
+ *  - Results are deterministic: no atomics in reductions, fixed split counts.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define MLA_API __attribute__((visibility("default")))
+#else
+#define MLA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_INVALID_ARG = 1,   /* null pointer, bad or inconsistent size, workspace too small */
+  MLA_UNSUPPORTED = 2,   /* valid but not built: head dims other than 128/64/128, K % 128 != 0 for fp8, ... */
+  MLA_HIP_ERROR = 3      /* a HIP launch or query failed */
+} mla_status;
+
+typedef enum {
+  MLA_F32 = 0,
+  MLA_BF16 = 1,
+  MLA_E4M3 = 2
+} mla_dtype;
+
+/* MLA sizes (DeepSeek-V3.2-Exp · Output projection, "Code": the MLA init names
+ * dim, q_lora_rank, kv_lora_rank, n_heads and the three head dims). The build
+ * supports qk_nope_head_dim = 128, qk_rope_head_dim = 64, v_head_dim = 128.
+ * softmax_scale is normally (qk_nope + qk_rope)^-0.5; rms_eps is the RMSNorm
+ * epsilon (inside the square root). */
+typedef struct {
+  int32_t dim;
+  int32_t q_lora_rank;
+  int32_t kv_lora_rank;
+  int32_t n_heads;
+  int32_t qk_nope_head_dim;
+  int32_t qk_rope_head_dim;
+  int32_t v_head_dim;
+  float softmax_scale;
+  float rms_eps;
+} mla_dims;
+
+/* Device pointers to the MLA weights (Kimi K2 · Query compression, "Code":
+ * module init). All projections are bias-free, [out, in]:
+ *   wq_a  [q_lora_rank, dim]                    q_norm_w  [q_lora_rank]  fp32
+ *   wq_b  [n_heads*192, q_lora_rank]             per head: 128 non-rotated, then 64 rotated
+ *   wkv_a [kv_lora_rank + 64, dim]               latent first, then the shared rotary key
+ *   kv_norm_w [kv_lora_rank] fp32
+ *   wkv_b [n_heads*256, kv_lora_rank]            per head: 128 key (non-rotated), then 128 value
+ *   wo    [dim, n_heads*128]
+ * weight_dtype is MLA_F32, MLA_BF16 or MLA_E4M3. With MLA_E4M3 every *_scale
+ * pointer is required: fp32 [ceil(out/128), in/128], one scale per 128 x 128
+ * block (Kimi K2 · Down projection, quantization_config); otherwise they are
+ * ignored. */
+typedef struct {
+  int32_t weight_dtype;
+  const void* wq_a;  const float* wq_a_scale;
+  const float* q_norm_w;
+  const void* wq_b;  const float* wq_b_scale;
+  const void* wkv_a; const float* wkv_a_scale;
+  const float* kv_norm_w;
+  const void* wkv_b; const float* wkv_b_scale;
+  const void* wo;    const float* wo_scale;
+} mla_weights;
+
+MLA_API const char* mla_version(void);
+/* Message of the last failed call on this thread ("" if none). */
+MLA_API const char* mla_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Whole-path entry points
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of workspace mla_prefill needs for these sizes (0 on invalid input). */
+MLA_API size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t weight_dtype, int32_t act_dtype,
+                                  int32_t B, int32_t T, int32_t topk);
+
+/* MLA prefill with an empty cache (DeepSeek-V3.2-Exp · Sparse attention, mode
+ * prefill: the path taken for more than one position; Kimi K2 · Output
+ * projection for the head flatten and o_proj). Positions are 0..T-1.
+ *   x        [B, T, dim]   act_dtype (MLA_F32 with F32 weights, or MLA_BF16)
+ *   rope_cos, rope_sin  fp32 [rope_len, 32]: cos/sin of pos * 10000^(-d/32)
+ *            for pos = row (see mla_rope_table); rope_len >= T
+ *   topk_idx [B, T, topk] int32 or NULL. Key t is live for query s iff t <= s
+ *            and (topk_idx == NULL or t appears in row (b, s)); -1 pads. Every
+ *            query must keep at least one live key (its own position suffices).
+ *   out      [B, T, dim]   act_dtype
+ *   kv_cache_out [B, T, kv_lora_rank + 64] bf16 (fp32 for MLA_F32) or NULL:
+ *            receives the per-position [normalised latent | rotated k_pe].
+ *   ws, ws_bytes  workspace of at least mla_prefill_workspace_size(...) bytes,
+ *            256-byte aligned. */
+MLA_API int mla_prefill(const mla_dims* dims, const mla_weights* w, const void* x, int32_t act_dtype,
+                int32_t B, int32_t T, const float* rope_cos, const float* rope_sin, int32_t rope_len,
+                const int32_t* topk_idx, int32_t topk, void* out, void* kv_cache_out,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace mla_decode needs (0 on invalid input). */
+MLA_API size_t mla_decode_workspace_size(const mla_dims* dims, int32_t weight_dtype, int32_t B, int32_t max_len);
+
+/* Single-token MLA decode, latent-absorbed (DeepSeek-V3.2-Exp · Sparse
+ * attention, "Explanation": a single decoded token scores the cached latent
+ * directly; DeepSeek-V3.2-Exp · Output projection at p = 1000).
+ * Per sequence b with P = cache_len[b]: the new token at position P produces
+ * its cache entry [normalised latent | rotated k_pe], which is written to
+ * kv_cache[b, P]; it then attends slots 0..P with kv_b's key half folded into
+ * the query and its value half applied after the attention, then wo.
+ *   x         [B, dim] bf16
+ *   kv_cache  [B, max_len, kv_lora_rank + 64] bf16, in/out (only slot P of
+ *             each sequence is written)
+ *   cache_len [B] int32 DEVICE array, 0 <= cache_len[b] < max_len (checked on
+ *             the device: an out-of-range sequence is skipped and its output
+ *             row is set to zero)
+ *   rope_cos, rope_sin  fp32 [rope_len, 32], rope_len >= max_len
+ *   out       [B, dim] bf16
+ * Needs bf16 weights and kv_lora_rank = 512. */
+MLA_API int mla_decode(const mla_dims* dims, const mla_weights* w, const void* x, int32_t B,
+               void* kv_cache, int32_t max_len, const int32_t* cache_len,
+               const float* rope_cos, const float* rope_sin, int32_t rope_len,
+               void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Building blocks (each is also a step of the paths above)
+ * ------------------------------------------------------------------------ */
+
+/* C[M, N] = A[M, K] . W[N, K]^T (a bias-free Linear with [out, in] weights,
+ * Kimi K2 · Output projection formula). A, W bf16; C bf16 or fp32 (c_dtype).
+ * Leading dims in elements; K % 8 == 0, lda/ldw % 8 == 0, A/W 16-byte aligned. */
+MLA_API int gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc,
+              int32_t c_dtype, int32_t M, int32_t N, int32_t K, void* stream);
+
+/* Same product in fp32 (A, W, C fp32), for the fp32 path. */
+MLA_API int gemm_f32(const float* A, int64_t lda, const float* W, int64_t ldw, float* C, int64_t ldc,
+             int32_t M, int32_t N, int32_t K, void* stream);
+
+/* Block-scaled FP8 product (Kimi K2 · Down projection, quantization_config):
+ *   C[m, n] = sum_g a_scale[m, g] * w_scale[n / 128, g] * sum_{k in g} Aq[m, k] * Wq[n, k]
+ * over 128-wide groups g along K. Aq [M, K] e4m3 with a_scale fp32 [M, K/128];
+ * Wq [N, K] e4m3 with w_scale fp32 [ceil(N/128), K/128]; all contiguous.
+ * C [M, N] (ldc) bf16 or fp32. K % 128 == 0. */
+MLA_API int gemm_fp8_blockscaled(const uint8_t* Aq, const float* a_scale, const uint8_t* Wq, const float* w_scale,
+                         void* C, int64_t ldc, int32_t c_dtype, int32_t M, int32_t N, int32_t K, void* stream);
+
+/* Row-wise RMSNorm and RoPE (the q_a / kv_a layernorms and the rotary part of
+ * the query and of the shared key; Kimi K2 · Query compression, "Code").
+ * For each of `rows` rows:
+ *   if norm_dim > 0: out[:norm_dim] = gamma * in[:norm_dim] / sqrt(mean(in[:norm_dim]^2) + eps)
+ *   for h < rope_heads: the 64 values at rope_off + h*rope_stride are rotated
+ *     rotate-half style (dim d pairs with d+32) by cos/sin row pos(row), where
+ *     pos(row) = pos ? pos[row] : row % pos_period.
+ * Other elements of `out` are not written. in == out is allowed.
+ * in_dtype/out_dtype: MLA_F32 or MLA_BF16; math in fp32. gamma fp32 (may be
+ * NULL when norm_dim == 0). */
+MLA_API int rmsnorm_rope(const void* in, int64_t ld_in, int32_t in_dtype, int32_t rows, int32_t norm_dim,
+                 const float* gamma, float eps, int32_t rope_off, int32_t rope_heads, int32_t rope_stride,
+                 const float* cos_tab, const float* sin_tab, int32_t rope_len, const int32_t* pos,
+                 int32_t pos_period, void* out, int64_t ld_out, int32_t out_dtype, void* stream);
+
+/* cos/sin table for RoPE: cos_tab[p, d] = cos(p * base^(-d/32)), sin likewise,
+ * for p < n_pos, d < 32, evaluated in fp64 and stored fp32. */
+MLA_API int mla_rope_table(float* cos_tab, float* sin_tab, int32_t n_pos, float base, void* stream);
+
+/* Dynamic activation quantisation to e4m3, one fp32 scale per row and per 128
+ * elements along K (Kimi K2 · Down projection: activation_scheme dynamic):
+ *   s = amax(group) / 448 (fp32; 0 for an all-zero group), q = e4m3_rne(a / s)
+ * with the quotient in fp32. a: [M, K] (lda) MLA_F32 or MLA_BF16; q [M, K]
+ * contiguous; scales [M, K/128]. K % 128 == 0. */
+MLA_API int mla_quant_e4m3_1x128(const void* a, int64_t lda, int32_t a_dtype, int32_t M, int32_t K,
+                         uint8_t* q, float* scales, void* stream);
+
+/* Weight quantisation to e4m3 with one fp32 scale per 128 x 128 block of
+ * [N, K] (Kimi K2 · Down projection, quantization_config weight_block_size).
+ * s = amax(block)/448 over the valid elements, q = e4m3_rne(w / s) with the
+ * quotient in fp32. w fp32 [N, K]; q [N, K]; scales [ceil(N/128), ceil(K/128)]. */
+MLA_API int mla_quant_e4m3_block128(const float* w, int32_t N, int32_t K, uint8_t* q, float* scales, void* stream);
+
+/* Top-k selection + causal mask as bits (DeepSeek-V3.2-Exp · Sparse
+ * attention, "Code" and the M^sel input): mask[b, s, w] bit j is 1 iff key
+ * t = 32w + j appears in topk_idx[b, s, :] and t <= s. topk_idx [B, T, topk]
+ * int32 (-1 and out-of-range entries ignored); mask uint32 [B, T, ceil(T/32)]. */
+MLA_API int mla_topk_to_bitmask(const int32_t* topk_idx, int32_t B, int32_t T, int32_t topk,
+                        uint32_t* mask, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H_ */

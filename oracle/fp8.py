@@ -15,6 +15,9 @@ The rest is the plainest reading, listed in the design doc:
 * activations: one scale per row and per 128 consecutive elements along the
   reduction dimension; weights: one scale per 128 x 128 block of [out, in]
   (edge blocks partial, their max taken over the valid elements only).
+* the quantiser's input is the activation as the workload holds it (bf16),
+  and the quotient a / s is taken in fp32, so that a code is decided in the
+  same precision the kernels decide it in.
 """
 import numpy as np
 
@@ -125,23 +128,35 @@ def quant_weight_block128(w):
     return codes, scales
 
 
-def linear_fp8(a, w_codes, w_scales, quotient="f64"):
-    """y = a . W^T with e4m3 operands and fp32 scales, accumulated in fp64.
-
-    a is quantised here (dynamic 1x128 groups along K). Then, for each output
+def fp8_gemm(a_codes, a_scales, w_codes, w_scales):
+    """Block-scaled product, accumulated in fp64 (Kimi K2 "Down projection"
+    page, quantization_config): for each output
     y[m, n] = sum_g s_a[m, g] * s_w[n // 128, g] * sum_{k in group g} dec(a_q[m, k]) * dec(w_q[n, k]).
-    The inner sums are exact in fp64 (products of two e4m3 values).
-    """
-    a = np.asarray(a, dtype=np.float64)
-    M, K = a.shape
+    The inner sums are exact in fp64 (products of two e4m3 values)."""
+    M, K = a_codes.shape
     N = w_codes.shape[0]
-    a_codes, a_scales = quant_act_1x128(a, quotient)
     A = e4m3_decode(a_codes)                       # [M, K]
     W = e4m3_decode(w_codes)                       # [N, K]
-    G = K // 128
     y = np.zeros((M, N), dtype=np.float64)
     sw_rows = w_scales[np.arange(N) // 128].astype(np.float64)   # [N, G]
-    for g in range(G):
+    for g in range(K // 128):
         part = A[:, g * 128:(g + 1) * 128] @ W[:, g * 128:(g + 1) * 128].T
         y += part * a_scales[:, g:g + 1].astype(np.float64) * sw_rows[None, :, g]
     return y
+
+
+def round_bf16(x):
+    """Nearest bfloat16 value of each fp64 element (8 significant bits, ties to
+    even), computed directly from fp64: x = m * 2^e with 0.5 <= |m| < 1, keep
+    rint(m * 256) / 256. Values here never reach the bf16 subnormal range."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+def linear_fp8(a, w_codes, w_scales):
+    """y = a . W^T with e4m3 operands. The activation is held in bf16 (the
+    workload's activation dtype), quantised in dynamic 1x128 groups along K
+    with the quotient in fp32, then the block-scaled product in fp64."""
+    a_codes, a_scales = quant_act_1x128(round_bf16(a).astype(np.float32), "f32")
+    return fp8_gemm(a_codes, a_scales, w_codes, w_scales)

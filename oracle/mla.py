@@ -233,10 +233,11 @@ def mla_prefill(x, w, d, topk_idx=None, rows=None, fp8=False, return_aux=False):
 # ----------------------------------------------------------------------------
 # decode
 
-def _decode_token(x_b, w, d, P, fq):
-    q_nope, q_pe = query_path(x_b[None], w, d, np.array([P]), fq)
-    entry = latent_path(x_b[None], w, d, np.array([P]), fq)[0]
-    return q_nope[0], q_pe[0], entry
+def _decode_tokens(x, w, d, P):
+    """Query parts and cache entries of the new tokens (row b at position P[b])."""
+    q_nope, q_pe = query_path(x, w, d, P)
+    entry = latent_path(x, w, d, P)
+    return q_nope, q_pe, entry
 
 
 def mla_decode(x, w, d, cache, cache_len, seqs=None):
@@ -253,16 +254,16 @@ def mla_decode(x, w, d, cache, cache_len, seqs=None):
     seqs = np.arange(x.shape[0]) if seqs is None else np.asarray(seqs)
     L = d["kv_lora_rank"]
     H = d["n_heads"]
-    outs, entries = [], []
-    for b in seqs:
-        P = int(cache_len[b])
-        q_nope, q_pe, entry = _decode_token(x[b], w, d, P, None)
-        C = np.concatenate([np.asarray(cache[b, :P], dtype=np.float64), entry[None]], axis=0)
+    P_all = np.asarray(cache_len)[seqs].astype(np.int64)
+    q_nope, q_pe, entries = _decode_tokens(x[seqs], w, d, P_all)
+    o = np.zeros((len(seqs), H * VDIM))
+    for i, b in enumerate(seqs):
+        P = int(P_all[i])
+        C = np.concatenate([np.asarray(cache[b, :P], dtype=np.float64), entries[i][None]], axis=0)
         k_nope, v = up_project(C[:, :L], w, d)
-        o, _ = attend_row(q_nope, q_pe, k_nope, C[:, L:], v, np.arange(P + 1), d["softmax_scale"])
-        outs.append(linear(o.reshape(1, H * VDIM), w["wo"])[0])
-        entries.append(entry)
-    return np.array(outs), np.array(entries)
+        o_h, _ = attend_row(q_nope[i], q_pe[i], k_nope, C[:, L:], v, np.arange(P + 1), d["softmax_scale"])
+        o[i] = o_h.reshape(-1)
+    return linear(o, w["wo"]), entries
 
 
 def mla_decode_absorbed(x, w, d, cache, cache_len, seqs=None):
@@ -280,19 +281,18 @@ def mla_decode_absorbed(x, w, d, cache, cache_len, seqs=None):
     H = d["n_heads"]
     wkv_b = np.asarray(w["wkv_b"], dtype=np.float64).reshape(H, NOPE + VDIM, L)
     W_UK, W_UV = wkv_b[:, :NOPE, :], wkv_b[:, NOPE:, :]
-    outs, entries = [], []
-    for b in seqs:
-        P = int(cache_len[b])
-        q_nope, q_pe, entry = _decode_token(x[b], w, d, P, None)
-        C = np.concatenate([np.asarray(cache[b, :P], dtype=np.float64), entry[None]], axis=0)
-        q_lat = np.einsum("hi,hic->hc", q_nope, W_UK)             # [H, L]
-        z = (q_lat @ C[:, :L].T + q_pe @ C[:, L:].T) * d["softmax_scale"]
+    P_all = np.asarray(cache_len)[seqs].astype(np.int64)
+    q_nope, q_pe, entries = _decode_tokens(x[seqs], w, d, P_all)
+    o = np.zeros((len(seqs), H * VDIM))
+    for i, b in enumerate(seqs):
+        P = int(P_all[i])
+        C = np.concatenate([np.asarray(cache[b, :P], dtype=np.float64), entries[i][None]], axis=0)
+        q_lat = np.einsum("hi,hic->hc", q_nope[i], W_UK)           # [H, L]
+        z = (q_lat @ C[:, :L].T + q_pe[i] @ C[:, L:].T) * d["softmax_scale"]
         p = softmax_over_live(z)                                  # [H, P+1]
         o_lat = p @ C[:, :L]                                      # [H, L]
-        o = np.einsum("hjc,hc->hj", W_UV, o_lat)                  # [H, 128]
-        outs.append(linear(o.reshape(1, H * VDIM), w["wo"])[0])
-        entries.append(entry)
-    return np.array(outs), np.array(entries)
+        o[i] = np.einsum("hjc,hc->hj", W_UV, o_lat).reshape(-1)   # [H*128]
+    return linear(o, w["wo"]), entries
 
 
 # ----------------------------------------------------------------------------

@@ -1,0 +1,156 @@
+"""Per-kernel parity of the HIP library against the fp64 oracle (GPU)."""
+import numpy as np
+import pytest
+import torch
+
+from head_latent_attention_fwd_amd import api, synth
+from oracle import fp8, mask, mla
+
+from helpers import BF16_TOL, F32_TOL, assert_parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def dev(a, dt):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(dt)
+
+
+def test_rope_table_matches_definition():
+    c, s = api.mla_rope_table(9000)
+    th = mla.rope_angles(np.arange(9000))
+    np.testing.assert_allclose(c.cpu().numpy(), np.cos(th), atol=2e-7, rtol=0)
+    np.testing.assert_allclose(s.cpu().numpy(), np.sin(th), atol=2e-7, rtol=0)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (130, 300, 200), (257, 2112, 7168), (2048, 7168, 2048),
+                                   (64, 24576, 1536)])
+@pytest.mark.parametrize("cdt", [torch.bfloat16, torch.float32])
+def test_gemm_bf16(M, N, K, cdt):
+    rng = np.random.default_rng(M * 7 + N + K)
+    a = synth.round_bf16(rng.standard_normal((M, K)))
+    w = synth.round_bf16(rng.standard_normal((N, K)) / np.sqrt(K))
+    C = torch.empty((M, N), dtype=cdt, device=DEV)
+    api.gemm_bf16(dev(a, torch.bfloat16), dev(w, torch.bfloat16), C)
+    assert_parity(C.float().cpu().numpy(), mla.linear(a, w), what=f"gemm {M}x{N}x{K}")
+
+
+def test_gemm_bf16_strided_operands():
+    rng = np.random.default_rng(1)
+    a = synth.round_bf16(rng.standard_normal((70, 600)))
+    w = synth.round_bf16(rng.standard_normal((90, 600)))
+    A = dev(a, torch.bfloat16)[:, 64:576]            # row stride 600, K = 512
+    W = dev(w, torch.bfloat16)[:, 64:576]
+    C = torch.zeros((70, 100), dtype=torch.float32, device=DEV)[:, :90]
+    api.gemm_bf16(A, W, C)
+    assert_parity(C.cpu().numpy(), mla.linear(a[:, 64:576], w[:, 64:576]))
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 5, 7), (130, 256, 512), (64, 384, 128)])
+def test_gemm_f32(M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    api.gemm_f32(dev(a, torch.float32), dev(w, torch.float32), C)
+    assert_parity(C.cpu().numpy(), mla.linear(a, w), tol=F32_TOL, cos=0.999999)
+
+
+def _act_with_edges(M, K, seed):
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((M, K)) * np.exp(rng.uniform(-8, 8, (M, 1)))
+    a[0, :128] = 0.0                                  # all-zero group
+    a[1, 5] = 1e30 if K > 5 else a[1, 0]              # one huge element
+    a[2, 128:256] = 1e-30 if K >= 256 else 0.0        # subnormal-sized group
+    return synth.round_bf16(a)
+
+
+@pytest.mark.parametrize("M,K", [(300, 7168), (17, 128), (64, 8192)])
+def test_quant_1x128_bit_exact(M, K):
+    a = _act_with_edges(M, K, M + K)
+    q, s = api.mla_quant_e4m3_1x128(dev(a, torch.bfloat16))
+    rq, rs = fp8.quant_act_1x128(a, quotient="f32")
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+
+
+@pytest.mark.parametrize("N,K", [(576, 7168), (130, 200), (1536, 7168)])
+def test_quant_block128_bit_exact(N, K):
+    rng = np.random.default_rng(N * K)
+    w = (rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
+    w[:128, :128] = 0.0
+    q, s = api.mla_quant_e4m3_block128(dev(w, torch.float32))
+    rq, rs = fp8.quant_weight_block128(w)
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+
+
+@pytest.mark.parametrize("M,N,K", [(130, 576, 7168), (256, 1024, 1536), (33, 200, 512)])
+def test_gemm_fp8_blockscaled(M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    a = synth.round_bf16(rng.standard_normal((M, K)))
+    w = (rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
+    Aq, As = api.mla_quant_e4m3_1x128(dev(a, torch.bfloat16))
+    Wq, Ws = api.mla_quant_e4m3_block128(dev(w, torch.float32))
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    api.gemm_fp8_blockscaled(Aq, As, Wq, Ws, C)
+    ac, as_ = fp8.quant_act_1x128(a, quotient="f32")
+    wc, ws = fp8.quant_weight_block128(w)
+    ref = fp8.fp8_gemm(ac, as_, wc, ws)
+    # identical codes; fp32 accumulation inside the fp8 MFMA and the promotion
+    # differ from fp64 by ~2e-5 of max|C| (measured)
+    assert_parity(C.cpu().numpy(), ref, tol=1e-4, cos=0.999999, what="fp8 gemm")
+
+
+def test_rmsnorm_rope_kv_and_q_layouts():
+    rng = np.random.default_rng(3)
+    T = 77
+    kv = synth.round_bf16(rng.standard_normal((T, 576)) * 3)
+    gamma = (1 + 0.1 * rng.standard_normal(512)).astype(np.float32)
+    c, s = api.mla_rope_table(128)
+    out = torch.empty((T, 576), dtype=torch.bfloat16, device=DEV)
+    api.rmsnorm_rope(dev(kv, torch.bfloat16), out, norm_dim=512, gamma=dev(gamma, torch.float32), eps=1e-6,
+                     rope_off=512, rope_heads=1, rope_stride=64, rope_cos=c, rope_sin=s, pos_period=T)
+    ref = mla.rmsnorm_rope_rows(kv, 512, gamma, 1e-6, 512, 1, 64, np.arange(T), 10000.0)
+    assert_parity(out.float().cpu().numpy(), ref, what="kv norm+rope")
+    # q layout: rope on 5 heads of 192, at offset 128, positions from a device array
+    q = synth.round_bf16(rng.standard_normal((T, 5 * 192)))
+    pos = rng.integers(0, 128, T).astype(np.int32)
+    qd = dev(q, torch.bfloat16)
+    api.rmsnorm_rope(qd, qd, rope_off=128, rope_heads=5, rope_stride=192, rope_cos=c, rope_sin=s,
+                     pos=dev(pos, torch.int32))
+    ref = mla.rmsnorm_rope_rows(q, 0, None, 0, 128, 5, 192, pos, 10000.0)
+    assert_parity(qd.float().cpu().numpy(), ref, what="q rope in place")
+    # untouched elements stay bit-identical
+    got = qd.float().cpu().numpy().reshape(T, 5, 192)[:, :, :128]
+    np.testing.assert_array_equal(got, q.reshape(T, 5, 192)[:, :, :128])
+
+
+def test_rmsnorm_f32():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((9, 1536)).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(1536)).astype(np.float32)
+    out = torch.empty((9, 1536), dtype=torch.float32, device=DEV)
+    api.rmsnorm_rope(dev(x, torch.float32), out, norm_dim=1536, gamma=dev(g, torch.float32), eps=1e-6)
+    assert_parity(out.cpu().numpy(), mla.rmsnorm(x, g, 1e-6), tol=1e-6, cos=0.9999999)
+
+
+@pytest.mark.parametrize("B,T,k", [(2, 100, 9), (1, 4100, 2048)])
+def test_topk_bitmask_bit_exact(B, T, k):
+    rng = np.random.default_rng(T)
+    idx = rng.integers(-3, T + 5, size=(B, T, k)).astype(np.int32)
+    idx[:, :, 0] = np.arange(T)[None, :]
+    m = api.mla_topk_to_bitmask(dev(idx, torch.int32))
+    ref = mask.topk_bitmask(idx, T)
+    np.testing.assert_array_equal(m.cpu().numpy().view(np.uint32), ref)
+
+
+def test_boundary_errors_do_not_launch():
+    d = api.make_dims(512, 128, 64, 2)
+    d.qk_nope_head_dim = 96
+    assert api.mla_prefill_workspace_size(d, 0, 0, 1, 1) == 0
+    a = torch.zeros((4, 100), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(api.MlaError) as e:
+        api.mla_quant_e4m3_1x128(a, scales=torch.zeros((4, 1), dtype=torch.float32, device=DEV))
+    assert e.value.code == api.MLA_UNSUPPORTED

@@ -1,0 +1,150 @@
+"""End-to-end parity of mla_prefill / mla_decode against the fp64 oracle (GPU).
+
+Small cases are compared element by element; the full-size workloads are
+compared on sampled query rows (every position still feeds keys and values)
+or on every decoded sequence.
+"""
+import numpy as np
+import pytest
+import torch
+
+from head_latent_attention_fwd_amd import runner, synth
+from oracle import mla
+
+from helpers import BF16_TOL, F32_TOL, FP8_TOL, assert_parity, config, oracle_dims, small_cfg
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill(cfg, seed):
+    inp = synth.gen_prefill(cfg, seed)
+    run = runner.Prefill(cfg, inp)
+    run.run()
+    torch.cuda.synchronize()
+    return inp, run
+
+
+def _check_prefill(cfg, seed, rows=None, batches=None, tol=BF16_TOL, cos=0.9999):
+    inp, run = _prefill(cfg, seed)
+    got = run.out.float().cpu().numpy()
+    d = oracle_dims(cfg)
+    b_sel = np.arange(cfg["B"]) if batches is None else np.asarray(batches)
+    topk = None if inp["topk_idx"] is None else inp["topk_idx"][b_sel]
+    ref = mla.mla_prefill(inp["x"][b_sel], inp["w"], d, topk_idx=topk, rows=rows, fp8=cfg["weight"] == "e4m3")
+    g = got[b_sel] if rows is None else got[b_sel][:, rows]
+    assert_parity(g, ref, tol=tol, cos=cos, what=cfg["name"])
+    return inp, run
+
+
+def test_prefill_tiny_fp32_config():
+    _check_prefill(config(0), synth.seed_of(0), tol=F32_TOL, cos=0.999999)
+
+
+def test_prefill_small_bf16_dense():
+    inp, run = _check_prefill(small_cfg(), 21)
+    # the cache entries [c | k_pe] written by prefill
+    d = oracle_dims(small_cfg())
+    entry = mla.latent_path(inp["x"][1], inp["w"], d, np.arange(200))
+    assert_parity(run.kv_cache[1].float().cpu().numpy(), entry, what="kv_cache_out")
+
+
+def test_prefill_small_bf16_topk_ragged():
+    _check_prefill(small_cfg(T=333, B=1, topk=40, n_heads=2), 22)
+
+
+def test_prefill_small_fp32_topk():
+    _check_prefill(small_cfg(T=70, B=2, topk=16, act="f32", weight="f32", dim=256), 23, tol=F32_TOL,
+                   cos=0.999999)
+
+
+def test_prefill_small_fp8():
+    _check_prefill(small_cfg(T=160, dim=512, q_lora_rank=256, kv_lora_rank=256, n_heads=2, weight="e4m3"), 24,
+                   tol=FP8_TOL, cos=0.999)
+
+
+def test_prefill_single_token_and_tiny_T():
+    _check_prefill(small_cfg(T=1, B=3), 25)
+    _check_prefill(small_cfg(T=2, B=1, topk=1), 26)
+
+
+def _sample_rows(T, rng, n=10):
+    fixed = [0, 1, 63, 64, 127, 128, T // 2, T - 1]
+    return np.unique(np.concatenate([[r for r in fixed if r < T], rng.integers(0, T, n)]))
+
+
+def test_prefill_kimi_k2_bf16_full_size_sampled():
+    cfg = config(1)
+    _check_prefill(cfg, synth.seed_of(1), rows=_sample_rows(cfg["T"], np.random.default_rng(1)))
+
+
+def test_prefill_kimi_k2_fp8_full_size_sampled():
+    cfg = config(2)
+    _check_prefill(cfg, synth.seed_of(2), rows=_sample_rows(cfg["T"], np.random.default_rng(2), 4),
+                   batches=[0, 3], tol=FP8_TOL, cos=0.999)
+
+
+def test_prefill_dsv32_sparse_full_size_sampled():
+    cfg = config(3)
+    _check_prefill(cfg, synth.seed_of(3), rows=_sample_rows(cfg["T"], np.random.default_rng(3)))
+
+
+def _check_decode(cfg, seed, cache_len=None, seqs=None, max_len=None):
+    inp = synth.gen_decode(cfg, seed, max_len=max_len)
+    if cache_len is not None:
+        inp["cache_len"] = np.asarray(cache_len, dtype=np.int32)
+    run = runner.Decode(cfg, inp)
+    run.run()
+    torch.cuda.synchronize()
+    d = oracle_dims(cfg)
+    ref, entry = mla.mla_decode_absorbed(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"], seqs=seqs)
+    got = run.out.float().cpu().numpy()
+    sel = np.arange(cfg["B"]) if seqs is None else np.asarray(seqs)
+    assert_parity(got[sel], ref, what=cfg["name"])
+    # the cache changed exactly at slot cache_len[b]; every other slot is bit-identical
+    new = run.cache.float().cpu().numpy()
+    old = run.cache0.float().cpu().numpy()
+    for i, b in enumerate(sel):
+        P = int(inp["cache_len"][b])
+        keep = np.ones(new.shape[1], dtype=bool)
+        keep[P] = False
+        np.testing.assert_array_equal(new[b][keep], old[b][keep])
+        assert_parity(new[b, P], entry[i], what="appended cache entry")
+    return inp, run
+
+
+def test_decode_small_varied_lengths():
+    cfg = dict(name="dec_small", mode="decode", B=6, cache_len=40, dim=1024, q_lora_rank=256, kv_lora_rank=512,
+               n_heads=64, act="bf16", weight="bf16")
+    _check_decode(cfg, 31, cache_len=[0, 1, 31, 32, 33, 40], max_len=48)
+
+
+def test_decode_dsv32_full_size():
+    cfg = config(4)
+    _check_decode(cfg, synth.seed_of(4), max_len=1024)
+
+
+def test_decode_out_of_range_length_gives_zero_row():
+    cfg = dict(name="dec_bad", mode="decode", B=3, cache_len=10, dim=512, q_lora_rank=128, kv_lora_rank=512,
+               n_heads=64, act="bf16", weight="bf16")
+    inp = synth.gen_decode(cfg, 32, max_len=16)
+    inp["cache_len"] = np.array([5, 16, -1], dtype=np.int32)
+    run = runner.Decode(cfg, inp)
+    run.run()
+    torch.cuda.synchronize()
+    out = run.out.float().cpu().numpy()
+    assert (out[1] == 0).all() and (out[2] == 0).all()
+    assert torch.equal(run.cache[1:], run.cache0[1:])
+    d = oracle_dims(cfg)
+    ref, _ = mla.mla_decode_absorbed(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"], seqs=[0])
+    assert_parity(out[:1], ref)
+
+
+def test_prefill_is_deterministic():
+    cfg = small_cfg(T=257, topk=32)
+    inp = synth.gen_prefill(cfg, 41)
+    run = runner.Prefill(cfg, inp)
+    run.run()
+    a = run.out.clone()
+    run.run()
+    torch.cuda.synchronize()
+    assert torch.equal(a, run.out)

@@ -134,11 +134,23 @@ def test_fp8_linear_equals_dequantised_matmul():
     w = (rng.standard_normal((200, 256)) / 16).astype(np.float32)
     wc, ws = fp8.quant_weight_block128(w)
     y = fp8.linear_fp8(a, wc, ws)
-    ac, as_ = fp8.quant_act_1x128(a)
+    ac, as_ = fp8.quant_act_1x128(fp8.round_bf16(a).astype(np.float32), "f32")
     A = fp8.e4m3_decode(ac) * np.repeat(as_, 128, axis=1)
     W = fp8.e4m3_decode(wc) * np.repeat(np.repeat(ws, 128, 0), 128, 1)[:200, :256]
     np.testing.assert_allclose(y, A @ W.T, rtol=1e-12, atol=1e-12)
     assert np.abs(y - a @ w.T.astype(np.float64)).max() < 0.1 * np.abs(a @ w.T).max()
+
+
+def test_round_bf16_direct_from_fp64():
+    r = fp8.round_bf16
+    assert r(1.0 + 2.0 ** -8) == 1.0                      # tie -> even (mantissa 0)
+    assert r(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6      # tie -> even
+    assert r(1.0 + 2.0 ** -8 + 2.0 ** -40) == 1.0 + 2.0 ** -7   # just above the tie: up (no double rounding)
+    assert r(-3.0) == -3.0 and r(0.0) == 0.0
+    rng = np.random.default_rng(20)
+    v = (rng.standard_normal(50000) * np.exp(rng.uniform(-30, 30, 50000))).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(r(v.astype(np.float64)), ref)
 
 
 # --------------------------------------------------------------------------
