@@ -50,6 +50,8 @@ _SIGS = {
     "gemm_fp8_blockscaled": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp]),
     "rmsnorm_rope": (ctypes.c_int, [vp, i64, i32, i32, i32, vp, f32, i32, i32, i32, vp, vp, i32, vp, i32,
                                     vp, i64, i32, vp]),
+    "mla_prefill_attention": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]),
+    "mla_decode_attention": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, f32, vp]),
     "mla_rope_table": (ctypes.c_int, [vp, vp, i32, f32, vp]),
     "mla_quant_e4m3_1x128": (ctypes.c_int, [vp, i64, i32, i32, i32, vp, vp, vp]),
     "mla_quant_e4m3_block128": (ctypes.c_int, [vp, i32, i32, vp, vp, vp]),
@@ -204,6 +206,33 @@ def rmsnorm_rope(inp, out, norm_dim=0, gamma=None, eps=1e-6, rope_off=0, rope_he
                             pos_period, _ptr(out), out.stride(0), _TORCH_DT[out.dtype], _stream(stream))
     _check(rc)
     return out
+
+
+def pad64(T):
+    return (T + 63) // 64 * 64
+
+
+def mla_prefill_attention(q, k_nope, v_t, k_pe, out, B, T, H, scale=192.0 ** -0.5, mask=None, stream=None):
+    """q [B*T, H*192]; k_nope [B, H, Tp, 128]; v_t [B, H, 128, Tp]; k_pe [B, Tp, 64]; out [B*T, H*128]
+    (Tp = pad64(T); the padding keys are zeroed by the call)."""
+    Tp = pad64(T)
+    for t, shp, n in ((k_nope, (B, H, Tp, 128), "k_nope"), (v_t, (B, H, 128, Tp), "v_t"), (k_pe, (B, Tp, 64), "k_pe")):
+        _need(t, q.dtype, n)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} must have shape {shp}")
+    rc = lib().mla_prefill_attention(_ptr(q), _ptr(k_nope), _ptr(v_t), _ptr(k_pe), _ptr(mask), _ptr(out),
+                                     _TORCH_DT[q.dtype], B, T, H, scale, _stream(stream))
+    _check(rc)
+    return out
+
+
+def mla_decode_attention(q_lat, cache, cache_len, o_lat, scale=192.0 ** -0.5, stream=None):
+    """q_lat [B, H, 576], cache [B, max_len, 576], cache_len [B] int32, o_lat [B, H, 512]."""
+    B, H, _ = q_lat.shape
+    rc = lib().mla_decode_attention(_ptr(q_lat), _ptr(cache), _ptr(cache_len), _ptr(o_lat), B, H, cache.shape[1],
+                                    scale, _stream(stream))
+    _check(rc)
+    return o_lat
 
 
 def mla_rope_table(n_pos, base=10000.0, device="cuda", stream=None):

@@ -72,8 +72,10 @@ int check_weights(const mla_weights* w, int wdt) {
 }
 
 struct PrefillWs {
-  void *cqkv, *cqn, *kvc, *q, *u, *attn, *mask, *aq, *as;
+  void *cqkv, *cqn, *kvc, *q, *kn, *vt, *kpe, *attn, *mask, *aq, *as;
 };
+
+int pad64(int T) { return (T + 63) & ~63; }
 
 size_t prefill_layout(const mla_dims* d, int wdt, int adt, int B, int T, int topk, bool own_kvc, void* ws,
                       PrefillWs* out) {
@@ -84,8 +86,11 @@ size_t prefill_layout(const mla_dims* d, int wdt, int adt, int B, int T, int top
   p.cqkv = c.take(M * (Dq + L + 64) * es);
   p.cqn = c.take(M * Dq * es);
   p.kvc = own_kvc ? c.take(M * (L + 64) * es) : nullptr;
+  const size_t Mp = (size_t)B * pad64(T);
   p.q = c.take(M * H * 192 * es);
-  p.u = c.take(M * H * 256 * es);
+  p.kn = c.take(Mp * H * 128 * es);
+  p.vt = c.take(Mp * H * 128 * es);
+  p.kpe = c.take(Mp * 64 * es);
   p.attn = c.take(M * H * 128 * es);
   p.mask = topk > 0 ? c.take((size_t)B * T * ((T + 31) / 32) * 4) : nullptr;
   if (wdt == MLA_E4M3) {
@@ -135,21 +140,26 @@ mla::NormRopeArgs norm_args(const void* in, int64_t ld_in, void* out, int64_t ld
 }
 
 // y[M, N] = act[M, K] . W^T for the path's weight format; fp8 quantises act first.
-int project(const mla_weights* w, int wdt, int adt, const void* act, int64_t lda, const void* W, const float* Ws,
+// With kv != nullptr the output goes through the k_nope / v^T split epilogue.
+int project(int wdt, int adt, const void* act, int64_t lda, const void* W, const float* Ws,
             const void* W2, const float* W2s, int n_split, void* out, int64_t ldo, int M, int N, int K,
-            const PrefillWs* ws, hipStream_t s) {
-  (void)w;
+            const PrefillWs* ws, hipStream_t s, const mla::KvSplit* kv = nullptr) {
+  const int epi = kv ? mla::EPI_KV_SPLIT : mla::EPI_ROWMAJOR;
   if (wdt == MLA_E4M3) {
     LAUNCH(mla::launch_quant_1x128(act, lda, adt, M, K, (uint8_t*)ws->aq, (float*)ws->as, s), "quant_e4m3_1x128");
     mla::GemmFp8Args g{};
     g.A = (const uint8_t*)ws->aq; g.a_scale = (const float*)ws->as;
     g.W = (const uint8_t*)W; g.w_scale = Ws; g.W2 = (const uint8_t*)W2; g.w2_scale = W2s; g.n_split = n_split;
     g.C = out; g.ldc = ldo; g.c_dtype = adt; g.M = M; g.N = N; g.K = K;
+    g.epi = epi;
+    if (kv) g.kv = *kv;
     LAUNCH(mla::launch_gemm_fp8(g, s), "gemm_fp8_blockscaled");
     return MLA_OK;
   }
   mla::GemmArgs g = gemm_args(act, lda, W, K, out, ldo, adt, M, N, K);
   g.W2 = W2; g.ldw2 = K; g.n_split = n_split;
+  g.epi = epi;
+  if (kv) g.kv = *kv;
   if (adt == MLA_F32) LAUNCH(mla::launch_gemm_f32(g, s), "gemm_f32");
   else LAUNCH(mla::launch_gemm_bf16(g, s), "gemm_bf16");
   return MLA_OK;
@@ -196,7 +206,7 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
   void* kvc = kv_cache_out ? kv_cache_out : p.kvc;
 
   // joint down-projection: [c_q | latent | k_pe] = x . [Wq_a ; Wkv_a]^T
-  if ((rc = project(w, wdt, adt, x, dim, w->wq_a, w->wq_a_scale, w->wkv_a, w->wkv_a_scale, Dq, p.cqkv, NQKV, M, NQKV,
+  if ((rc = project(wdt, adt, x, dim, w->wq_a, w->wq_a_scale, w->wkv_a, w->wkv_a_scale, Dq, p.cqkv, NQKV, M, NQKV,
                     dim, &p, s)))
     return rc;
   const size_t es = adt == MLA_F32 ? 4 : 2;
@@ -210,10 +220,11 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
     a.norm_dim = L; a.gamma = w->kv_norm_w; a.eps = d->rms_eps;
     a.rope_off = L; a.rope_heads = 1; a.rope_stride = 64;
     a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = rope_len; a.pos_period = T;
+    a.kpe = p.kpe; a.kpe_tp = pad64(T);
     LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(kv)");
   }
   // q = c_q . Wq_b^T, then RoPE on each head's rotary slice
-  if ((rc = project(w, wdt, adt, p.cqn, Dq, w->wq_b, w->wq_b_scale, nullptr, nullptr, H * 192, p.q, H * 192, M,
+  if ((rc = project(wdt, adt, p.cqn, Dq, w->wq_b, w->wq_b_scale, nullptr, nullptr, H * 192, p.q, H * 192, M,
                     H * 192, Dq, &p, s)))
     return rc;
   {
@@ -222,18 +233,22 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
     a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = rope_len; a.pos_period = T;
     LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(q_pe)");
   }
-  // [k_nope | v] per head = c . Wkv_b^T
-  if ((rc = project(w, wdt, adt, kvc, L + 64, w->wkv_b, w->wkv_b_scale, nullptr, nullptr, H * 256, p.u, H * 256, M,
-                    H * 256, L, &p, s)))
+  // per head [k_nope | v] = c . Wkv_b^T, stored as k_nope [B,H,Tp,128] and v^T [B,H,128,Tp]
+  const int Tp = pad64(T);
+  LAUNCH(mla::launch_zero_kv_padding(p.kn, p.vt, p.kpe, B, H, T, Tp, (int)es, s), "zero_kv_padding");
+  const mla::KvSplit split{p.vt, T, Tp, H};
+  if ((rc = project(wdt, adt, kvc, L + 64, w->wkv_b, w->wkv_b_scale, nullptr, nullptr, H * 256, p.kn, 0, M,
+                    H * 256, L, &p, s, &split)))
     return rc;
   if (topk > 0) LAUNCH(mla::launch_topk_bitmask(topk_idx, B, T, topk, (uint32_t*)p.mask, s), "topk_to_bitmask");
   mla::PrefillAttnArgs at{};
-  at.q = p.q; at.u = p.u; at.kv = kvc; at.ld_kv = L + 64; at.kpe_off = L;
-  at.mask = (const uint32_t*)p.mask; at.out = p.attn; at.B = B; at.T = T; at.H = H; at.scale = d->softmax_scale;
+  at.q = p.q; at.kn = p.kn; at.vt = p.vt; at.kpe = p.kpe;
+  at.mask = (const uint32_t*)p.mask; at.out = p.attn; at.B = B; at.T = T; at.Tp = Tp; at.H = H;
+  at.scale = d->softmax_scale;
   if (adt == MLA_F32) LAUNCH(mla::launch_prefill_attn_f32(at, s), "prefill_attn_f32");
   else LAUNCH(mla::launch_prefill_attn_bf16(at, s), "prefill_attn");
   // out = o . Wo^T
-  return project(w, wdt, adt, p.attn, H * 128, w->wo, w->wo_scale, nullptr, nullptr, dim, out, dim, M, dim, H * 128,
+  return project(wdt, adt, p.attn, H * 128, w->wo, w->wo_scale, nullptr, nullptr, dim, out, dim, M, dim, H * 128,
                  &p, s);
 }
 
@@ -381,6 +396,37 @@ int rmsnorm_rope(const void* in, int64_t ld_in, int32_t in_dtype, int32_t rows, 
   a.rope_off = rope_off; a.rope_heads = rope_heads; a.rope_stride = rope_stride;
   a.cos_tab = cos_tab; a.sin_tab = sin_tab; a.rope_len = rope_len; a.pos = pos; a.pos_period = pos_period > 0 ? pos_period : 1;
   LAUNCH(mla::launch_rmsnorm_rope(a, (hipStream_t)stream), "rmsnorm_rope");
+  return MLA_OK;
+}
+
+int mla_prefill_attention(const void* q, const void* k_nope, const void* v_t, const void* k_pe, const uint32_t* mask,
+                          void* out, int32_t dtype, int32_t B, int32_t T, int32_t H, float scale, void* stream) {
+  g_err.clear();
+  if (!q || !k_nope || !v_t || !k_pe || !out) return fail(MLA_INVALID_ARG, "NULL pointer");
+  if (B <= 0 || T <= 0 || H <= 0) return fail(MLA_INVALID_ARG, "bad sizes");
+  if (dtype != MLA_BF16 && dtype != MLA_F32) return fail(MLA_UNSUPPORTED, "dtype must be BF16 or F32");
+  hipStream_t s = (hipStream_t)stream;
+  const int Tp = pad64(T);
+  LAUNCH(mla::launch_zero_kv_padding((void*)k_nope, (void*)v_t, (void*)k_pe, B, H, T, Tp, dtype == MLA_F32 ? 4 : 2, s),
+         "zero_kv_padding");
+  mla::PrefillAttnArgs a{};
+  a.q = q; a.kn = k_nope; a.vt = v_t; a.kpe = k_pe; a.mask = mask; a.out = out;
+  a.B = B; a.T = T; a.Tp = Tp; a.H = H; a.scale = scale;
+  if (dtype == MLA_F32) LAUNCH(mla::launch_prefill_attn_f32(a, s), "prefill_attn_f32");
+  else LAUNCH(mla::launch_prefill_attn_bf16(a, s), "prefill_attn");
+  return MLA_OK;
+}
+
+int mla_decode_attention(const void* q_lat, const void* cache, const int32_t* cache_len, void* o_lat, int32_t B,
+                         int32_t H, int32_t max_len, float scale, void* stream) {
+  g_err.clear();
+  if (!q_lat || !cache || !cache_len || !o_lat) return fail(MLA_INVALID_ARG, "NULL pointer");
+  if (B <= 0 || H <= 0 || max_len <= 0) return fail(MLA_INVALID_ARG, "bad sizes");
+  if (H % 64) return fail(MLA_UNSUPPORTED, "H must be a multiple of 64");
+  mla::DecodeAttnArgs a{};
+  a.qlat = q_lat; a.cache = cache; a.cache_len = cache_len; a.olat = o_lat;
+  a.B = B; a.H = H; a.max_len = max_len; a.scale = scale;
+  LAUNCH(mla::launch_decode_attn(a, (hipStream_t)stream), "decode_attn");
   return MLA_OK;
 }
 

@@ -62,9 +62,30 @@ __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(NormRopeArgs a, int r
       const float x1 = ld(a.in, a.in_dtype, ib + o), x2 = ld(a.in, a.in_dtype, ib + o + 32);
       float c = 0.f, s = 0.f;
       if (ok) { c = a.cos_tab[pos * 32 + d]; s = a.sin_tab[pos * 32 + d]; }
-      st(a.out, a.out_dtype, ob + o, x1 * c - x2 * s);
-      st(a.out, a.out_dtype, ob + o + 32, x2 * c + x1 * s);
+      const float y1 = x1 * c - x2 * s, y2 = x2 * c + x1 * s;
+      st(a.out, a.out_dtype, ob + o, y1);
+      st(a.out, a.out_dtype, ob + o + 32, y2);
+      if (a.kpe) {
+        const int bb = row / a.pos_period, t = row - bb * a.pos_period;
+        const int64_t kb = ((int64_t)bb * a.kpe_tp + t) * 64 + d;
+        st(a.kpe, a.out_dtype, kb, y1);
+        st(a.kpe, a.out_dtype, kb + 32, y2);
+      }
     }
+  }
+}
+
+// Zero the padding keys t in [T, Tp) of kn [B,H,Tp,128], vt [B,H,128,Tp], kpe [B,Tp,64].
+template <typename E>
+__global__ __launch_bounds__(256) void zero_kv_padding_kernel(E* kn, E* vt, E* kpe, int H, int T, int Tp) {
+  const int bh = blockIdx.x, b = bh / H, h = bh - b * H, pad = Tp - T;
+  E* k = kn + ((int64_t)bh * Tp + T) * 128;
+  for (int i = threadIdx.x; i < pad * 128; i += 256) k[i] = E(0);
+  E* v = vt + (int64_t)bh * 128 * Tp;
+  for (int i = threadIdx.x; i < pad * 128; i += 256) v[(int64_t)(i / pad) * Tp + T + i % pad] = E(0);
+  if (h == 0) {
+    E* p = kpe + ((int64_t)b * Tp + T) * 64;
+    for (int i = threadIdx.x; i < pad * 64; i += 256) p[i] = E(0);
   }
 }
 
@@ -170,6 +191,16 @@ hipError_t launch_rmsnorm_rope(const NormRopeArgs& a, hipStream_t s) {
   // give zero rotations instead of reading past it.
   if (a.rows <= 0) return hipSuccess;
   rmsnorm_rope_kernel<<<a.rows, 256, 0, s>>>(a, a.rope_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_kv_padding(void* kn, void* vt, void* kpe, int B, int H, int T, int Tp, int elem_bytes,
+                                  hipStream_t s) {
+  if (Tp == T) return hipSuccess;
+  if (elem_bytes == 4)
+    zero_kv_padding_kernel<float><<<B * H, 256, 0, s>>>((float*)kn, (float*)vt, (float*)kpe, H, T, Tp);
+  else
+    zero_kv_padding_kernel<uint16_t><<<B * H, 256, 0, s>>>((uint16_t*)kn, (uint16_t*)vt, (uint16_t*)kpe, H, T, Tp);
   return hipGetLastError();
 }
 

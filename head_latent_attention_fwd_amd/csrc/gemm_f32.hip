@@ -49,7 +49,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       int m = m0 + tm + i, n = n0 + tn + j;
-      if (m < g.M && n < g.N) C[(int64_t)m * g.ldc + n] = acc[i][j];
+      if (m >= g.M || n >= g.N) continue;
+      if (g.epi == EPI_KV_SPLIT) kv_split_store(g.kv, (float*)g.C, (float*)g.kv.vt, m, n, acc[i][j]);
+      else C[(int64_t)m * g.ldc + n] = acc[i][j];
     }
 }
 

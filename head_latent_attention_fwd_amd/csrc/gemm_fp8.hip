@@ -151,12 +151,13 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmFp8Args g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm * WM + i * 32 + row32(r, lane);
-        if (m < M) {
-          if (g.c_dtype == DT_F32)
-            ((float*)g.C)[(int64_t)m * g.ldc + n] = acc[i][j][r];
-          else
-            ((uint16_t*)g.C)[(int64_t)m * g.ldc + n] = f2bf(acc[i][j][r]);
-        }
+        if (m >= M) continue;
+        if (g.epi == EPI_KV_SPLIT)
+          kv_split_store(g.kv, (uint16_t*)g.C, (uint16_t*)g.kv.vt, m, n, f2bf(acc[i][j][r]));
+        else if (g.c_dtype == DT_F32)
+          ((float*)g.C)[(int64_t)m * g.ldc + n] = acc[i][j][r];
+        else
+          ((uint16_t*)g.C)[(int64_t)m * g.ldc + n] = f2bf(acc[i][j][r]);
       }
     }
 }

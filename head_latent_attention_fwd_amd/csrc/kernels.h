@@ -11,6 +11,13 @@ enum { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
 // C[b][M, N] = A[b][M, K] . W[b]^T. W is [N, K] (K contiguous) unless w_kn, in
 // which case it is [K, N] (N contiguous). Rows n >= n_split of W come from W2
 // (row n - n_split), which lets one launch cover two stacked weight matrices.
+// Epilogues: EPI_ROWMAJOR writes C[m, n] (ldc). EPI_KV_SPLIT treats the
+// N = H*256 columns as per-head [k_nope 128 | v 128] and rows m = b*T + t, and
+// writes k_nope to C = KN [B, H, Tp, 128] and v transposed to C2 = VT [B, H, 128, Tp].
+enum { EPI_ROWMAJOR = 0, EPI_KV_SPLIT = 1 };
+struct KvSplit {
+  void* vt; int T, Tp, H;
+};
 struct GemmArgs {
   const void* A; int64_t lda; int64_t batch_a;
   const void* W; int64_t ldw; int64_t batch_w;
@@ -18,7 +25,17 @@ struct GemmArgs {
   void* C; int64_t ldc; int64_t batch_c; int c_dtype;
   int M, N, K, batch;
   bool w_kn;
+  int epi; KvSplit kv;
 };
+
+// Store of one output element for the EPI_KV_SPLIT layout (m = b*T + t, n = h*256 + j).
+template <typename T_>
+__device__ __forceinline__ void kv_split_store(const KvSplit& s, T_* kn, T_* vt, int m, int n, T_ v) {
+  const int b = m / s.T, t = m - b * s.T, h = n >> 8, j = n & 255;
+  const int64_t bh = (int64_t)b * s.H + h;
+  if (j < 128) kn[(bh * s.Tp + t) * 128 + j] = v;
+  else vt[(bh * 128 + (j - 128)) * s.Tp + t] = v;
+}
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s);
 
@@ -29,6 +46,7 @@ struct GemmFp8Args {
   const uint8_t* W2; const float* w2_scale; int n_split;
   void* C; int64_t ldc; int c_dtype;
   int M, N, K;
+  int epi; KvSplit kv;
 };
 hipError_t launch_gemm_fp8(const GemmFp8Args& g, hipStream_t s);
 
@@ -39,6 +57,9 @@ struct NormRopeArgs {
   int rope_off, rope_heads, rope_stride;
   const float* cos_tab; const float* sin_tab; int rope_len;
   const int32_t* pos; int pos_period;
+  // optional second copy of the rotated slice (rope_heads == 1): row m = b*T + t
+  // goes to kpe[(b*kpe_tp + t)*64], T = pos_period
+  void* kpe; int kpe_tp;
 };
 hipError_t launch_rmsnorm_rope(const NormRopeArgs& a, hipStream_t s);
 hipError_t launch_rope_table(float* c, float* sn, int n_pos, float base, hipStream_t s);
@@ -47,14 +68,18 @@ hipError_t launch_quant_1x128(const void* a, int64_t lda, int a_dtype, int M, in
 hipError_t launch_quant_block128(const float* w, int N, int K, uint8_t* q, float* scales, hipStream_t s);
 hipError_t launch_topk_bitmask(const int32_t* idx, int B, int T, int k, uint32_t* mask, hipStream_t s);
 
-// Prefill attention. q [B*T, H*192] (rope applied), u [B*T, H*256] = per head
-// [k_nope | v], kv [B*T, ld_kv] with the rotated shared key at kpe_off,
-// optional bitmask [B, T, ceil(T/32)], out [B*T, H*128].
+// Prefill attention. q [B*T, H*192] (rope applied), kn [B, H, Tp, 128],
+// vt [B, H, 128, Tp], kpe [B, Tp, 64] (rotated shared key), optional bitmask
+// [B, T, ceil(T/32)], out [B*T, H*128]. Tp = T rounded up to 64; the padding
+// keys (t >= T) of kn, vt and kpe must hold finite values.
 struct PrefillAttnArgs {
-  const void* q; const void* u; const void* kv; int64_t ld_kv; int kpe_off;
+  const void* q; const void* kn; const void* vt; const void* kpe;
   const uint32_t* mask; void* out;
-  int B, T, H; float scale;
+  int B, T, Tp, H; float scale;
 };
+// Zeroes the padding keys t in [T, Tp) of kn, vt and kpe (no-op when T == Tp).
+hipError_t launch_zero_kv_padding(void* kn, void* vt, void* kpe, int B, int H, int T, int Tp, int elem_bytes,
+                                  hipStream_t s);
 hipError_t launch_prefill_attn_bf16(const PrefillAttnArgs& a, hipStream_t s);
 hipError_t launch_prefill_attn_f32(const PrefillAttnArgs& a, hipStream_t s);
 

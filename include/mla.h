@@ -184,6 +184,33 @@ MLA_API int rmsnorm_rope(const void* in, int64_t ld_in, int32_t in_dtype, int32_
                  const float* cos_tab, const float* sin_tab, int32_t rope_len, const int32_t* pos,
                  int32_t pos_period, void* out, int64_t ld_out, int32_t out_dtype, void* stream);
 
+/* The fused prefill attention step alone (DeepSeek-V3.2-Exp · Sparse attention,
+ * "Code": scores over [non-rotated | shared rotary] keys, selection + causal
+ * mask, softmax, weighted values), never materialising the T x T scores.
+ * With Tp = T rounded up to a multiple of 64:
+ *   q      [B*T, H*192]    per head [q_nope 128 | q_pe 64], RoPE already applied
+ *   k_nope [B, H, Tp, 128] per-head non-rotated keys (kv_b output, key half)
+ *   v_t    [B, H, 128, Tp] per-head values, transposed (kv_b output, value half)
+ *   k_pe   [B, Tp, 64]     rotated shared key
+ *   mask   [B, T, ceil(T/32)] uint32 selection bits (mla_topk_to_bitmask) or NULL
+ *          for causal only; a key is live iff its bit is set and t <= s
+ *   out    [B*T, H*128]
+ * The padding keys t in [T, Tp) of k_nope, v_t and k_pe are overwritten with 0.
+ * dtype MLA_BF16 or MLA_F32 for every tensor. Rows with no live key give 0. */
+MLA_API int mla_prefill_attention(const void* q, const void* k_nope, const void* v_t, const void* k_pe,
+                                  const uint32_t* mask, void* out, int32_t dtype, int32_t B, int32_t T,
+                                  int32_t H, float scale, void* stream);
+
+/* The absorbed decode attention step alone (DeepSeek-V3.2-Exp · Sparse
+ * attention, "Explanation"): for each sequence b and head h,
+ *   o_lat[b, h] = sum_{t <= cache_len[b]} softmax_t(scale * q_lat[b, h] . C[b, t]) C[b, t, :512]
+ *   q_lat [B, H, 576] bf16 (latent-space query 512 | rotated q_pe 64)
+ *   cache [B, max_len, 576] bf16; cache_len [B] int32 device array
+ *   o_lat [B, H, 512] bf16 (zero for sequences whose cache_len is out of range)
+ * H must be a multiple of 64. */
+MLA_API int mla_decode_attention(const void* q_lat, const void* cache, const int32_t* cache_len, void* o_lat,
+                                 int32_t B, int32_t H, int32_t max_len, float scale, void* stream);
+
 /* cos/sin table for RoPE: cos_tab[p, d] = cos(p * base^(-d/32)), sin likewise,
  * for p < n_pos, d < 32, evaluated in fp64 and stored fp32. */
 MLA_API int mla_rope_table(float* cos_tab, float* sin_tab, int32_t n_pos, float base, void* stream);

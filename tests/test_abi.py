@@ -69,7 +69,9 @@ def test_workspace_sizes(lib):
     d = _dims()
     bf = api.mla_prefill_workspace_size(d, api.MLA_BF16, api.MLA_BF16, 1, 2048, 0)
     M = 2048
-    expect_min = M * (1536 + 576) * 2 + M * 1536 * 2 + M * 576 * 2 + M * 64 * (192 + 256 + 128) * 2
+    # [c_q|latent|k_pe], c_q normed, cache entries, q, k_nope + v^T, attention out, padded k_pe
+    expect_min = (M * (1536 + 576) * 2 + M * 1536 * 2 + M * 576 * 2 + M * 64 * (192 + 256 + 128) * 2
+                  + M * 64 * 2)
     assert expect_min <= bf <= expect_min + 256 * 16
     sp = api.mla_prefill_workspace_size(d, api.MLA_BF16, api.MLA_BF16, 1, 2048, 2048)
     assert sp - bf >= 2048 * 64 * 4

@@ -154,3 +154,49 @@ def test_boundary_errors_do_not_launch():
     with pytest.raises(api.MlaError) as e:
         api.mla_quant_e4m3_1x128(a, scales=torch.zeros((4, 1), dtype=torch.float32, device=DEV))
     assert e.value.code == api.MLA_UNSUPPORTED
+
+
+@pytest.mark.parametrize("B,T,H,k", [(2, 190, 3, 0), (1, 300, 2, 37), (1, 4096, 1, 2048), (3, 5, 2, 0)])
+def test_prefill_attention_step(B, T, H, k):
+    rng = np.random.default_rng(B * T + H + k)
+    Tp = api.pad64(T)
+    q = synth.round_bf16(rng.standard_normal((B * T, H * 192)))
+    kn = synth.round_bf16(rng.standard_normal((B, H, T, 128)))
+    v = synth.round_bf16(rng.standard_normal((B, H, T, 128)))
+    kp = synth.round_bf16(rng.standard_normal((B, T, 64)))
+    idx = synth.draw_topk(rng, B, T, k) if k else None
+    m = api.mla_topk_to_bitmask(dev(idx, torch.int32)) if k else None
+    # device layouts, with junk (NaN) in the padding keys: the call must zero it
+    KN = torch.full((B, H, Tp, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    KN[:, :, :T] = dev(kn, torch.bfloat16)
+    VT = torch.full((B, H, 128, Tp), float("nan"), dtype=torch.bfloat16, device=DEV)
+    VT[:, :, :, :T] = dev(np.ascontiguousarray(v.transpose(0, 1, 3, 2)), torch.bfloat16)
+    KP = torch.full((B, Tp, 64), float("nan"), dtype=torch.bfloat16, device=DEV)
+    KP[:, :T] = dev(kp, torch.bfloat16)
+    out = torch.empty((B * T, H * 128), dtype=torch.bfloat16, device=DEV)
+    api.mla_prefill_attention(dev(q, torch.bfloat16), KN, VT, KP, out, B, T, H, mask=m)
+    got = out.float().cpu().numpy().reshape(B, T, H, 128)
+    rows = sorted(set([0, T // 3, T - 1] + [int(r) for r in rng.integers(0, T, 6)]))
+    sc = 192.0 ** -0.5
+    for b in range(B):
+        qq = q.reshape(B, T, H, 192)[b]
+        ref = np.stack([mla.attend_row(qq[s, :, :128], qq[s, :, 128:], kn[b].transpose(1, 0, 2), kp[b],
+                                       v[b].transpose(1, 0, 2),
+                                       mla.live_keys(s, None if idx is None else idx[b, s]), sc)[0] for s in rows])
+        assert_parity(got[b, rows], ref, what=f"attention b={b}")
+
+
+def test_decode_attention_step():
+    rng = np.random.default_rng(9)
+    B, H, max_len = 5, 128, 300
+    lens = np.array([0, 31, 32, 299, 150], dtype=np.int32)
+    ql = synth.round_bf16(rng.standard_normal((B, H, 576)) * 0.3)
+    cache = synth.round_bf16(rng.standard_normal((B, max_len, 576)))
+    ol = torch.empty((B, H, 512), dtype=torch.bfloat16, device=DEV)
+    api.mla_decode_attention(dev(ql, torch.bfloat16), dev(cache, torch.bfloat16), dev(lens, torch.int32), ol)
+    got = ol.float().cpu().numpy()
+    for b in range(B):
+        C = cache[b, :lens[b] + 1].astype(np.float64)
+        z = ql[b].astype(np.float64) @ C.T * 192.0 ** -0.5
+        ref = mla.softmax_over_live(z) @ C[:, :512]
+        assert_parity(got[b], ref, what=f"decode attention b={b}")
