@@ -106,14 +106,18 @@ size_t prefill_layout(const mla_dims* d, int wdt, int adt, int B, int T, int top
 }
 
 struct DecodeWs {
-  void *cqkv, *cqn, *entry, *q, *qlat, *olat, *o;
+  void *part, *cqn, *entry, *q, *qlat, *olat, *o;
 };
+
+// split-K factors of the two decode projections with long K
+constexpr int DEC_SPLIT_QKV = 8, DEC_SPLIT_WO = 4;
 
 size_t decode_layout(const mla_dims* d, int B, void* ws, DecodeWs* out) {
   const size_t H = d->n_heads, Dq = d->q_lora_rank, L = d->kv_lora_rank;
   Carver c(ws);
   DecodeWs p{};
-  p.cqkv = c.take((size_t)B * (Dq + L + 64) * 2);
+  const size_t part_qkv = (size_t)DEC_SPLIT_QKV * B * (Dq + L + 64), part_wo = (size_t)DEC_SPLIT_WO * B * d->dim;
+  p.part = c.take((part_qkv > part_wo ? part_qkv : part_wo) * 4);
   p.cqn = c.take((size_t)B * Dq * 2);
   p.entry = c.take((size_t)B * (L + 64) * 2);
   p.q = c.take((size_t)B * H * 192 * 2);
@@ -162,6 +166,36 @@ int project(int wdt, int adt, const void* act, int64_t lda, const void* W, const
   if (kv) g.kv = *kv;
   if (adt == MLA_F32) LAUNCH(mla::launch_gemm_f32(g, s), "gemm_f32");
   else LAUNCH(mla::launch_gemm_bf16(g, s), "gemm_bf16");
+  return MLA_OK;
+}
+
+// Decode-shaped product C[z] = A[z] . W[z]^T over rows in chunks of 128; with
+// splits > 1 the fp32 partials land in P[split][M][N] (rows at P + m*N).
+// K chunk (elements) of a split-K skinny product and the number of chunks it makes.
+int skinny_kc(int K, int splits) {
+  const int ksteps = K / 64;
+  if (splits > ksteps) splits = ksteps;
+  return ((ksteps + splits - 1) / splits) * 64;
+}
+int skinny_splits(int K, int splits) { return (K + skinny_kc(K, splits) - 1) / skinny_kc(K, splits); }
+
+int skinny(const void* A, int64_t lda, int64_t batch_a, const void* W, int64_t ldw, int64_t batch_w,
+           const void* W2, int64_t ldw2, int n_split, void* C, int64_t ldc, int64_t batch_c, float* P, int M, int N,
+           int K, int batch, int nt, int splits, hipStream_t s) {
+  if (K % 64 || K == 0 || lda % 8 || batch_a % 8 || ldw % 8 || batch_w % 8 || (W2 && ldw2 % 8) ||
+      ((uintptr_t)A | (uintptr_t)W | (uintptr_t)W2) % 16)
+    return fail(MLA_UNSUPPORTED, "decode projection needs K % 64 == 0 and 16-byte aligned rows");
+  const int kc = skinny_kc(K, splits);
+  splits = skinny_splits(K, splits);
+  for (int m0 = 0; m0 < M; m0 += 128) {
+    mla::SkinnyArgs g{};
+    g.A = (const uint16_t*)A + (int64_t)m0 * lda; g.lda = lda; g.batch_a = batch_a;
+    g.W = W; g.ldw = ldw; g.batch_w = batch_w; g.W2 = W2; g.ldw2 = ldw2; g.n_split = n_split;
+    g.C = C ? (void*)((uint16_t*)C + (int64_t)m0 * ldc) : nullptr; g.ldc = ldc; g.batch_c = batch_c;
+    g.P = P ? P + (int64_t)m0 * N : nullptr; g.ps = (int64_t)M * N;
+    g.M = M - m0 < 128 ? M - m0 : 128; g.N = N; g.K = K; g.kc = kc; g.batch = batch;
+    LAUNCH(mla::launch_gemm_skinny(g, nt, splits, s), "gemm_skinny");
+  }
   return MLA_OK;
 }
 
@@ -277,27 +311,31 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B
   hipStream_t s = (hipStream_t)stream;
   const int H = d->n_heads, Dq = d->q_lora_rank, L = d->kv_lora_rank, dim = d->dim, NQKV = Dq + L + 64;
 
+  if (dim % 64 || Dq % 64) return fail(MLA_UNSUPPORTED, "decode needs dim and q_lora_rank multiples of 64");
+  float* part = (float*)p.part;
+  // [c_q | latent | k_pe] = x . [Wq_a ; Wkv_a]^T as split-K partials, summed by the norms
+  if ((rc = skinny(x, dim, 0, w->wq_a, dim, 0, w->wkv_a, dim, Dq, nullptr, 0, 0, part, B, NQKV, dim, 1, 64,
+                   DEC_SPLIT_QKV, s)))
+    return rc;
+  const int splits_qkv = skinny_splits(dim, DEC_SPLIT_QKV);
   {
-    mla::GemmArgs g = gemm_args(x, dim, w->wq_a, dim, p.cqkv, NQKV, MLA_BF16, B, NQKV, dim);
-    g.W2 = w->wkv_a; g.ldw2 = dim; g.n_split = Dq;
-    LAUNCH(mla::launch_gemm_bf16(g, s), "gemm(q_a|kv_a)");
-  }
-  {
-    mla::NormRopeArgs a = norm_args(p.cqkv, NQKV, p.cqn, Dq, MLA_BF16, B);
+    mla::NormRopeArgs a = norm_args(part, NQKV, p.cqn, Dq, MLA_F32, B);
+    a.out_dtype = MLA_BF16; a.in_splits = splits_qkv; a.split_stride = (int64_t)B * NQKV;
     a.norm_dim = Dq; a.gamma = w->q_norm_w; a.eps = d->rms_eps;
     LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm(q)");
   }
   {
-    mla::NormRopeArgs a = norm_args((const uint16_t*)p.cqkv + Dq, NQKV, p.entry, L + 64, MLA_BF16, B);
+    mla::NormRopeArgs a = norm_args(part + Dq, NQKV, p.entry, L + 64, MLA_F32, B);
+    a.out_dtype = MLA_BF16; a.in_splits = splits_qkv; a.split_stride = (int64_t)B * NQKV;
     a.norm_dim = L; a.gamma = w->kv_norm_w; a.eps = d->rms_eps;
     a.rope_off = L; a.rope_heads = 1; a.rope_stride = 64;
     a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = max_len; a.pos = cache_len;
     LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(kv)");
   }
-  {
-    mla::GemmArgs g = gemm_args(p.cqn, Dq, w->wq_b, Dq, p.q, H * 192, MLA_BF16, B, H * 192, Dq);
-    LAUNCH(mla::launch_gemm_bf16(g, s), "gemm(q_b)");
-  }
+  // q = c_q . Wq_b^T
+  if ((rc = skinny(p.cqn, Dq, 0, w->wq_b, Dq, 0, nullptr, 0, H * 192, p.q, H * 192, 0, nullptr, B, H * 192, Dq, 1, 64,
+                   1, s)))
+    return rc;
   {  // q_lat[b, h, :512] = q_nope[b, h] . W_UK_h  (W_UK_h = Wkv_b rows [256h, 256h+128), read [K, N])
     mla::GemmArgs g = gemm_args(p.q, H * 192, w->wkv_b, L, p.qlat, H * 576, MLA_BF16, B, L, 128);
     g.batch = H; g.batch_a = 192; g.batch_w = 256 * (int64_t)L; g.batch_c = 576; g.w_kn = true;
@@ -311,16 +349,16 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B
     a.B = B; a.H = H; a.max_len = max_len; a.scale = d->softmax_scale;
     LAUNCH(mla::launch_decode_attn(a, s), "decode_attn");
   }
-  {  // o[b, h] = W_UV_h . o_lat[b, h]  (W_UV_h = Wkv_b rows [256h+128, 256h+256))
-    mla::GemmArgs g = gemm_args(p.olat, H * 512, (const uint16_t*)w->wkv_b + 128 * (int64_t)L, L, p.o, H * 128,
-                                MLA_BF16, B, 128, L);
-    g.batch = H; g.batch_a = 512; g.batch_w = 256 * (int64_t)L; g.batch_c = 128;
-    LAUNCH(mla::launch_gemm_bf16(g, s), "gemm(un-absorb W_UV)");
-  }
-  {
-    mla::GemmArgs g = gemm_args(p.o, H * 128, w->wo, H * 128, out, dim, MLA_BF16, B, dim, H * 128);
-    LAUNCH(mla::launch_gemm_bf16(g, s), "gemm(wo)");
-  }
+  // o[b, h] = W_UV_h . o_lat[b, h]  (W_UV_h = Wkv_b rows [256h+128, 256h+256)), per head
+  if ((rc = skinny(p.olat, H * 512, 512, (const uint16_t*)w->wkv_b + 128 * (int64_t)L, L, 256 * (int64_t)L, nullptr,
+                   0, 128, p.o, H * 128, 128, nullptr, B, 128, L, H, 64, 1, s)))
+    return rc;
+  // out = o . Wo^T (split-K, then a fixed-order sum)
+  if ((rc = skinny(p.o, H * 128, 0, w->wo, H * 128, 0, nullptr, 0, dim, nullptr, 0, 0, part, B, dim, H * 128, 1, 128,
+                   DEC_SPLIT_WO, s)))
+    return rc;
+  LAUNCH(mla::launch_splitk_reduce(part, skinny_splits(H * 128, DEC_SPLIT_WO), B, dim, out, dim, s),
+         "splitk_reduce(wo)");
   return MLA_OK;
 }
 

@@ -21,7 +21,8 @@
 // 16-key block the K rows are stored with bits 2 and 3 of the key index
 // swapped: the 32x32 MFMA output then gives each lane 8 consecutive keys per
 // 16-key step, so the matching V^T operand is one 16-byte LDS read. 16-byte
-// chunks are XOR-swizzled by row in every region (conflict-free reads).
+// chunks are XOR-swizzled by row in every region (conflict-free reads with 32
+// or 64 LDS banks).
 //
 // The running max is only raised when a row's max grows by more than 2^8
 // (probabilities stay <= 256 in the meantime), so the O rescale is rare.
@@ -39,6 +40,8 @@ constexpr int LOADS = STAGE * 2 / 16 / 256;  // 16-byte direct loads per thread 
 constexpr float LAZY = 8.0f;
 
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+// chunk swizzle of 128-byte rows, conflict-free for 32 or 64 LDS banks
+__device__ __forceinline__ int sw8(int r) { return (r ^ (r >> 3)) & 7; }
 
 __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
@@ -70,16 +73,16 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int p = (wave * LOADS + i) * 64 + lane;
-    if (p < ST_KPE / 8) {                       // k_nope: row rho, chunk' = chunk ^ (rho & 7)
-      const int rho = p >> 4, c = (p & 15) ^ (rho & 7);
+    if (p < ST_KPE / 8) {                       // k_nope: row rho, chunk' = chunk ^ (rho & 15)
+      const int rho = p >> 4, c = (p & 15) ^ (rho & 15);
       src[i] = (const uint16_t*)a.kn + (bh * Tp + swap23(rho)) * 128 + c * 8;
       adv[i] = BKV * 128;
     } else if (p < ST_VT / 8) {                 // k_pe
-      const int q = p - ST_KPE / 8, rho = q >> 3, c = (q & 7) ^ (rho & 7);
+      const int q = p - ST_KPE / 8, rho = q >> 3, c = (q & 7) ^ sw8(rho);
       src[i] = (const uint16_t*)a.kpe + ((int64_t)b * Tp + swap23(rho)) * 64 + c * 8;
       adv[i] = BKV * 64;
     } else {                                    // v^T: row dv, 8-key chunk
-      const int q = p - ST_VT / 8, dv = q >> 3, c = (q & 7) ^ (dv & 7);
+      const int q = p - ST_VT / 8, dv = q >> 3, c = (q & 7) ^ sw8(dv);
       src[i] = (const uint16_t*)a.vt + (bh * 128 + dv) * Tp + c * 8;
       adv[i] = BKV;
     }
@@ -93,13 +96,14 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   };
 
   // LDS operand offsets (elements), invariant over tiles
-  const int x7 = l32 & 7;
-  int xk[4];
+  const int x15 = l32 & 15;
+  int xk[8], xp[2][4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) xk[v] = ((2 * v + hi) ^ x7) << 3;
-  int xv[4];
+  for (int v = 0; v < 8; ++v) xk[v] = ((2 * v + hi) ^ x15) << 3;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) xv[ks] = ((4 * (ks >> 1) + 2 * (ks & 1) + hi) ^ x7) << 3;
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) xp[kb][v] = ((2 * v + hi) ^ sw8(kb * 32 + l32)) << 3;
 
   floatx16 o[4];
 #pragma unroll
@@ -136,8 +140,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int rho = kb * 32 + l32;
-        const int off = kk < 8 ? ST_KN + rho * 128 + (kk >> 2) * 64 + xk[kk & 3]
-                               : ST_KPE + rho * 64 + xk[kk - 8];
+        const int off = kk < 8 ? ST_KN + rho * 128 + xk[kk] : ST_KPE + rho * 64 + xp[kb][kk - 8];
         s[kb] = mfma32(*(const bf16x8*)(sb + off), qf[kk], s[kb]);
       }
     }
@@ -190,7 +193,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x8 vf = *(const bf16x8*)(sb + ST_VT + (j * 32 + l32) * 64 + xv[ks]);
+        const int dv = j * 32 + l32;
+        const int c = (4 * (ks >> 1) + 2 * (ks & 1) + hi) ^ sw8(dv);
+        const bf16x8 vf = *(const bf16x8*)(sb + ST_VT + dv * 64 + (c << 3));
         o[j] = mfma32(vf, pf[ks], o[j]);
       }
   }

@@ -10,6 +10,14 @@ namespace {
 __device__ __forceinline__ float ld(const void* p, int dt, int64_t i) {
   return dt == DT_F32 ? ((const float*)p)[i] : bf2f(((const uint16_t*)p)[i]);
 }
+// input element i of a row-wise kernel: one array, or the sum of split-K partials
+__device__ __forceinline__ float ld_in(const NormRopeArgs& a, int64_t i) {
+  if (a.in_splits <= 1) return ld(a.in, a.in_dtype, i);
+  const float* p = (const float*)a.in;
+  float v = p[i];
+  for (int s = 1; s < a.in_splits; ++s) v += p[(int64_t)s * a.split_stride + i];
+  return v;
+}
 __device__ __forceinline__ void st(void* p, int dt, int64_t i, float v) {
   if (dt == DT_F32) ((float*)p)[i] = v;
   else ((uint16_t*)p)[i] = f2bf(v);
@@ -45,13 +53,13 @@ __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(NormRopeArgs a, int r
   if (a.norm_dim > 0) {
     float ss = 0.f;
     for (int i = tid; i < a.norm_dim; i += 256) {
-      float v = ld(a.in, a.in_dtype, ib + i);
+      float v = ld_in(a, ib + i);
       ss = fmaf(v, v, ss);
     }
     ss = block_sum(ss, red);
     const float r = 1.0f / sqrtf(ss / (float)a.norm_dim + a.eps);
     for (int i = tid; i < a.norm_dim; i += 256)
-      st(a.out, a.out_dtype, ob + i, a.gamma[i] * (ld(a.in, a.in_dtype, ib + i) * r));
+      st(a.out, a.out_dtype, ob + i, a.gamma[i] * (ld_in(a, ib + i) * r));
   }
   if (a.rope_heads > 0) {
     const int pos = a.pos ? a.pos[row] : row % a.pos_period;
@@ -59,7 +67,7 @@ __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(NormRopeArgs a, int r
     for (int p = tid; p < a.rope_heads * 32; p += 256) {
       const int h = p >> 5, d = p & 31;
       const int64_t o = a.rope_off + (int64_t)h * a.rope_stride + d;
-      const float x1 = ld(a.in, a.in_dtype, ib + o), x2 = ld(a.in, a.in_dtype, ib + o + 32);
+      const float x1 = ld_in(a, ib + o), x2 = ld_in(a, ib + o + 32);
       float c = 0.f, s = 0.f;
       if (ok) { c = a.cos_tab[pos * 32 + d]; s = a.sin_tab[pos * 32 + d]; }
       const float y1 = x1 * c - x2 * s, y2 = x2 * c + x1 * s;

@@ -1,0 +1,195 @@
+// Skinny bf16 GEMM for the decode step (M = batch <= 128 rows): C = A . W^T,
+// bound by streaming W from HBM. One workgroup owns all M rows, NT columns of
+// W and one K chunk (split-K over gridDim.y); every byte of W is read once and
+// the small A chunk is re-read from L2. K moves in 64-wide steps through a
+// 4-stage LDS ring of 16-byte direct-to-LDS loads (three steps in flight ahead
+// of the MFMAs); chunks of each 128-byte row are XOR-swizzled by
+// (row ^ row >> 3) & 7. Wave w computes rows 32w..32w+31 with
+// v_mfma_f32_32x32x16_bf16 (W as the first operand, so a lane's results are 4
+// consecutive columns of one row). With one split the bf16 result is stored
+// directly; otherwise fp32 partials go to P[split][M][N] and are summed in a
+// fixed order by splitk_reduce (or by the consumer), so results are
+// deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+namespace {
+
+constexpr int SK_BK = 64, SK_ST = 4;
+
+__device__ __forceinline__ int sk_sw(int row) { return (row ^ (row >> 3)) & 7; }
+
+template <int NT>
+__device__ __forceinline__ void gemm_skinny_body(const SkinnyArgs& g) {
+  constexpr int SLOTS = (128 + NT) * 8;          // 16-byte slots per stage
+  constexpr int LPT = SLOTS / 256;               // loads per thread per stage
+  constexpr int STAGE = SLOTS * 8;               // elements per stage
+  constexpr int FN = NT / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SK_ST * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int n0 = blockIdx.x * NT, split = blockIdx.y, z = blockIdx.z;
+  const int M = g.M, N = g.N;
+  const int k_begin = split * g.kc, k_end = min(g.K, k_begin + g.kc);
+  const int nk = (k_end - k_begin) / SK_BK;
+  const uint16_t* A = (const uint16_t*)g.A + (int64_t)z * g.batch_a + k_begin;
+  const uint16_t* W = (const uint16_t*)g.W + (int64_t)z * g.batch_w + k_begin;
+  const uint16_t* W2 = (const uint16_t*)g.W2 + k_begin;
+
+  // slot p of a stage: rows 0..127 of A, then rows 0..NT-1 of W, 8 chunks each
+  const uint16_t* src[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int p = (wave * LPT + i) * 64 + lane;
+    const int r = p >> 3;
+    if (p < 1024) {
+      const int c = (p & 7) ^ sk_sw(r);
+      src[i] = A + (int64_t)min(r, M - 1) * g.lda + c * 8;
+    } else {
+      const int rw = r - 128, c = (p & 7) ^ sk_sw(rw);
+      const int n = min(n0 + rw, N - 1);
+      src[i] = (n < g.n_split ? W + (int64_t)n * g.ldw : W2 + (int64_t)(n - g.n_split) * g.ldw2) + c * 8;
+    }
+  }
+  auto issue = [&](int kt) {
+    uint16_t* st = smem + (kt % SK_ST) * STAGE + wave * LPT * 512;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) __builtin_amdgcn_global_load_lds(src[i] + kt * SK_BK, st + i * 512, 16, 0, 0);
+  };
+  // wait until step kt has landed; `ahead` later steps may still be in flight
+  auto wait_ahead = [&](int ahead) {
+    if (ahead >= 3) {
+      if constexpr (LPT == 6) __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(18)" ::: "memory");
+      else __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(24)" ::: "memory");
+    } else if (ahead == 2) {
+      if constexpr (LPT == 6) __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(12)" ::: "memory");
+      else __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(16)" ::: "memory");
+    } else if (ahead == 1) {
+      if constexpr (LPT == 6) __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(6)" ::: "memory");
+      else __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+      __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+  };
+
+  floatx16 acc[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+
+  // swizzled offsets: A row 32 wave + l32 (parity of wave), W row 32 j + l32 (parity of j)
+  int xa[4], xw[2][4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    xa[kk] = ((2 * kk + hi) ^ sk_sw(32 * wave + l32)) << 3;
+    xw[0][kk] = ((2 * kk + hi) ^ sk_sw(l32)) << 3;
+    xw[1][kk] = ((2 * kk + hi) ^ sk_sw(32 + l32)) << 3;
+  }
+  bf16x8 fa[2], fb[2][FN];
+  auto read = [&](int kt, int kk, int buf) {
+    const uint16_t* st = smem + (kt % SK_ST) * STAGE;
+    fa[buf] = *(const bf16x8*)(st + (32 * wave + l32) * SK_BK + xa[kk]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[buf][j] = *(const bf16x8*)(st + (128 + 32 * j + l32) * SK_BK + xw[j & 1][kk]);
+  };
+
+  if (nk > 0) {
+    for (int s = 0; s < SK_ST; ++s)
+      if (s < nk) issue(s);
+    wait_ahead(min(nk, SK_ST) - 1);   // step 0 has landed
+  }
+  if (nk > 0) read(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cb = kk & 1;
+      if (kk < 3) {
+        read(kt, kk + 1, cb ^ 1);
+      } else if (kt + 1 < nk) {
+        wait_ahead(min(nk - 2 - kt, 2));
+        if (kt + SK_ST < nk) issue(kt + SK_ST);
+        read(kt + 1, 0, cb ^ 1);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[j] = mfma32(fb[cb][j], fa[cb], acc[j]);
+    }
+  }
+
+  // lane: row m = 32 wave + l32, columns n0 + 32 j + 8 rg + 4 hi + 0..3
+  const int m = 32 * wave + l32;
+  if (m >= M) return;
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int n = n0 + 32 * j + 8 * rg + 4 * hi;
+      if (n >= N) continue;
+      const float v0 = acc[j][4 * rg], v1 = acc[j][4 * rg + 1], v2 = acc[j][4 * rg + 2], v3 = acc[j][4 * rg + 3];
+      if (gridDim.y == 1) {
+        uint16_t* c = (uint16_t*)g.C + (int64_t)z * g.batch_c + (int64_t)m * g.ldc + n;
+        if (n + 4 <= N && (g.ldc & 3) == 0 && (g.batch_c & 3) == 0) {
+          *(uint2*)c = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+        } else {
+          const float v[4] = {v0, v1, v2, v3};
+          for (int e = 0; n + e < N; ++e) c[e] = f2bf(v[e]);
+        }
+      } else {
+        float* p = g.P + (int64_t)split * g.ps + (int64_t)m * N + n;
+        if (n + 4 <= N && (N & 3) == 0) {
+          *(float4*)p = make_float4(v0, v1, v2, v3);
+        } else {
+          const float v[4] = {v0, v1, v2, v3};
+          for (int e = 0; n + e < N; ++e) p[e] = v[e];
+        }
+      }
+    }
+}
+
+__global__ __launch_bounds__(256, 1) void gemm_skinny64_kernel(SkinnyArgs g) { gemm_skinny_body<64>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_skinny128_kernel(SkinnyArgs g) { gemm_skinny_body<128>(g); }
+
+// out[m, n] = sum over s of P[s][m][n] (s ascending), stored bf16.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* P, int S, int M, int N, uint16_t* out,
+                                                            int64_t ldo) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const int64_t total = (int64_t)M * N;
+  if (i >= total) return;
+  const int m = (int)(i / N), n = (int)(i - (int64_t)m * N);
+  if (n + 4 <= N && (N & 3) == 0) {
+    float4 acc = *(const float4*)(P + i);
+    for (int s = 1; s < S; ++s) {
+      const float4 v = *(const float4*)(P + (int64_t)s * total + i);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    *(uint2*)(out + (int64_t)m * ldo + n) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+  } else {
+    for (int e = 0; e < 4 && i + e < total; ++e) {
+      const int me = (int)((i + e) / N), ne = (int)((i + e) - (int64_t)me * N);
+      float a = 0.f;
+      for (int s = 0; s < S; ++s) a += P[(int64_t)s * total + i + e];
+      out[(int64_t)me * ldo + ne] = f2bf(a);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_skinny(const SkinnyArgs& g, int nt, int splits, hipStream_t s) {
+  dim3 grid((g.N + nt - 1) / nt, splits, g.batch);
+  if (nt == 64) gemm_skinny64_kernel<<<grid, 256, 0, s>>>(g);
+  else gemm_skinny128_kernel<<<grid, 256, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const float* P, int S, int M, int N, void* out, int64_t ldo, hipStream_t s) {
+  const int64_t total = (int64_t)M * N;
+  splitk_reduce_kernel<<<(unsigned)((total / 4 + 255) / 256 + 1), 256, 0, s>>>(P, S, M, N, (uint16_t*)out, ldo);
+  return hipGetLastError();
+}
+
+}  // namespace mla

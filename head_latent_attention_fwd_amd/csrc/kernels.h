@@ -50,6 +50,21 @@ struct GemmFp8Args {
 };
 hipError_t launch_gemm_fp8(const GemmFp8Args& g, hipStream_t s);
 
+// Decode-shaped GEMM (M <= 128): C[z][M, N] = A[z][M, K] . W[z][N, K]^T with
+// N tiles of nt (64 or 128) columns and `splits` K chunks of kc (multiple of
+// 64; K % 64 == 0). One split: bf16 C. Several: fp32 partials P[split][M][N].
+struct SkinnyArgs {
+  const void* A; int64_t lda; int64_t batch_a;
+  const void* W; int64_t ldw; int64_t batch_w;
+  const void* W2; int64_t ldw2; int n_split;
+  void* C; int64_t ldc; int64_t batch_c;
+  float* P; int64_t ps;   // partial of split s, row m: P + s*ps + m*N
+  int M, N, K, kc, batch;
+};
+hipError_t launch_gemm_skinny(const SkinnyArgs& g, int nt, int splits, hipStream_t s);
+// out[m, n] = sum_s P[s][m][n] as bf16 (row stride ldo).
+hipError_t launch_splitk_reduce(const float* P, int S, int M, int N, void* out, int64_t ldo, hipStream_t s);
+
 struct NormRopeArgs {
   const void* in; int64_t ld_in; int in_dtype;
   void* out; int64_t ld_out; int out_dtype;
@@ -60,6 +75,9 @@ struct NormRopeArgs {
   // optional second copy of the rotated slice (rope_heads == 1): row m = b*T + t
   // goes to kpe[(b*kpe_tp + t)*64], T = pos_period
   void* kpe; int kpe_tp;
+  // in_splits > 1: the input is the sum of in_splits fp32 partial arrays
+  // split_stride elements apart (split-K GEMM output)
+  int in_splits; int64_t split_stride;
 };
 hipError_t launch_rmsnorm_rope(const NormRopeArgs& a, hipStream_t s);
 hipError_t launch_rope_table(float* c, float* sn, int n_pos, float base, hipStream_t s);

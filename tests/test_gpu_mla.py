@@ -58,7 +58,7 @@ def test_prefill_small_fp32_topk():
 
 
 def test_prefill_small_fp8():
-    _check_prefill(small_cfg(T=160, dim=512, q_lora_rank=256, kv_lora_rank=256, n_heads=2, weight="e4m3"), 24,
+    _check_prefill(small_cfg(T=160, dim=1024, q_lora_rank=512, kv_lora_rank=512, n_heads=4, weight="e4m3"), 24,
                    tol=FP8_TOL, cos=0.999)
 
 
