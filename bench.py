@@ -208,7 +208,7 @@ def bench_decode(cfg_index, steps, warmup, kernels=False):
         ol = torch.empty((B, H, 512), device="cuda", dtype=torch.bfloat16)
         s = event_avg(lambda: api.mla_decode_attention(ql, run.cache, run.cache_len, ol), 10, flush=flush)
         res["kernels"] = {"attention": {"us": s * 1e6, "gbps": parts["cache"] / s / 1e9,
-                                        "frac": parts["cache"] / s / 1e9 / PEAK["hbm"]}}
+                                        "frac": parts["cache"] / s / 1e9 / PEAK["hbm"], "bytes": parts["cache"]}}
     del run, flush
     torch.cuda.empty_cache()
     return res
@@ -242,6 +242,22 @@ def cpu_baseline(cfg_index, rows=256):
     return {"value": flop / sec / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": sec, "sample": f"{cfg['name']}: K/V for all {T} positions, {rows} evenly spaced query rows "
                                       f"through attention and o_proj (fp64 numpy)"}
+
+
+def roofline_of(res):
+    """Roofline entry for the kernel that takes the most time in one workload."""
+    ks = res["kernels"]
+    dom = max(ks, key=lambda k: ks[k]["us"])
+    k = ks[dom]
+    if "tflops" in k:
+        src = ["attn_prefill.hip"] if dom == "attention" else ["gemm_bf16.hip"]
+        return {"kernel": dom, "bound": "mfma", "achieved": k["tflops"], "peak": PEAK["bf16"], "unit": "TFLOP/s",
+                "frac": k["frac"], "traffic": traffic_for(f"{res['workload']}:{dom}", src),
+                "algorithmic_flop_per_launch": k["flop"], "us_per_launch": k["us"]}
+    src = ["attn_decode.hip"] if dom == "attention" else ["gemm_skinny.hip"]
+    return {"kernel": dom, "bound": "hbm", "achieved": k["gbps"], "peak": PEAK["hbm"], "unit": "GB/s",
+            "frac": k["frac"], "traffic": traffic_for(f"{res['workload']}:{dom}", src),
+            "algorithmic_bytes_per_launch": k.get("bytes"), "us_per_launch": k["us"]}
 
 
 def main():
@@ -282,17 +298,9 @@ def main():
             "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
             "config": {k: head[k] for k in ("workload", "B", "T", "n_heads", "topk") if k in head}}
     if "kernels" in head:
-        ks = head["kernels"]
-        dom = max(ks, key=lambda k: ks[k]["us"])
-        src = ["attn_prefill.hip"] if dom == "attention" else ["gemm_bf16.hip"]
-        line["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": ks[dom]["tflops"], "peak": PEAK["bf16"],
-                            "unit": "TFLOP/s", "frac": ks[dom]["frac"],
-                            "traffic": traffic_for(f"{head['workload']}:{dom}", src),
-                            "algorithmic_flop_per_launch": ks[dom]["flop"]}
-    if 4 in results and "kernels" in results[4]:
-        line["roofline_decode_attention"] = {"bound": "hbm", "achieved": results[4]["kernels"]["attention"]["gbps"],
-                                             "peak": PEAK["hbm"], "unit": "GB/s",
-                                             "frac": results[4]["kernels"]["attention"]["frac"]}
+        line["roofline"] = roofline_of(head)
+    if 4 in results and results[4] is not head and "kernels" in results[4]:
+        line["roofline_decode_attention"] = roofline_of(results[4])
     line["workloads"] = {str(k): v for k, v in results.items()}
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -5,147 +5,292 @@
 // With kv_b's key half folded into the query, every head of sequence b scores
 // the same cache rows C_t = [latent 512 | rope key 64]:
 //   z[h, t] = scale * (q_lat[h] . C_t),  o_lat[h] = sum_t softmax_t(z[h]) C_t[:512]
-// so the cache is streamed from HBM once per sequence and shared by all heads.
+// so one cache tile in LDS serves all heads of a workgroup.
 //
-// One 256-thread workgroup per (64-head group, sequence); wave w owns 16 heads.
-// Scores are formed transposed (S^T = C . Q^T) on v_mfma_f32_16x16x32_bf16 so
-// a lane holds 8 keys of one head; o_lat^T = C^T . P^T reuses the
-// probabilities in place. Each 32-key tile is loaded once into LDS row-major
-// (A operand of the scores) and transposed (A operand of the output), the
-// transpose done as 8x8 register blocks.
+// Workgroup = (sequence b, group of 64 heads); the head groups of one
+// sequence are placed on the same XCD so the second read of the cache comes
+// from that XCD's L2. Cache tiles of 32 keys move HBM -> LDS with 16-byte
+// direct-to-LDS buffer loads through a 3-stage ring (two tiles in flight).
+// Wave (hb, dh) = (wave & 1, wave >> 1) serves heads 32hb..32hb+31:
+//   scores  S^T[t, h] = C[t, :] . Q^T[:, h]     each wave of a pair takes one half
+//           of the 576 contracted dims (its half of Q stays in registers) and
+//           the pair adds the two fp32 partials through LDS, in the same order;
+//   values  O^T[d, h] += C^T[d, t] . P^T[t, h]  for the wave's 256 latent dims,
+// both on v_mfma_f32_32x32x16_bf16 (C^T read with ds_read_b64_tr_b16). A lane's
+// score results are 16 keys of one head, which are exactly the k slots the
+// value product needs from P^T, so the probabilities stay in registers.
+//
+// Softmax: the running max of a head is fixed at its first live tile and
+// later tiles add exp2(z - m) <= 2^LAZY, so the accumulators are never
+// rescaled inside the loop. If a later score exceeds m + LAZY (a logit jump
+// of ~44 nats) the workgroup recomputes its output in two passes: exact
+// maxima first, then the accumulation with those maxima.
+//
+// LDS stage: latent rows [32][1024 B] then rope rows [32][128 B]. The 16-byte
+// chunks of latent row r are XOR-permuted within aligned groups of 16 by
+// ((r & 3) << 2) | ((r >> 2) & 3) and those of rope row r by (r >> 1) & 7, so
+// the row reads of the scores and the transposed reads of the values are free
+// of bank conflicts. The stages are distinct LDS objects and every access
+// names its stage statically, so the compiler can tell the reads of one stage
+// from the loads in flight into the others.
 #include "common.h"
 #include "kernels.h"
 
 namespace mla {
 namespace {
 
-constexpr int DKT = 32;        // keys per tile
-constexpr int CP = 576 + 8;    // sC pitch (elements)
-constexpr int TP = DKT + 4;    // sCt pitch (elements): conflict-free 8-byte reads
+constexpr int DKT = 32;                 // keys per tile
+constexpr int DROW = 576;               // elements per cache row
+constexpr int DLAT = DKT * 512;         // latent region of a stage (elements)
+constexpr int DSTAGE = DKT * DROW;      // elements per stage
+constexpr float LAZY = 64.f;            // log2-domain headroom over the fixed running max
+constexpr int BUF_DW3 = 0x00020000;     // gfx9 raw-buffer descriptor word 3
 
-__device__ __forceinline__ uint32_t sel_lo(uint32_t a_hi, uint32_t b_lo) { return (a_hi << 16) | (b_lo & 0xFFFFu); }
-__device__ __forceinline__ uint32_t sel_hi(uint32_t a_hi, uint32_t b_lo) { return (a_hi & 0xFFFF0000u) | (b_lo >> 16); }
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
 
-__global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sC[DKT * CP];
-  __shared__ __attribute__((aligned(16))) uint16_t sCt[512 * TP];
+__device__ __forceinline__ int swl(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swr(int r) { return (r >> 1) & 7; }
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int hg = blockIdx.x, b = blockIdx.y, H = a.H;
-  const int head = hg * 64 + wave * 16 + l16;
+__device__ __forceinline__ v4s read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+}
+
+struct DecodeCtx {
+  __amdgpu_buffer_rsrc_t rsrc;   // raw buffer over the cache rows of sequence b
+  int nkeys, ntiles, wave, lane, hi, dh;
+  float sl2;
+  float* xs;                     // [2][4 waves][16][64] partial-score exchange
+};
+
+__device__ __forceinline__ void load_lds16(const DecodeCtx& c, uint16_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0,
+                                           0);
+}
+
+// Loads tile kt into stage st (9 loads per thread): latent instruction i of
+// wave w fills row 8w + i (lane = physical chunk); the rope instruction of wave
+// w fills rows 8w..8w+7 (8 chunks each). Rows past the last key repeat it
+// (their scores are masked).
+__device__ __forceinline__ void issue_tile(const DecodeCtx& c, uint16_t* st, int kt) {
+  const int k0 = kt * DKT;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * c.wave + i;
+    const int t = min(k0 + r, c.nkeys - 1);
+    load_lds16(c, st + r * 512, (c.lane ^ swl(r)) << 4, t * (DROW * 2));
+  }
+  const int r = 8 * c.wave + (c.lane >> 3);
+  const int t = min(k0 + r, c.nkeys - 1);
+  load_lds16(c, st + DLAT + c.wave * 512, t * (DROW * 2) + 1024 + (((c.lane & 7) ^ swr(r)) << 4), 0);
+}
+
+// Partial scores of one tile over the wave's half of the contracted dims:
+// dh = 0 takes latent chunks 0..35, dh = 1 latent chunks 36..63 and the rope
+// chunks; chunk 2kk + hi meets query fragment kk.
+template <int DH>
+__device__ __forceinline__ floatx16 partial_scores(const uint16_t* st, int srow, int hi, const bf16x8 (&qf)[18]) {
+  auto frag = [&](int kk) {
+    const int c = 36 * DH + 2 * kk;   // + hi
+    if (c < 64) {
+      const int f = swl(srow) ^ hi;
+      return *(const bf16x8*)(st + srow * 512 + ((c & ~15) << 3) + (((c & 15) ^ f) << 3));
+    }
+    return *(const bf16x8*)(st + DLAT + srow * 64 + (((c - 64) ^ (swr(srow) ^ hi)) << 3));
+  };
+  // two accumulators (even / odd k steps) so consecutive MFMAs are independent;
+  // fragments are read two steps ahead
+  floatx16 sa, sb;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    sa[r] = 0.f;
+    sb[r] = 0.f;
+  }
+  bf16x8 f0 = frag(0), f1 = frag(1), f2;
+#pragma unroll
+  for (int kk = 0; kk < 18; ++kk) {
+    if (kk + 2 < 18) f2 = frag(kk + 2);
+    if (kk & 1) sb = mfma32(f0, qf[kk], sb);
+    else sa = mfma32(f0, qf[kk], sa);
+    f0 = f1;
+    f1 = f2;
+  }
+  return sa + sb;
+}
+
+// One pass over the sequence. SCORES_ONLY: m becomes the exact per-head max.
+// Otherwise accumulates o and l against m (set at the first live tile when it
+// is -inf); returns true when a score exceeded m + LAZY (results invalid).
+template <bool SCORES_ONLY>
+__device__ __forceinline__ bool attn_pass(const DecodeCtx& c, uint16_t* st0, uint16_t* st1, uint16_t* st2,
+                                          const bf16x8 (&qf)[18], float& m, float& l, floatx16 (&o)[8]) {
+  const int lane = c.lane, l32 = lane & 31, hi = c.hi;
+  // transposed reads: 16-lane group q reads rows 16 s + 4 (q >> 1) + 8 e + (lane % 16) / 4,
+  // columns 256 dh + 32 dt + 16 (q & 1) + 4 (lane % 4)
+  const int q4 = lane >> 4, L = lane & 15;
+  const int trow = 4 * (q4 >> 1) + (L >> 2);
+  const int tx = 2 * (q4 & 1) + ((L >> 1) & 1);
+  int toff[2][4];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4) {
+      const int r = trow + 8 * e;
+      toff[e][d4] = r * 512 + 256 * c.dh + (((4 * d4 + tx) ^ swl(r)) << 3) + 4 * (L & 1);
+    }
+  bool over = false;
+  if (!SCORES_ONLY) {
+    l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  }
+  auto step = [&](int kt, const uint16_t* st, uint16_t* next) {
+    __asm__ volatile("s_waitcnt vmcnt(9)" ::: "memory");   // tile kt landed, kt + 1 may be in flight
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    issue_tile(c, next, kt + 2);   // into the stage tile kt - 1 used
+
+    floatx16 sa = c.dh ? partial_scores<1>(st, l32, hi, qf) : partial_scores<0>(st, l32, hi, qf);
+    float* xw = c.xs + (kt & 1) * (4 * 16 * 64);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xw[(c.wave * 16 + r) * 64 + lane] = sa[r];
+    // exchange barrier: LDS writes only (a __syncthreads here would also drain the tile loads)
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    const int k0 = kt * DKT;
+    float part[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[r] = xw[((c.wave ^ 2) * 16 + r) * 64 + lane];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sa[r] = (c.dh ? part[r] + sa[r] : sa[r] + part[r]) * c.sl2;   // first + second half
+    if (k0 + DKT > c.nkeys) {   // wave-uniform: the tile runs past the last key
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (k0 + row32(r, lane) >= c.nkeys) sa[r] = -INFINITY;
+    }
+    float mx = sa[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sa[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (SCORES_ONLY) {
+      m = fmaxf(m, mx);
+      return;
+    }
+    if (m == -INFINITY) m = mx;   // first live keys of this head: nothing accumulated yet
+    over |= mx > m + LAZY;
+    bf16x8 pf[2];
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(sa[r] - m);   // masked keys: exp2(-inf) = 0
+      rs += p;
+      pf[r >> 3][r & 7] = (__bf16)p;
+    }
+    l += rs;
+    // value product, step j = (key half j / 8, d tile j % 8): consecutive MFMAs
+    // update different accumulators; C^T fragments read two steps ahead
+    auto vfrag = [&](int j) {
+      const int dt = j & 7, imm = 16 * (j >> 3) * 512 + 128 * (dt >> 2);
+      const v4s lo = read_tr(st + toff[0][dt & 3] + imm), up = read_tr(st + toff[1][dt & 3] + imm);
+      return __builtin_bit_cast(bf16x8, (v8s){lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+    };
+    bf16x8 vb0 = vfrag(0), vb1 = vfrag(1), vb2;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j + 2 < 16) vb2 = vfrag(j + 2);
+      o[j & 7] = mfma32(vb0, pf[j >> 3], o[j & 7]);
+      vb0 = vb1;
+      vb1 = vb2;
+    }
+  };
+  // The loop runs whole rounds of three tiles and always keeps two tiles in
+  // flight; tiles past the end hold copies of the last key (all masked, p = 0)
+  // and cost a little math. Straight-line rounds let the compiler's own LDS
+  // waits see which stage each load targets.
+  issue_tile(c, st0, 0);
+  issue_tile(c, st1, 1);
+  for (int kt = 0; kt < c.ntiles; kt += 3) {
+    step(kt, st0, st2);
+    step(kt + 1, st1, st0);
+    step(kt + 2, st2, st1);
+  }
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();   // every wave is done with the stages and the exchange buffer
+  return over;
+}
+
+__global__ __launch_bounds__(256, 1) void decode_attn_kernel(DecodeAttnArgs a, int n_hg) {
+  __shared__ __attribute__((aligned(16))) uint16_t st0[DSTAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t st1[DSTAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t st2[DSTAGE];
+  __shared__ __attribute__((aligned(16))) float xs[2 * 4 * 16 * 64];
+  __shared__ int s_over;
+
+  const int tid = threadIdx.x;
+  const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+  const int hg = loc % n_hg, b = (loc / n_hg) * 8 + xcd;
+  if (b >= a.B) return;
+  DecodeCtx c;
+  c.lane = tid & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  c.dh = c.wave >> 1;
+  c.hi = c.lane >> 5;
+  c.xs = xs;
+  c.sl2 = a.scale * 1.4426950408889634f;
   const int P = a.cache_len[b];
-  const bool ok = P >= 0 && P < a.max_len;
-  const int nkeys = ok ? P + 1 : 0;
+  c.nkeys = (P >= 0 && P < a.max_len) ? P + 1 : 0;
+  c.ntiles = (c.nkeys + DKT - 1) / DKT;
+  c.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.cache + (int64_t)b * a.max_len * DROW),
+                                             (short)0, a.max_len * DROW * 2, BUF_DW3);
+  const int head = hg * 64 + (c.wave & 1) * 32 + (c.lane & 31);
 
+  // this wave's half of the query: B operand of the score product, dims 288 dh + 16 kk + 8 hi + 0..7
   bf16x8 qf[18];
   {
-    const uint16_t* qp = (const uint16_t*)a.qlat + ((int64_t)b * H + head) * 576 + 8 * g;
+    const uint16_t* qp = (const uint16_t*)a.qlat + ((int64_t)b * a.H + head) * DROW + 288 * c.dh + 8 * c.hi;
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + kk * 32));
+    for (int kk = 0; kk < 18; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 16 * kk));
   }
-  floatx4 o[32];
-#pragma unroll
-  for (int cb = 0; cb < 32; ++cb) o[cb] = (floatx4){0.f, 0.f, 0.f, 0.f};
+  if (tid == 0) s_over = 0;
+  floatx16 o[8];
   float m = -INFINITY, l = 0.f;
-  const float sl2 = a.scale * 1.4426950408889634f;
-  const uint16_t* C = (const uint16_t*)a.cache + (int64_t)b * a.max_len * 576;
-
-  const int kg = tid & 3, cblk = tid >> 2;   // transpose block: keys 8kg.., latent dims 8cblk..
-  const int ntiles = (nkeys + DKT - 1) / DKT;
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int k0 = kt * DKT;
-    uint4 rv[8];
+  bool over = false;
+  if (c.ntiles > 0) over = attn_pass<false>(c, st0, st1, st2, qf, m, l, o);
+  else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = k0 + kg * 8 + e;
-      rv[e] = t < nkeys ? *(const uint4*)(C + (int64_t)t * 576 + cblk * 8) : make_uint4(0, 0, 0, 0);
-    }
-    {  // rope-key part of the tile: 32 keys x 8 chunks, one chunk per thread
-      const int key = tid >> 3, part = 64 + (tid & 7), t = k0 + key;
-      const uint4 v = t < nkeys ? *(const uint4*)(C + (int64_t)t * 576 + part * 8) : make_uint4(0, 0, 0, 0);
-      *(uint4*)&sC[key * CP + part * 8] = v;
-    }
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) *(uint4*)&sC[(kg * 8 + e) * CP + cblk * 8] = rv[e];
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = ((const uint32_t*)&rv[2 * j])[d >> 1];
-        const uint32_t hi2 = ((const uint32_t*)&rv[2 * j + 1])[d >> 1];
-        w[j] = (d & 1) ? sel_hi(hi2, lo) : sel_lo(hi2, lo);
-      }
-      uint16_t* dst = &sCt[(cblk * 8 + d) * TP + kg * 8];
-      *(uint2*)dst = make_uint2(w[0], w[1]);
-      *(uint2*)(dst + 4) = make_uint2(w[2], w[3]);
-    }
-    __syncthreads();
-
-    floatx4 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = (floatx4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 18; ++kk) {
-        const bf16x8 cf = *(const bf16x8*)&sC[(kb * 16 + l16) * CP + kk * 32 + 8 * g];
-        s[kb] = mfma16(cf, qf[kk], s[kb]);
-      }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = k0 + kb * 16 + 4 * g + r;
-        const float v = t < nkeys ? s[kb][r] * sl2 : -INFINITY;
-        s[kb][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx);
-    const float muse = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = exp2f(m - muse);
-    float rs = 0.f;
-    bf16x8 pf;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = exp2f(s[e >> 2][e & 3] - muse);
-      rs += p;
-      pf[e] = (__bf16)p;
-    }
-    l = l * alpha + rs;
-    m = mnew;
-    // keys of slot e: 16*(e/4) + 4g + e%4
-#pragma unroll
-    for (int cb = 0; cb < 32; ++cb) {
-      const uint16_t* vp = &sCt[(cb * 16 + l16) * TP + 4 * g];
-      const uint2 lo = *(const uint2*)vp, hi2 = *(const uint2*)(vp + 16);
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi2.x, hi2.y));
-      o[cb] = mfma16(vf, pf, o[cb] * alpha);
-    }
+      for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
     __syncthreads();
   }
-
-  float lt = l + __shfl_xor(l, 16);
-  lt += __shfl_xor(lt, 32);
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  uint16_t* op = (uint16_t*)a.olat + ((int64_t)b * H + head) * 512 + 4 * g;
-#pragma unroll
-  for (int cb = 0; cb < 32; ++cb) {
-    const uint2 pk = make_uint2(pack_bf16x2(o[cb][0] * inv, o[cb][1] * inv),
-                                pack_bf16x2(o[cb][2] * inv, o[cb][3] * inv));
-    *(uint2*)(op + cb * 16) = pk;
+  if (over) s_over = 1;
+  __syncthreads();
+  if (s_over) {   // rare: exact maxima, then accumulate against them (no score can exceed them)
+    m = -INFINITY;
+    attn_pass<true>(c, st0, st1, st2, qf, m, l, o);
+    attn_pass<false>(c, st0, st1, st2, qf, m, l, o);
   }
+  // o_lat[b, head, 256 dh + 32 dt + 8 rg + 4 hi + 0..3]
+  l += __shfl_xor(l, 32);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint16_t* out = (uint16_t*)a.olat + ((int64_t)b * a.H + head) * 512 + 256 * c.dh + 4 * c.hi;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+      *(uint2*)(out + 32 * dt + 8 * rg) = make_uint2(pack_bf16x2(o[dt][4 * rg] * inv, o[dt][4 * rg + 1] * inv),
+                                                     pack_bf16x2(o[dt][4 * rg + 2] * inv, o[dt][4 * rg + 3] * inv));
 }
 
 }  // namespace
 
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s) {
-  dim3 grid(a.H / 64, a.B);
-  decode_attn_kernel<<<grid, 256, 0, s>>>(a);
+  const int n_hg = a.H / 64;
+  const unsigned grid = 8u * (unsigned)((a.B + 7) / 8) * (unsigned)n_hg;
+  decode_attn_kernel<<<grid, 256, 0, s>>>(a, n_hg);
   return hipGetLastError();
 }
 

@@ -200,3 +200,25 @@ def test_decode_attention_step():
         z = ql[b].astype(np.float64) @ C.T * 192.0 ** -0.5
         ref = mla.softmax_over_live(z) @ C[:, :512]
         assert_parity(got[b], ref, what=f"decode attention b={b}")
+
+
+def test_decode_attention_large_logit_jump():
+    # later keys outscore the first tile by far more than the fixed-max headroom,
+    # which sends the kernel through its exact-max recomputation
+    rng = np.random.default_rng(10)
+    B, H, max_len = 3, 64, 300
+    lens = np.array([250, 100, 299], dtype=np.int32)
+    ql = synth.round_bf16(rng.standard_normal((B, H, 576)) * 0.3)
+    cache = rng.standard_normal((B, max_len, 576))
+    cache[0, 64:] *= 40.0
+    cache[1, 40:64] *= 40.0
+    cache[2, 128:] *= 60.0
+    cache = synth.round_bf16(cache)
+    ol = torch.empty((B, H, 512), dtype=torch.bfloat16, device=DEV)
+    api.mla_decode_attention(dev(ql, torch.bfloat16), dev(cache, torch.bfloat16), dev(lens, torch.int32), ol)
+    got = ol.float().cpu().numpy()
+    for b in range(B):
+        C = cache[b, :lens[b] + 1].astype(np.float64)
+        z = ql[b].astype(np.float64) @ C.T * 192.0 ** -0.5
+        ref = mla.softmax_over_live(z) @ C[:, :512]
+        assert_parity(got[b], ref, what=f"decode attention (logit jump) b={b}")
