@@ -73,9 +73,31 @@ int check_weights(const mla_weights* w, int wdt) {
 
 struct PrefillWs {
   void *cqkv, *cqn, *kvc, *q, *kn, *vt, *kpe, *attn, *mask, *aq, *as;
+  float* part;      // split-K partials of the joint down-projection (or NULL)
+  int qkv_splits;
 };
 
 int pad64(int T) { return (T + 63) & ~63; }
+
+mla::GemmArgs gemm_args(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc, int cdt, int M,
+                        int N, int K);
+
+// Arguments of the joint down-projection [c_q | latent | k_pe] = x . [Wq_a ; Wkv_a]^T.
+mla::GemmArgs qkv_args(const mla_dims* d, int adt, const void* x, const void* wq_a, const void* wkv_a, void* out,
+                       int M) {
+  const int Dq = d->q_lora_rank, NQKV = Dq + d->kv_lora_rank + 64;
+  mla::GemmArgs g = gemm_args(x, d->dim, wq_a, d->dim, out, NQKV, adt, M, NQKV, d->dim);
+  g.W2 = wkv_a; g.ldw2 = d->dim; g.n_split = Dq;
+  return g;
+}
+
+// K chunks of the bf16 joint down-projection: its output has few 256x256
+// tiles, so it runs split-K into fp32 partials that the two norms sum.
+int prefill_qkv_splits(const mla_dims* d, int wdt, int adt, int M) {
+  if (wdt != MLA_BF16 || adt != MLA_BF16) return 1;
+  const void* aligned = (const void*)(uintptr_t)256;
+  return mla::gemm_bf16_splits(qkv_args(d, adt, aligned, aligned, aligned, nullptr, M));
+}
 
 size_t prefill_layout(const mla_dims* d, int wdt, int adt, int B, int T, int topk, bool own_kvc, void* ws,
                       PrefillWs* out) {
@@ -93,6 +115,8 @@ size_t prefill_layout(const mla_dims* d, int wdt, int adt, int B, int T, int top
   p.kpe = c.take(Mp * 64 * es);
   p.attn = c.take(M * H * 128 * es);
   p.mask = topk > 0 ? c.take((size_t)B * T * ((T + 31) / 32) * 4) : nullptr;
+  p.qkv_splits = prefill_qkv_splits(d, wdt, adt, (int)M);
+  p.part = p.qkv_splits > 1 ? (float*)c.take((size_t)p.qkv_splits * M * (Dq + L + 64) * 4) : nullptr;
   if (wdt == MLA_E4M3) {
     size_t kmax = d->dim;
     if (Dq > kmax) kmax = Dq;
@@ -239,18 +263,34 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
   const int M = B * T, NQKV = Dq + L + 64;
   void* kvc = kv_cache_out ? kv_cache_out : p.kvc;
 
-  // joint down-projection: [c_q | latent | k_pe] = x . [Wq_a ; Wkv_a]^T
-  if ((rc = project(wdt, adt, x, dim, w->wq_a, w->wq_a_scale, w->wkv_a, w->wkv_a_scale, Dq, p.cqkv, NQKV, M, NQKV,
-                    dim, &p, s)))
+  // joint down-projection: [c_q | latent | k_pe] = x . [Wq_a ; Wkv_a]^T, split-K
+  // into fp32 partials when its output has too few tiles for the chip
+  mla::GemmArgs gq = qkv_args(d, adt, x, w->wq_a, w->wkv_a, p.cqkv, M);
+  const bool qkv_split = p.qkv_splits > 1 && mla::gemm_bf16_splits(gq) == p.qkv_splits;
+  if (qkv_split) {
+    gq.k_splits = p.qkv_splits; gq.part = p.part;
+    LAUNCH(mla::launch_gemm_bf16(gq, s), "gemm_bf16(split-K q_a|kv_a)");
+  } else if ((rc = project(wdt, adt, x, dim, w->wq_a, w->wq_a_scale, w->wkv_a, w->wkv_a_scale, Dq, p.cqkv, NQKV, M,
+                           NQKV, dim, &p, s))) {
     return rc;
+  }
   const size_t es = adt == MLA_F32 ? 4 : 2;
+  // the norms read either the bf16 projection or the sum of the fp32 partials
+  const void* qkv_in = qkv_split ? (const void*)p.part : p.cqkv;
+  const size_t qkv_es = qkv_split ? 4 : es;
+  auto from_qkv = [&](mla::NormRopeArgs& a) {
+    if (!qkv_split) return;
+    a.in_dtype = MLA_F32; a.in_splits = p.qkv_splits; a.split_stride = (int64_t)M * NQKV;
+  };
   {  // q_norm
-    mla::NormRopeArgs a = norm_args(p.cqkv, NQKV, p.cqn, Dq, adt, M);
+    mla::NormRopeArgs a = norm_args(qkv_in, NQKV, p.cqn, Dq, adt, M);
+    from_qkv(a);
     a.norm_dim = Dq; a.gamma = w->q_norm_w; a.eps = d->rms_eps;
     LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(q)");
   }
   {  // kv_norm on the latent, RoPE on the shared key -> [c | k_pe]
-    mla::NormRopeArgs a = norm_args((const char*)p.cqkv + Dq * es, NQKV, kvc, L + 64, adt, M);
+    mla::NormRopeArgs a = norm_args((const char*)qkv_in + Dq * qkv_es, NQKV, kvc, L + 64, adt, M);
+    from_qkv(a);
     a.norm_dim = L; a.gamma = w->kv_norm_w; a.eps = d->rms_eps;
     a.rope_off = L; a.rope_heads = 1; a.rope_stride = 64;
     a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = rope_len; a.pos_period = T;

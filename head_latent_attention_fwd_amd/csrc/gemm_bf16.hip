@@ -162,23 +162,34 @@ hipError_t run(const GemmArgs& g, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // Large-shape kernel: 256x256 tile per workgroup, 4 waves of 128x128 (4x4
-// blocks of 32x32, accumulators in AGPRs). K moves in 64-wide steps through a
-// 2-stage LDS ring (2 x 64 KB) filled by 16-byte direct-to-LDS loads, so rows
-// are whole 128-byte lines and no registers stage the data. The operand
-// fragments of the next 16-wide MFMA step are read from LDS while the current
-// step's 16 MFMAs run; one barrier per 64-wide step, after which that step's
-// stage is refilled with the step after next. 16-byte chunks of a row are
-// XOR-swizzled by (row ^ row >> 3) & 7: conflict-free operand reads with 32 or
-// 64 LDS banks. Tiles are numbered so that each XCD (workgroup id % 8) works
-// on a contiguous, M-grouped block of the output and its L2 serves the shared
-// A/W slabs. The bf16 epilogue goes through LDS for 16-byte coalesced stores.
-constexpr int GB_BM = 256, GB_BN = 256, GB_BK = 64;
-constexpr int GB_STAGE = (GB_BM + GB_BN) * GB_BK;   // elements per stage (64 KB)
-constexpr int GB_CP = GB_BN + 8;                   // epilogue C-tile pitch (elements)
-constexpr int GB_SMEM = 2 * GB_STAGE > GB_BM * GB_CP ? 2 * GB_STAGE : GB_BM * GB_CP;
+// blocks of 32x32, accumulators in AGPRs). K moves in 32-wide steps through a
+// 4-stage LDS ring (4 x 32 KB) filled by 16-byte direct-to-LDS loads; a
+// step's loads are issued while the three steps before it are consumed, so
+// the L2/HBM latency hides behind ~3000 cycles of math. The operand fragments of the
+// next 16-wide MFMA step are read from LDS while the current step's 16 MFMAs
+// run; one barrier per 32-wide step, after which the stage just consumed is
+// refilled with the step four ahead. Rows are 64 bytes (4 chunks of 16 B),
+// XOR-swizzled by ((row >> 1) ^ (row >> 3)) & 3: conflict-free operand reads
+// with 32 or 64 LDS banks. Tiles are numbered so that each XCD (workgroup id
+// % 8) works on a contiguous, M-grouped block of the output and its L2 serves
+// the shared A/W slabs. The bf16 epilogue goes through LDS for 16-byte
+// coalesced stores.
+constexpr int GB_BM = 256, GB_BN = 256, GB_BK = 32, GB_NST = 4;
+constexpr int GB_STAGE = (GB_BM + GB_BN) * GB_BK;   // elements per stage (32 KB)
+constexpr int GB_LOADS = GB_STAGE / 8 / 256;        // 16-byte loads per thread per stage
+constexpr int GB_CP = GB_BN + 8;                    // epilogue C-tile pitch (elements)
+constexpr int GB_SMEM = GB_NST * GB_STAGE > GB_BM * GB_CP ? GB_NST * GB_STAGE : GB_BM * GB_CP;
 constexpr int GB_GROUP_M = 8;
 
-__device__ __forceinline__ int gb_sw(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int gb_sw(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+// s_waitcnt vmcnt(n * GB_LOADS): stages still allowed in flight
+__device__ __forceinline__ void gb_wait_stages(int n) {
+  if (n >= 3) __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if (n == 2) __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (n == 1) __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
 __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[GB_SMEM];
@@ -190,19 +201,23 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int t
   const int span = GB_GROUP_M * tiles_n, grp = t / span, first_m = grp * GB_GROUP_M;
   const int gsz = min(tiles_m - first_m, GB_GROUP_M), r_in = t - grp * span;
   const int m0 = (first_m + r_in % gsz) * GB_BM, n0 = (r_in / gsz) * GB_BN;
-  const int M = g.M, N = g.N, K = g.K, z = blockIdx.y;
-  const uint16_t* A = (const uint16_t*)g.A + (int64_t)z * g.batch_a;
-  const uint16_t* W = (const uint16_t*)g.W + (int64_t)z * g.batch_w;
-  const uint16_t* W2 = (const uint16_t*)g.W2;
+  const int M = g.M, N = g.N, K = g.K;
+  const int split = g.k_splits > 1 ? (int)blockIdx.y : 0, z = g.k_splits > 1 ? 0 : (int)blockIdx.y;
+  // K chunk of this workgroup (whole K without split-K)
+  const int ksteps = K / GB_BK, per = (ksteps + max(g.k_splits, 1) - 1) / max(g.k_splits, 1);
+  const int kbeg = split * per * GB_BK;
+  const uint16_t* A = (const uint16_t*)g.A + (int64_t)z * g.batch_a + kbeg;
+  const uint16_t* W = (const uint16_t*)g.W + (int64_t)z * g.batch_w + kbeg;
+  const uint16_t* W2 = g.W2 ? (const uint16_t*)g.W2 + kbeg : nullptr;
 
-  // Direct-load slots: a stage holds A rows 0..255 then W rows 0..255, 8
-  // chunks per row (4096 slots); wave w fills 1 KB blocks 16w..16w+15.
-  const uint16_t* src[16];
+  // Direct-load slots: a stage holds A rows 0..255 then W rows 0..255, 4
+  // chunks per row (2048 slots); wave w fills 1 KB blocks 8w..8w+7.
+  const uint16_t* src[GB_LOADS];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int p = (wave * 16 + i) * 64 + lane;
-    const int q = p & 2047, r = q >> 3, c = (q & 7) ^ gb_sw(r);
-    if (p < 2048) {
+  for (int i = 0; i < GB_LOADS; ++i) {
+    const int p = (wave * GB_LOADS + i) * 64 + lane;
+    const int q = p & 1023, r = q >> 2, c = (q & 3) ^ gb_sw(r);
+    if (p < 1024) {
       const int m = min(m0 + r, M - 1);
       src[i] = A + (int64_t)m * g.lda + c * 8;
     } else {
@@ -211,9 +226,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int t
     }
   }
   auto issue = [&](int kt) {
-    uint16_t* st = smem + (kt & 1) * GB_STAGE + wave * 16 * 512;
+    uint16_t* st = smem + (kt % GB_NST) * GB_STAGE + wave * GB_LOADS * 512;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) __builtin_amdgcn_global_load_lds(src[i] + kt * GB_BK, st + i * 512, 16, 0, 0);
+    for (int i = 0; i < GB_LOADS; ++i)
+      __builtin_amdgcn_global_load_lds(src[i] + kt * GB_BK, st + i * 512, 16, 0, 0);
   };
 
   floatx16 acc[4][4];
@@ -224,60 +240,122 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int t
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // swizzled chunk offsets of this lane's rows: the row of fragment i is
-  // 128 w + 32 i + l32, whose swizzle depends on l32 and on the parity of i
-  int xo[2][4];
+  // swizzled chunk offset of this lane's rows (the swizzle depends on l32 only)
+  int xo[2];
 #pragma unroll
-  for (int par = 0; par < 2; ++par)
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) xo[par][kk] = ((2 * kk + hi) ^ gb_sw(32 * par + l32)) << 3;
+  for (int kk = 0; kk < 2; ++kk) xo[kk] = ((2 * kk + hi) ^ gb_sw(l32)) << 3;
   bf16x8 fa[2][4], fb[2][4];   // fragments of one 16-wide step, double-buffered
   auto read = [&](int kt, int kk, int buf) {
-    const uint16_t* st = smem + (kt & 1) * GB_STAGE;
+    const uint16_t* st = smem + (kt % GB_NST) * GB_STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      fa[buf][i] = *(const bf16x8*)(st + (wm * 128 + i * 32 + l32) * GB_BK + xo[i & 1][kk]);
+    for (int i = 0; i < 4; ++i) fa[buf][i] = *(const bf16x8*)(st + (wm * 128 + i * 32 + l32) * GB_BK + xo[kk]);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      fb[buf][j] = *(const bf16x8*)(st + GB_BM * GB_BK + (wn * 128 + j * 32 + l32) * GB_BK + xo[j & 1][kk]);
+      fb[buf][j] = *(const bf16x8*)(st + GB_BM * GB_BK + (wn * 128 + j * 32 + l32) * GB_BK + xo[kk]);
   };
 
-  const int nk = K / GB_BK;
-  issue(0);
-  if (nk > 1) {
-    issue(1);
-    __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  } else {
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
+  const int nk = min(per, ksteps - split * per);
+  for (int s = 0; s < GB_NST; ++s)
+    if (s < nk) issue(s);
+  gb_wait_stages(min(nk, GB_NST) - 1);   // step 0 has landed
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
   read(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  // operands swapped (W first): a lane's accumulator holds one row of C and
+  // 4 consecutive columns per group of 4 results
+  auto mma = [&](int buf) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int cb = kk & 1;
-      if (kk < 3) {
-        read(kt, kk + 1, cb ^ 1);
-      } else if (kt + 1 < nk) {
-        // every wave holds step kt in registers and step kt+1 has landed: a
-        // bare barrier (no fence, so nothing else is waited for), then stage
-        // kt & 1 takes step kt+2
-        __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        __asm__ volatile("" ::: "memory");
-        if (kt + 2 < nk) issue(kt + 2);
-        read(kt + 1, 0, cb ^ 1);
-      }
-      // operands swapped (W first): a lane's accumulator holds one row of C
-      // and 4 consecutive columns per group of 4 results
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fb[buf][j], fa[buf][i], acc[i][j]);
+  };
+  // Step kt: the second half of its fragments is read during the first
+  // half's MFMAs; then every wave holds step kt in registers and step kt+1
+  // has landed (kt+2, kt+3 may be in flight), so after a bare barrier the
+  // stage of step kt takes step kt+4. The steady-state loop has no branch
+  // inside, which keeps the compiler's own LDS waits tight.
+  // sched_barrier(0) keeps the compiler from moving the reads behind the MFMAs
+  // they are meant to overlap.
+  int kt = 0;
+  for (; kt + GB_NST < nk; ++kt) {
+    // the first-half fragments were read a whole MFMA group ago: a builtin
+    // lgkmcnt(0) here costs nothing and tells the compiler they are in
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_sched_barrier(0);
+    read(kt, 1, 1);
+    mma(0);
+    // one LDS read between every two MFMAs
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fb[cb][j], fa[cb][i], acc[i][j]);
+    for (int u = 0; u < 8; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // s_waitcnt vmcnt(16) lgkmcnt(0) as a builtin, so the compiler's own wait
+    // accounting knows the reads of this step are complete
+    __builtin_amdgcn_s_waitcnt(0x4070);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kt + GB_NST);
+    read(kt + 1, 0, 0);
+    mma(1);
+    // MFMAs interleaved with the refill loads and the next step's LDS reads
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (; kt < nk; ++kt) {   // the last steps: nothing left to issue
+    read(kt, 1, 1);
+    mma(0);
+    if (kt + 1 < nk) {
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      gb_wait_stages(min(nk - 2 - kt, GB_NST - 2));
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+      read(kt + 1, 0, 0);
+    }
+    mma(1);
   }
 
+  if (g.k_splits > 1) {
+    // fp32 partial sums through LDS, one 128-row half of the tile at a time
+    // (the waves with wm == half stage it), then 64 lanes per row store 1 KB
+    constexpr int FP = GB_BN + 4;   // fp32 pitch
+    float* P = g.part + (int64_t)split * M * N;
+    float* sf = (float*)smem;
+    for (int half = 0; half < 2; ++half) {
+      __syncthreads();   // the ring (or the previous half) is no longer read
+      if (wm == half) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg)
+              *(float4*)&sf[(i * 32 + l32) * FP + wn * 128 + j * 32 + 8 * rg + 4 * hi] =
+                  make_float4(acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]);
+      }
+      __syncthreads();
+      for (int c = tid; c < 128 * (GB_BN / 4); c += 256) {
+        const int row = c >> 6, ch = (c & 63) * 4, m = m0 + half * 128 + row, n = n0 + ch;
+        if (m >= M || n >= N) continue;
+        const float4 v = *(const float4*)&sf[row * FP + ch];
+        float* p = P + (int64_t)m * N + n;
+        if (n + 4 <= N) {
+          *(float4*)p = v;
+        } else {
+          const float e[4] = {v.x, v.y, v.z, v.w};
+          for (int k = 0; n + k < N; ++k) p[k] = e[k];
+        }
+      }
+    }
+    return;
+  }
   // Epilogue through LDS: the bf16 C tile is staged row-major (8-byte writes
   // of 4 consecutive columns), then stored in 16-byte pieces (row-major C or
   // the k_nope part of the KV split), or as 2-byte stores running along t
@@ -296,24 +374,39 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int t
       }
   __syncthreads();
   uint16_t* C = (uint16_t*)g.C + (int64_t)z * g.batch_c;
+  if (g.epi == EPI_KV_SPLIT) {
+    // the tile is one head (N % 256 == 0): columns 0..127 are k_nope, stored
+    // along the row (16 lanes per row); columns 128..255 are v, stored
+    // transposed with lanes running along t so each column's writes coalesce
+    const int h = n0 >> 8;
+    for (int c = tid; c < GB_BM * 16; c += 256) {
+      const int row = c >> 4, ch = (c & 15) * 8, m = m0 + row;
+      if (m >= M) continue;
+      const int bb = m / g.kv.T, tt = m - bb * g.kv.T;
+      const int64_t bh = (int64_t)bb * g.kv.H + h;
+      *(uint4*)(C + (bh * g.kv.Tp + tt) * 128 + ch) = *(const uint4*)&smem[row * GB_CP + ch];
+    }
+    for (int c = tid; c < GB_BM * 16; c += 256) {
+      const int row = c & (GB_BM - 1), ch = (c >> 8) * 8, m = m0 + row;
+      if (m >= M) continue;
+      const uint4 v = *(const uint4*)&smem[row * GB_CP + 128 + ch];
+      const uint16_t* e = (const uint16_t*)&v;
+      const int bb = m / g.kv.T, tt = m - bb * g.kv.T;
+      uint16_t* vt = (uint16_t*)g.kv.vt + (((int64_t)bb * g.kv.H + h) * 128 + ch) * g.kv.Tp + tt;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) vt[(int64_t)k * g.kv.Tp] = e[k];
+    }
+    return;
+  }
+  // row-major C: 32 lanes per row, 16-byte stores along the row
   for (int c = tid; c < GB_BM * (GB_BN / 8); c += 256) {
-    const int row = c & (GB_BM - 1), ch = (c >> 8) * 8, m = m0 + row, n = n0 + ch;
+    const int row = c >> 5, ch = (c & 31) * 8, m = m0 + row, n = n0 + ch;
     if (m >= M || n >= N) continue;
     const uint4 v = *(const uint4*)&smem[row * GB_CP + ch];
-    const uint16_t* e = (const uint16_t*)&v;
-    if (g.epi == EPI_KV_SPLIT) {
-      const int bb = m / g.kv.T, tt = m - bb * g.kv.T, h = n >> 8, jj = n & 255;
-      const int64_t bh = (int64_t)bb * g.kv.H + h;
-      if (jj < 128) {
-        *(uint4*)(C + (bh * g.kv.Tp + tt) * 128 + jj) = v;
-      } else {
-        uint16_t* vt = (uint16_t*)g.kv.vt + (bh * 128 + (jj - 128)) * g.kv.Tp + tt;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) vt[(int64_t)k * g.kv.Tp] = e[k];
-      }
-    } else if (n + 8 <= N) {
+    if (n + 8 <= N) {
       *(uint4*)(C + (int64_t)m * g.ldc + n) = v;
     } else {
+      const uint16_t* e = (const uint16_t*)&v;
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         if (n + k < N) C[(int64_t)m * g.ldc + n + k] = e[k];
@@ -323,17 +416,39 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int t
 
 }  // namespace
 
+namespace {
+// operand shapes the big-tile kernel takes
+bool big_ok(const GemmArgs& g) {
+  return !g.w_kn && g.M >= 256 && g.N >= 256 && g.K % GB_BK == 0 && (g.lda & 7) == 0 && (g.ldw & 7) == 0 &&
+         (g.n_split >= g.N || (g.ldw2 & 7) == 0) && (((uintptr_t)g.A | (uintptr_t)g.W | (uintptr_t)g.W2) & 15) == 0;
+}
+}  // namespace
+
+int gemm_bf16_splits(const GemmArgs& g) {
+  if (!big_ok(g) || g.batch != 1 || (g.N & 3) != 0) return 1;
+  const int tiles = ((g.M + GB_BM - 1) / GB_BM) * ((g.N + GB_BN - 1) / GB_BN);
+  if (tiles >= 128) return 1;
+  int splits = 256 / tiles;
+  const int ksteps = g.K / GB_BK;
+  if (splits > ksteps / 16) splits = ksteps / 16;   // at least 16 steps of 32 per chunk
+  if (splits < 2) return 1;
+  const int per = (ksteps + splits - 1) / splits;
+  return (ksteps + per - 1) / per;   // chunks actually made
+}
+
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
   if (g.w_kn) return run<128, 128, 2, 2, true>(g, s);
+  const int tm = (g.M + GB_BM - 1) / GB_BM, tn = (g.N + GB_BN - 1) / GB_BN;
+  const int per_xcd = (tm * tn + 7) / 8;
+  if (g.k_splits > 1) {   // the caller sized part[] from gemm_bf16_splits
+    if (!big_ok(g) || g.batch != 1 || !g.part || g.k_splits != gemm_bf16_splits(g)) return hipErrorInvalidValue;
+    gemm_bf16_big_kernel<<<dim3(8 * per_xcd, g.k_splits), 256, 0, s>>>(g, tm, tn, per_xcd);
+    return hipGetLastError();
+  }
   // bf16 output, 16-byte aligned rows (the KV split needs N % 256 == 0, true for H*256)
   const bool c_ok = g.c_dtype == DT_BF16 && (((uintptr_t)g.C) & 15) == 0 &&
                     (g.epi == EPI_KV_SPLIT ? (g.N & 255) == 0 : ((g.ldc & 7) == 0 && (g.batch_c & 7) == 0));
-  const bool big = c_ok && g.M >= 256 && g.N >= 256 && g.K % GB_BK == 0 && (g.lda & 7) == 0 && (g.ldw & 7) == 0 &&
-                   (g.n_split >= g.N || (g.ldw2 & 7) == 0) &&
-                   (((uintptr_t)g.A | (uintptr_t)g.W | (uintptr_t)g.W2) & 15) == 0;
-  if (big) {
-    const int tm = (g.M + GB_BM - 1) / GB_BM, tn = (g.N + GB_BN - 1) / GB_BN;
-    const int per_xcd = (tm * tn + 7) / 8;
+  if (c_ok && big_ok(g)) {
     gemm_bf16_big_kernel<<<dim3(8 * per_xcd, g.batch), 256, 0, s>>>(g, tm, tn, per_xcd);
     return hipGetLastError();
   }

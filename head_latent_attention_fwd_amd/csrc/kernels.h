@@ -26,6 +26,9 @@ struct GemmArgs {
   int M, N, K, batch;
   bool w_kn;
   int epi; KvSplit kv;
+  // split-K (batch == 1, big-tile path only): part[s][M][N] fp32 partial sums
+  // of K chunk s; C is not written
+  int k_splits; float* part;
 };
 
 // Store of one output element for the EPI_KV_SPLIT layout (m = b*T + t, n = h*256 + j).
@@ -37,6 +40,9 @@ __device__ __forceinline__ void kv_split_store(const KvSplit& s, T_* kn, T_* vt,
   else vt[(bh * 128 + (j - 128)) * s.Tp + t] = v;
 }
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
+// Number of K chunks the big-tile path would use for this shape (1 = no split;
+// a split is worth it when the output has too few 256x256 tiles to fill the chip).
+int gemm_bf16_splits(const GemmArgs& g);
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s);
 
 // Block-scaled e4m3 GEMM. W2/w2_scale as in GemmArgs (n_split multiple of 128).
