@@ -38,6 +38,7 @@ constexpr int BKV = 64;                   // keys per tile
 constexpr int ST_KN = 0, ST_KPE = 64 * 128, ST_VT = ST_KPE + 64 * 64, STAGE = ST_VT + 128 * 64;
 constexpr int LOADS = STAGE * 2 / 16 / 256;  // 16-byte direct loads per thread per tile (10)
 constexpr float LAZY = 8.0f;
+constexpr int BUF_DW3 = 0x00020000;       // gfx9 raw-buffer descriptor word 3
 
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 // chunk swizzle of 128-byte rows, conflict-free for 32 or 64 LDS banks
@@ -66,32 +67,40 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
     }
   }
 
-  // Direct-load slots: wave w fills 1 KB blocks LOADS*w .. LOADS*w + LOADS-1 of a
-  // stage; lane l of block i lands in 16-byte slot p = 64 i + l.
-  const uint16_t* src[LOADS];
-  int adv[LOADS];
+  // Direct-load slots: load i of wave w fills 1 KB block 4i + w of a stage;
+  // lane l lands in 16-byte slot p = 64 (4i + w) + l. Blocks 0..15 are k_nope,
+  // 16..23 k_pe and 24..39 v^T, so the region of load i is fixed by i and each
+  // load reads one raw buffer: a per-lane byte offset within the tile (fixed
+  // over tiles) plus a scalar tile offset.
+  const __amdgpu_buffer_rsrc_t rs_kn = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint16_t*)a.kn + bh * Tp * 128), (short)0, Tp * 128 * 2, BUF_DW3);
+  const __amdgpu_buffer_rsrc_t rs_kpe = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint16_t*)a.kpe + (int64_t)b * Tp * 64), (short)0, Tp * 64 * 2, BUF_DW3);
+  const __amdgpu_buffer_rsrc_t rs_vt = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint16_t*)a.vt + bh * 128 * Tp), (short)0, 128 * Tp * 2, BUF_DW3);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  int voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int p = (wave * LOADS + i) * 64 + lane;
-    if (p < ST_KPE / 8) {                       // k_nope: row rho, chunk' = chunk ^ (rho & 15)
+    const int p = (4 * i + wv) * 64 + lane;
+    if (i < 4) {                                // k_nope: row rho, chunk' = chunk ^ (rho & 15)
       const int rho = p >> 4, c = (p & 15) ^ (rho & 15);
-      src[i] = (const uint16_t*)a.kn + (bh * Tp + swap23(rho)) * 128 + c * 8;
-      adv[i] = BKV * 128;
-    } else if (p < ST_VT / 8) {                 // k_pe
+      voff[i] = (swap23(rho) * 128 + c * 8) * 2;
+    } else if (i < 6) {                         // k_pe
       const int q = p - ST_KPE / 8, rho = q >> 3, c = (q & 7) ^ sw8(rho);
-      src[i] = (const uint16_t*)a.kpe + ((int64_t)b * Tp + swap23(rho)) * 64 + c * 8;
-      adv[i] = BKV * 64;
+      voff[i] = (swap23(rho) * 64 + c * 8) * 2;
     } else {                                    // v^T: row dv, 8-key chunk
       const int q = p - ST_VT / 8, dv = q >> 3, c = (q & 7) ^ sw8(dv);
-      src[i] = (const uint16_t*)a.vt + (bh * 128 + dv) * Tp + c * 8;
-      adv[i] = BKV;
+      voff[i] = (dv * Tp + c * 8) * 2;
     }
   }
-  auto issue = [&](int stage) {
+  auto issue = [&](int stage, int k0) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      __builtin_amdgcn_global_load_lds(src[i], smem + stage * STAGE + (wave * LOADS + i) * 512, 16, 0, 0);
-      src[i] += adv[i];
+      auto* lds = (__attribute__((address_space(3))) void*)(smem + stage * STAGE + (4 * i + wv) * 512);
+      if (i < 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kn, lds, 16, voff[i], k0 * 256, 0, 0);
+      else if (i < 6) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kpe, lds, 16, voff[i], k0 * 128, 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_vt, lds, 16, voff[i], k0 * 2, 0, 0);
     }
   };
 
@@ -117,32 +126,46 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
 
   const int kv_end = min(T, q0 + BQ);
   const int ntiles = (kv_end + BKV - 1) / BKV;
-  issue(0);
+  // mask words of a tile (two 32-key words per query row), fetched one tile
+  // ahead and before the tile refill so that waiting for them never waits for it
+  auto mask_words = [&](int kt, uint32_t& w0, uint32_t& w1) {
+    w0 = w1 = 0xFFFFFFFFu;
+    if (mrow && kt < ntiles) {
+      const int wi = (kt * BKV) >> 5;
+      w0 = mrow[wi];
+      w1 = wi + 1 < W ? mrow[wi + 1] : 0u;
+    }
+  };
+  uint32_t nw0, nw1;
+  mask_words(0, nw0, nw1);
+  issue(0, 0);
   for (int kt = 0; kt < ntiles; ++kt) {
     const int cur = kt & 1, k0 = kt * BKV;
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kt + 1 < ntiles) issue(cur ^ 1);
+    const uint32_t mw0 = nw0, mw1 = nw1;
+    mask_words(kt + 1, nw0, nw1);
+    if (kt + 1 < ntiles) issue(cur ^ 1, k0 + BKV);
     if (k0 > qw + 31) continue;                  // every key of the tile is after this wave's queries
     const uint16_t* sb = smem + cur * STAGE;
-    uint32_t mw0 = 0xFFFFFFFFu, mw1 = 0xFFFFFFFFu;
-    if (mrow) {
-      mw0 = mrow[k0 >> 5];
-      mw1 = ((k0 >> 5) + 1 < W) ? mrow[(k0 >> 5) + 1] : 0u;
-    }
     floatx16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    // step u = (kk, kb) = (u / 2, u % 2); K fragments read two steps ahead
+    auto kfrag = [&](int u) {
+      const int kk = u >> 1, kb = u & 1, rho = kb * 32 + l32;
+      const int off = kk < 8 ? ST_KN + rho * 128 + xk[kk] : ST_KPE + rho * 64 + xp[kb][kk - 8];
+      return *(const bf16x8*)(sb + off);
+    };
+    bf16x8 kf0 = kfrag(0), kf1 = kfrag(1), kf2;
 #pragma unroll
-    for (int kk = 0; kk < 12; ++kk) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int rho = kb * 32 + l32;
-        const int off = kk < 8 ? ST_KN + rho * 128 + xk[kk] : ST_KPE + rho * 64 + xp[kb][kk - 8];
-        s[kb] = mfma32(*(const bf16x8*)(sb + off), qf[kk], s[kb]);
-      }
+    for (int u = 0; u < 24; ++u) {
+      if (u + 2 < 24) kf2 = kfrag(u + 2);
+      s[u & 1] = mfma32(kf0, qf[u >> 1], s[u & 1]);
+      kf0 = kf1;
+      kf1 = kf2;
     }
     // s[kb][r] holds key k0 + 32kb + 16(r/8) + 8hi + r%8
     const bool interior = !mrow && (k0 + BKV - 1 <= qw) && (k0 + BKV <= T);
@@ -189,15 +212,20 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
           pf[kb * 2 + half][e] = (__bf16)p;
         }
     // O^T += V^T . P^T; step ks covers keys 32(ks/2) + 16(ks%2) + 8hi + 0..7
+    // step u = (ks, j) = (u / 4, u % 4); V^T fragments read two steps ahead
+    auto vfrag = [&](int u) {
+      const int ks = u >> 2, dv = (u & 3) * 32 + l32;
+      const int c = (4 * (ks >> 1) + 2 * (ks & 1) + hi) ^ sw8(dv);
+      return *(const bf16x8*)(sb + ST_VT + dv * 64 + (c << 3));
+    };
+    bf16x8 vf0 = vfrag(0), vf1 = vfrag(1), vf2;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int dv = j * 32 + l32;
-        const int c = (4 * (ks >> 1) + 2 * (ks & 1) + hi) ^ sw8(dv);
-        const bf16x8 vf = *(const bf16x8*)(sb + ST_VT + dv * 64 + (c << 3));
-        o[j] = mfma32(vf, pf[ks], o[j]);
-      }
+    for (int u = 0; u < 16; ++u) {
+      if (u + 2 < 16) vf2 = vfrag(u + 2);
+      o[u & 3] = mfma32(vf0, pf[u >> 2], o[u & 3]);
+      vf0 = vf1;
+      vf1 = vf2;
+    }
   }
 
   const float lt = l + __shfl_xor(l, 32);

@@ -161,46 +161,71 @@ hipError_t run(const GemmArgs& g, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Large-shape kernel: 256x256 tile per workgroup, 4 waves of 128x128 (4x4
-// blocks of 32x32, accumulators in AGPRs). K moves in 32-wide steps through a
-// 4-stage LDS ring (4 x 32 KB) filled by 16-byte direct-to-LDS loads; a
-// step's loads are issued while the three steps before it are consumed, so
-// the L2/HBM latency hides behind ~3000 cycles of math. The operand fragments of the
-// next 16-wide MFMA step are read from LDS while the current step's 16 MFMAs
-// run; one barrier per 32-wide step, after which the stage just consumed is
-// refilled with the step four ahead. Rows are 64 bytes (4 chunks of 16 B),
-// XOR-swizzled by ((row >> 1) ^ (row >> 3)) & 3: conflict-free operand reads
-// with 32 or 64 LDS banks. Tiles are numbered so that each XCD (workgroup id
-// % 8) works on a contiguous, M-grouped block of the output and its L2 serves
-// the shared A/W slabs. The bf16 epilogue goes through LDS for 16-byte
-// coalesced stores.
-constexpr int GB_BM = 256, GB_BN = 256, GB_BK = 32, GB_NST = 4;
-constexpr int GB_STAGE = (GB_BM + GB_BN) * GB_BK;   // elements per stage (32 KB)
-constexpr int GB_LOADS = GB_STAGE / 8 / 256;        // 16-byte loads per thread per stage
-constexpr int GB_CP = GB_BN + 8;                    // epilogue C-tile pitch (elements)
-constexpr int GB_SMEM = GB_NST * GB_STAGE > GB_BM * GB_CP ? GB_NST * GB_STAGE : GB_BM * GB_CP;
-constexpr int GB_GROUP_M = 8;
+// Large-shape kernel: a BM x BN tile per 256-thread workgroup (BM = 32 WM FM,
+// BN = 32 WN FN; WM x WN waves, each FM x FN blocks of 32x32 with accumulators
+// in AGPRs). Shapes: 256x256 (2x2 waves of 4x4), 256x192 (2x2 of 4x3) and
+// 256x224 (4x1 of 2x7); the narrower tiles make the tile count a multiple of
+// the 256 CUs for N = 12288 and N = 7168. K moves in 32-wide steps through a
+// 4-stage LDS ring filled by 16-byte direct-to-LDS loads; a step's loads are
+// issued while the three steps before it are consumed, so the L2/HBM latency
+// hides behind ~3000 cycles of math. A stage holds BM rows of A and BNL >= BN
+// rows of W (rounded up so every thread issues the same number of loads; the
+// extra rows are loaded and ignored). The operand fragments of the next
+// 16-wide step are read from LDS between the current step's MFMAs; one
+// barrier per 32-wide step, after which the stage just consumed takes the step
+// four ahead. Rows are 64 bytes (4 chunks of 16 B), XOR-swizzled by
+// ((row >> 1) ^ (row >> 3)) & 3: conflict-free operand reads with 32 or 64
+// LDS banks. Tiles are numbered so that each XCD (workgroup id % 8) works on a
+// contiguous, M-grouped block of the output and its L2 serves the shared A/W
+// slabs. Output: bf16 through LDS with 16-byte coalesced stores (row-major or
+// the k_nope / v^T split of kv_b), or fp32 split-K partials.
+constexpr int GB_BK = 32, GB_NST = 4, GB_GROUP_M = 8;
+constexpr int GB_SMEM = 256 * (256 + 8);   // elements: the largest of ring and epilogue tile
 
 __device__ __forceinline__ int gb_sw(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
-// s_waitcnt vmcnt(n * GB_LOADS): stages still allowed in flight
+// s_waitcnt vmcnt(n * LOADS): stages still allowed in flight
+template <int LOADS>
 __device__ __forceinline__ void gb_wait_stages(int n) {
-  if (n >= 3) __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
-  else if (n == 2) __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (n == 1) __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  static_assert(LOADS == 7 || LOADS == 8, "wait counts below assume 7 or 8 loads per stage");
+  if (LOADS == 8) {
+    if (n >= 3) __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    else if (n == 2) __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (n == 1) __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (n >= 3) __asm__ volatile("s_waitcnt vmcnt(21)" ::: "memory");
+    else if (n == 2) __asm__ volatile("s_waitcnt vmcnt(14)" ::: "memory");
+    else if (n == 1) __asm__ volatile("s_waitcnt vmcnt(7)" ::: "memory");
+    else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
 }
 
-__global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
+template <int WM, int WN, int FM, int FN>
+struct BigTile {
+  static constexpr int BM = 32 * WM * FM, BN = 32 * WN * FN;
+  static constexpr int BNL = ((BM + BN + 63) / 64) * 64 - BM;   // W rows loaded per stage
+  static constexpr int ROWS = BM + BNL;
+  static constexpr int STAGE = ROWS * GB_BK;                      // elements
+  static constexpr int LOADS = ROWS * 4 / 256;                    // 16-byte loads per thread per stage
+  static constexpr int CP = BN + 8;                               // epilogue C-tile pitch (elements)
+  static_assert(WM * WN == 4 && BM == 256, "four waves over 256 rows");
+  static_assert(GB_NST * STAGE <= GB_SMEM && BM * CP <= GB_SMEM, "LDS budget");
+};
+
+template <int WM, int WN, int FM, int FN>
+__device__ __forceinline__ void gemm_bf16_big(const GemmArgs& g, int tiles_m, int tiles_n, int per_xcd) {
+  using TL = BigTile<WM, WN, FM, FN>;
+  constexpr int BM = TL::BM, BN = TL::BN, LOADS = TL::LOADS, STAGE = TL::STAGE, CP = TL::CP;
   __shared__ __attribute__((aligned(16))) uint16_t smem[GB_SMEM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, hi = lane >> 5;
+  const int wm = wave / WN, wn = wave % WN, l32 = lane & 31, hi = lane >> 5;
   const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
   const int t = xcd * per_xcd + loc, ntile = tiles_m * tiles_n;
   if (loc >= per_xcd || t >= ntile) return;
   const int span = GB_GROUP_M * tiles_n, grp = t / span, first_m = grp * GB_GROUP_M;
   const int gsz = min(tiles_m - first_m, GB_GROUP_M), r_in = t - grp * span;
-  const int m0 = (first_m + r_in % gsz) * GB_BM, n0 = (r_in / gsz) * GB_BN;
+  const int m0 = (first_m + r_in % gsz) * BM, n0 = (r_in / gsz) * BN;
   const int M = g.M, N = g.N, K = g.K;
   const int split = g.k_splits > 1 ? (int)blockIdx.y : 0, z = g.k_splits > 1 ? 0 : (int)blockIdx.y;
   // K chunk of this workgroup (whole K without split-K)
@@ -210,33 +235,34 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int t
   const uint16_t* W = (const uint16_t*)g.W + (int64_t)z * g.batch_w + kbeg;
   const uint16_t* W2 = g.W2 ? (const uint16_t*)g.W2 + kbeg : nullptr;
 
-  // Direct-load slots: a stage holds A rows 0..255 then W rows 0..255, 4
-  // chunks per row (2048 slots); wave w fills 1 KB blocks 8w..8w+7.
-  const uint16_t* src[GB_LOADS];
+  // Direct-load slots: a stage holds A rows 0..BM-1 then W rows 0..BNL-1, 4
+  // chunks per row; wave w fills 1 KB blocks LOADS w .. LOADS w + LOADS - 1.
+  const uint16_t* src[LOADS];
 #pragma unroll
-  for (int i = 0; i < GB_LOADS; ++i) {
-    const int p = (wave * GB_LOADS + i) * 64 + lane;
-    const int q = p & 1023, r = q >> 2, c = (q & 3) ^ gb_sw(r);
-    if (p < 1024) {
-      const int m = min(m0 + r, M - 1);
-      src[i] = A + (int64_t)m * g.lda + c * 8;
+  for (int i = 0; i < LOADS; ++i) {
+    const int p = (wave * LOADS + i) * 64 + lane;
+    const int r = p >> 2;
+    if (r < BM) {
+      const int c = (p & 3) ^ gb_sw(r);
+      src[i] = A + (int64_t)min(m0 + r, M - 1) * g.lda + c * 8;
     } else {
-      const int n = min(n0 + r, N - 1);
+      const int rw = r - BM, c = (p & 3) ^ gb_sw(rw);
+      const int n = min(n0 + rw, N - 1);
       src[i] = (n < g.n_split ? W + (int64_t)n * g.ldw : W2 + (int64_t)(n - g.n_split) * g.ldw2) + c * 8;
     }
   }
   auto issue = [&](int kt) {
-    uint16_t* st = smem + (kt % GB_NST) * GB_STAGE + wave * GB_LOADS * 512;
+    uint16_t* st = smem + (kt % GB_NST) * STAGE + wave * LOADS * 512;
 #pragma unroll
-    for (int i = 0; i < GB_LOADS; ++i)
+    for (int i = 0; i < LOADS; ++i)
       __builtin_amdgcn_global_load_lds(src[i] + kt * GB_BK, st + i * 512, 16, 0, 0);
   };
 
-  floatx16 acc[4][4];
+  floatx16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -244,38 +270,39 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int t
   int xo[2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) xo[kk] = ((2 * kk + hi) ^ gb_sw(l32)) << 3;
-  bf16x8 fa[2][4], fb[2][4];   // fragments of one 16-wide step, double-buffered
+  bf16x8 fa[2][FM], fb[2][FN];   // fragments of one 16-wide step, double-buffered
   auto read = [&](int kt, int kk, int buf) {
-    const uint16_t* st = smem + (kt % GB_NST) * GB_STAGE;
+    const uint16_t* st = smem + (kt % GB_NST) * STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[buf][i] = *(const bf16x8*)(st + (wm * 128 + i * 32 + l32) * GB_BK + xo[kk]);
+    for (int i = 0; i < FM; ++i)
+      fa[buf][i] = *(const bf16x8*)(st + (wm * FM * 32 + i * 32 + l32) * GB_BK + xo[kk]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      fb[buf][j] = *(const bf16x8*)(st + GB_BM * GB_BK + (wn * 128 + j * 32 + l32) * GB_BK + xo[kk]);
+    for (int j = 0; j < FN; ++j)
+      fb[buf][j] = *(const bf16x8*)(st + (BM + wn * FN * 32 + j * 32 + l32) * GB_BK + xo[kk]);
+  };
+  // operands swapped (W first): a lane's accumulator holds one row of C and
+  // 4 consecutive columns per group of 4 results
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(fb[buf][j], fa[buf][i], acc[i][j]);
   };
 
   const int nk = min(per, ksteps - split * per);
   for (int s = 0; s < GB_NST; ++s)
     if (s < nk) issue(s);
-  gb_wait_stages(min(nk, GB_NST) - 1);   // step 0 has landed
+  gb_wait_stages<LOADS>(min(nk, GB_NST) - 1);   // step 0 has landed
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
   read(0, 0, 0);
-  // operands swapped (W first): a lane's accumulator holds one row of C and
-  // 4 consecutive columns per group of 4 results
-  auto mma = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fb[buf][j], fa[buf][i], acc[i][j]);
-  };
   // Step kt: the second half of its fragments is read during the first
   // half's MFMAs; then every wave holds step kt in registers and step kt+1
   // has landed (kt+2, kt+3 may be in flight), so after a bare barrier the
   // stage of step kt takes step kt+4. The steady-state loop has no branch
-  // inside, which keeps the compiler's own LDS waits tight.
-  // sched_barrier(0) keeps the compiler from moving the reads behind the MFMAs
-  // they are meant to overlap.
+  // inside, which keeps the compiler's own LDS waits tight, and
+  // sched_group_barrier spreads the LDS reads and refill loads between MFMAs.
+  constexpr int NF = FM + FN, NMMA = FM * FN;
   int kt = 0;
   for (; kt + GB_NST < nk; ++kt) {
     // the first-half fragments were read a whole MFMA group ago: a builtin
@@ -284,25 +311,24 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int t
     __builtin_amdgcn_sched_barrier(0);
     read(kt, 1, 1);
     mma(0);
-    // one LDS read between every two MFMAs
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < NF; ++u) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, (NMMA + NF - 1) / NF, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // s_waitcnt vmcnt(16) lgkmcnt(0) as a builtin, so the compiler's own wait
-    // accounting knows the reads of this step are complete
-    __builtin_amdgcn_s_waitcnt(0x4070);
+    // lgkmcnt(0) and vmcnt(two stages) as a builtin, so the compiler's own
+    // wait accounting knows the reads of this step are complete
+    if (LOADS == 8) __builtin_amdgcn_s_waitcnt(0x4070);   // vmcnt(16)
+    else __builtin_amdgcn_s_waitcnt(0x007E);              // vmcnt(14)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     issue(kt + GB_NST);
     read(kt + 1, 0, 0);
     mma(1);
-    // MFMAs interleaved with the refill loads and the next step's LDS reads
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    for (int u = 0; u < NF; ++u) {
+      if (u < LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -314,7 +340,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int t
     mma(0);
     if (kt + 1 < nk) {
       __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      gb_wait_stages(min(nk - 2 - kt, GB_NST - 2));
+      gb_wait_stages<LOADS>(min(nk - 2 - kt, GB_NST - 2));
       __builtin_amdgcn_s_barrier();
       __asm__ volatile("" ::: "memory");
       read(kt + 1, 0, 0);
@@ -323,26 +349,26 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int t
   }
 
   if (g.k_splits > 1) {
-    // fp32 partial sums through LDS, one 128-row half of the tile at a time
-    // (the waves with wm == half stage it), then 64 lanes per row store 1 KB
-    constexpr int FP = GB_BN + 4;   // fp32 pitch
+    // fp32 partial sums through LDS, the rows of one wave row-group at a time
+    // (FM * 32 rows), then 64 lanes per row store BN floats
+    constexpr int FP = BN + 4, RG = FM * 32;   // fp32 pitch, rows per group
     float* P = g.part + (int64_t)split * M * N;
     float* sf = (float*)smem;
-    for (int half = 0; half < 2; ++half) {
-      __syncthreads();   // the ring (or the previous half) is no longer read
-      if (wm == half) {
+    for (int grp_m = 0; grp_m < WM; ++grp_m) {
+      __syncthreads();   // the ring (or the previous group) is no longer read
+      if (wm == grp_m) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg)
-              *(float4*)&sf[(i * 32 + l32) * FP + wn * 128 + j * 32 + 8 * rg + 4 * hi] =
+              *(float4*)&sf[(i * 32 + l32) * FP + wn * FN * 32 + j * 32 + 8 * rg + 4 * hi] =
                   make_float4(acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]);
       }
       __syncthreads();
-      for (int c = tid; c < 128 * (GB_BN / 4); c += 256) {
-        const int row = c >> 6, ch = (c & 63) * 4, m = m0 + half * 128 + row, n = n0 + ch;
+      for (int c = tid; c < RG * (BN / 4); c += 256) {
+        const int row = c / (BN / 4), ch = (c % (BN / 4)) * 4, m = m0 + grp_m * RG + row, n = n0 + ch;
         if (m >= M || n >= N) continue;
         const float4 v = *(const float4*)&sf[row * FP + ch];
         float* p = P + (int64_t)m * N + n;
@@ -357,39 +383,36 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int t
     return;
   }
   // Epilogue through LDS: the bf16 C tile is staged row-major (8-byte writes
-  // of 4 consecutive columns), then stored in 16-byte pieces (row-major C or
-  // the k_nope part of the KV split), or as 2-byte stores running along t
-  // (the transposed v part).
+  // of 4 consecutive columns), then stored in 16-byte pieces.
   __syncthreads();   // every wave is done reading the ring
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const int ml = wm * 128 + i * 32 + l32, nl = wn * 128 + j * 32 + 8 * rg + 4 * hi;
-        *(uint2*)&smem[ml * GB_CP + nl] =
-            make_uint2(pack_bf16x2(acc[i][j][4 * rg], acc[i][j][4 * rg + 1]),
-                       pack_bf16x2(acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]));
+        const int ml = wm * FM * 32 + i * 32 + l32, nl = wn * FN * 32 + j * 32 + 8 * rg + 4 * hi;
+        *(uint2*)&smem[ml * CP + nl] = make_uint2(pack_bf16x2(acc[i][j][4 * rg], acc[i][j][4 * rg + 1]),
+                                                  pack_bf16x2(acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]));
       }
   __syncthreads();
   uint16_t* C = (uint16_t*)g.C + (int64_t)z * g.batch_c;
-  if (g.epi == EPI_KV_SPLIT) {
+  if (BN == 256 && g.epi == EPI_KV_SPLIT) {
     // the tile is one head (N % 256 == 0): columns 0..127 are k_nope, stored
     // along the row (16 lanes per row); columns 128..255 are v, stored
     // transposed with lanes running along t so each column's writes coalesce
     const int h = n0 >> 8;
-    for (int c = tid; c < GB_BM * 16; c += 256) {
+    for (int c = tid; c < BM * 16; c += 256) {
       const int row = c >> 4, ch = (c & 15) * 8, m = m0 + row;
       if (m >= M) continue;
       const int bb = m / g.kv.T, tt = m - bb * g.kv.T;
       const int64_t bh = (int64_t)bb * g.kv.H + h;
-      *(uint4*)(C + (bh * g.kv.Tp + tt) * 128 + ch) = *(const uint4*)&smem[row * GB_CP + ch];
+      *(uint4*)(C + (bh * g.kv.Tp + tt) * 128 + ch) = *(const uint4*)&smem[row * CP + ch];
     }
-    for (int c = tid; c < GB_BM * 16; c += 256) {
-      const int row = c & (GB_BM - 1), ch = (c >> 8) * 8, m = m0 + row;
+    for (int c = tid; c < BM * 16; c += 256) {
+      const int row = c & (BM - 1), ch = (c / BM) * 8, m = m0 + row;
       if (m >= M) continue;
-      const uint4 v = *(const uint4*)&smem[row * GB_CP + 128 + ch];
+      const uint4 v = *(const uint4*)&smem[row * CP + 128 + ch];
       const uint16_t* e = (const uint16_t*)&v;
       const int bb = m / g.kv.T, tt = m - bb * g.kv.T;
       uint16_t* vt = (uint16_t*)g.kv.vt + (((int64_t)bb * g.kv.H + h) * 128 + ch) * g.kv.Tp + tt;
@@ -398,11 +421,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int t
     }
     return;
   }
-  // row-major C: 32 lanes per row, 16-byte stores along the row
-  for (int c = tid; c < GB_BM * (GB_BN / 8); c += 256) {
-    const int row = c >> 5, ch = (c & 31) * 8, m = m0 + row, n = n0 + ch;
+  // row-major C: BN / 8 lanes per row, 16-byte stores along the row
+  for (int c = tid; c < BM * (BN / 8); c += 256) {
+    const int row = c / (BN / 8), ch = (c % (BN / 8)) * 8, m = m0 + row, n = n0 + ch;
     if (m >= M || n >= N) continue;
-    const uint4 v = *(const uint4*)&smem[row * GB_CP + ch];
+    const uint4 v = *(const uint4*)&smem[row * CP + ch];
     if (n + 8 <= N) {
       *(uint4*)(C + (int64_t)m * g.ldc + n) = v;
     } else {
@@ -414,43 +437,74 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int t
   }
 }
 
+// one kernel per tile shape (plain kernels around the templated body)
+__global__ __launch_bounds__(256, 1) void gemm_bf16_big256_kernel(GemmArgs g, int tm, int tn, int per_xcd) {
+  gemm_bf16_big<2, 2, 4, 4>(g, tm, tn, per_xcd);
+}
+__global__ __launch_bounds__(256, 1) void gemm_bf16_big224_kernel(GemmArgs g, int tm, int tn, int per_xcd) {
+  gemm_bf16_big<4, 1, 2, 7>(g, tm, tn, per_xcd);
+}
+__global__ __launch_bounds__(256, 1) void gemm_bf16_big192_kernel(GemmArgs g, int tm, int tn, int per_xcd) {
+  gemm_bf16_big<2, 2, 4, 3>(g, tm, tn, per_xcd);
+}
+
 }  // namespace
 
 namespace {
-// operand shapes the big-tile kernel takes
+// operand shapes the big-tile kernels take
 bool big_ok(const GemmArgs& g) {
   return !g.w_kn && g.M >= 256 && g.N >= 256 && g.K % GB_BK == 0 && (g.lda & 7) == 0 && (g.ldw & 7) == 0 &&
          (g.n_split >= g.N || (g.ldw2 & 7) == 0) && (((uintptr_t)g.A | (uintptr_t)g.W | (uintptr_t)g.W2) & 15) == 0;
+}
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+// tile width: the widest of 256 / 224 / 192 whose tile count fills whole rounds
+// of 256 CUs best (the KV split and split-K use 256)
+int big_bn(const GemmArgs& g) {
+  if (g.epi == EPI_KV_SPLIT || g.k_splits > 1) return 256;
+  const int tm = cdiv(g.M, 256);
+  int best = 256;
+  double best_eff = 0;
+  for (int bn : {256, 224, 192}) {
+    const int tiles = tm * cdiv(g.N, bn) * g.batch;
+    const double eff = (double)tiles / (cdiv(tiles, 256) * 256.0) * ((double)g.N / (cdiv(g.N, bn) * bn));
+    if (eff > best_eff + 1e-9) { best_eff = eff; best = bn; }
+  }
+  return best;
+}
+hipError_t run_big(const GemmArgs& g, int bn, int ny, hipStream_t s) {
+  const int tm = cdiv(g.M, 256), tn = cdiv(g.N, bn);
+  const int per_xcd = cdiv(tm * tn, 8);
+  const dim3 grid(8 * per_xcd, ny);
+  if (bn == 224) gemm_bf16_big224_kernel<<<grid, 256, 0, s>>>(g, tm, tn, per_xcd);
+  else if (bn == 192) gemm_bf16_big192_kernel<<<grid, 256, 0, s>>>(g, tm, tn, per_xcd);
+  else gemm_bf16_big256_kernel<<<grid, 256, 0, s>>>(g, tm, tn, per_xcd);
+  return hipGetLastError();
 }
 }  // namespace
 
 int gemm_bf16_splits(const GemmArgs& g) {
   if (!big_ok(g) || g.batch != 1 || (g.N & 3) != 0) return 1;
-  const int tiles = ((g.M + GB_BM - 1) / GB_BM) * ((g.N + GB_BN - 1) / GB_BN);
+  const int tiles = cdiv(g.M, 256) * cdiv(g.N, 256);
   if (tiles >= 128) return 1;
   int splits = 256 / tiles;
   const int ksteps = g.K / GB_BK;
   if (splits > ksteps / 16) splits = ksteps / 16;   // at least 16 steps of 32 per chunk
   if (splits < 2) return 1;
-  const int per = (ksteps + splits - 1) / splits;
-  return (ksteps + per - 1) / per;   // chunks actually made
+  const int per = cdiv(ksteps, splits);
+  return cdiv(ksteps, per);   // chunks actually made
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
   if (g.w_kn) return run<128, 128, 2, 2, true>(g, s);
-  const int tm = (g.M + GB_BM - 1) / GB_BM, tn = (g.N + GB_BN - 1) / GB_BN;
-  const int per_xcd = (tm * tn + 7) / 8;
   if (g.k_splits > 1) {   // the caller sized part[] from gemm_bf16_splits
     if (!big_ok(g) || g.batch != 1 || !g.part || g.k_splits != gemm_bf16_splits(g)) return hipErrorInvalidValue;
-    gemm_bf16_big_kernel<<<dim3(8 * per_xcd, g.k_splits), 256, 0, s>>>(g, tm, tn, per_xcd);
-    return hipGetLastError();
+    return run_big(g, 256, g.k_splits, s);
   }
   // bf16 output, 16-byte aligned rows (the KV split needs N % 256 == 0, true for H*256)
   const bool c_ok = g.c_dtype == DT_BF16 && (((uintptr_t)g.C) & 15) == 0 &&
                     (g.epi == EPI_KV_SPLIT ? (g.N & 255) == 0 : ((g.ldc & 7) == 0 && (g.batch_c & 7) == 0));
   if (c_ok && big_ok(g)) {
-    gemm_bf16_big_kernel<<<dim3(8 * per_xcd, g.batch), 256, 0, s>>>(g, tm, tn, per_xcd);
-    return hipGetLastError();
+    return run_big(g, big_bn(g), g.batch, s);
   }
   return run<128, 128, 2, 2, false>(g, s);
 }
