@@ -304,7 +304,7 @@ def main():
     line["workloads"] = {str(k): v for k, v in results.items()}
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(1)
+        line["cpu_baseline"] = cpu_baseline(1, rows=640)
     print(json.dumps(line), flush=True)
 
 
