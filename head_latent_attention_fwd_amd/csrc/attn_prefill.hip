@@ -8,8 +8,9 @@
 // values per head already transposed [B, H, 128, Tp] (both written so by the
 // kv_b GEMM's epilogue) and the shared rotary key [B, Tp, 64].
 //
-// Work split: one 256-thread workgroup per (128-query tile, head, sequence),
-// heaviest (last) query tiles first; wave w owns queries [32w, 32w+32).
+// Work split: one 256-thread workgroup per (128-query tile, head, sequence);
+// the query tiles of one (sequence, head) run on one XCD, heaviest (last)
+// first; wave w owns queries [32w, 32w+32).
 // Scores are formed transposed, S^T = K . Q^T, on v_mfma_f32_32x32x16_bf16 so
 // a lane holds 32 keys of one query: the running max needs one exchange
 // (lane ^ 32) and the running sum stays lane-local; the bf16 probabilities are
@@ -50,8 +51,16 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int T = a.T, Tp = a.Tp, H = a.H;
-  const int qt = (int)gridDim.x - 1 - (int)blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  // XCD-aware order: workgroup id % 8 is the XCD, and each XCD takes whole
+  // (sequence, head) pairs, so the query tiles that re-read one head's keys
+  // and values share that XCD's L2; within a pair the longest (last) query
+  // tiles start first.
+  const int nq = (T + BQ - 1) / BQ;
+  const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+  const int pair = (loc / nq) * 8 + xcd;
+  if (pair >= a.B * H) return;
+  const int qt = nq - 1 - loc % nq;
+  const int h = pair % H, b = pair / H;
   const int64_t bh = (int64_t)b * H + h;
   const int q0 = qt * BQ, qw = q0 + wave * 32;
   const int qi = qw + l32;
@@ -277,7 +286,8 @@ __global__ __launch_bounds__(64) void prefill_attn_f32_kernel(PrefillAttnArgs a)
 }  // namespace
 
 hipError_t launch_prefill_attn_bf16(const PrefillAttnArgs& a, hipStream_t s) {
-  dim3 grid((a.T + BQ - 1) / BQ, a.H, a.B);
+  const int nq = (a.T + BQ - 1) / BQ, pairs = a.B * a.H;
+  const unsigned grid = 8u * (unsigned)((pairs + 7) / 8) * (unsigned)nq;
   prefill_attn_kernel<<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
