@@ -15,7 +15,7 @@ OUT = os.path.join(HERE, "libmla.so")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 
 SOURCES = ["api.cpp", "gemm_bf16.hip", "gemm_f32.hip", "gemm_fp8.hip", "gemm_skinny.hip", "elementwise.hip",
-           "attn_prefill.hip", "attn_decode.hip"]
+           "attn_prefill.hip", "attn_decode.hip", "decode_absorb.hip"]
 
 # Packed-fp32 instructions stay off: ordinary float code is compiled to
 # scalar VALU ops only.

@@ -130,7 +130,7 @@ size_t prefill_layout(const mla_dims* d, int wdt, int adt, int B, int T, int top
 }
 
 struct DecodeWs {
-  void *part, *cqn, *entry, *q, *qlat, *olat, *o;
+  void *part, *cqn, *q, *qlat, *olat, *o;
 };
 
 // split-K factors of the two decode projections with long K
@@ -143,7 +143,6 @@ size_t decode_layout(const mla_dims* d, int B, void* ws, DecodeWs* out) {
   const size_t part_qkv = (size_t)DEC_SPLIT_QKV * B * (Dq + L + 64), part_wo = (size_t)DEC_SPLIT_WO * B * d->dim;
   p.part = c.take((part_qkv > part_wo ? part_qkv : part_wo) * 4);
   p.cqn = c.take((size_t)B * Dq * 2);
-  p.entry = c.take((size_t)B * (L + 64) * 2);
   p.q = c.take((size_t)B * H * 192 * 2);
   p.qlat = c.take((size_t)B * H * 576 * 2);
   p.olat = c.take((size_t)B * H * 512 * 2);
@@ -365,24 +364,22 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B
     LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm(q)");
   }
   {
-    mla::NormRopeArgs a = norm_args(part + Dq, NQKV, p.entry, L + 64, MLA_F32, B);
+    // the normalised latent and rotated k_pe land directly in cache row cache_len[b]
+    mla::NormRopeArgs a = norm_args(part + Dq, NQKV, kv_cache, (int64_t)max_len * (L + 64), MLA_F32, B);
     a.out_dtype = MLA_BF16; a.in_splits = splits_qkv; a.split_stride = (int64_t)B * NQKV;
     a.norm_dim = L; a.gamma = w->kv_norm_w; a.eps = d->rms_eps;
     a.rope_off = L; a.rope_heads = 1; a.rope_stride = 64;
     a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = max_len; a.pos = cache_len;
-    LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(kv)");
+    a.out_pos_stride = L + 64; a.out_pos_max = max_len;
+    LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(kv) -> cache");
   }
   // q = c_q . Wq_b^T
   if ((rc = skinny(p.cqn, Dq, 0, w->wq_b, Dq, 0, nullptr, 0, H * 192, p.q, H * 192, 0, nullptr, B, H * 192, Dq, 1, 64,
                    1, s)))
     return rc;
-  {  // q_lat[b, h, :512] = q_nope[b, h] . W_UK_h  (W_UK_h = Wkv_b rows [256h, 256h+128), read [K, N])
-    mla::GemmArgs g = gemm_args(p.q, H * 192, w->wkv_b, L, p.qlat, H * 576, MLA_BF16, B, L, 128);
-    g.batch = H; g.batch_a = 192; g.batch_w = 256 * (int64_t)L; g.batch_c = 576; g.w_kn = true;
-    LAUNCH(mla::launch_gemm_bf16(g, s), "gemm(absorb W_UK)");
-  }
-  LAUNCH(mla::launch_decode_append(p.entry, kv_cache, cache_len, B, max_len, p.q, p.qlat, H, rope_cos, rope_sin, s),
-         "decode_append");
+  // q_lat[b, h] = [q_nope[b, h] . W_UK_h | RoPE(q_pe[b, h])]  (W_UK_h = Wkv_b rows [256h, 256h+128))
+  LAUNCH(mla::launch_decode_absorb(p.q, w->wkv_b, p.qlat, cache_len, rope_cos, rope_sin, B, H, max_len, s),
+         "decode_absorb");
   {
     mla::DecodeAttnArgs a{};
     a.qlat = p.qlat; a.cache = kv_cache; a.cache_len = cache_len; a.olat = p.olat;

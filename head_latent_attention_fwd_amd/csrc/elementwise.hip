@@ -11,10 +11,20 @@ __device__ __forceinline__ float ld(const void* p, int dt, int64_t i) {
   return dt == DT_F32 ? ((const float*)p)[i] : bf2f(((const uint16_t*)p)[i]);
 }
 // input element i of a row-wise kernel: one array, or the sum of split-K partials
+// (summed in split order; up to 16 partials are loaded before the first add)
 __device__ __forceinline__ float ld_in(const NormRopeArgs& a, int64_t i) {
   if (a.in_splits <= 1) return ld(a.in, a.in_dtype, i);
   const float* p = (const float*)a.in;
   float v = p[i];
+  if (a.in_splits <= 16) {
+    float t[15];
+#pragma unroll
+    for (int s = 1; s < 16; ++s) t[s - 1] = s < a.in_splits ? p[(int64_t)s * a.split_stride + i] : 0.f;
+#pragma unroll
+    for (int s = 1; s < 16; ++s)
+      if (s < a.in_splits) v += t[s - 1];
+    return v;
+  }
   for (int s = 1; s < a.in_splits; ++s) v += p[(int64_t)s * a.split_stride + i];
   return v;
 }
@@ -45,12 +55,37 @@ __device__ float block_max(float v, float* red) {
 }
 
 // RMSNorm (gamma * x / sqrt(mean(x^2) + eps)) over the row prefix and rotate-half
-// RoPE on rope_heads 64-wide slices; one 256-thread block per row.
+// RoPE on rope_heads 64-wide slices; one 256-thread block per row. Rows up to
+// 256 * NORM_PT wide are read once into registers.
+constexpr int NORM_PT = 8;
 __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(NormRopeArgs a, int rope_len) {
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x;
-  const int64_t ib = (int64_t)row * a.ld_in, ob = (int64_t)row * a.ld_out;
-  if (a.norm_dim > 0) {
+  const int64_t ib = (int64_t)row * a.ld_in;
+  int64_t ob = (int64_t)row * a.ld_out;
+  if (a.out_pos_stride > 0) {
+    const int P = a.pos[row];
+    if (P < 0 || P >= a.out_pos_max) return;
+    ob += (int64_t)P * a.out_pos_stride;
+  }
+  if (a.norm_dim > 0 && a.norm_dim <= 256 * NORM_PT) {
+    // the row stays in registers: one read of the input (and its partials)
+    float v[NORM_PT];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NORM_PT; ++j) {
+      const int i = tid + 256 * j;
+      v[j] = i < a.norm_dim ? ld_in(a, ib + i) : 0.f;
+      ss = fmaf(v[j], v[j], ss);
+    }
+    ss = block_sum(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)a.norm_dim + a.eps);
+#pragma unroll
+    for (int j = 0; j < NORM_PT; ++j) {
+      const int i = tid + 256 * j;
+      if (i < a.norm_dim) st(a.out, a.out_dtype, ob + i, a.gamma[i] * (v[j] * r));
+    }
+  } else if (a.norm_dim > 0) {
     float ss = 0.f;
     for (int i = tid; i < a.norm_dim; i += 256) {
       float v = ld_in(a, ib + i);
@@ -167,31 +202,6 @@ __global__ __launch_bounds__(256) void topk_bitmask_kernel(const int32_t* idx, i
   for (int i = threadIdx.x; i < W; i += 256) out[i] = words[i];
 }
 
-// Decode: append the new [latent | k_pe] entry at slot cache_len[b] and write
-// the rotated query rope part into the latent-space query.
-__global__ __launch_bounds__(256) void decode_append_kernel(const uint16_t* entry, uint16_t* cache,
-                                                            const int32_t* cache_len, int max_len,
-                                                            const uint16_t* q, uint16_t* qlat, int H,
-                                                            const float* cos_tab, const float* sin_tab) {
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int P = cache_len[b];
-  const bool ok = P >= 0 && P < max_len;
-  if (ok) {
-    uint16_t* dst = cache + ((int64_t)b * max_len + P) * 576;
-    for (int i = tid; i < 576; i += 256) dst[i] = entry[(int64_t)b * 576 + i];
-  }
-  for (int p = tid; p < H * 32; p += 256) {
-    const int h = p >> 5, d = p & 31;
-    const uint16_t* src = q + ((int64_t)b * H + h) * 192 + 128;
-    uint16_t* o = qlat + ((int64_t)b * H + h) * 576 + 512;
-    const float x1 = bf2f(src[d]), x2 = bf2f(src[d + 32]);
-    float c = 0.f, s = 0.f;
-    if (ok) { c = cos_tab[P * 32 + d]; s = sin_tab[P * 32 + d]; }
-    o[d] = f2bf(x1 * c - x2 * s);
-    o[d + 32] = f2bf(x2 * c + x1 * s);
-  }
-}
-
 }  // namespace
 
 hipError_t launch_rmsnorm_rope(const NormRopeArgs& a, hipStream_t s) {
@@ -235,14 +245,6 @@ hipError_t launch_quant_block128(const float* w, int N, int K, uint8_t* q, float
 hipError_t launch_topk_bitmask(const int32_t* idx, int B, int T, int k, uint32_t* mask, hipStream_t s) {
   dim3 grid(T, B);
   topk_bitmask_kernel<<<grid, 256, ((T + 31) / 32) * 4, s>>>(idx, T, k, mask);
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_append(const void* entry, void* cache, const int32_t* cache_len, int B, int max_len,
-                                const void* q, void* qlat, int H, const float* cos_tab, const float* sin_tab,
-                                hipStream_t s) {
-  decode_append_kernel<<<B, 256, 0, s>>>((const uint16_t*)entry, (uint16_t*)cache, cache_len, max_len,
-                                         (const uint16_t*)q, (uint16_t*)qlat, H, cos_tab, sin_tab);
   return hipGetLastError();
 }
 

@@ -84,6 +84,9 @@ struct NormRopeArgs {
   // in_splits > 1: the input is the sum of in_splits fp32 partial arrays
   // split_stride elements apart (split-K GEMM output)
   int in_splits; int64_t split_stride;
+  // out_pos_stride > 0: output row m starts at out + m*ld_out + pos[m]*out_pos_stride
+  // (a cache append) and rows whose pos is outside [0, out_pos_max) are not written
+  int64_t out_pos_stride; int out_pos_max;
 };
 hipError_t launch_rmsnorm_rope(const NormRopeArgs& a, hipStream_t s);
 hipError_t launch_rope_table(float* c, float* sn, int n_pos, float base, hipStream_t s);
@@ -116,10 +119,10 @@ struct DecodeAttnArgs {
   int B, H, max_len; float scale;
 };
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s);
-// Copies entry[b] ([576] bf16) to cache[b, cache_len[b]] and the rotated q_pe of
-// every head (q [B, H*192] at 128 + 192h) to qlat[b, h, 512:576].
-hipError_t launch_decode_append(const void* entry, void* cache, const int32_t* cache_len, int B,
-                                int max_len, const void* q, void* qlat, int H,
-                                const float* cos_tab, const float* sin_tab, hipStream_t s);
+// q_lat[b, h] = [q_nope[b, h] . W_UK_h | RoPE(q_pe[b, h], cache_len[b])] for kv_lora_rank 512;
+// q [B, H*192], wkv_b [H*256, 512], qlat [B, H, 576].
+hipError_t launch_decode_absorb(const void* q, const void* wkv_b, void* qlat, const int32_t* cache_len,
+                                const float* cos_tab, const float* sin_tab, int B, int H, int max_len,
+                                hipStream_t s);
 
 }  // namespace mla
