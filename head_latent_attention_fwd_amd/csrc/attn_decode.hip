@@ -44,7 +44,6 @@ constexpr int DROW = 576;               // elements per cache row
 constexpr int DLAT = DKT * 512;         // latent region of a stage (elements)
 constexpr int DSTAGE = DKT * DROW;      // elements per stage
 constexpr float LAZY = 64.f;            // log2-domain headroom over the fixed running max
-constexpr int BUF_DW3 = 0x00020000;     // gfx9 raw-buffer descriptor word 3
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));

@@ -39,7 +39,6 @@ constexpr int BKV = 64;                   // keys per tile
 constexpr int ST_KN = 0, ST_KPE = 64 * 128, ST_VT = ST_KPE + 64 * 64, STAGE = ST_VT + 128 * 64;
 constexpr int LOADS = STAGE * 2 / 16 / 256;  // 16-byte direct loads per thread per tile (10)
 constexpr float LAZY = 8.0f;
-constexpr int BUF_DW3 = 0x00020000;       // gfx9 raw-buffer descriptor word 3
 
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 // chunk swizzle of 128-byte rows, conflict-free for 32 or 64 LDS banks

@@ -165,97 +165,97 @@ hipError_t run(const GemmArgs& g, hipStream_t s) {
 // BN = 32 WN FN; WM x WN waves, each FM x FN blocks of 32x32 with accumulators
 // in AGPRs). Shapes: 256x256 (2x2 waves of 4x4), 256x192 (2x2 of 4x3) and
 // 256x224 (4x1 of 2x7); the narrower tiles make the tile count a multiple of
-// the 256 CUs for N = 12288 and N = 7168. K moves in 32-wide steps through a
-// 4-stage LDS ring filled by 16-byte direct-to-LDS loads; a step's loads are
-// issued while the three steps before it are consumed, so the L2/HBM latency
-// hides behind ~3000 cycles of math. A stage holds BM rows of A and BNL >= BN
-// rows of W (rounded up so every thread issues the same number of loads; the
-// extra rows are loaded and ignored). The operand fragments of the next
-// 16-wide step are read from LDS between the current step's MFMAs; one
-// barrier per 32-wide step, after which the stage just consumed takes the step
-// four ahead. Rows are 64 bytes (4 chunks of 16 B), XOR-swizzled by
-// ((row >> 1) ^ (row >> 3)) & 3: conflict-free operand reads with 32 or 64
-// LDS banks. Tiles are numbered so that each XCD (workgroup id % 8) works on a
-// contiguous, M-grouped block of the output and its L2 serves the shared A/W
-// slabs. Output: bf16 through LDS with 16-byte coalesced stores (row-major or
-// the k_nope / v^T split of kv_b), or fp32 split-K partials.
-constexpr int GB_BK = 32, GB_NST = 4, GB_GROUP_M = 8;
-constexpr int GB_SMEM = 256 * (256 + 8);   // elements: the largest of ring and epilogue tile
+// the 256 CUs for N = 12288 and N = 7168.
+//
+// K moves in 64-wide steps through two LDS stages that are distinct LDS
+// objects, so the code for each is straight-line and the compiler's waits for
+// the direct-to-LDS loads never cover the other stage. A stage holds BM rows of
+// A and BN rows of W, 128 bytes per row, filled by 16-byte raw-buffer loads
+// straight into LDS (a per-lane byte offset fixed for the whole K loop plus a
+// scalar k offset); chunks of a row are XOR-swizzled by (row >> 1) & 7, which
+// spreads the 16 lanes of every 16-byte operand read over all LDS banks.
+// Within a step the fragments of the next 16-wide sub-step are read between
+// the MFMAs of the current one. In the last sub-step every wave waits for the
+// other stage to land, one barrier retires the stage just consumed, its refill
+// (the step two ahead) is issued, and the first fragments of the other stage
+// are read, all between that sub-step's MFMAs. Tiles are numbered so that each
+// XCD (workgroup id % 8) works on a contiguous, M-grouped block of the output
+// and its L2 serves the shared A/W slabs. Output: bf16 through LDS with
+// 16-byte coalesced stores (row-major or the k_nope / v^T split of kv_b), or
+// fp32 split-K partials through a per-wave LDS patch.
+constexpr int GB_BK = 64, GB_GROUP_M = 8;
 
-__device__ __forceinline__ int gb_sw(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int gb_sw(int row) { return (row >> 1) & 7; }
 
-// s_waitcnt vmcnt(n * LOADS): stages still allowed in flight
-template <int LOADS>
-__device__ __forceinline__ void gb_wait_stages(int n) {
-  static_assert(LOADS == 7 || LOADS == 8, "wait counts below assume 7 or 8 loads per stage");
-  if (LOADS == 8) {
-    if (n >= 3) __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
-    else if (n == 2) __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if (n == 1) __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  } else {
-    if (n >= 3) __asm__ volatile("s_waitcnt vmcnt(21)" ::: "memory");
-    else if (n == 2) __asm__ volatile("s_waitcnt vmcnt(14)" ::: "memory");
-    else if (n == 1) __asm__ volatile("s_waitcnt vmcnt(7)" ::: "memory");
-    else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-}
+// s_waitcnt immediate: vmcnt (6 bits, split), expcnt 7, lgkmcnt (4 bits)
+constexpr int gb_wait(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8); }
 
 template <int WM, int WN, int FM, int FN>
 struct BigTile {
   static constexpr int BM = 32 * WM * FM, BN = 32 * WN * FN;
-  static constexpr int BNL = ((BM + BN + 63) / 64) * 64 - BM;   // W rows loaded per stage
-  static constexpr int ROWS = BM + BNL;
-  static constexpr int STAGE = ROWS * GB_BK;                      // elements
-  static constexpr int LOADS = ROWS * 4 / 256;                    // 16-byte loads per thread per stage
-  static constexpr int CP = BN + 8;                               // epilogue C-tile pitch (elements)
-  static_assert(WM * WN == 4 && BM == 256, "four waves over 256 rows");
-  static_assert(GB_NST * STAGE <= GB_SMEM && BM * CP <= GB_SMEM, "LDS budget");
+  static constexpr int ROWS = BM + BN;
+  static constexpr int LOADS = ROWS / 32;   // 16-byte loads per thread per stage
+  static constexpr int STAGE = ROWS * GB_BK;   // elements
+  static constexpr int CP = BN + 8;            // bf16 C-tile pitch (elements); rows 0..127 / 128..255 in stage 0 / 1
+  static constexpr int FP = 32 * FN + 4;       // fp32 per-wave patch pitch (floats)
+  static constexpr int HALF = (STAGE > 128 * CP ? STAGE : 128 * CP);
+  static_assert(WM * WN == 4 && BM == 256 && ROWS % 32 == 0, "four waves over 256 rows");
+  static_assert(2 * HALF * 2 <= 160 * 1024, "LDS budget");
+  static_assert(2 * 32 * FP * 4 <= HALF * 2, "split-K patches of two waves per stage");
 };
 
 template <int WM, int WN, int FM, int FN>
 __device__ __forceinline__ void gemm_bf16_big(const GemmArgs& g, int tiles_m, int tiles_n, int per_xcd) {
   using TL = BigTile<WM, WN, FM, FN>;
-  constexpr int BM = TL::BM, BN = TL::BN, LOADS = TL::LOADS, STAGE = TL::STAGE, CP = TL::CP;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[GB_SMEM];
+  constexpr int BM = TL::BM, BN = TL::BN, LOADS = TL::LOADS, CP = TL::CP, HALF = TL::HALF;
+  __shared__ __attribute__((aligned(16))) uint16_t s0[HALF];
+  __shared__ __attribute__((aligned(16))) uint16_t s1[HALF];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN, l32 = lane & 31, hi = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wv / WN, wn = wv % WN, l32 = lane & 31, hi = lane >> 5;
   const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
   const int t = xcd * per_xcd + loc, ntile = tiles_m * tiles_n;
   if (loc >= per_xcd || t >= ntile) return;
   const int span = GB_GROUP_M * tiles_n, grp = t / span, first_m = grp * GB_GROUP_M;
   const int gsz = min(tiles_m - first_m, GB_GROUP_M), r_in = t - grp * span;
-  const int m0 = (first_m + r_in % gsz) * BM, n0 = (r_in / gsz) * BN;
+  const int m0 = (first_m + r_in % gsz) * BM, tn = r_in / gsz;
   const int M = g.M, N = g.N, K = g.K;
   const int split = g.k_splits > 1 ? (int)blockIdx.y : 0, z = g.k_splits > 1 ? 0 : (int)blockIdx.y;
+  // With a second weight (rows n_split.. of the concatenated W), column tiles
+  // never straddle n_split: tiles 0..t1-1 cover [0, n_split), the rest
+  // [n_split, N). nend bounds the tile's region (rows past it are clamped).
+  const int nsp = g.W2 ? g.n_split : N, t1 = (nsp + BN - 1) / BN;
+  const bool second = tn >= t1;
+  const int n0 = second ? nsp + (tn - t1) * BN : tn * BN, nend = second ? N : nsp;
   // K chunk of this workgroup (whole K without split-K)
   const int ksteps = K / GB_BK, per = (ksteps + max(g.k_splits, 1) - 1) / max(g.k_splits, 1);
   const int kbeg = split * per * GB_BK;
+  const int nk = min(per, ksteps - split * per);
   const uint16_t* A = (const uint16_t*)g.A + (int64_t)z * g.batch_a + kbeg;
-  const uint16_t* W = (const uint16_t*)g.W + (int64_t)z * g.batch_w + kbeg;
-  const uint16_t* W2 = g.W2 ? (const uint16_t*)g.W2 + kbeg : nullptr;
+  const int64_t ldw = second ? g.ldw2 : g.ldw;
 
-  // Direct-load slots: a stage holds A rows 0..BM-1 then W rows 0..BNL-1, 4
-  // chunks per row; wave w fills 1 KB blocks LOADS w .. LOADS w + LOADS - 1.
-  const uint16_t* src[LOADS];
+  // Load slot i of wave w fills 1 KB block 4 i + w of a stage (8 rows of 8
+  // chunks); blocks 0..31 are A rows, the rest W rows. Rows past M or nend
+  // are clamped to the last one (loaded, never stored).
+  const uint16_t* Wb = second ? (const uint16_t*)g.W2 + kbeg + (int64_t)(n0 - nsp) * g.ldw2   // row n0 of the tile
+                              : (const uint16_t*)g.W + (int64_t)z * g.batch_w + kbeg + (int64_t)n0 * g.ldw;
+  const __amdgpu_buffer_rsrc_t rsA =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(((int64_t)(M - 1) * g.lda + K - kbeg) * 2), BUF_DW3);
+  const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)Wb, (short)0, (int)(((int64_t)(nend - 1 - n0) * ldw + K - kbeg) * 2), BUF_DW3);
+  int voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int p = (wave * LOADS + i) * 64 + lane;
-    const int r = p >> 2;
-    if (r < BM) {
-      const int c = (p & 3) ^ gb_sw(r);
-      src[i] = A + (int64_t)min(m0 + r, M - 1) * g.lda + c * 8;
-    } else {
-      const int rw = r - BM, c = (p & 3) ^ gb_sw(rw);
-      const int n = min(n0 + rw, N - 1);
-      src[i] = (n < g.n_split ? W + (int64_t)n * g.ldw : W2 + (int64_t)(n - g.n_split) * g.ldw2) + c * 8;
-    }
+    const int r = 8 * (4 * i + wv) + (lane >> 3), c = (lane & 7) ^ gb_sw(r);
+    if (i < 8) voff[i] = (int)(((int64_t)min(m0 + r, M - 1) * g.lda + c * 8) * 2);
+    else voff[i] = (int)(((int64_t)(min(n0 + r - BM, nend - 1) - n0) * ldw + c * 8) * 2);
   }
-  auto issue = [&](int kt) {
-    uint16_t* st = smem + (kt % GB_NST) * STAGE + wave * LOADS * 512;
+  auto issue = [&](uint16_t* st, int kt) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      __builtin_amdgcn_global_load_lds(src[i] + kt * GB_BK, st + i * 512, 16, 0, 0);
+    for (int i = 0; i < LOADS; ++i) {
+      auto* lds = (__attribute__((address_space(3))) void*)(st + (4 * i + wv) * 512);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(i < 8 ? rsA : rsW, lds, 16, voff[i], kt * 128, 0, 0);
+    }
   };
 
   floatx16 acc[FM][FN];
@@ -266,19 +266,17 @@ __device__ __forceinline__ void gemm_bf16_big(const GemmArgs& g, int tiles_m, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // swizzled chunk offset of this lane's rows (the swizzle depends on l32 only)
-  int xo[2];
+  // lane's row offsets in a stage; the swizzle depends on l32 only
+  const int ra = (wm * FM * 32 + l32) * GB_BK, rw = (BM + wn * FN * 32 + l32) * GB_BK;
+  int xo[4];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) xo[kk] = ((2 * kk + hi) ^ gb_sw(l32)) << 3;
-  bf16x8 fa[2][FM], fb[2][FN];   // fragments of one 16-wide step, double-buffered
-  auto read = [&](int kt, int kk, int buf) {
-    const uint16_t* st = smem + (kt % GB_NST) * STAGE;
+  for (int kk = 0; kk < 4; ++kk) xo[kk] = ((2 * kk + hi) ^ gb_sw(l32)) << 3;
+  bf16x8 fa[2][FM], fb[2][FN];   // fragments of one 16-wide sub-step, double-buffered
+  auto read = [&](const uint16_t* st, int kk, int buf) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      fa[buf][i] = *(const bf16x8*)(st + (wm * FM * 32 + i * 32 + l32) * GB_BK + xo[kk]);
+    for (int i = 0; i < FM; ++i) fa[buf][i] = *(const bf16x8*)(st + ra + i * 32 * GB_BK + xo[kk]);
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      fb[buf][j] = *(const bf16x8*)(st + (BM + wn * FN * 32 + j * 32 + l32) * GB_BK + xo[kk]);
+    for (int j = 0; j < FN; ++j) fb[buf][j] = *(const bf16x8*)(st + rw + j * 32 * GB_BK + xo[kk]);
   };
   // operands swapped (W first): a lane's accumulator holds one row of C and
   // 4 consecutive columns per group of 4 results
@@ -288,113 +286,109 @@ __device__ __forceinline__ void gemm_bf16_big(const GemmArgs& g, int tiles_m, in
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(fb[buf][j], fa[buf][i], acc[i][j]);
   };
-
-  const int nk = min(per, ksteps - split * per);
-  for (int s = 0; s < GB_NST; ++s)
-    if (s < nk) issue(s);
-  gb_wait_stages<LOADS>(min(nk, GB_NST) - 1);   // step 0 has landed
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-  read(0, 0, 0);
-  // Step kt: the second half of its fragments is read during the first
-  // half's MFMAs; then every wave holds step kt in registers and step kt+1
-  // has landed (kt+2, kt+3 may be in flight), so after a bare barrier the
-  // stage of step kt takes step kt+4. The steady-state loop has no branch
-  // inside, which keeps the compiler's own LDS waits tight, and
-  // sched_group_barrier spreads the LDS reads and refill loads between MFMAs.
   constexpr int NF = FM + FN, NMMA = FM * FN;
-  int kt = 0;
-  for (; kt + GB_NST < nk; ++kt) {
-    // the first-half fragments were read a whole MFMA group ago: a builtin
-    // lgkmcnt(0) here costs nothing and tells the compiler they are in
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_sched_barrier(0);
-    read(kt, 1, 1);
-    mma(0);
+  // one 64-wide step on stage `cur` (kt is the step's index); on return the
+  // first fragments of the other stage are in flight to fa/fb[0]
+  auto step = [&](uint16_t* cur, uint16_t* nxt, int kt) {
 #pragma unroll
-    for (int u = 0; u < NF; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, (NMMA + NF - 1) / NF, 0);
+    for (int kk = 0; kk < 3; ++kk) {
+      __builtin_amdgcn_s_waitcnt(gb_wait(63, 0));   // fragments of sub-step kk are in
+      __builtin_amdgcn_sched_barrier(0);
+      read(cur, kk + 1, (kk + 1) & 1);
+      mma(kk & 1);
+#pragma unroll
+      for (int u = 0; u < NF; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NMMA - NF, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // lgkmcnt(0) and vmcnt(two stages) as a builtin, so the compiler's own
-    // wait accounting knows the reads of this step are complete
-    if (LOADS == 8) __builtin_amdgcn_s_waitcnt(0x4070);   // vmcnt(16)
-    else __builtin_amdgcn_s_waitcnt(0x007E);              // vmcnt(14)
+    // every fragment of `cur` is in registers and the other stage has landed
+    // (its loads are the only ones in flight): retire `cur`, refill it with the
+    // step two ahead (clamped: a repeated last step is loaded and ignored)
+    __builtin_amdgcn_s_waitcnt(gb_wait(0, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue(kt + GB_NST);
-    read(kt + 1, 0, 0);
+    issue(cur, min(kt + 2, nk - 1));
+    read(nxt, 0, 0);
     mma(1);
 #pragma unroll
-    for (int u = 0; u < NF; ++u) {
+    for (int u = 0; u < NMMA; ++u) {
       if (u < LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (u < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
+  };
+
+  issue(s0, 0);
+  issue(s1, min(1, nk - 1));
+  __builtin_amdgcn_s_waitcnt(gb_wait(LOADS, 15));   // step 0 has landed
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  read(s0, 0, 0);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(s0, s1, kt);
+    step(s1, s0, kt + 1);
   }
-  for (; kt < nk; ++kt) {   // the last steps: nothing left to issue
-    read(kt, 1, 1);
-    mma(0);
-    if (kt + 1 < nk) {
-      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      gb_wait_stages<LOADS>(min(nk - 2 - kt, GB_NST - 2));
-      __builtin_amdgcn_s_barrier();
-      __asm__ volatile("" ::: "memory");
-      read(kt + 1, 0, 0);
-    }
-    mma(1);
-  }
+  if (kt < nk) step(s0, s1, kt);
+  // the repeated loads of the last steps land before the stages are reused
+  __builtin_amdgcn_s_waitcnt(gb_wait(0, 0));
+  __syncthreads();
 
   if (g.k_splits > 1) {
-    // fp32 partial sums through LDS, the rows of one wave row-group at a time
-    // (FM * 32 rows), then 64 lanes per row store BN floats
-    constexpr int FP = BN + 4, RG = FM * 32;   // fp32 pitch, rows per group
+    // fp32 partial sums: each wave stages 32 rows x 32 FN columns at a time in
+    // its own patch, then stores them row by row with 16-byte stores
+    constexpr int FP = TL::FP, CW = FN * 8;   // lanes per row (4 floats each)
     float* P = g.part + (int64_t)split * M * N;
-    float* sf = (float*)smem;
-    for (int grp_m = 0; grp_m < WM; ++grp_m) {
-      __syncthreads();   // the ring (or the previous group) is no longer read
-      if (wm == grp_m) {
+    float* patch = (float*)((wv >> 1) ? s1 : s0) + (wv & 1) * 32 * FP;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg)
-              *(float4*)&sf[(i * 32 + l32) * FP + wn * FN * 32 + j * 32 + 8 * rg + 4 * hi] =
-                  make_float4(acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]);
-      }
-      __syncthreads();
-      for (int c = tid; c < RG * (BN / 4); c += 256) {
-        const int row = c / (BN / 4), ch = (c % (BN / 4)) * 4, m = m0 + grp_m * RG + row, n = n0 + ch;
-        if (m >= M || n >= N) continue;
-        const float4 v = *(const float4*)&sf[row * FP + ch];
+        for (int rg = 0; rg < 4; ++rg)
+          *(float4*)&patch[l32 * FP + j * 32 + 8 * rg + 4 * hi] =
+              make_float4(acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]);
+      __builtin_amdgcn_s_waitcnt(gb_wait(63, 0));
+      __builtin_amdgcn_wave_barrier();
+      for (int c = lane; c < 32 * CW; c += 64) {
+        const int row = c / CW, ch = (c % CW) * 4;
+        const int m = m0 + wm * FM * 32 + i * 32 + row, n = n0 + wn * FN * 32 + ch;
+        if (m >= M || n >= nend) continue;
+        const float4 v = *(const float4*)&patch[row * FP + ch];
         float* p = P + (int64_t)m * N + n;
-        if (n + 4 <= N) {
+        if (n + 4 <= nend) {
           *(float4*)p = v;
         } else {
           const float e[4] = {v.x, v.y, v.z, v.w};
-          for (int k = 0; n + k < N; ++k) p[k] = e[k];
+          for (int k = 0; n + k < nend; ++k) p[k] = e[k];
         }
       }
+      __builtin_amdgcn_s_waitcnt(gb_wait(63, 0));
+      __builtin_amdgcn_wave_barrier();
     }
     return;
   }
   // Epilogue through LDS: the bf16 C tile is staged row-major (8-byte writes
-  // of 4 consecutive columns), then stored in 16-byte pieces.
-  __syncthreads();   // every wave is done reading the ring
+  // of 4 consecutive columns; rows 0..127 in stage 0, 128..255 in stage 1),
+  // then stored in 16-byte pieces.
+  auto crow = [&](int row) -> uint16_t* { return (row < 128 ? s0 : s1) + (row & 127) * CP; };
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int j = 0; j < FN; ++j) {
+      __builtin_amdgcn_sched_barrier(0);   // one block of accumulators at a time
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int ml = wm * FM * 32 + i * 32 + l32, nl = wn * FN * 32 + j * 32 + 8 * rg + 4 * hi;
-        *(uint2*)&smem[ml * CP + nl] = make_uint2(pack_bf16x2(acc[i][j][4 * rg], acc[i][j][4 * rg + 1]),
-                                                  pack_bf16x2(acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]));
+        *(uint2*)(crow(ml) + nl) = make_uint2(pack_bf16x2(acc[i][j][4 * rg], acc[i][j][4 * rg + 1]),
+                                              pack_bf16x2(acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]));
       }
+    }
   __syncthreads();
   uint16_t* C = (uint16_t*)g.C + (int64_t)z * g.batch_c;
   if (BN == 256 && g.epi == EPI_KV_SPLIT) {
@@ -407,12 +401,12 @@ __device__ __forceinline__ void gemm_bf16_big(const GemmArgs& g, int tiles_m, in
       if (m >= M) continue;
       const int bb = m / g.kv.T, tt = m - bb * g.kv.T;
       const int64_t bh = (int64_t)bb * g.kv.H + h;
-      *(uint4*)(C + (bh * g.kv.Tp + tt) * 128 + ch) = *(const uint4*)&smem[row * CP + ch];
+      *(uint4*)(C + (bh * g.kv.Tp + tt) * 128 + ch) = *(const uint4*)(crow(row) + ch);
     }
     for (int c = tid; c < BM * 16; c += 256) {
       const int row = c & (BM - 1), ch = (c / BM) * 8, m = m0 + row;
       if (m >= M) continue;
-      const uint4 v = *(const uint4*)&smem[row * CP + 128 + ch];
+      const uint4 v = *(const uint4*)(crow(row) + 128 + ch);
       const uint16_t* e = (const uint16_t*)&v;
       const int bb = m / g.kv.T, tt = m - bb * g.kv.T;
       uint16_t* vt = (uint16_t*)g.kv.vt + (((int64_t)bb * g.kv.H + h) * 128 + ch) * g.kv.Tp + tt;
@@ -424,15 +418,15 @@ __device__ __forceinline__ void gemm_bf16_big(const GemmArgs& g, int tiles_m, in
   // row-major C: BN / 8 lanes per row, 16-byte stores along the row
   for (int c = tid; c < BM * (BN / 8); c += 256) {
     const int row = c / (BN / 8), ch = (c % (BN / 8)) * 8, m = m0 + row, n = n0 + ch;
-    if (m >= M || n >= N) continue;
-    const uint4 v = *(const uint4*)&smem[row * CP + ch];
-    if (n + 8 <= N) {
+    if (m >= M || n >= nend) continue;
+    const uint4 v = *(const uint4*)(crow(row) + ch);
+    if (n + 8 <= nend) {
       *(uint4*)(C + (int64_t)m * g.ldc + n) = v;
     } else {
       const uint16_t* e = (const uint16_t*)&v;
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (n + k < N) C[(int64_t)m * g.ldc + n + k] = e[k];
+        if (n + k < nend) C[(int64_t)m * g.ldc + n + k] = e[k];
     }
   }
 }
@@ -453,10 +447,19 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big192_kernel(GemmArgs g, in
 namespace {
 // operand shapes the big-tile kernels take
 bool big_ok(const GemmArgs& g) {
-  return !g.w_kn && g.M >= 256 && g.N >= 256 && g.K % GB_BK == 0 && (g.lda & 7) == 0 && (g.ldw & 7) == 0 &&
-         (g.n_split >= g.N || (g.ldw2 & 7) == 0) && (((uintptr_t)g.A | (uintptr_t)g.W | (uintptr_t)g.W2) & 15) == 0;
+  // raw-buffer loads address each operand with 32-bit byte offsets
+  const int64_t lim = (int64_t)1 << 31;
+  const int nsp = g.W2 ? g.n_split : g.N;
+  const bool fits = ((int64_t)(g.M - 1) * g.lda + g.K) * 2 < lim && ((int64_t)(nsp - 1) * g.ldw + g.K) * 2 < lim &&
+                    (!g.W2 || (((int64_t)(g.N - nsp - 1) * g.ldw2 + g.K) * 2 < lim && (nsp & 7) == 0 && nsp < g.N &&
+                               (g.ldw2 & 7) == 0 && ((uintptr_t)g.W2 & 15) == 0));
+  return !g.w_kn && g.M >= 256 && g.N >= 256 && g.K % GB_BK == 0 && (g.lda & 7) == 0 && (g.ldw & 7) == 0 && fits &&
+         (((uintptr_t)g.A | (uintptr_t)g.W) & 15) == 0;
 }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
+int big_tiles_n(const GemmArgs& g, int bn) {
+  return g.W2 ? cdiv(g.n_split, bn) + cdiv(g.N - g.n_split, bn) : cdiv(g.N, bn);
+}
 // tile width: the widest of 256 / 224 / 192 whose tile count fills whole rounds
 // of 256 CUs best (the KV split and split-K use 256)
 int big_bn(const GemmArgs& g) {
@@ -465,14 +468,14 @@ int big_bn(const GemmArgs& g) {
   int best = 256;
   double best_eff = 0;
   for (int bn : {256, 224, 192}) {
-    const int tiles = tm * cdiv(g.N, bn) * g.batch;
-    const double eff = (double)tiles / (cdiv(tiles, 256) * 256.0) * ((double)g.N / (cdiv(g.N, bn) * bn));
+    const int tiles = tm * big_tiles_n(g, bn) * g.batch;
+    const double eff = (double)tiles / (cdiv(tiles, 256) * 256.0) * ((double)g.N / (big_tiles_n(g, bn) * bn));
     if (eff > best_eff + 1e-9) { best_eff = eff; best = bn; }
   }
   return best;
 }
 hipError_t run_big(const GemmArgs& g, int bn, int ny, hipStream_t s) {
-  const int tm = cdiv(g.M, 256), tn = cdiv(g.N, bn);
+  const int tm = cdiv(g.M, 256), tn = big_tiles_n(g, bn);
   const int per_xcd = cdiv(tm * tn, 8);
   const dim3 grid(8 * per_xcd, ny);
   if (bn == 224) gemm_bf16_big224_kernel<<<grid, 256, 0, s>>>(g, tm, tn, per_xcd);
@@ -484,11 +487,11 @@ hipError_t run_big(const GemmArgs& g, int bn, int ny, hipStream_t s) {
 
 int gemm_bf16_splits(const GemmArgs& g) {
   if (!big_ok(g) || g.batch != 1 || (g.N & 3) != 0) return 1;
-  const int tiles = cdiv(g.M, 256) * cdiv(g.N, 256);
+  const int tiles = cdiv(g.M, 256) * big_tiles_n(g, 256);
   if (tiles >= 128) return 1;
   int splits = 256 / tiles;
   const int ksteps = g.K / GB_BK;
-  if (splits > ksteps / 16) splits = ksteps / 16;   // at least 16 steps of 32 per chunk
+  if (splits > ksteps / 8) splits = ksteps / 8;   // at least 8 steps of 64 per chunk
   if (splits < 2) return 1;
   const int per = cdiv(ksteps, splits);
   return cdiv(ksteps, per);   // chunks actually made
