@@ -296,11 +296,16 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
     a.kpe = p.kpe; a.kpe_tp = pad64(T);
     LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(kv)");
   }
-  // q = c_q . Wq_b^T, then RoPE on each head's rotary slice
-  if ((rc = project(wdt, adt, p.cqn, Dq, w->wq_b, w->wq_b_scale, nullptr, nullptr, H * 192, p.q, H * 192, M,
-                    H * 192, Dq, &p, s)))
-    return rc;
-  {
+  // q = c_q . Wq_b^T, then RoPE on each head's rotary slice (in the GEMM's
+  // epilogue on the bf16 path)
+  mla::GemmArgs gr = gemm_args(p.cqn, Dq, w->wq_b, Dq, p.q, H * 192, adt, M, H * 192, Dq);
+  gr.epi = mla::EPI_QROPE; gr.rope = {rope_cos, rope_sin, T};
+  if (wdt == MLA_BF16 && adt == MLA_BF16 && mla::gemm_bf16_qrope_ok(gr)) {
+    LAUNCH(mla::launch_gemm_bf16(gr, s), "gemm_bf16(q_b + RoPE)");
+  } else {
+    if ((rc = project(wdt, adt, p.cqn, Dq, w->wq_b, w->wq_b_scale, nullptr, nullptr, H * 192, p.q, H * 192, M,
+                      H * 192, Dq, &p, s)))
+      return rc;
     mla::NormRopeArgs a = norm_args(p.q, H * 192, p.q, H * 192, adt, M);
     a.rope_off = 128; a.rope_heads = H; a.rope_stride = 192;
     a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = rope_len; a.pos_period = T;

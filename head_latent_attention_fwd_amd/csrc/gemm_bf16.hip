@@ -176,9 +176,10 @@ hipError_t run(const GemmArgs& g, hipStream_t s) {
 // spreads the 16 lanes of every 16-byte operand read over all LDS banks.
 // Within a step the fragments of the next 16-wide sub-step are read between
 // the MFMAs of the current one. In the last sub-step every wave waits for the
-// other stage to land, one barrier retires the stage just consumed, its refill
-// (the step two ahead) is issued, and the first fragments of the other stage
-// are read, all between that sub-step's MFMAs. Tiles are numbered so that each
+// other stage to land, one barrier retires the stage just consumed, and the
+// first fragments of the other stage are read between that sub-step's MFMAs;
+// the refill of the retired stage (the step two ahead) goes out in thirds
+// over that sub-step and the first two of the next step. Tiles are numbered so that each
 // XCD (workgroup id % 8) works on a contiguous, M-grouped block of the output
 // and its L2 serves the shared A/W slabs. Output: bf16 through LDS with
 // 16-byte coalesced stores (row-major or the k_nope / v^T split of kv_b), or
@@ -250,9 +251,11 @@ __device__ __forceinline__ void gemm_bf16_big(const GemmArgs& g, int tiles_m, in
     if (i < 8) voff[i] = (int)(((int64_t)min(m0 + r, M - 1) * g.lda + c * 8) * 2);
     else voff[i] = (int)(((int64_t)(min(n0 + r - BM, nend - 1) - n0) * ldw + c * 8) * 2);
   }
-  auto issue = [&](uint16_t* st, int kt) {
+  // loads i0 <= i < i1 of step kt into stage st
+  auto issue = [&](uint16_t* st, int kt, int i0, int i1) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
+      if (i < i0 || i >= i1) continue;
       auto* lds = (__attribute__((address_space(3))) void*)(st + (4 * i + wv) * 512);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(i < 8 ? rsA : rsW, lds, 16, voff[i], kt * 128, 0, 0);
     }
@@ -287,44 +290,62 @@ __device__ __forceinline__ void gemm_bf16_big(const GemmArgs& g, int tiles_m, in
       for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(fb[buf][j], fa[buf][i], acc[i][j]);
   };
   constexpr int NF = FM + FN, NMMA = FM * FN;
+  // The refill of a stage goes out in thirds: the first after the barrier
+  // that retires it, the other two in the first two sub-steps of the next
+  // step, so the loads never arrive in one burst.
+  constexpr int L1 = LOADS / 3, L2 = 2 * LOADS / 3;
   // one 64-wide step on stage `cur` (kt is the step's index); on return the
   // first fragments of the other stage are in flight to fa/fb[0]
   auto step = [&](uint16_t* cur, uint16_t* nxt, int kt) {
+    const int knext = min(kt + 1, nk - 1);
 #pragma unroll
     for (int kk = 0; kk < 3; ++kk) {
       __builtin_amdgcn_s_waitcnt(gb_wait(63, 0));   // fragments of sub-step kk are in
       __builtin_amdgcn_sched_barrier(0);
+      if (kk == 0) issue(nxt, knext, L1, L2);
+      if (kk == 1) issue(nxt, knext, L2, LOADS);
       read(cur, kk + 1, (kk + 1) & 1);
       mma(kk & 1);
+      if (kk < 2) {
+        constexpr int NL = L2 - L1 > LOADS - L2 ? L2 - L1 : LOADS - L2;
 #pragma unroll
-      for (int u = 0; u < NF; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        for (int u = 0; u < NMMA; ++u) {
+          if (u < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (u < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < NF; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NMMA - NF, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, NMMA - NF, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     // every fragment of `cur` is in registers and the other stage has landed
-    // (its loads are the only ones in flight): retire `cur`, refill it with the
-    // step two ahead (clamped: a repeated last step is loaded and ignored)
+    // (its loads are the only ones in flight): retire `cur` and start its
+    // refill with the step two ahead (clamped: a repeated last step is loaded
+    // and ignored)
     __builtin_amdgcn_s_waitcnt(gb_wait(0, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue(cur, min(kt + 2, nk - 1));
+    issue(cur, min(kt + 2, nk - 1), 0, L1);
     read(nxt, 0, 0);
     mma(1);
 #pragma unroll
     for (int u = 0; u < NMMA; ++u) {
-      if (u < LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (u < L1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (u < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  issue(s0, 0);
-  issue(s1, min(1, nk - 1));
-  __builtin_amdgcn_s_waitcnt(gb_wait(LOADS, 15));   // step 0 has landed
+  issue(s0, 0, 0, LOADS);
+  issue(s1, min(1, nk - 1), 0, L1);
+  __builtin_amdgcn_s_waitcnt(gb_wait(L1, 15));   // step 0 has landed
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   read(s0, 0, 0);
@@ -372,6 +393,29 @@ __device__ __forceinline__ void gemm_bf16_big(const GemmArgs& g, int tiles_m, in
       __builtin_amdgcn_wave_barrier();
     }
     return;
+  }
+  if constexpr (BN == 192 && WN == 2 && FN == 3) {
+    // q_b with RoPE: the tile is one head; the waves with wn = 1 hold its
+    // columns 96..191, block j = 1 is the first rotary half (128 + d) and
+    // j = 2 the second (160 + d), d = 8 rg + 4 hi + e, in the same registers
+    if (g.epi == EPI_QROPE && wn == 1) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = min(m0 + wm * FM * 32 + i * 32 + l32, M - 1), t = m % g.rope.T;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const float4 c = *(const float4*)&g.rope.cos[t * 32 + 8 * rg + 4 * hi];
+          const float4 sn = *(const float4*)&g.rope.sin[t * 32 + 8 * rg + 4 * hi];
+          const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x1 = acc[i][1][4 * rg + e], x2 = acc[i][2][4 * rg + e];
+            acc[i][1][4 * rg + e] = x1 * cc[e] - x2 * ss[e];
+            acc[i][2][4 * rg + e] = x2 * cc[e] + x1 * ss[e];
+          }
+        }
+      }
+    }
   }
   // Epilogue through LDS: the bf16 C tile is staged row-major (8-byte writes
   // of 4 consecutive columns; rows 0..127 in stage 0, 128..255 in stage 1),
@@ -497,7 +541,14 @@ int gemm_bf16_splits(const GemmArgs& g) {
   return cdiv(ksteps, per);   // chunks actually made
 }
 
+bool gemm_bf16_qrope_ok(const GemmArgs& g) {
+  return big_ok(g) && !g.W2 && g.batch == 1 && g.k_splits <= 1 && g.c_dtype == DT_BF16 && g.N % 192 == 0 &&
+         (g.ldc & 7) == 0 && (((uintptr_t)g.C) & 15) == 0 && g.rope.cos && g.rope.sin && g.rope.T > 0 &&
+         (((uintptr_t)g.rope.cos | (uintptr_t)g.rope.sin) & 15) == 0;
+}
+
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
+  if (g.epi == EPI_QROPE) return gemm_bf16_qrope_ok(g) ? run_big(g, 192, 1, s) : hipErrorInvalidValue;
   if (g.w_kn) return run<128, 128, 2, 2, true>(g, s);
   if (g.k_splits > 1) {   // the caller sized part[] from gemm_bf16_splits
     if (!big_ok(g) || g.batch != 1 || !g.part || g.k_splits != gemm_bf16_splits(g)) return hipErrorInvalidValue;

@@ -14,9 +14,14 @@ enum { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
 // Epilogues: EPI_ROWMAJOR writes C[m, n] (ldc). EPI_KV_SPLIT treats the
 // N = H*256 columns as per-head [k_nope 128 | v 128] and rows m = b*T + t, and
 // writes k_nope to C = KN [B, H, Tp, 128] and v transposed to C2 = VT [B, H, 128, Tp].
-enum { EPI_ROWMAJOR = 0, EPI_KV_SPLIT = 1 };
+// EPI_QROPE (bf16 big-tile path, N = H*192): row-major C with RoPE applied to
+// columns 128..191 of every 192-wide head (pairs (d, d + 32), position m % T).
+enum { EPI_ROWMAJOR = 0, EPI_KV_SPLIT = 1, EPI_QROPE = 2 };
 struct KvSplit {
   void* vt; int T, Tp, H;
+};
+struct RopeEpi {
+  const float* cos; const float* sin; int T;
 };
 struct GemmArgs {
   const void* A; int64_t lda; int64_t batch_a;
@@ -25,7 +30,7 @@ struct GemmArgs {
   void* C; int64_t ldc; int64_t batch_c; int c_dtype;
   int M, N, K, batch;
   bool w_kn;
-  int epi; KvSplit kv;
+  int epi; KvSplit kv; RopeEpi rope;
   // split-K (batch == 1, big-tile path only): part[s][M][N] fp32 partial sums
   // of K chunk s; C is not written
   int k_splits; float* part;
@@ -43,6 +48,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
 // Number of K chunks the big-tile path would use for this shape (1 = no split;
 // a split is worth it when the output has too few 256x256 tiles to fill the chip).
 int gemm_bf16_splits(const GemmArgs& g);
+// whether launch_gemm_bf16 takes g with epi = EPI_QROPE
+bool gemm_bf16_qrope_ok(const GemmArgs& g);
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s);
 
 // Block-scaled e4m3 GEMM. W2/w2_scale as in GemmArgs (n_split multiple of 128).
