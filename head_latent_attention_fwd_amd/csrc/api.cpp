@@ -166,6 +166,14 @@ mla::NormRopeArgs norm_args(const void* in, int64_t ld_in, void* out, int64_t ld
   return a;
 }
 
+// operand shapes and alignments the fused q / kv norm kernel takes
+bool qkv_norm_ok(const mla::QkvNormArgs& a) {
+  const uintptr_t al = (uintptr_t)a.in | (uintptr_t)a.gq | (uintptr_t)a.gkv;
+  const uintptr_t al8 = (uintptr_t)a.q_out | (uintptr_t)a.kv_out;
+  return (al & 15) == 0 && (al8 & 7) == 0 && a.Dq % 4 == 0 && a.L % 4 == 0 && a.ld_in % 4 == 0 &&
+         (a.Dq + a.L + 64) / 4 <= 1024 && a.in_splits <= 64 && (a.split_stride % 4) == 0;
+}
+
 // y[M, N] = act[M, K] . W^T for the path's weight format; fp8 quantises act first.
 // With kv != nullptr the output goes through the k_nope / v^T split epilogue.
 int project(int wdt, int adt, const void* act, int64_t lda, const void* W, const float* Ws,
@@ -281,6 +289,16 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
     if (!qkv_split) return;
     a.in_dtype = MLA_F32; a.in_splits = p.qkv_splits; a.split_stride = (int64_t)M * NQKV;
   };
+  mla::QkvNormArgs qa{};
+  qa.in = qkv_in; qa.ld_in = NQKV; qa.in_dtype = qkv_split ? MLA_F32 : adt;
+  qa.in_splits = qkv_split ? p.qkv_splits : 1; qa.split_stride = (int64_t)M * NQKV;
+  qa.rows = M; qa.Dq = Dq; qa.L = L; qa.gq = w->q_norm_w; qa.gkv = w->kv_norm_w; qa.eps = d->rms_eps;
+  qa.q_out = p.cqn; qa.ld_q = Dq; qa.kv_out = kvc; qa.ld_kv = L + 64;
+  qa.kpe = p.kpe; qa.kpe_tp = pad64(T);
+  qa.cos_tab = rope_cos; qa.sin_tab = rope_sin; qa.rope_len = rope_len; qa.pos_period = T;
+  if (adt == MLA_BF16 && qkv_norm_ok(qa)) {
+    LAUNCH(mla::launch_qkv_norm(qa, s), "qkv_norm");
+  } else {
   {  // q_norm
     mla::NormRopeArgs a = norm_args(qkv_in, NQKV, p.cqn, Dq, adt, M);
     from_qkv(a);
@@ -295,6 +313,7 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
     a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = rope_len; a.pos_period = T;
     a.kpe = p.kpe; a.kpe_tp = pad64(T);
     LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(kv)");
+  }
   }
   // q = c_q . Wq_b^T, then RoPE on each head's rotary slice (in the GEMM's
   // epilogue on the bf16 path)
@@ -362,21 +381,15 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B
                    DEC_SPLIT_QKV, s)))
     return rc;
   const int splits_qkv = skinny_splits(dim, DEC_SPLIT_QKV);
-  {
-    mla::NormRopeArgs a = norm_args(part, NQKV, p.cqn, Dq, MLA_F32, B);
-    a.out_dtype = MLA_BF16; a.in_splits = splits_qkv; a.split_stride = (int64_t)B * NQKV;
-    a.norm_dim = Dq; a.gamma = w->q_norm_w; a.eps = d->rms_eps;
-    LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm(q)");
-  }
-  {
-    // the normalised latent and rotated k_pe land directly in cache row cache_len[b]
-    mla::NormRopeArgs a = norm_args(part + Dq, NQKV, kv_cache, (int64_t)max_len * (L + 64), MLA_F32, B);
-    a.out_dtype = MLA_BF16; a.in_splits = splits_qkv; a.split_stride = (int64_t)B * NQKV;
-    a.norm_dim = L; a.gamma = w->kv_norm_w; a.eps = d->rms_eps;
-    a.rope_off = L; a.rope_heads = 1; a.rope_stride = 64;
+  {  // q_norm, kv_norm and RoPE of k_pe; the new [latent | k_pe] lands directly in cache row cache_len[b]
+    mla::QkvNormArgs a{};
+    a.in = part; a.ld_in = NQKV; a.in_dtype = MLA_F32; a.in_splits = splits_qkv; a.split_stride = (int64_t)B * NQKV;
+    a.rows = B; a.Dq = Dq; a.L = L; a.gq = w->q_norm_w; a.gkv = w->kv_norm_w; a.eps = d->rms_eps;
+    a.q_out = p.cqn; a.ld_q = Dq;
+    a.kv_out = kv_cache; a.ld_kv = (int64_t)max_len * (L + 64); a.kv_pos_stride = L + 64; a.kv_pos_max = max_len;
     a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = max_len; a.pos = cache_len;
-    a.out_pos_stride = L + 64; a.out_pos_max = max_len;
-    LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(kv) -> cache");
+    if (!qkv_norm_ok(a)) return fail(MLA_UNSUPPORTED, "decode needs 16-byte aligned norm weights and cache");
+    LAUNCH(mla::launch_qkv_norm(a, s), "qkv_norm -> cache");
   }
   // q = c_q . Wq_b^T
   if ((rc = skinny(p.cqn, Dq, 0, w->wq_b, Dq, 0, nullptr, 0, H * 192, p.q, H * 192, 0, nullptr, B, H * 192, Dq, 1, 64,

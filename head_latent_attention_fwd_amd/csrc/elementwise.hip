@@ -61,13 +61,7 @@ constexpr int NORM_PT = 8;
 __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(NormRopeArgs a, int rope_len) {
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x;
-  const int64_t ib = (int64_t)row * a.ld_in;
-  int64_t ob = (int64_t)row * a.ld_out;
-  if (a.out_pos_stride > 0) {
-    const int P = a.pos[row];
-    if (P < 0 || P >= a.out_pos_max) return;
-    ob += (int64_t)P * a.out_pos_stride;
-  }
+  const int64_t ib = (int64_t)row * a.ld_in, ob = (int64_t)row * a.ld_out;
   if (a.norm_dim > 0 && a.norm_dim <= 256 * NORM_PT) {
     // the row stays in registers: one read of the input (and its partials)
     float v[NORM_PT];
@@ -114,6 +108,97 @@ __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(NormRopeArgs a, int r
         st(a.kpe, a.out_dtype, kb, y1);
         st(a.kpe, a.out_dtype, kb + 32, y2);
       }
+    }
+  }
+}
+
+// The two RMSNorms of a down-projection row and the RoPE of its k_pe; one
+// 256-thread block per row, 4 consecutive elements per thread-chunk (16-byte
+// fp32 / 8-byte bf16 accesses), both sums of squares in one block reduction.
+constexpr int QKV_CH = 4;   // chunks of 4 per thread: rows up to 4096 wide
+__global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
+  __shared__ float red[2][4];
+  __shared__ float kpe_s[64];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nq = a.Dq >> 2, nkv = a.L >> 2, nch = nq + nkv + 16;
+  float4 v[QKV_CH];
+  float sq = 0.f, skv = 0.f;
+#pragma unroll
+  for (int j = 0; j < QKV_CH; ++j) {
+    const int c = tid + 256 * j;
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < nch) {
+      const int64_t i = (int64_t)row * a.ld_in + 4 * c;
+      if (a.in_dtype == DT_F32) {
+        const float* p = (const float*)a.in + i;
+        float4 t[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          if (s < a.in_splits) t[s] = *(const float4*)(p + (int64_t)s * a.split_stride);
+        x = t[0];
+#pragma unroll
+        for (int s = 1; s < 8; ++s)
+          if (s < a.in_splits) { x.x += t[s].x; x.y += t[s].y; x.z += t[s].z; x.w += t[s].w; }
+        for (int s = 8; s < a.in_splits; ++s) {
+          const float4 u = *(const float4*)(p + (int64_t)s * a.split_stride);
+          x.x += u.x; x.y += u.y; x.z += u.z; x.w += u.w;
+        }
+      } else {
+        const uint2 u = *(const uint2*)((const uint16_t*)a.in + i);
+        x = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+      }
+      const float q2 = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+      if (c < nq) sq += q2;
+      else if (c < nq + nkv) skv += q2;
+      else *(float4*)&kpe_s[4 * (c - nq - nkv)] = x;
+    }
+    v[j] = x;
+  }
+  sq = wave_sum(sq);
+  skv = wave_sum(skv);
+  if (lane == 0) { red[0][wave] = sq; red[1][wave] = skv; }
+  __syncthreads();
+  sq = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  skv = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const float rq = 1.0f / sqrtf(sq / (float)a.Dq + a.eps), rkv = 1.0f / sqrtf(skv / (float)a.L + a.eps);
+  const int P = a.pos ? a.pos[row] : row % a.pos_period;
+  uint16_t* kv = nullptr;
+  if (a.kv_pos_stride > 0) {
+    if (P >= 0 && P < a.kv_pos_max) kv = (uint16_t*)a.kv_out + (int64_t)row * a.ld_kv + (int64_t)P * a.kv_pos_stride;
+  } else {
+    kv = (uint16_t*)a.kv_out + (int64_t)row * a.ld_kv;
+  }
+  uint16_t* q = (uint16_t*)a.q_out + (int64_t)row * a.ld_q;
+#pragma unroll
+  for (int j = 0; j < QKV_CH; ++j) {
+    const int c = tid + 256 * j;
+    if (c < nq) {
+      const float4 g = *(const float4*)&a.gq[4 * c];
+      *(uint2*)(q + 4 * c) = make_uint2(pack_bf16x2(g.x * (v[j].x * rq), g.y * (v[j].y * rq)),
+                                        pack_bf16x2(g.z * (v[j].z * rq), g.w * (v[j].w * rq)));
+    } else if (c < nq + nkv && kv) {
+      const int e = 4 * (c - nq);
+      const float4 g = *(const float4*)&a.gkv[e];
+      *(uint2*)(kv + e) = make_uint2(pack_bf16x2(g.x * (v[j].x * rkv), g.y * (v[j].y * rkv)),
+                                     pack_bf16x2(g.z * (v[j].z * rkv), g.w * (v[j].w * rkv)));
+    }
+  }
+  if (tid < 32) {
+    const int d = tid;
+    const bool ok = P >= 0 && P < a.rope_len;
+    const float c = ok ? a.cos_tab[P * 32 + d] : 0.f, sn = ok ? a.sin_tab[P * 32 + d] : 0.f;
+    const float x1 = kpe_s[d], x2 = kpe_s[d + 32];
+    const float y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
+    if (kv) {
+      kv[a.L + d] = f2bf(y1);
+      kv[a.L + d + 32] = f2bf(y2);
+    }
+    if (a.kpe) {
+      const int bb = row / a.pos_period, t = row - bb * a.pos_period;
+      uint16_t* kp = (uint16_t*)a.kpe + ((int64_t)bb * a.kpe_tp + t) * 64;
+      kp[d] = f2bf(y1);
+      kp[d + 32] = f2bf(y2);
     }
   }
 }
@@ -209,6 +294,16 @@ hipError_t launch_rmsnorm_rope(const NormRopeArgs& a, hipStream_t s) {
   // give zero rotations instead of reading past it.
   if (a.rows <= 0) return hipSuccess;
   rmsnorm_rope_kernel<<<a.rows, 256, 0, s>>>(a, a.rope_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_norm(const QkvNormArgs& a, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  if ((a.Dq & 3) || (a.L & 3) || (a.ld_in & 3) || (a.Dq + a.L + 64) / 4 > 256 * QKV_CH ||
+      (a.in_dtype != DT_F32 && a.in_dtype != DT_BF16) || (a.in_dtype == DT_F32 && (a.split_stride & 3)) ||
+      (a.ld_q & 3) || (a.ld_kv & 3) || (a.kv_pos_stride & 3) || a.in_splits < 1 || (!a.pos && a.pos_period <= 0))
+    return hipErrorInvalidValue;
+  qkv_norm_kernel<<<a.rows, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

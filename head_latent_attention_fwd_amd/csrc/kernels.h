@@ -91,11 +91,27 @@ struct NormRopeArgs {
   // in_splits > 1: the input is the sum of in_splits fp32 partial arrays
   // split_stride elements apart (split-K GEMM output)
   int in_splits; int64_t split_stride;
-  // out_pos_stride > 0: output row m starts at out + m*ld_out + pos[m]*out_pos_stride
-  // (a cache append) and rows whose pos is outside [0, out_pos_max) are not written
-  int64_t out_pos_stride; int out_pos_max;
 };
 hipError_t launch_rmsnorm_rope(const NormRopeArgs& a, hipStream_t s);
+// Both RMSNorms of a down-projection row [c_q (Dq) | latent (L) | k_pe (64)]
+// and the RoPE of k_pe in one pass (bf16 outputs): q_out[m] = norm(c_q),
+// kv_out[m] = [norm(latent) | RoPE(k_pe)]. The input is bf16 or the sum of
+// in_splits fp32 partial arrays split_stride elements apart (split order).
+// kv_pos_stride > 0: the kv row goes to kv_out + m*ld_kv + pos[m]*kv_pos_stride
+// and is skipped when pos[m] is outside [0, kv_pos_max) (a cache append).
+// Position of row m: pos[m], else m % pos_period. Needs Dq, L, ld_in multiples
+// of 4 and (Dq + L + 64) / 4 <= 1024.
+struct QkvNormArgs {
+  const void* in; int64_t ld_in; int in_dtype; int in_splits; int64_t split_stride;
+  int rows, Dq, L;
+  const float* gq; const float* gkv; float eps;
+  void* q_out; int64_t ld_q;
+  void* kv_out; int64_t ld_kv; int64_t kv_pos_stride; int kv_pos_max;
+  void* kpe; int kpe_tp;   // optional copy of the rotated k_pe: row m = b*T + t -> kpe[(b*kpe_tp + t)*64]
+  const float* cos_tab; const float* sin_tab; int rope_len;
+  const int32_t* pos; int pos_period;
+};
+hipError_t launch_qkv_norm(const QkvNormArgs& a, hipStream_t s);
 hipError_t launch_rope_table(float* c, float* sn, int n_pos, float base, hipStream_t s);
 hipError_t launch_quant_1x128(const void* a, int64_t lda, int a_dtype, int M, int K,
                               uint8_t* q, float* scales, hipStream_t s);
