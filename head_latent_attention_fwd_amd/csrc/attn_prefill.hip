@@ -9,8 +9,9 @@
 // kv_b GEMM's epilogue) and the shared rotary key [B, Tp, 64].
 //
 // Work split: one 256-thread workgroup per (128-query tile, head, sequence);
-// the query tiles of one (sequence, head) run on one XCD, heaviest (last)
-// first; wave w owns queries [32w, 32w+32).
+// the query tiles of one (sequence, head) run on one XCD, and workgroups start
+// heaviest (last query tile) first across all pairs of that XCD; wave w owns
+// queries [32w, 32w+32).
 // Scores are formed transposed, S^T = K . Q^T, on v_mfma_f32_32x32x16_bf16 so
 // a lane holds 32 keys of one query: the running max needs one exchange
 // (lane ^ 32) and the running sum stays lane-local; the bf16 probabilities are
@@ -52,13 +53,14 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   const int T = a.T, Tp = a.Tp, H = a.H;
   // XCD-aware order: workgroup id % 8 is the XCD, and each XCD takes whole
   // (sequence, head) pairs, so the query tiles that re-read one head's keys
-  // and values share that XCD's L2; within a pair the longest (last) query
-  // tiles start first.
-  const int nq = (T + BQ - 1) / BQ;
+  // and values share that XCD's L2. Workgroups start in order of decreasing
+  // work (the last query tiles of every pair on the XCD first), which keeps
+  // the causal triangle from leaving CUs idle at the end.
+  const int nq = (T + BQ - 1) / BQ, ppx = (a.B * H + 7) / 8;
   const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
-  const int pair = (loc / nq) * 8 + xcd;
+  const int pair = (loc % ppx) * 8 + xcd;
   if (pair >= a.B * H) return;
-  const int qt = nq - 1 - loc % nq;
+  const int qt = nq - 1 - loc / ppx;
   const int h = pair % H, b = pair / H;
   const int64_t bh = (int64_t)b * H + h;
   const int q0 = qt * BQ, qw = q0 + wave * 32;

@@ -34,14 +34,14 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// word 3 of a gfx9 raw-buffer descriptor (32-bit data format, no swizzle, no stride)
+constexpr int BUF_DW3 = 0x00020000;
+
 // 32x32x16 bf16 MFMA: D[i][j] += sum_k A[i][k] B[k][j]. Lane l supplies row
 // (l % 32) of A and column (l % 32) of B, each with 8 k values; the k values
 // a lane supplies are the same set for A and B, so any consistent assignment
 // of logical k to (lane / 32, slot) gives the full sum. Result: lane l holds
 // column (l % 32), rows 8*(r/4) + 4*(l/32) + (r%4) for r = 0..15.
-// word 3 of a gfx9 raw-buffer descriptor (32-bit data format, no swizzle, no stride)
-constexpr int BUF_DW3 = 0x00020000;
-
 __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -394,29 +394,6 @@ __device__ __forceinline__ void gemm_bf16_big(const GemmArgs& g, int tiles_m, in
     }
     return;
   }
-  if constexpr (BN == 192 && WN == 2 && FN == 3) {
-    // q_b with RoPE: the tile is one head; the waves with wn = 1 hold its
-    // columns 96..191, block j = 1 is the first rotary half (128 + d) and
-    // j = 2 the second (160 + d), d = 8 rg + 4 hi + e, in the same registers
-    if (g.epi == EPI_QROPE && wn == 1) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int m = min(m0 + wm * FM * 32 + i * 32 + l32, M - 1), t = m % g.rope.T;
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const float4 c = *(const float4*)&g.rope.cos[t * 32 + 8 * rg + 4 * hi];
-          const float4 sn = *(const float4*)&g.rope.sin[t * 32 + 8 * rg + 4 * hi];
-          const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x1 = acc[i][1][4 * rg + e], x2 = acc[i][2][4 * rg + e];
-            acc[i][1][4 * rg + e] = x1 * cc[e] - x2 * ss[e];
-            acc[i][2][4 * rg + e] = x2 * cc[e] + x1 * ss[e];
-          }
-        }
-      }
-    }
-  }
   // Epilogue through LDS: the bf16 C tile is staged row-major (8-byte writes
   // of 4 consecutive columns; rows 0..127 in stage 0, 128..255 in stage 1),
   // then stored in 16-byte pieces.
@@ -433,6 +410,38 @@ __device__ __forceinline__ void gemm_bf16_big(const GemmArgs& g, int tiles_m, in
                                               pack_bf16x2(acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]));
       }
     }
+  if (BN == 192 && g.epi == EPI_QROPE) {
+    // q_b with RoPE: the tile is one head, columns 128 + d and 160 + d
+    // (d < 32) are the rotated pairs. Thread r rotates row r of the staged
+    // tile in place; the table row of its position m % T is fetched in one
+    // batch of loads while the staging completes.
+    const int m = min(m0 + tid, M - 1), t = m % g.rope.T;
+    float4 cs[8], sn[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      cs[q] = *(const float4*)&g.rope.cos[t * 32 + 4 * q];
+      sn[q] = *(const float4*)&g.rope.sin[t * 32 + 4 * q];
+    }
+    __syncthreads();
+    uint16_t* r = crow(tid);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint4 a = *(const uint4*)(r + 128 + 8 * q), b = *(const uint4*)(r + 160 + 8 * q);
+      uint16_t* ae = (uint16_t*)&a;
+      uint16_t* be = (uint16_t*)&b;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float4 c4 = cs[2 * q + (e >> 2)], s4 = sn[2 * q + (e >> 2)];
+        const float c = (e & 3) == 0 ? c4.x : (e & 3) == 1 ? c4.y : (e & 3) == 2 ? c4.z : c4.w;
+        const float sv = (e & 3) == 0 ? s4.x : (e & 3) == 1 ? s4.y : (e & 3) == 2 ? s4.z : s4.w;
+        const float x1 = bf2f(ae[e]), x2 = bf2f(be[e]);
+        ae[e] = f2bf(x1 * c - x2 * sv);
+        be[e] = f2bf(x2 * c + x1 * sv);
+      }
+      *(uint4*)(r + 128 + 8 * q) = a;
+      *(uint4*)(r + 160 + 8 * q) = b;
+    }
+  }
   __syncthreads();
   uint16_t* C = (uint16_t*)g.C + (int64_t)z * g.batch_c;
   if (BN == 256 && g.epi == EPI_KV_SPLIT) {
