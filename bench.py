@@ -93,14 +93,18 @@ def event_avg(fn, reps, warmup=2, flush=None):
 
 
 class Flusher:
-    """Writes 1 GiB so that the 256 MB MALL and the L2s hold nothing of the step."""
+    """Reads 1 GiB so that the 256 MB MALL and the L2s hold nothing of the step.
+    A read, not a write: a write would leave dirty lines whose write-back then
+    competes with the step's own reads, which a model's other layers (mostly
+    weight reads) would not cause."""
 
     def __init__(self):
         import torch
-        self.buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
 
     def __call__(self):
-        self.buf.fill_(1)
+        self.sink = self.buf.sum()
 
 
 def source_hash(*names):
@@ -201,7 +205,7 @@ def bench_decode(cfg_index, steps, warmup, kernels=False):
     sec = event_avg(run.run, steps, warmup=warmup, flush=flush)   # cache slot P is rewritten identically each step
     res = {"workload": cfg["name"], "B": cfg["B"], "cache_len": cfg["cache_len"], "n_heads": cfg["n_heads"],
            "us_per_step": sec * 1e6, "gbps": nbytes / sec / 1e9, "frac_of_hbm": nbytes / sec / 1e9 / PEAK["hbm"],
-           "algorithmic_bytes": nbytes, "bytes": parts, "timing": "HIP events per step, 1 GiB MALL flush between steps"}
+           "algorithmic_bytes": nbytes, "bytes": parts, "timing": "HIP events per step, 1 GiB read between steps (caches hold nothing of the step)"}
     if kernels:
         B, H = cfg["B"], cfg["n_heads"]
         ql = torch.randn((B, H, 576), device="cuda").to(torch.bfloat16)
