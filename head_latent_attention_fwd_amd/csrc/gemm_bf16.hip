@@ -536,19 +536,31 @@ hipError_t run_big(const GemmArgs& g, int bn, int ny, hipStream_t s) {
   else gemm_bf16_big256_kernel<<<grid, 256, 0, s>>>(g, tm, tn, per_xcd);
   return hipGetLastError();
 }
+
+// Split-K plan for outputs with too few tiles for the chip: the tile width
+// and chunk count whose workgroups fill the most of one round of 256 CUs
+// (counting padded columns as waste), at least 8 steps of 64 per chunk.
+struct SplitPlan { int bn, splits; };
+SplitPlan split_plan(const GemmArgs& g) {
+  SplitPlan best{256, 1};
+  if (!big_ok(g) || g.batch != 1 || (g.N & 3) != 0 || g.epi == EPI_KV_SPLIT) return best;
+  const int tm = cdiv(g.M, 256), ksteps = g.K / GB_BK;
+  double best_eff = 0;
+  for (int bn : {256, 224, 192}) {
+    const int tiles = tm * big_tiles_n(g, bn);
+    if (tiles >= 128) continue;
+    int splits = 256 / tiles;
+    if (splits > ksteps / 8) splits = ksteps / 8;
+    if (splits < 2) continue;
+    splits = cdiv(ksteps, cdiv(ksteps, splits));   // chunks actually made
+    const double eff = (double)tiles * splits / 256.0 * ((double)g.N / (big_tiles_n(g, bn) * bn));
+    if (eff > best_eff + 1e-9) { best_eff = eff; best = {bn, splits}; }
+  }
+  return best;
+}
 }  // namespace
 
-int gemm_bf16_splits(const GemmArgs& g) {
-  if (!big_ok(g) || g.batch != 1 || (g.N & 3) != 0) return 1;
-  const int tiles = cdiv(g.M, 256) * big_tiles_n(g, 256);
-  if (tiles >= 128) return 1;
-  int splits = 256 / tiles;
-  const int ksteps = g.K / GB_BK;
-  if (splits > ksteps / 8) splits = ksteps / 8;   // at least 8 steps of 64 per chunk
-  if (splits < 2) return 1;
-  const int per = cdiv(ksteps, splits);
-  return cdiv(ksteps, per);   // chunks actually made
-}
+int gemm_bf16_splits(const GemmArgs& g) { return split_plan(g).splits; }
 
 bool gemm_bf16_qrope_ok(const GemmArgs& g) {
   return big_ok(g) && !g.W2 && g.batch == 1 && g.k_splits <= 1 && g.c_dtype == DT_BF16 && g.N % 192 == 0 &&
@@ -561,7 +573,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
   if (g.w_kn) return run<128, 128, 2, 2, true>(g, s);
   if (g.k_splits > 1) {   // the caller sized part[] from gemm_bf16_splits
     if (!big_ok(g) || g.batch != 1 || !g.part || g.k_splits != gemm_bf16_splits(g)) return hipErrorInvalidValue;
-    return run_big(g, 256, g.k_splits, s);
+    return run_big(g, split_plan(g).bn, g.k_splits, s);
   }
   // bf16 output, 16-byte aligned rows (the KV split needs N % 256 == 0, true for H*256)
   const bool c_ok = g.c_dtype == DT_BF16 && (((uintptr_t)g.C) & 15) == 0 &&
