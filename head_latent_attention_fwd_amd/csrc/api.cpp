@@ -538,6 +538,7 @@ int mla_quant_e4m3_1x128(const void* a, int64_t lda, int32_t a_dtype, int32_t M,
   if (M < 0 || K <= 0 || lda < K) return fail(MLA_INVALID_ARG, "bad sizes");
   if (K % 128) return fail(MLA_UNSUPPORTED, "K must be a multiple of 128");
   if (a_dtype != MLA_F32 && a_dtype != MLA_BF16) return fail(MLA_UNSUPPORTED, "a_dtype must be F32 or BF16");
+  if (lda % 8 || (((uintptr_t)a | (uintptr_t)q) & 15)) return fail(MLA_UNSUPPORTED, "need lda % 8 == 0 and 16-byte aligned a, q");
   LAUNCH(mla::launch_quant_1x128(a, lda, a_dtype, M, K, q, scales, (hipStream_t)stream), "quant_e4m3_1x128");
   return MLA_OK;
 }

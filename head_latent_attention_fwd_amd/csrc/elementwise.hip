@@ -230,20 +230,45 @@ __device__ __forceinline__ uint32_t to_e4m3x2(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
-// One wave per (row, 128-group): s = amax/448, q = e4m3(x / s).
+// 16 lanes per (row, 128-group), 8 consecutive values per lane: s = amax/448,
+// q = e4m3(x / s) (fp32 quotient, round to nearest even, saturating). A
+// 256-thread block covers 16 groups of one row.
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* a, int64_t lda, int dt, int M, int K,
                                                           uint8_t* q, float* scales) {
-  const int G = K / 128;
-  const int g = blockIdx.x * 4 + (threadIdx.x >> 6), m = blockIdx.y, lane = threadIdx.x & 63;
-  if (g >= G) return;
-  const int64_t base = (int64_t)m * lda + g * 128 + lane * 2;
-  const float v0 = ld(a, dt, base), v1 = ld(a, dt, base + 1);
-  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  const int G = K / 128, tid = threadIdx.x;
+  const int g = blockIdx.x * 16 + (tid >> 4), m = blockIdx.y, sub = tid & 15;
+  if (g >= G) return;   // whole 16-lane groups leave together
+  const int64_t base = (int64_t)m * lda + g * 128 + sub * 8;
+  float v[8];
+  if (dt == DT_F32) {
+    const float4 x0 = *(const float4*)((const float*)a + base), x1 = *(const float4*)((const float*)a + base + 4);
+    v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w; v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+  } else {
+    const uint4 u = *(const uint4*)((const uint16_t*)a + base);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = __uint_as_float(w[e] << 16);
+      v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));   // within the 16 lanes
   const float s = amax / 448.0f;
-  uint32_t code = 0;
-  if (s != 0.f) code = to_e4m3x2(v0 / s, v1 / s);
-  *(uint16_t*)(q + (int64_t)m * K + g * 128 + lane * 2) = (uint16_t)code;
-  if (lane == 0) scales[(int64_t)m * G + g] = s;
+  uint2 code = make_uint2(0u, 0u);
+  if (s != 0.f) {
+    code.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2] / s, v[3] / s,
+                                                        __builtin_amdgcn_cvt_pk_fp8_f32(v[0] / s, v[1] / s, 0, false),
+                                                        true);
+    code.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[6] / s, v[7] / s,
+                                                        __builtin_amdgcn_cvt_pk_fp8_f32(v[4] / s, v[5] / s, 0, false),
+                                                        true);
+  }
+  *(uint2*)(q + (int64_t)m * K + g * 128 + sub * 8) = code;
+  if (sub == 0) scales[(int64_t)m * G + g] = s;
 }
 
 // One block per 128x128 weight block.
@@ -326,7 +351,8 @@ hipError_t launch_rope_table(float* c, float* sn, int n_pos, float base, hipStre
 hipError_t launch_quant_1x128(const void* a, int64_t lda, int a_dtype, int M, int K, uint8_t* q, float* scales,
                               hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  dim3 grid((K / 128 + 3) / 4, M);
+  if ((lda & 7) || (((uintptr_t)a | (uintptr_t)q) & 15)) return hipErrorInvalidValue;   // 16-byte row pieces
+  dim3 grid((K / 128 + 15) / 16, M);
   quant_1x128_kernel<<<grid, 256, 0, s>>>(a, lda, a_dtype, M, K, q, scales);
   return hipGetLastError();
 }

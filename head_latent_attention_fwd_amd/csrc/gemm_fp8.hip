@@ -162,9 +162,224 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmFp8Args g) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large-shape kernel: 256 x 256 tiles, eight waves as 4 x 2, each a 64 x 128
+// block of v_mfma_f32_32x32x64_f8f6f4 results (W as the first operand, so a
+// lane holds one output row and 4 consecutive columns per block row group).
+// A wave's 128 columns are one weight-scale block, so the promotion scale of
+// a lane's row in group g is one number s_g = a_scale[m, g] * w_scale[blk, g].
+// Instead of a second accumulator per group, the running sum is kept in units
+// of the latest scale: before group g's MFMAs it is multiplied by
+// s_{g-1} / s_g, and the final sum by s_last, which telescopes to
+// sum_g s_g P_g. A group with s_g = 0 has all-zero codes and leaves the sum
+// and the running scale unchanged. The accumulators stay in VGPRs for that
+// multiply; two waves per SIMD hide each other's LDS and MFMA latencies.
+// K moves one 128-wide scale group per step through two LDS stages (64 KB
+// each: 256 A rows then 256 W rows of 128 bytes, 16-byte chunks swizzled by
+// (row >> 1) & 7) filled by 16-byte raw-buffer loads straight into LDS.
+// Column tiles never straddle n_split (multiple of 128); output bf16 through
+// LDS (row-major or the k_nope / v^T split).
+constexpr int FB_BK = 128;                   // bytes of K per step (one scale group)
+constexpr int FB_STAGE = 512 * FB_BK;        // bytes per stage
+constexpr int FB_CP = 256 + 8;               // bf16 C-tile pitch (elements)
+constexpr int FB_HALF = FB_STAGE > 128 * FB_CP * 2 ? FB_STAGE : 128 * FB_CP * 2;   // bytes per LDS array
+constexpr int FB_GROUP_M = 8;
+
+__device__ __forceinline__ int fb_sw(int row) { return (row >> 1) & 7; }
+constexpr int fb_wait(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8); }
+
+__global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int tiles_m, int tiles_n, int per_xcd) {
+  __shared__ __attribute__((aligned(16))) uint8_t s0[FB_HALF];
+  __shared__ __attribute__((aligned(16))) uint8_t s1[FB_HALF];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wv >> 1, wn = wv & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+  const int t = xcd * per_xcd + loc, ntile = tiles_m * tiles_n;
+  if (loc >= per_xcd || t >= ntile) return;
+  const int span = FB_GROUP_M * tiles_n, grp = t / span, first_m = grp * FB_GROUP_M;
+  const int gsz = min(tiles_m - first_m, FB_GROUP_M), r_in = t - grp * span;
+  const int m0 = (first_m + r_in % gsz) * 256, tn = r_in / gsz;
+  const int M = g.M, N = g.N, K = g.K, KG = K / 128;
+  const int nsp = g.W2 ? g.n_split : N, t1 = (nsp + 255) / 256;
+  const bool second = tn >= t1;
+  const int nbase = second ? nsp : 0;                          // first row of this tile's weight matrix
+  const int n0 = second ? nsp + (tn - t1) * 256 : tn * 256, nend = second ? N : nsp;
+  const uint8_t* Wb = (second ? g.W2 : g.W) + (int64_t)(n0 - nbase) * K;
+  const float* wsc = second ? g.w2_scale : g.w_scale;
+  const int nblocks = (nend - nbase + 127) / 128;
+  const int wblk = min((n0 - nbase) / 128 + wn, nblocks - 1);
+  const float* wsrow = wsc + (int64_t)wblk * KG;
+
+  const __amdgpu_buffer_rsrc_t rsA =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (int)((int64_t)M * K), BUF_DW3);
+  const __amdgpu_buffer_rsrc_t rsW =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Wb, (short)0, (int)((int64_t)(nend - n0) * K), BUF_DW3);
+  // load i of wave w fills 1 KB block 8 i + w: blocks 0..31 are A rows, 32..63 W rows
+  int voff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * (8 * i + wv) + (lane >> 3), c = (lane & 7) ^ fb_sw(r);
+    if (i < 4) voff[i] = min(m0 + r, M - 1) * K + c * 16;
+    else voff[i] = (min(n0 + r - 256, nend - 1) - n0) * K + c * 16;
+  }
+  auto issue = [&](uint8_t* st, int kg) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(i < 4 ? rsA : rsW,
+                                               (__attribute__((address_space(3))) void*)(st + (8 * i + wv) * 1024), 16,
+                                               voff[i], kg * FB_BK, 0, 0);
+  };
+
+  // activation scales of the lane's two output rows
+  const float* as0 = g.a_scale + (int64_t)min(m0 + wm * 64 + l32, M - 1) * KG;
+  const float* as1 = g.a_scale + (int64_t)min(m0 + wm * 64 + 32 + l32, M - 1) * KG;
+
+  floatx16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  float srun0 = 0.f, srun1 = 0.f;
+
+  // 32-byte fragment of row `row` (row % 32 == l32) for k half ks: logical chunks 4 ks + 2 hi, +1
+  const int f = fb_sw(l32);
+  int xo[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) xo[ks][e] = ((4 * ks + 2 * hi + e) ^ f) << 4;
+  auto frag = [&](const uint8_t* st, int row, int ks) -> intx8 {
+    const intx4 lo = *(const intx4*)(st + row * FB_BK + xo[ks][0]);
+    const intx4 up = *(const intx4*)(st + row * FB_BK + xo[ks][1]);
+    return (intx8){lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+  };
+  const int ra = wm * 64 + l32, rw = 256 + wn * 128 + l32;
+
+  float sa0 = as0[0], sa1 = as1[0], sw = wsrow[0];
+  auto step = [&](const uint8_t* cur, uint8_t* refill, int kg) {
+    // promotion: keep the sum in units of this group's scale
+    const float n0s = sa0 * sw, n1s = sa1 * sw;
+    const float r0 = (n0s != 0.f && srun0 != 0.f) ? srun0 / n0s : 1.f;
+    const float r1 = (n1s != 0.f && srun1 != 0.f) ? srun1 / n1s : 1.f;
+    if (n0s != 0.f) srun0 = n0s;
+    if (n1s != 0.f) srun1 = n1s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[0][j] *= r0;
+      acc[1][j] *= r1;
+    }
+    // next group's scales (clamped: the last group repeats)
+    const int kn = min(kg + 1, KG - 1);
+    sa0 = as0[kn];
+    sa1 = as1[kn];
+    sw = wsrow[kn];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      intx8 af[2], wf[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = frag(cur, ra + 32 * i, ks);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wf[j] = frag(cur, rw + 32 * j, ks);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32_fp8(wf[j], af[i], acc[i][j]);
+    }
+    // every wave is done with `cur` and the other stage has landed
+    __builtin_amdgcn_s_waitcnt(fb_wait(0, 0));
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    issue(refill, min(kg + 2, KG - 1));
+  };
+
+  issue(s0, 0);
+  issue(s1, min(1, KG - 1));
+  __builtin_amdgcn_s_waitcnt(fb_wait(8, 15));   // group 0 has landed
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  int kg = 0;
+  for (; kg + 1 < KG; kg += 2) {
+    step(s0, s0, kg);
+    step(s1, s1, kg + 1);
+  }
+  if (kg < KG) step(s0, s0, kg);
+  __builtin_amdgcn_s_waitcnt(fb_wait(0, 0));
+  __syncthreads();
+
+  // epilogue: rows 0..127 of the bf16 C tile in s0, 128..255 in s1
+  auto crow = [&](int row) -> uint16_t* { return (uint16_t*)(row < 128 ? s0 : s1) + (row & 127) * FB_CP; };
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float sr = i ? srun1 : srun0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int ml = wm * 64 + i * 32 + l32, nl = wn * 128 + j * 32 + 8 * rg + 4 * hi;
+        *(uint2*)(crow(ml) + nl) = make_uint2(pack_bf16x2(acc[i][j][4 * rg] * sr, acc[i][j][4 * rg + 1] * sr),
+                                              pack_bf16x2(acc[i][j][4 * rg + 2] * sr, acc[i][j][4 * rg + 3] * sr));
+      }
+  }
+  __syncthreads();
+  uint16_t* C = (uint16_t*)g.C;
+  if (g.epi == EPI_KV_SPLIT) {
+    const int h = n0 >> 8;
+    for (int c = tid; c < 256 * 16; c += 512) {
+      const int row = c >> 4, ch = (c & 15) * 8, m = m0 + row;
+      if (m >= M) continue;
+      const int bb = m / g.kv.T, tt = m - bb * g.kv.T;
+      const int64_t bh = (int64_t)bb * g.kv.H + h;
+      *(uint4*)(C + (bh * g.kv.Tp + tt) * 128 + ch) = *(const uint4*)(crow(row) + ch);
+    }
+    for (int c = tid; c < 256 * 16; c += 512) {
+      const int row = c & 255, ch = (c >> 8) * 8, m = m0 + row;
+      if (m >= M) continue;
+      const uint4 v = *(const uint4*)(crow(row) + 128 + ch);
+      const uint16_t* e = (const uint16_t*)&v;
+      const int bb = m / g.kv.T, tt = m - bb * g.kv.T;
+      uint16_t* vt = (uint16_t*)g.kv.vt + (((int64_t)bb * g.kv.H + h) * 128 + ch) * g.kv.Tp + tt;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) vt[(int64_t)k * g.kv.Tp] = e[k];
+    }
+    return;
+  }
+  for (int c = tid; c < 256 * 32; c += 512) {
+    const int row = c >> 5, ch = (c & 31) * 8, m = m0 + row, n = n0 + ch;
+    if (m >= M || n >= nend) continue;
+    const uint4 v = *(const uint4*)(crow(row) + ch);
+    if (n + 8 <= nend) {
+      *(uint4*)(C + (int64_t)m * g.ldc + n) = v;
+    } else {
+      const uint16_t* e = (const uint16_t*)&v;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (n + k < nend) C[(int64_t)m * g.ldc + n + k] = e[k];
+    }
+  }
+}
+
+int fb_cdiv(int a, int b) { return (a + b - 1) / b; }
+bool fp8_big_ok(const GemmFp8Args& g) {
+  const int nsp = g.W2 ? g.n_split : g.N;
+  return g.c_dtype == DT_BF16 && g.M >= 256 && g.N >= 256 && g.K % 128 == 0 && (int64_t)g.M * g.K < (1LL << 31) &&
+         (int64_t)g.N * g.K < (1LL << 31) && (!g.W2 || (nsp % 128 == 0 && nsp < g.N)) &&
+         (g.epi != EPI_KV_SPLIT || g.N % 256 == 0) && (g.ldc & 7) == 0 && (((uintptr_t)g.C) & 15) == 0 &&
+         (((uintptr_t)g.A | (uintptr_t)g.W | (uintptr_t)g.W2) & 15) == 0;
+}
+
 }  // namespace
 
 hipError_t launch_gemm_fp8(const GemmFp8Args& g, hipStream_t s) {
+  if (fp8_big_ok(g)) {
+    const int nsp = g.W2 ? g.n_split : g.N;
+    const int tm = fb_cdiv(g.M, 256), tn = g.W2 ? fb_cdiv(nsp, 256) + fb_cdiv(g.N - nsp, 256) : fb_cdiv(g.N, 256);
+    const int per_xcd = fb_cdiv(tm * tn, 8);
+    gemm_fp8_big_kernel<<<8 * per_xcd, 512, 0, s>>>(g, tm, tn, per_xcd);
+    return hipGetLastError();
+  }
   dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, 1);
   gemm_fp8_kernel<128, 128, 2, 2><<<grid, 256, 0, s>>>(g);
   return hipGetLastError();

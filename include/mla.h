@@ -141,7 +141,8 @@ MLA_API size_t mla_decode_workspace_size(const mla_dims* dims, int32_t weight_dt
  *             row is set to zero)
  *   rope_cos, rope_sin  fp32 [rope_len, 32], rope_len >= max_len
  *   out       [B, dim] bf16
- * Needs bf16 weights and kv_lora_rank = 512. */
+ * Needs bf16 weights, kv_lora_rank = 512, n_heads a multiple of 64, and
+ * 16-byte aligned norm weights and cache (MLA_UNSUPPORTED otherwise). */
 MLA_API int mla_decode(const mla_dims* dims, const mla_weights* w, const void* x, int32_t B,
                void* kv_cache, int32_t max_len, const int32_t* cache_len,
                const float* rope_cos, const float* rope_sin, int32_t rope_len,
@@ -219,7 +220,8 @@ MLA_API int mla_rope_table(float* cos_tab, float* sin_tab, int32_t n_pos, float 
  * elements along K (Kimi K2 · Down projection: activation_scheme dynamic):
  *   s = amax(group) / 448 (fp32; 0 for an all-zero group), q = e4m3_rne(a / s)
  * with the quotient in fp32. a: [M, K] (lda) MLA_F32 or MLA_BF16; q [M, K]
- * contiguous; scales [M, K/128]. K % 128 == 0. */
+ * contiguous; scales [M, K/128]. K % 128 == 0, lda % 8 == 0, a and q 16-byte
+ * aligned (MLA_UNSUPPORTED otherwise). */
 MLA_API int mla_quant_e4m3_1x128(const void* a, int64_t lda, int32_t a_dtype, int32_t M, int32_t K,
                          uint8_t* q, float* scales, void* stream);
 
