@@ -178,8 +178,10 @@ bool qkv_norm_ok(const mla::QkvNormArgs& a) {
 // With kv != nullptr the output goes through the k_nope / v^T split epilogue.
 int project(int wdt, int adt, const void* act, int64_t lda, const void* W, const float* Ws,
             const void* W2, const float* W2s, int n_split, void* out, int64_t ldo, int M, int N, int K,
-            const PrefillWs* ws, hipStream_t s, const mla::KvSplit* kv = nullptr) {
+            const PrefillWs* ws, hipStream_t s, const mla::KvSplit* kv = nullptr, const mla::RopeEpi* rope = nullptr,
+            bool* roped = nullptr) {
   const int epi = kv ? mla::EPI_KV_SPLIT : mla::EPI_ROWMAJOR;
+  if (roped) *roped = false;
   if (wdt == MLA_E4M3) {
     LAUNCH(mla::launch_quant_1x128(act, lda, adt, M, K, (uint8_t*)ws->aq, (float*)ws->as, s), "quant_e4m3_1x128");
     mla::GemmFp8Args g{};
@@ -188,6 +190,11 @@ int project(int wdt, int adt, const void* act, int64_t lda, const void* W, const
     g.C = out; g.ldc = ldo; g.c_dtype = adt; g.M = M; g.N = N; g.K = K;
     g.epi = epi;
     if (kv) g.kv = *kv;
+    if (rope) {   // RoPE of the query's rotary slices in the GEMM's epilogue, where it applies
+      g.epi = mla::EPI_QROPE; g.rope = *rope;
+      if (mla::gemm_fp8_qrope_ok(g) && roped) *roped = true;
+      else { g.epi = epi; g.rope = mla::RopeEpi{}; }
+    }
     LAUNCH(mla::launch_gemm_fp8(g, s), "gemm_fp8_blockscaled");
     return MLA_OK;
   }
@@ -316,19 +323,22 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
   }
   }
   // q = c_q . Wq_b^T, then RoPE on each head's rotary slice (in the GEMM's
-  // epilogue on the bf16 path)
+  // epilogue on the bf16 and e4m3 paths, a separate pass otherwise)
   mla::GemmArgs gr = gemm_args(p.cqn, Dq, w->wq_b, Dq, p.q, H * 192, adt, M, H * 192, Dq);
   gr.epi = mla::EPI_QROPE; gr.rope = {rope_cos, rope_sin, T};
   if (wdt == MLA_BF16 && adt == MLA_BF16 && mla::gemm_bf16_qrope_ok(gr)) {
     LAUNCH(mla::launch_gemm_bf16(gr, s), "gemm_bf16(q_b + RoPE)");
   } else {
+    bool roped = false;
     if ((rc = project(wdt, adt, p.cqn, Dq, w->wq_b, w->wq_b_scale, nullptr, nullptr, H * 192, p.q, H * 192, M,
-                      H * 192, Dq, &p, s)))
+                      H * 192, Dq, &p, s, nullptr, &gr.rope, &roped)))
       return rc;
-    mla::NormRopeArgs a = norm_args(p.q, H * 192, p.q, H * 192, adt, M);
-    a.rope_off = 128; a.rope_heads = H; a.rope_stride = 192;
-    a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = rope_len; a.pos_period = T;
-    LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(q_pe)");
+    if (!roped) {
+      mla::NormRopeArgs a = norm_args(p.q, H * 192, p.q, H * 192, adt, M);
+      a.rope_off = 128; a.rope_heads = H; a.rope_stride = 192;
+      a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = rope_len; a.pos_period = T;
+      LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(q_pe)");
+    }
   }
   // per head [k_nope | v] = c . Wkv_b^T, stored as k_nope [B,H,Tp,128] and v^T [B,H,128,Tp]
   const int Tp = pad64(T);

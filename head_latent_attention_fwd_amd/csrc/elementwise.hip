@@ -90,7 +90,38 @@ __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(NormRopeArgs a, int r
     for (int i = tid; i < a.norm_dim; i += 256)
       st(a.out, a.out_dtype, ob + i, a.gamma[i] * (ld_in(a, ib + i) * r));
   }
-  if (a.rope_heads > 0) {
+  if (a.rope_heads > 0 && a.norm_dim == 0 && a.in_dtype == DT_BF16 && a.out_dtype == DT_BF16 && a.in_splits <= 1 &&
+      !a.kpe && ((a.rope_off | a.rope_stride | a.ld_in | a.ld_out) & 3) == 0 &&
+      (((uintptr_t)a.in | (uintptr_t)a.out | (uintptr_t)a.cos_tab | (uintptr_t)a.sin_tab) & 15) == 0) {
+    // bf16 rotation only (the query's rope slices): 4 pairs per thread step,
+    // 8-byte accesses
+    const int pos = a.pos ? a.pos[row] : row % a.pos_period;
+    const bool ok = pos >= 0 && pos < rope_len;
+    for (int p = tid; p < a.rope_heads * 8; p += 256) {
+      const int h = p >> 3, d0 = (p & 7) * 4;
+      const int64_t o = a.rope_off + (int64_t)h * a.rope_stride + d0;
+      const uint2 u1 = *(const uint2*)((const uint16_t*)a.in + ib + o);
+      const uint2 u2 = *(const uint2*)((const uint16_t*)a.in + ib + o + 32);
+      float4 c = make_float4(0.f, 0.f, 0.f, 0.f), sn = c;
+      if (ok) {
+        c = *(const float4*)&a.cos_tab[pos * 32 + d0];
+        sn = *(const float4*)&a.sin_tab[pos * 32 + d0];
+      }
+      const float x1[4] = {__uint_as_float(u1.x << 16), __uint_as_float(u1.x & 0xffff0000u),
+                           __uint_as_float(u1.y << 16), __uint_as_float(u1.y & 0xffff0000u)};
+      const float x2[4] = {__uint_as_float(u2.x << 16), __uint_as_float(u2.x & 0xffff0000u),
+                           __uint_as_float(u2.y << 16), __uint_as_float(u2.y & 0xffff0000u)};
+      const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+      float y1[4], y2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y1[e] = x1[e] * cc[e] - x2[e] * ss[e];
+        y2[e] = x2[e] * cc[e] + x1[e] * ss[e];
+      }
+      *(uint2*)((uint16_t*)a.out + ob + o) = make_uint2(pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3]));
+      *(uint2*)((uint16_t*)a.out + ob + o + 32) = make_uint2(pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3]));
+    }
+  } else if (a.rope_heads > 0) {
     const int pos = a.pos ? a.pos[row] : row % a.pos_period;
     const bool ok = pos >= 0 && pos < rope_len;
     for (int p = tid; p < a.rope_heads * 32; p += 256) {

@@ -323,6 +323,46 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
                                               pack_bf16x2(acc[i][j][4 * rg + 2] * sr, acc[i][j][4 * rg + 3] * sr));
       }
   }
+  if (g.epi == EPI_QROPE) {
+    // q_b with RoPE (N = H*192): the rotary columns [192 h + 128, 192 h + 192)
+    // of a head never cross a 256-column tile boundary; thread r rotates row r
+    // of the staged tile for each head whose rotary columns lie in the tile,
+    // with the table row of its position fetched in one batch
+    float4 cs[8], sn[8];
+    const int mr = min(m0 + tid, M - 1), tpos = mr % g.rope.T;
+    if (tid < 256) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        cs[q] = *(const float4*)&g.rope.cos[tpos * 32 + 4 * q];
+        sn[q] = *(const float4*)&g.rope.sin[tpos * 32 + 4 * q];
+      }
+    }
+    __syncthreads();
+    if (tid < 256) {
+      uint16_t* r = crow(tid);
+      for (int h = n0 / 192; h <= (n0 + 255) / 192; ++h) {
+        const int c0 = 192 * h + 128 - n0;
+        if (c0 < 0 || c0 + 64 > 256) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint4 x = *(const uint4*)(r + c0 + 8 * q), y = *(const uint4*)(r + c0 + 32 + 8 * q);
+          uint16_t* xe = (uint16_t*)&x;
+          uint16_t* ye = (uint16_t*)&y;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float4 c4 = cs[2 * q + (e >> 2)], s4 = sn[2 * q + (e >> 2)];
+            const float c = (e & 3) == 0 ? c4.x : (e & 3) == 1 ? c4.y : (e & 3) == 2 ? c4.z : c4.w;
+            const float sv = (e & 3) == 0 ? s4.x : (e & 3) == 1 ? s4.y : (e & 3) == 2 ? s4.z : s4.w;
+            const float x1 = bf2f(xe[e]), x2 = bf2f(ye[e]);
+            xe[e] = f2bf(x1 * c - x2 * sv);
+            ye[e] = f2bf(x2 * c + x1 * sv);
+          }
+          *(uint4*)(r + c0 + 8 * q) = x;
+          *(uint4*)(r + c0 + 32 + 8 * q) = y;
+        }
+      }
+    }
+  }
   __syncthreads();
   uint16_t* C = (uint16_t*)g.C;
   if (g.epi == EPI_KV_SPLIT) {
@@ -372,7 +412,13 @@ bool fp8_big_ok(const GemmFp8Args& g) {
 
 }  // namespace
 
+bool gemm_fp8_qrope_ok(const GemmFp8Args& g) {
+  return fp8_big_ok(g) && !g.W2 && g.N % 192 == 0 && g.rope.cos && g.rope.sin && g.rope.T > 0 &&
+         (((uintptr_t)g.rope.cos | (uintptr_t)g.rope.sin) & 15) == 0;
+}
+
 hipError_t launch_gemm_fp8(const GemmFp8Args& g, hipStream_t s) {
+  if (g.epi == EPI_QROPE && !gemm_fp8_qrope_ok(g)) return hipErrorInvalidValue;
   if (fp8_big_ok(g)) {
     const int nsp = g.W2 ? g.n_split : g.N;
     const int tm = fb_cdiv(g.M, 256), tn = g.W2 ? fb_cdiv(nsp, 256) + fb_cdiv(g.N - nsp, 256) : fb_cdiv(g.N, 256);

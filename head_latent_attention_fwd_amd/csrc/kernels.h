@@ -59,9 +59,11 @@ struct GemmFp8Args {
   const uint8_t* W2; const float* w2_scale; int n_split;
   void* C; int64_t ldc; int c_dtype;
   int M, N, K;
-  int epi; KvSplit kv;
+  int epi; KvSplit kv; RopeEpi rope;
 };
 hipError_t launch_gemm_fp8(const GemmFp8Args& g, hipStream_t s);
+// whether launch_gemm_fp8 takes g with epi = EPI_QROPE
+bool gemm_fp8_qrope_ok(const GemmFp8Args& g);
 
 // Decode-shaped GEMM (M <= 128): C[z][M, N] = A[z][M, K] . W[z][N, K]^T with
 // N tiles of nt (64 or 128) columns and `splits` K chunks of kc (multiple of
