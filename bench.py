@@ -6,7 +6,8 @@ A step is one whole pass of the path over one batch of synthetic input that is
 already resident in HBM: mla_prefill (x -> out) or mla_decode (x, cache -> out).
 The headline value is the Kimi-K2-shaped bf16 prefill (B=1, T=2048, H=64) in
 algorithmic TFLOP/s; the other workloads (fp8-weight prefill, sparse
-DeepSeek-V3.2-Exp prefill, absorbed decode) are reported beside it. Prints one
+DeepSeek-V3.2-Exp prefill, absorbed decode, Kimi-K2 shared-expert MLP) are
+reported beside it. Prints one
 JSON line.
 """
 import argparse
@@ -218,6 +219,28 @@ def bench_decode(cfg_index, steps, warmup, kernels=False):
     return res
 
 
+def bench_swiglu(steps, warmup, M=2048, hidden=7168, inter=2048):
+    """Kimi-K2 shared-expert SwiGLU MLP over the prefill's 2048 tokens:
+    out = (silu(x Wg^T) * (x Wu^T)) Wd^T, bf16."""
+    import torch
+    from head_latent_attention_fwd_amd import api
+    g = torch.Generator(device="cuda").manual_seed(5)
+    x = torch.randn((M, hidden), generator=g, device="cuda").to(torch.bfloat16)
+    wg = (torch.randn((inter, hidden), generator=g, device="cuda") / hidden ** 0.5).to(torch.bfloat16)
+    wu = (torch.randn((inter, hidden), generator=g, device="cuda") / hidden ** 0.5).to(torch.bfloat16)
+    wd = (torch.randn((hidden, inter), generator=g, device="cuda") / inter ** 0.5).to(torch.bfloat16)
+    out = torch.empty((M, hidden), device="cuda", dtype=torch.bfloat16)
+    ws = api.workspace(api.lib().mla_swiglu_workspace_size(M, inter))
+    flop = 2 * M * hidden * inter * 3
+    sec = wall_steps(lambda: api.mla_swiglu_mlp(x, wg, wu, wd, out=out, ws=ws), steps, warmup)
+    res = {"workload": "kimi_k2_shared_expert_mlp", "M": M, "hidden": hidden, "inter": inter,
+           "ms_per_step": sec * 1e3, "tflops": flop / sec / 1e12, "frac_of_bf16_peak": flop / sec / 1e12 / PEAK["bf16"],
+           "algorithmic_flop": flop}
+    del x, wg, wu, wd, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cfg_index, rows=256):
     """The fp64 oracle, as it stands, on a bounded sample of the prefill
     workload: keys/values for every position, then `rows` evenly spaced query
@@ -270,7 +293,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
-    ap.add_argument("--workloads", default="1,2,3,4", help="config indices to run (1 = headline)")
+    ap.add_argument("--workloads", default="1,2,3,4,5",
+                    help="config indices to run (1 = headline; 5 = shared-expert SwiGLU MLP)")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel event breakdown")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -289,6 +313,8 @@ def main():
         print(f"[bench] workload {i}", file=sys.stderr, flush=True)
         if i == 4:
             results[i] = bench_decode(i, args.steps, args.warmup, kernels)
+        elif i == 5:
+            results[i] = bench_swiglu(args.steps, args.warmup)
         else:
             results[i], _ = bench_prefill(i, args.steps, args.warmup, kernels and i == 1)
         if i == 1:

@@ -56,6 +56,8 @@ _SIGS = {
     "mla_quant_e4m3_1x128": (ctypes.c_int, [vp, i64, i32, i32, i32, vp, vp, vp]),
     "mla_quant_e4m3_block128": (ctypes.c_int, [vp, i32, i32, vp, vp, vp]),
     "mla_topk_to_bitmask": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
+    "mla_swiglu_workspace_size": (sz, [i32, i32]),
+    "mla_swiglu_mlp": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
 }
 
 _lib = None
@@ -267,3 +269,19 @@ def mla_topk_to_bitmask(topk_idx, T=None, stream=None):
     mask = torch.empty((B, Tq, (T + 31) // 32), dtype=torch.int32, device=topk_idx.device)
     _check(lib().mla_topk_to_bitmask(_ptr(topk_idx), B, T, k, _ptr(mask), _stream(stream)))
     return mask
+
+
+def mla_swiglu_mlp(x, w_gate, w_up, w_down, out=None, ws=None, stream=None):
+    """out = (silu(x w_gate^T) * (x w_up^T)) w_down^T, all bf16 on the device."""
+    for t, n in ((x, "x"), (w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
+        _need(t, torch.bfloat16, n)
+    M, hidden = x.shape
+    inter = w_gate.shape[0]
+    if out is None:
+        out = torch.empty((M, hidden), dtype=torch.bfloat16, device=x.device)
+    nbytes = lib().mla_swiglu_workspace_size(M, inter)
+    if ws is None:
+        ws = workspace(nbytes, x.device)
+    _check(lib().mla_swiglu_mlp(_ptr(x), M, hidden, inter, _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out),
+                                _ptr(ws), ws.numel(), _stream(stream)))
+    return out

@@ -570,4 +570,45 @@ int mla_topk_to_bitmask(const int32_t* topk_idx, int32_t B, int32_t T, int32_t t
   return MLA_OK;
 }
 
+size_t mla_swiglu_workspace_size(int32_t M, int32_t inter) {
+  if (M <= 0 || inter <= 0) return 0;
+  // [M, inter] gate and up products (the fused path uses the first as the product)
+  const size_t one = (((size_t)M * inter * 2) + 255) & ~(size_t)255;
+  return 3 * one;
+}
+
+int mla_swiglu_mlp(const void* x, int32_t M, int32_t hidden, int32_t inter, const void* w_gate, const void* w_up,
+                   const void* w_down, void* out, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (!x || !w_gate || !w_up || !w_down || !out || !ws) return fail(MLA_INVALID_ARG, "NULL pointer");
+  if (M <= 0 || hidden <= 0 || inter <= 0) return fail(MLA_INVALID_ARG, "bad sizes");
+  if (hidden % 64 || inter % 64) return fail(MLA_UNSUPPORTED, "hidden and inter must be multiples of 64");
+  if (((uintptr_t)x | (uintptr_t)w_gate | (uintptr_t)w_up | (uintptr_t)w_down | (uintptr_t)out) & 15)
+    return fail(MLA_UNSUPPORTED, "pointers must be 16-byte aligned");
+  if (ws_bytes < mla_swiglu_workspace_size(M, inter)) return fail(MLA_INVALID_ARG, "workspace too small");
+  if ((uintptr_t)ws & 255) return fail(MLA_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const size_t one = (((size_t)M * inter * 2) + 255) & ~(size_t)255;
+  uint16_t* h = (uint16_t*)ws;
+  // h = silu(x . Wg^T) * (x . Wu^T): one GEMM over paired gate / up tiles with
+  // the product in its epilogue, else two GEMMs and an elementwise pass
+  mla::GemmArgs g = gemm_args(x, hidden, w_gate, hidden, h, inter, MLA_BF16, M, inter, hidden);
+  g.W2 = w_up; g.ldw2 = hidden; g.epi = mla::EPI_SWIGLU;
+  if (mla::gemm_bf16_swiglu_ok(g)) {
+    LAUNCH(mla::launch_gemm_bf16(g, s), "gemm_bf16(gate|up + silu*mul)");
+  } else {
+    uint16_t* gt = (uint16_t*)((char*)ws + one);
+    uint16_t* up = (uint16_t*)((char*)ws + 2 * one);
+    LAUNCH(mla::launch_gemm_bf16(gemm_args(x, hidden, w_gate, hidden, gt, inter, MLA_BF16, M, inter, hidden), s),
+           "gemm_bf16(gate)");
+    LAUNCH(mla::launch_gemm_bf16(gemm_args(x, hidden, w_up, hidden, up, inter, MLA_BF16, M, inter, hidden), s),
+           "gemm_bf16(up)");
+    LAUNCH(mla::launch_silu_mul(gt, up, h, (int64_t)M * inter, s), "silu_mul");
+  }
+  // out = h . Wd^T
+  LAUNCH(mla::launch_gemm_bf16(gemm_args(h, inter, w_down, inter, out, hidden, MLA_BF16, M, hidden, inter), s),
+         "gemm_bf16(down)");
+  return MLA_OK;
+}
+
 }  // extern "C"

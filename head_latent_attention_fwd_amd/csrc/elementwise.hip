@@ -234,6 +234,22 @@ __global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
   }
 }
 
+// h = silu(g) * u, 8 bf16 values per thread (the unfused SwiGLU path).
+__global__ __launch_bounds__(256) void silu_mul_kernel(const uint4* g, const uint4* u, uint4* h, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const uint4 gv = g[i], uv = u[i];
+  const uint16_t* ge = (const uint16_t*)&gv;
+  const uint16_t* ue = (const uint16_t*)&uv;
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float gf = bf2f(ge[e]);
+    y[e] = gf / (1.0f + __builtin_amdgcn_exp2f(-gf * 1.4426950408889634f)) * bf2f(ue[e]);
+  }
+  h[i] = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+}
+
 // Zero the padding keys t in [T, Tp) of kn [B,H,Tp,128], vt [B,H,128,Tp], kpe [B,Tp,64].
 template <typename E>
 __global__ __launch_bounds__(256) void zero_kv_padding_kernel(E* kn, E* vt, E* kpe, int H, int T, int Tp) {
@@ -391,6 +407,13 @@ hipError_t launch_quant_1x128(const void* a, int64_t lda, int a_dtype, int M, in
 hipError_t launch_quant_block128(const float* w, int N, int K, uint8_t* q, float* scales, hipStream_t s) {
   dim3 grid((K + 127) / 128, (N + 127) / 128);
   quant_block128_kernel<<<grid, 256, 0, s>>>(w, N, K, q, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul(const void* g, const void* u, void* h, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t n8 = n / 8;
+  silu_mul_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>((const uint4*)g, (const uint4*)u, (uint4*)h, n8);
   return hipGetLastError();
 }
 

@@ -205,7 +205,7 @@ struct BigTile {
   static_assert(2 * 32 * FP * 4 <= HALF * 2, "split-K patches of two waves per stage");
 };
 
-template <int WM, int WN, int FM, int FN>
+template <int WM, int WN, int FM, int FN, bool PAIRED = false>
 __device__ __forceinline__ void gemm_bf16_big(const GemmArgs& g, int tiles_m, int tiles_n, int per_xcd) {
   using TL = BigTile<WM, WN, FM, FN>;
   constexpr int BM = TL::BM, BN = TL::BN, LOADS = TL::LOADS, CP = TL::CP, HALF = TL::HALF;
@@ -225,9 +225,14 @@ __device__ __forceinline__ void gemm_bf16_big(const GemmArgs& g, int tiles_m, in
   // With a second weight (rows n_split.. of the concatenated W), column tiles
   // never straddle n_split: tiles 0..t1-1 cover [0, n_split), the rest
   // [n_split, N). nend bounds the tile's region (rows past it are clamped).
-  const int nsp = g.W2 ? g.n_split : N, t1 = (nsp + BN - 1) / BN;
-  const bool second = tn >= t1;
-  const int n0 = second ? nsp + (tn - t1) * BN : tn * BN, nend = second ? N : nsp;
+  //
+  // PAIRED (SwiGLU gate / up, BN = 256): tile tn produces output columns
+  // [128 tn, 128 tn + 128); its W rows 0..127 are gate rows (W) and 128..255
+  // the same rows of up (W2), so the epilogue holds both halves of each column.
+  static_assert(!PAIRED || BN == 256, "paired tiles are 256 wide");
+  const int nsp = (g.W2 && !PAIRED) ? g.n_split : N, t1 = (nsp + BN - 1) / BN;
+  const bool second = !PAIRED && tn >= t1;
+  const int n0 = PAIRED ? tn * 128 : second ? nsp + (tn - t1) * BN : tn * BN, nend = second ? N : nsp;
   // K chunk of this workgroup (whole K without split-K)
   const int ksteps = K / GB_BK, per = (ksteps + max(g.k_splits, 1) - 1) / max(g.k_splits, 1);
   const int kbeg = split * per * GB_BK;
@@ -244,11 +249,17 @@ __device__ __forceinline__ void gemm_bf16_big(const GemmArgs& g, int tiles_m, in
       __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(((int64_t)(M - 1) * g.lda + K - kbeg) * 2), BUF_DW3);
   const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
       (void*)Wb, (short)0, (int)(((int64_t)(nend - 1 - n0) * ldw + K - kbeg) * 2), BUF_DW3);
+  const __amdgpu_buffer_rsrc_t rsW2 =
+      PAIRED ? __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)g.W2 + kbeg + (int64_t)n0 * g.ldw2), (short)0,
+                                                 (int)(((int64_t)(nend - 1 - n0) * g.ldw2 + K - kbeg) * 2), BUF_DW3)
+             : rsW;
   int voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int r = 8 * (4 * i + wv) + (lane >> 3), c = (lane & 7) ^ gb_sw(r);
     if (i < 8) voff[i] = (int)(((int64_t)min(m0 + r, M - 1) * g.lda + c * 8) * 2);
+    else if (PAIRED)   // slots 8..11: gate rows, 12..15: up rows (row r - BM - 128)
+      voff[i] = (int)(((int64_t)(min(n0 + ((r - BM) & 127), nend - 1) - n0) * (i < 12 ? g.ldw : g.ldw2) + c * 8) * 2);
     else voff[i] = (int)(((int64_t)(min(n0 + r - BM, nend - 1) - n0) * ldw + c * 8) * 2);
   }
   // loads i0 <= i < i1 of step kt into stage st
@@ -257,7 +268,8 @@ __device__ __forceinline__ void gemm_bf16_big(const GemmArgs& g, int tiles_m, in
     for (int i = 0; i < LOADS; ++i) {
       if (i < i0 || i >= i1) continue;
       auto* lds = (__attribute__((address_space(3))) void*)(st + (4 * i + wv) * 512);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(i < 8 ? rsA : rsW, lds, 16, voff[i], kt * 128, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(i < 8 ? rsA : (PAIRED && i >= 12 ? rsW2 : rsW), lds, 16, voff[i],
+                                               kt * 128, 0, 0);
     }
   };
 
@@ -444,6 +456,31 @@ __device__ __forceinline__ void gemm_bf16_big(const GemmArgs& g, int tiles_m, in
   }
   __syncthreads();
   uint16_t* C = (uint16_t*)g.C + (int64_t)z * g.batch_c;
+  if (PAIRED) {
+    // h[m, n0 + j] = silu(gate) * up from columns j and 128 + j of the staged tile
+    for (int c = tid; c < BM * 16; c += 256) {
+      const int row = c >> 4, ch = (c & 15) * 8, m = m0 + row, n = n0 + ch;
+      if (m >= M || n >= nend) continue;
+      const uint4 gv = *(const uint4*)(crow(row) + ch), uv = *(const uint4*)(crow(row) + 128 + ch);
+      const uint16_t* ge = (const uint16_t*)&gv;
+      const uint16_t* ue = (const uint16_t*)&uv;
+      float h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float gf = bf2f(ge[e]);
+        h[e] = gf / (1.0f + __builtin_amdgcn_exp2f(-gf * 1.4426950408889634f)) * bf2f(ue[e]);
+      }
+      const uint4 v = make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
+                                 pack_bf16x2(h[6], h[7]));
+      if (n + 8 <= nend) {
+        *(uint4*)(C + (int64_t)m * g.ldc + n) = v;
+      } else {
+        const uint16_t* e = (const uint16_t*)&v;
+        for (int k = 0; n + k < nend; ++k) C[(int64_t)m * g.ldc + n + k] = e[k];
+      }
+    }
+    return;
+  }
   if (BN == 256 && g.epi == EPI_KV_SPLIT) {
     // the tile is one head (N % 256 == 0): columns 0..127 are k_nope, stored
     // along the row (16 lanes per row); columns 128..255 are v, stored
@@ -493,6 +530,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big224_kernel(GemmArgs g, in
 }
 __global__ __launch_bounds__(256, 1) void gemm_bf16_big192_kernel(GemmArgs g, int tm, int tn, int per_xcd) {
   gemm_bf16_big<2, 2, 4, 3>(g, tm, tn, per_xcd);
+}
+__global__ __launch_bounds__(256, 1) void gemm_bf16_swiglu_kernel(GemmArgs g, int tm, int tn, int per_xcd) {
+  gemm_bf16_big<2, 2, 4, 4, true>(g, tm, tn, per_xcd);
 }
 
 }  // namespace
@@ -568,8 +608,23 @@ bool gemm_bf16_qrope_ok(const GemmArgs& g) {
          (((uintptr_t)g.rope.cos | (uintptr_t)g.rope.sin) & 15) == 0;
 }
 
+bool gemm_bf16_swiglu_ok(const GemmArgs& g) {
+  GemmArgs h = g;
+  h.W2 = nullptr;   // the pairing replaces the stacked-weight split
+  return big_ok(h) && g.W2 && g.batch == 1 && g.k_splits <= 1 && g.c_dtype == DT_BF16 && g.N % 128 == 0 &&
+         (g.ldw2 & 7) == 0 && (((uintptr_t)g.W2) & 15) == 0 &&
+         ((int64_t)(g.N - 1) * g.ldw2 + g.K) * 2 < ((int64_t)1 << 31) && (g.ldc & 7) == 0 &&
+         (((uintptr_t)g.C) & 15) == 0;
+}
+
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
   if (g.epi == EPI_QROPE) return gemm_bf16_qrope_ok(g) ? run_big(g, 192, 1, s) : hipErrorInvalidValue;
+  if (g.epi == EPI_SWIGLU) {
+    if (!gemm_bf16_swiglu_ok(g)) return hipErrorInvalidValue;
+    const int tm = cdiv(g.M, 256), tn = g.N / 128, per_xcd = cdiv(tm * tn, 8);
+    gemm_bf16_swiglu_kernel<<<8 * per_xcd, 256, 0, s>>>(g, tm, tn, per_xcd);
+    return hipGetLastError();
+  }
   if (g.w_kn) return run<128, 128, 2, 2, true>(g, s);
   if (g.k_splits > 1) {   // the caller sized part[] from gemm_bf16_splits
     if (!big_ok(g) || g.batch != 1 || !g.part || g.k_splits != gemm_bf16_splits(g)) return hipErrorInvalidValue;

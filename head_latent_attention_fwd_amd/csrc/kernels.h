@@ -16,7 +16,9 @@ enum { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
 // writes k_nope to C = KN [B, H, Tp, 128] and v transposed to C2 = VT [B, H, 128, Tp].
 // EPI_QROPE (bf16 big-tile path, N = H*192): row-major C with RoPE applied to
 // columns 128..191 of every 192-wide head (pairs (d, d + 32), position m % T).
-enum { EPI_ROWMAJOR = 0, EPI_KV_SPLIT = 1, EPI_QROPE = 2 };
+// EPI_SWIGLU (bf16 big-tile path): W = gate, W2 = up (same [N, K] shape);
+// C[m, n] = silu(A . W^T)[m, n] * (A . W2^T)[m, n] for N = the intermediate width.
+enum { EPI_ROWMAJOR = 0, EPI_KV_SPLIT = 1, EPI_QROPE = 2, EPI_SWIGLU = 3 };
 struct KvSplit {
   void* vt; int T, Tp, H;
 };
@@ -48,8 +50,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
 // Number of K chunks the big-tile path would use for this shape (1 = no split;
 // a split is worth it when the output has too few 256x256 tiles to fill the chip).
 int gemm_bf16_splits(const GemmArgs& g);
-// whether launch_gemm_bf16 takes g with epi = EPI_QROPE
+// whether launch_gemm_bf16 takes g with epi = EPI_QROPE / EPI_SWIGLU
 bool gemm_bf16_qrope_ok(const GemmArgs& g);
+bool gemm_bf16_swiglu_ok(const GemmArgs& g);
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s);
 
 // Block-scaled e4m3 GEMM. W2/w2_scale as in GemmArgs (n_split multiple of 128).
@@ -118,6 +121,8 @@ hipError_t launch_rope_table(float* c, float* sn, int n_pos, float base, hipStre
 hipError_t launch_quant_1x128(const void* a, int64_t lda, int a_dtype, int M, int K,
                               uint8_t* q, float* scales, hipStream_t s);
 hipError_t launch_quant_block128(const float* w, int N, int K, uint8_t* q, float* scales, hipStream_t s);
+// h[i] = silu(g[i]) * u[i] over n bf16 values (n % 8 == 0, 16-byte aligned).
+hipError_t launch_silu_mul(const void* g, const void* u, void* h, int64_t n, hipStream_t s);
 hipError_t launch_topk_bitmask(const int32_t* idx, int B, int T, int k, uint32_t* mask, hipStream_t s);
 
 // Prefill attention. q [B*T, H*192] (rope applied), kn [B, H, Tp, 128],

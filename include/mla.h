@@ -238,6 +238,25 @@ MLA_API int mla_quant_e4m3_block128(const float* w, int32_t N, int32_t K, uint8_
 MLA_API int mla_topk_to_bitmask(const int32_t* topk_idx, int32_t B, int32_t T, int32_t topk,
                         uint32_t* mask, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Shared-expert MLP
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of workspace mla_swiglu_mlp needs (0 on invalid input). */
+MLA_API size_t mla_swiglu_workspace_size(int32_t M, int32_t inter);
+
+/* Shared-expert SwiGLU MLP (Kimi K2 · Down projection: the shared expert
+ * applies down_proj to act_fn(gate_proj(x)) * up_proj(x), act_fn = silu,
+ * bias-free Linears):
+ *   out = (silu(x . Wg^T) * (x . Wu^T)) . Wd^T,  silu(z) = z / (1 + exp(-z))
+ *   x [M, hidden] bf16; w_gate, w_up [inter, hidden] bf16; w_down [hidden, inter]
+ *   bf16; out [M, hidden] bf16; ws: workspace of mla_swiglu_workspace_size(M,
+ *   inter) bytes, 256-byte aligned. hidden and inter multiples of 64, all
+ *   pointers 16-byte aligned (MLA_UNSUPPORTED otherwise). The gate / up
+ *   products are rounded to bf16 before silu and the product. */
+MLA_API int mla_swiglu_mlp(const void* x, int32_t M, int32_t hidden, int32_t inter, const void* w_gate,
+                   const void* w_up, const void* w_down, void* out, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -222,3 +222,32 @@ def test_decode_attention_large_logit_jump():
         z = ql[b].astype(np.float64) @ C.T * 192.0 ** -0.5
         ref = mla.softmax_over_live(z) @ C[:, :512]
         assert_parity(got[b], ref, what=f"decode attention (logit jump) b={b}")
+
+
+@pytest.mark.parametrize("M,hidden,inter", [(33, 192, 320), (300, 1024, 512), (1, 128, 128)])
+def test_swiglu_mlp(M, hidden, inter):
+    # inter % 128 != 0 takes the two-GEMM path, the rest the paired-tile GEMM
+    rng = np.random.default_rng(M + hidden + inter)
+    x = synth.round_bf16(rng.standard_normal((M, hidden)))
+    wg = synth.round_bf16(rng.standard_normal((inter, hidden)) / np.sqrt(hidden))
+    wu = synth.round_bf16(rng.standard_normal((inter, hidden)) / np.sqrt(hidden))
+    wd = synth.round_bf16(rng.standard_normal((hidden, inter)) / np.sqrt(inter))
+    out = api.mla_swiglu_mlp(dev(x, torch.bfloat16), dev(wg, torch.bfloat16), dev(wu, torch.bfloat16),
+                             dev(wd, torch.bfloat16))
+    assert_parity(out.float().cpu().numpy(), mla.swiglu_mlp(x, wg, wu, wd), what=f"swiglu {M}x{hidden}x{inter}")
+
+
+def test_swiglu_mlp_kimi_k2_shared_expert_sampled_rows():
+    # full size (2048 tokens, hidden 7168, inter 2048); rows are independent,
+    # so the oracle on sampled rows is the oracle of the whole batch there
+    M, hidden, inter = 2048, 7168, 2048
+    g = torch.Generator(device=DEV).manual_seed(5)
+    X = torch.randn((M, hidden), generator=g, device=DEV).to(torch.bfloat16)
+    Wg = (torch.randn((inter, hidden), generator=g, device=DEV) / hidden ** 0.5).to(torch.bfloat16)
+    Wu = (torch.randn((inter, hidden), generator=g, device=DEV) / hidden ** 0.5).to(torch.bfloat16)
+    Wd = (torch.randn((hidden, inter), generator=g, device=DEV) / inter ** 0.5).to(torch.bfloat16)
+    out = api.mla_swiglu_mlp(X, Wg, Wu, Wd)
+    rows = np.array([0, 1, 255, 256, 1023, 1500, 2046, 2047])
+    f64 = lambda t: t.double().cpu().numpy()
+    ref = mla.swiglu_mlp(f64(X[rows]), f64(Wg), f64(Wu), f64(Wd))
+    assert_parity(out[rows].float().cpu().numpy(), ref, what="swiglu Kimi-K2 shared expert")
