@@ -388,3 +388,21 @@ def test_swiglu_oracle_special_case():
     # gate = 0 gives silu(0) = 0, so the output is exactly 0
     x = np.ones((2, 8))
     assert not mla.swiglu_mlp(x, np.zeros((4, 8)), np.ones((4, 8)), np.ones((8, 4))).any()
+
+
+def test_swiglu_oracle_closed_form():
+    # one input feature, gate weight ln 3: sigmoid(ln 3) = 3/4, so the hidden
+    # unit is (3/4 ln 3) * up; gate and up are told apart by their values and
+    # the down projection by its two distinct output rows
+    x = np.array([[1.0], [2.0]])
+    wg, wu, wd = np.array([[np.log(3.0)]]), np.array([[5.0]]), np.array([[2.0], [-1.0]])
+    got = mla.swiglu_mlp(x, wg, wu, wd)
+    h0 = 0.75 * np.log(3.0) * 5.0                      # token 1: gate ln 3, up 5
+    g1 = 2 * np.log(3.0)                               # token 2: gate ln 9, sigmoid 9/10
+    h1 = 0.9 * g1 * 10.0
+    np.testing.assert_allclose(got, [[2 * h0, -h0], [2 * h1, -h1]], rtol=1e-14)
+    # silu is odd-symmetric around its linear part: silu(z) - silu(-z) = z
+    z = np.array([[0.3, -1.7, 4.0]])
+    I = np.eye(3)
+    d = mla.swiglu_mlp(z, I, I, I) - mla.swiglu_mlp(-z, I, I, -I)
+    np.testing.assert_allclose(d, z * z, rtol=1e-14)
