@@ -42,6 +42,9 @@ _SIGS = {
     "mla_prefill_workspace_size": (sz, [ctypes.POINTER(MlaDims), i32, i32, i32, i32, i32]),
     "mla_prefill": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaWeights), vp, i32, i32, i32,
                                    vp, vp, i32, vp, i32, vp, vp, vp, sz, vp]),
+    "mla_prefill_cached_workspace_size": (sz, [ctypes.POINTER(MlaDims), i32, i32, i32, i32, i32]),
+    "mla_prefill_cached": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaWeights), vp, i32, i32, i32,
+                                          vp, i32, vp, vp, i32, vp, i32, vp, vp, sz, vp]),
     "mla_decode_workspace_size": (sz, [ctypes.POINTER(MlaDims), i32, i32, i32]),
     "mla_decode": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaWeights), vp, i32, vp, i32, vp,
                                   vp, vp, i32, vp, vp, sz, vp]),
@@ -153,6 +156,30 @@ def mla_prefill(dims, weights, x, rope_cos, rope_sin, out, ws, topk_idx=None, kv
     rc = lib().mla_prefill(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), _TORCH_DT[x.dtype], B, T,
                            _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], _ptr(topk_idx), k, _ptr(out),
                            _ptr(kv_cache_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc)
+    return out
+
+
+def mla_prefill_cached_workspace_size(dims, weight_dtype, B, T, start_pos, topk=0):
+    return lib().mla_prefill_cached_workspace_size(ctypes.byref(dims), weight_dtype, B, T, start_pos, topk)
+
+
+def mla_prefill_cached(dims, weights, x, start_pos, kv_cache, rope_cos, rope_sin, out, ws, topk_idx=None,
+                       stream=None):
+    """x, out [B, T, dim] bf16 at positions start_pos..start_pos+T-1; kv_cache [B, max_len, kv_lora+64]
+    bf16 (rows < start_pos read, rows start_pos..start_pos+T-1 written); topk_idx [B, T, k] int32."""
+    B, T, _ = x.shape
+    for t, n in ((x, "x"), (kv_cache, "kv_cache"), (out, "out"), (rope_cos, "rope_cos"), (rope_sin, "rope_sin"),
+                 (ws, "ws")):
+        _need(t, name=n)
+    k = 0
+    if topk_idx is not None:
+        _need(topk_idx, torch.int32, "topk_idx")
+        k = topk_idx.shape[-1]
+    rc = lib().mla_prefill_cached(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T, int(start_pos),
+                                  _ptr(kv_cache), kv_cache.shape[1], _ptr(rope_cos), _ptr(rope_sin),
+                                  rope_cos.shape[0], _ptr(topk_idx), k, _ptr(out), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream))
     _check(rc)
     return out
 

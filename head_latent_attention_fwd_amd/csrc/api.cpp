@@ -99,31 +99,35 @@ int prefill_qkv_splits(const mla_dims* d, int wdt, int adt, int M) {
   return mla::gemm_bf16_splits(qkv_args(d, adt, aligned, aligned, aligned, nullptr, M));
 }
 
-size_t prefill_layout(const mla_dims* d, int wdt, int adt, int B, int T, int topk, bool own_kvc, void* ws,
+// Tk = keys per sequence (T, or start_pos + T with a cache)
+size_t prefill_layout(const mla_dims* d, int wdt, int adt, int B, int T, int Tk, int topk, bool own_kvc, void* ws,
                       PrefillWs* out) {
   const size_t M = (size_t)B * T, H = d->n_heads, Dq = d->q_lora_rank, L = d->kv_lora_rank;
   const size_t es = adt == MLA_F32 ? 4 : 2;
   Carver c(ws);
   PrefillWs p{};
-  p.cqkv = c.take(M * (Dq + L + 64) * es);
+  p.cqkv = wdt == MLA_E4M3 ? nullptr : c.take(M * (Dq + L + 64) * es);   // e4m3: fp32 product in part
   p.cqn = c.take(M * Dq * es);
   p.kvc = own_kvc ? c.take(M * (L + 64) * es) : nullptr;
-  const size_t Mp = (size_t)B * pad64(T);
+  const size_t Mp = (size_t)B * pad64(Tk);
   p.q = c.take(M * H * 192 * es);
   p.kn = c.take(Mp * H * 128 * es);
   p.vt = c.take(Mp * H * 128 * es);
   p.kpe = c.take(Mp * 64 * es);
   p.attn = c.take(M * H * 128 * es);
-  p.mask = topk > 0 ? c.take((size_t)B * T * ((T + 31) / 32) * 4) : nullptr;
+  p.mask = topk > 0 ? c.take((size_t)B * T * ((Tk + 31) / 32) * 4) : nullptr;
   p.qkv_splits = prefill_qkv_splits(d, wdt, adt, (int)M);
-  p.part = p.qkv_splits > 1 ? (float*)c.take((size_t)p.qkv_splits * M * (Dq + L + 64) * 4) : nullptr;
+  // fp32 input of the norms: split-K partials (bf16), the whole product (e4m3)
+  const size_t nparts = wdt == MLA_E4M3 ? 1 : p.qkv_splits > 1 ? p.qkv_splits : 0;
+  p.part = nparts ? (float*)c.take(nparts * M * (Dq + L + 64) * 4) : nullptr;
   if (wdt == MLA_E4M3) {
     size_t kmax = d->dim;
     if (Dq > kmax) kmax = Dq;
     if (L > kmax) kmax = L;
     if (H * 128 > kmax) kmax = H * 128;
-    p.aq = c.take(M * kmax);
-    p.as = c.take(M * (kmax / 128) * 4);
+    const size_t rows = M > (size_t)Tk ? M : (size_t)Tk;   // kv_b over a cache runs per sequence
+    p.aq = c.take(rows * kmax);
+    p.as = c.take(rows * (kmax / 128) * 4);
   }
   if (out) *out = p;
   return c.off;
@@ -179,7 +183,7 @@ bool qkv_norm_ok(const mla::QkvNormArgs& a) {
 int project(int wdt, int adt, const void* act, int64_t lda, const void* W, const float* Ws,
             const void* W2, const float* W2s, int n_split, void* out, int64_t ldo, int M, int N, int K,
             const PrefillWs* ws, hipStream_t s, const mla::KvSplit* kv = nullptr, const mla::RopeEpi* rope = nullptr,
-            bool* roped = nullptr) {
+            bool* roped = nullptr, int cdt = -1) {
   const int epi = kv ? mla::EPI_KV_SPLIT : mla::EPI_ROWMAJOR;
   if (roped) *roped = false;
   if (wdt == MLA_E4M3) {
@@ -187,7 +191,7 @@ int project(int wdt, int adt, const void* act, int64_t lda, const void* W, const
     mla::GemmFp8Args g{};
     g.A = (const uint8_t*)ws->aq; g.a_scale = (const float*)ws->as;
     g.W = (const uint8_t*)W; g.w_scale = Ws; g.W2 = (const uint8_t*)W2; g.w2_scale = W2s; g.n_split = n_split;
-    g.C = out; g.ldc = ldo; g.c_dtype = adt; g.M = M; g.N = N; g.K = K;
+    g.C = out; g.ldc = ldo; g.c_dtype = cdt < 0 ? adt : cdt; g.M = M; g.N = N; g.K = K;
     g.epi = epi;
     if (kv) g.kv = *kv;
     if (rope) {   // RoPE of the query's rotary slices in the GEMM's epilogue, where it applies
@@ -247,13 +251,20 @@ const char* mla_last_error(void) { return g_err.c_str(); }
 size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t weight_dtype, int32_t act_dtype, int32_t B, int32_t T,
                                   int32_t topk) {
   if (check_dims(dims) != MLA_OK || B <= 0 || T <= 0) return 0;
-  return prefill_layout(dims, weight_dtype, act_dtype, B, T, topk, true, nullptr, nullptr);
+  return prefill_layout(dims, weight_dtype, act_dtype, B, T, T, topk, true, nullptr, nullptr);
 }
 
-int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int32_t adt, int32_t B, int32_t T,
-                const float* rope_cos, const float* rope_sin, int32_t rope_len, const int32_t* topk_idx,
-                int32_t topk, void* out, void* kv_cache_out, void* ws, size_t ws_bytes, void* stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// Prefill of T new tokens per sequence at positions P..P+T-1 (P = 0: empty
+// cache). cache: [B, cache_bs / (L + 64), L + 64] entries, rows [0, P) given,
+// rows [P, P + T) written here; keys are rows 0..P+T-1.
+int prefill_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t adt, int32_t B, int32_t T, int32_t P,
+                 void* cache, int64_t cache_bs, bool own_cache, const float* rope_cos, const float* rope_sin,
+                 int32_t rope_len, const int32_t* topk_idx, int32_t topk, void* out, void* ws, size_t ws_bytes,
+                 void* stream) {
   int rc = check_dims(d);
   if (rc) return rc;
   if (!w) return fail(MLA_INVALID_ARG, "weights is NULL");
@@ -262,49 +273,59 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
     return fail(MLA_UNSUPPORTED, "supported (act, weight) dtypes: (F32, F32), (BF16, BF16), (BF16, E4M3)");
   if ((rc = check_weights(w, wdt))) return rc;
   if (!x || !out || !rope_cos || !rope_sin) return fail(MLA_INVALID_ARG, "x/out/rope tables must not be NULL");
-  if (B <= 0 || T <= 0) return fail(MLA_INVALID_ARG, "B and T must be positive");
-  if ((int64_t)B * T > (1LL << 30)) return fail(MLA_INVALID_ARG, "B*T too large");
-  if (rope_len < T) return fail(MLA_INVALID_ARG, "rope_len (%d) < T (%d)", rope_len, T);
+  if (B <= 0 || T <= 0 || P < 0) return fail(MLA_INVALID_ARG, "B and T must be positive, start_pos >= 0");
+  if ((int64_t)B * (P + (int64_t)T) > (1LL << 30)) return fail(MLA_INVALID_ARG, "B*(start_pos+T) too large");
+  if (rope_len < P + T) return fail(MLA_INVALID_ARG, "rope_len (%d) < start_pos + T (%d)", rope_len, P + T);
   if ((topk_idx == nullptr) != (topk <= 0)) return fail(MLA_INVALID_ARG, "topk_idx and topk > 0 go together");
   const int H = d->n_heads, Dq = d->q_lora_rank, L = d->kv_lora_rank, dim = d->dim;
   if (wdt == MLA_E4M3 && (dim % 128 || Dq % 128 || L % 128))
     return fail(MLA_UNSUPPORTED, "e4m3 weights need dim, q_lora_rank, kv_lora_rank multiples of 128");
+  const int Tk = P + T;
   PrefillWs p;
-  const size_t need = prefill_layout(d, wdt, adt, B, T, topk, kv_cache_out == nullptr, ws, &p);
+  const size_t need = prefill_layout(d, wdt, adt, B, T, Tk, topk, own_cache, ws, &p);
   if (!ws || ws_bytes < need) return fail(MLA_INVALID_ARG, "workspace too small: need %zu bytes", need);
   if ((uintptr_t)ws & 255) return fail(MLA_INVALID_ARG, "workspace must be 256-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   const int M = B * T, NQKV = Dq + L + 64;
-  void* kvc = kv_cache_out ? kv_cache_out : p.kvc;
+  void* kvc = own_cache ? p.kvc : cache;
+  if (own_cache) cache_bs = (int64_t)T * (L + 64);
 
   // joint down-projection: [c_q | latent | k_pe] = x . [Wq_a ; Wkv_a]^T, split-K
   // into fp32 partials when its output has too few tiles for the chip
   mla::GemmArgs gq = qkv_args(d, adt, x, w->wq_a, w->wkv_a, p.cqkv, M);
-  const bool qkv_split = p.qkv_splits > 1 && mla::gemm_bf16_splits(gq) == p.qkv_splits;
+  const bool qkv_split = wdt == MLA_BF16 && p.qkv_splits > 1 && mla::gemm_bf16_splits(gq) == p.qkv_splits;
+  // e4m3: the product goes to the norms in fp32 (a bf16 rounding there would
+  // move the normalised values that kv_b and q_b quantise again)
+  const bool qkv_f32 = qkv_split || wdt == MLA_E4M3;
+  const int qkv_nsplit = qkv_split ? p.qkv_splits : 1;
   if (qkv_split) {
     gq.k_splits = p.qkv_splits; gq.part = p.part;
     LAUNCH(mla::launch_gemm_bf16(gq, s), "gemm_bf16(split-K q_a|kv_a)");
-  } else if ((rc = project(wdt, adt, x, dim, w->wq_a, w->wq_a_scale, w->wkv_a, w->wkv_a_scale, Dq, p.cqkv, NQKV, M,
-                           NQKV, dim, &p, s))) {
+  } else if ((rc = project(wdt, adt, x, dim, w->wq_a, w->wq_a_scale, w->wkv_a, w->wkv_a_scale, Dq,
+                           qkv_f32 ? (void*)p.part : p.cqkv, NQKV, M, NQKV, dim, &p, s, nullptr, nullptr, nullptr,
+                           qkv_f32 ? MLA_F32 : -1))) {
     return rc;
   }
   const size_t es = adt == MLA_F32 ? 4 : 2;
-  // the norms read either the bf16 projection or the sum of the fp32 partials
-  const void* qkv_in = qkv_split ? (const void*)p.part : p.cqkv;
-  const size_t qkv_es = qkv_split ? 4 : es;
+  // the norms read either the projection in the activation type or fp32 (partial) sums
+  const void* qkv_in = qkv_f32 ? (const void*)p.part : p.cqkv;
+  const size_t qkv_es = qkv_f32 ? 4 : es;
   auto from_qkv = [&](mla::NormRopeArgs& a) {
-    if (!qkv_split) return;
-    a.in_dtype = MLA_F32; a.in_splits = p.qkv_splits; a.split_stride = (int64_t)M * NQKV;
+    if (!qkv_f32) return;
+    a.in_dtype = MLA_F32; a.in_splits = qkv_nsplit; a.split_stride = (int64_t)M * NQKV;
   };
+  const int Tp = pad64(Tk);
   mla::QkvNormArgs qa{};
-  qa.in = qkv_in; qa.ld_in = NQKV; qa.in_dtype = qkv_split ? MLA_F32 : adt;
-  qa.in_splits = qkv_split ? p.qkv_splits : 1; qa.split_stride = (int64_t)M * NQKV;
+  qa.in = qkv_in; qa.ld_in = NQKV; qa.in_dtype = qkv_f32 ? MLA_F32 : adt;
+  qa.in_splits = qkv_nsplit; qa.split_stride = (int64_t)M * NQKV;
   qa.rows = M; qa.Dq = Dq; qa.L = L; qa.gq = w->q_norm_w; qa.gkv = w->kv_norm_w; qa.eps = d->rms_eps;
-  qa.q_out = p.cqn; qa.ld_q = Dq; qa.kv_out = kvc; qa.ld_kv = L + 64;
-  qa.kpe = p.kpe; qa.kpe_tp = pad64(T);
-  qa.cos_tab = rope_cos; qa.sin_tab = rope_sin; qa.rope_len = rope_len; qa.pos_period = T;
+  qa.q_out = p.cqn; qa.ld_q = Dq; qa.kv_out = kvc; qa.ld_kv = L + 64; qa.kv_batch_stride = cache_bs;
+  qa.kpe = p.kpe; qa.kpe_tp = Tp;
+  qa.cos_tab = rope_cos; qa.sin_tab = rope_sin; qa.rope_len = rope_len; qa.pos_period = T; qa.pos_off = P;
   if (adt == MLA_BF16 && qkv_norm_ok(qa)) {
     LAUNCH(mla::launch_qkv_norm(qa, s), "qkv_norm");
+  } else if (P > 0 || cache_bs != (int64_t)T * (L + 64)) {
+    return fail(MLA_UNSUPPORTED, "prefill over a cache needs bf16 activations and 16-byte aligned norm weights");
   } else {
   {  // q_norm
     mla::NormRopeArgs a = norm_args(qkv_in, NQKV, p.cqn, Dq, adt, M);
@@ -318,14 +339,16 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
     a.norm_dim = L; a.gamma = w->kv_norm_w; a.eps = d->rms_eps;
     a.rope_off = L; a.rope_heads = 1; a.rope_stride = 64;
     a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = rope_len; a.pos_period = T;
-    a.kpe = p.kpe; a.kpe_tp = pad64(T);
+    a.kpe = p.kpe; a.kpe_tp = Tp;
     LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(kv)");
   }
   }
-  // q = c_q . Wq_b^T, then RoPE on each head's rotary slice (in the GEMM's
-  // epilogue on the bf16 and e4m3 paths, a separate pass otherwise)
+  // q = c_q . Wq_b^T, then RoPE on each head's rotary slice at position P + t
+  // (in the GEMM's epilogue on the bf16 and e4m3 paths, a separate pass otherwise)
+  const float* cos_p = rope_cos + (int64_t)P * 32;
+  const float* sin_p = rope_sin + (int64_t)P * 32;
   mla::GemmArgs gr = gemm_args(p.cqn, Dq, w->wq_b, Dq, p.q, H * 192, adt, M, H * 192, Dq);
-  gr.epi = mla::EPI_QROPE; gr.rope = {rope_cos, rope_sin, T};
+  gr.epi = mla::EPI_QROPE; gr.rope = {cos_p, sin_p, T};
   if (wdt == MLA_BF16 && adt == MLA_BF16 && mla::gemm_bf16_qrope_ok(gr)) {
     LAUNCH(mla::launch_gemm_bf16(gr, s), "gemm_bf16(q_b + RoPE)");
   } else {
@@ -336,27 +359,73 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
     if (!roped) {
       mla::NormRopeArgs a = norm_args(p.q, H * 192, p.q, H * 192, adt, M);
       a.rope_off = 128; a.rope_heads = H; a.rope_stride = 192;
-      a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = rope_len; a.pos_period = T;
+      a.cos_tab = cos_p; a.sin_tab = sin_p; a.rope_len = rope_len - P; a.pos_period = T;
       LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(q_pe)");
     }
   }
-  // per head [k_nope | v] = c . Wkv_b^T, stored as k_nope [B,H,Tp,128] and v^T [B,H,128,Tp]
-  const int Tp = pad64(T);
-  LAUNCH(mla::launch_zero_kv_padding(p.kn, p.vt, p.kpe, B, H, T, Tp, (int)es, s), "zero_kv_padding");
-  const mla::KvSplit split{p.vt, T, Tp, H};
-  if ((rc = project(wdt, adt, kvc, L + 64, w->wkv_b, w->wkv_b_scale, nullptr, nullptr, H * 256, p.kn, 0, M,
-                    H * 256, L, &p, s, &split)))
-    return rc;
-  if (topk > 0) LAUNCH(mla::launch_topk_bitmask(topk_idx, B, T, topk, (uint32_t*)p.mask, s), "topk_to_bitmask");
+  // per head [k_nope | v] = c . Wkv_b^T over all Tk keys, stored as
+  // k_nope [B,H,Tp,128] and v^T [B,H,128,Tp]; the cached keys' k_pe joins the new ones
+  LAUNCH(mla::launch_zero_kv_padding(p.kn, p.vt, p.kpe, B, H, Tk, Tp, (int)es, s), "zero_kv_padding");
+  LAUNCH(mla::launch_gather_kpe(kvc, cache_bs, L + 64, L, B, P, p.kpe, Tp, s), "gather_kpe");
+  if (P == 0 && cache_bs == (int64_t)T * (L + 64)) {   // one launch over the B*T contiguous entries
+    const mla::KvSplit split{p.vt, T, Tp, H};
+    if ((rc = project(wdt, adt, kvc, L + 64, w->wkv_b, w->wkv_b_scale, nullptr, nullptr, H * 256, p.kn, 0, M,
+                      H * 256, L, &p, s, &split)))
+      return rc;
+  } else {
+    for (int b = 0; b < B; ++b) {   // the sequences' cache rows are cache_bs apart
+      const mla::KvSplit split{(char*)p.vt + (size_t)b * H * 128 * Tp * es, Tk, Tp, H};
+      if ((rc = project(wdt, adt, (const char*)kvc + (size_t)b * cache_bs * es, L + 64, w->wkv_b, w->wkv_b_scale,
+                        nullptr, nullptr, H * 256, (char*)p.kn + (size_t)b * H * Tp * 128 * es, 0, Tk, H * 256, L,
+                        &p, s, &split)))
+        return rc;
+    }
+  }
+  if (topk > 0)
+    LAUNCH(mla::launch_topk_bitmask(topk_idx, B, T, topk, P, Tk, (uint32_t*)p.mask, s), "topk_to_bitmask");
   mla::PrefillAttnArgs at{};
   at.q = p.q; at.kn = p.kn; at.vt = p.vt; at.kpe = p.kpe;
-  at.mask = (const uint32_t*)p.mask; at.out = p.attn; at.B = B; at.T = T; at.Tp = Tp; at.H = H;
+  at.mask = (const uint32_t*)p.mask; at.out = p.attn; at.B = B; at.T = T; at.Tp = Tp; at.H = H; at.P = P;
   at.scale = d->softmax_scale;
   if (adt == MLA_F32) LAUNCH(mla::launch_prefill_attn_f32(at, s), "prefill_attn_f32");
   else LAUNCH(mla::launch_prefill_attn_bf16(at, s), "prefill_attn");
   // out = o . Wo^T
   return project(wdt, adt, p.attn, H * 128, w->wo, w->wo_scale, nullptr, nullptr, dim, out, dim, M, dim, H * 128,
                  &p, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_prefill(const mla_dims* d, const mla_weights* w, const void* x, int32_t adt, int32_t B, int32_t T,
+                const float* rope_cos, const float* rope_sin, int32_t rope_len, const int32_t* topk_idx,
+                int32_t topk, void* out, void* kv_cache_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  const int L = d ? d->kv_lora_rank : 0;
+  return prefill_impl(d, w, x, adt, B, T, 0, kv_cache_out, (int64_t)T * (L + 64), kv_cache_out == nullptr, rope_cos,
+                      rope_sin, rope_len, topk_idx, topk, out, ws, ws_bytes, stream);
+}
+
+size_t mla_prefill_cached_workspace_size(const mla_dims* dims, int32_t weight_dtype, int32_t B, int32_t T,
+                                         int32_t start_pos, int32_t topk) {
+  if (check_dims(dims) != MLA_OK || B <= 0 || T <= 0 || start_pos < 0) return 0;
+  return prefill_layout(dims, weight_dtype, MLA_BF16, B, T, start_pos + T, topk, false, nullptr, nullptr);
+}
+
+int mla_prefill_cached(const mla_dims* d, const mla_weights* w, const void* x, int32_t B, int32_t T,
+                       int32_t start_pos, void* kv_cache, int32_t max_len, const float* rope_cos,
+                       const float* rope_sin, int32_t rope_len, const int32_t* topk_idx, int32_t topk, void* out,
+                       void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (!d) return fail(MLA_INVALID_ARG, "dims is NULL");
+  if (!kv_cache) return fail(MLA_INVALID_ARG, "kv_cache must not be NULL");
+  if (start_pos < 0 || T <= 0 || max_len <= 0 || (int64_t)start_pos + T > max_len)
+    return fail(MLA_INVALID_ARG, "need 0 <= start_pos and start_pos + T (%lld) <= max_len (%d)",
+                (long long)start_pos + T, max_len);
+  if ((uintptr_t)kv_cache & 15) return fail(MLA_UNSUPPORTED, "kv_cache must be 16-byte aligned");
+  return prefill_impl(d, w, x, MLA_BF16, B, T, start_pos, kv_cache, (int64_t)max_len * (d->kv_lora_rank + 64), false,
+                      rope_cos, rope_sin, rope_len, topk_idx, topk, out, ws, ws_bytes, stream);
 }
 
 size_t mla_decode_workspace_size(const mla_dims* dims, int32_t weight_dtype, int32_t B, int32_t max_len) {
@@ -566,7 +635,7 @@ int mla_topk_to_bitmask(const int32_t* topk_idx, int32_t B, int32_t T, int32_t t
   if (!topk_idx || !mask) return fail(MLA_INVALID_ARG, "NULL pointer");
   if (B <= 0 || T <= 0 || topk <= 0) return fail(MLA_INVALID_ARG, "bad sizes");
   if (T > 65536 * 8) return fail(MLA_UNSUPPORTED, "T too large for the LDS row buffer");
-  LAUNCH(mla::launch_topk_bitmask(topk_idx, B, T, topk, mask, (hipStream_t)stream), "topk_to_bitmask");
+  LAUNCH(mla::launch_topk_bitmask(topk_idx, B, T, topk, 0, T, mask, (hipStream_t)stream), "topk_to_bitmask");
   return MLA_OK;
 }
 

@@ -8,6 +8,10 @@
 // values per head already transposed [B, H, 128, Tp] (both written so by the
 // kv_b GEMM's epilogue) and the shared rotary key [B, Tp, 64].
 //
+// With a non-empty cache the T queries sit at positions P..P+T-1 and attend
+// keys 0..P+T-1 (the P cached keys come first in kn / vt / kpe); P = 0 is the
+// plain prefill.
+//
 // Work split: one 256-thread workgroup per (128-query tile, head, sequence);
 // the query tiles of one (sequence, head) run on one XCD, and workgroups start
 // heaviest (last query tile) first across all pairs of that XCD; wave w owns
@@ -50,7 +54,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int T = a.T, Tp = a.Tp, H = a.H;
+  const int T = a.T, Tp = a.Tp, H = a.H, P = a.P, Tk = P + T;
   // XCD-aware order: workgroup id % 8 is the XCD, and each XCD takes whole
   // (sequence, head) pairs, so the query tiles that re-read one head's keys
   // and values share that XCD's L2. Workgroups start in order of decreasing
@@ -131,10 +135,12 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
     for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
   float m = -INFINITY, l = 0.f;
   const float sl2 = a.scale * 1.4426950408889634f;
-  const int W = (T + 31) >> 5;
+  const int W = (Tk + 31) >> 5;
   const uint32_t* mrow = a.mask ? a.mask + ((int64_t)b * T + (q_ok ? qi : 0)) * W : nullptr;
+  // absolute positions of the wave's last query and of this lane's query
+  const int pw = P + qw + 31, pi = P + qi;
 
-  const int kv_end = min(T, q0 + BQ);
+  const int kv_end = min(Tk, P + q0 + BQ);
   const int ntiles = (kv_end + BKV - 1) / BKV;
   // mask words of a tile (two 32-key words per query row), fetched one tile
   // ahead and before the tile refill so that waiting for them never waits for it
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
     const uint32_t mw0 = nw0, mw1 = nw1;
     mask_words(kt + 1, nw0, nw1);
     if (kt + 1 < ntiles) issue(cur ^ 1, k0 + BKV);
-    if (k0 > qw + 31) continue;                  // every key of the tile is after this wave's queries
+    if (k0 > pw) continue;                       // every key of the tile is after this wave's queries
     const uint16_t* sb = smem + cur * STAGE;
     floatx16 s[2];
 #pragma unroll
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
       kf1 = kf2;
     }
     // s[kb][r] holds key k0 + 32kb + 16(r/8) + 8hi + r%8
-    const bool interior = !mrow && (k0 + BKV - 1 <= qw) && (k0 + BKV <= T);
+    const bool interior = !mrow && (k0 + BKV - 1 <= P + qw) && (k0 + BKV <= Tk);
     if (!interior) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
         for (int r = 0; r < 16; ++r) {
           const int kr = 16 * (r >> 3) + 8 * hi + (r & 7);
           const int t = k0 + kb * 32 + kr;
-          const bool live = t <= qi && t < T && ((bits >> kr) & 1u);
+          const bool live = t <= pi && t < Tk && ((bits >> kr) & 1u);
           s[kb][r] = live ? s[kb][r] : -INFINITY;
         }
       }
@@ -257,17 +263,17 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
 // fp32 path: one wave per (query, head); lanes split the feature dims.
 __global__ __launch_bounds__(64) void prefill_attn_f32_kernel(PrefillAttnArgs a) {
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
-  const int T = a.T, Tp = a.Tp, H = a.H;
+  const int T = a.T, Tp = a.Tp, H = a.H, Tk = a.P + T;
   const int64_t bh = (int64_t)b * H + h;
   const float* Q = (const float*)a.q + ((int64_t)b * T + s) * H * 192 + h * 192;
   const float* KN = (const float*)a.kn + bh * Tp * 128;
   const float* VT = (const float*)a.vt + bh * 128 * Tp;
   const float* KP = (const float*)a.kpe + (int64_t)b * Tp * 64;
   const float q0 = Q[lane], q1 = Q[lane + 64], q2 = Q[lane + 128];
-  const int W = (T + 31) >> 5;
+  const int W = (Tk + 31) >> 5;
   const uint32_t* mrow = a.mask ? a.mask + ((int64_t)b * T + s) * W : nullptr;
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int t = 0; t <= s; ++t) {
+  for (int t = 0; t <= a.P + s; ++t) {
     if (mrow && !((mrow[t >> 5] >> (t & 31)) & 1u)) continue;
     float d = q0 * KN[t * 128 + lane] + q1 * KN[t * 128 + lane + 64] + q2 * KP[t * 64 + lane];
     d = wave_sum(d) * a.scale;

@@ -193,10 +193,18 @@ __global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
   sq = red[0][0] + red[0][1] + red[0][2] + red[0][3];
   skv = red[1][0] + red[1][1] + red[1][2] + red[1][3];
   const float rq = 1.0f / sqrtf(sq / (float)a.Dq + a.eps), rkv = 1.0f / sqrtf(skv / (float)a.L + a.eps);
-  const int P = a.pos ? a.pos[row] : row % a.pos_period;
+  int P, bb = 0;
+  if (a.pos) {
+    P = a.pos[row];
+  } else {
+    bb = row / a.pos_period;
+    P = a.pos_off + row - bb * a.pos_period;
+  }
   uint16_t* kv = nullptr;
   if (a.kv_pos_stride > 0) {
     if (P >= 0 && P < a.kv_pos_max) kv = (uint16_t*)a.kv_out + (int64_t)row * a.ld_kv + (int64_t)P * a.kv_pos_stride;
+  } else if (a.kv_batch_stride > 0) {
+    kv = (uint16_t*)a.kv_out + (int64_t)bb * a.kv_batch_stride + (int64_t)P * a.ld_kv;
   } else {
     kv = (uint16_t*)a.kv_out + (int64_t)row * a.ld_kv;
   }
@@ -226,8 +234,7 @@ __global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
       kv[a.L + d + 32] = f2bf(y2);
     }
     if (a.kpe) {
-      const int bb = row / a.pos_period, t = row - bb * a.pos_period;
-      uint16_t* kp = (uint16_t*)a.kpe + ((int64_t)bb * a.kpe_tp + t) * 64;
+      uint16_t* kp = (uint16_t*)a.kpe + ((int64_t)bb * a.kpe_tp + P) * 64;
       kp[d] = f2bf(y1);
       kp[d + 32] = f2bf(y2);
     }
@@ -248,6 +255,18 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const uint4* g, const uin
     y[e] = gf / (1.0f + __builtin_amdgcn_exp2f(-gf * 1.4426950408889634f)) * bf2f(ue[e]);
   }
   h[i] = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+}
+
+// kpe[b, t, :] = cache[b, t, kpe_off : kpe_off + 64] for t < P, one 16-byte chunk per thread.
+__global__ __launch_bounds__(256) void gather_kpe_kernel(const uint16_t* cache, int64_t cache_ld, int row_ld,
+                                                         int kpe_off, int B, int P, uint16_t* kpe, int Tp) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)B * P * 8) return;
+  const int c = (int)(i & 7);
+  const int64_t bt = i >> 3;
+  const int b = (int)(bt / P), t = (int)(bt - (int64_t)b * P);
+  *(uint4*)(kpe + ((int64_t)b * Tp + t) * 64 + 8 * c) =
+      *(const uint4*)(cache + (int64_t)b * cache_ld + (int64_t)t * row_ld + kpe_off + 8 * c);
 }
 
 // Zero the padding keys t in [T, Tp) of kn [B,H,Tp,128], vt [B,H,128,Tp], kpe [B,Tp,64].
@@ -344,15 +363,16 @@ __global__ __launch_bounds__(256) void quant_block128_kernel(const float* w, int
 }
 
 // One block per query row: OR the picks (t <= s) into LDS words, then store.
-__global__ __launch_bounds__(256) void topk_bitmask_kernel(const int32_t* idx, int T, int k, uint32_t* mask) {
+__global__ __launch_bounds__(256) void topk_bitmask_kernel(const int32_t* idx, int T, int k, int P, int Tk,
+                                                            uint32_t* mask) {
   extern __shared__ uint32_t words[];
-  const int s = blockIdx.x, b = blockIdx.y, W = (T + 31) / 32;
+  const int s = blockIdx.x, b = blockIdx.y, W = (Tk + 31) / 32;
   for (int i = threadIdx.x; i < W; i += 256) words[i] = 0u;
   __syncthreads();
   const int32_t* row = idx + ((int64_t)b * T + s) * k;
   for (int j = threadIdx.x; j < k; j += 256) {
     const int t = row[j];
-    if (t >= 0 && t <= s && t < T) atomicOr(&words[t >> 5], 1u << (t & 31));
+    if (t >= 0 && t <= P + s && t < Tk) atomicOr(&words[t >> 5], 1u << (t & 31));
   }
   __syncthreads();
   uint32_t* out = mask + ((int64_t)b * T + s) * W;
@@ -417,9 +437,21 @@ hipError_t launch_silu_mul(const void* g, const void* u, void* h, int64_t n, hip
   return hipGetLastError();
 }
 
-hipError_t launch_topk_bitmask(const int32_t* idx, int B, int T, int k, uint32_t* mask, hipStream_t s) {
+hipError_t launch_topk_bitmask(const int32_t* idx, int B, int T, int k, int P, int Tk, uint32_t* mask, hipStream_t s) {
+  if (P < 0 || Tk < P + T || (Tk + 31) / 32 * 4 > 65536) return hipErrorInvalidValue;
   dim3 grid(T, B);
-  topk_bitmask_kernel<<<grid, 256, ((T + 31) / 32) * 4, s>>>(idx, T, k, mask);
+  topk_bitmask_kernel<<<grid, 256, ((Tk + 31) / 32) * 4, s>>>(idx, T, k, P, Tk, mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_kpe(const void* cache, int64_t cache_ld, int row_ld, int kpe_off, int B, int P, void* kpe,
+                             int Tp, hipStream_t s) {
+  if (P <= 0) return hipSuccess;
+  if (P > Tp || (row_ld & 7) || (kpe_off & 7) || (cache_ld & 7) || (((uintptr_t)cache | (uintptr_t)kpe) & 15))
+    return hipErrorInvalidValue;
+  const int64_t n = (int64_t)B * P * 8;   // 16-byte chunks
+  gather_kpe_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const uint16_t*)cache, cache_ld, row_ld, kpe_off, B,
+                                                                P, (uint16_t*)kpe, Tp);
   return hipGetLastError();
 }
 

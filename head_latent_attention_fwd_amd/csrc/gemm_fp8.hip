@@ -309,6 +309,32 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
   __builtin_amdgcn_s_waitcnt(fb_wait(0, 0));
   __syncthreads();
 
+  if (g.c_dtype == DT_F32) {
+    // fp32 row-major output straight from the accumulators: a lane holds 4
+    // consecutive columns of one row per result group
+    float* Cf = (float*)g.C;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float sr = i ? srun1 : srun0;
+      const int m = m0 + wm * 64 + i * 32 + l32;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int n = n0 + wn * 128 + j * 32 + 8 * rg + 4 * hi;
+          const float4 v = make_float4(acc[i][j][4 * rg] * sr, acc[i][j][4 * rg + 1] * sr,
+                                       acc[i][j][4 * rg + 2] * sr, acc[i][j][4 * rg + 3] * sr);
+          if (n + 4 <= nend) {
+            *(float4*)(Cf + (int64_t)m * g.ldc + n) = v;
+          } else {
+            const float e[4] = {v.x, v.y, v.z, v.w};
+            for (int k = 0; k < 4 && n + k < nend; ++k) Cf[(int64_t)m * g.ldc + n + k] = e[k];
+          }
+        }
+    }
+    return;
+  }
   // epilogue: rows 0..127 of the bf16 C tile in s0, 128..255 in s1
   auto crow = [&](int row) -> uint16_t* { return (uint16_t*)(row < 128 ? s0 : s1) + (row & 127) * FB_CP; };
 #pragma unroll
@@ -404,7 +430,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
 int fb_cdiv(int a, int b) { return (a + b - 1) / b; }
 bool fp8_big_ok(const GemmFp8Args& g) {
   const int nsp = g.W2 ? g.n_split : g.N;
-  return g.c_dtype == DT_BF16 && g.M >= 256 && g.N >= 256 && g.K % 128 == 0 && (int64_t)g.M * g.K < (1LL << 31) &&
+  return (g.c_dtype == DT_BF16 || (g.c_dtype == DT_F32 && g.epi == EPI_ROWMAJOR && (g.ldc & 3) == 0)) && g.M >= 256 && g.N >= 256 && g.K % 128 == 0 && (int64_t)g.M * g.K < (1LL << 31) &&
          (int64_t)g.N * g.K < (1LL << 31) && (!g.W2 || (nsp % 128 == 0 && nsp < g.N)) &&
          (g.epi != EPI_KV_SPLIT || g.N % 256 == 0) && (g.ldc & 7) == 0 && (((uintptr_t)g.C) & 15) == 0 &&
          (((uintptr_t)g.A | (uintptr_t)g.W | (uintptr_t)g.W2) & 15) == 0;

@@ -111,10 +111,14 @@ struct QkvNormArgs {
   int rows, Dq, L;
   const float* gq; const float* gkv; float eps;
   void* q_out; int64_t ld_q;
-  void* kv_out; int64_t ld_kv; int64_t kv_pos_stride; int kv_pos_max;
-  void* kpe; int kpe_tp;   // optional copy of the rotated k_pe: row m = b*T + t -> kpe[(b*kpe_tp + t)*64]
+  // kv entry of row m: with kv_pos_stride > 0 (decode) kv_out + m*ld_kv + pos[m]*kv_pos_stride;
+  // else with kv_batch_stride > 0 kv_out + b*kv_batch_stride + (pos_off + t)*ld_kv
+  // (m = b*pos_period + t); else kv_out + m*ld_kv
+  void* kv_out; int64_t ld_kv; int64_t kv_pos_stride; int kv_pos_max; int64_t kv_batch_stride;
+  void* kpe; int kpe_tp;   // optional copy of the rotated k_pe: row m -> kpe[(b*kpe_tp + pos_off + t)*64]
   const float* cos_tab; const float* sin_tab; int rope_len;
-  const int32_t* pos; int pos_period;
+  // position of row m: pos[m] if pos is set, else pos_off + m % pos_period
+  const int32_t* pos; int pos_period; int pos_off;
 };
 hipError_t launch_qkv_norm(const QkvNormArgs& a, hipStream_t s);
 hipError_t launch_rope_table(float* c, float* sn, int n_pos, float base, hipStream_t s);
@@ -123,16 +127,24 @@ hipError_t launch_quant_1x128(const void* a, int64_t lda, int a_dtype, int M, in
 hipError_t launch_quant_block128(const float* w, int N, int K, uint8_t* q, float* scales, hipStream_t s);
 // h[i] = silu(g[i]) * u[i] over n bf16 values (n % 8 == 0, 16-byte aligned).
 hipError_t launch_silu_mul(const void* g, const void* u, void* h, int64_t n, hipStream_t s);
-hipError_t launch_topk_bitmask(const int32_t* idx, int B, int T, int k, uint32_t* mask, hipStream_t s);
+// mask [B, T, ceil(Tk/32)]: bit t of row (b, s) is set iff t appears in
+// idx[b, s, :] and t <= P + s (query s sits at position P + s) and t < Tk.
+hipError_t launch_topk_bitmask(const int32_t* idx, int B, int T, int k, int P, int Tk, uint32_t* mask, hipStream_t s);
+// Copies the rotated shared keys of cache rows [0, P) ([B, cache_ld] per
+// sequence, k_pe at element offset kpe_off of each row_ld-wide row) into kpe [B, Tp, 64].
+hipError_t launch_gather_kpe(const void* cache, int64_t cache_ld, int row_ld, int kpe_off, int B, int P, void* kpe,
+                             int Tp, hipStream_t s);
 
-// Prefill attention. q [B*T, H*192] (rope applied), kn [B, H, Tp, 128],
-// vt [B, H, 128, Tp], kpe [B, Tp, 64] (rotated shared key), optional bitmask
-// [B, T, ceil(T/32)], out [B*T, H*128]. Tp = T rounded up to 64; the padding
-// keys (t >= T) of kn, vt and kpe must hold finite values.
+// Prefill attention. T queries per sequence at positions P..P+T-1 over the
+// Tk = P + T keys 0..P+T-1 (P = 0: empty cache). q [B*T, H*192] (rope
+// applied), kn [B, H, Tp, 128], vt [B, H, 128, Tp], kpe [B, Tp, 64] (rotated
+// shared key), optional bitmask [B, T, ceil(Tk/32)], out [B*T, H*128].
+// Tp = Tk rounded up to 64; the padding keys (t >= Tk) of kn, vt and kpe must
+// hold finite values.
 struct PrefillAttnArgs {
   const void* q; const void* kn; const void* vt; const void* kpe;
   const uint32_t* mask; void* out;
-  int B, T, Tp, H; float scale;
+  int B, T, Tp, H; float scale; int P;
 };
 // Zeroes the padding keys t in [T, Tp) of kn, vt and kpe (no-op when T == Tp).
 hipError_t launch_zero_kv_padding(void* kn, void* vt, void* kpe, int B, int H, int T, int Tp, int elem_bytes,

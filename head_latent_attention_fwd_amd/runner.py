@@ -64,6 +64,32 @@ class Prefill:
                                topk_idx=self.topk, kv_cache_out=self.kv_cache, stream=stream)
 
 
+class PrefillCached:
+    """One prefill chunk of T tokens after start_pos cached ones, over a
+    [B, max_len, kv_lora + 64] bf16 cache (rows < start_pos given)."""
+
+    def __init__(self, cfg, inp, start_pos, device="cuda"):
+        self.cfg = cfg
+        B, T = cfg["B"], cfg["T"]
+        self.start_pos = start_pos
+        self.dims = dims_of(cfg)
+        self.wdt = _WDT[cfg["weight"]]
+        self.x = to_dev(inp["x"], torch.bfloat16, device)
+        self.w = device_weights(inp["w"], cfg["weight"], device)
+        self.weights = api.make_weights(self.w, self.wdt)
+        self.cache = to_dev(inp["cache"], torch.bfloat16, device)
+        self.cos, self.sin = api.mla_rope_table(self.cache.shape[1], device=device)
+        self.topk = None if inp.get("topk_idx") is None else to_dev(inp["topk_idx"], torch.int32, device)
+        self.out = torch.empty_like(self.x)
+        k = 0 if self.topk is None else self.topk.shape[-1]
+        self.ws = api.workspace(api.mla_prefill_cached_workspace_size(self.dims, self.wdt, B, T, start_pos, k),
+                                device)
+
+    def run(self, stream=None):
+        return api.mla_prefill_cached(self.dims, self.weights, self.x, self.start_pos, self.cache, self.cos,
+                                      self.sin, self.out, self.ws, topk_idx=self.topk, stream=stream)
+
+
 class Decode:
     """One single-token MLA decode step over a [B, max_len, 576] bf16 cache."""
 

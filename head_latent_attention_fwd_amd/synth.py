@@ -83,15 +83,18 @@ def _draw_weights(rng, cfg):
     return w
 
 
-def draw_topk(rng, B, T, k):
+def draw_topk(rng, B, T, k, start=0):
+    """Row s (at position start + s) keeps every earlier key if it has at most
+    k, else itself plus k - 1 distinct earlier keys drawn uniformly."""
     idx = np.full((B, T, k), -1, dtype=np.int32)
     for b in range(B):
         for s in range(T):
-            if s < k:
-                idx[b, s, :s + 1] = np.arange(s + 1)
+            p = start + s
+            if p < k:
+                idx[b, s, :p + 1] = np.arange(p + 1)
             else:
-                pick = rng.choice(s, k - 1, replace=False)
-                idx[b, s] = np.sort(np.append(pick, s))
+                pick = rng.choice(p, k - 1, replace=False)
+                idx[b, s] = np.sort(np.append(pick, p))
     return idx
 
 
@@ -109,6 +112,23 @@ def gen_prefill(cfg, seed):
     w = _draw_weights(rng, cfg)
     topk = draw_topk(rng, B, T, cfg["topk"]) if cfg.get("topk") else None
     return dict(x=x, w=w, topk_idx=topk)
+
+
+def gen_chunk(cfg, seed, start_pos, max_len=None):
+    """Inputs of a prefill chunk after start_pos cached tokens: x [B,T,dim], w,
+    cache [B,max_len,L+64] with rows < start_pos drawn like gen_decode's,
+    topk_idx over absolute positions or None."""
+    rng = np.random.default_rng(seed)
+    B, T, L = cfg["B"], cfg["T"], cfg["kv_lora_rank"]
+    max_len = max_len or (start_pos + T)
+    x = round_to(rng.standard_normal((B, T, cfg["dim"])), "bf16")
+    w = _draw_weights(rng, cfg)
+    cache = np.zeros((B, max_len, L + KV_ROPE), dtype=np.float32)
+    lat = w["kv_norm_w"][None, None, :] * rng.standard_normal((B, start_pos, L))
+    cache[:, :start_pos, :L] = round_to(lat, "bf16")
+    cache[:, :start_pos, L:] = round_to(rng.standard_normal((B, start_pos, KV_ROPE)), "bf16")
+    topk = draw_topk(rng, B, T, cfg["topk"], start_pos) if cfg.get("topk") else None
+    return dict(x=x, w=w, cache=cache, topk_idx=topk)
 
 
 def gen_decode(cfg, seed, max_len=None):

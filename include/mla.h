@@ -123,6 +123,35 @@ MLA_API int mla_prefill(const mla_dims* dims, const mla_weights* w, const void* 
                 const int32_t* topk_idx, int32_t topk, void* out, void* kv_cache_out,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of workspace mla_prefill_cached needs (0 on invalid input). */
+MLA_API size_t mla_prefill_cached_workspace_size(const mla_dims* dims, int32_t weight_dtype, int32_t B, int32_t T,
+                                         int32_t start_pos, int32_t topk);
+
+/* MLA prefill of a chunk of T new tokens per sequence after start_pos cached
+ * ones (chunked prefill). The pages define prefill with an empty cache
+ * (DeepSeek-V3.2-Exp · Sparse attention, mode prefill) and the cache as the
+ * per-position [normalised latent | rotated k_pe] that decode scores
+ * (Explanation there); this entry point reads them together: token s of the
+ * chunk sits at position start_pos + s, its entry is written to
+ * kv_cache[b, start_pos + s], and it attends keys 0..start_pos+s, the cached
+ * ones up-projected by kv_b exactly like the chunk's own. With start_pos = 0
+ * the result is mla_prefill's; chaining chunks gives the rows of one prefill
+ * over their concatenation.
+ *   x         [B, T, dim] bf16
+ *   kv_cache  [B, max_len, kv_lora_rank + 64] bf16, in/out: rows [0, start_pos)
+ *             are read, rows [start_pos, start_pos + T) are written; 16-byte aligned
+ *   start_pos >= 0, start_pos + T <= max_len (same for every sequence)
+ *   rope_cos, rope_sin  fp32 [rope_len, 32], rope_len >= start_pos + T
+ *   topk_idx  [B, T, topk] int32 or NULL: absolute key positions; key t is live
+ *             for chunk row s iff t <= start_pos + s and (no topk_idx or t is
+ *             listed in row (b, s)); -1 pads
+ *   out       [B, T, dim] bf16
+ * Weights bf16 or e4m3 (block-scaled, as for mla_prefill). */
+MLA_API int mla_prefill_cached(const mla_dims* dims, const mla_weights* w, const void* x, int32_t B, int32_t T,
+                       int32_t start_pos, void* kv_cache, int32_t max_len, const float* rope_cos,
+                       const float* rope_sin, int32_t rope_len, const int32_t* topk_idx, int32_t topk, void* out,
+                       void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of workspace mla_decode needs (0 on invalid input). */
 MLA_API size_t mla_decode_workspace_size(const mla_dims* dims, int32_t weight_dtype, int32_t B, int32_t max_len);
 

@@ -230,6 +230,42 @@ def mla_prefill(x, w, d, topk_idx=None, rows=None, fp8=False, return_aux=False):
     return (out, aux) if return_aux else out
 
 
+def mla_prefill_cached(x, w, d, cache, start_pos, topk_idx=None, rows=None, fp8=False):
+    """Prefill of a chunk after start_pos cached tokens. The pages define the
+    prefill with an empty cache ([SA] "Code", mode prefill) and the cache as
+    the per-position [normalised latent | rotated k_pe] entries that decode
+    scores ([SA] "Explanation"); read together, chunk token s sits at position
+    P + s (P = start_pos), makes its entry like any prefill token, and attends
+    keys 0..P+s: the cached entries followed by the chunk's own, all
+    up-projected by kv_b as in prefill.
+
+    x: [B, T, dim]; cache: [B, >= P, kv_lora + 64] entries of positions 0..P-1;
+    topk_idx: optional [B, T, k] absolute key positions (-1 pads); rows:
+    optional chunk rows to evaluate. Returns (out [B, len(rows), dim], the
+    chunk's entries [B, T, kv_lora + 64])."""
+    x = np.asarray(x, dtype=np.float64)
+    B, T, _ = x.shape
+    P = int(start_pos)
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    fq = quantise_weights(w) if fp8 else None
+    H = d["n_heads"]
+    L = d["kv_lora_rank"]
+    out = np.zeros((B, len(rows), d["dim"]))
+    entries = np.zeros((B, T, L + ROPE))
+    for b in range(B):
+        entries[b] = latent_path(x[b], w, d, P + np.arange(T), fq)
+        C = np.concatenate([np.asarray(cache[b, :P], dtype=np.float64).reshape(P, L + ROPE), entries[b]], axis=0)
+        k_nope, v = up_project(C[:, :L], w, d, fq)
+        q_nope, q_pe = query_path(x[b, rows], w, d, P + rows, fq)
+        o = np.zeros((len(rows), H * VDIM))
+        for i, s in enumerate(rows):
+            live = live_keys(P + int(s), None if topk_idx is None else topk_idx[b, s])
+            o_h, _ = attend_row(q_nope[i], q_pe[i], k_nope, C[:, L:], v, live, d["softmax_scale"])
+            o[i] = o_h.reshape(-1)
+        out[b] = _proj(o, w, "wo", fq)
+    return out, entries
+
+
 # ----------------------------------------------------------------------------
 # decode
 

@@ -148,3 +148,83 @@ def test_prefill_is_deterministic():
     run.run()
     torch.cuda.synchronize()
     assert torch.equal(a, run.out)
+
+
+# --------------------------------------------------------------------------
+# prefill over a non-empty cache (chunked prefill)
+
+def _check_chunk(cfg, seed, start_pos, max_len, rows=None, tol=BF16_TOL, cos=0.9999):
+    inp = synth.gen_chunk(cfg, seed, start_pos, max_len)
+    run = runner.PrefillCached(cfg, inp, start_pos)
+    run.run()
+    torch.cuda.synchronize()
+    d = oracle_dims(cfg)
+    ref, entries = mla.mla_prefill_cached(inp["x"], inp["w"], d, inp["cache"][:, :start_pos], start_pos,
+                                          topk_idx=inp["topk_idx"], rows=rows, fp8=cfg["weight"] == "e4m3")
+    got = run.out.float().cpu().numpy()
+    assert_parity(got if rows is None else got[:, rows], ref, tol=tol, cos=cos, what=f"{cfg['name']} chunk")
+    cache = run.cache.float().cpu().numpy()
+    T = cfg["T"]
+    assert_parity(cache[:, start_pos:start_pos + T], entries, tol=tol, cos=cos, what="chunk cache entries")
+    # rows before the chunk are read only, rows after it untouched
+    np.testing.assert_array_equal(cache[:, :start_pos], inp["cache"][:, :start_pos])
+    assert not cache[:, start_pos + T:].any()
+    return run
+
+
+def test_prefill_cached_small_bf16():
+    _check_chunk(small_cfg(T=100, B=2), 41, start_pos=150, max_len=300)
+
+
+def test_prefill_cached_small_topk_ragged():
+    _check_chunk(small_cfg(T=90, B=1, topk=40, n_heads=2), 42, start_pos=77, max_len=200)
+
+
+def test_prefill_cached_small_fp8():
+    _check_chunk(small_cfg(T=70, B=2, dim=1024, q_lora_rank=512, kv_lora_rank=512, n_heads=2, weight="e4m3"), 43,
+                 start_pos=64, max_len=160, tol=FP8_TOL, cos=0.999)
+
+
+def test_prefill_cached_start_zero_and_single_token():
+    _check_chunk(small_cfg(T=65, B=2), 44, start_pos=0, max_len=100)
+    _check_chunk(small_cfg(T=1, B=3), 45, start_pos=33, max_len=40)
+
+
+def test_prefill_chunks_chain_to_one_prefill():
+    """Two chunks through one device cache give the rows of one prefill over both."""
+    cfg = small_cfg(T=200, B=2)
+    inp = synth.gen_prefill(cfg, 46)
+    d = oracle_dims(cfg)
+    ref = mla.mla_prefill(inp["x"], inp["w"], d)
+    P = 120
+    parts = []
+    cache = None
+    for lo, hi in ((0, P), (P, 200)):
+        c = dict(cfg, T=hi - lo)
+        sub = dict(x=inp["x"][:, lo:hi], w=inp["w"], topk_idx=None,
+                   cache=np.zeros((2, 256, cfg["kv_lora_rank"] + 64), dtype=np.float32))
+        run = runner.PrefillCached(c, sub, lo)
+        if cache is not None:
+            run.cache.copy_(cache)
+        run.run()
+        torch.cuda.synchronize()
+        cache = run.cache
+        parts.append(run.out.float().cpu().numpy())
+    assert_parity(np.concatenate(parts, axis=1), ref, what="chained chunks")
+
+
+def test_prefill_cached_kimi_k2_full_size_sampled():
+    # a 2048-token chunk after 2048 cached tokens, Kimi-K2 shapes
+    cfg = config(1)
+    rows = _sample_rows(cfg["T"], np.random.default_rng(5))
+    _check_chunk(cfg, 47, start_pos=2048, max_len=4096, rows=rows)
+
+
+def test_prefill_cached_rejects_overflowing_chunk():
+    from head_latent_attention_fwd_amd import api
+    cfg = small_cfg(T=10, B=1)
+    inp = synth.gen_chunk(cfg, 48, 5, max_len=16)
+    run = runner.PrefillCached(cfg, inp, 5)
+    run.start_pos = 7        # 7 + 10 > 16
+    with pytest.raises(api.MlaError):
+        run.run()

@@ -355,6 +355,43 @@ def test_decode_equals_last_row_of_prefill():
     np.testing.assert_allclose(entry[0], aux["cache"][0][P], rtol=1e-13, atol=1e-14)
 
 
+def test_chunked_prefill_equals_one_prefill():
+    """Two chunks (the second over the cache the first made) give the rows of
+    one prefill over both, and the second chunk's entries are that prefill's."""
+    cfg, d, inp = small(T=21, B=2, seed=23)
+    out, aux = mla.mla_prefill(inp["x"], inp["w"], d, return_aux=True)
+    P = 13
+    o1, e1 = mla.mla_prefill_cached(inp["x"][:, :P], inp["w"], d, np.zeros((2, 0, 16 + 64)), 0)
+    o2, e2 = mla.mla_prefill_cached(inp["x"][:, P:], inp["w"], d, e1, P)
+    np.testing.assert_allclose(o1, out[:, :P], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(o2, out[:, P:], rtol=1e-11, atol=1e-12)
+    for b in range(2):
+        np.testing.assert_allclose(e2[b], aux["cache"][b][P:], rtol=1e-13, atol=1e-14)
+
+
+def test_chunked_prefill_with_selection_equals_one_prefill():
+    cfg, d, inp = small(T=20, seed=29)
+    rng = np.random.default_rng(3)
+    idx = np.full((1, 20, 5), -1, dtype=np.int64)
+    for s in range(20):
+        k = min(s + 1, 5)
+        idx[0, s, :k] = rng.choice(s + 1, k, replace=False)
+    out, aux = mla.mla_prefill(inp["x"], inp["w"], d, topk_idx=idx, return_aux=True)
+    P = 8
+    o2, _ = mla.mla_prefill_cached(inp["x"][:, P:], inp["w"], d, aux["cache"][0][None, :P], P, topk_idx=idx[:, P:])
+    np.testing.assert_allclose(o2, out[:, P:], rtol=1e-11, atol=1e-12)
+
+
+def test_one_token_chunk_equals_decode():
+    cfg, d, inp = small(T=9, seed=31)
+    rng = np.random.default_rng(4)
+    cache = rng.standard_normal((1, 30, 16 + 64))
+    o1, e1 = mla.mla_prefill_cached(inp["x"][:, :1], inp["w"], d, cache, 25)
+    o2, e2 = mla.mla_decode(inp["x"][:, 0], inp["w"], d, cache, np.array([25]))
+    np.testing.assert_allclose(o1[:, 0], o2, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(e1[:, 0], e2, rtol=1e-13, atol=1e-14)
+
+
 # --------------------------------------------------------------------------
 # selection mask
 
