@@ -6,7 +6,8 @@ A step is one whole pass of the path over one batch of synthetic input that is
 already resident in HBM: mla_prefill (x -> out) or mla_decode (x, cache -> out).
 The headline value is the Kimi-K2-shaped bf16 prefill (B=1, T=2048, H=64) in
 algorithmic TFLOP/s; the other workloads (fp8-weight prefill, sparse
-DeepSeek-V3.2-Exp prefill, absorbed decode, Kimi-K2 shared-expert MLP) are
+DeepSeek-V3.2-Exp prefill, absorbed decode with bf16 and with e4m3 weights,
+Kimi-K2 shared-expert MLP, chunked prefill over a 2048-token cache) are
 reported beside it. Prints one
 JSON line.
 """
@@ -52,7 +53,9 @@ def prefill_flops(cfg, topk_idx=None):
 def decode_bytes(cfg):
     H, Dq, L, d, B, P = (cfg["n_heads"], cfg["q_lora_rank"], cfg["kv_lora_rank"], cfg["dim"], cfg["B"],
                          cfg["cache_len"])
-    w = 2 * ((Dq + L + 64) * d + H * 192 * Dq + H * 256 * L + d * H * 128)
+    n_w = (Dq + L + 64) * d + H * 192 * Dq + H * 256 * L + d * H * 128
+    # bf16: 2 bytes a weight; e4m3: 1 byte plus one fp32 scale per 128 x 128 block
+    w = n_w + 4 * n_w // (128 * 128) if cfg.get("weight") == "e4m3" else 2 * n_w
     cache = 2 * B * (P + 1) * (L + 64)
     io = 2 * (2 * B * d + B * (L + 64))
     return w + cache + io, {"weights": w, "cache": cache, "io": io}
@@ -195,17 +198,17 @@ def prefill_kernel_breakdown(cfg, inp, run):
     return out
 
 
-def bench_decode(cfg_index, steps, warmup, kernels=False):
+def bench_decode(cfg_index, steps, warmup, kernels=False, weight="bf16"):
     import torch
     from head_latent_attention_fwd_amd import api, runner, synth
-    cfg = synth.CONFIGS[cfg_index]
+    cfg = dict(synth.CONFIGS[cfg_index], weight=weight)
     inp = synth.gen_decode(cfg, synth.seed_of(cfg_index))
     run = runner.Decode(cfg, inp)
     nbytes, parts = decode_bytes(cfg)
     flush = Flusher()
     sec = event_avg(run.run, steps, warmup=warmup, flush=flush)   # cache slot P is rewritten identically each step
-    res = {"workload": cfg["name"], "B": cfg["B"], "cache_len": cfg["cache_len"], "n_heads": cfg["n_heads"],
-           "us_per_step": sec * 1e6, "gbps": nbytes / sec / 1e9, "frac_of_hbm": nbytes / sec / 1e9 / PEAK["hbm"],
+    res = {"workload": cfg["name"] + ("_e4m3" if weight == "e4m3" else ""), "B": cfg["B"],
+           "cache_len": cfg["cache_len"], "n_heads": cfg["n_heads"], "weights": weight, "us_per_step": sec * 1e6, "gbps": nbytes / sec / 1e9, "frac_of_hbm": nbytes / sec / 1e9 / PEAK["hbm"],
            "algorithmic_bytes": nbytes, "bytes": parts, "timing": "HIP events per step, 1 GiB read between steps (caches hold nothing of the step)"}
     if kernels:
         B, H = cfg["B"], cfg["n_heads"]
@@ -215,6 +218,27 @@ def bench_decode(cfg_index, steps, warmup, kernels=False):
         res["kernels"] = {"attention": {"us": s * 1e6, "gbps": parts["cache"] / s / 1e9,
                                         "frac": parts["cache"] / s / 1e9 / PEAK["hbm"], "bytes": parts["cache"]}}
     del run, flush
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_chunk(steps, warmup, start_pos=2048):
+    """Kimi-K2 bf16 prefill of a 2048-token chunk after start_pos cached tokens
+    (B = 1, H = 64): kv_b runs over all start_pos + 2048 latents."""
+    import torch
+    from head_latent_attention_fwd_amd import runner, synth
+    cfg = synth.CONFIGS[1]
+    inp = synth.gen_chunk(cfg, 6, start_pos)
+    run = runner.PrefillCached(cfg, inp, start_pos)
+    H, Dq, L, d, T = cfg["n_heads"], cfg["q_lora_rank"], cfg["kv_lora_rank"], cfg["dim"], cfg["T"]
+    pairs = T * start_pos + T * (T + 1) // 2
+    flop = (2 * T * (Dq + L + 64) * d + 2 * T * H * 192 * Dq + 2 * (start_pos + T) * H * 256 * L
+            + 2 * T * d * H * 128 + 640 * H * pairs)
+    sec = wall_steps(run.run, steps, warmup)
+    res = {"workload": "kimi_k2_bf16_chunked_prefill", "B": 1, "T": T, "start_pos": start_pos, "n_heads": H,
+           "ms_per_step": sec * 1e3, "tflops": flop / sec / 1e12, "frac_of_bf16_peak": flop / sec / 1e12 / PEAK["bf16"],
+           "algorithmic_flop": flop}
+    del run
     torch.cuda.empty_cache()
     return res
 
@@ -293,8 +317,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
-    ap.add_argument("--workloads", default="1,2,3,4,5",
-                    help="config indices to run (1 = headline; 5 = shared-expert SwiGLU MLP)")
+    ap.add_argument("--workloads", default="1,2,3,4,5,6,7",
+                    help="config indices to run (1 = headline; 5 = shared-expert SwiGLU MLP; "
+                         "6 = chunked prefill after 2048 cached tokens; 7 = decode with e4m3 weights)")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel event breakdown")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -315,6 +340,10 @@ def main():
             results[i] = bench_decode(i, args.steps, args.warmup, kernels)
         elif i == 5:
             results[i] = bench_swiglu(args.steps, args.warmup)
+        elif i == 6:
+            results[i] = bench_chunk(args.steps, args.warmup)
+        elif i == 7:
+            results[i] = bench_decode(4, args.steps, args.warmup, weight="e4m3")
         else:
             results[i], _ = bench_prefill(i, args.steps, args.warmup, kernels and i == 1)
         if i == 1:

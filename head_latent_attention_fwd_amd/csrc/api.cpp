@@ -135,12 +135,13 @@ size_t prefill_layout(const mla_dims* d, int wdt, int adt, int B, int T, int Tk,
 
 struct DecodeWs {
   void *part, *cqn, *q, *qlat, *olat, *o;
+  void *aq, *as;   // e4m3 weights: the quantised activation of the current projection
 };
 
 // split-K factors of the two decode projections with long K
 constexpr int DEC_SPLIT_QKV = 8, DEC_SPLIT_WO = 4;
 
-size_t decode_layout(const mla_dims* d, int B, void* ws, DecodeWs* out) {
+size_t decode_layout(const mla_dims* d, int wdt, int B, void* ws, DecodeWs* out) {
   const size_t H = d->n_heads, Dq = d->q_lora_rank, L = d->kv_lora_rank;
   Carver c(ws);
   DecodeWs p{};
@@ -151,6 +152,13 @@ size_t decode_layout(const mla_dims* d, int B, void* ws, DecodeWs* out) {
   p.qlat = c.take((size_t)B * H * 576 * 2);
   p.olat = c.take((size_t)B * H * 512 * 2);
   p.o = c.take((size_t)B * H * 128 * 2);
+  if (wdt == MLA_E4M3) {   // widest activation: o_lat [B*H, 512] or x [B, dim]
+    size_t kmax = H * 512;
+    if ((size_t)d->dim > kmax) kmax = d->dim;
+    if (Dq > kmax) kmax = Dq;
+    p.aq = c.take((size_t)B * kmax);
+    p.as = c.take((size_t)B * (kmax / 128) * 4);
+  }
   if (out) *out = p;
   return c.off;
 }
@@ -239,6 +247,40 @@ int skinny(const void* A, int64_t lda, int64_t batch_a, const void* W, int64_t l
     LAUNCH(mla::launch_gemm_skinny(g, nt, splits, s), "gemm_skinny");
   }
   return MLA_OK;
+}
+
+// e4m3 x e4m3 decode-shaped product: A codes [M, K] (row stride lda bytes) with
+// 1x128 scales (row stride lds), W codes with 128x128 block scales (row stride
+// ldws = K/128); rows in chunks of 128, split-K chunks of at most 4096.
+int skinny_fp8(const void* A, int64_t lda, int64_t batch_a, const float* as, int64_t lds, int64_t batch_as,
+               const void* W, int64_t ldw, int64_t batch_w, const float* ws, int ldws, int64_t batch_ws,
+               const void* W2, int64_t ldw2, const float* ws2, int n_split, void* C, int64_t ldc, int64_t batch_c,
+               float* P, int M, int N, int K, int batch, int nt, int splits, hipStream_t s) {
+  const int kblocks = K / 128;
+  if (splits < (kblocks + 31) / 32) splits = (kblocks + 31) / 32;
+  if (splits > kblocks) splits = kblocks;
+  const int kc = ((kblocks + splits - 1) / splits) * 128;
+  splits = (K + kc - 1) / kc;
+  if (splits > 1 && !P) return fail(MLA_INVALID_ARG, "split-K product without a partial buffer");
+  for (int m0 = 0; m0 < M; m0 += 128) {
+    mla::SkinnyArgs g{};
+    g.A = (const uint8_t*)A + (int64_t)m0 * lda; g.lda = lda; g.batch_a = batch_a;
+    g.as = as + (int64_t)m0 * lds; g.lds = lds; g.batch_as = batch_as;
+    g.W = W; g.ldw = ldw; g.batch_w = batch_w; g.ws = ws; g.ldws = ldws; g.batch_ws = batch_ws;
+    g.W2 = W2; g.ldw2 = ldw2; g.ws2 = ws2; g.n_split = W2 ? n_split : N;
+    g.C = C ? (void*)((uint16_t*)C + (int64_t)m0 * ldc) : nullptr; g.ldc = ldc; g.batch_c = batch_c;
+    g.P = P ? P + (int64_t)m0 * N : nullptr; g.ps = (int64_t)M * N;
+    g.M = M - m0 < 128 ? M - m0 : 128; g.N = N; g.K = K; g.kc = kc; g.batch = batch;
+    LAUNCH(mla::launch_gemm_skinny_fp8(g, nt, splits, s), "gemm_skinny_fp8");
+  }
+  return MLA_OK;
+}
+int skinny_fp8_splits(int K, int splits) {
+  const int kblocks = K / 128;
+  if (splits < (kblocks + 31) / 32) splits = (kblocks + 31) / 32;
+  if (splits > kblocks) splits = kblocks;
+  const int kc = ((kblocks + splits - 1) / splits) * 128;
+  return (K + kc - 1) / kc;
 }
 
 }  // namespace
@@ -429,8 +471,10 @@ int mla_prefill_cached(const mla_dims* d, const mla_weights* w, const void* x, i
 }
 
 size_t mla_decode_workspace_size(const mla_dims* dims, int32_t weight_dtype, int32_t B, int32_t max_len) {
-  if (check_dims(dims) != MLA_OK || B <= 0 || max_len <= 0 || weight_dtype != MLA_BF16) return 0;
-  return decode_layout(dims, B, nullptr, nullptr);
+  if (check_dims(dims) != MLA_OK || B <= 0 || max_len <= 0 ||
+      (weight_dtype != MLA_BF16 && weight_dtype != MLA_E4M3))
+    return 0;
+  return decode_layout(dims, weight_dtype, B, nullptr, nullptr);
 }
 
 int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B, void* kv_cache, int32_t max_len,
@@ -439,7 +483,10 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B
   g_err.clear();
   int rc = check_dims(d);
   if (rc) return rc;
-  if ((rc = check_weights(w, MLA_BF16))) return rc;
+  if (!w) return fail(MLA_INVALID_ARG, "weights is NULL");
+  const int wdt = w->weight_dtype;
+  if (wdt != MLA_BF16 && wdt != MLA_E4M3) return fail(MLA_UNSUPPORTED, "decode needs bf16 or e4m3 weights");
+  if ((rc = check_weights(w, wdt))) return rc;
   if (d->kv_lora_rank != 512) return fail(MLA_UNSUPPORTED, "decode needs kv_lora_rank = 512");
   if (d->n_heads % 64) return fail(MLA_UNSUPPORTED, "decode needs n_heads to be a multiple of 64");
   if (!x || !kv_cache || !cache_len || !rope_cos || !rope_sin || !out)
@@ -447,19 +494,38 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B
   if (B <= 0 || max_len <= 0) return fail(MLA_INVALID_ARG, "B and max_len must be positive");
   if (rope_len < max_len) return fail(MLA_INVALID_ARG, "rope_len (%d) < max_len (%d)", rope_len, max_len);
   DecodeWs p;
-  const size_t need = decode_layout(d, B, ws, &p);
+  const size_t need = decode_layout(d, wdt, B, ws, &p);
   if (!ws || ws_bytes < need) return fail(MLA_INVALID_ARG, "workspace too small: need %zu bytes", need);
   if ((uintptr_t)ws & 255) return fail(MLA_INVALID_ARG, "workspace must be 256-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   const int H = d->n_heads, Dq = d->q_lora_rank, L = d->kv_lora_rank, dim = d->dim, NQKV = Dq + L + 64;
 
   if (dim % 64 || Dq % 64) return fail(MLA_UNSUPPORTED, "decode needs dim and q_lora_rank multiples of 64");
+  const bool fp8 = wdt == MLA_E4M3;
+  if (fp8 && (dim % 128 || Dq % 128))
+    return fail(MLA_UNSUPPORTED, "e4m3 decode needs dim and q_lora_rank multiples of 128");
   float* part = (float*)p.part;
+  uint8_t* aq = (uint8_t*)p.aq;
+  float* as = (float*)p.as;
+  // e4m3 weights: each projection's input is quantised in 1x128 groups first
+  auto quant = [&](const void* a, int64_t lda, int rows, int K) -> int {
+    LAUNCH(mla::launch_quant_1x128(a, lda, MLA_BF16, rows, K, aq, as, s), "quant_e4m3_1x128");
+    return MLA_OK;
+  };
   // [c_q | latent | k_pe] = x . [Wq_a ; Wkv_a]^T as split-K partials, summed by the norms
-  if ((rc = skinny(x, dim, 0, w->wq_a, dim, 0, w->wkv_a, dim, Dq, nullptr, 0, 0, part, B, NQKV, dim, 1, 64,
-                   DEC_SPLIT_QKV, s)))
-    return rc;
-  const int splits_qkv = skinny_splits(dim, DEC_SPLIT_QKV);
+  int splits_qkv;
+  if (fp8) {
+    if ((rc = quant(x, dim, B, dim))) return rc;
+    if ((rc = skinny_fp8(aq, dim, 0, as, dim / 128, 0, w->wq_a, dim, 0, w->wq_a_scale, dim / 128, 0, w->wkv_a, dim,
+                         w->wkv_a_scale, Dq, nullptr, 0, 0, part, B, NQKV, dim, 1, 64, DEC_SPLIT_QKV, s)))
+      return rc;
+    splits_qkv = skinny_fp8_splits(dim, DEC_SPLIT_QKV);
+  } else {
+    if ((rc = skinny(x, dim, 0, w->wq_a, dim, 0, w->wkv_a, dim, Dq, nullptr, 0, 0, part, B, NQKV, dim, 1, 64,
+                     DEC_SPLIT_QKV, s)))
+      return rc;
+    splits_qkv = skinny_splits(dim, DEC_SPLIT_QKV);
+  }
   {  // q_norm, kv_norm and RoPE of k_pe; the new [latent | k_pe] lands directly in cache row cache_len[b]
     mla::QkvNormArgs a{};
     a.in = part; a.ld_in = NQKV; a.in_dtype = MLA_F32; a.in_splits = splits_qkv; a.split_stride = (int64_t)B * NQKV;
@@ -471,11 +537,18 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B
     LAUNCH(mla::launch_qkv_norm(a, s), "qkv_norm -> cache");
   }
   // q = c_q . Wq_b^T
-  if ((rc = skinny(p.cqn, Dq, 0, w->wq_b, Dq, 0, nullptr, 0, H * 192, p.q, H * 192, 0, nullptr, B, H * 192, Dq, 1, 64,
-                   1, s)))
+  if (fp8) {
+    if ((rc = quant(p.cqn, Dq, B, Dq))) return rc;
+    if ((rc = skinny_fp8(aq, Dq, 0, as, Dq / 128, 0, w->wq_b, Dq, 0, w->wq_b_scale, Dq / 128, 0, nullptr, 0, nullptr,
+                         H * 192, p.q, H * 192, 0, nullptr, B, H * 192, Dq, 1, 64, 1, s)))
+      return rc;
+  } else if ((rc = skinny(p.cqn, Dq, 0, w->wq_b, Dq, 0, nullptr, 0, H * 192, p.q, H * 192, 0, nullptr, B, H * 192, Dq,
+                          1, 64, 1, s))) {
     return rc;
+  }
   // q_lat[b, h] = [q_nope[b, h] . W_UK_h | RoPE(q_pe[b, h])]  (W_UK_h = Wkv_b rows [256h, 256h+128))
-  LAUNCH(mla::launch_decode_absorb(p.q, w->wkv_b, p.qlat, cache_len, rope_cos, rope_sin, B, H, max_len, s),
+  LAUNCH(mla::launch_decode_absorb(p.q, w->wkv_b, fp8 ? w->wkv_b_scale : nullptr, p.qlat, cache_len, rope_cos,
+                                   rope_sin, B, H, max_len, s),
          "decode_absorb");
   {
     mla::DecodeAttnArgs a{};
@@ -484,15 +557,32 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B
     LAUNCH(mla::launch_decode_attn(a, s), "decode_attn");
   }
   // o[b, h] = W_UV_h . o_lat[b, h]  (W_UV_h = Wkv_b rows [256h+128, 256h+256)), per head
-  if ((rc = skinny(p.olat, H * 512, 512, (const uint16_t*)w->wkv_b + 128 * (int64_t)L, L, 256 * (int64_t)L, nullptr,
-                   0, 128, p.o, H * 128, 128, nullptr, B, 128, L, H, 64, 1, s)))
+  if (fp8) {   // o_lat quantised per (b, h) row in 4 groups; W_UV_h = block row 2h + 1 of the scales
+    if ((rc = quant(p.olat, L, B * H, L))) return rc;
+    if ((rc = skinny_fp8(aq, (int64_t)H * L, L, as, (int64_t)H * (L / 128), L / 128,
+                         (const uint8_t*)w->wkv_b + 128 * (int64_t)L, L, 256 * (int64_t)L, w->wkv_b_scale + L / 128,
+                         L / 128, 2 * (L / 128), nullptr, 0, nullptr, 128, p.o, H * 128, 128, nullptr, B, 128, L, H,
+                         64, 1, s)))
+      return rc;
+  } else if ((rc = skinny(p.olat, H * 512, 512, (const uint16_t*)w->wkv_b + 128 * (int64_t)L, L, 256 * (int64_t)L,
+                          nullptr, 0, 128, p.o, H * 128, 128, nullptr, B, 128, L, H, 64, 1, s))) {
     return rc;
+  }
   // out = o . Wo^T (split-K, then a fixed-order sum)
-  if ((rc = skinny(p.o, H * 128, 0, w->wo, H * 128, 0, nullptr, 0, dim, nullptr, 0, 0, part, B, dim, H * 128, 1, 128,
-                   DEC_SPLIT_WO, s)))
-    return rc;
-  LAUNCH(mla::launch_splitk_reduce(part, skinny_splits(H * 128, DEC_SPLIT_WO), B, dim, out, dim, s),
-         "splitk_reduce(wo)");
+  int splits_wo;
+  if (fp8) {
+    if ((rc = quant(p.o, H * 128, B, H * 128))) return rc;
+    if ((rc = skinny_fp8(aq, H * 128, 0, as, H, 0, w->wo, H * 128, 0, w->wo_scale, H, 0, nullptr, 0, nullptr, dim,
+                         nullptr, 0, 0, part, B, dim, H * 128, 1, 128, DEC_SPLIT_WO, s)))
+      return rc;
+    splits_wo = skinny_fp8_splits(H * 128, DEC_SPLIT_WO);
+  } else {
+    if ((rc = skinny(p.o, H * 128, 0, w->wo, H * 128, 0, nullptr, 0, dim, nullptr, 0, 0, part, B, dim, H * 128, 1,
+                     128, DEC_SPLIT_WO, s)))
+      return rc;
+    splits_wo = skinny_splits(H * 128, DEC_SPLIT_WO);
+  }
+  LAUNCH(mla::launch_splitk_reduce(part, splits_wo, B, dim, out, dim, s), "splitk_reduce(wo)");
   return MLA_OK;
 }
 

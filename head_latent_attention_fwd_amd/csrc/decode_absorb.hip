@@ -14,6 +14,11 @@
 // are 4 consecutive c of one sequence, stored as 8-byte pieces. Wave w covers
 // c in [256 z + 128 (w & 1), +128) and sequences [32 (w >> 1), +32) of the tile.
 // The q_pe rotation of the tile is split between the two halves by pair index.
+//
+// With e4m3 weights the half tile is read as codes, expanded to bf16 (exact:
+// every e4m3 value is a bf16 value) and written to LDS in the same layout; the
+// contraction runs over W_UK_h's 128 rows, which lie in one 128x128 scale block
+// row, so the block scale of each 128-column group multiplies the result.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,8 +33,10 @@ __device__ __forceinline__ v4s read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(512, 2) void decode_absorb_kernel(const uint16_t* __restrict__ q,
-                                                               const uint16_t* __restrict__ wkv_b,
+                                                               const void* __restrict__ wkv_b,
+                                                               const float* __restrict__ w_scale,
                                                                uint16_t* __restrict__ qlat,
                                                                const int32_t* __restrict__ cache_len,
                                                                const float* __restrict__ cos_tab,
@@ -38,14 +45,44 @@ __global__ __launch_bounds__(512, 2) void decode_absorb_kernel(const uint16_t* _
   __shared__ __attribute__((aligned(16))) uint16_t sw[128 * 256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, z = blockIdx.y, b0 = blockIdx.z * 128;
-  const uint16_t* W = wkv_b + (int64_t)h * 256 * 512 + 256 * z;
 
-  // W_UK_h half -> LDS: load i of wave w fills rows j = 16 i + 2 w + (lane >> 5)
+  if constexpr (FP8) {
+    // codes -> bf16 -> LDS: thread handles 16-byte pieces (row j, 16 columns 16 qc..) of the half
+    const uint8_t* W8 = (const uint8_t*)wkv_b + (int64_t)h * 256 * 512 + 256 * z;
+    uint4 v[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int j = 16 * i + 2 * wave + (lane >> 5);
-    __builtin_amdgcn_global_load_lds(W + (int64_t)j * 512 + (((lane & 31) ^ swj(j)) << 3), sw + (16 * i + 2 * wave) * 256,
-                                     16, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 512 * i, j = idx >> 4, qc = idx & 15;
+      v[i] = *(const uint4*)(W8 + (int64_t)j * 512 + qc * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 512 * i, j = idx >> 4, qc = idx & 15;
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      uint32_t o[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float2v lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[e], false);
+        const float2v up = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[e], true);
+        o[2 * e] = pack_bf16x2(lo[0], lo[1]);
+        o[2 * e + 1] = pack_bf16x2(up[0], up[1]);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int ch = 2 * qc + half;
+        *(uint4*)(sw + j * 256 + ((((ch & 15) ^ swj(j)) | (ch & 16)) << 3)) =
+            make_uint4(o[4 * half], o[4 * half + 1], o[4 * half + 2], o[4 * half + 3]);
+      }
+    }
+  } else {
+    // W_UK_h half -> LDS: load i of wave w fills rows j = 16 i + 2 w + (lane >> 5)
+    const uint16_t* W = (const uint16_t*)wkv_b + (int64_t)h * 256 * 512 + 256 * z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = 16 * i + 2 * wave + (lane >> 5);
+      __builtin_amdgcn_global_load_lds(W + (int64_t)j * 512 + (((lane & 31) ^ swj(j)) << 3),
+                                       sw + (16 * i + 2 * wave) * 256, 16, 0, 0);
+    }
   }
 
   // q fragments (B operand): lane (sequence l32, half hi) holds, for k-step
@@ -116,6 +153,13 @@ __global__ __launch_bounds__(512, 2) void decode_absorb_kernel(const uint16_t* _
       acc[cb] = mfma32(wf, qf[ks], acc[cb]);
     }
   // lane: sequence bq, dims c = 256 z + 128 wc + 32 cb + 8 rg + 4 hi + 0..3
+  if constexpr (FP8) {   // block (2h, 2z + wc) of the [2H, 4] scale grid
+    const float sc = w_scale[(int64_t)2 * h * 4 + 2 * z + wc];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[cb][r] *= sc;
+  }
   if (bq < B) {
     uint16_t* o = qlat + ((int64_t)bq * H + h) * 576 + 256 * z + 128 * wc + 4 * hi;
 #pragma unroll
@@ -129,12 +173,16 @@ __global__ __launch_bounds__(512, 2) void decode_absorb_kernel(const uint16_t* _
 
 }  // namespace
 
-hipError_t launch_decode_absorb(const void* q, const void* wkv_b, void* qlat, const int32_t* cache_len,
-                                const float* cos_tab, const float* sin_tab, int B, int H, int max_len,
-                                hipStream_t s) {
+hipError_t launch_decode_absorb(const void* q, const void* wkv_b, const float* w_scale, void* qlat,
+                                const int32_t* cache_len, const float* cos_tab, const float* sin_tab, int B, int H,
+                                int max_len, hipStream_t s) {
   dim3 grid(H, 2, (B + 127) / 128);
-  decode_absorb_kernel<<<grid, 512, 0, s>>>((const uint16_t*)q, (const uint16_t*)wkv_b, (uint16_t*)qlat, cache_len,
-                                            cos_tab, sin_tab, B, H, max_len);
+  if (w_scale)
+    decode_absorb_kernel<true><<<grid, 512, 0, s>>>((const uint16_t*)q, wkv_b, w_scale, (uint16_t*)qlat, cache_len,
+                                                    cos_tab, sin_tab, B, H, max_len);
+  else
+    decode_absorb_kernel<false><<<grid, 512, 0, s>>>((const uint16_t*)q, wkv_b, nullptr, (uint16_t*)qlat,
+                                                     cache_len, cos_tab, sin_tab, B, H, max_len);
   return hipGetLastError();
 }
 

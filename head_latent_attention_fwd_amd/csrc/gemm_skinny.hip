@@ -150,7 +150,177 @@ __device__ __forceinline__ void gemm_skinny_body(const SkinnyArgs& g) {
     }
 }
 
+// e4m3 x e4m3 variant: a 64-element bf16 step of the body above is one
+// 128-byte K block here (one scale group), staged through the same ring as
+// 16-byte chunks. Per block a wave runs two v_mfma_f32_32x32x64_f8f6f4 per
+// 32-column group into a block accumulator that is then added to the running
+// sum times a_scale[m, kb] * w_scale[n / 128, kb] (a lane's results share one
+// row m, and a tile of at most 128 columns lies in one scale block). The
+// scales of the workgroup's K chunk (at most SKF_KB blocks) are staged in LDS
+// before the ring starts, so the ring's wait counts see only its own loads.
+constexpr int SKF_KB = 32;
+template <int NT>
+__device__ __forceinline__ void gemm_skinny_fp8_body(const SkinnyArgs& g) {
+  constexpr int SLOTS = (128 + NT) * 8;
+  constexpr int LPT = SLOTS / 256;
+  constexpr int STAGE = SLOTS * 8;               // uint16 units per stage
+  constexpr int FN = NT / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SK_ST * STAGE];
+  __shared__ float sa_s[128][SKF_KB + 1];
+  __shared__ float sw_s[SKF_KB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int n0 = blockIdx.x * NT, split = blockIdx.y, z = blockIdx.z;
+  const int M = g.M, N = g.N;
+  const int k_begin = split * g.kc, k_end = min(g.K, k_begin + g.kc);
+  const int nk = (k_end - k_begin) / 128;
+  {  // scales of this chunk: rows of A, the tile's weight block row
+    const int kb0 = k_begin / 128;
+    const float* wsr = n0 < g.n_split ? g.ws + z * g.batch_ws + (int64_t)(n0 / 128) * g.ldws + kb0
+                                      : g.ws2 + (int64_t)((n0 - g.n_split) / 128) * g.ldws + kb0;
+    for (int i = tid; i < 128 * nk; i += 256) {
+      const int r = i / nk, kb = i - r * nk;
+      sa_s[r][kb] = g.as[z * g.batch_as + (int64_t)min(r, M - 1) * g.lds + kb0 + kb];
+    }
+    if (tid < nk) sw_s[tid] = wsr[tid];
+  }
+  // byte strides halved: the ring moves uint16 pairs
+  const uint16_t* A = (const uint16_t*)((const uint8_t*)g.A + z * g.batch_a + k_begin);
+  const uint16_t* W = (const uint16_t*)((const uint8_t*)g.W + z * g.batch_w + k_begin);
+  const uint16_t* W2 = (const uint16_t*)((const uint8_t*)g.W2 + k_begin);
+  const int64_t lda = g.lda / 2, ldw = g.ldw / 2, ldw2 = g.ldw2 / 2;
+
+  const uint16_t* src[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int p = (wave * LPT + i) * 64 + lane;
+    const int r = p >> 3;
+    if (p < 1024) {
+      const int c = (p & 7) ^ sk_sw(r);
+      src[i] = A + (int64_t)min(r, M - 1) * lda + c * 8;
+    } else {
+      const int rw = r - 128, c = (p & 7) ^ sk_sw(rw);
+      const int n = min(n0 + rw, N - 1);
+      src[i] = (n < g.n_split ? W + (int64_t)n * ldw : W2 + (int64_t)(n - g.n_split) * ldw2) + c * 8;
+    }
+  }
+  auto issue = [&](int kt) {
+    uint16_t* st = smem + (kt % SK_ST) * STAGE + wave * LPT * 512;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) __builtin_amdgcn_global_load_lds(src[i] + kt * SK_BK, st + i * 512, 16, 0, 0);
+  };
+  auto wait_ahead = [&](int ahead) {
+    if (ahead >= 3) {
+      if constexpr (LPT == 6) __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(18)" ::: "memory");
+      else __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(24)" ::: "memory");
+    } else if (ahead == 2) {
+      if constexpr (LPT == 6) __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(12)" ::: "memory");
+      else __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(16)" ::: "memory");
+    } else if (ahead == 1) {
+      if constexpr (LPT == 6) __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(6)" ::: "memory");
+      else __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+      __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+  };
+
+  floatx16 acc[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+
+  // a lane's 32 k bytes of sub-step s are chunks 4 s + 2 hi and 4 s + 2 hi + 1
+  const int ra = 32 * wave + l32;
+  int xa[2][2], xw[2][2][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int ch = 4 * s + 2 * hi + e;
+      xa[s][e] = (ch ^ sk_sw(ra)) << 3;
+      xw[0][s][e] = (ch ^ sk_sw(l32)) << 3;
+      xw[1][s][e] = (ch ^ sk_sw(32 + l32)) << 3;
+    }
+  auto frag = [&](const uint16_t* row, const int* x) {
+    const uint4 lo = *(const uint4*)(row + x[0]), up = *(const uint4*)(row + x[1]);
+    return (intx8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)up.x, (int)up.y, (int)up.z, (int)up.w};
+  };
+
+  const int m = ra;
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the scale loads, before the ring's
+  if (nk > 0) {
+    for (int s = 0; s < SK_ST; ++s)
+      if (s < nk) issue(s);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_ahead(min(nk - 1 - kt, 3));   // step kt (and the staged scales) have landed
+    const float f = sa_s[m][kt] * sw_s[kt];
+    const uint16_t* st = smem + (kt % SK_ST) * STAGE;
+    floatx16 blk[FN];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const intx8 af = frag(st + ra * SK_BK, xa[s]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const intx8 wf = frag(st + (128 + 32 * j + l32) * SK_BK, xw[j & 1][s]);
+        if (s == 0) {
+          floatx16 zero;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) zero[r] = 0.f;
+          blk[j] = mfma32_fp8(wf, af, zero);
+        } else {
+          blk[j] = mfma32_fp8(wf, af, blk[j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][r] = fmaf(blk[j][r], f, acc[j][r]);
+    // every wave is done with stage kt before it is refilled
+    if (kt + SK_ST < nk) {
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+      issue(kt + SK_ST);
+    }
+  }
+
+  if (m >= M) return;
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int n = n0 + 32 * j + 8 * rg + 4 * hi;
+      if (n >= N) continue;
+      const float v0 = acc[j][4 * rg], v1 = acc[j][4 * rg + 1], v2 = acc[j][4 * rg + 2], v3 = acc[j][4 * rg + 3];
+      if (gridDim.y == 1) {
+        uint16_t* c = (uint16_t*)g.C + (int64_t)z * g.batch_c + (int64_t)m * g.ldc + n;
+        if (n + 4 <= N && (g.ldc & 3) == 0 && (g.batch_c & 3) == 0) {
+          *(uint2*)c = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+        } else {
+          const float v[4] = {v0, v1, v2, v3};
+          for (int e = 0; n + e < N; ++e) c[e] = f2bf(v[e]);
+        }
+      } else {
+        float* p = g.P + (int64_t)split * g.ps + (int64_t)m * N + n;
+        if (n + 4 <= N && (N & 3) == 0) {
+          *(float4*)p = make_float4(v0, v1, v2, v3);
+        } else {
+          const float v[4] = {v0, v1, v2, v3};
+          for (int e = 0; n + e < N; ++e) p[e] = v[e];
+        }
+      }
+    }
+}
+
 __global__ __launch_bounds__(256, 1) void gemm_skinny64_kernel(SkinnyArgs g) { gemm_skinny_body<64>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_skinny_fp8_64_kernel(SkinnyArgs g) { gemm_skinny_fp8_body<64>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_skinny_fp8_128_kernel(SkinnyArgs g) { gemm_skinny_fp8_body<128>(g); }
 __global__ __launch_bounds__(256, 1) void gemm_skinny128_kernel(SkinnyArgs g) { gemm_skinny_body<128>(g); }
 
 // out[m, n] = sum over s of P[s][m][n] (s ascending), stored bf16.
@@ -183,6 +353,18 @@ hipError_t launch_gemm_skinny(const SkinnyArgs& g, int nt, int splits, hipStream
   dim3 grid((g.N + nt - 1) / nt, splits, g.batch);
   if (nt == 64) gemm_skinny64_kernel<<<grid, 256, 0, s>>>(g);
   else gemm_skinny128_kernel<<<grid, 256, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_skinny_fp8(const SkinnyArgs& g, int nt, int splits, hipStream_t s) {
+  if (g.K % 128 || g.kc % 128 || g.lda % 16 || g.ldw % 16 || (g.W2 && (g.ldw2 % 16 || g.n_split % 128)) ||
+      g.batch_a % 16 || g.batch_w % 16 || g.M > 128 || (nt != 64 && nt != 128) || g.kc > 128 * SKF_KB ||
+      !g.as || !g.ws || (g.W2 && !g.ws2) ||
+      (((uintptr_t)g.A | (uintptr_t)g.W | (uintptr_t)g.W2) & 15))
+    return hipErrorInvalidValue;
+  dim3 grid((g.N + nt - 1) / nt, splits, g.batch);
+  if (nt == 64) gemm_skinny_fp8_64_kernel<<<grid, 256, 0, s>>>(g);
+  else gemm_skinny_fp8_128_kernel<<<grid, 256, 0, s>>>(g);
   return hipGetLastError();
 }
 

@@ -78,8 +78,16 @@ struct SkinnyArgs {
   void* C; int64_t ldc; int64_t batch_c;
   float* P; int64_t ps;   // partial of split s, row m: P + s*ps + m*N
   int M, N, K, kc, batch;
+  // e4m3 operands (launch_gemm_skinny_fp8): A codes with 1x128 group scales
+  // as[z*batch_as + m*lds + k/128]; W codes with 128x128 block scales
+  // ws[z*batch_ws + (n/128)*ldws + k/128] (ws2 for the rows of W2, n - n_split)
+  const float* as; int64_t lds; int64_t batch_as;
+  const float* ws; const float* ws2; int ldws; int64_t batch_ws;
 };
 hipError_t launch_gemm_skinny(const SkinnyArgs& g, int nt, int splits, hipStream_t s);
+// The same product with e4m3 A and W (strides in bytes = elements; K, kc,
+// lda, ldw multiples of 128 / 16; n_split a multiple of 128; nt 64 or 128).
+hipError_t launch_gemm_skinny_fp8(const SkinnyArgs& g, int nt, int splits, hipStream_t s);
 // out[m, n] = sum_s P[s][m][n] as bf16 (row stride ldo).
 hipError_t launch_splitk_reduce(const float* P, int S, int M, int N, void* out, int64_t ldo, hipStream_t s);
 
@@ -162,9 +170,10 @@ struct DecodeAttnArgs {
 };
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s);
 // q_lat[b, h] = [q_nope[b, h] . W_UK_h | RoPE(q_pe[b, h], cache_len[b])] for kv_lora_rank 512;
-// q [B, H*192], wkv_b [H*256, 512], qlat [B, H, 576].
-hipError_t launch_decode_absorb(const void* q, const void* wkv_b, void* qlat, const int32_t* cache_len,
-                                const float* cos_tab, const float* sin_tab, int B, int H, int max_len,
-                                hipStream_t s);
+// q [B, H*192], wkv_b [H*256, 512] (bf16, or e4m3 codes with block scales
+// w_scale [2H, 4]; w_scale == nullptr for bf16), qlat [B, H, 576].
+hipError_t launch_decode_absorb(const void* q, const void* wkv_b, const float* w_scale, void* qlat,
+                                const int32_t* cache_len, const float* cos_tab, const float* sin_tab, int B, int H,
+                                int max_len, hipStream_t s);
 
 }  // namespace mla

@@ -97,16 +97,17 @@ class Decode:
         self.cfg = cfg
         B = cfg["B"]
         self.dims = dims_of(cfg)
+        self.wdt = _WDT[cfg.get("weight", "bf16")]
         self.x = to_dev(inp["x"], torch.bfloat16, device)
-        self.w = device_weights(inp["w"], "bf16", device)
-        self.weights = api.make_weights(self.w, api.MLA_BF16)
+        self.w = device_weights(inp["w"], cfg.get("weight", "bf16"), device)
+        self.weights = api.make_weights(self.w, self.wdt)
         self.cache0 = to_dev(inp["cache"], torch.bfloat16, device)
         self.cache = self.cache0.clone()
         self.cache_len = to_dev(inp["cache_len"], torch.int32, device)
         max_len = self.cache.shape[1]
         self.cos, self.sin = api.mla_rope_table(max_len, device=device)
         self.out = torch.empty((B, cfg["dim"]), dtype=torch.bfloat16, device=device)
-        self.ws = api.workspace(api.mla_decode_workspace_size(self.dims, api.MLA_BF16, B, max_len), device)
+        self.ws = api.workspace(api.mla_decode_workspace_size(self.dims, self.wdt, B, max_len), device)
 
     def run(self, stream=None):
         return api.mla_decode(self.dims, self.weights, self.x, self.cache, self.cache_len, self.cos, self.sin,

@@ -152,7 +152,7 @@ MLA_API int mla_prefill_cached(const mla_dims* dims, const mla_weights* w, const
                        const float* rope_sin, int32_t rope_len, const int32_t* topk_idx, int32_t topk, void* out,
                        void* ws, size_t ws_bytes, void* stream);
 
-/* Bytes of workspace mla_decode needs (0 on invalid input). */
+/* Bytes of workspace mla_decode needs for bf16 or e4m3 weights (0 on invalid input). */
 MLA_API size_t mla_decode_workspace_size(const mla_dims* dims, int32_t weight_dtype, int32_t B, int32_t max_len);
 
 /* Single-token MLA decode, latent-absorbed (DeepSeek-V3.2-Exp · Sparse
@@ -170,8 +170,13 @@ MLA_API size_t mla_decode_workspace_size(const mla_dims* dims, int32_t weight_dt
  *             row is set to zero)
  *   rope_cos, rope_sin  fp32 [rope_len, 32], rope_len >= max_len
  *   out       [B, dim] bf16
- * Needs bf16 weights, kv_lora_rank = 512, n_heads a multiple of 64, and
- * 16-byte aligned norm weights and cache (MLA_UNSUPPORTED otherwise). */
+ * Weights bf16, or e4m3 with 128x128 block scales (Kimi K2 · Down projection,
+ * quantization_config: e4m3, dynamic activation scheme, 128x128 weight
+ * blocks): then the inputs of q_a|kv_a, q_b, W_UV and wo are quantised in
+ * dynamic 1x128 groups as in prefill, and the absorbed key half uses the
+ * dequantised W_UK with the bf16 query. Needs kv_lora_rank = 512, n_heads a
+ * multiple of 64, dim and q_lora_rank multiples of 128 for e4m3, and 16-byte
+ * aligned norm weights and cache (MLA_UNSUPPORTED otherwise). */
 MLA_API int mla_decode(const mla_dims* dims, const mla_weights* w, const void* x, int32_t B,
                void* kv_cache, int32_t max_len, const int32_t* cache_len,
                const float* rope_cos, const float* rope_sin, int32_t rope_len,

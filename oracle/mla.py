@@ -269,10 +269,10 @@ def mla_prefill_cached(x, w, d, cache, start_pos, topk_idx=None, rows=None, fp8=
 # ----------------------------------------------------------------------------
 # decode
 
-def _decode_tokens(x, w, d, P):
+def _decode_tokens(x, w, d, P, fp8=None):
     """Query parts and cache entries of the new tokens (row b at position P[b])."""
-    q_nope, q_pe = query_path(x, w, d, P)
-    entry = latent_path(x, w, d, P)
+    q_nope, q_pe = query_path(x, w, d, P, fp8)
+    entry = latent_path(x, w, d, P, fp8)
     return q_nope, q_pe, entry
 
 
@@ -302,7 +302,7 @@ def mla_decode(x, w, d, cache, cache_len, seqs=None):
     return linear(o, w["wo"]), entries
 
 
-def mla_decode_absorbed(x, w, d, cache, cache_len, seqs=None):
+def mla_decode_absorbed(x, w, d, cache, cache_len, seqs=None, fp8=False):
     """Single-token decode with kv_b absorbed: the same result as mla_decode by
     reassociating the products. With W_UK_h = Wkv_b rows [256h, 256h+128) and
     W_UV_h = rows [256h+128, 256h+256):
@@ -310,15 +310,27 @@ def mla_decode_absorbed(x, w, d, cache, cache_len, seqs=None):
       z[h, t] = scale * (q_lat_h . C_t[:L] + q_pe_h . C_t[L:])
       o_lat_h = sum_t softmax(z)[h, t] * C_t[:L]
       o_h     = W_UV_h o_lat_h
+    With fp8=True (w holds fp32 masters, block-quantised here as in prefill):
+    q_a, kv_a, q_b and wo are fp8 Linears (dynamic 1x128 activation groups);
+    W_UK enters dequantised (codes times block scale) since it is applied
+    along its output dimension; W_UV_h is applied to o_lat_h as an fp8 Linear
+    (o_lat_h quantised in 1x128 groups, the head's block row of scales).
     Returns (out, new_entry) like mla_decode."""
     x = np.asarray(x, dtype=np.float64)
     seqs = np.arange(x.shape[0]) if seqs is None else np.asarray(seqs)
     L = d["kv_lora_rank"]
     H = d["n_heads"]
-    wkv_b = np.asarray(w["wkv_b"], dtype=np.float64).reshape(H, NOPE + VDIM, L)
-    W_UK, W_UV = wkv_b[:, :NOPE, :], wkv_b[:, NOPE:, :]
+    fq = quantise_weights(w) if fp8 else None
+    if fp8:
+        from .fp8 import e4m3_decode, linear_fp8
+        codes, scales = fq["wkv_b"]
+        deq = e4m3_decode(codes) * np.repeat(np.repeat(scales.astype(np.float64), 128, 0), 128, 1)
+        W_UK = deq.reshape(H, NOPE + VDIM, L)[:, :NOPE, :]
+    else:
+        wkv_b = np.asarray(w["wkv_b"], dtype=np.float64).reshape(H, NOPE + VDIM, L)
+        W_UK, W_UV = wkv_b[:, :NOPE, :], wkv_b[:, NOPE:, :]
     P_all = np.asarray(cache_len)[seqs].astype(np.int64)
-    q_nope, q_pe, entries = _decode_tokens(x[seqs], w, d, P_all)
+    q_nope, q_pe, entries = _decode_tokens(x[seqs], w, d, P_all, fq)
     o = np.zeros((len(seqs), H * VDIM))
     for i, b in enumerate(seqs):
         P = int(P_all[i])
@@ -327,8 +339,14 @@ def mla_decode_absorbed(x, w, d, cache, cache_len, seqs=None):
         z = (q_lat @ C[:, :L].T + q_pe[i] @ C[:, L:].T) * d["softmax_scale"]
         p = softmax_over_live(z)                                  # [H, P+1]
         o_lat = p @ C[:, :L]                                      # [H, L]
-        o[i] = np.einsum("hjc,hc->hj", W_UV, o_lat).reshape(-1)   # [H*128]
-    return linear(o, w["wo"]), entries
+        if fp8:
+            for h in range(H):
+                r0 = 256 * h + NOPE
+                o[i, h * VDIM:(h + 1) * VDIM] = linear_fp8(o_lat[h][None], codes[r0:r0 + VDIM],
+                                                           scales[r0 // 128:r0 // 128 + 1])[0]
+        else:
+            o[i] = np.einsum("hjc,hc->hj", W_UV, o_lat).reshape(-1)   # [H*128]
+    return _proj(o, w, "wo", fq), entries
 
 
 # ----------------------------------------------------------------------------

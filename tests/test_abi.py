@@ -84,7 +84,11 @@ def test_workspace_sizes(lib):
     bad = _dims()
     bad.v_head_dim = 64
     assert api.mla_prefill_workspace_size(bad, api.MLA_BF16, api.MLA_BF16, 1, 16, 0) == 0
-    assert api.mla_decode_workspace_size(d, api.MLA_E4M3, 4, 16) == 0
+    dd = api.make_dims(7168, 1536, 512, 128)
+    db = api.mla_decode_workspace_size(dd, api.MLA_BF16, 128, 1024)
+    # e4m3 adds the quantised activation of the widest projection input, o_lat [128*128, 512]
+    assert api.mla_decode_workspace_size(dd, api.MLA_E4M3, 128, 1024) >= db + 128 * 128 * 512 * (1 + 4 / 128)
+    assert api.mla_decode_workspace_size(d, api.MLA_F32, 4, 16) == 0
 
 
 P = ctypes.c_void_p

@@ -89,6 +89,8 @@ def test_prefill_dsv32_sparse_full_size_sampled():
 
 
 def _check_decode(cfg, seed, cache_len=None, seqs=None, max_len=None):
+    fp8 = cfg.get("weight") == "e4m3"
+    tol, cos = (FP8_TOL, 0.999) if fp8 else (BF16_TOL, 0.9999)
     inp = synth.gen_decode(cfg, seed, max_len=max_len)
     if cache_len is not None:
         inp["cache_len"] = np.asarray(cache_len, dtype=np.int32)
@@ -96,10 +98,10 @@ def _check_decode(cfg, seed, cache_len=None, seqs=None, max_len=None):
     run.run()
     torch.cuda.synchronize()
     d = oracle_dims(cfg)
-    ref, entry = mla.mla_decode_absorbed(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"], seqs=seqs)
+    ref, entry = mla.mla_decode_absorbed(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"], seqs=seqs, fp8=fp8)
     got = run.out.float().cpu().numpy()
     sel = np.arange(cfg["B"]) if seqs is None else np.asarray(seqs)
-    assert_parity(got[sel], ref, what=cfg["name"])
+    assert_parity(got[sel], ref, tol=tol, cos=cos, what=cfg["name"])
     # the cache changed exactly at slot cache_len[b]; every other slot is bit-identical
     new = run.cache.float().cpu().numpy()
     old = run.cache0.float().cpu().numpy()
@@ -108,7 +110,7 @@ def _check_decode(cfg, seed, cache_len=None, seqs=None, max_len=None):
         keep = np.ones(new.shape[1], dtype=bool)
         keep[P] = False
         np.testing.assert_array_equal(new[b][keep], old[b][keep])
-        assert_parity(new[b, P], entry[i], what="appended cache entry")
+        assert_parity(new[b, P], entry[i], tol=tol, cos=cos, what="appended cache entry")
     return inp, run
 
 
@@ -121,6 +123,18 @@ def test_decode_small_varied_lengths():
 def test_decode_dsv32_full_size():
     cfg = config(4)
     _check_decode(cfg, synth.seed_of(4), max_len=1024)
+
+
+def test_decode_fp8_small_varied_lengths():
+    cfg = dict(name="dec_small_fp8", mode="decode", B=6, cache_len=40, dim=1024, q_lora_rank=256,
+               kv_lora_rank=512, n_heads=64, act="bf16", weight="e4m3")
+    _check_decode(cfg, 33, cache_len=[0, 1, 31, 32, 33, 40], max_len=48)
+
+
+def test_decode_fp8_dsv32_full_size_sampled():
+    # e4m3 weights at the DeepSeek-V3.2-Exp decode shapes (B = 128, 1000 cached)
+    cfg = config(4, weight="e4m3")
+    _check_decode(cfg, synth.seed_of(4), max_len=1024, seqs=[0, 1, 37, 64, 100, 127])
 
 
 def test_decode_out_of_range_length_gives_zero_row():

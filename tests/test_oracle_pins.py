@@ -392,6 +392,32 @@ def test_one_token_chunk_equals_decode():
     np.testing.assert_allclose(e1[:, 0], e2, rtol=1e-13, atol=1e-14)
 
 
+def test_fp8_absorbed_decode_tracks_the_exact_decode():
+    """With e4m3 weights the absorbed decode stays within fp8 rounding of the
+    exact (fp64, unquantised) decode. Every 128x128 weight block is scaled by
+    its own power of two, so a scale taken from the wrong block (or dropped)
+    moves the result by far more than the rounding does."""
+    cfg = dict(name="t", mode="decode", B=3, cache_len=20, dim=256, q_lora_rank=256, kv_lora_rank=512,
+               n_heads=2, act="bf16", weight="e4m3")
+    inp = synth.gen_decode(cfg, 51, max_len=24)
+    rng = np.random.default_rng(52)
+    w = dict(inp["w"])
+    for n in ("wq_a", "wq_b", "wkv_a", "wkv_b", "wo"):
+        a = np.asarray(w[n], dtype=np.float64)
+        f = 2.0 ** rng.integers(-3, 4, size=(-(-a.shape[0] // 128), -(-a.shape[1] // 128)))
+        w[n] = (a * np.repeat(np.repeat(f, 128, 0), 128, 1)[:a.shape[0], :a.shape[1]]).astype(np.float32)
+    d = mla.default_dims(256, 256, 512, 2)
+    exact, e_exact = mla.mla_decode(inp["x"], w, d, inp["cache"], inp["cache_len"])
+    got, e_got = mla.mla_decode_absorbed(inp["x"], w, d, inp["cache"], inp["cache_len"], fp8=True)
+    err = np.abs(got - exact).max() / np.abs(exact).max()
+    cos = (got * exact).sum() / np.linalg.norm(got) / np.linalg.norm(exact)
+    # five chained e4m3 products (each ~5 % RMS rounding) give ~8 % RMS here
+    # (cosine 0.9965); a scale from a neighbouring block row or one shared
+    # scale for W_UK gives max errors above 1 and cosines below 0.65
+    assert err < 0.3 and cos > 0.99, (err, cos)
+    assert np.abs(e_got - e_exact).max() / np.abs(e_exact).max() < 0.3
+
+
 # --------------------------------------------------------------------------
 # selection mask
 
