@@ -136,6 +136,7 @@ size_t prefill_layout(const mla_dims* d, int wdt, int adt, int B, int T, int Tk,
 struct DecodeWs {
   void *part, *cqn, *q, *qlat, *olat, *o;
   void *aq, *as;   // e4m3 weights: the quantised activation of the current projection
+  void *oq, *os;   // e4m3 weights: o quantised by the W_UV product for wo
 };
 
 // split-K factors of the two decode projections with long K
@@ -158,6 +159,8 @@ size_t decode_layout(const mla_dims* d, int wdt, int B, void* ws, DecodeWs* out)
     if (Dq > kmax) kmax = Dq;
     p.aq = c.take((size_t)B * kmax);
     p.as = c.take((size_t)B * (kmax / 128) * 4);
+    p.oq = c.take((size_t)B * H * 128);
+    p.os = c.take((size_t)B * H * 4);
   }
   if (out) *out = p;
   return c.off;
@@ -255,7 +258,8 @@ int skinny(const void* A, int64_t lda, int64_t batch_a, const void* W, int64_t l
 int skinny_fp8(const void* A, int64_t lda, int64_t batch_a, const float* as, int64_t lds, int64_t batch_as,
                const void* W, int64_t ldw, int64_t batch_w, const float* ws, int ldws, int64_t batch_ws,
                const void* W2, int64_t ldw2, const float* ws2, int n_split, void* C, int64_t ldc, int64_t batch_c,
-               float* P, int M, int N, int K, int batch, int nt, int splits, hipStream_t s) {
+               float* P, int M, int N, int K, int batch, int nt, int splits, hipStream_t s, uint8_t* qc = nullptr,
+               float* qs = nullptr) {
   const int kblocks = K / 128;
   if (splits < (kblocks + 31) / 32) splits = (kblocks + 31) / 32;
   if (splits > kblocks) splits = kblocks;
@@ -271,6 +275,7 @@ int skinny_fp8(const void* A, int64_t lda, int64_t batch_a, const float* as, int
     g.C = C ? (void*)((uint16_t*)C + (int64_t)m0 * ldc) : nullptr; g.ldc = ldc; g.batch_c = batch_c;
     g.P = P ? P + (int64_t)m0 * N : nullptr; g.ps = (int64_t)M * N;
     g.M = M - m0 < 128 ? M - m0 : 128; g.N = N; g.K = K; g.kc = kc; g.batch = batch;
+    g.qc = qc ? qc + (int64_t)m0 * ldc : nullptr; g.qs = qs ? qs + (int64_t)m0 * (ldc / 128) : nullptr;
     LAUNCH(mla::launch_gemm_skinny_fp8(g, nt, splits, s), "gemm_skinny_fp8");
   }
   return MLA_OK;
@@ -533,12 +538,12 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B
     a.q_out = p.cqn; a.ld_q = Dq;
     a.kv_out = kv_cache; a.ld_kv = (int64_t)max_len * (L + 64); a.kv_pos_stride = L + 64; a.kv_pos_max = max_len;
     a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = max_len; a.pos = cache_len;
+    if (fp8) { a.q_codes = aq; a.q_scales = as; }   // q_b's input, quantised in the same pass
     if (!qkv_norm_ok(a)) return fail(MLA_UNSUPPORTED, "decode needs 16-byte aligned norm weights and cache");
     LAUNCH(mla::launch_qkv_norm(a, s), "qkv_norm -> cache");
   }
   // q = c_q . Wq_b^T
   if (fp8) {
-    if ((rc = quant(p.cqn, Dq, B, Dq))) return rc;
     if ((rc = skinny_fp8(aq, Dq, 0, as, Dq / 128, 0, w->wq_b, Dq, 0, w->wq_b_scale, Dq / 128, 0, nullptr, 0, nullptr,
                          H * 192, p.q, H * 192, 0, nullptr, B, H * 192, Dq, 1, 64, 1, s)))
       return rc;
@@ -561,8 +566,8 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B
     if ((rc = quant(p.olat, L, B * H, L))) return rc;
     if ((rc = skinny_fp8(aq, (int64_t)H * L, L, as, (int64_t)H * (L / 128), L / 128,
                          (const uint8_t*)w->wkv_b + 128 * (int64_t)L, L, 256 * (int64_t)L, w->wkv_b_scale + L / 128,
-                         L / 128, 2 * (L / 128), nullptr, 0, nullptr, 128, p.o, H * 128, 128, nullptr, B, 128, L, H,
-                         64, 1, s)))
+                         L / 128, 2 * (L / 128), nullptr, 0, nullptr, 128, nullptr, H * 128, 128, nullptr, B, 128, L,
+                         H, 128, 1, s, (uint8_t*)p.oq, (float*)p.os)))   // o leaves as wo's e4m3 input
       return rc;
   } else if ((rc = skinny(p.olat, H * 512, 512, (const uint16_t*)w->wkv_b + 128 * (int64_t)L, L, 256 * (int64_t)L,
                           nullptr, 0, 128, p.o, H * 128, 128, nullptr, B, 128, L, H, 64, 1, s))) {
@@ -571,8 +576,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B
   // out = o . Wo^T (split-K, then a fixed-order sum)
   int splits_wo;
   if (fp8) {
-    if ((rc = quant(p.o, H * 128, B, H * 128))) return rc;
-    if ((rc = skinny_fp8(aq, H * 128, 0, as, H, 0, w->wo, H * 128, 0, w->wo_scale, H, 0, nullptr, 0, nullptr, dim,
+    if ((rc = skinny_fp8(p.oq, H * 128, 0, (const float*)p.os, H, 0, w->wo, H * 128, 0, w->wo_scale, H, 0, nullptr, 0, nullptr, dim,
                          nullptr, 0, 0, part, B, dim, H * 128, 1, 128, DEC_SPLIT_WO, s)))
       return rc;
     splits_wo = skinny_fp8_splits(H * 128, DEC_SPLIT_WO);

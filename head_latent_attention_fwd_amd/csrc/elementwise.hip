@@ -214,8 +214,23 @@ __global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
     const int c = tid + 256 * j;
     if (c < nq) {
       const float4 g = *(const float4*)&a.gq[4 * c];
-      *(uint2*)(q + 4 * c) = make_uint2(pack_bf16x2(g.x * (v[j].x * rq), g.y * (v[j].y * rq)),
-                                        pack_bf16x2(g.z * (v[j].z * rq), g.w * (v[j].w * rq)));
+      const uint2 pk = make_uint2(pack_bf16x2(g.x * (v[j].x * rq), g.y * (v[j].y * rq)),
+                                  pack_bf16x2(g.z * (v[j].z * rq), g.w * (v[j].w * rq)));
+      *(uint2*)(q + 4 * c) = pk;
+      if (a.q_codes) {   // 32 consecutive lanes hold one 128-wide group
+        const float y0 = __uint_as_float(pk.x << 16), y1 = __uint_as_float(pk.x & 0xffff0000u);
+        const float y2 = __uint_as_float(pk.y << 16), y3 = __uint_as_float(pk.y & 0xffff0000u);
+        float amax = fmaxf(fmaxf(fabsf(y0), fabsf(y1)), fmaxf(fabsf(y2), fabsf(y3)));
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        const float s = amax / 448.0f;
+        uint32_t code = 0u;
+        if (s != 0.f)
+          code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+              y2 / s, y3 / s, __builtin_amdgcn_cvt_pk_fp8_f32(y0 / s, y1 / s, 0, false), true);
+        *(uint32_t*)(a.q_codes + (int64_t)row * a.Dq + 4 * c) = code;
+        if ((c & 31) == 0) a.q_scales[(int64_t)row * (a.Dq >> 7) + (c >> 5)] = s;
+      }
     } else if (c < nq + nkv && kv) {
       const int e = 4 * (c - nq);
       const float4 g = *(const float4*)&a.gkv[e];
@@ -298,12 +313,13 @@ __device__ __forceinline__ uint32_t to_e4m3x2(float a, float b) {
 
 // 16 lanes per (row, 128-group), 8 consecutive values per lane: s = amax/448,
 // q = e4m3(x / s) (fp32 quotient, round to nearest even, saturating). A
-// 256-thread block covers 16 groups of one row.
+// 256-thread block covers 16 consecutive (row, group) pairs in row-major order.
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* a, int64_t lda, int dt, int M, int K,
                                                           uint8_t* q, float* scales) {
-  const int G = K / 128, tid = threadIdx.x;
-  const int g = blockIdx.x * 16 + (tid >> 4), m = blockIdx.y, sub = tid & 15;
-  if (g >= G) return;   // whole 16-lane groups leave together
+  const int G = K / 128, tid = threadIdx.x, sub = tid & 15;
+  const int64_t pair = (int64_t)blockIdx.x * 16 + (tid >> 4);
+  if (pair >= (int64_t)M * G) return;   // whole 16-lane groups leave together
+  const int m = (int)(pair / G), g = (int)(pair - (int64_t)m * G);
   const int64_t base = (int64_t)m * lda + g * 128 + sub * 8;
   float v[8];
   if (dt == DT_F32) {
@@ -393,7 +409,8 @@ hipError_t launch_qkv_norm(const QkvNormArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   if ((a.Dq & 3) || (a.L & 3) || (a.ld_in & 3) || (a.Dq + a.L + 64) / 4 > 256 * QKV_CH ||
       (a.in_dtype != DT_F32 && a.in_dtype != DT_BF16) || (a.in_dtype == DT_F32 && (a.split_stride & 3)) ||
-      (a.ld_q & 3) || (a.ld_kv & 3) || (a.kv_pos_stride & 3) || a.in_splits < 1 || (!a.pos && a.pos_period <= 0))
+      (a.ld_q & 3) || (a.ld_kv & 3) || (a.kv_pos_stride & 3) || a.in_splits < 1 || (!a.pos && a.pos_period <= 0) ||
+      (a.q_codes && ((a.Dq & 127) || !a.q_scales || ((uintptr_t)a.q_codes & 3))))
     return hipErrorInvalidValue;
   qkv_norm_kernel<<<a.rows, 256, 0, s>>>(a);
   return hipGetLastError();
@@ -419,8 +436,8 @@ hipError_t launch_quant_1x128(const void* a, int64_t lda, int a_dtype, int M, in
                               hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if ((lda & 7) || (((uintptr_t)a | (uintptr_t)q) & 15)) return hipErrorInvalidValue;   // 16-byte row pieces
-  dim3 grid((K / 128 + 15) / 16, M);
-  quant_1x128_kernel<<<grid, 256, 0, s>>>(a, lda, a_dtype, M, K, q, scales);
+  const int64_t pairs = (int64_t)M * (K / 128);
+  quant_1x128_kernel<<<(unsigned)((pairs + 15) / 16), 256, 0, s>>>(a, lda, a_dtype, M, K, q, scales);
   return hipGetLastError();
 }
 

@@ -205,10 +205,19 @@ __device__ __forceinline__ void gemm_skinny_fp8_body(const SkinnyArgs& g) {
       src[i] = (n < g.n_split ? W + (int64_t)n * ldw : W2 + (int64_t)(n - g.n_split) * ldw2) + c * 8;
     }
   }
+  // The ring's loads are written as asm so that the compiler does not order
+  // every later LDS read behind them; wait_ahead's explicit counts order them.
   auto issue = [&](int kt) {
-    uint16_t* st = smem + (kt % SK_ST) * STAGE + wave * LPT * 512;
+    const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(
+        smem + (kt % SK_ST) * STAGE + wave * LPT * 512);
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) __builtin_amdgcn_global_load_lds(src[i] + kt * SK_BK, st + i * 512, 16, 0, 0);
+    for (int i = 0; i < LPT; ++i) {
+      const uint32_t base = __builtin_amdgcn_readfirstlane(st + i * 1024);
+      __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                       :
+                       : "v"(src[i] + kt * SK_BK), "s"(base)
+                       : "memory", "m0");
+    }
   };
   auto wait_ahead = [&](int ahead) {
     if (ahead >= 3) {
@@ -246,50 +255,99 @@ __device__ __forceinline__ void gemm_skinny_fp8_body(const SkinnyArgs& g) {
       xw[1][s][e] = (ch ^ sk_sw(32 + l32)) << 3;
     }
   auto frag = [&](const uint16_t* row, const int* x) {
-    const uint4 lo = *(const uint4*)(row + x[0]), up = *(const uint4*)(row + x[1]);
-    return (intx8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)up.x, (int)up.y, (int)up.z, (int)up.w};
+    const intx4 lo = __builtin_bit_cast(intx4, *(const bf16x8*)(row + x[0]));
+    const intx4 up = __builtin_bit_cast(intx4, *(const bf16x8*)(row + x[1]));
+    return (intx8){lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
   };
 
   const int m = ra;
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the scale loads, before the ring's
+  // fragments of one step: A (two 32-byte sub-steps) and W per column group
+  intx8 af[2], wf[2][FN];
+  auto read = [&](int kt) {
+    const uint16_t* st = smem + (kt % SK_ST) * STAGE;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      af[s] = frag(st + ra * SK_BK, xa[s]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) wf[s][j] = frag(st + (128 + 32 * j + l32) * SK_BK, xw[j & 1][s]);
+    }
+  };
+  // a_scale[m, kb] * w_scale[kb] of step kb, read from LDS in an asm block
+  // that waits for its own reads: the compiler would otherwise order these
+  // reads behind every load of the ring still in flight
+  auto scale = [&](int kb) {
+    const uint32_t pa = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&sa_s[m][kb];
+    const uint32_t pw = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&sw_s[kb];
+    float a, w;
+    __asm__ volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(a), "=&v"(w)
+                     : "v"(pa), "v"(pw)
+                     : "memory");
+    return a * w;
+  };
+  float f = 0.f;
   if (nk > 0) {
     for (int s = 0; s < SK_ST; ++s)
       if (s < nk) issue(s);
+    wait_ahead(min(nk, SK_ST) - 1);   // step 0 (and the staged scales) have landed
+    read(0);
+    f = scale(0);
   }
   for (int kt = 0; kt < nk; ++kt) {
-    wait_ahead(min(nk - 1 - kt, 3));   // step kt (and the staged scales) have landed
-    const float f = sa_s[m][kt] * sw_s[kt];
-    const uint16_t* st = smem + (kt % SK_ST) * STAGE;
     floatx16 blk[FN];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const intx8 af = frag(st + ra * SK_BK, xa[s]);
+    for (int j = 0; j < FN; ++j) {
+      floatx16 zero;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const intx8 wf = frag(st + (128 + 32 * j + l32) * SK_BK, xw[j & 1][s]);
-        if (s == 0) {
-          floatx16 zero;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) zero[r] = 0.f;
-          blk[j] = mfma32_fp8(wf, af, zero);
-        } else {
-          blk[j] = mfma32_fp8(wf, af, blk[j]);
-        }
-      }
+      for (int r = 0; r < 16; ++r) zero[r] = 0.f;
+      blk[j] = mfma32_fp8(wf[0][j], af[0], zero);
+      blk[j] = mfma32_fp8(wf[1][j], af[1], blk[j]);
+    }
+    const float fc = f;
+    // step kt + 1 has landed and every wave is done with stage kt, which is
+    // refilled; the next step's fragments are read while these MFMAs run
+    if (kt + 1 < nk) {
+      wait_ahead(min(nk - 2 - kt, 2));
+      if (kt + SK_ST < nk) issue(kt + SK_ST);
+      f = scale(kt + 1);
+      read(kt + 1);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][r] = fmaf(blk[j][r], f, acc[j][r]);
-    // every wave is done with stage kt before it is refilled
-    if (kt + SK_ST < nk) {
-      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      __asm__ volatile("" ::: "memory");
-      issue(kt + SK_ST);
-    }
+      for (int r = 0; r < 16; ++r) acc[j][r] = fmaf(blk[j][r], fc, acc[j][r]);
   }
 
+  if (NT == 128 && g.qc) {
+    // e4m3 output: the row's 128 columns are this lane's 64 values and those
+    // of lane ^ 32; quantised from their bf16 values (rows past M idle along)
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc[j][r] = __uint_as_float((uint32_t)f2bf(acc[j][r]) << 16);
+        amax = fmaxf(amax, fabsf(acc[j][r]));
+      }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const float s = amax / 448.0f;
+    if (m >= M) return;
+    uint8_t* qrow = g.qc + (int64_t)m * g.ldc + (int64_t)z * g.batch_c;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const float v0 = acc[j][4 * rg], v1 = acc[j][4 * rg + 1], v2 = acc[j][4 * rg + 2], v3 = acc[j][4 * rg + 3];
+        uint32_t code = 0u;
+        if (s != 0.f)
+          code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+              v2 / s, v3 / s, __builtin_amdgcn_cvt_pk_fp8_f32(v0 / s, v1 / s, 0, false), true);
+        *(uint32_t*)(qrow + 32 * j + 8 * rg + 4 * hi) = code;
+      }
+    if (hi == 0) g.qs[(int64_t)m * (g.ldc / 128) + z * (g.batch_c / 128)] = s;
+    return;
+  }
   if (m >= M) return;
 #pragma unroll
   for (int j = 0; j < FN; ++j)
@@ -360,6 +418,7 @@ hipError_t launch_gemm_skinny_fp8(const SkinnyArgs& g, int nt, int splits, hipSt
   if (g.K % 128 || g.kc % 128 || g.lda % 16 || g.ldw % 16 || (g.W2 && (g.ldw2 % 16 || g.n_split % 128)) ||
       g.batch_a % 16 || g.batch_w % 16 || g.M > 128 || (nt != 64 && nt != 128) || g.kc > 128 * SKF_KB ||
       !g.as || !g.ws || (g.W2 && !g.ws2) ||
+      (g.qc && (nt != 128 || g.N != 128 || splits != 1 || !g.qs || g.ldc % 128 || g.batch_c % 128)) ||
       (((uintptr_t)g.A | (uintptr_t)g.W | (uintptr_t)g.W2) & 15))
     return hipErrorInvalidValue;
   dim3 grid((g.N + nt - 1) / nt, splits, g.batch);

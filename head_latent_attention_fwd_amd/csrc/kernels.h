@@ -83,6 +83,10 @@ struct SkinnyArgs {
   // ws[z*batch_ws + (n/128)*ldws + k/128] (ws2 for the rows of W2, n - n_split)
   const float* as; int64_t lds; int64_t batch_as;
   const float* ws; const float* ws2; int ldws; int64_t batch_ws;
+  // optional e4m3 output instead of C (fp8 kernel, nt = N = 128, one split):
+  // row m of batch z -> codes qc[m*ldc + z*batch_c + n], scale qs[m*ldc/128 + z*batch_c/128]
+  // of its bf16-rounded values, one 1x128 group per row
+  uint8_t* qc; float* qs;
 };
 hipError_t launch_gemm_skinny(const SkinnyArgs& g, int nt, int splits, hipStream_t s);
 // The same product with e4m3 A and W (strides in bytes = elements; K, kc,
@@ -127,6 +131,9 @@ struct QkvNormArgs {
   const float* cos_tab; const float* sin_tab; int rope_len;
   // position of row m: pos[m] if pos is set, else pos_off + m % pos_period
   const int32_t* pos; int pos_period; int pos_off;
+  // optional e4m3 copy of the normalised q (Dq % 128 == 0): codes [rows, Dq] and
+  // 1x128 scales [rows, Dq/128] of its bf16 values, as launch_quant_1x128 makes them
+  uint8_t* q_codes; float* q_scales;
 };
 hipError_t launch_qkv_norm(const QkvNormArgs& a, hipStream_t s);
 hipError_t launch_rope_table(float* c, float* sn, int n_pos, float base, hipStream_t s);
