@@ -545,10 +545,10 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B
   // q = c_q . Wq_b^T
   if (fp8) {
     if ((rc = skinny_fp8(aq, Dq, 0, as, Dq / 128, 0, w->wq_b, Dq, 0, w->wq_b_scale, Dq / 128, 0, nullptr, 0, nullptr,
-                         H * 192, p.q, H * 192, 0, nullptr, B, H * 192, Dq, 1, 64, 1, s)))
+                         H * 192, p.q, H * 192, 0, nullptr, B, H * 192, Dq, 1, 128, 1, s)))
       return rc;
   } else if ((rc = skinny(p.cqn, Dq, 0, w->wq_b, Dq, 0, nullptr, 0, H * 192, p.q, H * 192, 0, nullptr, B, H * 192, Dq,
-                          1, 64, 1, s))) {
+                          1, 128, 1, s))) {
     return rc;
   }
   // q_lat[b, h] = [q_nope[b, h] . W_UK_h | RoPE(q_pe[b, h])]  (W_UK_h = Wkv_b rows [256h, 256h+128))
