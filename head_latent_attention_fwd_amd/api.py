@@ -46,6 +46,11 @@ _SIGS = {
     "mla_prefill_cached": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaWeights), vp, i32, i32, i32,
                                           vp, i32, vp, vp, i32, vp, i32, vp, vp, sz, vp]),
     "mla_decode_workspace_size": (sz, [ctypes.POINTER(MlaDims), i32, i32, i32]),
+    "mla_decode_sparse": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaWeights), vp, i32, vp, i32, vp,
+                                         vp, i32, vp, vp, i32, vp, vp, sz, vp]),
+    "mla_prefill_absorbed_workspace_size": (sz, [ctypes.POINTER(MlaDims), i32, i32]),
+    "mla_prefill_absorbed": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaWeights), vp, i32, i32, vp,
+                                            vp, i32, vp, i32, vp, vp, vp, sz, vp]),
     "mla_decode": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaWeights), vp, i32, vp, i32, vp,
                                   vp, vp, i32, vp, vp, sz, vp]),
     "gemm_bf16": (ctypes.c_int, [vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, vp]),
@@ -184,15 +189,40 @@ def mla_prefill_cached(dims, weights, x, start_pos, kv_cache, rope_cos, rope_sin
     return out
 
 
-def mla_decode(dims, weights, x, kv_cache, cache_len, rope_cos, rope_sin, out, ws, stream=None):
-    """x, out [B, dim] bf16; kv_cache [B, max_len, kv_lora+64] bf16 (updated in place); cache_len [B] int32."""
+def mla_decode(dims, weights, x, kv_cache, cache_len, rope_cos, rope_sin, out, ws, topk_idx=None, stream=None):
+    """x, out [B, dim] bf16; kv_cache [B, max_len, kv_lora+64] bf16 (updated in place); cache_len [B] int32;
+    topk_idx [B, k] int32 (optional): attend only the listed positions (mla_decode_sparse)."""
     B = x.shape[0]
     for t, n in ((x, "x"), (kv_cache, "kv_cache"), (out, "out"), (ws, "ws")):
         _need(t, name=n)
     _need(cache_len, torch.int32, "cache_len")
-    rc = lib().mla_decode(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, _ptr(kv_cache),
-                          kv_cache.shape[1], _ptr(cache_len), _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
-                          _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    if topk_idx is None:
+        rc = lib().mla_decode(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, _ptr(kv_cache),
+                              kv_cache.shape[1], _ptr(cache_len), _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
+                              _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    else:
+        _need(topk_idx, torch.int32, "topk_idx")
+        rc = lib().mla_decode_sparse(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, _ptr(kv_cache),
+                                     kv_cache.shape[1], _ptr(cache_len), _ptr(topk_idx), topk_idx.shape[-1],
+                                     _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], _ptr(out), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc)
+    return out
+
+
+def mla_prefill_absorbed_workspace_size(dims, B, T):
+    return lib().mla_prefill_absorbed_workspace_size(ctypes.byref(dims), B, T)
+
+
+def mla_prefill_absorbed(dims, weights, x, rope_cos, rope_sin, topk_idx, out, ws, kv_cache_out=None, stream=None):
+    """Top-k prefill in the absorbed latent form. x, out [B, T, dim] bf16; topk_idx [B, T, k] int32."""
+    B, T, _ = x.shape
+    for t, n in ((x, "x"), (out, "out"), (ws, "ws")):
+        _need(t, torch.bfloat16 if n != "ws" else None, n)
+    _need(topk_idx, torch.int32, "topk_idx")
+    rc = lib().mla_prefill_absorbed(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T, _ptr(rope_cos),
+                                    _ptr(rope_sin), rope_cos.shape[0], _ptr(topk_idx), topk_idx.shape[-1], _ptr(out),
+                                    _ptr(kv_cache_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc)
     return out
 

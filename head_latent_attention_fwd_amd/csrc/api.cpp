@@ -166,6 +166,29 @@ size_t decode_layout(const mla_dims* d, int wdt, int B, void* ws, DecodeWs* out)
   return c.off;
 }
 
+struct AbsorbedWs {
+  void *cqkv, *cqn, *kvc, *q, *qlat, *olat, *o;
+  float* part;
+  int qkv_splits;
+};
+
+size_t absorbed_layout(const mla_dims* d, int B, int T, bool own_kvc, void* ws, AbsorbedWs* out) {
+  const size_t M = (size_t)B * T, H = d->n_heads, Dq = d->q_lora_rank, L = d->kv_lora_rank;
+  Carver c(ws);
+  AbsorbedWs p{};
+  p.cqkv = c.take(M * (Dq + L + 64) * 2);
+  p.cqn = c.take(M * Dq * 2);
+  p.kvc = own_kvc ? c.take(M * (L + 64) * 2) : nullptr;
+  p.q = c.take(M * H * 192 * 2);
+  p.qlat = c.take(M * H * (L + 64) * 2);
+  p.olat = c.take(M * H * L * 2);
+  p.o = c.take(M * H * 128 * 2);
+  p.qkv_splits = prefill_qkv_splits(d, MLA_BF16, MLA_BF16, (int)M);
+  p.part = p.qkv_splits > 1 ? (float*)c.take((size_t)p.qkv_splits * M * (Dq + L + 64) * 4) : nullptr;
+  if (out) *out = p;
+  return c.off;
+}
+
 mla::GemmArgs gemm_args(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc, int cdt, int M,
                         int N, int K) {
   mla::GemmArgs g{};
@@ -482,10 +505,14 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t weight_dtype, int
   return decode_layout(dims, weight_dtype, B, nullptr, nullptr);
 }
 
-int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B, void* kv_cache, int32_t max_len,
-               const int32_t* cache_len, const float* rope_cos, const float* rope_sin, int32_t rope_len, void* out,
-               void* ws, size_t ws_bytes, void* stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// Decode step; with topk_idx the attention covers only the listed positions.
+int decode_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t B, void* kv_cache, int32_t max_len,
+                const int32_t* cache_len, const int32_t* topk_idx, int32_t topk, const float* rope_cos,
+                const float* rope_sin, int32_t rope_len, void* out, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_dims(d);
   if (rc) return rc;
   if (!w) return fail(MLA_INVALID_ARG, "weights is NULL");
@@ -559,6 +586,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B
     mla::DecodeAttnArgs a{};
     a.qlat = p.qlat; a.cache = kv_cache; a.cache_len = cache_len; a.olat = p.olat;
     a.B = B; a.H = H; a.max_len = max_len; a.scale = d->softmax_scale;
+    a.idx = topk_idx; a.topk = topk;
     LAUNCH(mla::launch_decode_attn(a, s), "decode_attn");
   }
   // o[b, h] = W_UV_h . o_lat[b, h]  (W_UV_h = Wkv_b rows [256h+128, 256h+256)), per head
@@ -587,6 +615,119 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B
     splits_wo = skinny_splits(H * 128, DEC_SPLIT_WO);
   }
   LAUNCH(mla::launch_splitk_reduce(part, splits_wo, B, dim, out, dim, s), "splitk_reduce(wo)");
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode(const mla_dims* d, const mla_weights* w, const void* x, int32_t B, void* kv_cache, int32_t max_len,
+               const int32_t* cache_len, const float* rope_cos, const float* rope_sin, int32_t rope_len, void* out,
+               void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  return decode_impl(d, w, x, B, kv_cache, max_len, cache_len, nullptr, 0, rope_cos, rope_sin, rope_len, out, ws,
+                     ws_bytes, stream);
+}
+
+int mla_decode_sparse(const mla_dims* d, const mla_weights* w, const void* x, int32_t B, void* kv_cache,
+                      int32_t max_len, const int32_t* cache_len, const int32_t* topk_idx, int32_t topk,
+                      const float* rope_cos, const float* rope_sin, int32_t rope_len, void* out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (!topk_idx) return fail(MLA_INVALID_ARG, "topk_idx must not be NULL");
+  if (topk <= 0 || topk > mla::DECODE_TOPK_MAX)
+    return fail(MLA_UNSUPPORTED, "topk must be in [1, %d]", mla::DECODE_TOPK_MAX);
+  return decode_impl(d, w, x, B, kv_cache, max_len, cache_len, topk_idx, topk, rope_cos, rope_sin, rope_len, out, ws,
+                     ws_bytes, stream);
+}
+
+size_t mla_prefill_absorbed_workspace_size(const mla_dims* dims, int32_t B, int32_t T) {
+  if (check_dims(dims) != MLA_OK || B <= 0 || T <= 0) return 0;
+  return absorbed_layout(dims, B, T, true, nullptr, nullptr);
+}
+
+int mla_prefill_absorbed(const mla_dims* d, const mla_weights* w, const void* x, int32_t B, int32_t T,
+                         const float* rope_cos, const float* rope_sin, int32_t rope_len, const int32_t* topk_idx,
+                         int32_t topk, void* out, void* kv_cache_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if ((rc = check_weights(w, MLA_BF16))) return rc;
+  if (d->kv_lora_rank != 512) return fail(MLA_UNSUPPORTED, "the absorbed prefill needs kv_lora_rank = 512");
+  if (d->n_heads % 64) return fail(MLA_UNSUPPORTED, "the absorbed prefill needs n_heads a multiple of 64");
+  if (!x || !out || !rope_cos || !rope_sin || !topk_idx)
+    return fail(MLA_INVALID_ARG, "x/out/rope tables/topk_idx must not be NULL");
+  if (B <= 0 || T <= 0) return fail(MLA_INVALID_ARG, "B and T must be positive");
+  if ((int64_t)B * T > (1LL << 24)) return fail(MLA_INVALID_ARG, "B*T too large");
+  if (rope_len < T) return fail(MLA_INVALID_ARG, "rope_len (%d) < T (%d)", rope_len, T);
+  if (topk <= 0 || topk > mla::DECODE_TOPK_MAX)
+    return fail(MLA_UNSUPPORTED, "topk must be in [1, %d]", mla::DECODE_TOPK_MAX);
+  AbsorbedWs p;
+  const size_t need = absorbed_layout(d, B, T, kv_cache_out == nullptr, ws, &p);
+  if (!ws || ws_bytes < need) return fail(MLA_INVALID_ARG, "workspace too small: need %zu bytes", need);
+  if ((uintptr_t)ws & 255) return fail(MLA_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const int H = d->n_heads, Dq = d->q_lora_rank, L = d->kv_lora_rank, dim = d->dim, NQKV = Dq + L + 64, M = B * T;
+  void* kvc = kv_cache_out ? kv_cache_out : p.kvc;
+  const uint16_t* wkv_b = (const uint16_t*)w->wkv_b;
+
+  // [c_q | latent | k_pe] and the norms exactly as in prefill: the cache entries and c_q
+  mla::GemmArgs gq = qkv_args(d, MLA_BF16, x, w->wq_a, w->wkv_a, p.cqkv, M);
+  const bool qkv_split = p.qkv_splits > 1 && mla::gemm_bf16_splits(gq) == p.qkv_splits;
+  if (qkv_split) {
+    gq.k_splits = p.qkv_splits; gq.part = p.part;
+    LAUNCH(mla::launch_gemm_bf16(gq, s), "gemm_bf16(split-K q_a|kv_a)");
+  } else {
+    LAUNCH(mla::launch_gemm_bf16(gq, s), "gemm_bf16(q_a|kv_a)");
+  }
+  mla::QkvNormArgs qa{};
+  qa.in = qkv_split ? (const void*)p.part : p.cqkv; qa.ld_in = NQKV; qa.in_dtype = qkv_split ? MLA_F32 : MLA_BF16;
+  qa.in_splits = qkv_split ? p.qkv_splits : 1; qa.split_stride = (int64_t)M * NQKV;
+  qa.rows = M; qa.Dq = Dq; qa.L = L; qa.gq = w->q_norm_w; qa.gkv = w->kv_norm_w; qa.eps = d->rms_eps;
+  qa.q_out = p.cqn; qa.ld_q = Dq; qa.kv_out = kvc; qa.ld_kv = L + 64;
+  qa.cos_tab = rope_cos; qa.sin_tab = rope_sin; qa.rope_len = rope_len; qa.pos_period = T;
+  if (!qkv_norm_ok(qa)) return fail(MLA_UNSUPPORTED, "the absorbed prefill needs 16-byte aligned norm weights");
+  LAUNCH(mla::launch_qkv_norm(qa, s), "qkv_norm");
+  // q = c_q . Wq_b^T with the rotary slices rotated at position t
+  mla::GemmArgs gr = gemm_args(p.cqn, Dq, w->wq_b, Dq, p.q, H * 192, MLA_BF16, M, H * 192, Dq);
+  gr.epi = mla::EPI_QROPE; gr.rope = {rope_cos, rope_sin, T};
+  if (mla::gemm_bf16_qrope_ok(gr)) {
+    LAUNCH(mla::launch_gemm_bf16(gr, s), "gemm_bf16(q_b + RoPE)");
+  } else {
+    gr.epi = mla::EPI_ROWMAJOR;
+    LAUNCH(mla::launch_gemm_bf16(gr, s), "gemm_bf16(q_b)");
+    mla::NormRopeArgs a = norm_args(p.q, H * 192, p.q, H * 192, MLA_BF16, M);
+    a.rope_off = 128; a.rope_heads = H; a.rope_stride = 192;
+    a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = rope_len; a.pos_period = T;
+    LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(q_pe)");
+  }
+  // q_lat[m, h] = [q_nope[m, h] . W_UK_h | q_pe[m, h]]: per head, W_UK_h = Wkv_b rows
+  // [256h, 256h+128) taken as the [K = 128, N = 512] operand
+  {
+    mla::GemmArgs g = gemm_args(p.q, H * 192, wkv_b, L, p.qlat, H * 576, MLA_BF16, M, L, 128);
+    g.batch = H; g.batch_a = 192; g.batch_w = 256 * (int64_t)L; g.batch_c = 576; g.w_kn = true;
+    LAUNCH(mla::launch_gemm_bf16(g, s), "gemm_bf16(absorb W_UK)");
+    LAUNCH(mla::launch_copy_rows((const uint16_t*)p.q + 128, 192, (uint16_t*)p.qlat + L, 576, (int64_t)M * H, 64, s),
+           "copy q_pe");
+  }
+  // attention of every token over its selected cache entries, in the latent space
+  {
+    mla::DecodeAttnArgs a{};
+    a.qlat = p.qlat; a.cache = kvc; a.cache_len = nullptr; a.olat = p.olat;
+    a.B = M; a.H = H; a.max_len = T; a.scale = d->softmax_scale;
+    a.idx = topk_idx; a.topk = topk; a.rows_per_seq = T;
+    LAUNCH(mla::launch_decode_attn(a, s), "sparse latent attention");
+  }
+  // o[m, h] = W_UV_h . o_lat[m, h] per head (W_UV_h = Wkv_b rows [256h+128, 256h+256)), then wo
+  {
+    mla::GemmArgs g = gemm_args(p.olat, H * (int64_t)L, wkv_b + 128 * (int64_t)L, L, p.o, H * 128, MLA_BF16, M, 128,
+                                L);
+    g.batch = H; g.batch_a = L; g.batch_w = 256 * (int64_t)L; g.batch_c = 128;
+    LAUNCH(mla::launch_gemm_bf16(g, s), "gemm_bf16(W_UV)");
+  }
+  LAUNCH(mla::launch_gemm_bf16(gemm_args(p.o, H * 128, w->wo, H * 128, out, dim, MLA_BF16, M, dim, H * 128), s),
+         "gemm_bf16(wo)");
   return MLA_OK;
 }
 

@@ -26,6 +26,12 @@
 // of ~44 nats) the workgroup recomputes its output in two passes: exact
 // maxima first, then the accumulation with those maxima.
 //
+// Selected keys: with an index list the workgroup first compacts the row's
+// live positions into LDS (ballot ranks, list order kept), padded with the
+// last one, and tile row r then loads cache row keys[k0 + r] instead of k0 + r;
+// everything after the loads is the dense path over nkeys = #live keys. The
+// same kernel serves a prefill in the absorbed form, one query row per token.
+//
 // LDS stage: latent rows [32][1024 B] then rope rows [32][128 B]. The 16-byte
 // chunks of latent row r are XOR-permuted within aligned groups of 16 by
 // ((r & 3) << 2) | ((r >> 2) & 3) and those of rope row r by (r >> 1) & 7, so
@@ -60,7 +66,11 @@ struct DecodeCtx {
   int nkeys, ntiles, wave, lane, hi, dh;
   float sl2;
   float* xs;                     // [2][4 waves][16][64] partial-score exchange
+  bool sparse;                   // tile rows from `keys` (else keys 0..nkeys-1)
+  const __attribute__((address_space(3))) int* keys;   // compacted selected positions
 };
+
+constexpr int KEYS_LDS = DECODE_TOPK_MAX + 4 * DKT;   // room for the tiles issued past the end
 
 __device__ __forceinline__ void load_lds16(const DecodeCtx& c, uint16_t* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0,
@@ -73,6 +83,17 @@ __device__ __forceinline__ void load_lds16(const DecodeCtx& c, uint16_t* lds, in
 // (their scores are masked).
 __device__ __forceinline__ void issue_tile(const DecodeCtx& c, uint16_t* st, int kt) {
   const int k0 = kt * DKT;
+  if (c.sparse) {   // cache rows from the compacted list (entries past nkeys repeat the last key)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * c.wave + i;
+      load_lds16(c, st + r * 512, (c.lane ^ swl(r)) << 4, __builtin_amdgcn_readfirstlane(c.keys[k0 + r]) * (DROW * 2));
+    }
+    const int r = 8 * c.wave + (c.lane >> 3);
+    const int t = c.keys[k0 + r];
+    load_lds16(c, st + DLAT + c.wave * 512, t * (DROW * 2) + 1024 + (((c.lane & 7) ^ swr(r)) << 4), 0);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = 8 * c.wave + i;
@@ -221,17 +242,23 @@ __device__ __forceinline__ bool attn_pass(const DecodeCtx& c, uint16_t* st0, uin
   return over;
 }
 
+template <bool SPARSE>
 __global__ __launch_bounds__(256, 1) void decode_attn_kernel(DecodeAttnArgs a, int n_hg) {
   __shared__ __attribute__((aligned(16))) uint16_t st0[DSTAGE];
   __shared__ __attribute__((aligned(16))) uint16_t st1[DSTAGE];
   __shared__ __attribute__((aligned(16))) uint16_t st2[DSTAGE];
   __shared__ __attribute__((aligned(16))) float xs[2 * 4 * 16 * 64];
+  __shared__ __attribute__((aligned(16))) int keys[SPARSE ? KEYS_LDS : 4];
+  __shared__ int wcount[4];
   __shared__ int s_over;
 
   const int tid = threadIdx.x;
   const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
-  const int hg = loc % n_hg, b = (loc / n_hg) * 8 + xcd;
-  if (b >= a.B) return;
+  // query row q; its cache sequence b and last key P
+  const int hg = loc % n_hg, q = (loc / n_hg) * 8 + xcd;
+  if (q >= a.B) return;
+  const int b = SPARSE && a.rows_per_seq > 0 ? q / a.rows_per_seq : q;
+  const int P = SPARSE && a.rows_per_seq > 0 ? q - b * a.rows_per_seq : a.cache_len[b];
   DecodeCtx c;
   c.lane = tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -239,8 +266,30 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(DecodeAttnArgs a, i
   c.hi = c.lane >> 5;
   c.xs = xs;
   c.sl2 = a.scale * 1.4426950408889634f;
-  const int P = a.cache_len[b];
+  c.sparse = SPARSE;
+  c.keys = (const __attribute__((address_space(3))) int*)keys;
   c.nkeys = (P >= 0 && P < a.max_len) ? P + 1 : 0;
+  if (SPARSE) {   // live listed positions t <= P, compacted in list order
+    const int32_t* row = a.idx + (int64_t)q * a.topk;
+    int base = 0;
+    for (int j0 = 0; j0 < a.topk; j0 += 256) {
+      const int j = j0 + tid;
+      const int t = j < a.topk ? row[j] : -1;
+      const bool ok = c.nkeys > 0 && t >= 0 && t <= P;
+      const uint64_t bal = __ballot(ok);
+      if (c.lane == 0) wcount[c.wave] = __popcll(bal);
+      __syncthreads();
+      int off = base;
+      for (int w = 0; w < c.wave; ++w) off += wcount[w];
+      if (ok) keys[off + __popcll(bal & ((1ull << c.lane) - 1))] = t;
+      base += wcount[0] + wcount[1] + wcount[2] + wcount[3];
+      __syncthreads();
+    }
+    c.nkeys = base;
+    const int last = base > 0 ? keys[base - 1] : 0;
+    for (int j = base + tid; j < KEYS_LDS; j += 256) keys[j] = last;
+    __syncthreads();
+  }
   c.ntiles = (c.nkeys + DKT - 1) / DKT;
   c.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.cache + (int64_t)b * a.max_len * DROW),
                                              (short)0, a.max_len * DROW * 2, BUF_DW3);
@@ -249,7 +298,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(DecodeAttnArgs a, i
   // this wave's half of the query: B operand of the score product, dims 288 dh + 16 kk + 8 hi + 0..7
   bf16x8 qf[18];
   {
-    const uint16_t* qp = (const uint16_t*)a.qlat + ((int64_t)b * a.H + head) * DROW + 288 * c.dh + 8 * c.hi;
+    const uint16_t* qp = (const uint16_t*)a.qlat + ((int64_t)q * a.H + head) * DROW + 288 * c.dh + 8 * c.hi;
 #pragma unroll
     for (int kk = 0; kk < 18; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 16 * kk));
   }
@@ -275,7 +324,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(DecodeAttnArgs a, i
   // o_lat[b, head, 256 dh + 32 dt + 8 rg + 4 hi + 0..3]
   l += __shfl_xor(l, 32);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  uint16_t* out = (uint16_t*)a.olat + ((int64_t)b * a.H + head) * 512 + 256 * c.dh + 4 * c.hi;
+  uint16_t* out = (uint16_t*)a.olat + ((int64_t)q * a.H + head) * 512 + 256 * c.dh + 4 * c.hi;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -289,7 +338,13 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(DecodeAttnArgs a, i
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s) {
   const int n_hg = a.H / 64;
   const unsigned grid = 8u * (unsigned)((a.B + 7) / 8) * (unsigned)n_hg;
-  decode_attn_kernel<<<grid, 256, 0, s>>>(a, n_hg);
+  if (a.idx) {
+    if (a.topk <= 0 || a.topk > DECODE_TOPK_MAX || a.rows_per_seq < 0) return hipErrorInvalidValue;
+    decode_attn_kernel<true><<<grid, 256, 0, s>>>(a, n_hg);
+  } else {
+    if (a.rows_per_seq != 0) return hipErrorInvalidValue;
+    decode_attn_kernel<false><<<grid, 256, 0, s>>>(a, n_hg);
+  }
   return hipGetLastError();
 }
 

@@ -256,6 +256,16 @@ __global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
   }
 }
 
+// Strided row copy, one 16-byte chunk per thread.
+__global__ __launch_bounds__(256) void copy_rows_kernel(const uint16_t* src, int64_t sld, uint16_t* dst, int64_t dld,
+                                                        int64_t rows, int cpr) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * cpr) return;
+  const int64_t r = i / cpr;
+  const int c = (int)(i - r * cpr);
+  *(uint4*)(dst + r * dld + 8 * c) = *(const uint4*)(src + r * sld + 8 * c);
+}
+
 // h = silu(g) * u, 8 bf16 values per thread (the unfused SwiGLU path).
 __global__ __launch_bounds__(256) void silu_mul_kernel(const uint4* g, const uint4* u, uint4* h, int64_t n8) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -444,6 +454,15 @@ hipError_t launch_quant_1x128(const void* a, int64_t lda, int a_dtype, int M, in
 hipError_t launch_quant_block128(const float* w, int N, int K, uint8_t* q, float* scales, hipStream_t s) {
   dim3 grid((K + 127) / 128, (N + 127) / 128);
   quant_block128_kernel<<<grid, 256, 0, s>>>(w, N, K, q, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(const uint16_t* src, int64_t sld, uint16_t* dst, int64_t dld, int64_t rows, int cols,
+                            hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if ((cols & 7) || (sld & 7) || (dld & 7) || (((uintptr_t)src | (uintptr_t)dst) & 15)) return hipErrorInvalidValue;
+  const int64_t n = rows * (cols / 8);
+  copy_rows_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(src, sld, dst, dld, rows, cols / 8);
   return hipGetLastError();
 }
 

@@ -140,6 +140,10 @@ hipError_t launch_rope_table(float* c, float* sn, int n_pos, float base, hipStre
 hipError_t launch_quant_1x128(const void* a, int64_t lda, int a_dtype, int M, int K,
                               uint8_t* q, float* scales, hipStream_t s);
 hipError_t launch_quant_block128(const float* w, int N, int K, uint8_t* q, float* scales, hipStream_t s);
+// dst[r*dld + c] = src[r*sld + c] for r < rows, c < cols (16-bit elements;
+// cols, sld, dld multiples of 8 and both pointers 16-byte aligned).
+hipError_t launch_copy_rows(const uint16_t* src, int64_t sld, uint16_t* dst, int64_t dld, int64_t rows, int cols,
+                            hipStream_t s);
 // h[i] = silu(g[i]) * u[i] over n bf16 values (n % 8 == 0, 16-byte aligned).
 hipError_t launch_silu_mul(const void* g, const void* u, void* h, int64_t n, hipStream_t s);
 // mask [B, T, ceil(Tk/32)]: bit t of row (b, s) is set iff t appears in
@@ -170,11 +174,19 @@ hipError_t launch_prefill_attn_f32(const PrefillAttnArgs& a, hipStream_t s);
 // Decode pieces.
 struct DecodeAttnArgs {
   const void* qlat;      // [B, H, 576] bf16: absorbed query (512) | rotated q_pe (64)
-  const void* cache;     // [B, max_len, 576] bf16
+  const void* cache;     // [B, max_len, 576] bf16 (with rows_per_seq: [B / rows_per_seq, max_len, 576])
   const int32_t* cache_len;
   void* olat;            // [B, H, 512] bf16
   int B, H, max_len; float scale;
+  // Selected keys (optional): row q attends only the positions listed in
+  // idx[q*topk .. q*topk + topk) (distinct; -1 and positions past the row's
+  // last key are ignored), topk <= DECODE_TOPK_MAX. rows_per_seq > 0 (only with
+  // idx): query row q is token q % rows_per_seq of sequence q / rows_per_seq,
+  // its last key that position (prefill); else row q is sequence q with last
+  // key cache_len[q] (decode).
+  const int32_t* idx; int topk; int rows_per_seq;
 };
+constexpr int DECODE_TOPK_MAX = 2048;
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s);
 // q_lat[b, h] = [q_nope[b, h] . W_UK_h | RoPE(q_pe[b, h], cache_len[b])] for kv_lora_rank 512;
 // q [B, H*192], wkv_b [H*256, 512] (bf16, or e4m3 codes with block scales

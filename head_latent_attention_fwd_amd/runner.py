@@ -108,7 +108,29 @@ class Decode:
         self.cos, self.sin = api.mla_rope_table(max_len, device=device)
         self.out = torch.empty((B, cfg["dim"]), dtype=torch.bfloat16, device=device)
         self.ws = api.workspace(api.mla_decode_workspace_size(self.dims, self.wdt, B, max_len), device)
+        self.topk = None if inp.get("topk_idx") is None else to_dev(inp["topk_idx"], torch.int32, device)
 
     def run(self, stream=None):
         return api.mla_decode(self.dims, self.weights, self.x, self.cache, self.cache_len, self.cos, self.sin,
-                              self.out, self.ws, stream=stream)
+                              self.out, self.ws, topk_idx=self.topk, stream=stream)
+
+
+class PrefillAbsorbed:
+    """One top-k prefill in the absorbed latent form (bf16)."""
+
+    def __init__(self, cfg, inp, device="cuda"):
+        self.cfg = cfg
+        B, T = cfg["B"], cfg["T"]
+        self.dims = dims_of(cfg)
+        self.x = to_dev(inp["x"], torch.bfloat16, device)
+        self.w = device_weights(inp["w"], "bf16", device)
+        self.weights = api.make_weights(self.w, api.MLA_BF16)
+        self.cos, self.sin = api.mla_rope_table(T, device=device)
+        self.topk = to_dev(inp["topk_idx"], torch.int32, device)
+        self.out = torch.empty_like(self.x)
+        self.kv_cache = torch.empty((B, T, cfg["kv_lora_rank"] + 64), dtype=torch.bfloat16, device=device)
+        self.ws = api.workspace(api.mla_prefill_absorbed_workspace_size(self.dims, B, T), device)
+
+    def run(self, stream=None):
+        return api.mla_prefill_absorbed(self.dims, self.weights, self.x, self.cos, self.sin, self.topk, self.out,
+                                        self.ws, kv_cache_out=self.kv_cache, stream=stream)

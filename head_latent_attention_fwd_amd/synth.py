@@ -145,4 +145,13 @@ def gen_decode(cfg, seed, max_len=None):
     cache[:, :P, :L] = round_to(lat, "bf16")
     cache[:, :P, L:] = round_to(rng.standard_normal((B, P, KV_ROPE)), "bf16")
     cache_len = np.full((B,), P, dtype=np.int32)
-    return dict(x=x, w=w, cache=cache, cache_len=cache_len)
+    topk = None
+    if cfg.get("topk"):   # the new token at position P selects like a prefill row at P
+        k = cfg["topk"]
+        topk = np.full((B, k), -1, dtype=np.int32)
+        for b in range(B):
+            if P < k:
+                topk[b, :P + 1] = np.arange(P + 1)
+            else:
+                topk[b] = np.sort(np.append(rng.choice(P, k - 1, replace=False), P))
+    return dict(x=x, w=w, cache=cache, cache_len=cache_len, topk_idx=topk)

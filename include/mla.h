@@ -272,6 +272,40 @@ MLA_API int mla_quant_e4m3_block128(const float* w, int32_t N, int32_t K, uint8_
 MLA_API int mla_topk_to_bitmask(const int32_t* topk_idx, int32_t B, int32_t T, int32_t topk,
                         uint32_t* mask, void* stream);
 
+/* Single-token decode over selected cache positions (DeepSeek-V3.2-Exp ·
+ * Sparse attention: the indexer's selection, applied with the causal mask, in
+ * the latent form a decoded token uses). As mla_decode, except that sequence b
+ * attends only the positions listed in topk_idx[b, 0:topk] that are <= its new
+ * position cache_len[b] (the new token's own slot must be listed to be
+ * attended).
+ *   topk_idx [B, topk] int32 DEVICE array, distinct positions per row, -1 pads
+ *            (a repeated position would be counted once per occurrence)
+ *   1 <= topk <= 2048 (MLA_UNSUPPORTED otherwise). Workspace as mla_decode. */
+MLA_API int mla_decode_sparse(const mla_dims* dims, const mla_weights* w, const void* x, int32_t B,
+                      void* kv_cache, int32_t max_len, const int32_t* cache_len, const int32_t* topk_idx,
+                      int32_t topk, const float* rope_cos, const float* rope_sin, int32_t rope_len,
+                      void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace mla_prefill_absorbed needs (0 on invalid input). */
+MLA_API size_t mla_prefill_absorbed_workspace_size(const mla_dims* dims, int32_t B, int32_t T);
+
+/* Prefill with a top-k selection computed in the absorbed latent form
+ * (DeepSeek-V3.2-Exp · Sparse attention: the same scores, selection and causal
+ * mask as mla_prefill with topk_idx; the Explanation's latent scoring applied to
+ * every token): kv_b's key half is folded into each token's query, every token
+ * gathers only its selected cache entries [normalised latent | rotated k_pe]
+ * (all heads share them), and the value half is applied after the attention.
+ * The work per token is proportional to topk instead of its position.
+ *   x [B, T, dim] bf16, bf16 weights, kv_lora_rank = 512, n_heads a multiple of 64
+ *   topk_idx [B, T, topk] int32 DEVICE array (required), distinct per row, -1 pads;
+ *            key t is live for query s iff t <= s and t is listed; 1 <= topk <= 2048
+ *   out [B, T, dim] bf16; kv_cache_out [B, T, kv_lora_rank + 64] bf16 or NULL
+ * Workspace: mla_prefill_absorbed_workspace_size bytes, 256-byte aligned. */
+MLA_API int mla_prefill_absorbed(const mla_dims* dims, const mla_weights* w, const void* x, int32_t B, int32_t T,
+                         const float* rope_cos, const float* rope_sin, int32_t rope_len,
+                         const int32_t* topk_idx, int32_t topk, void* out, void* kv_cache_out, void* ws,
+                         size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Shared-expert MLP
  * ------------------------------------------------------------------------ */

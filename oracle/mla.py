@@ -276,12 +276,13 @@ def _decode_tokens(x, w, d, P, fp8=None):
     return q_nope, q_pe, entry
 
 
-def mla_decode(x, w, d, cache, cache_len, seqs=None):
+def mla_decode(x, w, d, cache, cache_len, seqs=None, topk_idx=None):
     """Single-token decode, unabsorbed definition ([SA] "Explanation": one
     decoded token scores the cached latent; [DO] shapes [B,1,16384] -> [B,1,7168]).
 
     Per sequence b with P = cache_len[b]: the new token (position P) makes the
-    entry [c | k_pe] and is appended at slot P; keys are slots 0..P; every
+    entry [c | k_pe] and is appended at slot P; keys are slots 0..P (with
+    topk_idx [B, k]: the listed ones among them, [SA] "Code" mask); every
     cached latent is up-projected by kv_b into per-head k_nope and v exactly
     as in prefill, then standard attention and wo.
     x: [B, dim]; cache: [B, max_len, kv_lora+64] values; cache_len: [B].
@@ -297,12 +298,13 @@ def mla_decode(x, w, d, cache, cache_len, seqs=None):
         P = int(P_all[i])
         C = np.concatenate([np.asarray(cache[b, :P], dtype=np.float64), entries[i][None]], axis=0)
         k_nope, v = up_project(C[:, :L], w, d)
-        o_h, _ = attend_row(q_nope[i], q_pe[i], k_nope, C[:, L:], v, np.arange(P + 1), d["softmax_scale"])
+        live = live_keys(P, None if topk_idx is None else topk_idx[b])
+        o_h, _ = attend_row(q_nope[i], q_pe[i], k_nope, C[:, L:], v, live, d["softmax_scale"])
         o[i] = o_h.reshape(-1)
     return linear(o, w["wo"]), entries
 
 
-def mla_decode_absorbed(x, w, d, cache, cache_len, seqs=None, fp8=False):
+def mla_decode_absorbed(x, w, d, cache, cache_len, seqs=None, fp8=False, topk_idx=None):
     """Single-token decode with kv_b absorbed: the same result as mla_decode by
     reassociating the products. With W_UK_h = Wkv_b rows [256h, 256h+128) and
     W_UV_h = rows [256h+128, 256h+256):
@@ -315,6 +317,7 @@ def mla_decode_absorbed(x, w, d, cache, cache_len, seqs=None, fp8=False):
     W_UK enters dequantised (codes times block scale) since it is applied
     along its output dimension; W_UV_h is applied to o_lat_h as an fp8 Linear
     (o_lat_h quantised in 1x128 groups, the head's block row of scales).
+    With topk_idx [B, k] only the listed slots among 0..P are keys.
     Returns (out, new_entry) like mla_decode."""
     x = np.asarray(x, dtype=np.float64)
     seqs = np.arange(x.shape[0]) if seqs is None else np.asarray(seqs)
@@ -335,9 +338,10 @@ def mla_decode_absorbed(x, w, d, cache, cache_len, seqs=None, fp8=False):
     for i, b in enumerate(seqs):
         P = int(P_all[i])
         C = np.concatenate([np.asarray(cache[b, :P], dtype=np.float64), entries[i][None]], axis=0)
+        C = C[live_keys(P, None if topk_idx is None else topk_idx[b])]
         q_lat = np.einsum("hi,hic->hc", q_nope[i], W_UK)           # [H, L]
         z = (q_lat @ C[:, :L].T + q_pe[i] @ C[:, L:].T) * d["softmax_scale"]
-        p = softmax_over_live(z)                                  # [H, P+1]
+        p = softmax_over_live(z)                                  # [H, live keys]
         o_lat = p @ C[:, :L]                                      # [H, L]
         if fp8:
             for h in range(H):

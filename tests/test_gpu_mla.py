@@ -98,7 +98,8 @@ def _check_decode(cfg, seed, cache_len=None, seqs=None, max_len=None):
     run.run()
     torch.cuda.synchronize()
     d = oracle_dims(cfg)
-    ref, entry = mla.mla_decode_absorbed(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"], seqs=seqs, fp8=fp8)
+    ref, entry = mla.mla_decode_absorbed(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"], seqs=seqs, fp8=fp8,
+                                         topk_idx=inp.get("topk_idx"))
     got = run.out.float().cpu().numpy()
     sel = np.arange(cfg["B"]) if seqs is None else np.asarray(seqs)
     assert_parity(got[sel], ref, tol=tol, cos=cos, what=cfg["name"])
@@ -242,3 +243,69 @@ def test_prefill_cached_rejects_overflowing_chunk():
     run.start_pos = 7        # 7 + 10 > 16
     with pytest.raises(api.MlaError):
         run.run()
+
+
+# --------------------------------------------------------------------------
+# selected keys: decode over a selection, prefill in the absorbed latent form
+
+def test_decode_sparse_small_varied_lengths():
+    cfg = dict(name="dec_sparse", mode="decode", B=6, cache_len=40, dim=1024, q_lora_rank=256, kv_lora_rank=512,
+               n_heads=64, act="bf16", weight="bf16", topk=9)
+    inp_len = [0, 1, 31, 32, 33, 40]
+    inp = synth.gen_decode(cfg, 71, max_len=48)
+    inp["cache_len"] = np.asarray(inp_len, dtype=np.int32)
+    rng = np.random.default_rng(72)
+    # rows mix valid picks, -1 padding and positions past the row's own slot (ignored)
+    idx = np.full((6, 9), -1, dtype=np.int32)
+    for b, P in enumerate(inp_len):
+        k = min(P + 1, 7)
+        idx[b, :k] = rng.choice(P + 1, k, replace=False)
+        idx[b, 8] = min(P + 3, 47)
+    inp["topk_idx"] = idx
+    run = runner.Decode(cfg, inp)
+    run.run()
+    torch.cuda.synchronize()
+    d = oracle_dims(cfg)
+    ref, _ = mla.mla_decode_absorbed(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"], topk_idx=idx)
+    assert_parity(run.out.float().cpu().numpy(), ref, what="sparse decode")
+
+
+def test_decode_sparse_cache_past_2048():
+    # 3000 cached positions, 2048 selected per sequence
+    cfg = dict(name="dec_sparse_long", mode="decode", B=4, cache_len=3000, dim=1024, q_lora_rank=256,
+               kv_lora_rank=512, n_heads=128, act="bf16", weight="bf16", topk=2048)
+    _check_decode(cfg, 73, max_len=3008)
+
+
+def test_decode_sparse_dsv32_full_size_sampled():
+    cfg = config(4, cache_len=4000, topk=2048)
+    _check_decode(cfg, synth.seed_of(4), max_len=4096, seqs=[0, 1, 63, 127])
+
+
+def _check_absorbed(cfg, seed, rows=None):
+    inp = synth.gen_prefill(cfg, seed)
+    run = runner.PrefillAbsorbed(cfg, inp)
+    run.run()
+    torch.cuda.synchronize()
+    d = oracle_dims(cfg)
+    ref = mla.mla_prefill(inp["x"], inp["w"], d, topk_idx=inp["topk_idx"], rows=rows)
+    got = run.out.float().cpu().numpy()
+    assert_parity(got if rows is None else got[:, rows], ref, what=f"{cfg['name']} absorbed")
+    return inp, run
+
+
+def test_prefill_absorbed_small_topk():
+    inp, run = _check_absorbed(small_cfg(T=300, B=2, topk=40, n_heads=64), 74)
+    d = oracle_dims(small_cfg())
+    entry = mla.latent_path(inp["x"][1], inp["w"], d, np.arange(300))
+    assert_parity(run.kv_cache[1].float().cpu().numpy(), entry, what="kv_cache_out")
+
+
+def test_prefill_absorbed_selection_wider_than_rows():
+    # topk above T: every row keeps its whole causal prefix
+    _check_absorbed(small_cfg(T=100, B=1, topk=128, n_heads=128), 75)
+
+
+def test_prefill_absorbed_dsv32_full_size_sampled():
+    cfg = config(3)
+    _check_absorbed(cfg, synth.seed_of(3), rows=_sample_rows(cfg["T"], np.random.default_rng(3)))

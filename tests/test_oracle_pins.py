@@ -418,6 +418,30 @@ def test_fp8_absorbed_decode_tracks_the_exact_decode():
     assert np.abs(e_got - e_exact).max() / np.abs(e_exact).max() < 0.3
 
 
+def test_selected_decode_equals_the_selected_prefill_row():
+    """Decoding token P over the cache of tokens 0..P-1 with a selection gives
+    the prefill row P under the same selection (absorbed and unabsorbed forms);
+    a selection listing every position reduces to the plain decode."""
+    cfg, d, inp = small(T=15, seed=61)
+    rng = np.random.default_rng(62)
+    idx = np.full((1, 15, 6), -1, dtype=np.int64)
+    for s in range(15):
+        k = min(s + 1, 6)
+        idx[0, s, :k] = rng.choice(s + 1, k, replace=False)
+    out, aux = mla.mla_prefill(inp["x"], inp["w"], d, topk_idx=idx, return_aux=True)
+    P = 14
+    cache = aux["cache"][0][None, :P]
+    x_new = inp["x"][:, P]
+    o1, _ = mla.mla_decode(x_new, inp["w"], d, cache, np.array([P]), topk_idx=idx[:, P])
+    o2, _ = mla.mla_decode_absorbed(x_new, inp["w"], d, cache, np.array([P]), topk_idx=idx[:, P])
+    np.testing.assert_allclose(o1[0], out[0, P], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(o2[0], out[0, P], rtol=1e-11, atol=1e-12)
+    everything = np.arange(P + 1)[None]
+    o3, _ = mla.mla_decode_absorbed(x_new, inp["w"], d, cache, np.array([P]), topk_idx=everything)
+    o4, _ = mla.mla_decode_absorbed(x_new, inp["w"], d, cache, np.array([P]))
+    np.testing.assert_allclose(o3, o4, rtol=1e-12, atol=1e-13)
+
+
 # --------------------------------------------------------------------------
 # selection mask
 
