@@ -56,8 +56,9 @@ def decode_bytes(cfg):
     n_w = (Dq + L + 64) * d + H * 192 * Dq + H * 256 * L + d * H * 128
     # bf16: 2 bytes a weight; e4m3: 1 byte plus one fp32 scale per 128 x 128 block
     w = n_w + 4 * n_w // (128 * 128) if cfg.get("weight") == "e4m3" else 2 * n_w
-    cache = 2 * B * (P + 1) * (L + 64)
-    io = 2 * (2 * B * d + B * (L + 64))
+    keys = min(P + 1, cfg["topk"]) if cfg.get("topk") else P + 1   # a selection reads only its keys
+    cache = 2 * B * keys * (L + 64)
+    io = 2 * (2 * B * d + B * (L + 64)) + (4 * B * cfg["topk"] if cfg.get("topk") else 0)
     return w + cache + io, {"weights": w, "cache": cache, "io": io}
 
 
@@ -198,16 +199,17 @@ def prefill_kernel_breakdown(cfg, inp, run):
     return out
 
 
-def bench_decode(cfg_index, steps, warmup, kernels=False, weight="bf16"):
+def bench_decode(cfg_index, steps, warmup, kernels=False, weight="bf16", **over):
     import torch
     from head_latent_attention_fwd_amd import api, runner, synth
-    cfg = dict(synth.CONFIGS[cfg_index], weight=weight)
-    inp = synth.gen_decode(cfg, synth.seed_of(cfg_index))
+    cfg = dict(synth.CONFIGS[cfg_index], weight=weight, **over)
+    inp = synth.gen_decode(cfg, synth.seed_of(cfg_index), max_len=cfg["cache_len"] + 1)
     run = runner.Decode(cfg, inp)
     nbytes, parts = decode_bytes(cfg)
     flush = Flusher()
     sec = event_avg(run.run, steps, warmup=warmup, flush=flush)   # cache slot P is rewritten identically each step
-    res = {"workload": cfg["name"] + ("_e4m3" if weight == "e4m3" else ""), "B": cfg["B"],
+    res = {"workload": cfg["name"] + ("_e4m3" if weight == "e4m3" else "") + (f"_top{cfg['topk']}" if cfg.get("topk")
+                                                                             else ""), "B": cfg["B"],
            "cache_len": cfg["cache_len"], "n_heads": cfg["n_heads"], "weights": weight, "us_per_step": sec * 1e6, "gbps": nbytes / sec / 1e9, "frac_of_hbm": nbytes / sec / 1e9 / PEAK["hbm"],
            "algorithmic_bytes": nbytes, "bytes": parts, "timing": "HIP events per step, 1 GiB read between steps (caches hold nothing of the step)"}
     if kernels:
@@ -219,6 +221,33 @@ def bench_decode(cfg_index, steps, warmup, kernels=False, weight="bf16"):
                                         "frac": parts["cache"] / s / 1e9 / PEAK["hbm"], "bytes": parts["cache"]}}
     del run, flush
     torch.cuda.empty_cache()
+    return res
+
+
+def bench_absorbed(cfg_index, steps, warmup, T=None):
+    """Top-k prefill computed in the absorbed latent form (gathered keys shared
+    by all heads), on a DeepSeek-V3.2-Exp sparse shape; optionally also the
+    dense-masked path at the same shape for the crossover."""
+    import torch
+    from head_latent_attention_fwd_amd import runner, synth
+    cfg = dict(synth.CONFIGS[cfg_index])
+    if T is not None:
+        cfg["T"] = T
+    inp = synth.gen_prefill(cfg, synth.seed_of(cfg_index))
+    flops, g, attn = prefill_flops(cfg, inp["topk_idx"])
+    run = runner.PrefillAbsorbed(cfg, inp)
+    sec = wall_steps(run.run, steps, warmup)
+    res = {"workload": cfg["name"] + "_absorbed_gather", "B": cfg["B"], "T": cfg["T"], "n_heads": cfg["n_heads"],
+           "topk": cfg["topk"], "ms_per_step": sec * 1e3, "tflops": flops / sec / 1e12,
+           "frac_of_bf16_peak": flops / sec / 1e12 / PEAK["bf16"], "algorithmic_flop": flops}
+    del run
+    torch.cuda.empty_cache()
+    if T is not None:   # the dense-masked path at the same shape
+        dense = runner.Prefill(cfg, inp, keep_cache=False)
+        sec_d = wall_steps(dense.run, steps, warmup)
+        res["dense_masked_ms_per_step"] = sec_d * 1e3
+        del dense
+        torch.cuda.empty_cache()
     return res
 
 
@@ -317,9 +346,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
-    ap.add_argument("--workloads", default="1,2,3,4,5,6,7",
+    ap.add_argument("--workloads", default="1,2,3,4,5,6,7,8,9",
                     help="config indices to run (1 = headline; 5 = shared-expert SwiGLU MLP; "
-                         "6 = chunked prefill after 2048 cached tokens; 7 = decode with e4m3 weights)")
+                         "6 = chunked prefill after 2048 cached tokens; 7 = decode with e4m3 weights; "
+                         "8 = config 3 in the absorbed gather form; 9 = top-2048 decode over 4000 cached; "
+                         "10 = absorbed vs dense-masked top-k prefill at T = 16384)")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel event breakdown")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -344,6 +375,12 @@ def main():
             results[i] = bench_chunk(args.steps, args.warmup)
         elif i == 7:
             results[i] = bench_decode(4, args.steps, args.warmup, weight="e4m3")
+        elif i == 8:
+            results[i] = bench_absorbed(3, args.steps, args.warmup)
+        elif i == 9:
+            results[i] = bench_decode(4, args.steps, args.warmup, cache_len=4000, topk=2048)
+        elif i == 10:
+            results[i] = bench_absorbed(3, max(1, args.steps // 4), 1, T=16384)
         else:
             results[i], _ = bench_prefill(i, args.steps, args.warmup, kernels and i == 1)
         if i == 1:
