@@ -167,7 +167,7 @@ size_t decode_layout(const mla_dims* d, int wdt, int B, void* ws, DecodeWs* out)
 }
 
 struct AbsorbedWs {
-  void *cqkv, *cqn, *kvc, *q, *qlat, *olat, *o;
+  void *cqkv, *cqn, *kvc, *q, *qlat, *olat, *o, *wukt;
   float* part;
   int qkv_splits;
 };
@@ -183,6 +183,7 @@ size_t absorbed_layout(const mla_dims* d, int B, int T, bool own_kvc, void* ws, 
   p.qlat = c.take(M * H * (L + 64) * 2);
   p.olat = c.take(M * H * L * 2);
   p.o = c.take(M * H * 128 * 2);
+  p.wukt = c.take(H * L * 128 * 2);
   p.qkv_splits = prefill_qkv_splits(d, MLA_BF16, MLA_BF16, (int)M);
   p.part = p.qkv_splits > 1 ? (float*)c.take((size_t)p.qkv_splits * M * (Dq + L + 64) * 4) : nullptr;
   if (out) *out = p;
@@ -703,10 +704,13 @@ int mla_prefill_absorbed(const mla_dims* d, const mla_weights* w, const void* x,
     LAUNCH(mla::launch_rmsnorm_rope(a, s), "rmsnorm_rope(q_pe)");
   }
   // q_lat[m, h] = [q_nope[m, h] . W_UK_h | q_pe[m, h]]: per head, W_UK_h = Wkv_b rows
-  // [256h, 256h+128) taken as the [K = 128, N = 512] operand
+  // [256h, 256h+128) transposed once per call to the [N = 512, K = 128] operand
+  // of the big-tile GEMM
   {
-    mla::GemmArgs g = gemm_args(p.q, H * 192, wkv_b, L, p.qlat, H * 576, MLA_BF16, M, L, 128);
-    g.batch = H; g.batch_a = 192; g.batch_w = 256 * (int64_t)L; g.batch_c = 576; g.w_kn = true;
+    LAUNCH(mla::launch_transpose16(wkv_b, L, 256 * (int64_t)L, (uint16_t*)p.wukt, 128, (int64_t)L * 128, 128, L, H, s),
+           "transpose W_UK");
+    mla::GemmArgs g = gemm_args(p.q, H * 192, p.wukt, 128, p.qlat, H * 576, MLA_BF16, M, L, 128);
+    g.batch = H; g.batch_a = 192; g.batch_w = (int64_t)L * 128; g.batch_c = 576;
     LAUNCH(mla::launch_gemm_bf16(g, s), "gemm_bf16(absorb W_UK)");
     LAUNCH(mla::launch_copy_rows((const uint16_t*)p.q + 128, 192, (uint16_t*)p.qlat + L, 576, (int64_t)M * H, 64, s),
            "copy q_pe");

@@ -256,6 +256,24 @@ __global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
   }
 }
 
+// Batched transpose through a 64 x 65 LDS tile.
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* src, int64_t sld, int64_t sb, uint16_t* dst,
+                                                          int64_t dld, int64_t db, int rows, int cols) {
+  __shared__ uint16_t t[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64, z = blockIdx.z;
+  const uint16_t* S = src + z * sb;
+  uint16_t* D = dst + z * db;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = i >> 6, c = i & 63;
+    if (r0 + r < rows && c0 + c < cols) t[r][c] = S[(int64_t)(r0 + r) * sld + c0 + c];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int c = i >> 6, r = i & 63;
+    if (r0 + r < rows && c0 + c < cols) D[(int64_t)(c0 + c) * dld + r0 + r] = t[r][c];
+  }
+}
+
 // Strided row copy, one 16-byte chunk per thread.
 __global__ __launch_bounds__(256) void copy_rows_kernel(const uint16_t* src, int64_t sld, uint16_t* dst, int64_t dld,
                                                         int64_t rows, int cpr) {
@@ -454,6 +472,14 @@ hipError_t launch_quant_1x128(const void* a, int64_t lda, int a_dtype, int M, in
 hipError_t launch_quant_block128(const float* w, int N, int K, uint8_t* q, float* scales, hipStream_t s) {
   dim3 grid((K + 127) / 128, (N + 127) / 128);
   quant_block128_kernel<<<grid, 256, 0, s>>>(w, N, K, q, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose16(const uint16_t* src, int64_t sld, int64_t sb, uint16_t* dst, int64_t dld, int64_t db,
+                              int rows, int cols, int batch, hipStream_t s) {
+  if (rows <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
+  dim3 grid((cols + 63) / 64, (rows + 63) / 64, batch);
+  transpose16_kernel<<<grid, 256, 0, s>>>(src, sld, sb, dst, dld, db, rows, cols);
   return hipGetLastError();
 }
 

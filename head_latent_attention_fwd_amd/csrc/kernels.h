@@ -144,6 +144,10 @@ hipError_t launch_quant_block128(const float* w, int N, int K, uint8_t* q, float
 // cols, sld, dld multiples of 8 and both pointers 16-byte aligned).
 hipError_t launch_copy_rows(const uint16_t* src, int64_t sld, uint16_t* dst, int64_t dld, int64_t rows, int cols,
                             hipStream_t s);
+// dst[z][c][r] = src[z][r][c] (16-bit elements) for r < rows, c < cols; row
+// strides sld / dld, batch strides sb / db.
+hipError_t launch_transpose16(const uint16_t* src, int64_t sld, int64_t sb, uint16_t* dst, int64_t dld, int64_t db,
+                              int rows, int cols, int batch, hipStream_t s);
 // h[i] = silu(g[i]) * u[i] over n bf16 values (n % 8 == 0, 16-byte aligned).
 hipError_t launch_silu_mul(const void* g, const void* u, void* h, int64_t n, hipStream_t s);
 // mask [B, T, ceil(Tk/32)]: bit t of row (b, s) is set iff t appears in
