@@ -157,3 +157,48 @@ def test_building_block_argument_errors(hostonly):
     assert lib.rmsnorm_rope(fake(), 100, api.MLA_BF16, 4, 0, None, 0.0, 64, 1, 64, fake(), fake(), 16, None, 16,
                             fake(), 100, api.MLA_BF16, None) == api.MLA_INVALID_ARG   # slice past ld
     assert lib.mla_rope_table(fake(), fake(), 0, 10000.0, None) == api.MLA_INVALID_ARG
+
+
+def test_widened_entry_point_argument_errors(hostonly):
+    # chunked prefill, selected-key decode, absorbed prefill and the SwiGLU MLP
+    # reject bad arguments before any device call
+    lib = hostonly
+    d = _dims()
+    w = api.MlaWeights(api.MLA_BF16, *[fake(i + 1) for i in range(12)])
+
+    def chunk(T=16, start=8, max_len=32, cache=fake(), rl=64, wsb=1 << 40):
+        return lib.mla_prefill_cached(ctypes.byref(d), ctypes.byref(w), fake(), 1, T, start, cache, max_len, fake(),
+                                      fake(), rl, None, 0, fake(), fake(), wsb, None)
+    assert chunk(cache=None) == api.MLA_INVALID_ARG
+    assert chunk(start=20) == api.MLA_INVALID_ARG and "max_len" in api.mla_last_error()   # 20 + 16 > 32
+    assert chunk(start=-1) == api.MLA_INVALID_ARG
+    assert chunk(rl=20) == api.MLA_INVALID_ARG and "rope_len" in api.mla_last_error()
+    assert chunk(cache=ctypes.c_void_p(0x1008)) == api.MLA_UNSUPPORTED                    # misaligned cache
+    assert chunk(wsb=100) == api.MLA_INVALID_ARG and "workspace" in api.mla_last_error()
+    assert api.mla_prefill_cached_workspace_size(d, api.MLA_BF16, 1, 16, 64, 0) > \
+        api.mla_prefill_cached_workspace_size(d, api.MLA_BF16, 1, 16, 0, 0)   # k_nope / v^T for 80 keys (padded to 128)
+
+    dd = api.make_dims(7168, 1536, 512, 128)
+
+    def sparse(idx=fake(), k=2048, wsb=1 << 40):
+        return lib.mla_decode_sparse(ctypes.byref(dd), ctypes.byref(w), fake(), 4, fake(), 16, fake(), idx, k,
+                                     fake(), fake(), 16, fake(), fake(), wsb, None)
+    assert sparse(idx=None) == api.MLA_INVALID_ARG
+    assert sparse(k=0) == api.MLA_UNSUPPORTED and sparse(k=2049) == api.MLA_UNSUPPORTED
+    assert sparse(wsb=10) == api.MLA_INVALID_ARG
+
+    def absorbed(idx=fake(), k=64, T=16, rl=16, dims=dd):
+        return lib.mla_prefill_absorbed(ctypes.byref(dims), ctypes.byref(w), fake(), 1, T, fake(), fake(), rl, idx, k,
+                                        fake(), None, fake(), 1 << 40, None)
+    assert absorbed(idx=None) == api.MLA_INVALID_ARG
+    assert absorbed(k=4096) == api.MLA_UNSUPPORTED
+    assert absorbed(rl=8) == api.MLA_INVALID_ARG
+    assert absorbed(dims=api.make_dims(7168, 1536, 512, 100)) == api.MLA_UNSUPPORTED
+    assert api.mla_prefill_absorbed_workspace_size(dd, 1, 16) > 0
+
+    def mlp(hidden=128, inter=128, x=fake(), wsb=1 << 40):
+        return lib.mla_swiglu_mlp(x, 4, hidden, inter, fake(), fake(), fake(), fake(), fake(), wsb, None)
+    assert mlp(x=None) == api.MLA_INVALID_ARG
+    assert mlp(hidden=100) == api.MLA_UNSUPPORTED
+    assert mlp(wsb=10) == api.MLA_INVALID_ARG
+    assert lib.mla_swiglu_workspace_size(4, 128) >= 3 * 4 * 128 * 2
