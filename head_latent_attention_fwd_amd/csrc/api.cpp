@@ -125,6 +125,7 @@ size_t prefill_layout(const mla_dims* d, int wdt, int adt, int B, int T, int Tk,
     if (Dq > kmax) kmax = Dq;
     if (L > kmax) kmax = L;
     if (H * 128 > kmax) kmax = H * 128;
+    if (Dq + L > kmax) kmax = Dq + L;   // the norm pass's codes of c_q and the latent side by side
     const size_t rows = M > (size_t)Tk ? M : (size_t)Tk;   // kv_b over a cache runs per sequence
     p.aq = c.take(rows * kmax);
     p.as = c.take(rows * (kmax / 128) * 4);
@@ -218,13 +219,17 @@ bool qkv_norm_ok(const mla::QkvNormArgs& a) {
 int project(int wdt, int adt, const void* act, int64_t lda, const void* W, const float* Ws,
             const void* W2, const float* W2s, int n_split, void* out, int64_t ldo, int M, int N, int K,
             const PrefillWs* ws, hipStream_t s, const mla::KvSplit* kv = nullptr, const mla::RopeEpi* rope = nullptr,
-            bool* roped = nullptr, int cdt = -1) {
+            bool* roped = nullptr, int cdt = -1, const uint8_t* act_codes = nullptr,
+            const float* act_scales = nullptr) {
   const int epi = kv ? mla::EPI_KV_SPLIT : mla::EPI_ROWMAJOR;
   if (roped) *roped = false;
   if (wdt == MLA_E4M3) {
-    LAUNCH(mla::launch_quant_1x128(act, lda, adt, M, K, (uint8_t*)ws->aq, (float*)ws->as, s), "quant_e4m3_1x128");
+    // the activation's e4m3 codes: made by an earlier pass (act_codes), or quantised here
+    if (!act_codes)
+      LAUNCH(mla::launch_quant_1x128(act, lda, adt, M, K, (uint8_t*)ws->aq, (float*)ws->as, s), "quant_e4m3_1x128");
     mla::GemmFp8Args g{};
-    g.A = (const uint8_t*)ws->aq; g.a_scale = (const float*)ws->as;
+    g.A = act_codes ? act_codes : (const uint8_t*)ws->aq;
+    g.a_scale = act_codes ? act_scales : (const float*)ws->as;
     g.W = (const uint8_t*)W; g.w_scale = Ws; g.W2 = (const uint8_t*)W2; g.w2_scale = W2s; g.n_split = n_split;
     g.C = out; g.ldc = ldo; g.c_dtype = cdt < 0 ? adt : cdt; g.M = M; g.N = N; g.K = K;
     g.epi = epi;
@@ -393,11 +398,25 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t
   qa.q_out = p.cqn; qa.ld_q = Dq; qa.kv_out = kvc; qa.ld_kv = L + 64; qa.kv_batch_stride = cache_bs;
   qa.kpe = p.kpe; qa.kpe_tp = Tp;
   qa.cos_tab = rope_cos; qa.sin_tab = rope_sin; qa.rope_len = rope_len; qa.pos_period = T; qa.pos_off = P;
+  // e4m3: the norm pass also quantises c_q (q_b's input) and, when kv_b reads
+  // exactly these rows, the latent (kv_b's input)
+  const bool kv_fresh = P == 0 && cache_bs == (int64_t)T * (L + 64);
+  uint8_t* cq_codes = nullptr; float* cq_scales = nullptr;
+  uint8_t* kv_codes = nullptr; float* kv_scales = nullptr;
+  if (wdt == MLA_E4M3) {
+    cq_codes = (uint8_t*)p.aq; cq_scales = (float*)p.as;
+    qa.q_codes = cq_codes; qa.q_scales = cq_scales;
+    if (kv_fresh) {
+      kv_codes = cq_codes + (size_t)M * Dq; kv_scales = cq_scales + (size_t)M * (Dq / 128);
+      qa.kv_codes = kv_codes; qa.kv_scales = kv_scales;
+    }
+  }
   if (adt == MLA_BF16 && qkv_norm_ok(qa)) {
     LAUNCH(mla::launch_qkv_norm(qa, s), "qkv_norm");
   } else if (P > 0 || cache_bs != (int64_t)T * (L + 64)) {
     return fail(MLA_UNSUPPORTED, "prefill over a cache needs bf16 activations and 16-byte aligned norm weights");
   } else {
+    cq_codes = nullptr; kv_codes = nullptr;   // the separate norm passes quantise nothing
   {  // q_norm
     mla::NormRopeArgs a = norm_args(qkv_in, NQKV, p.cqn, Dq, adt, M);
     from_qkv(a);
@@ -425,7 +444,7 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t
   } else {
     bool roped = false;
     if ((rc = project(wdt, adt, p.cqn, Dq, w->wq_b, w->wq_b_scale, nullptr, nullptr, H * 192, p.q, H * 192, M,
-                      H * 192, Dq, &p, s, nullptr, &gr.rope, &roped)))
+                      H * 192, Dq, &p, s, nullptr, &gr.rope, &roped, -1, cq_codes, cq_scales)))
       return rc;
     if (!roped) {
       mla::NormRopeArgs a = norm_args(p.q, H * 192, p.q, H * 192, adt, M);
@@ -438,10 +457,10 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t
   // k_nope [B,H,Tp,128] and v^T [B,H,128,Tp]; the cached keys' k_pe joins the new ones
   LAUNCH(mla::launch_zero_kv_padding(p.kn, p.vt, p.kpe, B, H, Tk, Tp, (int)es, s), "zero_kv_padding");
   LAUNCH(mla::launch_gather_kpe(kvc, cache_bs, L + 64, L, B, P, p.kpe, Tp, s), "gather_kpe");
-  if (P == 0 && cache_bs == (int64_t)T * (L + 64)) {   // one launch over the B*T contiguous entries
+  if (kv_fresh) {   // one launch over the B*T contiguous entries
     const mla::KvSplit split{p.vt, T, Tp, H};
     if ((rc = project(wdt, adt, kvc, L + 64, w->wkv_b, w->wkv_b_scale, nullptr, nullptr, H * 256, p.kn, 0, M,
-                      H * 256, L, &p, s, &split)))
+                      H * 256, L, &p, s, &split, nullptr, nullptr, -1, kv_codes, kv_scales)))
       return rc;
   } else {
     for (int b = 0; b < B; ++b) {   // the sequences' cache rows are cache_bs apart
@@ -458,11 +477,14 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t
   at.q = p.q; at.kn = p.kn; at.vt = p.vt; at.kpe = p.kpe;
   at.mask = (const uint32_t*)p.mask; at.out = p.attn; at.B = B; at.T = T; at.Tp = Tp; at.H = H; at.P = P;
   at.scale = d->softmax_scale;
+  const bool o_codes = wdt == MLA_E4M3 && adt == MLA_BF16;   // wo's e4m3 input straight from the attention
+  if (o_codes) { at.oq = (uint8_t*)p.aq; at.os = (float*)p.as; }
   if (adt == MLA_F32) LAUNCH(mla::launch_prefill_attn_f32(at, s), "prefill_attn_f32");
   else LAUNCH(mla::launch_prefill_attn_bf16(at, s), "prefill_attn");
   // out = o . Wo^T
   return project(wdt, adt, p.attn, H * 128, w->wo, w->wo_scale, nullptr, nullptr, dim, out, dim, M, dim, H * 128,
-                 &p, s);
+                 &p, s, nullptr, nullptr, nullptr, -1, o_codes ? (const uint8_t*)p.aq : nullptr,
+                 o_codes ? (const float*)p.as : nullptr);
 }
 
 }  // namespace

@@ -246,6 +246,37 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
 
   const float lt = l + __shfl_xor(l, 32);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (a.oq) {
+    // e4m3 output for the next projection: the (query, head) row's 128 values
+    // are this lane's 64 and those of lane ^ 32, one scale group
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        o[j][r] = __uint_as_float((uint32_t)f2bf(o[j][r] * inv) << 16);
+        amax = fmaxf(amax, fabsf(o[j][r]));
+      }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const float sc = amax / 448.0f;
+    if (q_ok) {
+      const int64_t row = (int64_t)b * T + qi;
+      uint8_t* op = a.oq + row * ((int64_t)H * 128) + h * 128;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const float v0 = o[j][r], v1 = o[j][r + 1], v2 = o[j][r + 2], v3 = o[j][r + 3];
+          uint32_t code = 0u;
+          if (sc != 0.f)
+            code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+                v2 / sc, v3 / sc, __builtin_amdgcn_cvt_pk_fp8_f32(v0 / sc, v1 / sc, 0, false), true);
+          *(uint32_t*)(op + j * 32 + row32(r, lane)) = code;
+        }
+      if (hi == 0) a.os[row * H + h] = sc;
+    }
+    return;
+  }
   if (q_ok) {
     uint16_t* op = (uint16_t*)a.out + ((int64_t)b * T + qi) * ((int64_t)H * 128) + h * 128;
 #pragma unroll

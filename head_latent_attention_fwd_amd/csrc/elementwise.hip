@@ -234,8 +234,23 @@ __global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
     } else if (c < nq + nkv && kv) {
       const int e = 4 * (c - nq);
       const float4 g = *(const float4*)&a.gkv[e];
-      *(uint2*)(kv + e) = make_uint2(pack_bf16x2(g.x * (v[j].x * rkv), g.y * (v[j].y * rkv)),
-                                     pack_bf16x2(g.z * (v[j].z * rkv), g.w * (v[j].w * rkv)));
+      const uint2 pk = make_uint2(pack_bf16x2(g.x * (v[j].x * rkv), g.y * (v[j].y * rkv)),
+                                  pack_bf16x2(g.z * (v[j].z * rkv), g.w * (v[j].w * rkv)));
+      *(uint2*)(kv + e) = pk;
+      if (a.kv_codes) {   // as for q: 32 consecutive lanes hold one 128-wide group
+        const float y0 = __uint_as_float(pk.x << 16), y1 = __uint_as_float(pk.x & 0xffff0000u);
+        const float y2 = __uint_as_float(pk.y << 16), y3 = __uint_as_float(pk.y & 0xffff0000u);
+        float amax = fmaxf(fmaxf(fabsf(y0), fabsf(y1)), fmaxf(fabsf(y2), fabsf(y3)));
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        const float s = amax / 448.0f;
+        uint32_t code = 0u;
+        if (s != 0.f)
+          code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+              y2 / s, y3 / s, __builtin_amdgcn_cvt_pk_fp8_f32(y0 / s, y1 / s, 0, false), true);
+        *(uint32_t*)(a.kv_codes + (int64_t)row * a.L + e) = code;
+        if (((c - nq) & 31) == 0) a.kv_scales[(int64_t)row * (a.L >> 7) + ((c - nq) >> 5)] = s;
+      }
     }
   }
   if (tid < 32) {
@@ -438,7 +453,8 @@ hipError_t launch_qkv_norm(const QkvNormArgs& a, hipStream_t s) {
   if ((a.Dq & 3) || (a.L & 3) || (a.ld_in & 3) || (a.Dq + a.L + 64) / 4 > 256 * QKV_CH ||
       (a.in_dtype != DT_F32 && a.in_dtype != DT_BF16) || (a.in_dtype == DT_F32 && (a.split_stride & 3)) ||
       (a.ld_q & 3) || (a.ld_kv & 3) || (a.kv_pos_stride & 3) || a.in_splits < 1 || (!a.pos && a.pos_period <= 0) ||
-      (a.q_codes && ((a.Dq & 127) || !a.q_scales || ((uintptr_t)a.q_codes & 3))))
+      (a.q_codes && ((a.Dq & 127) || !a.q_scales || ((uintptr_t)a.q_codes & 3))) ||
+      (a.kv_codes && ((a.Dq & 127) || (a.L & 127) || !a.kv_scales || ((uintptr_t)a.kv_codes & 3))))
     return hipErrorInvalidValue;
   qkv_norm_kernel<<<a.rows, 256, 0, s>>>(a);
   return hipGetLastError();

@@ -134,6 +134,8 @@ struct QkvNormArgs {
   // optional e4m3 copy of the normalised q (Dq % 128 == 0): codes [rows, Dq] and
   // 1x128 scales [rows, Dq/128] of its bf16 values, as launch_quant_1x128 makes them
   uint8_t* q_codes; float* q_scales;
+  // the same for the normalised latent (L % 128 == 0): codes [rows, L], scales [rows, L/128]
+  uint8_t* kv_codes; float* kv_scales;
 };
 hipError_t launch_qkv_norm(const QkvNormArgs& a, hipStream_t s);
 hipError_t launch_rope_table(float* c, float* sn, int n_pos, float base, hipStream_t s);
@@ -168,6 +170,9 @@ struct PrefillAttnArgs {
   const void* q; const void* kn; const void* vt; const void* kpe;
   const uint32_t* mask; void* out;
   int B, T, Tp, H; float scale; int P;
+  // optional (bf16 kernel): the output as e4m3 codes [B*T, H*128] with one 1x128
+  // scale per (row, head) [B*T, H], quantised from its bf16 values, instead of out
+  uint8_t* oq; float* os;
 };
 // Zeroes the padding keys t in [T, Tp) of kn, vt and kpe (no-op when T == Tp).
 hipError_t launch_zero_kv_padding(void* kn, void* vt, void* kpe, int B, int H, int T, int Tp, int elem_bytes,
