@@ -347,15 +347,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--workloads", default="1,2,3,4,5,6,7,8,9",
-                    help="config indices to run (1 = headline; 5 = shared-expert SwiGLU MLP; "
-                         "6 = chunked prefill after 2048 cached tokens; 7 = decode with e4m3 weights; "
-                         "8 = config 3 in the absorbed gather form; 9 = top-2048 decode over 4000 cached; "
-                         "10 = absorbed vs dense-masked top-k prefill at T = 16384)")
+                    help="1 Kimi-K2 bf16 prefill B1 T2048 (the headline); 2 the same with e4m3 weights, B4 T4096; "
+                         "3 DeepSeek-V3.2-Exp top-2048 prefill T8192 (dense-masked); 4 DeepSeek-V3.2-Exp decode "
+                         "B128, 1000 cached; 5 Kimi-K2 shared-expert SwiGLU MLP over 2048 tokens; 6 workload 1 as "
+                         "a chunk after 2048 cached tokens; 7 workload 4 with e4m3 weights; 8 workload 3 in the "
+                         "absorbed gather form; 9 workload 4 over 4000 cached with a top-2048 selection; 10 the "
+                         "absorbed and dense-masked top-2048 prefill at T16384")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel event breakdown")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md, sharding).",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (one GPU's share of a sharded "
+              "layer is what it runs).", file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"

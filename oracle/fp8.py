@@ -5,7 +5,7 @@ __graft_entry__.py and by bench.py's cpu_baseline leg, never by the library.
 What the pages fix (Kimi K2 "Down projection" page, config.json excerpt in its
 "Code" section, and the "Direct evidence" note under it): weights are stored as
 e4m3 with one scale per 128 x 128 block, and activations use a dynamic scheme.
-The rest is the plainest reading, listed in the design doc:
+The rest is the plainest reading the pages support:
 
 * e4m3fn: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; no infinity;
   S.1111.111 is NaN; largest finite magnitude 448; subnormal step 2^-9.

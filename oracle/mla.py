@@ -21,7 +21,7 @@ Sources (the pages of the model atlas on MLA):
   [DO]  "DeepSeek-V3.2-Exp · Output projection" page (decode, p=1000):
         shapes, "Parameters" table, "Code" section (MLA init excerpt).
 
-Readings where the pages are silent (all listed in the design doc):
+Readings where the pages are silent:
   RMSNorm  y = gamma * x / sqrt(mean(x^2) + eps)      (only the class is named)
   RoPE     rotate-half over the 64 rotary dims: dim d pairs with d+32,
            theta_d = pos * base^(-d/32), base 10000    (no formula on the pages)
