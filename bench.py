@@ -272,24 +272,32 @@ def bench_chunk(steps, warmup, start_pos=2048):
     return res
 
 
-def bench_swiglu(steps, warmup, M=2048, hidden=7168, inter=2048):
+def bench_swiglu(steps, warmup, M=2048, hidden=7168, inter=2048, e4m3=False):
     """Kimi-K2 shared-expert SwiGLU MLP over the prefill's 2048 tokens:
-    out = (silu(x Wg^T) * (x Wu^T)) Wd^T, bf16."""
+    out = (silu(x Wg^T) * (x Wu^T)) Wd^T, bf16 or e4m3 block-scaled weights."""
     import torch
     from head_latent_attention_fwd_amd import api
     g = torch.Generator(device="cuda").manual_seed(5)
     x = torch.randn((M, hidden), generator=g, device="cuda").to(torch.bfloat16)
-    wg = (torch.randn((inter, hidden), generator=g, device="cuda") / hidden ** 0.5).to(torch.bfloat16)
-    wu = (torch.randn((inter, hidden), generator=g, device="cuda") / hidden ** 0.5).to(torch.bfloat16)
-    wd = (torch.randn((hidden, inter), generator=g, device="cuda") / inter ** 0.5).to(torch.bfloat16)
+    wg = torch.randn((inter, hidden), generator=g, device="cuda") / hidden ** 0.5
+    wu = torch.randn((inter, hidden), generator=g, device="cuda") / hidden ** 0.5
+    wd = torch.randn((hidden, inter), generator=g, device="cuda") / inter ** 0.5
     out = torch.empty((M, hidden), device="cuda", dtype=torch.bfloat16)
-    ws = api.workspace(api.lib().mla_swiglu_workspace_size(M, inter))
     flop = 2 * M * hidden * inter * 3
-    sec = wall_steps(lambda: api.mla_swiglu_mlp(x, wg, wu, wd, out=out, ws=ws), steps, warmup)
-    res = {"workload": "kimi_k2_shared_expert_mlp", "M": M, "hidden": hidden, "inter": inter,
-           "ms_per_step": sec * 1e3, "tflops": flop / sec / 1e12, "frac_of_bf16_peak": flop / sec / 1e12 / PEAK["bf16"],
-           "algorithmic_flop": flop}
-    del x, wg, wu, wd, out, ws
+    if e4m3:
+        q = [api.mla_quant_e4m3_block128(w) for w in (wg, wu, wd)]
+        ws = api.workspace(api.lib().mla_swiglu_e4m3_workspace_size(M, hidden, inter))
+        fn = lambda: api.mla_swiglu_mlp_e4m3(x, *q, out=out, ws=ws)
+    else:
+        wg, wu, wd = (w.to(torch.bfloat16) for w in (wg, wu, wd))
+        ws = api.workspace(api.lib().mla_swiglu_workspace_size(M, inter))
+        fn = lambda: api.mla_swiglu_mlp(x, wg, wu, wd, out=out, ws=ws)
+    sec = wall_steps(fn, steps, warmup)
+    peak = PEAK["fp8"] if e4m3 else PEAK["bf16"]
+    res = {"workload": "kimi_k2_shared_expert_mlp" + ("_e4m3" if e4m3 else ""), "M": M, "hidden": hidden,
+           "inter": inter, "ms_per_step": sec * 1e3, "tflops": flop / sec / 1e12,
+           ("frac_of_fp8_peak" if e4m3 else "frac_of_bf16_peak"): flop / sec / 1e12 / peak, "algorithmic_flop": flop}
+    del x, wg, wu, wd, out, ws, fn
     torch.cuda.empty_cache()
     return res
 
@@ -346,13 +354,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
-    ap.add_argument("--workloads", default="1,2,3,4,5,6,7,8,9",
+    ap.add_argument("--workloads", default="1,2,3,4,5,6,7,8,9,11",
                     help="1 Kimi-K2 bf16 prefill B1 T2048 (the headline); 2 the same with e4m3 weights, B4 T4096; "
                          "3 DeepSeek-V3.2-Exp top-2048 prefill T8192 (dense-masked); 4 DeepSeek-V3.2-Exp decode "
                          "B128, 1000 cached; 5 Kimi-K2 shared-expert SwiGLU MLP over 2048 tokens; 6 workload 1 as "
                          "a chunk after 2048 cached tokens; 7 workload 4 with e4m3 weights; 8 workload 3 in the "
                          "absorbed gather form; 9 workload 4 over 4000 cached with a top-2048 selection; 10 the "
-                         "absorbed and dense-masked top-2048 prefill at T16384")
+                         "absorbed and dense-masked top-2048 prefill at T16384; 11 workload 5 with e4m3 weights")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel event breakdown")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -381,6 +389,8 @@ def main():
             results[i] = bench_absorbed(3, args.steps, args.warmup)
         elif i == 9:
             results[i] = bench_decode(4, args.steps, args.warmup, cache_len=4000, topk=2048)
+        elif i == 11:
+            results[i] = bench_swiglu(args.steps, args.warmup, e4m3=True)
         elif i == 10:
             results[i] = bench_absorbed(3, max(1, args.steps // 4), 1, T=16384)
         else:

@@ -66,6 +66,8 @@ _SIGS = {
     "mla_topk_to_bitmask": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
     "mla_swiglu_workspace_size": (sz, [i32, i32]),
     "mla_swiglu_mlp": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+    "mla_swiglu_e4m3_workspace_size": (sz, [i32, i32, i32]),
+    "mla_swiglu_mlp_e4m3": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
 }
 
 _lib = None
@@ -341,4 +343,23 @@ def mla_swiglu_mlp(x, w_gate, w_up, w_down, out=None, ws=None, stream=None):
         ws = workspace(nbytes, x.device)
     _check(lib().mla_swiglu_mlp(_ptr(x), M, hidden, inter, _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out),
                                 _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def mla_swiglu_mlp_e4m3(x, gate, up, down, out=None, ws=None, stream=None):
+    """SwiGLU MLP with e4m3 weights: gate, up, down are (codes uint8, scales fp32) pairs
+    as mla_quant_e4m3_block128 returns them; x, out [M, hidden] bf16."""
+    _need(x, torch.bfloat16, "x")
+    for (c, sc), n in ((gate, "gate"), (up, "up"), (down, "down")):
+        _need(c, torch.uint8, n)
+        _need(sc, torch.float32, n + " scales")
+    M, hidden = x.shape
+    inter = gate[0].shape[0]
+    if out is None:
+        out = torch.empty((M, hidden), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = workspace(lib().mla_swiglu_e4m3_workspace_size(M, hidden, inter), x.device)
+    _check(lib().mla_swiglu_mlp_e4m3(_ptr(x), M, hidden, inter, _ptr(gate[0]), _ptr(gate[1]), _ptr(up[0]),
+                                     _ptr(up[1]), _ptr(down[0]), _ptr(down[1]), _ptr(out), _ptr(ws), ws.numel(),
+                                     _stream(stream)))
     return out

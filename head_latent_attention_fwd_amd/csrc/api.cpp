@@ -941,4 +941,48 @@ int mla_swiglu_mlp(const void* x, int32_t M, int32_t hidden, int32_t inter, cons
   return MLA_OK;
 }
 
+size_t mla_swiglu_e4m3_workspace_size(int32_t M, int32_t hidden, int32_t inter) {
+  if (M <= 0 || hidden <= 0 || inter <= 0) return 0;
+  Carver c(nullptr);
+  c.take((size_t)M * hidden); c.take((size_t)M * (hidden / 128) * 4);   // x codes, scales
+  c.take((size_t)M * inter * 4);                                        // [gate | up] (bf16)
+  c.take((size_t)M * inter); c.take((size_t)M * (inter / 128) * 4);     // h codes, scales
+  return c.off;
+}
+
+int mla_swiglu_mlp_e4m3(const void* x, int32_t M, int32_t hidden, int32_t inter, const void* w_gate,
+                        const float* gate_scale, const void* w_up, const float* up_scale, const void* w_down,
+                        const float* down_scale, void* out, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (!x || !w_gate || !w_up || !w_down || !gate_scale || !up_scale || !down_scale || !out || !ws)
+    return fail(MLA_INVALID_ARG, "NULL pointer");
+  if (M <= 0 || hidden <= 0 || inter <= 0) return fail(MLA_INVALID_ARG, "bad sizes");
+  if (hidden % 128 || inter % 128) return fail(MLA_UNSUPPORTED, "hidden and inter must be multiples of 128");
+  if (((uintptr_t)x | (uintptr_t)w_gate | (uintptr_t)w_up | (uintptr_t)w_down | (uintptr_t)out) & 15)
+    return fail(MLA_UNSUPPORTED, "pointers must be 16-byte aligned");
+  if (ws_bytes < mla_swiglu_e4m3_workspace_size(M, hidden, inter)) return fail(MLA_INVALID_ARG, "workspace too small");
+  if ((uintptr_t)ws & 255) return fail(MLA_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  Carver c(ws);
+  uint8_t* xq = (uint8_t*)c.take((size_t)M * hidden);
+  float* xs = (float*)c.take((size_t)M * (hidden / 128) * 4);
+  uint16_t* gu = (uint16_t*)c.take((size_t)M * inter * 4);
+  uint8_t* hq = (uint8_t*)c.take((size_t)M * inter);
+  float* hs = (float*)c.take((size_t)M * (inter / 128) * 4);
+  // x in dynamic 1x128 groups, then [gate | up] in one product over the stacked weights
+  LAUNCH(mla::launch_quant_1x128(x, hidden, MLA_BF16, M, hidden, xq, xs, s), "quant_e4m3_1x128(x)");
+  mla::GemmFp8Args g{};
+  g.A = xq; g.a_scale = xs; g.W = (const uint8_t*)w_gate; g.w_scale = gate_scale;
+  g.W2 = (const uint8_t*)w_up; g.w2_scale = up_scale; g.n_split = inter;
+  g.C = gu; g.ldc = 2 * inter; g.c_dtype = MLA_BF16; g.M = M; g.N = 2 * inter; g.K = hidden; g.epi = mla::EPI_ROWMAJOR;
+  LAUNCH(mla::launch_gemm_fp8(g, s), "gemm_fp8(gate|up)");
+  // h = silu(gate) * up, rounded to bf16 and quantised for the down projection in one pass
+  LAUNCH(mla::launch_silu_mul_quant(gu, 2 * inter, M, inter, hq, hs, s), "silu_mul_quant");
+  mla::GemmFp8Args d{};
+  d.A = hq; d.a_scale = hs; d.W = (const uint8_t*)w_down; d.w_scale = down_scale; d.n_split = hidden;
+  d.C = out; d.ldc = hidden; d.c_dtype = MLA_BF16; d.M = M; d.N = hidden; d.K = inter; d.epi = mla::EPI_ROWMAJOR;
+  LAUNCH(mla::launch_gemm_fp8(d, s), "gemm_fp8(down)");
+  return MLA_OK;
+}
+
 }  // extern "C"

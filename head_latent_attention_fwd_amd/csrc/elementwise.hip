@@ -289,6 +289,41 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* src, i
   }
 }
 
+// SwiGLU product of a stacked gate | up row and its e4m3 codes: 8 columns per
+// thread, 16 threads per 128-wide group (max over the group by shuffles).
+__global__ __launch_bounds__(256) void silu_mul_quant_kernel(const uint16_t* gu, int64_t ld, int rows, int cols,
+                                                             uint8_t* hq, float* hs) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int cpr = cols / 8;
+  if (i >= (int64_t)rows * cpr) return;   // whole 16-lane groups leave together (cols % 128 == 0)
+  const int64_t r = i / cpr;
+  const int c = (int)(i - r * cpr) * 8;
+  const uint4 gv = *(const uint4*)(gu + r * ld + c), uv = *(const uint4*)(gu + r * ld + cols + c);
+  const uint16_t* ge = (const uint16_t*)&gv;
+  const uint16_t* ue = (const uint16_t*)&uv;
+  float y[8], amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float gf = bf2f(ge[e]);
+    y[e] = bf2f(f2bf(gf / (1.0f + __builtin_amdgcn_exp2f(-gf * 1.4426950408889634f)) * bf2f(ue[e])));
+    amax = fmaxf(amax, fabsf(y[e]));
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  const float sc = amax / 448.0f;
+  uint2 code = make_uint2(0u, 0u);
+  if (sc != 0.f) {
+    code.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2] / sc, y[3] / sc,
+                                                        __builtin_amdgcn_cvt_pk_fp8_f32(y[0] / sc, y[1] / sc, 0, false),
+                                                        true);
+    code.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6] / sc, y[7] / sc,
+                                                        __builtin_amdgcn_cvt_pk_fp8_f32(y[4] / sc, y[5] / sc, 0, false),
+                                                        true);
+  }
+  *(uint2*)(hq + r * cols + c) = code;
+  if ((c & 127) == 0) hs[r * (cols / 128) + c / 128] = sc;
+}
+
 // Strided row copy, one 16-byte chunk per thread.
 __global__ __launch_bounds__(256) void copy_rows_kernel(const uint16_t* src, int64_t sld, uint16_t* dst, int64_t dld,
                                                         int64_t rows, int cpr) {
@@ -496,6 +531,15 @@ hipError_t launch_transpose16(const uint16_t* src, int64_t sld, int64_t sb, uint
   if (rows <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
   dim3 grid((cols + 63) / 64, (rows + 63) / 64, batch);
   transpose16_kernel<<<grid, 256, 0, s>>>(src, sld, sb, dst, dld, db, rows, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_quant(const void* gu, int64_t ld, int rows, int cols, uint8_t* hq, float* hs,
+                                 hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if ((cols & 127) || (ld & 7) || ld < 2 * cols || (((uintptr_t)gu | (uintptr_t)hq) & 15)) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)rows * (cols / 8);
+  silu_mul_quant_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const uint16_t*)gu, ld, rows, cols, hq, hs);
   return hipGetLastError();
 }
 

@@ -150,6 +150,11 @@ hipError_t launch_copy_rows(const uint16_t* src, int64_t sld, uint16_t* dst, int
 // strides sld / dld, batch strides sb / db.
 hipError_t launch_transpose16(const uint16_t* src, int64_t sld, int64_t sb, uint16_t* dst, int64_t dld, int64_t db,
                               int rows, int cols, int batch, hipStream_t s);
+// Row r of gu [rows, ld] holds gate in columns [0, cols) and up in [cols, 2 cols):
+// h = bf16(silu(gate) * up), quantised in 1x128 groups to codes hq [rows, cols]
+// and scales hs [rows, cols/128] (cols % 128 == 0, ld % 8 == 0, 16-byte aligned).
+hipError_t launch_silu_mul_quant(const void* gu, int64_t ld, int rows, int cols, uint8_t* hq, float* hs,
+                                 hipStream_t s);
 // h[i] = silu(g[i]) * u[i] over n bf16 values (n % 8 == 0, 16-byte aligned).
 hipError_t launch_silu_mul(const void* g, const void* u, void* h, int64_t n, hipStream_t s);
 // mask [B, T, ceil(Tk/32)]: bit t of row (b, s) is set iff t appears in

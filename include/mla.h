@@ -325,6 +325,22 @@ MLA_API size_t mla_swiglu_workspace_size(int32_t M, int32_t inter);
 MLA_API int mla_swiglu_mlp(const void* x, int32_t M, int32_t hidden, int32_t inter, const void* w_gate,
                    const void* w_up, const void* w_down, void* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of workspace mla_swiglu_mlp_e4m3 needs (0 on invalid input). */
+MLA_API size_t mla_swiglu_e4m3_workspace_size(int32_t M, int32_t hidden, int32_t inter);
+
+/* The shared-expert SwiGLU MLP with e4m3 weights in the checkpoint's format
+ * (Kimi K2 · Down projection, quantization_config: e4m3, dynamic activation
+ * scheme, 128x128 weight blocks): every Linear quantises its bf16 input in
+ * dynamic 1x128 groups and runs the block-scaled e4m3 product.
+ *   w_gate, w_up [inter, hidden] e4m3 codes with scales [inter/128, hidden/128]
+ *   fp32; w_down [hidden, inter] codes with scales [hidden/128, inter/128];
+ *   x, out [M, hidden] bf16; hidden and inter multiples of 128. The gate and up
+ *   products and h are rounded to bf16, as in mla_swiglu_mlp. */
+MLA_API int mla_swiglu_mlp_e4m3(const void* x, int32_t M, int32_t hidden, int32_t inter, const void* w_gate,
+                        const float* gate_scale, const void* w_up, const float* up_scale,
+                        const void* w_down, const float* down_scale, void* out, void* ws, size_t ws_bytes,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -369,7 +369,14 @@ def rmsnorm_rope_rows(inp, norm_dim, gamma, eps, rope_off, rope_heads, rope_stri
     return out
 
 
-def swiglu_mlp(x, wg, wu, wd):
-    """Shared-expert SwiGLU MLP ([DN] "Direct evidence": down(silu(gate x) * up x))."""
-    g = linear(x, wg)
-    return linear((g / (1.0 + np.exp(-g))) * linear(x, wu), wd)
+def swiglu_mlp(x, wg, wu, wd, fp8=False):
+    """Shared-expert SwiGLU MLP ([DN] "Direct evidence": down(silu(gate x) * up x)).
+    With fp8=True the weights are fp32 masters, block-quantised here, and every
+    Linear is the e4m3 block-scaled product of [DN] quantization_config."""
+    if not fp8:
+        g = linear(x, wg)
+        return linear((g / (1.0 + np.exp(-g))) * linear(x, wu), wd)
+    from .fp8 import linear_fp8, quant_weight_block128
+    g = linear_fp8(x, *quant_weight_block128(wg))
+    h = (g / (1.0 + np.exp(-g))) * linear_fp8(x, *quant_weight_block128(wu))
+    return linear_fp8(h, *quant_weight_block128(wd))

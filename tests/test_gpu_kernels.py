@@ -6,7 +6,7 @@ import torch
 from head_latent_attention_fwd_amd import api, synth
 from oracle import fp8, mask, mla
 
-from helpers import BF16_TOL, F32_TOL, assert_parity
+from helpers import BF16_TOL, F32_TOL, FP8_TOL, assert_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -251,3 +251,20 @@ def test_swiglu_mlp_kimi_k2_shared_expert_sampled_rows():
     f64 = lambda t: t.double().cpu().numpy()
     ref = mla.swiglu_mlp(f64(X[rows]), f64(Wg), f64(Wu), f64(Wd))
     assert_parity(out[rows].float().cpu().numpy(), ref, what="swiglu Kimi-K2 shared expert")
+
+
+
+@pytest.mark.parametrize("M,hidden,inter", [(300, 1024, 512), (2048, 7168, 2048)])
+def test_swiglu_mlp_e4m3(M, hidden, inter):
+    # e4m3 weights quantised on the device from fp32 masters; the full Kimi-K2
+    # shared-expert size is compared on sampled rows (rows are independent)
+    rng = np.random.default_rng(M + 5)
+    x = synth.round_bf16(rng.standard_normal((M, hidden)))
+    wg = (rng.standard_normal((inter, hidden)) / np.sqrt(hidden)).astype(np.float32)
+    wu = (rng.standard_normal((inter, hidden)) / np.sqrt(hidden)).astype(np.float32)
+    wd = (rng.standard_normal((hidden, inter)) / np.sqrt(inter)).astype(np.float32)
+    q = [api.mla_quant_e4m3_block128(dev(w, torch.float32)) for w in (wg, wu, wd)]
+    out = api.mla_swiglu_mlp_e4m3(dev(x, torch.bfloat16), *q)
+    rows = np.arange(M) if M <= 512 else np.array([0, 1, 255, 256, 1023, 2047])
+    ref = mla.swiglu_mlp(x[rows], wg, wu, wd, fp8=True)
+    assert_parity(out.float().cpu().numpy()[rows], ref, tol=FP8_TOL, cos=0.999, what=f"swiglu e4m3 {M}")

@@ -493,3 +493,23 @@ def test_swiglu_oracle_closed_form():
     I = np.eye(3)
     d = mla.swiglu_mlp(z, I, I, I) - mla.swiglu_mlp(-z, I, I, -I)
     np.testing.assert_allclose(d, z * z, rtol=1e-14)
+
+
+
+def test_swiglu_fp8_tracks_the_exact_mlp():
+    """e4m3 SwiGLU stays within fp8 rounding of the exact MLP when every
+    128 x 128 weight block carries its own power-of-two scale; a scale taken
+    from the wrong block would miss by far more."""
+    rng = np.random.default_rng(91)
+    M, hidden, inter = 8, 256, 384
+    x = synth.round_bf16(rng.standard_normal((M, hidden)))
+    def blocky(n, k):
+        w = rng.standard_normal((n, k)) / np.sqrt(k)
+        f = 2.0 ** rng.integers(-3, 4, size=(n // 128, k // 128))
+        return (w * np.repeat(np.repeat(f, 128, 0), 128, 1)).astype(np.float32)
+    wg, wu, wd = blocky(inter, hidden), blocky(inter, hidden), blocky(hidden, inter)
+    exact = mla.swiglu_mlp(x, wg, wu, wd)
+    got = mla.swiglu_mlp(x, wg, wu, wd, fp8=True)
+    err = np.abs(got - exact).max() / np.abs(exact).max()
+    cos = (got * exact).sum() / np.linalg.norm(got) / np.linalg.norm(exact)
+    assert err < 0.15 and cos > 0.995, (err, cos)
