@@ -610,11 +610,11 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
     a.qlat = p.qlat; a.cache = kv_cache; a.cache_len = cache_len; a.olat = p.olat;
     a.B = B; a.H = H; a.max_len = max_len; a.scale = d->softmax_scale;
     a.idx = topk_idx; a.topk = topk;
+    if (fp8) { a.oq = aq; a.os = as; }   // o_lat leaves as W_UV's e4m3 input
     LAUNCH(mla::launch_decode_attn(a, s), "decode_attn");
   }
   // o[b, h] = W_UV_h . o_lat[b, h]  (W_UV_h = Wkv_b rows [256h+128, 256h+256)), per head
-  if (fp8) {   // o_lat quantised per (b, h) row in 4 groups; W_UV_h = block row 2h + 1 of the scales
-    if ((rc = quant(p.olat, L, B * H, L))) return rc;
+  if (fp8) {   // o_lat codes per (b, h) row in 4 groups; W_UV_h = block row 2h + 1 of the scales
     if ((rc = skinny_fp8(aq, (int64_t)H * L, L, as, (int64_t)H * (L / 128), L / 128,
                          (const uint8_t*)w->wkv_b + 128 * (int64_t)L, L, 256 * (int64_t)L, w->wkv_b_scale + L / 128,
                          L / 128, 2 * (L / 128), nullptr, 0, nullptr, 128, nullptr, H * 128, 128, nullptr, B, 128, L,

@@ -324,6 +324,38 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(DecodeAttnArgs a, i
   // o_lat[b, head, 256 dh + 32 dt + 8 rg + 4 hi + 0..3]
   l += __shfl_xor(l, 32);
   const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (a.oq) {
+    // e4m3 output: dims [256 dh + 128 g2, +128) are one group, held by this
+    // lane (dt = 4 g2 .. 4 g2 + 3) and lane ^ 32
+    const int64_t row = (int64_t)q * a.H + head;
+#pragma unroll
+    for (int g2 = 0; g2 < 2; ++g2) {
+      float amax = 0.f;
+#pragma unroll
+      for (int dt = 4 * g2; dt < 4 * g2 + 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          o[dt][r] = __uint_as_float((uint32_t)f2bf(o[dt][r] * inv) << 16);
+          amax = fmaxf(amax, fabsf(o[dt][r]));
+        }
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      const float sc = amax / 448.0f;
+      uint8_t* oq = a.oq + row * 512 + 256 * c.dh + 4 * c.hi;
+#pragma unroll
+      for (int dt = 4 * g2; dt < 4 * g2 + 4; ++dt)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const float v0 = o[dt][4 * rg], v1 = o[dt][4 * rg + 1], v2 = o[dt][4 * rg + 2], v3 = o[dt][4 * rg + 3];
+          uint32_t code = 0u;
+          if (sc != 0.f)
+            code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+                v2 / sc, v3 / sc, __builtin_amdgcn_cvt_pk_fp8_f32(v0 / sc, v1 / sc, 0, false), true);
+          *(uint32_t*)(oq + 32 * dt + 8 * rg) = code;
+        }
+      if (c.hi == 0) a.os[row * 4 + 2 * c.dh + g2] = sc;
+    }
+    return;
+  }
   uint16_t* out = (uint16_t*)a.olat + ((int64_t)q * a.H + head) * 512 + 256 * c.dh + 4 * c.hi;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)

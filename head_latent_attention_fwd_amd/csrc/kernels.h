@@ -199,6 +199,9 @@ struct DecodeAttnArgs {
   // its last key that position (prefill); else row q is sequence q with last
   // key cache_len[q] (decode).
   const int32_t* idx; int topk; int rows_per_seq;
+  // optional: o_lat as e4m3 codes [B*H, 512] with 1x128 scales [B*H, 4],
+  // quantised from its bf16 values, instead of olat
+  uint8_t* oq; float* os;
 };
 constexpr int DECODE_TOPK_MAX = 2048;
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s);
