@@ -941,11 +941,14 @@ int mla_swiglu_mlp(const void* x, int32_t M, int32_t hidden, int32_t inter, cons
   return MLA_OK;
 }
 
+// split-K chunks of the e4m3 gate|up product when it has few output tiles
+constexpr int SWIGLU_FP8_SPLITS = 2;
+
 size_t mla_swiglu_e4m3_workspace_size(int32_t M, int32_t hidden, int32_t inter) {
   if (M <= 0 || hidden <= 0 || inter <= 0) return 0;
   Carver c(nullptr);
   c.take((size_t)M * hidden); c.take((size_t)M * (hidden / 128) * 4);   // x codes, scales
-  c.take((size_t)M * inter * 4);                                        // [gate | up] (bf16)
+  c.take((size_t)SWIGLU_FP8_SPLITS * M * inter * 8);                    // [gate | up] fp32 partials
   c.take((size_t)M * inter); c.take((size_t)M * (inter / 128) * 4);     // h codes, scales
   return c.off;
 }
@@ -966,7 +969,7 @@ int mla_swiglu_mlp_e4m3(const void* x, int32_t M, int32_t hidden, int32_t inter,
   Carver c(ws);
   uint8_t* xq = (uint8_t*)c.take((size_t)M * hidden);
   float* xs = (float*)c.take((size_t)M * (hidden / 128) * 4);
-  uint16_t* gu = (uint16_t*)c.take((size_t)M * inter * 4);
+  float* gu = (float*)c.take((size_t)SWIGLU_FP8_SPLITS * M * inter * 8);
   uint8_t* hq = (uint8_t*)c.take((size_t)M * inter);
   float* hs = (float*)c.take((size_t)M * (inter / 128) * 4);
   // x in dynamic 1x128 groups, then [gate | up] in one product over the stacked weights
@@ -974,10 +977,19 @@ int mla_swiglu_mlp_e4m3(const void* x, int32_t M, int32_t hidden, int32_t inter,
   mla::GemmFp8Args g{};
   g.A = xq; g.a_scale = xs; g.W = (const uint8_t*)w_gate; g.w_scale = gate_scale;
   g.W2 = (const uint8_t*)w_up; g.w2_scale = up_scale; g.n_split = inter;
-  g.C = gu; g.ldc = 2 * inter; g.c_dtype = MLA_BF16; g.M = M; g.N = 2 * inter; g.K = hidden; g.epi = mla::EPI_ROWMAJOR;
+  g.C = gu; g.ldc = 2 * inter; g.c_dtype = MLA_F32; g.M = M; g.N = 2 * inter; g.K = hidden; g.epi = mla::EPI_ROWMAJOR;
+  // split-K when the output has too few 256 x 256 tiles for the chip (fp32 partials)
+  const int tiles = ((M + 255) / 256) * ((2 * inter + 255) / 256);
+  const int groups = hidden / 128;
+  int splits = (tiles >= 192 || M < 256) ? 1 : SWIGLU_FP8_SPLITS;   // the big-tile path takes split-K
+  if (splits > groups) splits = groups;
+  const int per = (groups + splits - 1) / splits;
+  if ((groups + per - 1) / per != splits) splits = 1;                // every chunk non-empty
+  g.k_splits = splits; g.split_stride = (int64_t)M * 2 * inter;
   LAUNCH(mla::launch_gemm_fp8(g, s), "gemm_fp8(gate|up)");
   // h = silu(gate) * up, rounded to bf16 and quantised for the down projection in one pass
-  LAUNCH(mla::launch_silu_mul_quant(gu, 2 * inter, M, inter, hq, hs, s), "silu_mul_quant");
+  LAUNCH(mla::launch_silu_mul_quant(gu, 2 * inter, splits, (int64_t)M * 2 * inter, M, inter, hq, hs, s),
+         "silu_mul_quant");
   mla::GemmFp8Args d{};
   d.A = hq; d.a_scale = hs; d.W = (const uint8_t*)w_down; d.w_scale = down_scale; d.n_split = hidden;
   d.C = out; d.ldc = hidden; d.c_dtype = MLA_BF16; d.M = M; d.N = hidden; d.K = inter; d.epi = mla::EPI_ROWMAJOR;

@@ -291,21 +291,42 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* src, i
 
 // SwiGLU product of a stacked gate | up row and its e4m3 codes: 8 columns per
 // thread, 16 threads per 128-wide group (max over the group by shuffles).
-__global__ __launch_bounds__(256) void silu_mul_quant_kernel(const uint16_t* gu, int64_t ld, int rows, int cols,
-                                                             uint8_t* hq, float* hs) {
+__global__ __launch_bounds__(256) void silu_mul_quant_kernel(const void* gu, int64_t ld, int nsplit,
+                                                             int64_t split_stride, int rows, int cols, uint8_t* hq,
+                                                             float* hs) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int cpr = cols / 8;
   if (i >= (int64_t)rows * cpr) return;   // whole 16-lane groups leave together (cols % 128 == 0)
   const int64_t r = i / cpr;
   const int c = (int)(i - r * cpr) * 8;
-  const uint4 gv = *(const uint4*)(gu + r * ld + c), uv = *(const uint4*)(gu + r * ld + cols + c);
-  const uint16_t* ge = (const uint16_t*)&gv;
-  const uint16_t* ue = (const uint16_t*)&uv;
+  float gf[8], uf[8];
+  if (nsplit > 0) {   // fp32 partials, summed in split order (gate and up products rounded to bf16)
+    const float* p = (const float*)gu + r * ld + c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { gf[e] = 0.f; uf[e] = 0.f; }
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float4 g0 = *(const float4*)(p + sp * split_stride), g1 = *(const float4*)(p + sp * split_stride + 4);
+      const float4 u0 = *(const float4*)(p + sp * split_stride + cols);
+      const float4 u1 = *(const float4*)(p + sp * split_stride + cols + 4);
+      gf[0] += g0.x; gf[1] += g0.y; gf[2] += g0.z; gf[3] += g0.w; gf[4] += g1.x; gf[5] += g1.y; gf[6] += g1.z;
+      gf[7] += g1.w;
+      uf[0] += u0.x; uf[1] += u0.y; uf[2] += u0.z; uf[3] += u0.w; uf[4] += u1.x; uf[5] += u1.y; uf[6] += u1.z;
+      uf[7] += u1.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { gf[e] = bf2f(f2bf(gf[e])); uf[e] = bf2f(f2bf(uf[e])); }
+  } else {
+    const uint16_t* b = (const uint16_t*)gu + r * ld + c;
+    const uint4 gv = *(const uint4*)b, uv = *(const uint4*)(b + cols);
+    const uint16_t* ge = (const uint16_t*)&gv;
+    const uint16_t* ue = (const uint16_t*)&uv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { gf[e] = bf2f(ge[e]); uf[e] = bf2f(ue[e]); }
+  }
   float y[8], amax = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float gf = bf2f(ge[e]);
-    y[e] = bf2f(f2bf(gf / (1.0f + __builtin_amdgcn_exp2f(-gf * 1.4426950408889634f)) * bf2f(ue[e])));
+    y[e] = bf2f(f2bf(gf[e] / (1.0f + __builtin_amdgcn_exp2f(-gf[e] * 1.4426950408889634f)) * uf[e]));
     amax = fmaxf(amax, fabsf(y[e]));
   }
 #pragma unroll
@@ -534,12 +555,15 @@ hipError_t launch_transpose16(const uint16_t* src, int64_t sld, int64_t sb, uint
   return hipGetLastError();
 }
 
-hipError_t launch_silu_mul_quant(const void* gu, int64_t ld, int rows, int cols, uint8_t* hq, float* hs,
-                                 hipStream_t s) {
+hipError_t launch_silu_mul_quant(const void* gu, int64_t ld, int nsplit, int64_t split_stride, int rows, int cols,
+                                 uint8_t* hq, float* hs, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if ((cols & 127) || (ld & 7) || ld < 2 * cols || (((uintptr_t)gu | (uintptr_t)hq) & 15)) return hipErrorInvalidValue;
+  if ((cols & 127) || (ld & 7) || ld < 2 * cols || (split_stride & 3) || nsplit < 0 ||
+      (((uintptr_t)gu | (uintptr_t)hq) & 15))
+    return hipErrorInvalidValue;
   const int64_t n = (int64_t)rows * (cols / 8);
-  silu_mul_quant_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const uint16_t*)gu, ld, rows, cols, hq, hs);
+  silu_mul_quant_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(gu, ld, nsplit, split_stride, rows, cols, hq,
+                                                                    hs);
   return hipGetLastError();
 }
 

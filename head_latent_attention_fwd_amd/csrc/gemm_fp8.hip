@@ -200,7 +200,10 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
   const int span = FB_GROUP_M * tiles_n, grp = t / span, first_m = grp * FB_GROUP_M;
   const int gsz = min(tiles_m - first_m, FB_GROUP_M), r_in = t - grp * span;
   const int m0 = (first_m + r_in % gsz) * 256, tn = r_in / gsz;
-  const int M = g.M, N = g.N, K = g.K, KG = K / 128;
+  const int M = g.M, N = g.N, K = g.K;
+  // K groups [kg0, KG) of this workgroup's split (all of them without split-K)
+  const int ns = max(g.k_splits, 1), per = (K / 128 + ns - 1) / ns, split = blockIdx.y;
+  const int kg0 = split * per, KG = min(K / 128, kg0 + per);
   const int nsp = g.W2 ? g.n_split : N, t1 = (nsp + 255) / 256;
   const bool second = tn >= t1;
   const int nbase = second ? nsp : 0;                          // first row of this tile's weight matrix
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
   const float* wsc = second ? g.w2_scale : g.w_scale;
   const int nblocks = (nend - nbase + 127) / 128;
   const int wblk = min((n0 - nbase) / 128 + wn, nblocks - 1);
-  const float* wsrow = wsc + (int64_t)wblk * KG;
+  const float* wsrow = wsc + (int64_t)wblk * (K / 128);   // scale rows hold every K group
 
   const __amdgpu_buffer_rsrc_t rsA =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (int)((int64_t)M * K), BUF_DW3);
@@ -232,8 +235,8 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
   };
 
   // activation scales of the lane's two output rows
-  const float* as0 = g.a_scale + (int64_t)min(m0 + wm * 64 + l32, M - 1) * KG;
-  const float* as1 = g.a_scale + (int64_t)min(m0 + wm * 64 + 32 + l32, M - 1) * KG;
+  const float* as0 = g.a_scale + (int64_t)min(m0 + wm * 64 + l32, M - 1) * (K / 128);
+  const float* as1 = g.a_scale + (int64_t)min(m0 + wm * 64 + 32 + l32, M - 1) * (K / 128);
 
   floatx16 acc[2][4];
 #pragma unroll
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
   };
   const int ra = wm * 64 + l32, rw = 256 + wn * 128 + l32;
 
-  float sa0 = as0[0], sa1 = as1[0], sw = wsrow[0];
+  float sa0 = as0[kg0], sa1 = as1[kg0], sw = wsrow[kg0];
   auto step = [&](const uint8_t* cur, uint8_t* refill, int kg) {
     // promotion: keep the sum in units of this group's scale
     const float n0s = sa0 * sw, n1s = sa1 * sw;
@@ -295,12 +298,12 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
     issue(refill, min(kg + 2, KG - 1));
   };
 
-  issue(s0, 0);
-  issue(s1, min(1, KG - 1));
+  issue(s0, kg0);
+  issue(s1, min(kg0 + 1, KG - 1));
   __builtin_amdgcn_s_waitcnt(fb_wait(8, 15));   // group 0 has landed
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
-  int kg = 0;
+  int kg = kg0;
   for (; kg + 1 < KG; kg += 2) {
     step(s0, s0, kg);
     step(s1, s1, kg + 1);
@@ -312,7 +315,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
   if (g.c_dtype == DT_F32) {
     // fp32 row-major output straight from the accumulators: a lane holds 4
     // consecutive columns of one row per result group
-    float* Cf = (float*)g.C;
+    float* Cf = (float*)g.C + (int64_t)split * g.split_stride;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const float sr = i ? srun1 : srun0;
@@ -445,11 +448,15 @@ bool gemm_fp8_qrope_ok(const GemmFp8Args& g) {
 
 hipError_t launch_gemm_fp8(const GemmFp8Args& g, hipStream_t s) {
   if (g.epi == EPI_QROPE && !gemm_fp8_qrope_ok(g)) return hipErrorInvalidValue;
+  if (g.k_splits > 1 && (!fp8_big_ok(g) || g.c_dtype != DT_F32 || g.epi != EPI_ROWMAJOR ||
+                         fb_cdiv(g.K / 128, fb_cdiv(g.K / 128, g.k_splits)) != g.k_splits ||   // no empty chunk
+                         g.split_stride < (int64_t)(g.M - 1) * g.ldc + g.N))
+    return hipErrorInvalidValue;
   if (fp8_big_ok(g)) {
     const int nsp = g.W2 ? g.n_split : g.N;
     const int tm = fb_cdiv(g.M, 256), tn = g.W2 ? fb_cdiv(nsp, 256) + fb_cdiv(g.N - nsp, 256) : fb_cdiv(g.N, 256);
     const int per_xcd = fb_cdiv(tm * tn, 8);
-    gemm_fp8_big_kernel<<<8 * per_xcd, 512, 0, s>>>(g, tm, tn, per_xcd);
+    gemm_fp8_big_kernel<<<dim3(8 * per_xcd, g.k_splits > 1 ? g.k_splits : 1), 512, 0, s>>>(g, tm, tn, per_xcd);
     return hipGetLastError();
   }
   dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, 1);

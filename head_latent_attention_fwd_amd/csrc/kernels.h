@@ -63,6 +63,9 @@ struct GemmFp8Args {
   void* C; int64_t ldc; int c_dtype;
   int M, N, K;
   int epi; KvSplit kv; RopeEpi rope;
+  // split-K (256x256 path, fp32 row-major output): chunk s of the 128-wide K
+  // groups writes its partial sums to (float*)C + s * split_stride
+  int k_splits; int64_t split_stride;
 };
 hipError_t launch_gemm_fp8(const GemmFp8Args& g, hipStream_t s);
 // whether launch_gemm_fp8 takes g with epi = EPI_QROPE
@@ -150,11 +153,13 @@ hipError_t launch_copy_rows(const uint16_t* src, int64_t sld, uint16_t* dst, int
 // strides sld / dld, batch strides sb / db.
 hipError_t launch_transpose16(const uint16_t* src, int64_t sld, int64_t sb, uint16_t* dst, int64_t dld, int64_t db,
                               int rows, int cols, int batch, hipStream_t s);
-// Row r of gu [rows, ld] holds gate in columns [0, cols) and up in [cols, 2 cols):
-// h = bf16(silu(gate) * up), quantised in 1x128 groups to codes hq [rows, cols]
-// and scales hs [rows, cols/128] (cols % 128 == 0, ld % 8 == 0, 16-byte aligned).
-hipError_t launch_silu_mul_quant(const void* gu, int64_t ld, int rows, int cols, uint8_t* hq, float* hs,
-                                 hipStream_t s);
+// Row r of gu [rows, ld] holds gate in columns [0, cols) and up in [cols, 2 cols)
+// (bf16, or with nsplit > 0 the fp32 split-K partials gu + s*split_stride,
+// summed in split order): h = bf16(silu(gate) * up), quantised in 1x128 groups
+// to codes hq [rows, cols] and scales hs [rows, cols/128] (cols % 128 == 0,
+// ld % 8 == 0, 16-byte aligned).
+hipError_t launch_silu_mul_quant(const void* gu, int64_t ld, int nsplit, int64_t split_stride, int rows, int cols,
+                                 uint8_t* hq, float* hs, hipStream_t s);
 // h[i] = silu(g[i]) * u[i] over n bf16 values (n % 8 == 0, 16-byte aligned).
 hipError_t launch_silu_mul(const void* g, const void* u, void* h, int64_t n, hipStream_t s);
 // mask [B, T, ceil(Tk/32)]: bit t of row (b, s) is set iff t appears in
