@@ -356,3 +356,28 @@ def test_decode_graph_replay_matches_eager():
         run.run()                        # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(run.out, eager)
+
+
+def test_one_token_chunk_matches_decode_on_the_gpu():
+    """A one-token chunk after P cached tokens and the decode step for the same
+    token go through different kernels (dense prefill attention vs the latent
+    decode attention) and must agree with each other and the oracle."""
+    cfg = dict(name="chunk1", mode="prefill", B=3, T=1, dim=1024, q_lora_rank=256, kv_lora_rank=512, n_heads=64,
+               act="bf16", weight="bf16", topk=0, cache_len=150)
+    P, max_len = 150, 160
+    inp = synth.gen_chunk(cfg, 79, P, max_len)
+    chunk = runner.PrefillCached(cfg, inp, P)
+    chunk.run()
+    dec_inp = dict(x=inp["x"][:, 0], w=inp["w"], cache=inp["cache"], cache_len=np.full(3, P, dtype=np.int32))
+    dec = runner.Decode(dict(cfg, mode="decode"), dec_inp)
+    dec.run()
+    torch.cuda.synchronize()
+    a = chunk.out[:, 0].float().cpu().numpy()
+    b = dec.out.float().cpu().numpy()
+    d = oracle_dims(cfg)
+    ref, _ = mla.mla_decode(inp["x"][:, 0], inp["w"], d, inp["cache"], np.full(3, P))
+    assert_parity(a, ref, what="one-token chunk")
+    assert_parity(b, ref, what="decode")
+    assert_parity(a, b, what="chunk vs decode")
+    # both wrote the same cache entry at slot P
+    assert_parity(chunk.cache[:, P].float().cpu().numpy(), dec.cache[:, P].float().cpu().numpy(), what="entry")
