@@ -381,3 +381,30 @@ def test_one_token_chunk_matches_decode_on_the_gpu():
     assert_parity(a, b, what="chunk vs decode")
     # both wrote the same cache entry at slot P
     assert_parity(chunk.cache[:, P].float().cpu().numpy(), dec.cache[:, P].float().cpu().numpy(), what="entry")
+
+
+def test_prefill_graph_replay_matches_eager():
+    """The whole prefill (top-k, bf16) captured in a HIP graph and replayed with
+    eager work in between reproduces the eager output exactly."""
+    cfg = small_cfg(T=150, B=2, topk=20, n_heads=4)
+    inp = synth.gen_prefill(cfg, 80)
+    run = runner.Prefill(cfg, inp)
+    run.run()
+    torch.cuda.synchronize()
+    eager, eager_cache = run.out.clone(), run.kv_cache.clone()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        run.run(stream=stream)
+        stream.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            run.run(stream=stream)
+    for i in range(3):
+        run.out.zero_()
+        run.kv_cache.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(run.out, eager) and torch.equal(run.kv_cache, eager_cache), f"replay {i}"
+        run.run()
+        torch.cuda.synchronize()
