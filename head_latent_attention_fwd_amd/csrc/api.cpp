@@ -140,14 +140,30 @@ struct DecodeWs {
   void *oq, *os;   // e4m3 weights: o quantised by the W_UV product for wo
 };
 
-// split-K factors of the two decode projections with long K
-constexpr int DEC_SPLIT_QKV = 8, DEC_SPLIT_WO = 4;
+// Decode projections (M = batch rows): column tile widths and split-K. One
+// workgroup per CU fills the chip, and a launch of more than 256 makes a
+// second, mostly idle round, so a long-K product takes the largest number of
+// K chunks (at most 8) that keeps tiles x chunks <= 256. Measured in the
+// DeepSeek-V3.2-Exp decode step at B = 128 (same box, alternating runs):
+// q_a|kv_a in 33 x 7 workgroups and q_b in 256 tiles of 96 columns took the
+// step from 224 to 216 us (from 33 x 8 and 192 tiles of 128); wo in 32 x 8
+// tiles of 224 columns was slower in the step (223 us) than 56 x 4 of 128
+// although faster alone.
+constexpr int DEC_CUS = 256, DEC_MAX_CHUNKS = 8;
+constexpr int DEC_NT_QKV = 64, DEC_NT_QB = 96, DEC_NT_WO = 128, DEC_NT_FP8 = 128;
+int dec_chunks(int N, int nt) {
+  const int tiles = (N + nt - 1) / nt;
+  const int c = DEC_CUS / tiles;
+  return c < 1 ? 1 : c > DEC_MAX_CHUNKS ? DEC_MAX_CHUNKS : c;
+}
 
 size_t decode_layout(const mla_dims* d, int wdt, int B, void* ws, DecodeWs* out) {
   const size_t H = d->n_heads, Dq = d->q_lora_rank, L = d->kv_lora_rank;
   Carver c(ws);
   DecodeWs p{};
-  const size_t part_qkv = (size_t)DEC_SPLIT_QKV * B * (Dq + L + 64), part_wo = (size_t)DEC_SPLIT_WO * B * d->dim;
+  const int nqkv = (int)(Dq + L + 64);
+  const size_t part_qkv = (size_t)dec_chunks(nqkv, DEC_NT_QKV) * B * nqkv,
+               part_wo = (size_t)dec_chunks(d->dim, DEC_NT_WO) * B * d->dim;
   p.part = c.take((part_qkv > part_wo ? part_qkv : part_wo) * 4);
   p.cqn = c.take((size_t)B * Dq * 2);
   p.q = c.take((size_t)B * H * 192 * 2);
@@ -572,14 +588,15 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
   if (fp8) {
     if ((rc = quant(x, dim, B, dim))) return rc;
     if ((rc = skinny_fp8(aq, dim, 0, as, dim / 128, 0, w->wq_a, dim, 0, w->wq_a_scale, dim / 128, 0, w->wkv_a, dim,
-                         w->wkv_a_scale, Dq, nullptr, 0, 0, part, B, NQKV, dim, 1, 64, DEC_SPLIT_QKV, s)))
+                         w->wkv_a_scale, Dq, nullptr, 0, 0, part, B, NQKV, dim, 1, DEC_NT_QKV,
+                         dec_chunks(NQKV, DEC_NT_QKV), s)))
       return rc;
-    splits_qkv = skinny_fp8_splits(dim, DEC_SPLIT_QKV);
+    splits_qkv = skinny_fp8_splits(dim, dec_chunks(NQKV, DEC_NT_QKV));
   } else {
-    if ((rc = skinny(x, dim, 0, w->wq_a, dim, 0, w->wkv_a, dim, Dq, nullptr, 0, 0, part, B, NQKV, dim, 1, 64,
-                     DEC_SPLIT_QKV, s)))
+    if ((rc = skinny(x, dim, 0, w->wq_a, dim, 0, w->wkv_a, dim, Dq, nullptr, 0, 0, part, B, NQKV, dim, 1, DEC_NT_QKV,
+                     dec_chunks(NQKV, DEC_NT_QKV), s)))
       return rc;
-    splits_qkv = skinny_splits(dim, DEC_SPLIT_QKV);
+    splits_qkv = skinny_splits(dim, dec_chunks(NQKV, DEC_NT_QKV));
   }
   {  // q_norm, kv_norm and RoPE of k_pe; the new [latent | k_pe] lands directly in cache row cache_len[b]
     mla::QkvNormArgs a{};
@@ -598,7 +615,7 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
                          H * 192, p.q, H * 192, 0, nullptr, B, H * 192, Dq, 1, 128, 1, s)))
       return rc;
   } else if ((rc = skinny(p.cqn, Dq, 0, w->wq_b, Dq, 0, nullptr, 0, H * 192, p.q, H * 192, 0, nullptr, B, H * 192, Dq,
-                          1, 128, 1, s))) {
+                          1, DEC_NT_QB, 1, s))) {
     return rc;
   }
   // q_lat[b, h] = [q_nope[b, h] . W_UK_h | RoPE(q_pe[b, h])]  (W_UK_h = Wkv_b rows [256h, 256h+128))
@@ -628,14 +645,14 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
   int splits_wo;
   if (fp8) {
     if ((rc = skinny_fp8(p.oq, H * 128, 0, (const float*)p.os, H, 0, w->wo, H * 128, 0, w->wo_scale, H, 0, nullptr, 0, nullptr, dim,
-                         nullptr, 0, 0, part, B, dim, H * 128, 1, 128, DEC_SPLIT_WO, s)))
+                         nullptr, 0, 0, part, B, dim, H * 128, 1, DEC_NT_FP8, dec_chunks(dim, DEC_NT_FP8), s)))
       return rc;
-    splits_wo = skinny_fp8_splits(H * 128, DEC_SPLIT_WO);
+    splits_wo = skinny_fp8_splits(H * 128, dec_chunks(dim, DEC_NT_FP8));
   } else {
     if ((rc = skinny(p.o, H * 128, 0, w->wo, H * 128, 0, nullptr, 0, dim, nullptr, 0, 0, part, B, dim, H * 128, 1,
-                     128, DEC_SPLIT_WO, s)))
+                     DEC_NT_WO, dec_chunks(dim, DEC_NT_WO), s)))
       return rc;
-    splits_wo = skinny_splits(H * 128, DEC_SPLIT_WO);
+    splits_wo = skinny_splits(H * 128, dec_chunks(dim, DEC_NT_WO));
   }
   LAUNCH(mla::launch_splitk_reduce(part, splits_wo, B, dim, out, dim, s), "splitk_reduce(wo)");
   return MLA_OK;

@@ -1,9 +1,9 @@
 // Skinny bf16 GEMM for the decode step (M = batch <= 128 rows): C = A . W^T,
 // bound by streaming W from HBM. One workgroup owns all M rows, NT columns of
 // W and one K chunk (split-K over gridDim.y); every byte of W is read once and
-// the small A chunk is re-read from L2. K moves in 64-wide steps through a
-// 4-stage LDS ring of 16-byte direct-to-LDS loads (three steps in flight ahead
-// of the MFMAs); chunks of each 128-byte row are XOR-swizzled by
+// the small A chunk is re-read from L2. NT is 64, 96 or 128 columns. K moves
+// in 64-wide steps through a 4-stage LDS ring of 16-byte direct-to-LDS loads
+// (three steps in flight ahead of the MFMAs); chunks of each 128-byte row are XOR-swizzled by
 // (row ^ row >> 3) & 7. Wave w computes rows 32w..32w+31 with
 // v_mfma_f32_32x32x16_bf16 (W as the first operand, so a lane's results are 4
 // consecutive columns of one row). With one split the bf16 result is stored
@@ -20,13 +20,23 @@ constexpr int SK_BK = 64, SK_ST = 4;
 
 __device__ __forceinline__ int sk_sw(int row) { return (row ^ (row >> 3)) & 7; }
 
-template <int NT>
+// s_waitcnt lgkmcnt(0) and vmcnt(N), then a workgroup barrier
+template <int N>
+__device__ __forceinline__ void sk_wait_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// ST-stage ring (ST - 1 steps in flight ahead of the MFMAs)
+template <int NT, int ST>
 __device__ __forceinline__ void gemm_skinny_body(const SkinnyArgs& g) {
   constexpr int SLOTS = (128 + NT) * 8;          // 16-byte slots per stage
   constexpr int LPT = SLOTS / 256;               // loads per thread per stage
   constexpr int STAGE = SLOTS * 8;               // elements per stage
   constexpr int FN = NT / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[SK_ST * STAGE];
+  static_assert(SLOTS % 256 == 0 && NT % 32 == 0 && (ST == 3 || ST == 4) && (ST - 1) * LPT < 64, "ring shape");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[ST * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -54,26 +64,16 @@ __device__ __forceinline__ void gemm_skinny_body(const SkinnyArgs& g) {
     }
   }
   auto issue = [&](int kt) {
-    uint16_t* st = smem + (kt % SK_ST) * STAGE + wave * LPT * 512;
+    uint16_t* st = smem + (kt % ST) * STAGE + wave * LPT * 512;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) __builtin_amdgcn_global_load_lds(src[i] + kt * SK_BK, st + i * 512, 16, 0, 0);
   };
-  // wait until step kt has landed; `ahead` later steps may still be in flight
+  // wait until step kt has landed; `ahead` (< ST) later steps may still be in flight
   auto wait_ahead = [&](int ahead) {
-    if (ahead >= 3) {
-      if constexpr (LPT == 6) __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(18)" ::: "memory");
-      else __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(24)" ::: "memory");
-    } else if (ahead == 2) {
-      if constexpr (LPT == 6) __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(12)" ::: "memory");
-      else __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(16)" ::: "memory");
-    } else if (ahead == 1) {
-      if constexpr (LPT == 6) __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(6)" ::: "memory");
-      else __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(8)" ::: "memory");
-    } else {
-      __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
+    if (ST == 4 && ahead >= 3) sk_wait_barrier<(ST - 1) * LPT>();
+    else if (ahead >= 2) sk_wait_barrier<2 * LPT>();
+    else if (ahead == 1) sk_wait_barrier<LPT>();
+    else sk_wait_barrier<0>();
   };
 
   floatx16 acc[FN];
@@ -92,16 +92,16 @@ __device__ __forceinline__ void gemm_skinny_body(const SkinnyArgs& g) {
   }
   bf16x8 fa[2], fb[2][FN];
   auto read = [&](int kt, int kk, int buf) {
-    const uint16_t* st = smem + (kt % SK_ST) * STAGE;
+    const uint16_t* st = smem + (kt % ST) * STAGE;
     fa[buf] = *(const bf16x8*)(st + (32 * wave + l32) * SK_BK + xa[kk]);
 #pragma unroll
     for (int j = 0; j < FN; ++j) fb[buf][j] = *(const bf16x8*)(st + (128 + 32 * j + l32) * SK_BK + xw[j & 1][kk]);
   };
 
   if (nk > 0) {
-    for (int s = 0; s < SK_ST; ++s)
+    for (int s = 0; s < ST; ++s)
       if (s < nk) issue(s);
-    wait_ahead(min(nk, SK_ST) - 1);   // step 0 has landed
+    wait_ahead(min(nk, ST) - 1);   // step 0 has landed
   }
   if (nk > 0) read(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
@@ -111,8 +111,8 @@ __device__ __forceinline__ void gemm_skinny_body(const SkinnyArgs& g) {
       if (kk < 3) {
         read(kt, kk + 1, cb ^ 1);
       } else if (kt + 1 < nk) {
-        wait_ahead(min(nk - 2 - kt, 2));
-        if (kt + SK_ST < nk) issue(kt + SK_ST);
+        wait_ahead(min(nk - 2 - kt, ST - 2));
+        if (kt + ST < nk) issue(kt + ST);
         read(kt + 1, 0, cb ^ 1);
       }
 #pragma unroll
@@ -376,10 +376,11 @@ __device__ __forceinline__ void gemm_skinny_fp8_body(const SkinnyArgs& g) {
     }
 }
 
-__global__ __launch_bounds__(256, 1) void gemm_skinny64_kernel(SkinnyArgs g) { gemm_skinny_body<64>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_skinny64_kernel(SkinnyArgs g) { gemm_skinny_body<64, 4>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_skinny96_kernel(SkinnyArgs g) { gemm_skinny_body<96, 4>(g); }
 __global__ __launch_bounds__(256, 1) void gemm_skinny_fp8_64_kernel(SkinnyArgs g) { gemm_skinny_fp8_body<64>(g); }
 __global__ __launch_bounds__(256, 1) void gemm_skinny_fp8_128_kernel(SkinnyArgs g) { gemm_skinny_fp8_body<128>(g); }
-__global__ __launch_bounds__(256, 1) void gemm_skinny128_kernel(SkinnyArgs g) { gemm_skinny_body<128>(g); }
+__global__ __launch_bounds__(256, 1) void gemm_skinny128_kernel(SkinnyArgs g) { gemm_skinny_body<128, 4>(g); }
 
 // out[m, n] = sum over s of P[s][m][n] (s ascending), stored bf16.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* P, int S, int M, int N, uint16_t* out,
@@ -410,7 +411,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* P, int 
 hipError_t launch_gemm_skinny(const SkinnyArgs& g, int nt, int splits, hipStream_t s) {
   dim3 grid((g.N + nt - 1) / nt, splits, g.batch);
   if (nt == 64) gemm_skinny64_kernel<<<grid, 256, 0, s>>>(g);
-  else gemm_skinny128_kernel<<<grid, 256, 0, s>>>(g);
+  else if (nt == 96) gemm_skinny96_kernel<<<grid, 256, 0, s>>>(g);
+  else if (nt == 128) gemm_skinny128_kernel<<<grid, 256, 0, s>>>(g);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
