@@ -317,7 +317,7 @@ def test_prefill_cached_topk_fp8_batched():
                            topk=24), 49, start_pos=130, max_len=256, tol=FP8_TOL, cos=0.999)
 
 
-@pytest.mark.xfail(strict=False, reason="e4m3 requantisation of bf16 intermediates (q_lat, o_lat, o) gives "
+@pytest.mark.xfail(strict=False, reason="e4m3 requantisation of bf16 intermediates (c_q, o_lat, o) gives "
                    "3.4e-2 max error (cosine 0.99955) here, above the 3e-2 bar; each row alone is within it")
 def test_decode_sparse_fp8_dsv32_sampled():
     # e4m3 weights, 3000 cached, top-2048 per sequence, DeepSeek-V3.2-Exp shapes
