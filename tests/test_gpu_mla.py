@@ -138,6 +138,17 @@ def test_decode_fp8_dsv32_full_size_sampled():
     _check_decode(cfg, synth.seed_of(4), max_len=1024, seqs=[0, 1, 37, 64, 100, 127])
 
 
+@pytest.mark.parametrize("weight", ["bf16", "e4m3"])
+def test_decode_batch_past_128_rows(weight):
+    # 140 sequences: the projections run in two 128-row chunks, the absorb kernel
+    # in two sequence blocks and the attention grid ends in a partial group of 8
+    cfg = dict(name="dec_b140", mode="decode", B=140, cache_len=20, dim=1024, q_lora_rank=256, kv_lora_rank=512,
+               n_heads=64, act="bf16", weight=weight)
+    lens = [(7 * b) % 21 for b in range(140)]
+    _check_decode(cfg, 43 if weight == "bf16" else 44, cache_len=lens, max_len=24,
+                  seqs=[0, 1, 5, 127, 128, 129, 138, 139])
+
+
 def test_decode_out_of_range_length_gives_zero_row():
     cfg = dict(name="dec_bad", mode="decode", B=3, cache_len=10, dim=512, q_lora_rank=128, kv_lora_rank=512,
                n_heads=64, act="bf16", weight="bf16")
