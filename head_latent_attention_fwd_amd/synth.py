@@ -13,10 +13,12 @@ consume its output. Recipe:
 * top-k selection: query rows s < k keep every key 0..s; rows s >= k keep
   their own position plus k-1 distinct keys drawn uniformly from 0..s-1;
   stored ascending, int32, padded with -1.
-* decode cache: slots 0..P-1 hold [latent | rope key]; the latent is drawn
-  like an RMSNorm output, gamma_kv * z with z ~ N(0, 1) (normalising an
-  N(0, 1) row moves it by its rms, 1 +- 0.03 at 512 dims), and the rope key is
-  N(0, 1) (an isotropic Gaussian keeps its law under rotation). Slots >= P are 0.
+* decode cache: slots 0..P-1 hold [latent | rope key]. The latent row is
+  "N(0, 1), RMSNorm applied": z ~ N(0, 1), divided by sqrt(mean(z^2) + 1e-6)
+  and multiplied by gamma_kv (the draw's distribution recipe, done in fp64
+  before the one rounding to bf16). The rope key is N(0, 1), taken as already
+  rotated (an isotropic Gaussian keeps its law under rotation). Slots >= P
+  are 0. Chunked-prefill caches are drawn the same way.
 * fp8 weights: the fp32 masters are returned; each side block-quantises them.
 """
 import numpy as np
@@ -98,6 +100,13 @@ def draw_topk(rng, B, T, k, start=0):
     return idx
 
 
+def _normed_latents(rng, gamma, shape):
+    """Cache latents per the decode workload: N(0, 1) rows scaled to unit root
+    mean square (eps 1e-6 under the root) and multiplied by gamma."""
+    z = rng.standard_normal(shape)
+    return gamma * z / np.sqrt(np.mean(z * z, axis=-1, keepdims=True) + 1e-6)
+
+
 def make_cfg(index=None, **over):
     cfg = dict(CONFIGS[index]) if index is not None else {}
     cfg.update(over)
@@ -124,7 +133,7 @@ def gen_chunk(cfg, seed, start_pos, max_len=None):
     x = round_to(rng.standard_normal((B, T, cfg["dim"])), "bf16")
     w = _draw_weights(rng, cfg)
     cache = np.zeros((B, max_len, L + KV_ROPE), dtype=np.float32)
-    lat = w["kv_norm_w"][None, None, :] * rng.standard_normal((B, start_pos, L))
+    lat = _normed_latents(rng, w["kv_norm_w"].astype(np.float64), (B, start_pos, L))
     cache[:, :start_pos, :L] = round_to(lat, "bf16")
     cache[:, :start_pos, L:] = round_to(rng.standard_normal((B, start_pos, KV_ROPE)), "bf16")
     topk = draw_topk(rng, B, T, cfg["topk"], start_pos) if cfg.get("topk") else None
@@ -141,7 +150,7 @@ def gen_decode(cfg, seed, max_len=None):
     x = round_to(rng.standard_normal((B, cfg["dim"])), "f32" if cfg["act"] == "f32" else "bf16")
     w = _draw_weights(rng, cfg)
     cache = np.zeros((B, max_len, L + KV_ROPE), dtype=np.float32)
-    lat = w["kv_norm_w"][None, None, :] * rng.standard_normal((B, P, L))
+    lat = _normed_latents(rng, w["kv_norm_w"].astype(np.float64), (B, P, L))
     cache[:, :P, :L] = round_to(lat, "bf16")
     cache[:, :P, L:] = round_to(rng.standard_normal((B, P, KV_ROPE)), "bf16")
     cache_len = np.full((B,), P, dtype=np.int32)

@@ -15,9 +15,14 @@ The rest is the plainest reading the pages support:
 * activations: one scale per row and per 128 consecutive elements along the
   reduction dimension; weights: one scale per 128 x 128 block of [out, in]
   (edge blocks partial, their max taken over the valid elements only).
-* the quantiser's input is the activation as the workload holds it (bf16),
-  and the quotient a / s is taken in fp32, so that a code is decided in the
-  same precision the kernels decide it in.
+* the quantiser's input is the activation tensor the Linear receives. The
+  workload is a bf16 model ("bf16 in / fp32 accumulate", with fp8 weights as
+  a variant of it), so that tensor holds bf16 values: the oracle rounds its
+  fp64 activation to bf16 before quantising it. Scales are fp32 (the
+  workload's "one fp32 scale per 128x128 block"); the quotient a / s of a
+  bf16 value by an fp32 scale is taken in fp32, the precision both operands
+  already have. A CPU test measures how far quantising the unrounded fp64
+  activation instead would move a product of the fp8 workload's size.
 """
 import numpy as np
 
@@ -152,6 +157,23 @@ def round_bf16(x):
     x = np.asarray(x, dtype=np.float64)
     m, e = np.frexp(x)
     return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+def dequant_weight(w_codes, w_scales):
+    """Value the block-scaled weight stands for: codes times their block's scale."""
+    N, K = w_codes.shape
+    s = np.repeat(np.repeat(np.asarray(w_scales, dtype=np.float64), 128, 0), 128, 1)[:N, :K]
+    return e4m3_decode(w_codes) * s
+
+
+def quant_dequant_act(a):
+    """Value an activation stands for after the dynamic 1x128 quantisation that
+    linear_fp8 applies to its input (bf16 activation, fp32 quotient): each
+    code times its group's scale. fp8_gemm of these codes equals the product
+    of this array with the dequantised weight, so a reassociated product (an
+    absorbed weight) sees the same operand."""
+    codes, scales = quant_act_1x128(round_bf16(a).astype(np.float32), "f32")
+    return e4m3_decode(codes) * np.repeat(scales.astype(np.float64), 128, axis=1)
 
 
 def linear_fp8(a, w_codes, w_scales):

@@ -276,7 +276,7 @@ def _decode_tokens(x, w, d, P, fp8=None):
     return q_nope, q_pe, entry
 
 
-def mla_decode(x, w, d, cache, cache_len, seqs=None, topk_idx=None):
+def mla_decode(x, w, d, cache, cache_len, seqs=None, topk_idx=None, fp8=False):
     """Single-token decode, unabsorbed definition ([SA] "Explanation": one
     decoded token scores the cached latent; [DO] shapes [B,1,16384] -> [B,1,7168]).
 
@@ -285,38 +285,49 @@ def mla_decode(x, w, d, cache, cache_len, seqs=None, topk_idx=None):
     topk_idx [B, k]: the listed ones among them, [SA] "Code" mask); every
     cached latent is up-projected by kv_b into per-head k_nope and v exactly
     as in prefill, then standard attention and wo.
+
+    With fp8=True (w holds the fp32 masters, block-quantised here as in
+    prefill, [DN] quantization_config) every Linear is the e4m3 block-scaled
+    product with its input quantised in dynamic 1x128 groups, applied exactly
+    as prefill applies it: q_a, kv_a and q_b to the new token, kv_b to every
+    cached latent (and to the new one), wo to the flattened head outputs.
+    Only live keys are up-projected (dead keys carry weight exactly 0).
     x: [B, dim]; cache: [B, max_len, kv_lora+64] values; cache_len: [B].
     Returns (out [len(seqs), dim], new_entry [len(seqs), kv_lora+64])."""
     x = np.asarray(x, dtype=np.float64)
     seqs = np.arange(x.shape[0]) if seqs is None else np.asarray(seqs)
     L = d["kv_lora_rank"]
     H = d["n_heads"]
+    fq = quantise_weights(w) if fp8 else None
     P_all = np.asarray(cache_len)[seqs].astype(np.int64)
-    q_nope, q_pe, entries = _decode_tokens(x[seqs], w, d, P_all)
+    q_nope, q_pe, entries = _decode_tokens(x[seqs], w, d, P_all, fq)
     o = np.zeros((len(seqs), H * VDIM))
     for i, b in enumerate(seqs):
         P = int(P_all[i])
         C = np.concatenate([np.asarray(cache[b, :P], dtype=np.float64), entries[i][None]], axis=0)
-        k_nope, v = up_project(C[:, :L], w, d)
-        live = live_keys(P, None if topk_idx is None else topk_idx[b])
-        o_h, _ = attend_row(q_nope[i], q_pe[i], k_nope, C[:, L:], v, live, d["softmax_scale"])
+        C = C[live_keys(P, None if topk_idx is None else topk_idx[b])]
+        k_nope, v = up_project(C[:, :L], w, d, fq)
+        o_h, _ = attend_row(q_nope[i], q_pe[i], k_nope, C[:, L:], v, np.arange(C.shape[0]), d["softmax_scale"])
         o[i] = o_h.reshape(-1)
-    return linear(o, w["wo"]), entries
+    return _proj(o, w, "wo", fq), entries
 
 
 def mla_decode_absorbed(x, w, d, cache, cache_len, seqs=None, fp8=False, topk_idx=None):
-    """Single-token decode with kv_b absorbed: the same result as mla_decode by
-    reassociating the products. With W_UK_h = Wkv_b rows [256h, 256h+128) and
-    W_UV_h = rows [256h+128, 256h+256):
+    """Single-token decode with kv_b absorbed: mla_decode's result, reached by
+    reassociating its products ([SA] "Explanation": the decoded token scores
+    the cached latent directly). With W_UK_h = Wkv_b rows [256h, 256h+128) and
+    W_UV_h = rows [256h+128, 256h+256), and c_t the latent kv_b receives:
       q_lat_h = W_UK_h^T q_nope_h                      (latent-space query)
-      z[h, t] = scale * (q_lat_h . C_t[:L] + q_pe_h . C_t[L:])
-      o_lat_h = sum_t softmax(z)[h, t] * C_t[:L]
+      z[h, t] = scale * (q_lat_h . c_t + q_pe_h . k_pe_t)
+      o_lat_h = sum_t softmax(z)[h, t] * c_t
       o_h     = W_UV_h o_lat_h
-    With fp8=True (w holds fp32 masters, block-quantised here as in prefill):
-    q_a, kv_a, q_b and wo are fp8 Linears (dynamic 1x128 activation groups);
-    W_UK enters dequantised (codes times block scale) since it is applied
-    along its output dimension; W_UV_h is applied to o_lat_h as an fp8 Linear
-    (o_lat_h quantised in 1x128 groups, the head's block row of scales).
+    With fp8=True the same reassociation of mla_decode(fp8=True): kv_b's
+    product on a latent is the block-scaled e4m3 product, i.e. the product of
+    the dequantised weight (codes times block scale) with the dequantised
+    latent (its 1x128 codes times group scale). So W_UK and W_UV enter
+    dequantised and c_t is the dequantised quantised latent, in the scores and
+    in the values alike; the rotary key is not an input of kv_b and stays as
+    cached. q_a, kv_a, q_b and wo stay e4m3 Linears.
     With topk_idx [B, k] only the listed slots among 0..P are keys.
     Returns (out, new_entry) like mla_decode."""
     x = np.asarray(x, dtype=np.float64)
@@ -325,13 +336,12 @@ def mla_decode_absorbed(x, w, d, cache, cache_len, seqs=None, fp8=False, topk_id
     H = d["n_heads"]
     fq = quantise_weights(w) if fp8 else None
     if fp8:
-        from .fp8 import e4m3_decode, linear_fp8
-        codes, scales = fq["wkv_b"]
-        deq = e4m3_decode(codes) * np.repeat(np.repeat(scales.astype(np.float64), 128, 0), 128, 1)
-        W_UK = deq.reshape(H, NOPE + VDIM, L)[:, :NOPE, :]
+        from .fp8 import dequant_weight, quant_dequant_act
+        wkv_b = dequant_weight(*fq["wkv_b"])
     else:
-        wkv_b = np.asarray(w["wkv_b"], dtype=np.float64).reshape(H, NOPE + VDIM, L)
-        W_UK, W_UV = wkv_b[:, :NOPE, :], wkv_b[:, NOPE:, :]
+        wkv_b = np.asarray(w["wkv_b"], dtype=np.float64)
+    wkv_b = wkv_b.reshape(H, NOPE + VDIM, L)
+    W_UK, W_UV = wkv_b[:, :NOPE, :], wkv_b[:, NOPE:, :]
     P_all = np.asarray(cache_len)[seqs].astype(np.int64)
     q_nope, q_pe, entries = _decode_tokens(x[seqs], w, d, P_all, fq)
     o = np.zeros((len(seqs), H * VDIM))
@@ -339,17 +349,12 @@ def mla_decode_absorbed(x, w, d, cache, cache_len, seqs=None, fp8=False, topk_id
         P = int(P_all[i])
         C = np.concatenate([np.asarray(cache[b, :P], dtype=np.float64), entries[i][None]], axis=0)
         C = C[live_keys(P, None if topk_idx is None else topk_idx[b])]
+        lat = quant_dequant_act(C[:, :L]) if fp8 else C[:, :L]
         q_lat = np.einsum("hi,hic->hc", q_nope[i], W_UK)           # [H, L]
-        z = (q_lat @ C[:, :L].T + q_pe[i] @ C[:, L:].T) * d["softmax_scale"]
+        z = (q_lat @ lat.T + q_pe[i] @ C[:, L:].T) * d["softmax_scale"]
         p = softmax_over_live(z)                                  # [H, live keys]
-        o_lat = p @ C[:, :L]                                      # [H, L]
-        if fp8:
-            for h in range(H):
-                r0 = 256 * h + NOPE
-                o[i, h * VDIM:(h + 1) * VDIM] = linear_fp8(o_lat[h][None], codes[r0:r0 + VDIM],
-                                                           scales[r0 // 128:r0 // 128 + 1])[0]
-        else:
-            o[i] = np.einsum("hjc,hc->hj", W_UV, o_lat).reshape(-1)   # [H*128]
+        o_lat = p @ lat                                           # [H, L]
+        o[i] = np.einsum("hjc,hc->hj", W_UV, o_lat).reshape(-1)   # [H*128]
     return _proj(o, w, "wo", fq), entries
 
 

@@ -392,30 +392,149 @@ def test_one_token_chunk_equals_decode():
     np.testing.assert_allclose(e1[:, 0], e2, rtol=1e-13, atol=1e-14)
 
 
-def test_fp8_absorbed_decode_tracks_the_exact_decode():
-    """With e4m3 weights the absorbed decode stays within fp8 rounding of the
+def _fp8_tiny(seed=51, B=3, P=20, max_len=24):
+    cfg = dict(name="t", mode="decode", B=B, cache_len=P, dim=256, q_lora_rank=256, kv_lora_rank=128,
+               n_heads=2, act="bf16", weight="e4m3")
+    inp = synth.gen_decode(cfg, seed, max_len=max_len)
+    return inp, mla.default_dims(256, 256, 128, 2)
+
+
+def test_fp8_absorbed_decode_equals_unabsorbed_definition():
+    """The absorbed e4m3 decode (dequantised W_UK / W_UV, dequantised 1x128
+    latents) is an exact reassociation of the unabsorbed definition (kv_b as
+    the e4m3 Linear on every cached latent), with and without a selection."""
+    inp, d = _fp8_tiny()
+    inp["cache_len"] = np.array([0, 7, 20], dtype=np.int32)
+    o1, e1 = mla.mla_decode(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"], fp8=True)
+    o2, e2 = mla.mla_decode_absorbed(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"], fp8=True)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-12 * np.abs(o1).max())
+    assert np.array_equal(e1, e2)
+    idx = np.array([[0, -1, -1], [6, 2, 30], [20, 3, 3]])
+    o1, _ = mla.mla_decode(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"], topk_idx=idx, fp8=True)
+    o2, _ = mla.mla_decode_absorbed(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"], topk_idx=idx, fp8=True)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-12 * np.abs(o1).max())
+
+
+def test_fp8_decode_equals_last_row_of_fp8_prefill():
+    """e4m3 decode of token P against the cache an e4m3 prefill makes for
+    tokens 0..P-1 gives that prefill's row P: decode applies every Linear,
+    kv_b on the cached latents included, exactly as prefill does. Also under a
+    top-k selection (the prefill row's own selection)."""
+    cfg = dict(name="t", mode="prefill", B=1, T=11, dim=256, q_lora_rank=256, kv_lora_rank=128, n_heads=2,
+               act="bf16", weight="e4m3", topk=0)
+    inp = synth.gen_prefill(cfg, 53)
+    d = mla.default_dims(256, 256, 128, 2)
+    idx = np.full((1, 11, 4), -1, dtype=np.int64)
+    rng = np.random.default_rng(54)
+    for s in range(11):
+        k = min(s + 1, 4)
+        idx[0, s, :k] = rng.choice(s + 1, k, replace=False)
+    P = 10
+    for sel in (None, idx):
+        out, aux = mla.mla_prefill(inp["x"], inp["w"], d, topk_idx=sel, fp8=True, return_aux=True)
+        cache = aux["cache"][0][None, :P]
+        dsel = None if sel is None else sel[:, P]
+        o1, entry = mla.mla_decode(inp["x"][:, P], inp["w"], d, cache, np.array([P]), topk_idx=dsel, fp8=True)
+        o2, _ = mla.mla_decode_absorbed(inp["x"][:, P], inp["w"], d, cache, np.array([P]), topk_idx=dsel, fp8=True)
+        np.testing.assert_allclose(o1[0], out[0, P], rtol=1e-11, atol=1e-12 * np.abs(out).max())
+        np.testing.assert_allclose(o2[0], out[0, P], rtol=1e-11, atol=1e-12 * np.abs(out).max())
+        np.testing.assert_allclose(entry[0], aux["cache"][0][P], rtol=1e-13, atol=1e-14)
+
+
+def test_fp8_decode_tracks_the_exact_decode():
+    """With e4m3 weights the decode definition stays within fp8 rounding of the
     exact (fp64, unquantised) decode. Every 128x128 weight block is scaled by
     its own power of two, so a scale taken from the wrong block (or dropped)
     moves the result by far more than the rounding does."""
-    cfg = dict(name="t", mode="decode", B=3, cache_len=20, dim=256, q_lora_rank=256, kv_lora_rank=512,
-               n_heads=2, act="bf16", weight="e4m3")
-    inp = synth.gen_decode(cfg, 51, max_len=24)
+    inp, d = _fp8_tiny(seed=55)
     rng = np.random.default_rng(52)
     w = dict(inp["w"])
     for n in ("wq_a", "wq_b", "wkv_a", "wkv_b", "wo"):
         a = np.asarray(w[n], dtype=np.float64)
         f = 2.0 ** rng.integers(-3, 4, size=(-(-a.shape[0] // 128), -(-a.shape[1] // 128)))
         w[n] = (a * np.repeat(np.repeat(f, 128, 0), 128, 1)[:a.shape[0], :a.shape[1]]).astype(np.float32)
-    d = mla.default_dims(256, 256, 512, 2)
     exact, e_exact = mla.mla_decode(inp["x"], w, d, inp["cache"], inp["cache_len"])
-    got, e_got = mla.mla_decode_absorbed(inp["x"], w, d, inp["cache"], inp["cache_len"], fp8=True)
+    got, e_got = mla.mla_decode(inp["x"], w, d, inp["cache"], inp["cache_len"], fp8=True)
     err = np.abs(got - exact).max() / np.abs(exact).max()
     cos = (got * exact).sum() / np.linalg.norm(got) / np.linalg.norm(exact)
-    # five chained e4m3 products (each ~5 % RMS rounding) give ~8 % RMS here
-    # (cosine 0.9965); a scale from a neighbouring block row or one shared
-    # scale for W_UK gives max errors above 1 and cosines below 0.65
+    # six chained e4m3 products (~5 % RMS rounding each) stay near cosine
+    # 0.99; a scale from a neighbouring block row or one shared scale for a
+    # weight gives max errors above 1 and cosines below 0.65
     assert err < 0.3 and cos > 0.99, (err, cos)
     assert np.abs(e_got - e_exact).max() / np.abs(e_exact).max() < 0.3
+
+
+def test_fp8_decode_quantises_the_cached_latents():
+    """kv_b is an e4m3 Linear in the definition, so its input (each cached
+    latent) is quantised in 1x128 groups: replacing every cached latent by its
+    dequantised e4m3 value leaves the decode unchanged, while an unquantised
+    latent in the absorbed scores would not."""
+    inp, d = _fp8_tiny(seed=56)
+    o1, _ = mla.mla_decode(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"], fp8=True)
+    cache = np.array(inp["cache"], dtype=np.float64)
+    for b in range(cache.shape[0]):
+        P = int(inp["cache_len"][b])
+        cache[b, :P, :128] = fp8.quant_dequant_act(cache[b, :P, :128])
+    o2, _ = mla.mla_decode(inp["x"], inp["w"], d, cache, inp["cache_len"], fp8=True)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-12 * np.abs(o1).max())
+    # the quantised value really differs from the cached one
+    assert np.abs(cache[:, :20, :128] - np.asarray(inp["cache"])[:, :20, :128]).max() > 1e-3
+
+
+def test_activation_quantiser_input_reading():
+    """The activation quantiser takes the bf16 activation (the workload is a
+    bf16 model). Quantising the unrounded fp64 activation instead moves a
+    product of the fp8 prefill's shapes by about 1-2 % of its largest output
+    (a bf16 rounding carries ~3 % of elements across an e4m3 rounding
+    boundary), measured here on 16 rows of the q_a|kv_a (K 7168) and q_b
+    (K 1536) products: inside the 3e-2 fp8 bar, but large enough that the
+    oracle has to take the same reading as the kernels."""
+    rng = np.random.default_rng(3)
+    errs = {}
+    for name, N, K in (("q_a|kv_a", 2112, 7168), ("q_b", 1536, 1536)):
+        a = rng.standard_normal((16, K))
+        w = (rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
+        wc, ws = fp8.quant_weight_block128(w)
+        y_bf16 = fp8.linear_fp8(a, wc, ws)
+        ac, as_ = fp8.quant_act_1x128(a, "f64")
+        y_f64 = fp8.fp8_gemm(ac, as_, wc, ws)
+        errs[name] = np.abs(y_bf16 - y_f64).max() / np.abs(y_f64).max()
+    assert all(2e-3 < e < 3e-2 for e in errs.values()), errs
+
+
+def test_rmsnorm_rope_rows_hand_built():
+    """Offsets and strides of the row-wise norm + RoPE helper: a row whose
+    normalised part is (3, 4, 0, ...) scaled by known gammas, rope slices that
+    hold unit vectors at known positions, and untouched elements between and
+    after them."""
+    norm_dim, rope_off, heads, stride = 4, 10, 2, 70
+    width = rope_off + (heads - 1) * stride + 64 + 5
+    inp = np.full((2, width), 7.0)
+    inp[:, :norm_dim] = [3.0, 4.0, 0.0, 0.0]
+    gamma = np.array([1.0, 2.0, 3.0, 4.0])
+    for h in range(heads):
+        o = rope_off + h * stride
+        inp[:, o:o + 64] = 0.0
+        inp[:, o + h] = 1.0            # head 0: unit dim 0; head 1: unit dim 1
+    pos = np.array([0.0, 2.0])
+    out = mla.rmsnorm_rope_rows(inp, norm_dim, gamma, 0.0, rope_off, heads, stride, pos, 10000.0)
+    rms = np.sqrt((9 + 16) / 4)
+    np.testing.assert_allclose(out[:, :4], [[3 / rms, 8 / rms, 0, 0]] * 2, rtol=1e-14)
+    # row 0 is at position 0: rotation is the identity
+    np.testing.assert_array_equal(out[0, rope_off:], inp[0, rope_off:])
+    # row 1 at position 2: dim d pairs with d + 32 and turns by 2 * 10000^(-d/32)
+    for h in range(heads):
+        o = rope_off + h * stride
+        th = 2.0 * 10000.0 ** (-h / 32)
+        expect = np.zeros(64)
+        expect[h], expect[h + 32] = np.cos(th), np.sin(th)
+        np.testing.assert_allclose(out[1, o:o + 64], expect, atol=1e-15)
+    # everything outside the norm part and the rope slices passes through
+    keep = np.ones(width, dtype=bool)
+    keep[:norm_dim] = False
+    for h in range(heads):
+        keep[rope_off + h * stride:rope_off + h * stride + 64] = False
+    np.testing.assert_array_equal(out[:, keep], inp[:, keep])
 
 
 def test_selected_decode_equals_the_selected_prefill_row():
