@@ -48,7 +48,7 @@ _SIGS = {
     "mla_decode_workspace_size": (sz, [ctypes.POINTER(MlaDims), i32, i32, i32]),
     "mla_decode_sparse": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaWeights), vp, i32, vp, i32, vp,
                                          vp, i32, vp, vp, i32, vp, vp, sz, vp]),
-    "mla_prefill_absorbed_workspace_size": (sz, [ctypes.POINTER(MlaDims), i32, i32]),
+    "mla_prefill_absorbed_workspace_size": (sz, [ctypes.POINTER(MlaDims), i32, i32, i32]),
     "mla_prefill_absorbed": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaWeights), vp, i32, i32, vp,
                                             vp, i32, vp, i32, vp, vp, vp, sz, vp]),
     "mla_decode": (ctypes.c_int, [ctypes.POINTER(MlaDims), ctypes.POINTER(MlaWeights), vp, i32, vp, i32, vp,
@@ -59,7 +59,8 @@ _SIGS = {
     "rmsnorm_rope": (ctypes.c_int, [vp, i64, i32, i32, i32, vp, f32, i32, i32, i32, vp, vp, i32, vp, i32,
                                     vp, i64, i32, vp]),
     "mla_prefill_attention": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]),
-    "mla_decode_attention": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, f32, vp]),
+    "mla_decode_attention_workspace_size": (sz, [i32, i32, i32]),
+    "mla_decode_attention": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, f32, vp, sz, vp]),
     "mla_rope_table": (ctypes.c_int, [vp, vp, i32, f32, vp]),
     "mla_quant_e4m3_1x128": (ctypes.c_int, [vp, i64, i32, i32, i32, vp, vp, vp]),
     "mla_quant_e4m3_block128": (ctypes.c_int, [vp, i32, i32, vp, vp, vp]),
@@ -212,8 +213,8 @@ def mla_decode(dims, weights, x, kv_cache, cache_len, rope_cos, rope_sin, out, w
     return out
 
 
-def mla_prefill_absorbed_workspace_size(dims, B, T):
-    return lib().mla_prefill_absorbed_workspace_size(ctypes.byref(dims), B, T)
+def mla_prefill_absorbed_workspace_size(dims, B, T, topk):
+    return lib().mla_prefill_absorbed_workspace_size(ctypes.byref(dims), B, T, topk)
 
 
 def mla_prefill_absorbed(dims, weights, x, rope_cos, rope_sin, topk_idx, out, ws, kv_cache_out=None, stream=None):
@@ -287,11 +288,18 @@ def mla_prefill_attention(q, k_nope, v_t, k_pe, out, B, T, H, scale=192.0 ** -0.
     return out
 
 
-def mla_decode_attention(q_lat, cache, cache_len, o_lat, scale=192.0 ** -0.5, stream=None):
-    """q_lat [B, H, 576], cache [B, max_len, 576], cache_len [B] int32, o_lat [B, H, 512]."""
+def mla_decode_attention_workspace_size(B, H, max_len):
+    return lib().mla_decode_attention_workspace_size(B, H, max_len)
+
+
+def mla_decode_attention(q_lat, cache, cache_len, o_lat, ws=None, scale=192.0 ** -0.5, stream=None):
+    """q_lat [B, H, 576], cache [B, max_len, 576], cache_len [B] int32, o_lat [B, H, 512];
+    ws: workspace of mla_decode_attention_workspace_size bytes (allocated here when None)."""
     B, H, _ = q_lat.shape
+    if ws is None:
+        ws = workspace(mla_decode_attention_workspace_size(B, H, cache.shape[1]), q_lat.device)
     rc = lib().mla_decode_attention(_ptr(q_lat), _ptr(cache), _ptr(cache_len), _ptr(o_lat), B, H, cache.shape[1],
-                                    scale, _stream(stream))
+                                    scale, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc)
     return o_lat
 

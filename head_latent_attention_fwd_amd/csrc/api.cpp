@@ -79,6 +79,11 @@ struct PrefillWs {
 
 int pad64(int T) { return (T + 63) & ~63; }
 
+// Longest cache a sequence may have: the attention kernels address a
+// sequence's rows through one raw buffer of max_len * 576 bf16 values, whose
+// byte size must stay below 2^31.
+constexpr int MAX_CACHE_LEN = 1 << 20;
+
 mla::GemmArgs gemm_args(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc, int cdt, int M,
                         int N, int K);
 
@@ -135,9 +140,13 @@ size_t prefill_layout(const mla_dims* d, int wdt, int adt, int B, int T, int Tk,
 }
 
 struct DecodeWs {
-  void *part, *cqn, *q, *qlat, *olat, *o;
-  void *aq, *as;   // e4m3 weights: the quantised activation of the current projection
-  void *oq, *os;   // e4m3 weights: o quantised by the W_UV product for wo
+  void *part, *cqn, *q, *qlat, *o;
+  void *attn;          // splits == 1: o_lat [B, H, 512] bf16; else the split partials [splits][B*H][512]
+  float* lse;          // splits > 1: [splits][B*H]
+  int32_t *keys, *nkeys;   // selected keys: compacted lists [B][DECODE_TOPK_MAX], counts [B]
+  int splits;
+  void *aq, *as;   // e4m3 weights: the quantised activation of the current projection (x, then c_q)
+  void *oq, *os;   // e4m3 weights: o quantised by the un-absorb kernel for wo
 };
 
 // Decode projections (M = batch rows): column tile widths and split-K. One
@@ -156,28 +165,46 @@ int dec_chunks(int N, int nt) {
   const int c = DEC_CUS / tiles;
   return c < 1 ? 1 : c > DEC_MAX_CHUNKS ? DEC_MAX_CHUNKS : c;
 }
+int skinny_splits(int K, int splits);
+int skinny_fp8_splits(int K, int splits);
 
-size_t decode_layout(const mla_dims* d, int wdt, int B, void* ws, DecodeWs* out) {
+// K chunks the q_a|kv_a and wo products of a decode step use (the same
+// functions pick them at launch, so the partial buffer always fits)
+int dec_qkv_splits(const mla_dims* d, int wdt) {
+  const int nqkv = d->q_lora_rank + d->kv_lora_rank + 64;
+  return wdt == MLA_E4M3 ? skinny_fp8_splits(d->dim, dec_chunks(nqkv, DEC_NT_QKV))
+                         : skinny_splits(d->dim, dec_chunks(nqkv, DEC_NT_QKV));
+}
+int dec_wo_splits(const mla_dims* d, int wdt) {
+  const int K = d->n_heads * 128;
+  return wdt == MLA_E4M3 ? skinny_fp8_splits(K, dec_chunks(d->dim, DEC_NT_FP8))
+                         : skinny_splits(K, dec_chunks(d->dim, DEC_NT_WO));
+}
+
+size_t decode_layout(const mla_dims* d, int wdt, int B, int max_len, void* ws, DecodeWs* out) {
   const size_t H = d->n_heads, Dq = d->q_lora_rank, L = d->kv_lora_rank;
   Carver c(ws);
   DecodeWs p{};
   const int nqkv = (int)(Dq + L + 64);
-  const size_t part_qkv = (size_t)dec_chunks(nqkv, DEC_NT_QKV) * B * nqkv,
-               part_wo = (size_t)dec_chunks(d->dim, DEC_NT_WO) * B * d->dim;
+  const size_t part_qkv = (size_t)dec_qkv_splits(d, wdt) * B * nqkv,
+               part_wo = (size_t)dec_wo_splits(d, wdt) * B * d->dim;
   p.part = c.take((part_qkv > part_wo ? part_qkv : part_wo) * 4);
   p.cqn = c.take((size_t)B * Dq * 2);
   p.q = c.take((size_t)B * H * 192 * 2);
   p.qlat = c.take((size_t)B * H * 576 * 2);
-  p.olat = c.take((size_t)B * H * 512 * 2);
-  p.o = c.take((size_t)B * H * 128 * 2);
-  if (wdt == MLA_E4M3) {   // widest activation: o_lat [B*H, 512] or x [B, dim]
-    size_t kmax = H * 512;
-    if ((size_t)d->dim > kmax) kmax = d->dim;
-    if (Dq > kmax) kmax = Dq;
+  p.splits = mla::decode_splits(B, (int)H, max_len);
+  p.attn = c.take((size_t)p.splits * B * H * 512 * 2);
+  p.lse = p.splits > 1 ? (float*)c.take((size_t)p.splits * B * H * 4) : nullptr;
+  p.keys = (int32_t*)c.take((size_t)B * mla::DECODE_TOPK_MAX * 4);
+  p.nkeys = (int32_t*)c.take((size_t)B * 4);
+  if (wdt == MLA_E4M3) {   // widest quantised projection input: x [B, dim] or c_q [B, q_lora_rank]
+    const size_t kmax = (size_t)d->dim > Dq ? (size_t)d->dim : Dq;
     p.aq = c.take((size_t)B * kmax);
     p.as = c.take((size_t)B * (kmax / 128) * 4);
     p.oq = c.take((size_t)B * H * 128);
     p.os = c.take((size_t)B * H * 4);
+  } else {
+    p.o = c.take((size_t)B * H * 128 * 2);
   }
   if (out) *out = p;
   return c.off;
@@ -186,10 +213,11 @@ size_t decode_layout(const mla_dims* d, int wdt, int B, void* ws, DecodeWs* out)
 struct AbsorbedWs {
   void *cqkv, *cqn, *kvc, *q, *qlat, *olat, *o, *wukt;
   float* part;
+  int32_t *keys, *nkeys;   // compacted selections [M][topk], counts [M]
   int qkv_splits;
 };
 
-size_t absorbed_layout(const mla_dims* d, int B, int T, bool own_kvc, void* ws, AbsorbedWs* out) {
+size_t absorbed_layout(const mla_dims* d, int B, int T, int topk, bool own_kvc, void* ws, AbsorbedWs* out) {
   const size_t M = (size_t)B * T, H = d->n_heads, Dq = d->q_lora_rank, L = d->kv_lora_rank;
   Carver c(ws);
   AbsorbedWs p{};
@@ -203,6 +231,8 @@ size_t absorbed_layout(const mla_dims* d, int B, int T, bool own_kvc, void* ws, 
   p.wukt = c.take(H * L * 128 * 2);
   p.qkv_splits = prefill_qkv_splits(d, MLA_BF16, MLA_BF16, (int)M);
   p.part = p.qkv_splits > 1 ? (float*)c.take((size_t)p.qkv_splits * M * (Dq + L + 64) * 4) : nullptr;
+  p.keys = (int32_t*)c.take(M * (size_t)topk * 4);
+  p.nkeys = (int32_t*)c.take(M * 4);
   if (out) *out = p;
   return c.off;
 }
@@ -541,7 +571,7 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t weight_dtype, int
   if (check_dims(dims) != MLA_OK || B <= 0 || max_len <= 0 ||
       (weight_dtype != MLA_BF16 && weight_dtype != MLA_E4M3))
     return 0;
-  return decode_layout(dims, weight_dtype, B, nullptr, nullptr);
+  return decode_layout(dims, weight_dtype, B, max_len, nullptr, nullptr);
 }
 
 }  // extern "C"
@@ -563,9 +593,12 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
   if (!x || !kv_cache || !cache_len || !rope_cos || !rope_sin || !out)
     return fail(MLA_INVALID_ARG, "x/kv_cache/cache_len/rope tables/out must not be NULL");
   if (B <= 0 || max_len <= 0) return fail(MLA_INVALID_ARG, "B and max_len must be positive");
+  if (max_len > MAX_CACHE_LEN) return fail(MLA_INVALID_ARG, "max_len (%d) above %d", max_len, MAX_CACHE_LEN);
   if (rope_len < max_len) return fail(MLA_INVALID_ARG, "rope_len (%d) < max_len (%d)", rope_len, max_len);
+  if (((uintptr_t)x | (uintptr_t)kv_cache | (uintptr_t)out) & 15)
+    return fail(MLA_UNSUPPORTED, "decode needs 16-byte aligned x, kv_cache and out");
   DecodeWs p;
-  const size_t need = decode_layout(d, wdt, B, ws, &p);
+  const size_t need = decode_layout(d, wdt, B, max_len, ws, &p);
   if (!ws || ws_bytes < need) return fail(MLA_INVALID_ARG, "workspace too small: need %zu bytes", need);
   if ((uintptr_t)ws & 255) return fail(MLA_INVALID_ARG, "workspace must be 256-byte aligned");
   hipStream_t s = (hipStream_t)stream;
@@ -578,25 +611,17 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
   float* part = (float*)p.part;
   uint8_t* aq = (uint8_t*)p.aq;
   float* as = (float*)p.as;
-  // e4m3 weights: each projection's input is quantised in 1x128 groups first
-  auto quant = [&](const void* a, int64_t lda, int rows, int K) -> int {
-    LAUNCH(mla::launch_quant_1x128(a, lda, MLA_BF16, rows, K, aq, as, s), "quant_e4m3_1x128");
-    return MLA_OK;
-  };
   // [c_q | latent | k_pe] = x . [Wq_a ; Wkv_a]^T as split-K partials, summed by the norms
-  int splits_qkv;
-  if (fp8) {
-    if ((rc = quant(x, dim, B, dim))) return rc;
+  const int splits_qkv = dec_qkv_splits(d, wdt);
+  if (fp8) {   // x quantised in 1x128 groups first
+    LAUNCH(mla::launch_quant_1x128(x, dim, MLA_BF16, B, dim, aq, as, s), "quant_e4m3_1x128(x)");
     if ((rc = skinny_fp8(aq, dim, 0, as, dim / 128, 0, w->wq_a, dim, 0, w->wq_a_scale, dim / 128, 0, w->wkv_a, dim,
                          w->wkv_a_scale, Dq, nullptr, 0, 0, part, B, NQKV, dim, 1, DEC_NT_QKV,
                          dec_chunks(NQKV, DEC_NT_QKV), s)))
       return rc;
-    splits_qkv = skinny_fp8_splits(dim, dec_chunks(NQKV, DEC_NT_QKV));
-  } else {
-    if ((rc = skinny(x, dim, 0, w->wq_a, dim, 0, w->wkv_a, dim, Dq, nullptr, 0, 0, part, B, NQKV, dim, 1, DEC_NT_QKV,
-                     dec_chunks(NQKV, DEC_NT_QKV), s)))
-      return rc;
-    splits_qkv = skinny_splits(dim, dec_chunks(NQKV, DEC_NT_QKV));
+  } else if ((rc = skinny(x, dim, 0, w->wq_a, dim, 0, w->wkv_a, dim, Dq, nullptr, 0, 0, part, B, NQKV, dim, 1,
+                          DEC_NT_QKV, dec_chunks(NQKV, DEC_NT_QKV), s))) {
+    return rc;
   }
   {  // q_norm, kv_norm and RoPE of k_pe; the new [latent | k_pe] lands directly in cache row cache_len[b]
     mla::QkvNormArgs a{};
@@ -606,7 +631,7 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
     a.kv_out = kv_cache; a.ld_kv = (int64_t)max_len * (L + 64); a.kv_pos_stride = L + 64; a.kv_pos_max = max_len;
     a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = max_len; a.pos = cache_len;
     if (fp8) { a.q_codes = aq; a.q_scales = as; }   // q_b's input, quantised in the same pass
-    if (!qkv_norm_ok(a)) return fail(MLA_UNSUPPORTED, "decode needs 16-byte aligned norm weights and cache");
+    if (!qkv_norm_ok(a)) return fail(MLA_UNSUPPORTED, "decode needs 16-byte aligned norm weights");
     LAUNCH(mla::launch_qkv_norm(a, s), "qkv_norm -> cache");
   }
   // q = c_q . Wq_b^T
@@ -622,39 +647,42 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
   LAUNCH(mla::launch_decode_absorb(p.q, w->wkv_b, fp8 ? w->wkv_b_scale : nullptr, p.qlat, cache_len, rope_cos,
                                    rope_sin, B, H, max_len, s),
          "decode_absorb");
+  if (topk_idx)   // each row's selection as its ascending, duplicate-free list of live positions
+    LAUNCH(mla::launch_decode_compact(topk_idx, topk, cache_len, 0, B, max_len, p.keys, mla::DECODE_TOPK_MAX, p.nkeys,
+                                      s),
+           "decode_compact");
   {
     mla::DecodeAttnArgs a{};
-    a.qlat = p.qlat; a.cache = kv_cache; a.cache_len = cache_len; a.olat = p.olat;
-    a.B = B; a.H = H; a.max_len = max_len; a.scale = d->softmax_scale;
-    a.idx = topk_idx; a.topk = topk;
-    if (fp8) { a.oq = aq; a.os = as; }   // o_lat leaves as W_UV's e4m3 input
+    a.qlat = p.qlat; a.cache = kv_cache; a.cache_len = cache_len;
+    a.R = B; a.H = H; a.max_len = max_len; a.scale = d->softmax_scale;
+    if (topk_idx) { a.keys = p.keys; a.nkeys = p.nkeys; a.kstride = mla::DECODE_TOPK_MAX; }
+    a.splits = p.splits;
+    if (p.splits == 1) a.olat = p.attn;
+    else { a.part = p.attn; a.lse = p.lse; }
+    a.quant_latent = fp8;   // kv_b's e4m3 input: the dequantised 1x128 latent
     LAUNCH(mla::launch_decode_attn(a, s), "decode_attn");
   }
-  // o[b, h] = W_UV_h . o_lat[b, h]  (W_UV_h = Wkv_b rows [256h+128, 256h+256)), per head
-  if (fp8) {   // o_lat codes per (b, h) row in 4 groups; W_UV_h = block row 2h + 1 of the scales
-    if ((rc = skinny_fp8(aq, (int64_t)H * L, L, as, (int64_t)H * (L / 128), L / 128,
-                         (const uint8_t*)w->wkv_b + 128 * (int64_t)L, L, 256 * (int64_t)L, w->wkv_b_scale + L / 128,
-                         L / 128, 2 * (L / 128), nullptr, 0, nullptr, 128, nullptr, H * 128, 128, nullptr, B, 128, L,
-                         H, 128, 1, s, (uint8_t*)p.oq, (float*)p.os)))   // o leaves as wo's e4m3 input
-      return rc;
-  } else if ((rc = skinny(p.olat, H * 512, 512, (const uint16_t*)w->wkv_b + 128 * (int64_t)L, L, 256 * (int64_t)L,
-                          nullptr, 0, 128, p.o, H * 128, 128, nullptr, B, 128, L, H, 64, 1, s))) {
-    return rc;
+  {  // o[b, h] = W_UV_h . o_lat[b, h] (splits merged in order); e4m3: o leaves as wo's quantised input
+    mla::UnabsorbArgs u{};
+    u.part = p.attn; u.lse = p.lse; u.splits = p.splits;
+    u.wkv_b = w->wkv_b; u.w_scale = fp8 ? w->wkv_b_scale : nullptr;
+    u.ldo = (int64_t)H * 128;
+    if (fp8) { u.oq = (uint8_t*)p.oq; u.os = (float*)p.os; }
+    else u.o = p.o;
+    u.B = B; u.H = H;
+    LAUNCH(mla::launch_decode_unabsorb(u, s), "decode_unabsorb");
   }
   // out = o . Wo^T (split-K, then a fixed-order sum)
-  int splits_wo;
   if (fp8) {
-    if ((rc = skinny_fp8(p.oq, H * 128, 0, (const float*)p.os, H, 0, w->wo, H * 128, 0, w->wo_scale, H, 0, nullptr, 0, nullptr, dim,
-                         nullptr, 0, 0, part, B, dim, H * 128, 1, DEC_NT_FP8, dec_chunks(dim, DEC_NT_FP8), s)))
+    if ((rc = skinny_fp8(p.oq, H * 128, 0, (const float*)p.os, H, 0, w->wo, H * 128, 0, w->wo_scale, H, 0, nullptr, 0,
+                         nullptr, dim, nullptr, 0, 0, part, B, dim, H * 128, 1, DEC_NT_FP8,
+                         dec_chunks(dim, DEC_NT_FP8), s)))
       return rc;
-    splits_wo = skinny_fp8_splits(H * 128, dec_chunks(dim, DEC_NT_FP8));
-  } else {
-    if ((rc = skinny(p.o, H * 128, 0, w->wo, H * 128, 0, nullptr, 0, dim, nullptr, 0, 0, part, B, dim, H * 128, 1,
-                     DEC_NT_WO, dec_chunks(dim, DEC_NT_WO), s)))
-      return rc;
-    splits_wo = skinny_splits(H * 128, dec_chunks(dim, DEC_NT_WO));
+  } else if ((rc = skinny(p.o, H * 128, 0, w->wo, H * 128, 0, nullptr, 0, dim, nullptr, 0, 0, part, B, dim, H * 128,
+                          1, DEC_NT_WO, dec_chunks(dim, DEC_NT_WO), s))) {
+    return rc;
   }
-  LAUNCH(mla::launch_splitk_reduce(part, splits_wo, B, dim, out, dim, s), "splitk_reduce(wo)");
+  LAUNCH(mla::launch_splitk_reduce(part, dec_wo_splits(d, wdt), B, dim, out, dim, s), "splitk_reduce(wo)");
   return MLA_OK;
 }
 
@@ -682,9 +710,9 @@ int mla_decode_sparse(const mla_dims* d, const mla_weights* w, const void* x, in
                      ws_bytes, stream);
 }
 
-size_t mla_prefill_absorbed_workspace_size(const mla_dims* dims, int32_t B, int32_t T) {
-  if (check_dims(dims) != MLA_OK || B <= 0 || T <= 0) return 0;
-  return absorbed_layout(dims, B, T, true, nullptr, nullptr);
+size_t mla_prefill_absorbed_workspace_size(const mla_dims* dims, int32_t B, int32_t T, int32_t topk) {
+  if (check_dims(dims) != MLA_OK || B <= 0 || T <= 0 || topk <= 0 || topk > mla::DECODE_TOPK_MAX) return 0;
+  return absorbed_layout(dims, B, T, topk, true, nullptr, nullptr);
 }
 
 int mla_prefill_absorbed(const mla_dims* d, const mla_weights* w, const void* x, int32_t B, int32_t T,
@@ -704,7 +732,10 @@ int mla_prefill_absorbed(const mla_dims* d, const mla_weights* w, const void* x,
   if (topk <= 0 || topk > mla::DECODE_TOPK_MAX)
     return fail(MLA_UNSUPPORTED, "topk must be in [1, %d]", mla::DECODE_TOPK_MAX);
   AbsorbedWs p;
-  const size_t need = absorbed_layout(d, B, T, kv_cache_out == nullptr, ws, &p);
+  if (T > MAX_CACHE_LEN) return fail(MLA_INVALID_ARG, "T (%d) above %d", T, MAX_CACHE_LEN);
+  if (((uintptr_t)x | (uintptr_t)out | (uintptr_t)kv_cache_out) & 15)
+    return fail(MLA_UNSUPPORTED, "the absorbed prefill needs 16-byte aligned x, out and kv_cache_out");
+  const size_t need = absorbed_layout(d, B, T, topk, kv_cache_out == nullptr, ws, &p);
   if (!ws || ws_bytes < need) return fail(MLA_INVALID_ARG, "workspace too small: need %zu bytes", need);
   if ((uintptr_t)ws & 255) return fail(MLA_INVALID_ARG, "workspace must be 256-byte aligned");
   hipStream_t s = (hipStream_t)stream;
@@ -754,12 +785,14 @@ int mla_prefill_absorbed(const mla_dims* d, const mla_weights* w, const void* x,
     LAUNCH(mla::launch_copy_rows((const uint16_t*)p.q + 128, 192, (uint16_t*)p.qlat + L, 576, (int64_t)M * H, 64, s),
            "copy q_pe");
   }
-  // attention of every token over its selected cache entries, in the latent space
+  // attention of every token over its selected cache entries (compacted to an
+  // ascending, duplicate-free list first), in the latent space; one key run per token
+  LAUNCH(mla::launch_decode_compact(topk_idx, topk, nullptr, T, M, T, p.keys, topk, p.nkeys, s), "compact selection");
   {
     mla::DecodeAttnArgs a{};
-    a.qlat = p.qlat; a.cache = kvc; a.cache_len = nullptr; a.olat = p.olat;
-    a.B = M; a.H = H; a.max_len = T; a.scale = d->softmax_scale;
-    a.idx = topk_idx; a.topk = topk; a.rows_per_seq = T;
+    a.qlat = p.qlat; a.cache = kvc; a.cache_len = nullptr; a.olat = p.olat; a.splits = 1;
+    a.R = M; a.H = H; a.max_len = T; a.scale = d->softmax_scale;
+    a.keys = p.keys; a.nkeys = p.nkeys; a.kstride = topk; a.rows_per_seq = T;
     LAUNCH(mla::launch_decode_attn(a, s), "sparse latent attention");
   }
   // o[m, h] = W_UV_h . o_lat[m, h] per head (W_UV_h = Wkv_b rows [256h+128, 256h+256)), then wo
@@ -867,16 +900,39 @@ int mla_prefill_attention(const void* q, const void* k_nope, const void* v_t, co
   return MLA_OK;
 }
 
+size_t mla_decode_attention_workspace_size(int32_t B, int32_t H, int32_t max_len) {
+  if (B <= 0 || H <= 0 || max_len <= 0) return 0;
+  const int ns = mla::decode_splits(B, H, max_len);
+  if (ns == 1) return 256;
+  return align256((size_t)ns * B * H * 512 * 2) + align256((size_t)ns * B * H * 4);
+}
+
 int mla_decode_attention(const void* q_lat, const void* cache, const int32_t* cache_len, void* o_lat, int32_t B,
-                         int32_t H, int32_t max_len, float scale, void* stream) {
+                         int32_t H, int32_t max_len, float scale, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   if (!q_lat || !cache || !cache_len || !o_lat) return fail(MLA_INVALID_ARG, "NULL pointer");
   if (B <= 0 || H <= 0 || max_len <= 0) return fail(MLA_INVALID_ARG, "bad sizes");
+  if (max_len > MAX_CACHE_LEN) return fail(MLA_INVALID_ARG, "max_len (%d) above %d", max_len, MAX_CACHE_LEN);
   if (H % 64) return fail(MLA_UNSUPPORTED, "H must be a multiple of 64");
+  if (((uintptr_t)q_lat | (uintptr_t)cache | (uintptr_t)o_lat) & 15)
+    return fail(MLA_UNSUPPORTED, "q_lat, cache and o_lat must be 16-byte aligned");
+  const size_t need = mla_decode_attention_workspace_size(B, H, max_len);
+  if (!ws || ws_bytes < need) return fail(MLA_INVALID_ARG, "workspace too small: need %zu bytes", need);
+  if ((uintptr_t)ws & 255) return fail(MLA_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
   mla::DecodeAttnArgs a{};
-  a.qlat = q_lat; a.cache = cache; a.cache_len = cache_len; a.olat = o_lat;
-  a.B = B; a.H = H; a.max_len = max_len; a.scale = scale;
-  LAUNCH(mla::launch_decode_attn(a, (hipStream_t)stream), "decode_attn");
+  a.qlat = q_lat; a.cache = cache; a.cache_len = cache_len;
+  a.R = B; a.H = H; a.max_len = max_len; a.scale = scale;
+  a.splits = mla::decode_splits(B, H, max_len);
+  Carver c(ws);
+  if (a.splits == 1) {
+    a.olat = o_lat;
+  } else {
+    a.part = c.take((size_t)a.splits * B * H * 512 * 2);
+    a.lse = (float*)c.take((size_t)a.splits * B * H * 4);
+  }
+  LAUNCH(mla::launch_decode_attn(a, s), "decode_attn");
+  if (a.splits > 1) LAUNCH(mla::launch_decode_combine(a.part, a.lse, a.splits, (int64_t)B * H, o_lat, s), "combine");
   return MLA_OK;
 }
 

@@ -2,23 +2,28 @@
 // attention, "Explanation": a single decoded token scores the cached latent
 // directly; DeepSeek-V3.2-Exp · Output projection page at p = 1000).
 //
-// With kv_b's key half folded into the query, every head of sequence b scores
-// the same cache rows C_t = [latent 512 | rope key 64]:
+// With kv_b's key half folded into the query, every head of row q scores the
+// same cache rows C_t = [latent 512 | rope key 64]:
 //   z[h, t] = scale * (q_lat[h] . C_t),  o_lat[h] = sum_t softmax_t(z[h]) C_t[:512]
-// so one cache tile in LDS serves all heads of a workgroup.
+// so one cache tile in LDS serves every head of the row.
 //
-// Workgroup = (sequence b, group of 64 heads); the head groups of one
-// sequence are placed on the same XCD so the second read of the cache comes
-// from that XCD's L2. Cache tiles of 32 keys move HBM -> LDS with 16-byte
-// direct-to-LDS buffer loads through a 3-stage ring (two tiles in flight).
-// Wave (hb, dh) = (wave & 1, wave >> 1) serves heads 32hb..32hb+31:
-//   scores  S^T[t, h] = C[t, :] . Q^T[:, h]     each wave of a pair takes one half
-//           of the 576 contracted dims (its half of Q stays in registers) and
-//           the pair adds the two fp32 partials through LDS, in the same order;
-//   values  O^T[d, h] += C^T[d, t] . P^T[t, h]  for the wave's 256 latent dims,
-// both on v_mfma_f32_32x32x16_bf16 (C^T read with ds_read_b64_tr_b16). A lane's
-// score results are 16 keys of one head, which are exactly the k slots the
-// value product needs from P^T, so the probabilities stay in registers.
+// Workgroup = (row q, group of 128 heads, key split j): four waves, wave w
+// owns heads 32w..32w+31 of the group, so each cache row of the split is read
+// from HBM once for all 128 heads. The key range of a row is cut into
+// `splits` runs of whole 32-key tiles; with one split the workgroup writes the
+// normalised o_lat, otherwise its normalised partial and its log2-sum-exp,
+// which the consumer merges in split order (launch_decode_combine or the
+// un-absorb kernel). The splits of a row are placed on one XCD.
+//
+// Per tile, per wave (v_mfma_f32_32x32x16_bf16, fp32 accumulators):
+//   scores  S^T[t, h] = C[t, :] . Q^T[:, h]   36 k-steps over all 576 dims; the
+//           wave's 32 query columns stay in registers for the whole pass;
+//   values  O^T[d, h] += C^T[d, t] . P^T[t, h] for all 512 latent dims (C^T
+//           read with ds_read_b64_tr_b16). A lane's score results are 16 keys of
+//           one head, exactly the k slots the value product needs from P^T,
+//           so the probabilities stay in registers.
+// Cache tiles move HBM -> LDS with 16-byte direct-to-LDS buffer loads through
+// a 3-stage ring (two tiles in flight).
 //
 // Softmax: the running max of a head is fixed at its first live tile and
 // later tiles add exp2(z - m) <= 2^LAZY, so the accumulators are never
@@ -26,11 +31,20 @@
 // of ~44 nats) the workgroup recomputes its output in two passes: exact
 // maxima first, then the accumulation with those maxima.
 //
-// Selected keys: with an index list the workgroup first compacts the row's
-// live positions into LDS (ballot ranks, list order kept), padded with the
-// last one, and tile row r then loads cache row keys[k0 + r] instead of k0 + r;
-// everything after the loads is the dense path over nkeys = #live keys. The
-// same kernel serves a prefill in the absorbed form, one query row per token.
+// Selected keys: launch_decode_compact first turns each row's index list into
+// its ascending, duplicate-free list of live positions; the workgroup copies
+// its split's part of that list to LDS (padded with its last key) and tile row
+// r loads cache row keys[k0 + r]. The same kernel serves a prefill in the
+// absorbed form, one query row per token.
+//
+// e4m3 weights (QLAT): kv_b is an e4m3 Linear whose input, the latent, is
+// quantised in dynamic 1x128 groups (Kimi K2 · Down projection,
+// quantization_config). The absorbed product therefore sees each latent as
+// its dequantised value: once a tile has landed, the workgroup replaces every
+// latent 128-group of the tile in LDS by scale * e4m3(x / scale) (scale =
+// amax / 448 in fp32, quotient from the correctly rounded reciprocal plus one
+// residual correction), rounded to bf16. The rope key is not an input of kv_b
+// and is used as cached.
 //
 // LDS stage: latent rows [32][1024 B] then rope rows [32][128 B]. The 16-byte
 // chunks of latent row r are XOR-permuted within aligned groups of 16 by
@@ -50,6 +64,7 @@ constexpr int DROW = 576;               // elements per cache row
 constexpr int DLAT = DKT * 512;         // latent region of a stage (elements)
 constexpr int DSTAGE = DKT * DROW;      // elements per stage
 constexpr float LAZY = 64.f;            // log2-domain headroom over the fixed running max
+constexpr int KEYS_LDS = DECODE_TOPK_MAX + 4 * DKT;   // a split's keys plus the tiles issued past its end
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
@@ -62,56 +77,93 @@ __device__ __forceinline__ v4s read_tr(const uint16_t* p) {
 }
 
 struct DecodeCtx {
-  __amdgpu_buffer_rsrc_t rsrc;   // raw buffer over the cache rows of sequence b
-  int nkeys, ntiles, wave, lane, hi, dh;
+  __amdgpu_buffer_rsrc_t rsrc;   // raw buffer over the cache rows of the row's sequence
+  int k0, kend;                  // keys [k0, kend) of this split (dense: positions; sparse: list slots)
+  int ntiles, wave, lane, hi;
+  bool active;                   // the wave's heads exist
   float sl2;
-  float* xs;                     // [2][4 waves][16][64] partial-score exchange
-  bool sparse;                   // tile rows from `keys` (else keys 0..nkeys-1)
-  const __attribute__((address_space(3))) int* keys;   // compacted selected positions
+  bool sparse;
+  const __attribute__((address_space(3))) int* keys;   // split's selected positions (sparse)
 };
-
-constexpr int KEYS_LDS = DECODE_TOPK_MAX + 4 * DKT;   // room for the tiles issued past the end
 
 __device__ __forceinline__ void load_lds16(const DecodeCtx& c, uint16_t* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0,
                                            0);
 }
 
-// Loads tile kt into stage st (9 loads per thread): latent instruction i of
-// wave w fills row 8w + i (lane = physical chunk); the rope instruction of wave
-// w fills rows 8w..8w+7 (8 chunks each). Rows past the last key repeat it
-// (their scores are masked).
+// Loads tile kt of the split into stage st (9 loads per thread): latent
+// instruction i of wave w fills row 8w + i (lane = physical chunk); the rope
+// instruction of wave w fills rows 8w..8w+7 (8 chunks each). Rows past the
+// split's last key repeat it (their scores are masked).
 __device__ __forceinline__ void issue_tile(const DecodeCtx& c, uint16_t* st, int kt) {
-  const int k0 = kt * DKT;
-  if (c.sparse) {   // cache rows from the compacted list (entries past nkeys repeat the last key)
+  const int base = kt * DKT;
+  if (c.sparse) {   // list slots past the split's end hold its last key
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 8 * c.wave + i;
-      load_lds16(c, st + r * 512, (c.lane ^ swl(r)) << 4, __builtin_amdgcn_readfirstlane(c.keys[k0 + r]) * (DROW * 2));
+      load_lds16(c, st + r * 512, (c.lane ^ swl(r)) << 4,
+                 __builtin_amdgcn_readfirstlane(c.keys[base + r]) * (DROW * 2));
     }
     const int r = 8 * c.wave + (c.lane >> 3);
-    const int t = c.keys[k0 + r];
+    const int t = c.keys[base + r];
     load_lds16(c, st + DLAT + c.wave * 512, t * (DROW * 2) + 1024 + (((c.lane & 7) ^ swr(r)) << 4), 0);
     return;
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = 8 * c.wave + i;
-    const int t = min(k0 + r, c.nkeys - 1);
+    const int t = min(c.k0 + base + r, c.kend - 1);
     load_lds16(c, st + r * 512, (c.lane ^ swl(r)) << 4, t * (DROW * 2));
   }
   const int r = 8 * c.wave + (c.lane >> 3);
-  const int t = min(k0 + r, c.nkeys - 1);
+  const int t = min(c.k0 + base + r, c.kend - 1);
   load_lds16(c, st + DLAT + c.wave * 512, t * (DROW * 2) + 1024 + (((c.lane & 7) ^ swr(r)) << 4), 0);
 }
 
-// Partial scores of one tile over the wave's half of the contracted dims:
-// dh = 0 takes latent chunks 0..35, dh = 1 latent chunks 36..63 and the rope
-// chunks; chunk 2kk + hi meets query fragment kk.
-template <int DH>
-__device__ __forceinline__ floatx16 partial_scores(const uint16_t* st, int srow, int hi, const bf16x8 (&qf)[18]) {
+// e4m3 view of a tile's latent: thread (row r = tid / 8, group g = (tid / 2) % 4,
+// half hf = tid % 2) takes the 8 chunks 16 g + 8 hf .. + 7 of row r; the two
+// halves of a group are neighbouring lanes.
+__device__ __forceinline__ void quant_dequant_tile(uint16_t* st, int tid) {
+  const int r = tid >> 3, g = (tid >> 1) & 3, hf = tid & 1;
+  uint4 v[8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int ch = 8 * hf + i;   // chunk within the group's aligned 16
+    v[i] = *(const uint4*)(st + r * 512 + ((16 * g + (ch ^ swl(r))) << 3));
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[e] << 16)), fabsf(__uint_as_float(w[e] & 0xffff0000u))));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  const float s = amax / 448.0f;
+  const float rc = s != 0.f ? 1.0f / s : 0.f;
+  // x / s: q0 = x * rc (rc correctly rounded), then one residual step
+  auto quo = [&](float x) {
+    const float q0 = x * rc;
+    return __builtin_fmaf(__builtin_fmaf(-q0, s, x), rc, q0);
+  };
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xffff0000u);
+      const int code = __builtin_amdgcn_cvt_pk_fp8_f32(quo(x0), quo(x1), 0, false);
+      const float2v d = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
+      o[e] = pack_bf16x2(d[0] * s, d[1] * s);
+    }
+    const int ch = 8 * hf + i;
+    *(uint4*)(st + r * 512 + ((16 * g + (ch ^ swl(r))) << 3)) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// Scores of one tile over all 576 dims: chunk 2 kk + hi meets query fragment kk.
+__device__ __forceinline__ floatx16 tile_scores(const uint16_t* st, int srow, int hi, const bf16x8 (&qf)[36]) {
   auto frag = [&](int kk) {
-    const int c = 36 * DH + 2 * kk;   // + hi
+    const int c = 2 * kk;   // + hi
     if (c < 64) {
       const int f = swl(srow) ^ hi;
       return *(const bf16x8*)(st + srow * 512 + ((c & ~15) << 3) + (((c & 15) ^ f) << 3));
@@ -128,8 +180,8 @@ __device__ __forceinline__ floatx16 partial_scores(const uint16_t* st, int srow,
   }
   bf16x8 f0 = frag(0), f1 = frag(1), f2;
 #pragma unroll
-  for (int kk = 0; kk < 18; ++kk) {
-    if (kk + 2 < 18) f2 = frag(kk + 2);
+  for (int kk = 0; kk < 36; ++kk) {
+    if (kk + 2 < 36) f2 = frag(kk + 2);
     if (kk & 1) sb = mfma32(f0, qf[kk], sb);
     else sa = mfma32(f0, qf[kk], sa);
     f0 = f1;
@@ -138,15 +190,15 @@ __device__ __forceinline__ floatx16 partial_scores(const uint16_t* st, int srow,
   return sa + sb;
 }
 
-// One pass over the sequence. SCORES_ONLY: m becomes the exact per-head max.
+// One pass over the split. SCORES_ONLY: m becomes the exact per-head max.
 // Otherwise accumulates o and l against m (set at the first live tile when it
 // is -inf); returns true when a score exceeded m + LAZY (results invalid).
-template <bool SCORES_ONLY>
+template <bool SCORES_ONLY, bool QLAT>
 __device__ __forceinline__ bool attn_pass(const DecodeCtx& c, uint16_t* st0, uint16_t* st1, uint16_t* st2,
-                                          const bf16x8 (&qf)[18], float& m, float& l, floatx16 (&o)[8]) {
+                                          const bf16x8 (&qf)[36], float& m, float& l, floatx16 (&o)[16]) {
   const int lane = c.lane, l32 = lane & 31, hi = c.hi;
-  // transposed reads: 16-lane group q reads rows 16 s + 4 (q >> 1) + 8 e + (lane % 16) / 4,
-  // columns 256 dh + 32 dt + 16 (q & 1) + 4 (lane % 4)
+  // transposed reads: 16-lane group q4 reads rows 16 s + 4 (q4 >> 1) + 8 e + (lane % 16) / 4,
+  // columns 32 dt + 16 (q4 & 1) + 4 (lane % 4)
   const int q4 = lane >> 4, L = lane & 15;
   const int trow = 4 * (q4 >> 1) + (L >> 2);
   const int tx = 2 * (q4 & 1) + ((L >> 1) & 1);
@@ -156,40 +208,37 @@ __device__ __forceinline__ bool attn_pass(const DecodeCtx& c, uint16_t* st0, uin
 #pragma unroll
     for (int d4 = 0; d4 < 4; ++d4) {
       const int r = trow + 8 * e;
-      toff[e][d4] = r * 512 + 256 * c.dh + (((4 * d4 + tx) ^ swl(r)) << 3) + 4 * (L & 1);
+      toff[e][d4] = r * 512 + (((4 * d4 + tx) ^ swl(r)) << 3) + 4 * (L & 1);
     }
   bool over = false;
   if (!SCORES_ONLY) {
     l = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+    for (int dt = 0; dt < 16; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
   }
-  auto step = [&](int kt, const uint16_t* st, uint16_t* next) {
+  const int nk = c.kend - c.k0;
+  auto step = [&](int kt, uint16_t* st, uint16_t* next) {
     __asm__ volatile("s_waitcnt vmcnt(9)" ::: "memory");   // tile kt landed, kt + 1 may be in flight
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
     issue_tile(c, next, kt + 2);   // into the stage tile kt - 1 used
-
-    floatx16 sa = c.dh ? partial_scores<1>(st, l32, hi, qf) : partial_scores<0>(st, l32, hi, qf);
-    float* xw = c.xs + (kt & 1) * (4 * 16 * 64);
+    if (QLAT) {   // replace the landed tile's latent by its dequantised e4m3 value
+      quant_dequant_tile(st, 64 * c.wave + lane);
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // LDS writes only: the loads stay in flight
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+    }
+    if (!c.active) return;
+    floatx16 sa = tile_scores(st, l32, hi, qf);
+    const int kb = kt * DKT;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) xw[(c.wave * 16 + r) * 64 + lane] = sa[r];
-    // exchange barrier: LDS writes only (a __syncthreads here would also drain the tile loads)
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-    const int k0 = kt * DKT;
-    float part[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) part[r] = xw[((c.wave ^ 2) * 16 + r) * 64 + lane];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sa[r] = (c.dh ? part[r] + sa[r] : sa[r] + part[r]) * c.sl2;   // first + second half
-    if (k0 + DKT > c.nkeys) {   // wave-uniform: the tile runs past the last key
+    for (int r = 0; r < 16; ++r) sa[r] *= c.sl2;
+    if (kb + DKT > nk) {   // wave-uniform: the tile runs past the split's last key
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (k0 + row32(r, lane) >= c.nkeys) sa[r] = -INFINITY;
+        if (kb + row32(r, lane) >= nk) sa[r] = -INFINITY;
     }
     float mx = sa[0];
 #pragma unroll
@@ -210,26 +259,25 @@ __device__ __forceinline__ bool attn_pass(const DecodeCtx& c, uint16_t* st0, uin
       pf[r >> 3][r & 7] = (__bf16)p;
     }
     l += rs;
-    // value product, step j = (key half j / 8, d tile j % 8): consecutive MFMAs
-    // update different accumulators; C^T fragments read two steps ahead
+    // value product, step j = (key half j / 16, d tile j % 16); C^T fragments
+    // read two steps ahead
     auto vfrag = [&](int j) {
-      const int dt = j & 7, imm = 16 * (j >> 3) * 512 + 128 * (dt >> 2);
+      const int dt = j & 15, imm = 16 * (j >> 4) * 512 + 128 * (dt >> 2);
       const v4s lo = read_tr(st + toff[0][dt & 3] + imm), up = read_tr(st + toff[1][dt & 3] + imm);
       return __builtin_bit_cast(bf16x8, (v8s){lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
     };
     bf16x8 vb0 = vfrag(0), vb1 = vfrag(1), vb2;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j + 2 < 16) vb2 = vfrag(j + 2);
-      o[j & 7] = mfma32(vb0, pf[j >> 3], o[j & 7]);
+    for (int j = 0; j < 32; ++j) {
+      if (j + 2 < 32) vb2 = vfrag(j + 2);
+      o[j & 15] = mfma32(vb0, pf[j >> 4], o[j & 15]);
       vb0 = vb1;
       vb1 = vb2;
     }
   };
-  // The loop runs whole rounds of three tiles and always keeps two tiles in
-  // flight; tiles past the end hold copies of the last key (all masked, p = 0)
-  // and cost a little math. Straight-line rounds let the compiler's own LDS
-  // waits see which stage each load targets.
+  // Whole rounds of three tiles, two always in flight; tiles past the end hold
+  // copies of the last key (all masked, p = 0). Straight-line rounds let the
+  // compiler's own LDS waits see which stage each load targets.
   issue_tile(c, st0, 0);
   issue_tile(c, st1, 1);
   for (int kt = 0; kt < c.ntiles; kt += 3) {
@@ -238,78 +286,70 @@ __device__ __forceinline__ bool attn_pass(const DecodeCtx& c, uint16_t* st0, uin
     step(kt + 2, st2, st1);
   }
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();   // every wave is done with the stages and the exchange buffer
+  __syncthreads();   // every wave is done with the stages
   return over;
 }
 
-template <bool SPARSE>
+template <bool SPARSE, bool QLAT>
 __global__ __launch_bounds__(256, 1) void decode_attn_kernel(DecodeAttnArgs a, int n_hg) {
   __shared__ __attribute__((aligned(16))) uint16_t st0[DSTAGE];
   __shared__ __attribute__((aligned(16))) uint16_t st1[DSTAGE];
   __shared__ __attribute__((aligned(16))) uint16_t st2[DSTAGE];
-  __shared__ __attribute__((aligned(16))) float xs[2 * 4 * 16 * 64];
   __shared__ __attribute__((aligned(16))) int keys[SPARSE ? KEYS_LDS : 4];
-  __shared__ int wcount[4];
   __shared__ int s_over;
 
   const int tid = threadIdx.x;
+  const int NS = a.splits;
+  // workgroup -> (row q, head group hg, split j); all of a row's workgroups on one XCD
   const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
-  // query row q; its cache sequence b and last key P
-  const int hg = loc % n_hg, q = (loc / n_hg) * 8 + xcd;
-  if (q >= a.B) return;
-  const int b = SPARSE && a.rows_per_seq > 0 ? q / a.rows_per_seq : q;
-  const int P = SPARSE && a.rows_per_seq > 0 ? q - b * a.rows_per_seq : a.cache_len[b];
+  const int j = loc % NS, hg = (loc / NS) % n_hg, q = (loc / (NS * n_hg)) * 8 + xcd;
+  if (q >= a.R) return;
+  const int b = a.rows_per_seq > 0 ? q / a.rows_per_seq : q;
+  const int P = a.rows_per_seq > 0 ? q - b * a.rows_per_seq : a.cache_len[b];
+  const bool valid = P >= 0 && P < a.max_len;
   DecodeCtx c;
   c.lane = tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  c.dh = c.wave >> 1;
   c.hi = c.lane >> 5;
-  c.xs = xs;
   c.sl2 = a.scale * 1.4426950408889634f;
   c.sparse = SPARSE;
   c.keys = (const __attribute__((address_space(3))) int*)keys;
-  c.nkeys = (P >= 0 && P < a.max_len) ? P + 1 : 0;
-  if (SPARSE) {   // live listed positions t <= P, compacted in list order
-    const int32_t* row = a.idx + (int64_t)q * a.topk;
-    int base = 0;
-    for (int j0 = 0; j0 < a.topk; j0 += 256) {
-      const int j = j0 + tid;
-      const int t = j < a.topk ? row[j] : -1;
-      const bool ok = c.nkeys > 0 && t >= 0 && t <= P;
-      const uint64_t bal = __ballot(ok);
-      if (c.lane == 0) wcount[c.wave] = __popcll(bal);
-      __syncthreads();
-      int off = base;
-      for (int w = 0; w < c.wave; ++w) off += wcount[w];
-      if (ok) keys[off + __popcll(bal & ((1ull << c.lane) - 1))] = t;
-      base += wcount[0] + wcount[1] + wcount[2] + wcount[3];
-      __syncthreads();
-    }
-    c.nkeys = base;
-    const int last = base > 0 ? keys[base - 1] : 0;
-    for (int j = base + tid; j < KEYS_LDS; j += 256) keys[j] = last;
+  // the row's keys (positions 0..P, or its compacted list) cut into NS runs of whole tiles
+  const int n_all = !valid ? 0 : SPARSE ? a.nkeys[q] : P + 1;
+  const int tiles_all = (n_all + DKT - 1) / DKT, tps = (tiles_all + NS - 1) / NS;
+  c.k0 = min(n_all, j * tps * DKT);
+  c.kend = min(n_all, (j + 1) * tps * DKT);
+  if (SPARSE) {   // this split's slots of the compacted list, padded with its last key
+    const int32_t* row = a.keys + (int64_t)q * a.kstride;
+    const int n = c.kend - c.k0;
+    const int last = n > 0 ? row[c.kend - 1] : 0;
+    for (int i = tid; i < KEYS_LDS; i += 256) keys[i] = i < n ? row[c.k0 + i] : last;
+    c.k0 = 0;
+    c.kend = n;
     __syncthreads();
   }
-  c.ntiles = (c.nkeys + DKT - 1) / DKT;
+  c.ntiles = (c.kend - c.k0 + DKT - 1) / DKT;
   c.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.cache + (int64_t)b * a.max_len * DROW),
                                              (short)0, a.max_len * DROW * 2, BUF_DW3);
-  const int head = hg * 64 + (c.wave & 1) * 32 + (c.lane & 31);
+  const int head = hg * 128 + 32 * c.wave + (c.lane & 31);
+  c.active = hg * 128 + 32 * c.wave < a.H;
 
-  // this wave's half of the query: B operand of the score product, dims 288 dh + 16 kk + 8 hi + 0..7
-  bf16x8 qf[18];
+  // the wave's query: B operand of the score product, dims 16 kk + 8 hi + 0..7
+  bf16x8 qf[36];
   {
-    const uint16_t* qp = (const uint16_t*)a.qlat + ((int64_t)q * a.H + head) * DROW + 288 * c.dh + 8 * c.hi;
+    const uint16_t* qp = (const uint16_t*)a.qlat + ((int64_t)q * a.H + min(head, a.H - 1)) * DROW + 8 * c.hi;
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 16 * kk));
+    for (int kk = 0; kk < 36; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 16 * kk));
   }
   if (tid == 0) s_over = 0;
-  floatx16 o[8];
+  floatx16 o[16];
   float m = -INFINITY, l = 0.f;
   bool over = false;
-  if (c.ntiles > 0) over = attn_pass<false>(c, st0, st1, st2, qf, m, l, o);
-  else {
+  if (c.ntiles > 0) {
+    over = attn_pass<false, QLAT>(c, st0, st1, st2, qf, m, l, o);
+  } else {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+    for (int dt = 0; dt < 16; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
     __syncthreads();
@@ -318,65 +358,162 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(DecodeAttnArgs a, i
   __syncthreads();
   if (s_over) {   // rare: exact maxima, then accumulate against them (no score can exceed them)
     m = -INFINITY;
-    attn_pass<true>(c, st0, st1, st2, qf, m, l, o);
-    attn_pass<false>(c, st0, st1, st2, qf, m, l, o);
+    attn_pass<true, QLAT>(c, st0, st1, st2, qf, m, l, o);
+    attn_pass<false, QLAT>(c, st0, st1, st2, qf, m, l, o);
   }
-  // o_lat[b, head, 256 dh + 32 dt + 8 rg + 4 hi + 0..3]
+  if (!c.active) return;
+  // lane: head `head`, dims 32 dt + 8 rg + 4 hi + 0..3
   l += __shfl_xor(l, 32);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (a.oq) {
-    // e4m3 output: dims [256 dh + 128 g2, +128) are one group, held by this
-    // lane (dt = 4 g2 .. 4 g2 + 3) and lane ^ 32
-    const int64_t row = (int64_t)q * a.H + head;
+  const int64_t row = (int64_t)q * a.H + head;
+  uint16_t* out = NS == 1 ? (uint16_t*)a.olat + row * 512 : (uint16_t*)a.part + ((int64_t)j * a.R * a.H + row) * 512;
+  out += 4 * c.hi;
 #pragma unroll
-    for (int g2 = 0; g2 < 2; ++g2) {
-      float amax = 0.f;
-#pragma unroll
-      for (int dt = 4 * g2; dt < 4 * g2 + 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          o[dt][r] = __uint_as_float((uint32_t)f2bf(o[dt][r] * inv) << 16);
-          amax = fmaxf(amax, fabsf(o[dt][r]));
-        }
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
-      const float sc = amax / 448.0f;
-      uint8_t* oq = a.oq + row * 512 + 256 * c.dh + 4 * c.hi;
-#pragma unroll
-      for (int dt = 4 * g2; dt < 4 * g2 + 4; ++dt)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const float v0 = o[dt][4 * rg], v1 = o[dt][4 * rg + 1], v2 = o[dt][4 * rg + 2], v3 = o[dt][4 * rg + 3];
-          uint32_t code = 0u;
-          if (sc != 0.f)
-            code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
-                v2 / sc, v3 / sc, __builtin_amdgcn_cvt_pk_fp8_f32(v0 / sc, v1 / sc, 0, false), true);
-          *(uint32_t*)(oq + 32 * dt + 8 * rg) = code;
-        }
-      if (c.hi == 0) a.os[row * 4 + 2 * c.dh + g2] = sc;
-    }
-    return;
-  }
-  uint16_t* out = (uint16_t*)a.olat + ((int64_t)q * a.H + head) * 512 + 256 * c.dh + 4 * c.hi;
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+  for (int dt = 0; dt < 16; ++dt)
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg)
       *(uint2*)(out + 32 * dt + 8 * rg) = make_uint2(pack_bf16x2(o[dt][4 * rg] * inv, o[dt][4 * rg + 1] * inv),
                                                      pack_bf16x2(o[dt][4 * rg + 2] * inv, o[dt][4 * rg + 3] * inv));
+  if (NS > 1 && c.hi == 0) a.lse[(int64_t)j * a.R * a.H + row] = l > 0.f ? m + __log2f(l) : -INFINITY;
+}
+
+// One workgroup per row: the listed positions t with 0 <= t <= last key of the
+// row, ascending and without repeats. A list that is already ascending (after
+// invalid entries are dropped) skips the bitonic sort.
+__global__ __launch_bounds__(256) void decode_compact_kernel(const int32_t* __restrict__ idx, int topk,
+                                                             const int32_t* __restrict__ cache_len, int rows_per_seq,
+                                                             int max_len, int32_t* __restrict__ keys, int kstride,
+                                                             int32_t* __restrict__ nkeys) {
+  __shared__ int v[DECODE_TOPK_MAX];
+  __shared__ int wcount[4];
+  __shared__ int s_unsorted;
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = rows_per_seq > 0 ? q / rows_per_seq : q;
+  const int P = rows_per_seq > 0 ? q - b * rows_per_seq : cache_len[b];
+  const bool valid = P >= 0 && P < max_len;
+  int n2 = 1;
+  while (n2 < topk) n2 <<= 1;
+  const int32_t* src = idx + (int64_t)q * topk;
+  if (tid == 0) s_unsorted = 0;
+  for (int i = tid; i < n2; i += 256) {
+    const int t = i < topk ? src[i] : -1;
+    v[i] = valid && t >= 0 && t <= P ? t : INT_MAX;
+  }
+  __syncthreads();
+  bool uns = false;
+  for (int i = tid; i + 1 < n2; i += 256) uns |= v[i] > v[i + 1];
+  if (uns) s_unsorted = 1;
+  __syncthreads();
+  if (s_unsorted) {
+    for (int k = 2; k <= n2; k <<= 1)
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        for (int i = tid; i < n2; i += 256) {
+          const int ixj = i ^ jj;
+          if (ixj > i) {
+            const int x = v[i], y = v[ixj];
+            if ((x > y) == ((i & k) == 0)) {
+              v[i] = y;
+              v[ixj] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+  }
+  // keep the first of each run of equal live positions, in order
+  int32_t* dst = keys + (int64_t)q * kstride;
+  int base = 0;
+  for (int i0 = 0; i0 < n2; i0 += 256) {
+    const int i = i0 + tid;
+    const int x = i < n2 ? v[i] : INT_MAX;
+    const bool keep = x != INT_MAX && (i == 0 || v[i - 1] != x);
+    const uint64_t bal = __ballot(keep);
+    if (lane == 0) wcount[wave] = __popcll(bal);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wave; ++w) off += wcount[w];
+    if (keep) dst[off + __popcll(bal & ((1ull << lane) - 1))] = x;
+    base += wcount[0] + wcount[1] + wcount[2] + wcount[3];
+    __syncthreads();
+  }
+  if (tid == 0) nkeys[q] = base;
+}
+
+// o_lat[r] = sum_j w_j part[j][r] / sum_j w_j with w_j = exp2(lse[j][r] - max_j lse), in split order
+// (rows with every lse = -inf get 0). One thread per 8 dims of a row.
+__global__ __launch_bounds__(256) void decode_combine_kernel(const uint16_t* __restrict__ part,
+                                                             const float* __restrict__ lse, int splits, int64_t rows,
+                                                             uint16_t* __restrict__ olat) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = i >> 6;
+  if (r >= rows) return;
+  const int c8 = (int)(i & 63) * 8;
+  float mx = -INFINITY;
+  for (int j = 0; j < splits; ++j) mx = fmaxf(mx, lse[j * rows + r]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, den = 0.f;
+  if (mx != -INFINITY) {
+    for (int j = 0; j < splits; ++j) {
+      const float w = __builtin_amdgcn_exp2f(lse[j * rows + r] - mx);
+      den += w;
+      const uint4 u = *(const uint4*)(part + ((int64_t)j * rows + r) * 512 + c8);
+      const uint32_t p[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += w * __uint_as_float(p[e] << 16);
+        acc[2 * e + 1] += w * __uint_as_float(p[e] & 0xffff0000u);
+      }
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  *(uint4*)(olat + r * 512 + c8) = make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                                              pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                                              pack_bf16x2(acc[4] * inv, acc[5] * inv),
+                                              pack_bf16x2(acc[6] * inv, acc[7] * inv));
 }
 
 }  // namespace
 
+int decode_splits(int rows, int H, int max_keys) {
+  const int n_hg = (H + 127) / 128;
+  const int wgs = rows * n_hg;
+  int ns = wgs >= 256 ? 1 : (256 + wgs - 1) / wgs;
+  const int tiles = (max_keys + DKT - 1) / DKT;
+  const int cap = tiles / 4 > 1 ? tiles / 4 : 1;   // at least ~4 tiles per split
+  if (ns > cap) ns = cap;
+  if (ns > DECODE_MAX_SPLITS) ns = DECODE_MAX_SPLITS;
+  return ns;
+}
+
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s) {
-  const int n_hg = a.H / 64;
-  const unsigned grid = 8u * (unsigned)((a.B + 7) / 8) * (unsigned)n_hg;
-  if (a.idx) {
-    if (a.topk <= 0 || a.topk > DECODE_TOPK_MAX || a.rows_per_seq < 0) return hipErrorInvalidValue;
-    decode_attn_kernel<true><<<grid, 256, 0, s>>>(a, n_hg);
+  const int n_hg = (a.H + 127) / 128;
+  if (a.splits < 1 || a.splits > DECODE_MAX_SPLITS || (a.splits > 1 && (!a.part || !a.lse)) ||
+      (a.splits == 1 && !a.olat))
+    return hipErrorInvalidValue;
+  const unsigned grid = 8u * (unsigned)((a.R + 7) / 8) * (unsigned)n_hg * (unsigned)a.splits;
+  if (a.keys) {
+    if (!a.nkeys || a.kstride < 0 || a.kstride > DECODE_TOPK_MAX) return hipErrorInvalidValue;
+    if (a.quant_latent) decode_attn_kernel<true, true><<<grid, 256, 0, s>>>(a, n_hg);
+    else decode_attn_kernel<true, false><<<grid, 256, 0, s>>>(a, n_hg);
   } else {
     if (a.rows_per_seq != 0) return hipErrorInvalidValue;
-    decode_attn_kernel<false><<<grid, 256, 0, s>>>(a, n_hg);
+    if (a.quant_latent) decode_attn_kernel<false, true><<<grid, 256, 0, s>>>(a, n_hg);
+    else decode_attn_kernel<false, false><<<grid, 256, 0, s>>>(a, n_hg);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_compact(const int32_t* idx, int topk, const int32_t* cache_len, int rows_per_seq, int rows,
+                                 int max_len, int32_t* keys, int kstride, int32_t* nkeys, hipStream_t s) {
+  if (topk <= 0 || topk > DECODE_TOPK_MAX || kstride < topk) return hipErrorInvalidValue;
+  decode_compact_kernel<<<rows, 256, 0, s>>>(idx, topk, cache_len, rows_per_seq, max_len, keys, kstride, nkeys);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_combine(const void* part, const float* lse, int splits, int64_t rows, void* olat,
+                                 hipStream_t s) {
+  const int64_t threads = rows * 64;
+  decode_combine_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>((const uint16_t*)part, lse, splits, rows,
+                                                                         (uint16_t*)olat);
   return hipGetLastError();
 }
 

@@ -187,3 +187,170 @@ hipError_t launch_decode_absorb(const void* q, const void* wkv_b, const float* w
 }
 
 }  // namespace mla
+
+// ---------------------------------------------------------------------------
+// Value un-absorption of the latent-space decode step:
+//   o[b, 128 h + j] = sum_c W_UV_h[j, c] o_lat[b, h, c]    (W_UV_h = Wkv_b rows [256h + 128, 256h + 256))
+// with o_lat merged here from the attention's per-split partials:
+//   o_lat = sum_s w_s part_s / sum_s w_s,  w_s = exp2(lse_s - max_s lse_s)   (split order)
+// (splits == 1: o_lat is read as is). With e4m3 weights the product is the
+// block-scaled one of the dequantised weight: W_UV_h's codes are expanded
+// exactly to bf16 and the block scale of column group g = c / 128 is folded
+// into o_lat's group g before it is rounded to bf16 for the MFMA.
+//
+// One 256-thread workgroup per (head h, block of 64 rows b); wave w takes
+// rows 16w..16w+15 and all 128 j on v_mfma_f32_16x16x32_bf16 (W_UV_h as the
+// first operand, so a lane's results are 4 consecutive j of one row). W_UV_h
+// [128 j, 512 c] sits in LDS as bf16 (128 KB), 16-byte chunk ch of row j at
+// chunk ch ^ (j & 15) of the row. Outputs: o in bf16 and, for an e4m3 wo, o's
+// codes and its scale per (row, head) (one 1x128 group), quantised from the
+// bf16 values.
+namespace mla {
+namespace {
+
+__global__ __launch_bounds__(256, 1) void decode_unabsorb_kernel(UnabsorbArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sw[128 * 512];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, b0 = blockIdx.y * 64;
+  const int H = a.H;
+  const bool fp8 = a.w_scale != nullptr;
+  if (fp8) {   // codes -> bf16 -> LDS: 16-byte piece i of the thread = row j, codes 16 cc .. 16 cc + 15
+    const uint8_t* W8 = (const uint8_t*)a.wkv_b + ((int64_t)256 * h + 128) * 512;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int idx = tid + 256 * i, j = idx >> 5, cc = idx & 31;
+      const uint4 v = *(const uint4*)(W8 + (int64_t)j * 512 + 16 * cc);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float2v lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[e], false);
+        const float2v up = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[e], true);
+        o[2 * e] = pack_bf16x2(lo[0], lo[1]);
+        o[2 * e + 1] = pack_bf16x2(up[0], up[1]);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int ch = 2 * cc + half;
+        *(uint4*)(sw + j * 512 + ((ch ^ (j & 15)) << 3)) =
+            make_uint4(o[4 * half], o[4 * half + 1], o[4 * half + 2], o[4 * half + 3]);
+      }
+    }
+  } else {   // bf16 rows straight to LDS: load i of wave w fills row j = 4 i + w (one 1 KB row)
+    const uint16_t* W = (const uint16_t*)a.wkv_b + ((int64_t)256 * h + 128) * 512;
+#pragma unroll 8
+    for (int i = 0; i < 32; ++i) {
+      const int j = 4 * i + wave, ch = lane;   // lane fills physical chunk `lane`
+      __builtin_amdgcn_global_load_lds(W + (int64_t)j * 512 + ((ch ^ (j & 15)) << 3), sw + j * 512, 16, 0, 0);
+    }
+  }
+
+  // this lane's row for the B operand: b = b0 + 16 wave + lane % 16, k chunk lane / 16
+  const int g4 = lane >> 4, L = lane & 15;
+  const int bq = b0 + 16 * wave + L;
+  const bool row_ok = bq < a.B;
+  const int64_t rh = (int64_t)min(bq, a.B - 1) * H + h;
+  const int64_t rows = (int64_t)a.B * H;
+  // split weights exp2(lse_s - max) are recomputed where used (no indexed register array)
+  float mx = -INFINITY, den = 0.f;
+  if (a.splits > 1) {
+    for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.lse[s * rows + rh]);
+    if (mx != -INFINITY)
+      for (int s = 0; s < a.splits; ++s) den += __builtin_amdgcn_exp2f(a.lse[s * rows + rh] - mx);
+  }
+  const float inv = a.splits > 1 ? (den > 0.f ? 1.f / den : 0.f) : 1.f;
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // W_UV_h landed in LDS (direct loads)
+  __syncthreads();
+
+  floatx4 acc[8];
+#pragma unroll
+  for (int jt = 0; jt < 8; ++jt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[jt][r] = 0.f;
+  const uint16_t* part = (const uint16_t*)a.part;
+#pragma unroll 2
+  for (int ks = 0; ks < 16; ++ks) {
+    const int c0 = 32 * ks + 8 * g4;   // the 8 columns of this lane's k slots
+    float f[8];
+    if (a.splits == 1) {
+      const uint4 u = *(const uint4*)(part + rh * 512 + c0);
+      const uint32_t p[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[2 * e] = __uint_as_float(p[e] << 16);
+        f[2 * e + 1] = __uint_as_float(p[e] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = 0.f;
+      if (mx != -INFINITY)
+        for (int s = 0; s < a.splits; ++s) {
+          const float ws = __builtin_amdgcn_exp2f(a.lse[s * rows + rh] - mx);
+          const uint4 u = *(const uint4*)(part + (s * rows + rh) * 512 + c0);
+          const uint32_t p[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            f[2 * e] += ws * __uint_as_float(p[e] << 16);
+            f[2 * e + 1] += ws * __uint_as_float(p[e] & 0xffff0000u);
+          }
+        }
+    }
+    float sc = inv;
+    if (fp8) sc *= a.w_scale[(int64_t)(2 * h + 1) * 4 + (c0 >> 7)];
+    const bf16x8 bfr = __builtin_bit_cast(
+        bf16x8, make_uint4(pack_bf16x2(f[0] * sc, f[1] * sc), pack_bf16x2(f[2] * sc, f[3] * sc),
+                           pack_bf16x2(f[4] * sc, f[5] * sc), pack_bf16x2(f[6] * sc, f[7] * sc)));
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) {
+      const int j = 16 * jt + L, ch = 4 * ks + g4;
+      const bf16x8 wfr = *(const bf16x8*)(sw + j * 512 + ((ch ^ (j & 15)) << 3));
+      acc[jt] = mfma16(wfr, bfr, acc[jt]);
+    }
+  }
+  if (!row_ok) return;
+  // lane: row bq, j = 16 jt + 4 g4 + 0..3
+  uint16_t* o = a.o ? (uint16_t*)a.o + (int64_t)bq * a.ldo + 128 * h + 4 * g4 : nullptr;
+  float v[8][4];
+  float amax = 0.f;
+#pragma unroll
+  for (int jt = 0; jt < 8; ++jt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[jt][r] = __uint_as_float((uint32_t)f2bf(acc[jt][r]) << 16);
+      amax = fmaxf(amax, fabsf(v[jt][r]));
+    }
+  if (o) {
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt)
+      *(uint2*)(o + 16 * jt) = make_uint2(pack_bf16x2(v[jt][0], v[jt][1]), pack_bf16x2(v[jt][2], v[jt][3]));
+  }
+  if (a.oq) {   // one 1x128 group per (row, head): lanes L, L + 16, L + 32, L + 48 hold it
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const float sc = amax / 448.0f;
+    uint8_t* q = a.oq + (int64_t)bq * a.ldo + 128 * h + 4 * g4;
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) {
+      uint32_t code = 0u;
+      if (sc != 0.f)
+        code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+            v[jt][2] / sc, v[jt][3] / sc, __builtin_amdgcn_cvt_pk_fp8_f32(v[jt][0] / sc, v[jt][1] / sc, 0, false),
+            true);
+      *(uint32_t*)(q + 16 * jt) = code;
+    }
+    if (g4 == 0) a.os[(int64_t)bq * (a.ldo / 128) + h] = sc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_unabsorb(const UnabsorbArgs& a, hipStream_t s) {
+  if (a.splits < 1 || a.splits > DECODE_MAX_SPLITS || (a.splits > 1 && !a.lse) || a.ldo % 128 ||
+      (!a.o && !a.oq) || (a.oq && !a.os))
+    return hipErrorInvalidValue;
+  dim3 grid(a.H, (a.B + 63) / 64);
+  decode_unabsorb_kernel<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -191,25 +191,53 @@ hipError_t launch_prefill_attn_bf16(const PrefillAttnArgs& a, hipStream_t s);
 hipError_t launch_prefill_attn_f32(const PrefillAttnArgs& a, hipStream_t s);
 
 // Decode pieces.
-struct DecodeAttnArgs {
-  const void* qlat;      // [B, H, 576] bf16: absorbed query (512) | rotated q_pe (64)
-  const void* cache;     // [B, max_len, 576] bf16 (with rows_per_seq: [B / rows_per_seq, max_len, 576])
-  const int32_t* cache_len;
-  void* olat;            // [B, H, 512] bf16
-  int B, H, max_len; float scale;
-  // Selected keys (optional): row q attends only the positions listed in
-  // idx[q*topk .. q*topk + topk) (distinct; -1 and positions past the row's
-  // last key are ignored), topk <= DECODE_TOPK_MAX. rows_per_seq > 0 (only with
-  // idx): query row q is token q % rows_per_seq of sequence q / rows_per_seq,
-  // its last key that position (prefill); else row q is sequence q with last
-  // key cache_len[q] (decode).
-  const int32_t* idx; int topk; int rows_per_seq;
-  // optional: o_lat as e4m3 codes [B*H, 512] with 1x128 scales [B*H, 4],
-  // quantised from its bf16 values, instead of olat
-  uint8_t* oq; float* os;
-};
 constexpr int DECODE_TOPK_MAX = 2048;
+constexpr int DECODE_MAX_SPLITS = 16;
+// Latent-space attention, one query row q at a time over cache rows C_t =
+// [latent 512 | rope 64] (bf16): o_lat[q, h] = sum_t softmax_t(scale * q_lat[q, h] . C_t) C_t[:512].
+struct DecodeAttnArgs {
+  const void* qlat;      // [R, H, 576] bf16: absorbed query (512) | rotated q_pe (64)
+  const void* cache;     // [S, max_len, 576] bf16
+  const int32_t* cache_len;   // decode: row q is sequence q with last key cache_len[q]
+  int R, H, max_len; float scale;
+  // rows_per_seq > 0 (selected keys only): row q is token q % rows_per_seq of
+  // sequence q / rows_per_seq, its last key that position (absorbed prefill)
+  int rows_per_seq;
+  // Selected keys (optional): the compacted lists launch_decode_compact makes,
+  // row q's live positions keys[q*kstride .. + nkeys[q]) (ascending, distinct)
+  const int32_t* keys; const int32_t* nkeys; int kstride;
+  // The row's keys are cut into `splits` runs of whole 32-key tiles. splits == 1:
+  // olat [R, H, 512] bf16 is the normalised output. splits > 1: part
+  // [splits][R*H][512] bf16 holds each run's normalised output and lse
+  // [splits][R*H] its log2-sum-exp of the scaled scores (-inf for an empty run).
+  int splits;
+  void* olat; void* part; float* lse;
+  // e4m3 kv_b: every latent enters as its dequantised 1x128 e4m3 value
+  bool quant_latent;
+};
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s);
+// Splits that fill the chip for `rows` query rows of H heads over at most
+// max_keys keys (at most DECODE_MAX_SPLITS, about four tiles or more each).
+int decode_splits(int rows, int H, int max_keys);
+// keys[q*kstride ..] = row q's listed positions t with 0 <= t <= last(q) (last(q) =
+// q % rows_per_seq when rows_per_seq > 0, else cache_len[q]; rows with
+// last(q) outside [0, max_len) get none), ascending, repeats removed;
+// nkeys[q] = their number. idx [rows, topk] with topk <= DECODE_TOPK_MAX; kstride >= topk.
+hipError_t launch_decode_compact(const int32_t* idx, int topk, const int32_t* cache_len, int rows_per_seq, int rows,
+                                 int max_len, int32_t* keys, int kstride, int32_t* nkeys, hipStream_t s);
+// olat[r] from the split partials of launch_decode_attn, merged in split order (rows = R*H).
+hipError_t launch_decode_combine(const void* part, const float* lse, int splits, int64_t rows, void* olat,
+                                 hipStream_t s);
+// o[b, 128 h + j] = sum_c W_UV_h[j, c] o_lat[b, h, c] (W_UV_h = wkv_b rows [256h + 128, 256h + 256),
+// kv_lora_rank 512), o_lat merged from the attention's split partials (splits == 1: part = o_lat).
+struct UnabsorbArgs {
+  const void* part; const float* lse; int splits;   // as DecodeAttnArgs (rows B*H)
+  const void* wkv_b; const float* w_scale;          // bf16, or e4m3 codes with block scales [2H, 4]
+  void* o; int64_t ldo;                             // o [B, ldo] bf16 (ldo = H*128), or NULL
+  uint8_t* oq; float* os;                           // or/and e4m3 codes [B, ldo] + scales [B, ldo/128]
+  int B, H;
+};
+hipError_t launch_decode_unabsorb(const UnabsorbArgs& a, hipStream_t s);
 // q_lat[b, h] = [q_nope[b, h] . W_UK_h | RoPE(q_pe[b, h], cache_len[b])] for kv_lora_rank 512;
 // q [B, H*192], wkv_b [H*256, 512] (bf16, or e4m3 codes with block scales
 // w_scale [2H, 4]; w_scale == nullptr for bf16), qlat [B, H, 576].

@@ -129,7 +129,7 @@ class PrefillAbsorbed:
         self.topk = to_dev(inp["topk_idx"], torch.int32, device)
         self.out = torch.empty_like(self.x)
         self.kv_cache = torch.empty((B, T, cfg["kv_lora_rank"] + 64), dtype=torch.bfloat16, device=device)
-        self.ws = api.workspace(api.mla_prefill_absorbed_workspace_size(self.dims, B, T), device)
+        self.ws = api.workspace(api.mla_prefill_absorbed_workspace_size(self.dims, B, T, self.topk.shape[-1]), device)
 
     def run(self, stream=None):
         return api.mla_prefill_absorbed(self.dims, self.weights, self.x, self.cos, self.sin, self.topk, self.out,

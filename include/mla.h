@@ -152,7 +152,8 @@ MLA_API int mla_prefill_cached(const mla_dims* dims, const mla_weights* w, const
                        const float* rope_sin, int32_t rope_len, const int32_t* topk_idx, int32_t topk, void* out,
                        void* ws, size_t ws_bytes, void* stream);
 
-/* Bytes of workspace mla_decode needs for bf16 or e4m3 weights (0 on invalid input). */
+/* Bytes of workspace mla_decode and mla_decode_sparse need for bf16 or e4m3
+ * weights (0 on invalid input). */
 MLA_API size_t mla_decode_workspace_size(const mla_dims* dims, int32_t weight_dtype, int32_t B, int32_t max_len);
 
 /* Single-token MLA decode, latent-absorbed (DeepSeek-V3.2-Exp · Sparse
@@ -168,15 +169,20 @@ MLA_API size_t mla_decode_workspace_size(const mla_dims* dims, int32_t weight_dt
  *   cache_len [B] int32 DEVICE array, 0 <= cache_len[b] < max_len (checked on
  *             the device: an out-of-range sequence is skipped and its output
  *             row is set to zero)
+ *   max_len   <= 2^20 (MLA_INVALID_ARG otherwise)
  *   rope_cos, rope_sin  fp32 [rope_len, 32], rope_len >= max_len
  *   out       [B, dim] bf16
  * Weights bf16, or e4m3 with 128x128 block scales (Kimi K2 · Down projection,
  * quantization_config: e4m3, dynamic activation scheme, 128x128 weight
- * blocks): then the inputs of q_a|kv_a, q_b, W_UV and wo are quantised in
- * dynamic 1x128 groups as in prefill, and the absorbed key half uses the
- * dequantised W_UK with the bf16 query. Needs kv_lora_rank = 512, n_heads a
+ * blocks). With e4m3 every Linear is applied as prefill applies it: the
+ * inputs of q_a|kv_a, q_b and wo are quantised in dynamic 1x128 groups, and
+ * kv_b acts on each cached latent quantised in 1x128 groups; the absorbed
+ * form reaches that result with the dequantised W_UK and W_UV and each
+ * latent's dequantised 1x128 value. Needs kv_lora_rank = 512, n_heads a
  * multiple of 64, dim and q_lora_rank multiples of 128 for e4m3, and 16-byte
- * aligned norm weights and cache (MLA_UNSUPPORTED otherwise). */
+ * aligned x, out, cache and norm weights (MLA_UNSUPPORTED otherwise). The
+ * key range of each sequence may be cut into several runs whose partial
+ * results are merged in a fixed order, so results are deterministic. */
 MLA_API int mla_decode(const mla_dims* dims, const mla_weights* w, const void* x, int32_t B,
                void* kv_cache, int32_t max_len, const int32_t* cache_len,
                const float* rope_cos, const float* rope_sin, int32_t rope_len,
@@ -236,15 +242,23 @@ MLA_API int mla_prefill_attention(const void* q, const void* k_nope, const void*
                                   const uint32_t* mask, void* out, int32_t dtype, int32_t B, int32_t T,
                                   int32_t H, float scale, void* stream);
 
+/* Bytes of workspace mla_decode_attention needs (0 on invalid input): the
+ * per-run partial outputs when the key range of a sequence is cut into runs. */
+MLA_API size_t mla_decode_attention_workspace_size(int32_t B, int32_t H, int32_t max_len);
+
 /* The absorbed decode attention step alone (DeepSeek-V3.2-Exp · Sparse
  * attention, "Explanation"): for each sequence b and head h,
  *   o_lat[b, h] = sum_{t <= cache_len[b]} softmax_t(scale * q_lat[b, h] . C[b, t]) C[b, t, :512]
  *   q_lat [B, H, 576] bf16 (latent-space query 512 | rotated q_pe 64)
- *   cache [B, max_len, 576] bf16; cache_len [B] int32 device array
+ *   cache [B, max_len, 576] bf16; cache_len [B] int32 device array; max_len <= 2^20
  *   o_lat [B, H, 512] bf16 (zero for sequences whose cache_len is out of range)
- * H must be a multiple of 64. */
+ *   ws, ws_bytes  workspace of at least mla_decode_attention_workspace_size(B, H,
+ *   max_len) bytes, 256-byte aligned (partial results of the key runs, merged
+ *   in a fixed order)
+ * H must be a multiple of 64; q_lat, cache and o_lat 16-byte aligned. */
 MLA_API int mla_decode_attention(const void* q_lat, const void* cache, const int32_t* cache_len, void* o_lat,
-                                 int32_t B, int32_t H, int32_t max_len, float scale, void* stream);
+                                 int32_t B, int32_t H, int32_t max_len, float scale, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /* cos/sin table for RoPE: cos_tab[p, d] = cos(p * base^(-d/32)), sin likewise,
  * for p < n_pos, d < 32, evaluated in fp64 and stored fp32. */
@@ -278,8 +292,10 @@ MLA_API int mla_topk_to_bitmask(const int32_t* topk_idx, int32_t B, int32_t T, i
  * attends only the positions listed in topk_idx[b, 0:topk] that are <= its new
  * position cache_len[b] (the new token's own slot must be listed to be
  * attended).
- *   topk_idx [B, topk] int32 DEVICE array, distinct positions per row, -1 pads
- *            (a repeated position would be counted once per occurrence)
+ *   topk_idx [B, topk] int32 DEVICE array of positions, -1 pads; entries
+ *            outside [0, cache_len[b]] are ignored and a repeated position
+ *            counts once (the selection is a set, as a 0 / -inf mask makes it),
+ *            in any order
  *   1 <= topk <= 2048 (MLA_UNSUPPORTED otherwise). Workspace as mla_decode. */
 MLA_API int mla_decode_sparse(const mla_dims* dims, const mla_weights* w, const void* x, int32_t B,
                       void* kv_cache, int32_t max_len, const int32_t* cache_len, const int32_t* topk_idx,
@@ -287,7 +303,7 @@ MLA_API int mla_decode_sparse(const mla_dims* dims, const mla_weights* w, const 
                       void* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace mla_prefill_absorbed needs (0 on invalid input). */
-MLA_API size_t mla_prefill_absorbed_workspace_size(const mla_dims* dims, int32_t B, int32_t T);
+MLA_API size_t mla_prefill_absorbed_workspace_size(const mla_dims* dims, int32_t B, int32_t T, int32_t topk);
 
 /* Prefill with a top-k selection computed in the absorbed latent form
  * (DeepSeek-V3.2-Exp · Sparse attention: the same scores, selection and causal
@@ -296,11 +312,12 @@ MLA_API size_t mla_prefill_absorbed_workspace_size(const mla_dims* dims, int32_t
  * gathers only its selected cache entries [normalised latent | rotated k_pe]
  * (all heads share them), and the value half is applied after the attention.
  * The work per token is proportional to topk instead of its position.
- *   x [B, T, dim] bf16, bf16 weights, kv_lora_rank = 512, n_heads a multiple of 64
- *   topk_idx [B, T, topk] int32 DEVICE array (required), distinct per row, -1 pads;
- *            key t is live for query s iff t <= s and t is listed; 1 <= topk <= 2048
+ *   x [B, T, dim] bf16 (16-byte aligned), bf16 weights, kv_lora_rank = 512, n_heads a multiple of 64
+ *   topk_idx [B, T, topk] int32 DEVICE array (required), -1 pads, any order;
+ *            key t is live for query s iff t <= s and t is listed (a repeated
+ *            position counts once); 1 <= topk <= 2048
  *   out [B, T, dim] bf16; kv_cache_out [B, T, kv_lora_rank + 64] bf16 or NULL
- * Workspace: mla_prefill_absorbed_workspace_size bytes, 256-byte aligned. */
+ * Workspace: mla_prefill_absorbed_workspace_size(dims, B, T, topk) bytes, 256-byte aligned. */
 MLA_API int mla_prefill_absorbed(const mla_dims* dims, const mla_weights* w, const void* x, int32_t B, int32_t T,
                          const float* rope_cos, const float* rope_sin, int32_t rope_len,
                          const int32_t* topk_idx, int32_t topk, void* out, void* kv_cache_out, void* ws,

@@ -86,8 +86,18 @@ def test_workspace_sizes(lib):
     assert api.mla_prefill_workspace_size(bad, api.MLA_BF16, api.MLA_BF16, 1, 16, 0) == 0
     dd = api.make_dims(7168, 1536, 512, 128)
     db = api.mla_decode_workspace_size(dd, api.MLA_BF16, 128, 1024)
-    # e4m3 adds the quantised activation of the widest projection input, o_lat [128*128, 512]
-    assert api.mla_decode_workspace_size(dd, api.MLA_E4M3, 128, 1024) >= db + 128 * 128 * 512 * (1 + 4 / 128)
+    # 128 sequences x 128 heads fill half the chip per key run, so the attention
+    # cuts each sequence's keys into two runs: two bf16 partials of o_lat + their lse
+    runs = 2 * 128 * 128 * 512 * 2 + 2 * 128 * 128 * 4
+    assert db >= runs + 128 * 128 * 576 * 2 + 128 * 2048 * 4   # + q_lat + compacted selections
+    # one run when the rows fill the chip by themselves
+    assert api.mla_decode_attention_workspace_size(512, 128, 1024) == 256
+    assert api.mla_decode_attention_workspace_size(128, 128, 1024) >= runs
+    # e4m3 weights with 256 heads: wo's K = 32768 runs in 8 K chunks, and the
+    # partial buffer holds all of them (8 x 128 rows x 7168 fp32)
+    d256 = api.make_dims(7168, 1536, 512, 256)
+    e256 = api.mla_decode_workspace_size(d256, api.MLA_E4M3, 128, 1024)
+    assert e256 >= 8 * 128 * 7168 * 4 + 128 * 256 * 576 * 2
     assert api.mla_decode_workspace_size(d, api.MLA_F32, 4, 16) == 0
 
 
@@ -133,14 +143,25 @@ def test_decode_argument_errors(hostonly):
     d = api.make_dims(7168, 1536, 512, 128)
     w = api.MlaWeights(api.MLA_BF16, *[fake(i + 1) for i in range(12)])
 
-    def call(B=4, max_len=16, rl=16, cl=fake(), wsb=1 << 40, dd=d):
-        return lib.mla_decode(ctypes.byref(dd), ctypes.byref(w), fake(), B, fake(), max_len, cl, fake(), fake(), rl,
+    def call(B=4, max_len=16, rl=16, cl=fake(), wsb=1 << 40, dd=d, cache=fake()):
+        return lib.mla_decode(ctypes.byref(dd), ctypes.byref(w), fake(), B, cache, max_len, cl, fake(), fake(), rl,
                               fake(), fake(), wsb, None)
     assert call(cl=None) == api.MLA_INVALID_ARG
     assert call(rl=8) == api.MLA_INVALID_ARG
     assert call(wsb=10) == api.MLA_INVALID_ARG
     assert call(dd=api.make_dims(7168, 1536, 256, 128)) == api.MLA_UNSUPPORTED
     assert call(dd=api.make_dims(7168, 1536, 512, 100)) == api.MLA_UNSUPPORTED
+    # a cache that is not 16-byte aligned, and one too long for the 32-bit buffer range
+    assert call(cache=ctypes.c_void_p(0x1008)) == api.MLA_UNSUPPORTED and "aligned" in api.mla_last_error()
+    assert call(max_len=(1 << 20) + 1, rl=(1 << 20) + 1) == api.MLA_INVALID_ARG and "max_len" in api.mla_last_error()
+    # the attention step alone: the same bounds, plus its own workspace
+    att = lambda q=fake(), cache=fake(), ml=16, wsb=1 << 40, H=128: lib.mla_decode_attention(
+        q, cache, fake(), fake(), 4, H, ml, 0.07, fake(), wsb, None)
+    assert att(q=ctypes.c_void_p(0x1004)) == api.MLA_UNSUPPORTED
+    assert att(cache=ctypes.c_void_p(0x1008)) == api.MLA_UNSUPPORTED
+    assert att(ml=(1 << 20) + 1) == api.MLA_INVALID_ARG
+    assert att(H=96) == api.MLA_UNSUPPORTED
+    assert att(wsb=10, ml=4096) == api.MLA_INVALID_ARG and "workspace" in api.mla_last_error()
 
 
 def test_building_block_argument_errors(hostonly):
@@ -194,7 +215,7 @@ def test_widened_entry_point_argument_errors(hostonly):
     assert absorbed(k=4096) == api.MLA_UNSUPPORTED
     assert absorbed(rl=8) == api.MLA_INVALID_ARG
     assert absorbed(dims=api.make_dims(7168, 1536, 512, 100)) == api.MLA_UNSUPPORTED
-    assert api.mla_prefill_absorbed_workspace_size(dd, 1, 16) > 0
+    assert api.mla_prefill_absorbed_workspace_size(dd, 1, 16, 8) > 0
 
     def mlp(hidden=128, inter=128, x=fake(), wsb=1 << 40):
         return lib.mla_swiglu_mlp(x, 4, hidden, inter, fake(), fake(), fake(), fake(), fake(), wsb, None)

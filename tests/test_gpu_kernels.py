@@ -202,6 +202,65 @@ def test_decode_attention_step():
         assert_parity(got[b], ref, what=f"decode attention b={b}")
 
 
+@pytest.mark.parametrize("B,H,max_len,lens", [(1, 128, 4100, [4099]), (2, 64, 1100, [1000, 17]),
+                                               (300, 128, 40, None)])
+def test_decode_attention_key_runs(B, H, max_len, lens):
+    """Key ranges cut into several runs (one long sequence: 16 runs; two
+    sequences of different lengths; many sequences: one run), merged in order."""
+    rng = np.random.default_rng(B + H + max_len)
+    lens = np.asarray(lens if lens is not None else rng.integers(0, max_len, B), dtype=np.int32)
+    ql = synth.round_bf16(rng.standard_normal((B, H, 576)) * 0.3)
+    cache = synth.round_bf16(rng.standard_normal((B, max_len, 576)))
+    ol = torch.empty((B, H, 512), dtype=torch.bfloat16, device=DEV)
+    api.mla_decode_attention(dev(ql, torch.bfloat16), dev(cache, torch.bfloat16), dev(lens, torch.int32), ol)
+    got = ol.float().cpu().numpy()
+    for b in sorted(set([0, B - 1, B // 2])):
+        C = cache[b, :lens[b] + 1].astype(np.float64)
+        z = ql[b].astype(np.float64) @ C.T * 192.0 ** -0.5
+        ref = mla.softmax_over_live(z) @ C[:, :512]
+        assert_parity(got[b], ref, what=f"decode attention runs b={b}")
+
+
+def _prefill_attention_every_tile(B, T, H, k, seed):
+    """mla_prefill_attention at a full workload shape, one query row from every
+    128-row tile of every head (all heads of a row are compared), against the
+    oracle's attend_row (DeepSeek-V3.2-Exp · Sparse attention, Code)."""
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    Tp = api.pad64(T)
+    bf = torch.bfloat16
+    Q = torch.randn((B * T, H * 192), generator=g, device=DEV).to(bf)
+    KN = torch.randn((B, H, Tp, 128), generator=g, device=DEV).to(bf)
+    VT = torch.randn((B, H, 128, Tp), generator=g, device=DEV).to(bf)
+    KP = torch.randn((B, Tp, 64), generator=g, device=DEV).to(bf)
+    rng = np.random.default_rng(seed)
+    idx = synth.draw_topk(rng, B, T, k) if k else None
+    m = api.mla_topk_to_bitmask(dev(idx, torch.int32)) if k else None
+    out = torch.empty((B * T, H * 128), dtype=bf, device=DEV)
+    api.mla_prefill_attention(Q, KN, VT, KP, out, B, T, H, mask=m)
+    torch.cuda.synchronize()
+    rows = np.array([min(T - 1, 128 * i + int(rng.integers(0, 128))) for i in range((T + 127) // 128)])
+    rows[0], rows[-1] = 0, T - 1
+    got = out.view(B, T, H, 128)[:, torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    sc = 192.0 ** -0.5
+    for b in range(B):
+        q = Q.view(B, T, H, 192)[b, torch.from_numpy(rows).to(DEV)].double().cpu().numpy()
+        kn = KN[b, :, :T].double().cpu().numpy().transpose(1, 0, 2)      # [T, H, 128]
+        v = VT[b, :, :, :T].double().cpu().numpy().transpose(2, 0, 1)    # [T, H, 128]
+        kp = KP[b, :T].double().cpu().numpy()
+        for i, s in enumerate(rows):
+            live = mla.live_keys(int(s), None if idx is None else idx[b, s])
+            ref, _ = mla.attend_row(q[i, :, :128], q[i, :, 128:], kn, kp, v, live, sc)
+            assert_parity(got[b, i], ref, what=f"attention row {s} (tile {s // 128})")
+
+
+def test_prefill_attention_every_tile_kimi_k2_shape():
+    _prefill_attention_every_tile(1, 2048, 64, 0, 91)
+
+
+def test_prefill_attention_every_tile_dsv32_topk_shape():
+    _prefill_attention_every_tile(1, 8192, 128, 2048, 92)
+
+
 def test_decode_attention_large_logit_jump():
     # later keys outscore the first tile by far more than the fixed-max headroom,
     # which sends the kernel through its exact-max recomputation

@@ -98,8 +98,14 @@ def _check_decode(cfg, seed, cache_len=None, seqs=None, max_len=None):
     run.run()
     torch.cuda.synchronize()
     d = oracle_dims(cfg)
-    ref, entry = mla.mla_decode_absorbed(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"], seqs=seqs, fp8=fp8,
-                                         topk_idx=inp.get("topk_idx"))
+    if fp8 and cfg["B"] * cfg["cache_len"] <= 4096:
+        # e4m3: the unabsorbed definition (every Linear as prefill applies it, kv_b on each cached latent)
+        ref, entry = mla.mla_decode(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"], seqs=seqs, fp8=True,
+                                    topk_idx=inp.get("topk_idx"))
+    else:
+        # its exact reassociation (pinned equal to it on the CPU), much cheaper at full size
+        ref, entry = mla.mla_decode_absorbed(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"], seqs=seqs,
+                                             fp8=fp8, topk_idx=inp.get("topk_idx"))
     got = run.out.float().cpu().numpy()
     sel = np.arange(cfg["B"]) if seqs is None else np.asarray(seqs)
     assert_parity(got[sel], ref, tol=tol, cos=cos, what=cfg["name"])
@@ -328,8 +334,6 @@ def test_prefill_cached_topk_fp8_batched():
                            topk=24), 49, start_pos=130, max_len=256, tol=FP8_TOL, cos=0.999)
 
 
-@pytest.mark.xfail(strict=False, reason="e4m3 requantisation of bf16 intermediates (c_q, o_lat, o) gives "
-                   "3.4e-2 max error (cosine 0.99955) here, above the 3e-2 bar; each row alone is within it")
 def test_decode_sparse_fp8_dsv32_sampled():
     # e4m3 weights, 3000 cached, top-2048 per sequence, DeepSeek-V3.2-Exp shapes
     cfg = config(4, weight="e4m3", cache_len=3000, topk=2048)
@@ -419,3 +423,58 @@ def test_prefill_graph_replay_matches_eager():
         assert torch.equal(run.out, eager) and torch.equal(run.kv_cache, eager_cache), f"replay {i}"
         run.run()
         torch.cuda.synchronize()
+
+
+def test_decode_sparse_repeated_and_unsorted_positions():
+    """A selection is a set: repeated positions count once and the order of the
+    list does not matter (DeepSeek-V3.2-Exp · Sparse attention, Code: picks are
+    scattered as 0 into a -inf mask)."""
+    cfg = dict(name="dec_dup", mode="decode", B=4, cache_len=300, dim=1024, q_lora_rank=256, kv_lora_rank=512,
+               n_heads=128, act="bf16", weight="bf16", topk=64)
+    inp = synth.gen_decode(cfg, 81, max_len=320)
+    inp["cache_len"] = np.array([300, 5, 299, 150], dtype=np.int32)
+    rng = np.random.default_rng(82)
+    idx = np.full((4, 64), -1, dtype=np.int32)
+    for b, P in enumerate(inp["cache_len"]):
+        pick = rng.choice(P + 1, min(P + 1, 30), replace=False)
+        lst = np.concatenate([pick, pick[:10], pick[:3], [P + 7, -1]])   # repeats, a future slot, padding
+        rng.shuffle(lst)
+        idx[b, :len(lst)] = lst
+    inp["topk_idx"] = idx
+    run = runner.Decode(cfg, inp)
+    run.run()
+    torch.cuda.synchronize()
+    d = oracle_dims(cfg)
+    ref, _ = mla.mla_decode(inp["x"], inp["w"], d, inp["cache"], inp["cache_len"], topk_idx=idx)
+    assert_parity(run.out.float().cpu().numpy(), ref, what="decode, repeated selection")
+    # the same selection without repeats gives the same output bit for bit
+    uniq = np.full_like(idx, -1)
+    for b in range(4):
+        u = np.unique(idx[b][idx[b] >= 0])
+        uniq[b, :len(u)] = u
+    run.topk.copy_(torch.from_numpy(uniq))
+    first = run.out.clone()
+    run.cache.copy_(run.cache0)
+    run.run()
+    torch.cuda.synchronize()
+    assert torch.equal(run.out, first)
+
+
+def test_prefill_absorbed_repeated_positions():
+    cfg = small_cfg(B=1, T=120, topk=24, n_heads=64)
+    inp = synth.gen_prefill(cfg, 83)
+    idx = inp["topk_idx"].copy()
+    rng = np.random.default_rng(84)
+    for s in range(120):   # overwrite the padding and a few picks with repeats, then shuffle the row
+        row = idx[0, s]
+        live = row[row >= 0]
+        if len(live) > 2:
+            row[-3:] = live[:3]
+        rng.shuffle(row)
+    inp["topk_idx"] = idx
+    run = runner.PrefillAbsorbed(cfg, inp)
+    run.run()
+    torch.cuda.synchronize()
+    d = oracle_dims(cfg)
+    ref = mla.mla_prefill(inp["x"], inp["w"], d, topk_idx=idx)
+    assert_parity(run.out.float().cpu().numpy(), ref, what="absorbed prefill, repeated selection")
