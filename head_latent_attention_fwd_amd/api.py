@@ -62,6 +62,9 @@ _SIGS = {
     "mla_decode_attention_workspace_size": (sz, [i32, i32, i32]),
     "mla_decode_attention": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, f32, vp, sz, vp]),
     "mla_rope_table": (ctypes.c_int, [vp, vp, i32, f32, vp]),
+    "gemm_decode_workspace_size": (sz, [i32, i32, i32, i32]),
+    "gemm_bf16_decode": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, sz, vp]),
+    "gemm_fp8_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, vp, sz, vp]),
     "mla_quant_e4m3_1x128": (ctypes.c_int, [vp, i64, i32, i32, i32, vp, vp, vp]),
     "mla_quant_e4m3_block128": (ctypes.c_int, [vp, i32, i32, vp, vp, vp]),
     "mla_topk_to_bitmask": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
@@ -256,6 +259,27 @@ def gemm_fp8_blockscaled(Aq, a_scale, Wq, w_scale, C, stream=None):
     rc = lib().gemm_fp8_blockscaled(_ptr(Aq), _ptr(a_scale), _ptr(Wq), _ptr(w_scale), _ptr(C), C.stride(0),
                                     _TORCH_DT[C.dtype], M, N, K, _stream(stream))
     _check(rc)
+    return C
+
+
+def gemm_bf16_decode(A, W, C, ws=None, stream=None):
+    """Decode-shaped C[M, N] = A[M, K] . W[N, K]^T (M <= 128), bf16, contiguous."""
+    M, K = A.shape
+    N = W.shape[0]
+    if ws is None:
+        ws = workspace(lib().gemm_decode_workspace_size(MLA_BF16, M, N, K), A.device)
+    _check(lib().gemm_bf16_decode(_ptr(A), _ptr(W), _ptr(C), M, N, K, _ptr(ws), ws.numel(), _stream(stream)))
+    return C
+
+
+def gemm_fp8_decode(Aq, a_scale, Wq, w_scale, C, ws=None, stream=None):
+    """Decode-shaped block-scaled e4m3 product (M <= 128), bf16 out."""
+    M, K = Aq.shape
+    N = Wq.shape[0]
+    if ws is None:
+        ws = workspace(lib().gemm_decode_workspace_size(MLA_E4M3, M, N, K), Aq.device)
+    _check(lib().gemm_fp8_decode(_ptr(Aq), _ptr(a_scale), _ptr(Wq), _ptr(w_scale), _ptr(C), M, N, K, _ptr(ws),
+                                 ws.numel(), _stream(stream)))
     return C
 
 

@@ -168,6 +168,19 @@ int dec_chunks(int N, int nt) {
 int skinny_splits(int K, int splits);
 int skinny_fp8_splits(int K, int splits);
 
+// Column tile width and K chunks of a decode-shaped product with N outputs: a
+// narrow output (the joint q_a|kv_a down-projection) takes 64-wide tiles and
+// K chunks; a wide one whose tiles alone fill the chip (q_b) one chunk of
+// 96-wide (bf16) or 128-wide (e4m3) tiles; the rest (wo) 128-wide tiles and K
+// chunks. At the DeepSeek-V3.2-Exp shapes these are the decode step's choices.
+struct DecTiling { int nt, chunks; };
+DecTiling dec_tiling(int N, bool fp8) {
+  if (N <= 4096) return {DEC_NT_QKV, dec_chunks(N, DEC_NT_QKV)};
+  const int wide = fp8 ? DEC_NT_FP8 : DEC_NT_QB;
+  if ((N + wide - 1) / wide >= (fp8 ? 150 : 200)) return {wide, 1};
+  return {DEC_NT_WO, dec_chunks(N, DEC_NT_WO)};
+}
+
 // K chunks the q_a|kv_a and wo products of a decode step use (the same
 // functions pick them at launch, so the partial buffer always fits)
 int dec_qkv_splits(const mla_dims* d, int wdt) {
@@ -849,6 +862,56 @@ int gemm_fp8_blockscaled(const uint8_t* Aq, const float* a_scale, const uint8_t*
   g.A = Aq; g.a_scale = a_scale; g.W = Wq; g.w_scale = w_scale; g.W2 = nullptr; g.w2_scale = nullptr; g.n_split = N;
   g.C = C; g.ldc = ldc; g.c_dtype = c_dtype; g.M = M; g.N = N; g.K = K;
   LAUNCH(mla::launch_gemm_fp8(g, (hipStream_t)stream), "gemm_fp8_blockscaled");
+  return MLA_OK;
+}
+
+size_t gemm_decode_workspace_size(int32_t weight_dtype, int32_t M, int32_t N, int32_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || (weight_dtype != MLA_BF16 && weight_dtype != MLA_E4M3)) return 0;
+  const bool fp8 = weight_dtype == MLA_E4M3;
+  if (K % (fp8 ? 128 : 64)) return 0;
+  const DecTiling t = dec_tiling(N, fp8);
+  const int splits = fp8 ? skinny_fp8_splits(K, t.chunks) : skinny_splits(K, t.chunks);
+  return splits > 1 ? align256((size_t)splits * (M < 128 ? M : 128) * N * 4) : 256;
+}
+
+int gemm_bf16_decode(const void* A, const void* W, void* C, int32_t M, int32_t N, int32_t K, void* ws,
+                     size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (!A || !W || !C) return fail(MLA_INVALID_ARG, "NULL pointer");
+  if (M <= 0 || M > 128 || N <= 0 || K <= 0) return fail(MLA_INVALID_ARG, "need 0 < M <= 128, N > 0, K > 0");
+  if (K % 64) return fail(MLA_UNSUPPORTED, "K must be a multiple of 64");
+  if (((uintptr_t)A | (uintptr_t)W | (uintptr_t)C) & 15) return fail(MLA_UNSUPPORTED, "A, W, C must be 16-byte aligned");
+  const size_t need = gemm_decode_workspace_size(MLA_BF16, M, N, K);
+  if (!ws || ws_bytes < need) return fail(MLA_INVALID_ARG, "workspace too small: need %zu bytes", need);
+  if ((uintptr_t)ws & 255) return fail(MLA_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const DecTiling t = dec_tiling(N, false);
+  const int splits = skinny_splits(K, t.chunks);
+  int rc = skinny(A, K, 0, W, K, 0, nullptr, 0, N, splits > 1 ? nullptr : C, N, 0, splits > 1 ? (float*)ws : nullptr,
+                  M, N, K, 1, t.nt, t.chunks, s);
+  if (rc) return rc;
+  if (splits > 1) LAUNCH(mla::launch_splitk_reduce((const float*)ws, splits, M, N, C, N, s), "splitk_reduce");
+  return MLA_OK;
+}
+
+int gemm_fp8_decode(const uint8_t* Aq, const float* a_scale, const uint8_t* Wq, const float* w_scale, void* C,
+                    int32_t M, int32_t N, int32_t K, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (!Aq || !a_scale || !Wq || !w_scale || !C) return fail(MLA_INVALID_ARG, "NULL pointer");
+  if (M <= 0 || M > 128 || N <= 0 || K <= 0) return fail(MLA_INVALID_ARG, "need 0 < M <= 128, N > 0, K > 0");
+  if (K % 128) return fail(MLA_UNSUPPORTED, "K must be a multiple of 128");
+  if (((uintptr_t)Aq | (uintptr_t)Wq | (uintptr_t)C) & 15)
+    return fail(MLA_UNSUPPORTED, "Aq, Wq, C must be 16-byte aligned");
+  const size_t need = gemm_decode_workspace_size(MLA_E4M3, M, N, K);
+  if (!ws || ws_bytes < need) return fail(MLA_INVALID_ARG, "workspace too small: need %zu bytes", need);
+  if ((uintptr_t)ws & 255) return fail(MLA_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const DecTiling t = dec_tiling(N, true);
+  const int splits = skinny_fp8_splits(K, t.chunks);
+  int rc = skinny_fp8(Aq, K, 0, a_scale, K / 128, 0, Wq, K, 0, w_scale, K / 128, 0, nullptr, 0, nullptr, N,
+                      splits > 1 ? nullptr : C, N, 0, splits > 1 ? (float*)ws : nullptr, M, N, K, 1, t.nt, t.chunks, s);
+  if (rc) return rc;
+  if (splits > 1) LAUNCH(mla::launch_splitk_reduce((const float*)ws, splits, M, N, C, N, s), "splitk_reduce");
   return MLA_OK;
 }
 

@@ -7,23 +7,26 @@
 //   z[h, t] = scale * (q_lat[h] . C_t),  o_lat[h] = sum_t softmax_t(z[h]) C_t[:512]
 // so one cache tile in LDS serves every head of the row.
 //
-// Workgroup = (row q, group of 128 heads, key split j): four waves, wave w
-// owns heads 32w..32w+31 of the group, so each cache row of the split is read
-// from HBM once for all 128 heads. The key range of a row is cut into
-// `splits` runs of whole 32-key tiles; with one split the workgroup writes the
-// normalised o_lat, otherwise its normalised partial and its log2-sum-exp,
-// which the consumer merges in split order (launch_decode_combine or the
-// un-absorb kernel). The splits of a row are placed on one XCD.
+// Workgroup = (row q, group of 64 heads, key run j), four waves. The key
+// range of a row is cut into `splits` runs of whole 32-key tiles (as many as
+// it takes for rows x head groups x runs to fill the chip); with one run the
+// workgroup writes the normalised o_lat, otherwise its normalised partial and
+// its log2-sum-exp, which the consumer merges in run order
+// (launch_decode_combine or the un-absorb kernel). All workgroups of a row are
+// placed on one XCD, so the second head group's read of a cache tile comes
+// from that XCD's L2.
 //
-// Per tile, per wave (v_mfma_f32_32x32x16_bf16, fp32 accumulators):
-//   scores  S^T[t, h] = C[t, :] . Q^T[:, h]   36 k-steps over all 576 dims; the
-//           wave's 32 query columns stay in registers for the whole pass;
-//   values  O^T[d, h] += C^T[d, t] . P^T[t, h] for all 512 latent dims (C^T
-//           read with ds_read_b64_tr_b16). A lane's score results are 16 keys of
-//           one head, exactly the k slots the value product needs from P^T,
-//           so the probabilities stay in registers.
-// Cache tiles move HBM -> LDS with 16-byte direct-to-LDS buffer loads through
-// a 3-stage ring (two tiles in flight).
+// Wave (hb, dh) = (wave & 1, wave >> 1) serves heads 32hb..32hb+31 of the group:
+//   scores  S^T[t, h] = C[t, :] . Q^T[:, h]   each wave of the pair (hb, 0) /
+//           (hb, 1) takes one half of the 576 contracted dims (its half of Q
+//           stays in registers) and the pair adds the two fp32 partials
+//           through LDS, in the same order;
+//   values  O^T[d, h] += C^T[d, t] . P^T[t, h] for the wave's 256 latent dims,
+// both on v_mfma_f32_32x32x16_bf16 (C^T read with ds_read_b64_tr_b16). A
+// lane's score results are 16 keys of one head, exactly the k slots the value
+// product needs from P^T, so the probabilities stay in registers. Cache tiles
+// move HBM -> LDS with 16-byte direct-to-LDS buffer loads through a 3-stage
+// ring (two tiles in flight).
 //
 // Softmax: the running max of a head is fixed at its first live tile and
 // later tiles add exp2(z - m) <= 2^LAZY, so the accumulators are never
@@ -78,12 +81,11 @@ __device__ __forceinline__ v4s read_tr(const uint16_t* p) {
 
 struct DecodeCtx {
   __amdgpu_buffer_rsrc_t rsrc;   // raw buffer over the cache rows of the row's sequence
-  int k0, kend;                  // keys [k0, kend) of this split (dense: positions; sparse: list slots)
-  int ntiles, wave, lane, hi;
-  bool active;                   // the wave's heads exist
+  int k0, nkeys, ntiles, wave, lane, hi, dh;   // keys k0 .. k0 + nkeys - 1 (dense) or list slots (sparse)
   float sl2;
-  bool sparse;
-  const __attribute__((address_space(3))) int* keys;   // split's selected positions (sparse)
+  float* xs;                     // [2][4 waves][16][64] partial-score exchange
+  bool sparse;                   // tile rows from `keys` (else keys k0..k0+nkeys-1)
+  const __attribute__((address_space(3))) int* keys;   // the run's selected positions
 };
 
 __device__ __forceinline__ void load_lds16(const DecodeCtx& c, uint16_t* lds, int voff, int soff) {
@@ -91,32 +93,31 @@ __device__ __forceinline__ void load_lds16(const DecodeCtx& c, uint16_t* lds, in
                                            0);
 }
 
-// Loads tile kt of the split into stage st (9 loads per thread): latent
+// Loads tile kt of the run into stage st (9 loads per thread): latent
 // instruction i of wave w fills row 8w + i (lane = physical chunk); the rope
 // instruction of wave w fills rows 8w..8w+7 (8 chunks each). Rows past the
-// split's last key repeat it (their scores are masked).
+// run's last key repeat it (their scores are masked).
 __device__ __forceinline__ void issue_tile(const DecodeCtx& c, uint16_t* st, int kt) {
-  const int base = kt * DKT;
-  if (c.sparse) {   // list slots past the split's end hold its last key
+  const int k0 = kt * DKT;
+  if (c.sparse) {   // cache rows from the run's list (slots past its end repeat the last key)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 8 * c.wave + i;
-      load_lds16(c, st + r * 512, (c.lane ^ swl(r)) << 4,
-                 __builtin_amdgcn_readfirstlane(c.keys[base + r]) * (DROW * 2));
+      load_lds16(c, st + r * 512, (c.lane ^ swl(r)) << 4, __builtin_amdgcn_readfirstlane(c.keys[k0 + r]) * (DROW * 2));
     }
     const int r = 8 * c.wave + (c.lane >> 3);
-    const int t = c.keys[base + r];
+    const int t = c.keys[k0 + r];
     load_lds16(c, st + DLAT + c.wave * 512, t * (DROW * 2) + 1024 + (((c.lane & 7) ^ swr(r)) << 4), 0);
     return;
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = 8 * c.wave + i;
-    const int t = min(c.k0 + base + r, c.kend - 1);
+    const int t = c.k0 + min(k0 + r, c.nkeys - 1);
     load_lds16(c, st + r * 512, (c.lane ^ swl(r)) << 4, t * (DROW * 2));
   }
   const int r = 8 * c.wave + (c.lane >> 3);
-  const int t = min(c.k0 + base + r, c.kend - 1);
+  const int t = c.k0 + min(k0 + r, c.nkeys - 1);
   load_lds16(c, st + DLAT + c.wave * 512, t * (DROW * 2) + 1024 + (((c.lane & 7) ^ swr(r)) << 4), 0);
 }
 
@@ -160,10 +161,13 @@ __device__ __forceinline__ void quant_dequant_tile(uint16_t* st, int tid) {
   }
 }
 
-// Scores of one tile over all 576 dims: chunk 2 kk + hi meets query fragment kk.
-__device__ __forceinline__ floatx16 tile_scores(const uint16_t* st, int srow, int hi, const bf16x8 (&qf)[36]) {
+// Partial scores of one tile over the wave's half of the contracted dims:
+// dh = 0 takes latent chunks 0..35, dh = 1 latent chunks 36..63 and the rope
+// chunks; chunk 2kk + hi meets query fragment kk.
+template <int DH>
+__device__ __forceinline__ floatx16 partial_scores(const uint16_t* st, int srow, int hi, const bf16x8 (&qf)[18]) {
   auto frag = [&](int kk) {
-    const int c = 2 * kk;   // + hi
+    const int c = 36 * DH + 2 * kk;   // + hi
     if (c < 64) {
       const int f = swl(srow) ^ hi;
       return *(const bf16x8*)(st + srow * 512 + ((c & ~15) << 3) + (((c & 15) ^ f) << 3));
@@ -180,8 +184,8 @@ __device__ __forceinline__ floatx16 tile_scores(const uint16_t* st, int srow, in
   }
   bf16x8 f0 = frag(0), f1 = frag(1), f2;
 #pragma unroll
-  for (int kk = 0; kk < 36; ++kk) {
-    if (kk + 2 < 36) f2 = frag(kk + 2);
+  for (int kk = 0; kk < 18; ++kk) {
+    if (kk + 2 < 18) f2 = frag(kk + 2);
     if (kk & 1) sb = mfma32(f0, qf[kk], sb);
     else sa = mfma32(f0, qf[kk], sa);
     f0 = f1;
@@ -190,15 +194,15 @@ __device__ __forceinline__ floatx16 tile_scores(const uint16_t* st, int srow, in
   return sa + sb;
 }
 
-// One pass over the split. SCORES_ONLY: m becomes the exact per-head max.
+// One pass over the sequence. SCORES_ONLY: m becomes the exact per-head max.
 // Otherwise accumulates o and l against m (set at the first live tile when it
 // is -inf); returns true when a score exceeded m + LAZY (results invalid).
 template <bool SCORES_ONLY, bool QLAT>
 __device__ __forceinline__ bool attn_pass(const DecodeCtx& c, uint16_t* st0, uint16_t* st1, uint16_t* st2,
-                                          const bf16x8 (&qf)[36], float& m, float& l, floatx16 (&o)[16]) {
+                                          const bf16x8 (&qf)[18], float& m, float& l, floatx16 (&o)[8]) {
   const int lane = c.lane, l32 = lane & 31, hi = c.hi;
-  // transposed reads: 16-lane group q4 reads rows 16 s + 4 (q4 >> 1) + 8 e + (lane % 16) / 4,
-  // columns 32 dt + 16 (q4 & 1) + 4 (lane % 4)
+  // transposed reads: 16-lane group q reads rows 16 s + 4 (q >> 1) + 8 e + (lane % 16) / 4,
+  // columns 256 dh + 32 dt + 16 (q & 1) + 4 (lane % 4)
   const int q4 = lane >> 4, L = lane & 15;
   const int trow = 4 * (q4 >> 1) + (L >> 2);
   const int tx = 2 * (q4 & 1) + ((L >> 1) & 1);
@@ -208,17 +212,16 @@ __device__ __forceinline__ bool attn_pass(const DecodeCtx& c, uint16_t* st0, uin
 #pragma unroll
     for (int d4 = 0; d4 < 4; ++d4) {
       const int r = trow + 8 * e;
-      toff[e][d4] = r * 512 + (((4 * d4 + tx) ^ swl(r)) << 3) + 4 * (L & 1);
+      toff[e][d4] = r * 512 + 256 * c.dh + (((4 * d4 + tx) ^ swl(r)) << 3) + 4 * (L & 1);
     }
   bool over = false;
   if (!SCORES_ONLY) {
     l = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt)
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
   }
-  const int nk = c.kend - c.k0;
   auto step = [&](int kt, uint16_t* st, uint16_t* next) {
     __asm__ volatile("s_waitcnt vmcnt(9)" ::: "memory");   // tile kt landed, kt + 1 may be in flight
     __builtin_amdgcn_s_barrier();
@@ -230,15 +233,25 @@ __device__ __forceinline__ bool attn_pass(const DecodeCtx& c, uint16_t* st0, uin
       __builtin_amdgcn_s_barrier();
       __asm__ volatile("" ::: "memory");
     }
-    if (!c.active) return;
-    floatx16 sa = tile_scores(st, l32, hi, qf);
-    const int kb = kt * DKT;
+
+    floatx16 sa = c.dh ? partial_scores<1>(st, l32, hi, qf) : partial_scores<0>(st, l32, hi, qf);
+    float* xw = c.xs + (kt & 1) * (4 * 16 * 64);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sa[r] *= c.sl2;
-    if (kb + DKT > nk) {   // wave-uniform: the tile runs past the split's last key
+    for (int r = 0; r < 16; ++r) xw[(c.wave * 16 + r) * 64 + lane] = sa[r];
+    // exchange barrier: LDS writes only (a __syncthreads here would also drain the tile loads)
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    const int k0 = kt * DKT;
+    float part[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[r] = xw[((c.wave ^ 2) * 16 + r) * 64 + lane];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sa[r] = (c.dh ? part[r] + sa[r] : sa[r] + part[r]) * c.sl2;   // first + second half
+    if (k0 + DKT > c.nkeys) {   // wave-uniform: the tile runs past the last key
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (kb + row32(r, lane) >= nk) sa[r] = -INFINITY;
+        if (k0 + row32(r, lane) >= c.nkeys) sa[r] = -INFINITY;
     }
     float mx = sa[0];
 #pragma unroll
@@ -259,25 +272,26 @@ __device__ __forceinline__ bool attn_pass(const DecodeCtx& c, uint16_t* st0, uin
       pf[r >> 3][r & 7] = (__bf16)p;
     }
     l += rs;
-    // value product, step j = (key half j / 16, d tile j % 16); C^T fragments
-    // read two steps ahead
+    // value product, step j = (key half j / 8, d tile j % 8): consecutive MFMAs
+    // update different accumulators; C^T fragments read two steps ahead
     auto vfrag = [&](int j) {
-      const int dt = j & 15, imm = 16 * (j >> 4) * 512 + 128 * (dt >> 2);
+      const int dt = j & 7, imm = 16 * (j >> 3) * 512 + 128 * (dt >> 2);
       const v4s lo = read_tr(st + toff[0][dt & 3] + imm), up = read_tr(st + toff[1][dt & 3] + imm);
       return __builtin_bit_cast(bf16x8, (v8s){lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
     };
     bf16x8 vb0 = vfrag(0), vb1 = vfrag(1), vb2;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      if (j + 2 < 32) vb2 = vfrag(j + 2);
-      o[j & 15] = mfma32(vb0, pf[j >> 4], o[j & 15]);
+    for (int j = 0; j < 16; ++j) {
+      if (j + 2 < 16) vb2 = vfrag(j + 2);
+      o[j & 7] = mfma32(vb0, pf[j >> 3], o[j & 7]);
       vb0 = vb1;
       vb1 = vb2;
     }
   };
-  // Whole rounds of three tiles, two always in flight; tiles past the end hold
-  // copies of the last key (all masked, p = 0). Straight-line rounds let the
-  // compiler's own LDS waits see which stage each load targets.
+  // The loop runs whole rounds of three tiles and always keeps two tiles in
+  // flight; tiles past the end hold copies of the last key (all masked, p = 0)
+  // and cost a little math. Straight-line rounds let the compiler's own LDS
+  // waits see which stage each load targets.
   issue_tile(c, st0, 0);
   issue_tile(c, st1, 1);
   for (int kt = 0; kt < c.ntiles; kt += 3) {
@@ -286,7 +300,7 @@ __device__ __forceinline__ bool attn_pass(const DecodeCtx& c, uint16_t* st0, uin
     step(kt + 2, st2, st1);
   }
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();   // every wave is done with the stages
+  __syncthreads();   // every wave is done with the stages and the exchange buffer
   return over;
 }
 
@@ -295,12 +309,13 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(DecodeAttnArgs a, i
   __shared__ __attribute__((aligned(16))) uint16_t st0[DSTAGE];
   __shared__ __attribute__((aligned(16))) uint16_t st1[DSTAGE];
   __shared__ __attribute__((aligned(16))) uint16_t st2[DSTAGE];
+  __shared__ __attribute__((aligned(16))) float xs[2 * 4 * 16 * 64];
   __shared__ __attribute__((aligned(16))) int keys[SPARSE ? KEYS_LDS : 4];
   __shared__ int s_over;
 
   const int tid = threadIdx.x;
   const int NS = a.splits;
-  // workgroup -> (row q, head group hg, split j); all of a row's workgroups on one XCD
+  // workgroup -> (row q, head group hg, run j); all of a row's workgroups on one XCD
   const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
   const int j = loc % NS, hg = (loc / NS) % n_hg, q = (loc / (NS * n_hg)) * 8 + xcd;
   if (q >= a.R) return;
@@ -310,46 +325,44 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(DecodeAttnArgs a, i
   DecodeCtx c;
   c.lane = tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  c.dh = c.wave >> 1;
   c.hi = c.lane >> 5;
+  c.xs = xs;
   c.sl2 = a.scale * 1.4426950408889634f;
   c.sparse = SPARSE;
   c.keys = (const __attribute__((address_space(3))) int*)keys;
   // the row's keys (positions 0..P, or its compacted list) cut into NS runs of whole tiles
   const int n_all = !valid ? 0 : SPARSE ? a.nkeys[q] : P + 1;
   const int tiles_all = (n_all + DKT - 1) / DKT, tps = (tiles_all + NS - 1) / NS;
-  c.k0 = min(n_all, j * tps * DKT);
-  c.kend = min(n_all, (j + 1) * tps * DKT);
-  if (SPARSE) {   // this split's slots of the compacted list, padded with its last key
+  const int kb = min(n_all, j * tps * DKT), ke = min(n_all, (j + 1) * tps * DKT);
+  c.k0 = SPARSE ? 0 : kb;
+  c.nkeys = ke - kb;
+  if (SPARSE) {   // this run's slots of the compacted list, padded with its last key
     const int32_t* row = a.keys + (int64_t)q * a.kstride;
-    const int n = c.kend - c.k0;
-    const int last = n > 0 ? row[c.kend - 1] : 0;
-    for (int i = tid; i < KEYS_LDS; i += 256) keys[i] = i < n ? row[c.k0 + i] : last;
-    c.k0 = 0;
-    c.kend = n;
+    const int last = c.nkeys > 0 ? row[ke - 1] : 0;
+    for (int i = tid; i < KEYS_LDS; i += 256) keys[i] = i < c.nkeys ? row[kb + i] : last;
     __syncthreads();
   }
-  c.ntiles = (c.kend - c.k0 + DKT - 1) / DKT;
+  c.ntiles = (c.nkeys + DKT - 1) / DKT;
   c.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.cache + (int64_t)b * a.max_len * DROW),
                                              (short)0, a.max_len * DROW * 2, BUF_DW3);
-  const int head = hg * 128 + 32 * c.wave + (c.lane & 31);
-  c.active = hg * 128 + 32 * c.wave < a.H;
+  const int head = hg * 64 + (c.wave & 1) * 32 + (c.lane & 31);
 
-  // the wave's query: B operand of the score product, dims 16 kk + 8 hi + 0..7
-  bf16x8 qf[36];
+  // this wave's half of the query: B operand of the score product, dims 288 dh + 16 kk + 8 hi + 0..7
+  bf16x8 qf[18];
   {
-    const uint16_t* qp = (const uint16_t*)a.qlat + ((int64_t)q * a.H + min(head, a.H - 1)) * DROW + 8 * c.hi;
+    const uint16_t* qp = (const uint16_t*)a.qlat + ((int64_t)q * a.H + head) * DROW + 288 * c.dh + 8 * c.hi;
 #pragma unroll
-    for (int kk = 0; kk < 36; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 16 * kk));
+    for (int kk = 0; kk < 18; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 16 * kk));
   }
   if (tid == 0) s_over = 0;
-  floatx16 o[16];
+  floatx16 o[8];
   float m = -INFINITY, l = 0.f;
   bool over = false;
-  if (c.ntiles > 0) {
-    over = attn_pass<false, QLAT>(c, st0, st1, st2, qf, m, l, o);
-  } else {
+  if (c.ntiles > 0) over = attn_pass<false, QLAT>(c, st0, st1, st2, qf, m, l, o);
+  else {
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt)
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
     __syncthreads();
@@ -361,20 +374,19 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(DecodeAttnArgs a, i
     attn_pass<true, QLAT>(c, st0, st1, st2, qf, m, l, o);
     attn_pass<false, QLAT>(c, st0, st1, st2, qf, m, l, o);
   }
-  if (!c.active) return;
-  // lane: head `head`, dims 32 dt + 8 rg + 4 hi + 0..3
+  // lane: head `head`, dims 256 dh + 32 dt + 8 rg + 4 hi + 0..3
   l += __shfl_xor(l, 32);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const int64_t row = (int64_t)q * a.H + head;
   uint16_t* out = NS == 1 ? (uint16_t*)a.olat + row * 512 : (uint16_t*)a.part + ((int64_t)j * a.R * a.H + row) * 512;
-  out += 4 * c.hi;
+  out += 256 * c.dh + 4 * c.hi;
 #pragma unroll
-  for (int dt = 0; dt < 16; ++dt)
+  for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg)
       *(uint2*)(out + 32 * dt + 8 * rg) = make_uint2(pack_bf16x2(o[dt][4 * rg] * inv, o[dt][4 * rg + 1] * inv),
                                                      pack_bf16x2(o[dt][4 * rg + 2] * inv, o[dt][4 * rg + 3] * inv));
-  if (NS > 1 && c.hi == 0) a.lse[(int64_t)j * a.R * a.H + row] = l > 0.f ? m + __log2f(l) : -INFINITY;
+  if (NS > 1 && c.dh == 0 && c.hi == 0) a.lse[(int64_t)j * a.R * a.H + row] = l > 0.f ? m + __log2f(l) : -INFINITY;
 }
 
 // One workgroup per row: the listed positions t with 0 <= t <= last key of the
@@ -474,7 +486,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const uint16_t* __r
 }  // namespace
 
 int decode_splits(int rows, int H, int max_keys) {
-  const int n_hg = (H + 127) / 128;
+  const int n_hg = (H + 63) / 64;
   const int wgs = rows * n_hg;
   int ns = wgs >= 256 ? 1 : (256 + wgs - 1) / wgs;
   const int tiles = (max_keys + DKT - 1) / DKT;
@@ -485,7 +497,8 @@ int decode_splits(int rows, int H, int max_keys) {
 }
 
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s) {
-  const int n_hg = (a.H + 127) / 128;
+  if (a.H % 64) return hipErrorInvalidValue;
+  const int n_hg = a.H / 64;
   if (a.splits < 1 || a.splits > DECODE_MAX_SPLITS || (a.splits > 1 && (!a.part || !a.lse)) ||
       (a.splits == 1 && !a.olat))
     return hipErrorInvalidValue;
@@ -518,3 +531,4 @@ hipError_t launch_decode_combine(const void* part, const float* lse, int splits,
 }
 
 }  // namespace mla
+

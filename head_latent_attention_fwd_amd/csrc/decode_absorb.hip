@@ -214,13 +214,32 @@ __global__ __launch_bounds__(256, 1) void decode_unabsorb_kernel(UnabsorbArgs a)
   const int h = blockIdx.x, b0 = blockIdx.y * 64;
   const int H = a.H;
   const bool fp8 = a.w_scale != nullptr;
+  // this lane's row for the B operand: b = b0 + 16 wave + lane % 16, k chunk lane / 16
+  const int g4 = lane >> 4, L = lane & 15;
+  const int bq = b0 + 16 * wave + L;
+  const bool row_ok = bq < a.B;
+  const int64_t rh = (int64_t)min(bq, a.B - 1) * H + h;
+  const int64_t rows = (int64_t)a.B * H;
+  const uint16_t* part = (const uint16_t*)a.part;
+  // One run: the lane's 16 o_lat fragments are loaded before W_UV_h is staged
+  // so that both are in flight together.
+  uint4 frag[16];
+  if (a.splits == 1) {
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) frag[ks] = *(const uint4*)(part + rh * 512 + 32 * ks + 8 * g4);
+  }
   if (fp8) {   // codes -> bf16 -> LDS: 16-byte piece i of the thread = row j, codes 16 cc .. 16 cc + 15
     const uint8_t* W8 = (const uint8_t*)a.wkv_b + ((int64_t)256 * h + 128) * 512;
-#pragma unroll 4
+    uint4 wv[16];
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int idx = tid + 256 * i, j = idx >> 5, cc = idx & 31;
-      const uint4 v = *(const uint4*)(W8 + (int64_t)j * 512 + 16 * cc);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      wv[i] = *(const uint4*)(W8 + (int64_t)j * 512 + 16 * cc);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int idx = tid + 256 * i, j = idx >> 5, cc = idx & 31;
+      const uint32_t w[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
       uint32_t o[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -244,14 +263,7 @@ __global__ __launch_bounds__(256, 1) void decode_unabsorb_kernel(UnabsorbArgs a)
       __builtin_amdgcn_global_load_lds(W + (int64_t)j * 512 + ((ch ^ (j & 15)) << 3), sw + j * 512, 16, 0, 0);
     }
   }
-
-  // this lane's row for the B operand: b = b0 + 16 wave + lane % 16, k chunk lane / 16
-  const int g4 = lane >> 4, L = lane & 15;
-  const int bq = b0 + 16 * wave + L;
-  const bool row_ok = bq < a.B;
-  const int64_t rh = (int64_t)min(bq, a.B - 1) * H + h;
-  const int64_t rows = (int64_t)a.B * H;
-  // split weights exp2(lse_s - max) are recomputed where used (no indexed register array)
+  // run weights exp2(lse_s - max) are recomputed where used (no indexed register array)
   float mx = -INFINITY, den = 0.f;
   if (a.splits > 1) {
     for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.lse[s * rows + rh]);
@@ -267,39 +279,41 @@ __global__ __launch_bounds__(256, 1) void decode_unabsorb_kernel(UnabsorbArgs a)
   for (int jt = 0; jt < 8; ++jt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[jt][r] = 0.f;
-  const uint16_t* part = (const uint16_t*)a.part;
-#pragma unroll 2
+#pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
     const int c0 = 32 * ks + 8 * g4;   // the 8 columns of this lane's k slots
-    float f[8];
-    if (a.splits == 1) {
-      const uint4 u = *(const uint4*)(part + rh * 512 + c0);
-      const uint32_t p[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f[2 * e] = __uint_as_float(p[e] << 16);
-        f[2 * e + 1] = __uint_as_float(p[e] & 0xffff0000u);
-      }
+    bf16x8 bfr;
+    if (a.splits == 1 && !fp8) {
+      bfr = __builtin_bit_cast(bf16x8, frag[ks]);
     } else {
+      float f[8];
+      if (a.splits == 1) {
+        const uint32_t p[4] = {frag[ks].x, frag[ks].y, frag[ks].z, frag[ks].w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = 0.f;
-      if (mx != -INFINITY)
-        for (int s = 0; s < a.splits; ++s) {
-          const float ws = __builtin_amdgcn_exp2f(a.lse[s * rows + rh] - mx);
-          const uint4 u = *(const uint4*)(part + (s * rows + rh) * 512 + c0);
-          const uint32_t p[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            f[2 * e] += ws * __uint_as_float(p[e] << 16);
-            f[2 * e + 1] += ws * __uint_as_float(p[e] & 0xffff0000u);
-          }
+        for (int e = 0; e < 4; ++e) {
+          f[2 * e] = __uint_as_float(p[e] << 16);
+          f[2 * e + 1] = __uint_as_float(p[e] & 0xffff0000u);
         }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = 0.f;
+        if (mx != -INFINITY)
+          for (int s = 0; s < a.splits; ++s) {
+            const float ws = __builtin_amdgcn_exp2f(a.lse[s * rows + rh] - mx);
+            const uint4 u = *(const uint4*)(part + (s * rows + rh) * 512 + c0);
+            const uint32_t p[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              f[2 * e] += ws * __uint_as_float(p[e] << 16);
+              f[2 * e + 1] += ws * __uint_as_float(p[e] & 0xffff0000u);
+            }
+          }
+      }
+      float sc = inv;
+      if (fp8) sc *= a.w_scale[(int64_t)(2 * h + 1) * 4 + (c0 >> 7)];
+      bfr = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(f[0] * sc, f[1] * sc), pack_bf16x2(f[2] * sc, f[3] * sc),
+                                                  pack_bf16x2(f[4] * sc, f[5] * sc), pack_bf16x2(f[6] * sc, f[7] * sc)));
     }
-    float sc = inv;
-    if (fp8) sc *= a.w_scale[(int64_t)(2 * h + 1) * 4 + (c0 >> 7)];
-    const bf16x8 bfr = __builtin_bit_cast(
-        bf16x8, make_uint4(pack_bf16x2(f[0] * sc, f[1] * sc), pack_bf16x2(f[2] * sc, f[3] * sc),
-                           pack_bf16x2(f[4] * sc, f[5] * sc), pack_bf16x2(f[6] * sc, f[7] * sc)));
 #pragma unroll
     for (int jt = 0; jt < 8; ++jt) {
       const int j = 16 * jt + L, ch = 4 * ks + g4;

@@ -210,6 +210,24 @@ MLA_API int gemm_f32(const float* A, int64_t lda, const float* W, int64_t ldw, f
 MLA_API int gemm_fp8_blockscaled(const uint8_t* Aq, const float* a_scale, const uint8_t* Wq, const float* w_scale,
                          void* C, int64_t ldc, int32_t c_dtype, int32_t M, int32_t N, int32_t K, void* stream);
 
+/* Decode-shaped products: the same bias-free Linear for a batch of single
+ * tokens, M <= 128 rows (DeepSeek-V3.2-Exp · Output projection, decode at
+ * p = 1000: [B, 1, 16384] -> [B, 1, 7168]). Every weight byte is streamed once
+ * from HBM; a long K is cut into chunks whose fp32 partials (in the
+ * workspace) are summed in a fixed order. These are the kernels mla_decode
+ * runs for q_a|kv_a, q_b and wo.
+ *   gemm_bf16_decode: A [M, K], W [N, K] bf16, C [M, N] bf16; K % 64 == 0
+ *   gemm_fp8_decode:  Aq [M, K] e4m3 codes with a_scale [M, K/128], Wq [N, K]
+ *                     with w_scale [ceil(N/128), K/128] (block-scaled product
+ *                     as gemm_fp8_blockscaled), C [M, N] bf16; K % 128 == 0
+ * All contiguous and 16-byte aligned; ws of gemm_decode_workspace_size bytes,
+ * 256-byte aligned. */
+MLA_API size_t gemm_decode_workspace_size(int32_t weight_dtype, int32_t M, int32_t N, int32_t K);
+MLA_API int gemm_bf16_decode(const void* A, const void* W, void* C, int32_t M, int32_t N, int32_t K, void* ws,
+                             size_t ws_bytes, void* stream);
+MLA_API int gemm_fp8_decode(const uint8_t* Aq, const float* a_scale, const uint8_t* Wq, const float* w_scale,
+                            void* C, int32_t M, int32_t N, int32_t K, void* ws, size_t ws_bytes, void* stream);
+
 /* Row-wise RMSNorm and RoPE (the q_a / kv_a layernorms and the rotary part of
  * the query and of the shared key; Kimi K2 · Query compression, "Code").
  * For each of `rows` rows:

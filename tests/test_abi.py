@@ -86,13 +86,15 @@ def test_workspace_sizes(lib):
     assert api.mla_prefill_workspace_size(bad, api.MLA_BF16, api.MLA_BF16, 1, 16, 0) == 0
     dd = api.make_dims(7168, 1536, 512, 128)
     db = api.mla_decode_workspace_size(dd, api.MLA_BF16, 128, 1024)
-    # 128 sequences x 128 heads fill half the chip per key run, so the attention
-    # cuts each sequence's keys into two runs: two bf16 partials of o_lat + their lse
-    runs = 2 * 128 * 128 * 512 * 2 + 2 * 128 * 128 * 4
-    assert db >= runs + 128 * 128 * 576 * 2 + 128 * 2048 * 4   # + q_lat + compacted selections
-    # one run when the rows fill the chip by themselves
-    assert api.mla_decode_attention_workspace_size(512, 128, 1024) == 256
-    assert api.mla_decode_attention_workspace_size(128, 128, 1024) >= runs
+    # 128 sequences x 2 groups of 64 heads fill the chip: one key run, o_lat written directly
+    assert db >= 128 * 128 * 512 * 2 + 128 * 128 * 576 * 2 + 128 * 2048 * 4   # o_lat + q_lat + selections
+    assert api.mla_decode_attention_workspace_size(128, 128, 1024) == 256
+    # 64 sequences fill half of it: two runs, two bf16 partials of o_lat + their lse
+    runs = 2 * 64 * 128 * 512 * 2 + 2 * 64 * 128 * 4
+    assert api.mla_decode_attention_workspace_size(64, 128, 1024) >= runs
+    assert api.mla_decode_workspace_size(dd, api.MLA_BF16, 64, 1024) >= runs
+    # one long sequence: 16 runs
+    assert api.mla_decode_attention_workspace_size(1, 128, 8192) >= 16 * 128 * 512 * 2
     # e4m3 weights with 256 heads: wo's K = 32768 runs in 8 K chunks, and the
     # partial buffer holds all of them (8 x 128 rows x 7168 fp32)
     d256 = api.make_dims(7168, 1536, 512, 256)

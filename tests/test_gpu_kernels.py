@@ -327,3 +327,32 @@ def test_swiglu_mlp_e4m3(M, hidden, inter):
     rows = np.arange(M) if M <= 512 else np.array([0, 1, 255, 256, 1023, 2047])
     ref = mla.swiglu_mlp(x[rows], wg, wu, wd, fp8=True)
     assert_parity(out.float().cpu().numpy()[rows], ref, tol=FP8_TOL, cos=0.999, what=f"swiglu e4m3 {M}")
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 7168, 16384), (128, 24576, 1536), (128, 2112, 7168), (5, 200, 640)])
+def test_gemm_bf16_decode(M, N, K):
+    """Decode-shaped product (the decode step's q_a|kv_a, q_b and wo kernels) against the oracle's Linear."""
+    g = torch.Generator(device=DEV).manual_seed(M + N + K)
+    A = torch.randn((M, K), generator=g, device=DEV).to(torch.bfloat16)
+    W = (torch.randn((N, K), generator=g, device=DEV) / K ** 0.5).to(torch.bfloat16)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    api.gemm_bf16_decode(A, W, C)
+    rows = np.unique(np.array([0, M // 2, M - 1]))
+    ref = mla.linear(A[rows].double().cpu().numpy(), W.double().cpu().numpy())
+    assert_parity(C[rows].float().cpu().numpy(), ref, what=f"decode gemm {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 7168, 16384), (128, 24576, 1536), (7, 300, 1024)])
+def test_gemm_fp8_decode(M, N, K):
+    """Decode-shaped block-scaled e4m3 product against the oracle's block-scaled
+    sum over the same codes and scales (Kimi K2 · Down projection, quantization_config)."""
+    g = torch.Generator(device=DEV).manual_seed(M * 3 + N + K)
+    a = torch.randn((M, K), generator=g, device=DEV).to(torch.bfloat16)
+    w = torch.randn((N, K), generator=g, device=DEV) / K ** 0.5
+    Aq, As = api.mla_quant_e4m3_1x128(a)
+    Wq, Ws = api.mla_quant_e4m3_block128(w)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    api.gemm_fp8_decode(Aq, As, Wq, Ws, C)
+    rows = np.unique(np.array([0, M // 2, M - 1]))
+    ref = fp8.fp8_gemm(Aq[rows].cpu().numpy(), As[rows].cpu().numpy(), Wq.cpu().numpy(), Ws.cpu().numpy())
+    assert_parity(C[rows].float().cpu().numpy(), ref, what=f"decode fp8 gemm {M}x{N}x{K}")
