@@ -61,6 +61,7 @@ _SIGS = {
     "mla_prefill_attention": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]),
     "mla_decode_attention_workspace_size": (sz, [i32, i32, i32]),
     "mla_decode_attention": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, f32, vp, sz, vp]),
+    "mla_decode_attention_noalloc": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, f32, vp]),
     "mla_rope_table": (ctypes.c_int, [vp, vp, i32, f32, vp]),
     "gemm_decode_workspace_size": (sz, [i32, i32, i32, i32]),
     "gemm_bf16_decode": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, sz, vp]),
@@ -324,6 +325,15 @@ def mla_decode_attention(q_lat, cache, cache_len, o_lat, ws=None, scale=192.0 **
         ws = workspace(mla_decode_attention_workspace_size(B, H, cache.shape[1]), q_lat.device)
     rc = lib().mla_decode_attention(_ptr(q_lat), _ptr(cache), _ptr(cache_len), _ptr(o_lat), B, H, cache.shape[1],
                                     scale, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc)
+    return o_lat
+
+
+def mla_decode_attention_noalloc(q_lat, cache, cache_len, o_lat, scale=192.0 ** -0.5, stream=None):
+    """mla_decode_attention with the library's own scratch (no allocation anywhere in the call)."""
+    B, H, _ = q_lat.shape
+    rc = lib().mla_decode_attention_noalloc(_ptr(q_lat), _ptr(cache), _ptr(cache_len), _ptr(o_lat), B, H,
+                                            cache.shape[1], scale, _stream(stream))
     _check(rc)
     return o_lat
 

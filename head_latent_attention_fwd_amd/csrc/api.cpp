@@ -999,6 +999,23 @@ int mla_decode_attention(const void* q_lat, const void* cache, const int32_t* ca
   return MLA_OK;
 }
 
+int mla_decode_attention_noalloc(const void* q_lat, const void* cache, const int32_t* cache_len, void* o_lat,
+                                 int32_t B, int32_t H, int32_t max_len, float scale, void* stream) {
+  g_err.clear();
+  if (!q_lat || !cache || !cache_len || !o_lat) return fail(MLA_INVALID_ARG, "NULL pointer");
+  if (B <= 0 || H <= 0 || max_len <= 0) return fail(MLA_INVALID_ARG, "bad sizes");
+  const size_t need = mla_decode_attention_workspace_size(B, H, max_len);
+  if (need > mla::DECODE_SCRATCH_BYTES)
+    return fail(MLA_INVALID_ARG, "needs %zu bytes of scratch, more than the %zu the library holds", need,
+                mla::DECODE_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const hipError_t e = mla::decode_scratch(&ws);
+  if (e != hipSuccess) return fail(MLA_HIP_ERROR, "scratch lookup: %s", hipGetErrorString(e));
+  const int rc = mla_decode_attention(q_lat, cache, cache_len, o_lat, B, H, max_len, scale, ws,
+                                      mla::DECODE_SCRATCH_BYTES, stream);
+  return rc;
+}
+
 int mla_rope_table(float* cos_tab, float* sin_tab, int32_t n_pos, float base, void* stream) {
   g_err.clear();
   if (!cos_tab || !sin_tab) return fail(MLA_INVALID_ARG, "NULL table");

@@ -56,6 +56,8 @@
 // of bank conflicts. The stages are distinct LDS objects and every access
 // names its stage statically, so the compiler can tell the reads of one stage
 // from the loads in flight into the others.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -532,3 +534,35 @@ hipError_t launch_decode_combine(const void* part, const float* lse, int splits,
 
 }  // namespace mla
 
+// ---------------------------------------------------------------------------
+// Library-held scratch for the allocation-free variant of the decode attention
+// (callers that cannot allocate: code under graph capture, tight serving
+// loops). Each GPU the library runs on holds its own copy of this array until
+// the process ends; host code never passes the array's name to a kernel (on
+// the host it is only a stand-in), only the device address that
+// hipGetSymbolAddress returns for the current device.
+namespace {
+static __device__ __align__(256) uint8_t scratch[mla::DECODE_SCRATCH_BYTES];
+}  // namespace
+
+namespace mla {
+
+hipError_t decode_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* per_device[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {   // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
+}
+
+}  // namespace mla

@@ -238,6 +238,10 @@ struct UnabsorbArgs {
   int B, H;
 };
 hipError_t launch_decode_unabsorb(const UnabsorbArgs& a, hipStream_t s);
+// Size of the library-held scratch of the allocation-free decode attention,
+// and its device address on the current device (looked up once per device).
+constexpr size_t DECODE_SCRATCH_BYTES = (size_t)32 << 20;
+hipError_t decode_scratch(void** ptr);
 // q_lat[b, h] = [q_nope[b, h] . W_UK_h | RoPE(q_pe[b, h], cache_len[b])] for kv_lora_rank 512;
 // q [B, H*192], wkv_b [H*256, 512] (bf16, or e4m3 codes with block scales
 // w_scale [2H, 4]; w_scale == nullptr for bf16), qlat [B, H, 576].

@@ -11,8 +11,9 @@
  * Conventions shared by every entry point:
  *  - Tensor pointers are DEVICE pointers owned by the caller. The library never
  *    allocates device memory; scratch comes from a caller workspace whose size
- *    the *_workspace_size queries return. Host-side structs are read during the
- *    call only.
+ *    the *_workspace_size queries return (mla_decode_attention_noalloc instead
+ *    uses a fixed scratch array the library holds per GPU). Host-side structs
+ *    are read during the call only.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
  *    enqueued asynchronously on it; no entry point synchronises.
  *  - Matrices are row-major. Weights are [out, in] (K contiguous). Activations
@@ -277,6 +278,19 @@ MLA_API size_t mla_decode_attention_workspace_size(int32_t B, int32_t H, int32_t
 MLA_API int mla_decode_attention(const void* q_lat, const void* cache, const int32_t* cache_len, void* o_lat,
                                  int32_t B, int32_t H, int32_t max_len, float scale, void* ws, size_t ws_bytes,
                                  void* stream);
+
+/* The same decode attention for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): no
+ * workspace argument; the partial results of the key runs live in a 32 MiB
+ * scratch array the library holds on each GPU it runs on (kept until the
+ * process ends). Arguments and result as mla_decode_attention; sizes whose
+ * workspace (mla_decode_attention_workspace_size) exceeds 32 MiB are
+ * rejected with MLA_INVALID_ARG. Calls on one GPU share that array: calls
+ * that overlap on one GPU (other streams, other host threads) race and must
+ * be ordered by the caller. Allocates no memory. */
+MLA_API int mla_decode_attention_noalloc(const void* q_lat, const void* cache, const int32_t* cache_len,
+                                         void* o_lat, int32_t B, int32_t H, int32_t max_len, float scale,
+                                         void* stream);
 
 /* cos/sin table for RoPE: cos_tab[p, d] = cos(p * base^(-d/32)), sin likewise,
  * for p < n_pos, d < 32, evaluated in fp64 and stored fp32. */
