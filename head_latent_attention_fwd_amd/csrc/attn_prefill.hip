@@ -12,10 +12,10 @@
 // keys 0..P+T-1 (the P cached keys come first in kn / vt / kpe); P = 0 is the
 // plain prefill.
 //
-// Work split: one 256-thread workgroup per (128-query tile, head, sequence);
-// the query tiles of one (sequence, head) run on one XCD, and workgroups start
-// heaviest (last query tile) first across all pairs of that XCD; wave w owns
-// queries [32w, 32w+32).
+// Work split: one 256-thread workgroup per (two 128-query tiles, head,
+// sequence): tiles nq - 1 - z and z of the pair, so all workgroups carry the
+// same causal work; the pairs of an XCD are walked one after another so their
+// keys and values stay in its L2; wave w owns queries [32w, 32w+32) of a tile.
 // Scores are formed transposed, S^T = K . Q^T, on v_mfma_f32_32x32x16_bf16 so
 // a lane holds 32 keys of one query: the running max needs one exchange
 // (lane ^ 32) and the running sum stays lane-local; the bf16 probabilities are
@@ -30,8 +30,16 @@
 // chunks are XOR-swizzled by row in every region (conflict-free reads with 32
 // or 64 LDS banks).
 //
-// The running max is only raised when a row's max grows by more than 2^8
-// (probabilities stay <= 256 in the meantime), so the O rescale is rare.
+// Softmax: a query's running max is fixed at its first live keys and later
+// keys add exp2(z - m) unrescaled (fp32 holds any z - m below 2^7; the bf16
+// probabilities have the same exponent range), so O is never rescaled. If the
+// sum of a query then leaves [0, 2^64) (a logit jump of more than ~44 nats)
+// the workgroup redoes its tile in two passes of the same loop: exact maxima
+// first, then the accumulation against them.
+// Masks: per 32-key block a lane builds one 32-bit word of the keys live for
+// its query (selection bits, causal limit, sequence end); tiles wholly inside
+// every query's causal range without a selection skip it. Every branch
+// condition of the tile loop is wave-uniform.
 #include "common.h"
 #include "kernels.h"
 
@@ -43,31 +51,34 @@ constexpr int BKV = 64;                   // keys per tile
 // one LDS stage (bf16 elements): k_nope [64][128] | k_pe [64][64] | v^T [128][64]
 constexpr int ST_KN = 0, ST_KPE = 64 * 128, ST_VT = ST_KPE + 64 * 64, STAGE = ST_VT + 128 * 64;
 constexpr int LOADS = STAGE * 2 / 16 / 256;  // 16-byte direct loads per thread per tile (10)
-constexpr float LAZY = 8.0f;
+constexpr float LSUM_MAX = 18446744073709551616.0f;   // 2^64: a query sum beyond this ran past its fixed max
 
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 // chunk swizzle of 128-byte rows, conflict-free for 32 or 64 LDS banks
 __device__ __forceinline__ int sw8(int r) { return (r ^ (r >> 3)) & 7; }
 
 __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];   // 80 KB: two workgroups per CU
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int T = a.T, Tp = a.Tp, H = a.H, P = a.P, Tk = P + T;
-  // XCD-aware order: workgroup id % 8 is the XCD, and each XCD takes whole
-  // (sequence, head) pairs, so the query tiles that re-read one head's keys
-  // and values share that XCD's L2. Workgroups start in order of decreasing
-  // work (the last query tiles of every pair on the XCD first), which keeps
-  // the causal triangle from leaving CUs idle at the end.
-  const int nq = (T + BQ - 1) / BQ, ppx = (a.B * H + 7) / 8;
+  // Work order: workgroup id % 8 is the XCD; each XCD takes whole (sequence,
+  // head) pairs one after another, and a workgroup takes the query tiles
+  // nq - 1 - z and z of its pair (zigzag), so every workgroup has the same
+  // causal work and the keys and values of the pairs in flight on an XCD stay
+  // in its L2 (the second tile re-reads a prefix the first one just streamed).
+  const int nq = (T + BQ - 1) / BQ, nz = (nq + 1) / 2;
   const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
-  const int pair = (loc % ppx) * 8 + xcd;
+  const int pair = (loc / nz) * 8 + xcd, z = loc % nz;
   if (pair >= a.B * H) return;
-  const int qt = nq - 1 - loc / ppx;
   const int h = pair % H, b = pair / H;
   const int64_t bh = (int64_t)b * H + h;
-  const int q0 = qt * BQ, qw = q0 + wave * 32;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  for (int zz = 0; zz < 2; ++zz) {
+  const int qt = zz ? z : nq - 1 - z;
+  if (zz && qt == nq - 1 - z) break;   // odd tile count: the middle tile is alone
+  const int q0 = qt * BQ, qw = q0 + wv * 32;   // wave-uniform
   const int qi = qw + l32;
   const bool q_ok = qi < T;
 
@@ -92,7 +103,6 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
       (void*)((const uint16_t*)a.kpe + (int64_t)b * Tp * 64), (short)0, Tp * 64 * 2, BUF_DW3);
   const __amdgpu_buffer_rsrc_t rs_vt = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const uint16_t*)a.vt + bh * 128 * Tp), (short)0, 128 * Tp * 2, BUF_DW3);
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
   int voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
@@ -129,118 +139,148 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
     for (int v = 0; v < 4; ++v) xp[kb][v] = ((2 * v + hi) ^ sw8(kb * 32 + l32)) << 3;
 
   floatx16 o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
   float m = -INFINITY, l = 0.f;
   const float sl2 = a.scale * 1.4426950408889634f;
   const int W = (Tk + 31) >> 5;
-  const uint32_t* mrow = a.mask ? a.mask + ((int64_t)b * T + (q_ok ? qi : 0)) * W : nullptr;
-  // absolute positions of the wave's last query and of this lane's query
-  const int pw = P + qw + 31, pi = P + qi;
+  const bool has_mask = a.mask != nullptr;   // wave-uniform (mrow is a per-lane row pointer)
+  const uint32_t* mrow = has_mask ? a.mask + ((int64_t)b * T + (q_ok ? qi : 0)) * W : nullptr;
+  // absolute position of this lane's query
+  const int pi = P + qi;
 
   const int kv_end = min(Tk, P + q0 + BQ);
   const int ntiles = (kv_end + BKV - 1) / BKV;
-  // mask words of a tile (two 32-key words per query row), fetched one tile
+  // selection words of a tile (two 32-key words per query row), fetched one tile
   // ahead and before the tile refill so that waiting for them never waits for it
   auto mask_words = [&](int kt, uint32_t& w0, uint32_t& w1) {
     w0 = w1 = 0xFFFFFFFFu;
-    if (mrow && kt < ntiles) {
+    if (has_mask && kt < ntiles) {
       const int wi = (kt * BKV) >> 5;
       w0 = mrow[wi];
       w1 = wi + 1 < W ? mrow[wi + 1] : 0u;
     }
   };
-  uint32_t nw0, nw1;
-  mask_words(0, nw0, nw1);
-  issue(0, 0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int cur = kt & 1, k0 = kt * BKV;
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const uint32_t mw0 = nw0, mw1 = nw1;
-    mask_words(kt + 1, nw0, nw1);
-    if (kt + 1 < ntiles) issue(cur ^ 1, k0 + BKV);
-    if (k0 > pw) continue;                       // every key of the tile is after this wave's queries
-    const uint16_t* sb = smem + cur * STAGE;
-    floatx16 s[2];
+  // keys j of the 32-key block starting at key kb0 that are live for this
+  // lane's query, shifted so that bit 16 (r / 8) + r % 8 is the key of result
+  // slot r (lane half hi holds keys 16 (r / 8) + 8 hi + r % 8)
+  auto live_word = [&](uint32_t sel, int kb0) {
+    const int lim = min(pi, Tk - 1) - kb0;   // keys j <= lim exist and are causal
+    const uint32_t lm = lim >= 31 ? 0xFFFFFFFFu : lim < 0 ? 0u : ((2u << lim) - 1u);
+    return (sel & lm) >> (8 * hi);
+  };
+
+  // mode 0: accumulate with each query's max fixed at its first live keys;
+  // mode 1 (after an overflow anywhere in the workgroup): exact maxima only;
+  // mode 2: accumulate against those maxima. One copy of the loop serves all
+  // three (the mode is workgroup-uniform).
+  for (int mode = 0;;) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-    // step u = (kk, kb) = (u / 2, u % 2); K fragments read two steps ahead
-    auto kfrag = [&](int u) {
-      const int kk = u >> 1, kb = u & 1, rho = kb * 32 + l32;
-      const int off = kk < 8 ? ST_KN + rho * 128 + xk[kk] : ST_KPE + rho * 64 + xp[kb][kk - 8];
-      return *(const bf16x8*)(sb + off);
-    };
-    bf16x8 kf0 = kfrag(0), kf1 = kfrag(1), kf2;
+      for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
+    l = 0.f;
+    uint32_t nw0, nw1;
+    mask_words(0, nw0, nw1);
+    issue(0, 0);
+    for (int kt = 0; kt < ntiles; ++kt) {
+      const int cur = kt & 1, k0 = kt * BKV;
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      const uint32_t mw0 = nw0, mw1 = nw1;
+      mask_words(kt + 1, nw0, nw1);
+      if (kt + 1 < ntiles) issue(cur ^ 1, k0 + BKV);
+      // No early exit: a tile wholly after this wave's queries (k0 > pw) goes
+      // through the masked path with every key dead, so O is updated on every
+      // path and the compiler keeps it in place.
+      const uint16_t* sb = smem + cur * STAGE;
+      floatx16 s[2];
 #pragma unroll
-    for (int u = 0; u < 24; ++u) {
-      if (u + 2 < 24) kf2 = kfrag(u + 2);
-      s[u & 1] = mfma32(kf0, qf[u >> 1], s[u & 1]);
-      kf0 = kf1;
-      kf1 = kf2;
-    }
-    // s[kb][r] holds key k0 + 32kb + 16(r/8) + 8hi + r%8
-    const bool interior = !mrow && (k0 + BKV - 1 <= P + qw) && (k0 + BKV <= Tk);
-    if (!interior) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t bits = kb ? mw1 : mw0;
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      // step u = (kk, kb) = (u / 2, u % 2); K fragments read two steps ahead
+      auto kfrag = [&](int u) {
+        const int kk = u >> 1, kb = u & 1, rho = kb * 32 + l32;
+        const int off = kk < 8 ? ST_KN + rho * 128 + xk[kk] : ST_KPE + rho * 64 + xp[kb][kk - 8];
+        return *(const bf16x8*)(sb + off);
+      };
+      bf16x8 kf[24];   // one value per unrolled step (no register copies)
+      kf[0] = kfrag(0);
+      kf[1] = kfrag(1);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kr = 16 * (r >> 3) + 8 * hi + (r & 7);
-          const int t = k0 + kb * 32 + kr;
-          const bool live = t <= pi && t < Tk && ((bits >> kr) & 1u);
-          s[kb][r] = live ? s[kb][r] : -INFINITY;
+      for (int u = 0; u < 24; ++u) {
+        if (u + 2 < 24) kf[u + 2] = kfrag(u + 2);
+        s[u & 1] = mfma32(kf[u], qf[u >> 1], s[u & 1]);
+      }
+      // s[kb][r] holds key k0 + 32kb + 16(r/8) + 8hi + r%8
+      const bool interior = !has_mask && (k0 + BKV - 1 <= P + qw) && (k0 + BKV <= Tk);   // wave-uniform
+      if (!interior) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint32_t w = live_word(kb ? mw1 : mw0, k0 + 32 * kb);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!((w >> (16 * (r >> 3) + (r & 7))) & 1u)) s[kb][r] = -INFINITY;
         }
       }
+      if (mode == 1 || (mode == 0 && __any(m == -INFINITY))) {   // maxima wanted (uniform condition)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+        if (mode == 1) m = fmaxf(m, mx);
+        else if (m == -INFINITY) m = mx;   // the query's first live keys: nothing accumulated yet
+      }
+      // (mode 1 still runs the value product below; its O is discarded)
+      const float ms = m == -INFINITY ? 0.f : m;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][half * 8 + e], sl2, -ms));
+            l += p;
+            pf[kb * 2 + half][e] = (__bf16)p;
+          }
+      // O^T += V^T . P^T; step ks covers keys 32(ks/2) + 16(ks%2) + 8hi + 0..7
+      // step u = (ks, j) = (u / 4, u % 4); V^T fragments read two steps ahead
+      auto vfrag = [&](int u) {
+        const int ks = u >> 2, dv = (u & 3) * 32 + l32;
+        const int c = (4 * (ks >> 1) + 2 * (ks & 1) + hi) ^ sw8(dv);
+        return *(const bf16x8*)(sb + ST_VT + dv * 64 + (c << 3));
+      };
+      bf16x8 vf[16];
+      vf[0] = vfrag(0);
+      vf[1] = vfrag(1);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (u + 2 < 16) vf[u + 2] = vfrag(u + 2);
+        o[u & 3] = mfma32(vf[u], pf[u >> 2], o[u & 3]);
+      }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-    const bool raise = mx > m + LAZY;
-    if (__any(raise)) {
-      const float mn = raise ? mx : m;
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);   // m = -inf gives 0
-      l *= alpha;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
-      m = mn;
-    }
-    const float ms = m == -INFINITY ? 0.f : m;
-    bf16x8 pf[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][half * 8 + e], sl2, -ms));
-          l += p;
-          pf[kb * 2 + half][e] = (__bf16)p;
-        }
-    // O^T += V^T . P^T; step ks covers keys 32(ks/2) + 16(ks%2) + 8hi + 0..7
-    // step u = (ks, j) = (u / 4, u % 4); V^T fragments read two steps ahead
-    auto vfrag = [&](int u) {
-      const int ks = u >> 2, dv = (u & 3) * 32 + l32;
-      const int c = (4 * (ks >> 1) + 2 * (ks & 1) + hi) ^ sw8(dv);
-      return *(const bf16x8*)(sb + ST_VT + dv * 64 + (c << 3));
-    };
-    bf16x8 vf0 = vfrag(0), vf1 = vfrag(1), vf2;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      if (u + 2 < 16) vf2 = vfrag(u + 2);
-      o[u & 3] = mfma32(vf0, pf[u >> 2], o[u & 3]);
-      vf0 = vf1;
-      vf1 = vf2;
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();   // the stages are free for another pass
+    if (mode == 0) {
+      // a query whose sum left [0, 2^64) ran past its fixed max: exact two-pass
+      // redo of the whole workgroup, decided through a flag in the (now idle) stage memory
+      int* flag = (int*)smem;
+      if (tid == 0) flag[0] = 0;
+      __syncthreads();
+      const float lsum = l + __shfl_xor(l, 32);
+      if (__any(!(lsum < LSUM_MAX)) && lane == 0) flag[0] = 1;
+      __syncthreads();
+      const bool redo = flag[0] != 0;
+      __syncthreads();   // every wave has read the flag before stage 0 is reloaded
+      if (!redo) break;
+      mode = 1;
+      m = -INFINITY;
+    } else if (mode == 1) {
+      mode = 2;
+    } else {
+      break;
     }
   }
 
@@ -275,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
         }
       if (hi == 0) a.os[row * H + h] = sc;
     }
-    return;
+    continue;
   }
   if (q_ok) {
     uint16_t* op = (uint16_t*)a.out + ((int64_t)b * T + qi) * ((int64_t)H * 128) + h * 128;
@@ -289,6 +329,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
         *(uint2*)(op + dv) = pk2;
       }
   }
+  }   // zigzag tiles
 }
 
 // fp32 path: one wave per (query, head); lanes split the feature dims.
@@ -325,7 +366,7 @@ __global__ __launch_bounds__(64) void prefill_attn_f32_kernel(PrefillAttnArgs a)
 
 hipError_t launch_prefill_attn_bf16(const PrefillAttnArgs& a, hipStream_t s) {
   const int nq = (a.T + BQ - 1) / BQ, pairs = a.B * a.H;
-  const unsigned grid = 8u * (unsigned)((pairs + 7) / 8) * (unsigned)nq;
+  const unsigned grid = 8u * (unsigned)((pairs + 7) / 8) * (unsigned)((nq + 1) / 2);
   prefill_attn_kernel<<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }

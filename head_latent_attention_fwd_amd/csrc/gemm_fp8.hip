@@ -269,16 +269,14 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
     const float r1 = (n1s != 0.f && srun1 != 0.f) ? srun1 / n1s : 1.f;
     if (n0s != 0.f) srun0 = n0s;
     if (n1s != 0.f) srun1 = n1s;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[0][j] *= r0;
-      acc[1][j] *= r1;
-    }
     // next group's scales (clamped: the last group repeats)
     const int kn = min(kg + 1, KG - 1);
     sa0 = as0[kn];
     sa1 = as1[kn];
     sw = wsrow[kn];
+    // first k half: each 32x32 block is rescaled right before its MFMA, so the
+    // 16 multiplies of the next block issue while the matrix core runs this
+    // one; the second k half follows with no VALU work between MFMAs
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       intx8 af[2], wf[4];
@@ -289,7 +287,14 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32_fp8(wf[j], af[i], acc[i][j]);
+        for (int j = 0; j < 4; ++j) {
+          if (ks == 0) {
+            acc[i][j] *= i ? r1 : r0;
+            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);   // 16 VALU (the block's rescale)
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // then its MFMA
+          }
+          acc[i][j] = mfma32_fp8(wf[j], af[i], acc[i][j]);
+        }
     }
     // every wave is done with `cur` and the other stage has landed
     __builtin_amdgcn_s_waitcnt(fb_wait(0, 0));

@@ -253,6 +253,39 @@ def _prefill_attention_every_tile(B, T, H, k, seed):
             assert_parity(got[b, i], ref, what=f"attention row {s} (tile {s // 128})")
 
 
+@pytest.mark.parametrize("k", [0, 24])
+def test_prefill_attention_large_logit_jump(k):
+    """Later keys outscore a query's first live keys by far more than the fixed
+    running max allows (sums beyond 2^64), which sends the workgroup through its
+    exact two-pass redo."""
+    rng = np.random.default_rng(11 + k)
+    B, T, H = 1, 300, 2
+    Tp = api.pad64(T)
+    q = synth.round_bf16(rng.standard_normal((B * T, H * 192)))
+    kn = rng.standard_normal((B, H, T, 128))
+    kn[:, :, 100:] *= 40.0
+    kn = synth.round_bf16(kn)
+    v = synth.round_bf16(rng.standard_normal((B, H, T, 128)))
+    kp = synth.round_bf16(rng.standard_normal((B, T, 64)))
+    idx = synth.draw_topk(rng, B, T, k) if k else None
+    m = api.mla_topk_to_bitmask(dev(idx, torch.int32)) if k else None
+    KN = torch.zeros((B, H, Tp, 128), dtype=torch.bfloat16, device=DEV)
+    KN[:, :, :T] = dev(kn, torch.bfloat16)
+    VT = torch.zeros((B, H, 128, Tp), dtype=torch.bfloat16, device=DEV)
+    VT[:, :, :, :T] = dev(np.ascontiguousarray(v.transpose(0, 1, 3, 2)), torch.bfloat16)
+    KP = torch.zeros((B, Tp, 64), dtype=torch.bfloat16, device=DEV)
+    KP[:, :T] = dev(kp, torch.bfloat16)
+    out = torch.empty((B * T, H * 128), dtype=torch.bfloat16, device=DEV)
+    api.mla_prefill_attention(dev(q, torch.bfloat16), KN, VT, KP, out, B, T, H, mask=m)
+    got = out.float().cpu().numpy().reshape(B, T, H, 128)
+    rows = [0, 99, 100, 101, 150, 255, 256, 299]
+    qq = q.reshape(B, T, H, 192)[0]
+    ref = np.stack([mla.attend_row(qq[s, :, :128], qq[s, :, 128:], kn[0].transpose(1, 0, 2), kp[0],
+                                   v[0].transpose(1, 0, 2), mla.live_keys(s, None if idx is None else idx[0, s]),
+                                   192.0 ** -0.5)[0] for s in rows])
+    assert_parity(got[0, rows], ref, what="attention (logit jump)")
+
+
 def test_prefill_attention_every_tile_kimi_k2_shape():
     _prefill_attention_every_tile(1, 2048, 64, 0, 91)
 
