@@ -474,12 +474,14 @@ def main():
         line["roofline"] = roofline_of(head)
     line["rooflines"] = {r["workload"]: roofline_of(r) for r in results.values() if "kernels" in r}
     if 4 in results and "kernels" in results[4]:
-        k = results[4]["kernels"]["attention"]
-        line["roofline_decode_attention"] = {
-            "workload": results[4]["workload"], "kernel": "attention", "bound": "hbm", "achieved": k["gbps"],
-            "peak": PEAK["hbm"], "unit": "GB/s", "frac": k["frac"], "us_per_launch": k["us"],
-            "algorithmic_bytes_per_launch": k["bytes"],
-            "traffic": traffic_for(f"{results[4]['workload']}:attention", KERNEL_SOURCES["attention_decode"])}
+        # The decode step's two largest kernels, both bound by HBM.
+        for name, key in (("attention", "roofline_decode_attention"), ("gemm_wo", "roofline_decode_wo")):
+            k = results[4]["kernels"][name]
+            line[key] = {
+                "workload": results[4]["workload"], "kernel": name, "bound": "hbm", "achieved": k["gbps"],
+                "peak": PEAK["hbm"], "unit": "GB/s", "frac": k["frac"], "us_per_launch": k["us"],
+                "algorithmic_bytes_per_launch": k["bytes"],
+                "traffic": traffic_for(f"{results[4]['workload']}:{name}", KERNEL_SOURCES[k["src"]])}
     line["workloads"] = {str(k): v for k, v in results.items()}
     if not args.no_cpu:
         print("[bench] cpu baselines (oracle)", file=sys.stderr, flush=True)
