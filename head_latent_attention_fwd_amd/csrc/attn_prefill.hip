@@ -23,7 +23,9 @@
 //
 // Tiles move HBM -> LDS with gfx950's 16-byte direct-to-LDS loads into a
 // two-stage ring (one barrier per tile; the next tile's loads fly while the
-// current tile is consumed), 40 KB per stage, two workgroups per CU. Within a
+// current tile is consumed), 40 KB per stage, two workgroups per CU. The tile
+// loop is unrolled over the two stages so every LDS address is a per-lane
+// base plus an immediate. Within a
 // 16-key block the K rows are stored with bits 2 and 3 of the key index
 // swapped: the 32x32 MFMA output then gives each lane 8 consecutive keys per
 // 16-key step, so the matching V^T operand is one 16-byte LDS read. 16-byte
@@ -32,7 +34,9 @@
 //
 // Softmax: a query's running max is fixed at its first live keys and later
 // keys add exp2(z - m) unrescaled (fp32 holds any z - m below 2^7; the bf16
-// probabilities have the same exponent range), so O is never rescaled. If the
+// probabilities have the same exponent range), so O is never rescaled. The
+// row sum adds the bf16-rounded probabilities (two per v_dot2 against ones),
+// the same weights the value product uses. If the
 // sum of a query then leaves [0, 2^64) (a logit jump of more than ~44 nats)
 // the workgroup redoes its tile in two passes of the same loop: exact maxima
 // first, then the accumulation against them.
@@ -40,6 +44,8 @@
 // its query (selection bits, causal limit, sequence end); tiles wholly inside
 // every query's causal range without a selection skip it. Every branch
 // condition of the tile loop is wave-uniform.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -172,17 +178,23 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   // mode 1 (after an overflow anywhere in the workgroup): exact maxima only;
   // mode 2: accumulate against those maxima. One copy of the loop serves all
   // three (the mode is workgroup-uniform).
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   for (int mode = 0;;) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
-    l = 0.f;
+    // the sum runs over the bf16 probabilities that enter the value product
+    // (two partial sums: shorter dependency chains)
+    float l0 = 0.f, l1 = 0.f;
     uint32_t nw0, nw1;
     mask_words(0, nw0, nw1);
     issue(0, 0);
-    for (int kt = 0; kt < ntiles; ++kt) {
-      const int cur = kt & 1, k0 = kt * BKV;
+    // one tile; the stage is a compile-time constant so that every LDS address
+    // is a per-lane base plus an immediate offset
+    auto tile = [&](int kt, auto stage) {
+      constexpr int cur = decltype(stage)::value;
+      const int k0 = kt * BKV;
       __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       const uint32_t mw0 = nw0, mw1 = nw1;
@@ -197,7 +209,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      // step u = (kk, kb) = (u / 2, u % 2); K fragments read two steps ahead
+      // step u = (kk, kb) = (u / 2, u % 2); K fragments read three steps ahead
       auto kfrag = [&](int u) {
         const int kk = u >> 1, kb = u & 1, rho = kb * 32 + l32;
         const int off = kk < 8 ? ST_KN + rho * 128 + xk[kk] : ST_KPE + rho * 64 + xp[kb][kk - 8];
@@ -206,9 +218,10 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
       bf16x8 kf[24];   // one value per unrolled step (no register copies)
       kf[0] = kfrag(0);
       kf[1] = kfrag(1);
+      kf[2] = kfrag(2);
 #pragma unroll
       for (int u = 0; u < 24; ++u) {
-        if (u + 2 < 24) kf[u + 2] = kfrag(u + 2);
+        if (u + 3 < 24) kf[u + 3] = kfrag(u + 3);
         s[u & 1] = mfma32(kf[u], qf[u >> 1], s[u & 1]);
       }
       // s[kb][r] holds key k0 + 32kb + 16(r/8) + 8hi + r%8
@@ -238,13 +251,17 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
+        for (int half = 0; half < 2; ++half) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][half * 8 + e], sl2, -ms));
-            l += p;
-            pf[kb * 2 + half][e] = (__bf16)p;
+          for (int e = 0; e < 8; ++e)
+            pf[kb * 2 + half][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][half * 8 + e], sl2, -ms));
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pr = {pf[kb * 2 + half][e], pf[kb * 2 + half][e + 1]};
+            if (kb) l1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l1, false);
+            else l0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l0, false);
           }
+        }
       // O^T += V^T . P^T; step ks covers keys 32(ks/2) + 16(ks%2) + 8hi + 0..7
       // step u = (ks, j) = (u / 4, u % 4); V^T fragments read two steps ahead
       auto vfrag = [&](int u) {
@@ -260,7 +277,12 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
         if (u + 2 < 16) vf[u + 2] = vfrag(u + 2);
         o[u & 3] = mfma32(vf[u], pf[u >> 2], o[u & 3]);
       }
+    };
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      tile(kt, std::integral_constant<int, 0>());
+      if (kt + 1 < ntiles) tile(kt + 1, std::integral_constant<int, 1>());
     }
+    l = l0 + l1;
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();   // the stages are free for another pass
     if (mode == 0) {

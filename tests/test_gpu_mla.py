@@ -62,6 +62,14 @@ def test_prefill_small_fp8():
                    tol=FP8_TOL, cos=0.999)
 
 
+def test_prefill_ragged_batches_cross_store_groups():
+    # T = 261: the second sequence starts inside a group of 8 token rows, so
+    # kv_b's v^T stores take both the 16-byte and the element-wise path
+    _check_prefill(small_cfg(T=261, B=2, n_heads=2), 27)
+    _check_prefill(small_cfg(T=261, B=2, dim=1024, q_lora_rank=512, kv_lora_rank=512, n_heads=2, weight="e4m3"), 28,
+                   tol=FP8_TOL, cos=0.999)
+
+
 def test_prefill_single_token_and_tiny_T():
     _check_prefill(small_cfg(T=1, B=3), 25)
     _check_prefill(small_cfg(T=2, B=1, topk=1), 26)
