@@ -140,27 +140,22 @@ __device__ __forceinline__ void quant_dequant_tile(uint16_t* st, int tid) {
       amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[e] << 16)), fabsf(__uint_as_float(w[e] & 0xffff0000u))));
   }
   amax = fmaxf(amax, __shfl_xor(amax, 1));
-  const float s = amax / 448.0f;
-  const float rc = s != 0.f ? 1.0f / s : 0.f;
-  // x / s: q0 = x * rc (rc correctly rounded), then one residual step
-  auto quo = [&](float x) {
-    const float q0 = x * rc;
-    return __builtin_fmaf(__builtin_fmaf(-q0, s, x), rc, q0);
-  };
+  e4m3_quotients(amax, true, [&](const float s, auto quo) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-    uint32_t o[4];
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      uint32_t o[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xffff0000u);
-      const int code = __builtin_amdgcn_cvt_pk_fp8_f32(quo(x0), quo(x1), 0, false);
-      const float2v d = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
-      o[e] = pack_bf16x2(d[0] * s, d[1] * s);
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xffff0000u);
+        const int code = __builtin_amdgcn_cvt_pk_fp8_f32(quo(x0), quo(x1), 0, false);
+        const float2v d = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
+        o[e] = pack_bf16x2(d[0] * s, d[1] * s);
+      }
+      const int ch = 8 * hf + i;
+      *(uint4*)(st + r * 512 + ((16 * g + (ch ^ swl(r))) << 3)) = make_uint4(o[0], o[1], o[2], o[3]);
     }
-    const int ch = 8 * hf + i;
-    *(uint4*)(st + r * 512 + ((16 * g + (ch ^ swl(r))) << 3)) = make_uint4(o[0], o[1], o[2], o[3]);
-  }
+  });
 }
 
 // Partial scores of one tile over the wave's half of the contracted dims:

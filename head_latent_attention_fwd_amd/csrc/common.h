@@ -55,4 +55,27 @@ __device__ __forceinline__ floatx16 mfma32_fp8(intx8 a, intx8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// Quotients x / s of the e4m3 activation quantisers, s = amax / 448, for a
+// group whose values x (|x| <= amax) and amax are bf16 values. For
+// amax >= 2^-60 the correctly rounded reciprocal rc = 1 / s, q0 = x rc and one
+// residual step q0 + (x - q0 s) rc (the residual exact in one FMA) equal the
+// correctly rounded quotient for every such pair (checked exhaustively over
+// all bf16 x and amax; quotients below 2^-12, code 0 either way, aside).
+// Smaller groups, and values that are not bf16 (bf16_values = false), divide;
+// an all-zero group (s = 0) gives zero quotients. body(s, quo) runs once with
+// the quotient function the group takes, so the choice is one branch per group.
+template <class Body>
+__device__ __forceinline__ void e4m3_quotients(float amax, bool bf16_values, Body&& body) {
+  const float s = amax / 448.0f;
+  if (bf16_values && amax >= 0x1p-60f) {
+    const float rc = 1.0f / s;
+    body(s, [s, rc](float x) {
+      const float q0 = x * rc;
+      return __builtin_fmaf(__builtin_fmaf(-q0, s, x), rc, q0);
+    });
+  } else {
+    body(s, [s](float x) { return s != 0.f ? x / s : 0.f; });
+  }
+}
+
 __device__ __forceinline__ int row32(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }

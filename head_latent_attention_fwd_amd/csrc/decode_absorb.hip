@@ -341,18 +341,19 @@ __global__ __launch_bounds__(256, 1) void decode_unabsorb_kernel(UnabsorbArgs a)
   if (a.oq) {   // one 1x128 group per (row, head): lanes L, L + 16, L + 32, L + 48 hold it
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
-    const float sc = amax / 448.0f;
-    uint8_t* q = a.oq + (int64_t)bq * a.ldo + 128 * h + 4 * g4;
+    e4m3_quotients(amax, true, [&](const float sc, auto quo) {
+      uint8_t* q = a.oq + (int64_t)bq * a.ldo + 128 * h + 4 * g4;
 #pragma unroll
-    for (int jt = 0; jt < 8; ++jt) {
-      uint32_t code = 0u;
-      if (sc != 0.f)
-        code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
-            v[jt][2] / sc, v[jt][3] / sc, __builtin_amdgcn_cvt_pk_fp8_f32(v[jt][0] / sc, v[jt][1] / sc, 0, false),
-            true);
-      *(uint32_t*)(q + 16 * jt) = code;
-    }
-    if (g4 == 0) a.os[(int64_t)bq * (a.ldo / 128) + h] = sc;
+      for (int jt = 0; jt < 8; ++jt) {
+        uint32_t code = 0u;
+        if (sc != 0.f)
+          code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+              quo(v[jt][2]), quo(v[jt][3]), __builtin_amdgcn_cvt_pk_fp8_f32(quo(v[jt][0]), quo(v[jt][1]), 0, false),
+              true);
+        *(uint32_t*)(q + 16 * jt) = code;
+      }
+      if (g4 == 0) a.os[(int64_t)bq * (a.ldo / 128) + h] = sc;
+    });
   }
 }
 

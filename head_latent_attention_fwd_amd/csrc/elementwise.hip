@@ -223,13 +223,14 @@ __global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
         float amax = fmaxf(fmaxf(fabsf(y0), fabsf(y1)), fmaxf(fabsf(y2), fabsf(y3)));
 #pragma unroll
         for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-        const float s = amax / 448.0f;
-        uint32_t code = 0u;
-        if (s != 0.f)
-          code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
-              y2 / s, y3 / s, __builtin_amdgcn_cvt_pk_fp8_f32(y0 / s, y1 / s, 0, false), true);
-        *(uint32_t*)(a.q_codes + (int64_t)row * a.Dq + 4 * c) = code;
-        if ((c & 31) == 0) a.q_scales[(int64_t)row * (a.Dq >> 7) + (c >> 5)] = s;
+        e4m3_quotients(amax, true, [&](const float s, auto quo) {
+          uint32_t code = 0u;
+          if (s != 0.f)
+            code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+                quo(y2), quo(y3), __builtin_amdgcn_cvt_pk_fp8_f32(quo(y0), quo(y1), 0, false), true);
+          *(uint32_t*)(a.q_codes + (int64_t)row * a.Dq + 4 * c) = code;
+          if ((c & 31) == 0) a.q_scales[(int64_t)row * (a.Dq >> 7) + (c >> 5)] = s;
+        });
       }
     } else if (c < nq + nkv && kv) {
       const int e = 4 * (c - nq);
@@ -243,13 +244,14 @@ __global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
         float amax = fmaxf(fmaxf(fabsf(y0), fabsf(y1)), fmaxf(fabsf(y2), fabsf(y3)));
 #pragma unroll
         for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-        const float s = amax / 448.0f;
-        uint32_t code = 0u;
-        if (s != 0.f)
-          code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
-              y2 / s, y3 / s, __builtin_amdgcn_cvt_pk_fp8_f32(y0 / s, y1 / s, 0, false), true);
-        *(uint32_t*)(a.kv_codes + (int64_t)row * a.L + e) = code;
-        if (((c - nq) & 31) == 0) a.kv_scales[(int64_t)row * (a.L >> 7) + ((c - nq) >> 5)] = s;
+        e4m3_quotients(amax, true, [&](const float s, auto quo) {
+          uint32_t code = 0u;
+          if (s != 0.f)
+            code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+                quo(y2), quo(y3), __builtin_amdgcn_cvt_pk_fp8_f32(quo(y0), quo(y1), 0, false), true);
+          *(uint32_t*)(a.kv_codes + (int64_t)row * a.L + e) = code;
+          if (((c - nq) & 31) == 0) a.kv_scales[(int64_t)row * (a.L >> 7) + ((c - nq) >> 5)] = s;
+        });
       }
     }
   }
@@ -331,18 +333,19 @@ __global__ __launch_bounds__(256) void silu_mul_quant_kernel(const void* gu, int
   }
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-  const float sc = amax / 448.0f;
-  uint2 code = make_uint2(0u, 0u);
-  if (sc != 0.f) {
-    code.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2] / sc, y[3] / sc,
-                                                        __builtin_amdgcn_cvt_pk_fp8_f32(y[0] / sc, y[1] / sc, 0, false),
-                                                        true);
-    code.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6] / sc, y[7] / sc,
-                                                        __builtin_amdgcn_cvt_pk_fp8_f32(y[4] / sc, y[5] / sc, 0, false),
-                                                        true);
-  }
-  *(uint2*)(hq + r * cols + c) = code;
-  if ((c & 127) == 0) hs[r * (cols / 128) + c / 128] = sc;
+  e4m3_quotients(amax, true, [&](const float sc, auto quo) {
+    uint2 code = make_uint2(0u, 0u);
+    if (sc != 0.f) {
+      code.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(quo(y[2]), quo(y[3]),
+                                                          __builtin_amdgcn_cvt_pk_fp8_f32(quo(y[0]), quo(y[1]), 0, false),
+                                                          true);
+      code.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(quo(y[6]), quo(y[7]),
+                                                          __builtin_amdgcn_cvt_pk_fp8_f32(quo(y[4]), quo(y[5]), 0, false),
+                                                          true);
+    }
+    *(uint2*)(hq + r * cols + c) = code;
+    if ((c & 127) == 0) hs[r * (cols / 128) + c / 128] = sc;
+  });
 }
 
 // Strided row copy, one 16-byte chunk per thread.
@@ -438,18 +441,19 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* a, int64_t
   for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));   // within the 16 lanes
-  const float s = amax / 448.0f;
-  uint2 code = make_uint2(0u, 0u);
-  if (s != 0.f) {
-    code.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2] / s, v[3] / s,
-                                                        __builtin_amdgcn_cvt_pk_fp8_f32(v[0] / s, v[1] / s, 0, false),
-                                                        true);
-    code.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[6] / s, v[7] / s,
-                                                        __builtin_amdgcn_cvt_pk_fp8_f32(v[4] / s, v[5] / s, 0, false),
-                                                        true);
-  }
-  *(uint2*)(q + (int64_t)m * K + g * 128 + sub * 8) = code;
-  if (sub == 0) scales[(int64_t)m * G + g] = s;
+  e4m3_quotients(amax, dt != DT_F32, [&](const float s, auto quo) {
+    uint2 code = make_uint2(0u, 0u);
+    if (s != 0.f) {
+      code.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(quo(v[2]), quo(v[3]),
+                                                          __builtin_amdgcn_cvt_pk_fp8_f32(quo(v[0]), quo(v[1]), 0, false),
+                                                          true);
+      code.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(quo(v[6]), quo(v[7]),
+                                                          __builtin_amdgcn_cvt_pk_fp8_f32(quo(v[4]), quo(v[5]), 0, false),
+                                                          true);
+    }
+    *(uint2*)(q + (int64_t)m * K + g * 128 + sub * 8) = code;
+    if (sub == 0) scales[(int64_t)m * G + g] = s;
+  });
 }
 
 // One block per 128x128 weight block.

@@ -331,21 +331,22 @@ __device__ __forceinline__ void gemm_skinny_fp8_body(const SkinnyArgs& g) {
         amax = fmaxf(amax, fabsf(acc[j][r]));
       }
     amax = fmaxf(amax, __shfl_xor(amax, 32));
-    const float s = amax / 448.0f;
     if (m >= M) return;
     uint8_t* qrow = g.qc + (int64_t)m * g.ldc + (int64_t)z * g.batch_c;
+    e4m3_quotients(amax, true, [&](const float s, auto quo) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const float v0 = acc[j][4 * rg], v1 = acc[j][4 * rg + 1], v2 = acc[j][4 * rg + 2], v3 = acc[j][4 * rg + 3];
-        uint32_t code = 0u;
-        if (s != 0.f)
-          code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
-              v2 / s, v3 / s, __builtin_amdgcn_cvt_pk_fp8_f32(v0 / s, v1 / s, 0, false), true);
-        *(uint32_t*)(qrow + 32 * j + 8 * rg + 4 * hi) = code;
-      }
-    if (hi == 0) g.qs[(int64_t)m * (g.ldc / 128) + z * (g.batch_c / 128)] = s;
+        for (int rg = 0; rg < 4; ++rg) {
+          const float v0 = acc[j][4 * rg], v1 = acc[j][4 * rg + 1], v2 = acc[j][4 * rg + 2], v3 = acc[j][4 * rg + 3];
+          uint32_t code = 0u;
+          if (s != 0.f)
+            code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+                quo(v2), quo(v3), __builtin_amdgcn_cvt_pk_fp8_f32(quo(v0), quo(v1), 0, false), true);
+          *(uint32_t*)(qrow + 32 * j + 8 * rg + 4 * hi) = code;
+        }
+      if (hi == 0) g.qs[(int64_t)m * (g.ldc / 128) + z * (g.batch_c / 128)] = s;
+    });
     return;
   }
   if (m >= M) return;
