@@ -78,4 +78,12 @@ __device__ __forceinline__ void e4m3_quotients(float amax, bool bf16_values, Bod
   }
 }
 
+// Stores marked non-temporal, for the large GEMM outputs (kv_b's k_nope /
+// v^T, q_b's q, wo's output): written once, read by a later kernel, too big to
+// stay in the caches anyway. Measured on the e4m3 prefill GEMMs: 3-10 % faster
+// than plain stores.
+__device__ __forceinline__ void store_nt16(void* p, uint4 v) {
+  __builtin_nontemporal_store((intx4){(int)v.x, (int)v.y, (int)v.z, (int)v.w}, (intx4*)p);
+}
+
 __device__ __forceinline__ int row32(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }

@@ -406,7 +406,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
       if (m >= M) continue;
       const int bb = m / g.kv.T, tt = m - bb * g.kv.T;
       const int64_t bh = (int64_t)bb * g.kv.H + h;
-      *(uint4*)(C + (bh * g.kv.Tp + tt) * 128 + ch) = *(const uint4*)(crow(row) + ch);
+      store_nt16(C + (bh * g.kv.Tp + tt) * 128 + ch, *(const uint4*)(crow(row) + ch));
     }
     for (int c = tid; c < 256 * 16; c += 512) {
       const int row = c & 255, ch = (c >> 8) * 8, m = m0 + row;
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
     if (m >= M || n >= nend) continue;
     const uint4 v = *(const uint4*)(crow(row) + ch);
     if (n + 8 <= nend) {
-      *(uint4*)(C + (int64_t)m * g.ldc + n) = v;
+      store_nt16(C + (int64_t)m * g.ldc + n, v);
     } else {
       const uint16_t* e = (const uint16_t*)&v;
 #pragma unroll

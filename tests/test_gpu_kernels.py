@@ -103,6 +103,28 @@ def test_gemm_fp8_blockscaled(M, N, K):
     assert_parity(C.cpu().numpy(), ref, tol=1e-4, cos=0.999999, what="fp8 gemm")
 
 
+@pytest.mark.parametrize("M,N,K,out", [(4352, 4096, 512, torch.bfloat16), (600, 2112, 1024, torch.float32),
+                                       (1000, 1280, 2048, torch.bfloat16)])
+def test_gemm_fp8_blockscaled_many_tiles(M, N, K, out):
+    # more 256 x 256 tiles than CUs (a workgroup walks several, carrying the
+    # next tile's first K groups over), a ragged last row tile, a 64-wide last
+    # column tile (N = 2112), bf16 and fp32 outputs
+    rng = np.random.default_rng(M * 7 + N + K)
+    a = synth.round_bf16(rng.standard_normal((M, K)))
+    w = (rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
+    Aq, As = api.mla_quant_e4m3_1x128(dev(a, torch.bfloat16))
+    Wq, Ws = api.mla_quant_e4m3_block128(dev(w, torch.float32))
+    C = torch.full((M, N), 7.0, dtype=out, device=DEV)
+    api.gemm_fp8_blockscaled(Aq, As, Wq, Ws, C)
+    ac, as_ = fp8.quant_act_1x128(a, quotient="f32")
+    wc, ws = fp8.quant_weight_block128(w)
+    ref = fp8.fp8_gemm(ac, as_, wc, ws)
+    if out == torch.bfloat16:
+        ref = synth.round_bf16(ref)
+    assert_parity(C.float().cpu().numpy(), ref, tol=1e-4 if out == torch.float32 else 8e-3, cos=0.999999,
+                  what="fp8 gemm, many tiles")
+
+
 def test_rmsnorm_rope_kv_and_q_layouts():
     rng = np.random.default_rng(3)
     T = 77
