@@ -416,7 +416,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
       const int bb = m / g.kv.T, tt = m - bb * g.kv.T;
       uint16_t* vt = (uint16_t*)g.kv.vt + (((int64_t)bb * g.kv.H + h) * 128 + ch) * g.kv.Tp + tt;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) vt[(int64_t)k * g.kv.Tp] = e[k];
+      for (int k = 0; k < 8; ++k) __builtin_nontemporal_store(e[k], vt + (int64_t)k * g.kv.Tp);
     }
     return;
   }
