@@ -537,7 +537,7 @@ def main():
         samples = {2: 24, 1: 256, 3: 32, 4: 64}
         base = {}
         for c, rows in samples.items():
-            print(f"[bench] cpu baseline config {c}", file=sys.stderr, flush=True)
+            print(f"[bench] cpu baseline, workload {c}, {rows} sampled rows", file=sys.stderr, flush=True)
             base[str(c)] = cpu_baseline(c, rows)
         line["cpu_baseline"] = base[str(HEADLINE)]
         line["cpu_baselines"] = base

@@ -10,10 +10,14 @@
 // 16-byte chunks XOR-permuted within aligned groups of 16 by
 // ((j & 3) << 2) | ((j >> 2) & 3). The product C^T[c, b] = W_UK_h^T[c, j] .
 // q^T[j, b] runs on v_mfma_f32_32x32x16_bf16 with W_UK_h^T read by
-// ds_read_b64_tr_b16 and q read straight from global memory; a lane's results
-// are 4 consecutive c of one sequence, stored as 8-byte pieces. Wave w covers
-// c in [256 z + 128 (w & 1), +128) and sequences [32 (w >> 1), +32) of the tile.
-// The q_pe rotation of the tile is split between the two halves by pair index.
+// ds_read_b64_tr_b16 and q read straight from global memory, one 16-byte load
+// per K step (the k slots of half hi of step ks are rows 16 ks + 8 hi + 0..7).
+// Wave w covers c in [256 z + 128 (w & 1), +128) and sequences [32 (w >> 1),
+// +32) of the tile. The results go back through LDS (the W half's space, as
+// [128 sequences][256 c] bf16, 16-byte chunk k of row r at k ^ (r & 31)) so
+// that each sequence's 512-byte piece of q_lat is written by 32 adjacent
+// 16-byte stores. The q_pe rotation of the tile is split between the two
+// halves by pair index.
 //
 // With e4m3 weights the half tile is read as codes, expanded to bf16 (exact:
 // every e4m3 value is a bf16 value) and written to LDS in the same layout; the
@@ -86,17 +90,14 @@ __global__ __launch_bounds__(512, 2) void decode_absorb_kernel(const uint16_t* _
   }
 
   // q fragments (B operand): lane (sequence l32, half hi) holds, for k-step
-  // ks, q_nope dims 16 ks + 4 hi + 0..3 and 16 ks + 8 + 4 hi + 0..3
+  // ks, q_nope dims 16 ks + 8 hi + 0..7
   const int l32 = lane & 31, hi = lane >> 5, wc = wave & 1, wb = wave >> 1;
   const int bq = b0 + wb * 32 + l32;
   bf16x8 qf[8];
   {
-    const uint16_t* qp = q + ((int64_t)min(bq, B - 1) * H + h) * 192 + 4 * hi;
+    const uint16_t* qp = q + ((int64_t)min(bq, B - 1) * H + h) * 192 + 8 * hi;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint2 lo = *(const uint2*)(qp + 16 * ks), up = *(const uint2*)(qp + 16 * ks + 8);
-      qf[ks] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, up.x, up.y));
-    }
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(qp + 16 * ks);
   }
 
   // q_pe rotation: thread handles pair d = 16 z + (tid & 15) of sequences
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(512, 2) void decode_absorb_kernel(const uint16_t* _
   }
   __syncthreads();
 
-  // W^T fragments: 16-lane group g reads rows j = 16 ks + 4 (g >> 1) + 8 e + (lane % 16) / 4,
+  // W^T fragments: 16-lane group g reads rows j = 16 ks + 8 (g >> 1) + 4 e + (lane % 16) / 4,
   // columns c = 128 wc + 32 cb + 16 (g & 1) + 4 (lane % 4) of the half
   const int g = lane >> 4, L = lane & 15;
   floatx16 acc[4];
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(512, 2) void decode_absorb_kernel(const uint16_t* _
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int c = 128 * wc + 32 * cb + 16 * (g & 1) + 4 * (L & 3);
-      const int j0 = 16 * ks + 4 * (g >> 1) + (L >> 2), j1 = j0 + 8;
+      const int j0 = 16 * ks + 8 * (g >> 1) + (L >> 2), j1 = j0 + 4;
       const int ch = c >> 3;   // 16-byte chunk of column c
       const uint16_t* p0 = sw + j0 * 256 + ((((ch & 15) ^ swj(j0)) | (ch & 16)) << 3) + (c & 7);
       const uint16_t* p1 = sw + j1 * 256 + ((((ch & 15) ^ swj(j1)) | (ch & 16)) << 3) + (c & 7);
@@ -160,14 +161,26 @@ __global__ __launch_bounds__(512, 2) void decode_absorb_kernel(const uint16_t* _
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[cb][r] *= sc;
   }
-  if (bq < B) {
-    uint16_t* o = qlat + ((int64_t)bq * H + h) * 576 + 256 * z + 128 * wc + 4 * hi;
+  __syncthreads();   // every wave is done reading the W half
+  {
+    const int r = wb * 32 + l32;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg)
-        *(uint2*)(o + 32 * cb + 8 * rg) = make_uint2(pack_bf16x2(acc[cb][4 * rg], acc[cb][4 * rg + 1]),
-                                                     pack_bf16x2(acc[cb][4 * rg + 2], acc[cb][4 * rg + 3]));
+      for (int rg = 0; rg < 4; ++rg) {
+        const int k = 16 * wc + 4 * cb + rg;   // 16-byte chunk of c = 128 wc + 32 cb + 8 rg
+        *(uint2*)(sw + r * 256 + ((k ^ (r & 31)) << 3) + 4 * hi) =
+            make_uint2(pack_bf16x2(acc[cb][4 * rg], acc[cb][4 * rg + 1]),
+                       pack_bf16x2(acc[cb][4 * rg + 2], acc[cb][4 * rg + 3]));
+      }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {   // pass i: rows 16 i + tid / 32, chunk tid % 32
+    const int r = 16 * i + (tid >> 5), k = tid & 31;
+    if (b0 + r < B)
+      *(uint4*)(qlat + ((int64_t)(b0 + r) * H + h) * 576 + 256 * z + 8 * k) =
+          *(const uint4*)(sw + r * 256 + ((k ^ (r & 31)) << 3));
   }
 }
 
@@ -202,9 +215,10 @@ hipError_t launch_decode_absorb(const void* q, const void* wkv_b, const float* w
 // rows 16w..16w+15 and all 128 j on v_mfma_f32_16x16x32_bf16 (W_UV_h as the
 // first operand, so a lane's results are 4 consecutive j of one row). W_UV_h
 // [128 j, 512 c] sits in LDS as bf16 (128 KB), 16-byte chunk ch of row j at
-// chunk ch ^ (j & 15) of the row. Outputs: o in bf16 and, for an e4m3 wo, o's
-// codes and its scale per (row, head) (one 1x128 group), quantised from the
-// bf16 values.
+// chunk ch ^ (j & 15) of the row. Outputs: o in bf16 (staged through LDS so
+// that each row's 256-byte piece goes out as 16 adjacent 16-byte stores) and,
+// for an e4m3 wo, o's codes and its scale per (row, head) (one 1x128 group),
+// quantised from the bf16 values.
 namespace mla {
 namespace {
 
@@ -321,9 +335,7 @@ __global__ __launch_bounds__(256, 1) void decode_unabsorb_kernel(UnabsorbArgs a)
       acc[jt] = mfma16(wfr, bfr, acc[jt]);
     }
   }
-  if (!row_ok) return;
   // lane: row bq, j = 16 jt + 4 g4 + 0..3
-  uint16_t* o = a.o ? (uint16_t*)a.o + (int64_t)bq * a.ldo + 128 * h + 4 * g4 : nullptr;
   float v[8][4];
   float amax = 0.f;
 #pragma unroll
@@ -333,11 +345,25 @@ __global__ __launch_bounds__(256, 1) void decode_unabsorb_kernel(UnabsorbArgs a)
       v[jt][r] = __uint_as_float((uint32_t)f2bf(acc[jt][r]) << 16);
       amax = fmaxf(amax, fabsf(v[jt][r]));
     }
-  if (o) {
+  if (a.o) {   // through LDS: [64 rows][128 j] bf16, 16-byte chunk k of row r at k ^ (r & 15)
+    __syncthreads();   // every wave is done reading W_UV_h
+    const int r = 16 * wave + L;
 #pragma unroll
-    for (int jt = 0; jt < 8; ++jt)
-      *(uint2*)(o + 16 * jt) = make_uint2(pack_bf16x2(v[jt][0], v[jt][1]), pack_bf16x2(v[jt][2], v[jt][3]));
+    for (int jt = 0; jt < 8; ++jt) {
+      const int k = 2 * jt + (g4 >> 1);
+      *(uint2*)(sw + r * 128 + ((k ^ (r & 15)) << 3) + 4 * (g4 & 1)) =
+          make_uint2(pack_bf16x2(v[jt][0], v[jt][1]), pack_bf16x2(v[jt][2], v[jt][3]));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {   // pass i: rows 16 i + tid / 16, chunk tid % 16
+      const int rr = 16 * i + (tid >> 4), k = tid & 15;
+      if (b0 + rr < a.B)
+        *(uint4*)((uint16_t*)a.o + (int64_t)(b0 + rr) * a.ldo + 128 * h + 8 * k) =
+            *(const uint4*)(sw + rr * 128 + ((k ^ (rr & 15)) << 3));
+    }
   }
+  if (!row_ok) return;
   if (a.oq) {   // one 1x128 group per (row, head): lanes L, L + 16, L + 32, L + 48 hold it
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
