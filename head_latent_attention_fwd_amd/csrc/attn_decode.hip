@@ -7,32 +7,36 @@
 //   z[h, t] = scale * (q_lat[h] . C_t),  o_lat[h] = sum_t softmax_t(z[h]) C_t[:512]
 // so one cache tile in LDS serves every head of the row.
 //
-// Workgroup = (row q, group of 64 heads, key run j), four waves. The key
-// range of a row is cut into `splits` runs of whole 32-key tiles (as many as
-// it takes for rows x head groups x runs to fill the chip); with one run the
-// workgroup writes the normalised o_lat, otherwise its normalised partial and
-// its log2-sum-exp, which the consumer merges in run order
-// (launch_decode_combine or the un-absorb kernel). All workgroups of a row are
-// placed on one XCD, so the second head group's read of a cache tile comes
-// from that XCD's L2.
+// Workgroup = (row q, group of 64 heads, key run j), eight waves in two roles
+// (two waves per SIMD, one of each). The key range of a row is cut into
+// `splits` runs of whole 32-key tiles (as many as it takes for rows x head
+// groups x runs to fill the chip); with one run the workgroup writes the
+// normalised o_lat, otherwise its normalised partial and its log2-sum-exp,
+// which the consumer merges in run order (launch_decode_combine or the
+// un-absorb kernel). All workgroups of a row are placed on one XCD, so the
+// second head group's read of a cache tile comes from that XCD's L2.
 //
-// Wave (hb, dh) = (wave & 1, wave >> 1) serves heads 32hb..32hb+31 of the group:
-//   scores  S^T[t, h] = C[t, :] . Q^T[:, h]   each wave of the pair (hb, 0) /
-//           (hb, 1) takes one half of the 576 contracted dims (its half of Q
-//           stays in registers) and the pair adds the two fp32 partials
-//           through LDS, in the same order;
-//   values  O^T[d, h] += C^T[d, t] . P^T[t, h] for the wave's 256 latent dims,
-// both on v_mfma_f32_32x32x16_bf16 (C^T read with ds_read_b64_tr_b16). A
-// lane's score results are 16 keys of one head, exactly the k slots the value
-// product needs from P^T, so the probabilities stay in registers. Cache tiles
-// move HBM -> LDS with 16-byte direct-to-LDS buffer loads through a 3-stage
-// ring (two tiles in flight).
+//   score wave s (waves 0..3), heads 16 s .. 16 s + 15 of the group: the
+//     whole 576-dim product S^T[t, h] = C[t, :] . Q^T[:, h] on
+//     v_mfma_f32_16x16x32_bf16 (its query stays in registers), the softmax,
+//     and the tile's probabilities P[h, t] (bf16) into an LDS buffer;
+//   value wave v (waves 4..7), latent dims 128 v .. 128 v + 127 of every head
+//     of the group: O^T[d, h] += C^T[d, t] . P^T[t, h] on
+//     v_mfma_f32_32x32x16_bf16, one tile behind the score waves (C^T read with
+//     ds_read_b64_tr_b16, P^T as 16-byte rows of the buffer).
+// Cache tiles move HBM -> LDS by 16-byte direct-to-LDS loads through a
+// 3-stage ring with two tiles in flight. A value wave reloads the 8 KB of the
+// stage that only it reads (its 128 dims of the 32 rows) as soon as its own
+// fragments of the tile are in registers; the score waves reload the rope
+// rows one tile later, after every score wave has read them. One barrier per
+// tile orders it all.
 //
-// Softmax: the running max of a head is fixed at its first live tile and
-// later tiles add exp2(z - m) <= 2^LAZY, so the accumulators are never
-// rescaled inside the loop. If a later score exceeds m + LAZY (a logit jump
-// of ~44 nats) the workgroup recomputes its output in two passes: exact
-// maxima first, then the accumulation with those maxima.
+// Softmax: the running max of a head stays at its first live tile's value
+// while later tiles add exp2(z - m) <= 2^LAZY. A tile whose max exceeds
+// m + LAZY (a logit jump of ~44 nats) moves m to that max; the score wave
+// scales its row sum by exp2(m_old - m_new) and hands the same factor to the
+// value waves with the tile's probabilities, which scale their accumulators
+// before adding the tile (a wave-uniform branch taken only then).
 //
 // Selected keys: launch_decode_compact first turns each row's index list into
 // its ascending, duplicate-free list of live positions; the workgroup copies
@@ -43,19 +47,17 @@
 // e4m3 weights (QLAT): kv_b is an e4m3 Linear whose input, the latent, is
 // quantised in dynamic 1x128 groups (Kimi K2 · Down projection,
 // quantization_config). The absorbed product therefore sees each latent as
-// its dequantised value: once a tile has landed, the workgroup replaces every
-// latent 128-group of the tile in LDS by scale * e4m3(x / scale) (scale =
-// amax / 448 in fp32, quotient from the correctly rounded reciprocal plus one
-// residual correction), rounded to bf16. The rope key is not an input of kv_b
-// and is used as cached.
+// its dequantised value: once a tile has landed, the score waves replace
+// every latent 128-group of the tile in LDS by scale * e4m3(x / scale)
+// (scale = amax / 448 in fp32, quotient from the correctly rounded reciprocal
+// plus one residual correction), rounded to bf16, before anyone reads it. The
+// rope key is not an input of kv_b and is used as cached.
 //
-// LDS stage: latent rows [32][1024 B] then rope rows [32][128 B]. The 16-byte
-// chunks of latent row r are XOR-permuted within aligned groups of 16 by
-// ((r & 3) << 2) | ((r >> 2) & 3) and those of rope row r by (r >> 1) & 7, so
-// the row reads of the scores and the transposed reads of the values are free
-// of bank conflicts. The stages are distinct LDS objects and every access
-// names its stage statically, so the compiler can tell the reads of one stage
-// from the loads in flight into the others.
+// LDS stage: the latent as four 128-dim groups, each [32 rows][256 B], then
+// the rope rows [32][128 B]. The 16-byte chunks of a latent group's row r are
+// XOR-permuted by ((r & 3) << 2) | ((r >> 2) & 3) and those of rope row r by
+// (r >> 1) & 7, so the score waves' row reads and the value waves' transposed
+// reads are free of bank conflicts.
 #include <mutex>
 
 #include "common.h"
@@ -66,10 +68,11 @@ namespace {
 
 constexpr int DKT = 32;                 // keys per tile
 constexpr int DROW = 576;               // elements per cache row
-constexpr int DLAT = DKT * 512;         // latent region of a stage (elements)
+constexpr int DGRP = DKT * 128;         // elements of one 128-dim latent group of a stage
+constexpr int DLAT = 4 * DGRP;          // latent region of a stage (elements)
 constexpr int DSTAGE = DKT * DROW;      // elements per stage
-constexpr float LAZY = 64.f;            // log2-domain headroom over the fixed running max
-constexpr int KEYS_LDS = DECODE_TOPK_MAX + 4 * DKT;   // a split's keys plus the tiles issued past its end
+constexpr float LAZY = 64.f;            // log2-domain headroom over the running max
+constexpr int KEYS_LDS = DECODE_TOPK_MAX + DKT;   // a split's keys plus the rest of its last tile
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
@@ -81,59 +84,29 @@ __device__ __forceinline__ v4s read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
 }
 
-struct DecodeCtx {
-  __amdgpu_buffer_rsrc_t rsrc;   // raw buffer over the cache rows of the row's sequence
-  int k0, nkeys, ntiles, wave, lane, hi, dh;   // keys k0 .. k0 + nkeys - 1 (dense) or list slots (sparse)
-  float sl2;
-  float* xs;                     // [2][4 waves][16][64] partial-score exchange
-  bool sparse;                   // tile rows from `keys` (else keys k0..k0+nkeys-1)
-  const __attribute__((address_space(3))) int* keys;   // the run's selected positions
-};
-
-__device__ __forceinline__ void load_lds16(const DecodeCtx& c, uint16_t* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0,
-                                           0);
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p);
 }
 
-// Loads tile kt of the run into stage st (9 loads per thread): latent
-// instruction i of wave w fills row 8w + i (lane = physical chunk); the rope
-// instruction of wave w fills rows 8w..8w+7 (8 chunks each). Rows past the
-// run's last key repeat it (their scores are masked).
-__device__ __forceinline__ void issue_tile(const DecodeCtx& c, uint16_t* st, int kt) {
-  const int k0 = kt * DKT;
-  if (c.sparse) {   // cache rows from the run's list (slots past its end repeat the last key)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 8 * c.wave + i;
-      load_lds16(c, st + r * 512, (c.lane ^ swl(r)) << 4, __builtin_amdgcn_readfirstlane(c.keys[k0 + r]) * (DROW * 2));
-    }
-    const int r = 8 * c.wave + (c.lane >> 3);
-    const int t = c.keys[k0 + r];
-    load_lds16(c, st + DLAT + c.wave * 512, t * (DROW * 2) + 1024 + (((c.lane & 7) ^ swr(r)) << 4), 0);
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 8 * c.wave + i;
-    const int t = c.k0 + min(k0 + r, c.nkeys - 1);
-    load_lds16(c, st + r * 512, (c.lane ^ swl(r)) << 4, t * (DROW * 2));
-  }
-  const int r = 8 * c.wave + (c.lane >> 3);
-  const int t = c.k0 + min(k0 + r, c.nkeys - 1);
-  load_lds16(c, st + DLAT + c.wave * 512, t * (DROW * 2) + 1024 + (((c.lane & 7) ^ swr(r)) << 4), 0);
+// 16-byte direct-to-LDS load: lane l's bytes land at LDS byte address base + 16 l.
+// Written as asm so that the compiler does not order later LDS reads behind
+// it; the ring's explicit vmcnt waits do.
+__device__ __forceinline__ void dma16(const uint16_t* src, uint32_t base) {
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(base)
+                   : "memory", "m0");
 }
 
-// e4m3 view of a tile's latent: thread (row r = tid / 8, group g = (tid / 2) % 4,
-// half hf = tid % 2) takes the 8 chunks 16 g + 8 hf .. + 7 of row r; the two
-// halves of a group are neighbouring lanes.
+// e4m3 view of a tile's latent (score waves, tid 0..255): thread (row r = tid / 8,
+// group g = (tid / 2) % 4, half hf = tid % 2) takes the 8 chunks 8 hf .. 8 hf + 7
+// of group g of row r; the two halves of a group are neighbouring lanes.
 __device__ __forceinline__ void quant_dequant_tile(uint16_t* st, int tid) {
   const int r = tid >> 3, g = (tid >> 1) & 3, hf = tid & 1;
+  uint16_t* row = st + g * DGRP + r * 128;
   uint4 v[8];
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int ch = 8 * hf + i;   // chunk within the group's aligned 16
-    v[i] = *(const uint4*)(st + r * 512 + ((16 * g + (ch ^ swl(r))) << 3));
+    v[i] = *(const uint4*)(row + (((8 * hf + i) ^ swl(r)) << 3));
     const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -152,165 +125,34 @@ __device__ __forceinline__ void quant_dequant_tile(uint16_t* st, int tid) {
         const float2v d = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
         o[e] = pack_bf16x2(d[0] * s, d[1] * s);
       }
-      const int ch = 8 * hf + i;
-      *(uint4*)(st + r * 512 + ((16 * g + (ch ^ swl(r))) << 3)) = make_uint4(o[0], o[1], o[2], o[3]);
+      *(uint4*)(row + (((8 * hf + i) ^ swl(r)) << 3)) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   });
 }
 
-// Partial scores of one tile over the wave's half of the contracted dims:
-// dh = 0 takes latent chunks 0..35, dh = 1 latent chunks 36..63 and the rope
-// chunks; chunk 2kk + hi meets query fragment kk.
-template <int DH>
-__device__ __forceinline__ floatx16 partial_scores(const uint16_t* st, int srow, int hi, const bf16x8 (&qf)[18]) {
-  auto frag = [&](int kk) {
-    const int c = 36 * DH + 2 * kk;   // + hi
-    if (c < 64) {
-      const int f = swl(srow) ^ hi;
-      return *(const bf16x8*)(st + srow * 512 + ((c & ~15) << 3) + (((c & 15) ^ f) << 3));
-    }
-    return *(const bf16x8*)(st + DLAT + srow * 64 + (((c - 64) ^ (swr(srow) ^ hi)) << 3));
-  };
-  // two accumulators (even / odd k steps) so consecutive MFMAs are independent;
-  // fragments are read two steps ahead
-  floatx16 sa, sb;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    sa[r] = 0.f;
-    sb[r] = 0.f;
-  }
-  bf16x8 f0 = frag(0), f1 = frag(1), f2;
-#pragma unroll
-  for (int kk = 0; kk < 18; ++kk) {
-    if (kk + 2 < 18) f2 = frag(kk + 2);
-    if (kk & 1) sb = mfma32(f0, qf[kk], sb);
-    else sa = mfma32(f0, qf[kk], sa);
-    f0 = f1;
-    f1 = f2;
-  }
-  return sa + sb;
+// LDS waits before a barrier: the wave's own LDS writes done and at most
+// `ahead` of its direct loads still in flight (their counts are wave-uniform).
+template <int N>
+__device__ __forceinline__ void wait_tile(bool more) {
+  if (more) __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  else __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(0)" ::: "memory");
 }
-
-// One pass over the sequence. SCORES_ONLY: m becomes the exact per-head max.
-// Otherwise accumulates o and l against m (set at the first live tile when it
-// is -inf); returns true when a score exceeded m + LAZY (results invalid).
-template <bool SCORES_ONLY, bool QLAT>
-__device__ __forceinline__ bool attn_pass(const DecodeCtx& c, uint16_t* st0, uint16_t* st1, uint16_t* st2,
-                                          const bf16x8 (&qf)[18], float& m, float& l, floatx16 (&o)[8]) {
-  const int lane = c.lane, l32 = lane & 31, hi = c.hi;
-  // transposed reads: 16-lane group q reads rows 16 s + 4 (q >> 1) + 8 e + (lane % 16) / 4,
-  // columns 256 dh + 32 dt + 16 (q & 1) + 4 (lane % 4)
-  const int q4 = lane >> 4, L = lane & 15;
-  const int trow = 4 * (q4 >> 1) + (L >> 2);
-  const int tx = 2 * (q4 & 1) + ((L >> 1) & 1);
-  int toff[2][4];
-#pragma unroll
-  for (int e = 0; e < 2; ++e)
-#pragma unroll
-    for (int d4 = 0; d4 < 4; ++d4) {
-      const int r = trow + 8 * e;
-      toff[e][d4] = r * 512 + 256 * c.dh + (((4 * d4 + tx) ^ swl(r)) << 3) + 4 * (L & 1);
-    }
-  bool over = false;
-  if (!SCORES_ONLY) {
-    l = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  }
-  auto step = [&](int kt, uint16_t* st, uint16_t* next) {
-    __asm__ volatile("s_waitcnt vmcnt(9)" ::: "memory");   // tile kt landed, kt + 1 may be in flight
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-    issue_tile(c, next, kt + 2);   // into the stage tile kt - 1 used
-    if (QLAT) {   // replace the landed tile's latent by its dequantised e4m3 value
-      quant_dequant_tile(st, 64 * c.wave + lane);
-      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // LDS writes only: the loads stay in flight
-      __builtin_amdgcn_s_barrier();
-      __asm__ volatile("" ::: "memory");
-    }
-
-    floatx16 sa = c.dh ? partial_scores<1>(st, l32, hi, qf) : partial_scores<0>(st, l32, hi, qf);
-    float* xw = c.xs + (kt & 1) * (4 * 16 * 64);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) xw[(c.wave * 16 + r) * 64 + lane] = sa[r];
-    // exchange barrier: LDS writes only (a __syncthreads here would also drain the tile loads)
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-    const int k0 = kt * DKT;
-    float part[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) part[r] = xw[((c.wave ^ 2) * 16 + r) * 64 + lane];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sa[r] = (c.dh ? part[r] + sa[r] : sa[r] + part[r]) * c.sl2;   // first + second half
-    if (k0 + DKT > c.nkeys) {   // wave-uniform: the tile runs past the last key
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (k0 + row32(r, lane) >= c.nkeys) sa[r] = -INFINITY;
-    }
-    float mx = sa[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sa[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (SCORES_ONLY) {
-      m = fmaxf(m, mx);
-      return;
-    }
-    if (m == -INFINITY) m = mx;   // first live keys of this head: nothing accumulated yet
-    over |= mx > m + LAZY;
-    bf16x8 pf[2];
-    float rs = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(sa[r] - m);   // masked keys: exp2(-inf) = 0
-      rs += p;
-      pf[r >> 3][r & 7] = (__bf16)p;
-    }
-    l += rs;
-    // value product, step j = (key half j / 8, d tile j % 8): consecutive MFMAs
-    // update different accumulators; C^T fragments read two steps ahead
-    auto vfrag = [&](int j) {
-      const int dt = j & 7, imm = 16 * (j >> 3) * 512 + 128 * (dt >> 2);
-      const v4s lo = read_tr(st + toff[0][dt & 3] + imm), up = read_tr(st + toff[1][dt & 3] + imm);
-      return __builtin_bit_cast(bf16x8, (v8s){lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
-    };
-    bf16x8 vb0 = vfrag(0), vb1 = vfrag(1), vb2;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j + 2 < 16) vb2 = vfrag(j + 2);
-      o[j & 7] = mfma32(vb0, pf[j >> 3], o[j & 7]);
-      vb0 = vb1;
-      vb1 = vb2;
-    }
-  };
-  // The loop runs whole rounds of three tiles and always keeps two tiles in
-  // flight; tiles past the end hold copies of the last key (all masked, p = 0)
-  // and cost a little math. Straight-line rounds let the compiler's own LDS
-  // waits see which stage each load targets.
-  issue_tile(c, st0, 0);
-  issue_tile(c, st1, 1);
-  for (int kt = 0; kt < c.ntiles; kt += 3) {
-    step(kt, st0, st2);
-    step(kt + 1, st1, st0);
-    step(kt + 2, st2, st1);
-  }
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();   // every wave is done with the stages and the exchange buffer
-  return over;
+__device__ __forceinline__ void barrier() {
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
 }
 
 template <bool SPARSE, bool QLAT>
-__global__ __launch_bounds__(256, 1) void decode_attn_kernel(DecodeAttnArgs a, int n_hg) {
-  __shared__ __attribute__((aligned(16))) uint16_t st0[DSTAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t st1[DSTAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t st2[DSTAGE];
-  __shared__ __attribute__((aligned(16))) float xs[2 * 4 * 16 * 64];
+__global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a, int n_hg) {
+  __shared__ __attribute__((aligned(16))) uint16_t stages[3 * DSTAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t pbuf[2][64 * DKT];   // P[h][t] bf16, per tile parity
+  __shared__ float fbuf[2][64];                                          // rescale factor per head
+  __shared__ float s_l[64];
   __shared__ __attribute__((aligned(16))) int keys[SPARSE ? KEYS_LDS : 4];
-  __shared__ int s_over;
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool score = wave < 4;
   const int NS = a.splits;
   // workgroup -> (row q, head group hg, run j); all of a row's workgroups on one XCD
   const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
@@ -319,71 +161,224 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(DecodeAttnArgs a, i
   const int b = a.rows_per_seq > 0 ? q / a.rows_per_seq : q;
   const int P = a.rows_per_seq > 0 ? q - b * a.rows_per_seq : a.cache_len[b];
   const bool valid = P >= 0 && P < a.max_len;
-  DecodeCtx c;
-  c.lane = tid & 63;
-  c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  c.dh = c.wave >> 1;
-  c.hi = c.lane >> 5;
-  c.xs = xs;
-  c.sl2 = a.scale * 1.4426950408889634f;
-  c.sparse = SPARSE;
-  c.keys = (const __attribute__((address_space(3))) int*)keys;
   // the row's keys (positions 0..P, or its compacted list) cut into NS runs of whole tiles
   const int n_all = !valid ? 0 : SPARSE ? a.nkeys[q] : P + 1;
   const int tiles_all = (n_all + DKT - 1) / DKT, tps = (tiles_all + NS - 1) / NS;
   const int kb = min(n_all, j * tps * DKT), ke = min(n_all, (j + 1) * tps * DKT);
-  c.k0 = SPARSE ? 0 : kb;
-  c.nkeys = ke - kb;
+  const int nkeys = ke - kb, nt = (nkeys + DKT - 1) / DKT;
   if (SPARSE) {   // this run's slots of the compacted list, padded with its last key
     const int32_t* row = a.keys + (int64_t)q * a.kstride;
-    const int last = c.nkeys > 0 ? row[ke - 1] : 0;
-    for (int i = tid; i < KEYS_LDS; i += 256) keys[i] = i < c.nkeys ? row[kb + i] : last;
+    const int last = nkeys > 0 ? row[ke - 1] : 0;
+    for (int i = tid; i < KEYS_LDS; i += 512) keys[i] = i < nkeys ? row[kb + i] : last;
     __syncthreads();
   }
-  c.ntiles = (c.nkeys + DKT - 1) / DKT;
-  c.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.cache + (int64_t)b * a.max_len * DROW),
-                                             (short)0, a.max_len * DROW * 2, BUF_DW3);
-  const int head = hg * 64 + (c.wave & 1) * 32 + (c.lane & 31);
+  const uint16_t* cache = (const uint16_t*)a.cache + (int64_t)b * a.max_len * DROW;
+  // cache row of tile slot x of the run (slots past its end repeat its last key)
+  auto key_row = [&](int x) { return SPARSE ? keys[x] : kb + min(x, nkeys - 1); };
+  const float sl2 = a.scale * 1.4426950408889634f;
+  const int64_t hrow0 = (int64_t)q * a.H + hg * 64;   // first (row, head) of the group
 
-  // this wave's half of the query: B operand of the score product, dims 288 dh + 16 kk + 8 hi + 0..7
-  bf16x8 qf[18];
-  {
-    const uint16_t* qp = (const uint16_t*)a.qlat + ((int64_t)q * a.H + head) * DROW + 288 * c.dh + 8 * c.hi;
+  if (score) {
+    // ---------------- score wave s: heads 16 s + (lane % 16) ----------------
+    const int s = wave, hl = 16 * s + (lane & 15), kq = lane >> 4;
+    // query: B operand of the 16x16x32 product, dims 32 ks + 8 kq + 0..7
+    bf16x8 qf[18];
+    {
+      const uint16_t* qp = (const uint16_t*)a.qlat + (hrow0 + hl) * DROW + 8 * kq;
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 16 * kk));
-  }
-  if (tid == 0) s_over = 0;
-  floatx16 o[8];
-  float m = -INFINITY, l = 0.f;
-  bool over = false;
-  if (c.ntiles > 0) over = attn_pass<false, QLAT>(c, st0, st1, st2, qf, m, l, o);
-  else {
+      for (int ks = 0; ks < 18; ++ks) qf[ks] = *(const bf16x8*)(qp + 32 * ks);
+    }
+    // rope rows of tile kt: rows 8 s + lane / 8, physical chunk lane % 8
+    auto issue_rope = [&](int kt, uint16_t* st) {
+      const int r = 8 * s + (lane >> 3);
+      dma16(cache + (int64_t)key_row(kt * DKT + r) * DROW + 512 + (((lane & 7) ^ swr(r)) << 3),
+            lds_addr(st + DLAT + s * 512));
+    };
+    float m = -INFINITY, l = 0.f;
+    if (nt > 0) issue_rope(0, stages);
+    if (nt > 1) issue_rope(1, stages + DSTAGE);
+    int cur = 0;   // stage of tile i
+    for (int i = 0; i <= nt; ++i) {
+      wait_tile<1>(i + 1 < nt);
+      barrier();
+      uint16_t* st = stages + cur * DSTAGE;
+      if (QLAT) {
+        if (i < nt) quant_dequant_tile(st, tid);
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        barrier();
+      }
+      if (i < nt) {
+        // A operand rows t = 16 tb + lane % 16, chunk 4 ks + kq of the 72 in a row
+        auto afrag = [&](int tb, int ks) {
+          const int t = 16 * tb + (lane & 15), c = 4 * ks + kq;
+          if (ks < 16) return *(const bf16x8*)(st + (c >> 4) * DGRP + t * 128 + (((c & 15) ^ swl(t)) << 3));
+          return *(const bf16x8*)(st + DLAT + t * 64 + (((c - 64) ^ swr(t)) << 3));
+        };
+        floatx4 acc[2][2];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+          for (int r = 0; r < 4; ++r) acc[u][0][r] = acc[u][1][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) acc[tb][ks & 1] = mfma16(afrag(tb, ks), qf[ks], acc[tb][ks & 1]);
+        // lane: head hl, keys 16 tb + 4 kq + r of the tile
+        const int k0 = i * DKT;
+        float z[8];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) z[4 * tb + r] = (acc[tb][0][r] + acc[tb][1][r]) * sl2;
+        if (k0 + DKT > nkeys) {   // wave-uniform: the tile runs past the last key
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (k0 + 16 * (e >> 2) + 4 * kq + (e & 3) >= nkeys) z[e] = -INFINITY;
+        }
+        float mx = z[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        float f = 1.f;
+        if (m == -INFINITY) m = mx;   // first live keys of this head: nothing accumulated yet
+        else if (mx > m + LAZY) {     // rare: move the max, rescale what is accumulated
+          f = __builtin_amdgcn_exp2f(m - mx);
+          l *= f;
+          m = mx;
+        }
+        const float mref = m == -INFINITY ? 0.f : m;
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(z[e] - mref);   // masked keys: exp2(-inf) = 0
+          l += p[e];
+        }
+        uint16_t* pb = pbuf[i & 1] + hl * DKT;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {   // keys 16 tb + 4 kq .. +3: chunk 2 tb + kq / 2, half kq % 2
+          const int ch = (2 * tb + (kq >> 1)) ^ ((hl >> 2) & 3);
+          *(uint2*)(pb + (ch << 3) + 4 * (kq & 1)) =
+              make_uint2(pack_bf16x2(p[4 * tb], p[4 * tb + 1]), pack_bf16x2(p[4 * tb + 2], p[4 * tb + 3]));
+        }
+        if (lane < 16) fbuf[i & 1][hl] = f;
+      }
+      // rope rows of tile i + 2 into the stage tile i - 1 used (every score wave read them before this tile's barrier)
+      const int nx = cur == 0 ? 2 : cur - 1;
+      if (i + 2 < nt) issue_rope(i + 2, stages + nx * DSTAGE);
+      cur = cur == 2 ? 0 : cur + 1;
+    }
+    // row sums over the four lanes of a head; log2-sum-exp of a run
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (lane < 16) {
+      s_l[hl] = l;
+      if (NS > 1) a.lse[(int64_t)j * a.R * a.H + hrow0 + hl] = l > 0.f ? m + __log2f(l) : -INFINITY;
+    }
+    __syncthreads();
+    __syncthreads();
+  } else {
+    // ---------------- value wave v: latent dims 128 v .. 128 v + 127 ----------------
+    const int v = wave - 4, hi = lane >> 5, L = lane & 15, q4 = lane >> 4;
+    // latent of tile kt, this wave's group: load i fills rows 4 i + lane / 16, physical chunk lane % 16
+    auto issue_lat = [&](int kt, uint16_t* st) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        dma16(cache + (int64_t)key_row(kt * DKT + r) * DROW + 128 * v + (((lane & 15) ^ swl(r)) << 3),
+              lds_addr(st + v * DGRP + i * 512));
+      }
+    };
+    // transposed reads: 16-lane group q4 reads rows 16 ks + 8 hi + 4 e + L / 4,
+    // columns 32 dt + 16 (q4 & 1) + 4 (L % 4) of the group; the lane's k slots are keys 16 ks + 8 hi + 0..7
+    const int tx = 2 * (q4 & 1) + ((L >> 1) & 1);
+    floatx16 o[4][2];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][hb][r] = 0.f;
+    if (nt > 0) issue_lat(0, stages);
+    if (nt > 1) issue_lat(1, stages + DSTAGE);
+    int prev = 2;   // stage of tile i - 1
+    for (int i = 0; i <= nt; ++i) {
+      wait_tile<8>(i + 1 < nt);
+      barrier();
+      if (QLAT) barrier();
+      uint16_t* st = stages + prev * DSTAGE;
+      if (i >= 1) {
+        const uint16_t* pb = pbuf[(i - 1) & 1];
+        const float f0 = fbuf[(i - 1) & 1][lane & 31], f1 = fbuf[(i - 1) & 1][32 + (lane & 31)];
+        bf16x8 pf[2][2];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const int h = 32 * hb + (lane & 31), ch = (2 * ks + hi) ^ ((h >> 2) & 3);
+            pf[hb][ks] = *(const bf16x8*)(pb + h * DKT + (ch << 3));
+          }
+        bf16x8 cf[4][2];
+        const uint16_t* sg = st + v * DGRP;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const int r0 = 16 * ks + 8 * hi + (L >> 2), r1 = r0 + 4;
+            const v4s lo = read_tr(sg + r0 * 128 + (((4 * dt + tx) ^ swl(r0)) << 3) + 4 * (L & 1));
+            const v4s up = read_tr(sg + r1 * 128 + (((4 * dt + tx) ^ swl(r1)) << 3) + 4 * (L & 1));
+            cf[dt][ks] = __builtin_bit_cast(bf16x8, (v8s){lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+          }
+        // every read of this stage's group has returned: refill it with tile i + 2
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (i + 2 < nt) issue_lat(i + 2, st);
+        if (__builtin_amdgcn_ballot_w64(f0 != 1.f || f1 != 1.f)) {   // a head's max moved
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              o[dt][0][r] *= f0;
+              o[dt][1][r] *= f1;
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) o[dt][hb] = mfma32(cf[dt][ks], pf[hb][ks], o[dt][hb]);
+      } else if (i + 2 < nt) {
+        issue_lat(2, stages + 2 * DSTAGE);
+      }
+      prev = prev == 2 ? 0 : prev + 1;
+    }
+    __syncthreads();   // row sums and maxima of every head are in LDS
+    // lane: heads 32 hb + lane % 32, dims 128 v + 32 dt + 8 rg + 4 hi + 0..3; normalised
+    // bf16 results to LDS as [64 heads][512 dims], 16-byte chunk c of head h at c ^ (h & 31)
+    uint16_t* so = stages;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int h = 32 * hb + (lane & 31);
+      const float lh = s_l[h], inv = lh > 0.f ? 1.f / lh : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int c = 16 * v + 4 * dt + rg;
+          *(uint2*)(so + h * 512 + ((c ^ (h & 31)) << 3) + 4 * hi) =
+              make_uint2(pack_bf16x2(o[dt][hb][4 * rg] * inv, o[dt][hb][4 * rg + 1] * inv),
+                         pack_bf16x2(o[dt][hb][4 * rg + 2] * inv, o[dt][hb][4 * rg + 3] * inv));
+        }
+    }
     __syncthreads();
   }
-  if (over) s_over = 1;
-  __syncthreads();
-  if (s_over) {   // rare: exact maxima, then accumulate against them (no score can exceed them)
-    m = -INFINITY;
-    attn_pass<true, QLAT>(c, st0, st1, st2, qf, m, l, o);
-    attn_pass<false, QLAT>(c, st0, st1, st2, qf, m, l, o);
+  // every wave: heads 8 p + wave, one 1 KB row per pass
+  uint16_t* out = NS == 1 ? (uint16_t*)a.olat + hrow0 * 512 : (uint16_t*)a.part + ((int64_t)j * a.R * a.H + hrow0) * 512;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int h = 8 * p + wave;
+    *(uint4*)(out + (int64_t)h * 512 + 8 * lane) = *(const uint4*)(stages + h * 512 + ((lane ^ (h & 31)) << 3));
   }
-  // lane: head `head`, dims 256 dh + 32 dt + 8 rg + 4 hi + 0..3
-  l += __shfl_xor(l, 32);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  const int64_t row = (int64_t)q * a.H + head;
-  uint16_t* out = NS == 1 ? (uint16_t*)a.olat + row * 512 : (uint16_t*)a.part + ((int64_t)j * a.R * a.H + row) * 512;
-  out += 256 * c.dh + 4 * c.hi;
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg)
-      *(uint2*)(out + 32 * dt + 8 * rg) = make_uint2(pack_bf16x2(o[dt][4 * rg] * inv, o[dt][4 * rg + 1] * inv),
-                                                     pack_bf16x2(o[dt][4 * rg + 2] * inv, o[dt][4 * rg + 3] * inv));
-  if (NS > 1 && c.dh == 0 && c.hi == 0) a.lse[(int64_t)j * a.R * a.H + row] = l > 0.f ? m + __log2f(l) : -INFINITY;
 }
 
 // One workgroup per row: the listed positions t with 0 <= t <= last key of the
@@ -502,12 +497,12 @@ hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s) {
   const unsigned grid = 8u * (unsigned)((a.R + 7) / 8) * (unsigned)n_hg * (unsigned)a.splits;
   if (a.keys) {
     if (!a.nkeys || a.kstride < 0 || a.kstride > DECODE_TOPK_MAX) return hipErrorInvalidValue;
-    if (a.quant_latent) decode_attn_kernel<true, true><<<grid, 256, 0, s>>>(a, n_hg);
-    else decode_attn_kernel<true, false><<<grid, 256, 0, s>>>(a, n_hg);
+    if (a.quant_latent) decode_attn_kernel<true, true><<<grid, 512, 0, s>>>(a, n_hg);
+    else decode_attn_kernel<true, false><<<grid, 512, 0, s>>>(a, n_hg);
   } else {
     if (a.rows_per_seq != 0) return hipErrorInvalidValue;
-    if (a.quant_latent) decode_attn_kernel<false, true><<<grid, 256, 0, s>>>(a, n_hg);
-    else decode_attn_kernel<false, false><<<grid, 256, 0, s>>>(a, n_hg);
+    if (a.quant_latent) decode_attn_kernel<false, true><<<grid, 512, 0, s>>>(a, n_hg);
+    else decode_attn_kernel<false, false><<<grid, 512, 0, s>>>(a, n_hg);
   }
   return hipGetLastError();
 }

@@ -318,7 +318,7 @@ def test_prefill_attention_every_tile_dsv32_topk_shape():
 
 def test_decode_attention_large_logit_jump():
     # later keys outscore the first tile by far more than the fixed-max headroom,
-    # which sends the kernel through its exact-max recomputation
+    # which moves the running max and rescales what was accumulated
     rng = np.random.default_rng(10)
     B, H, max_len = 3, 64, 300
     lens = np.array([250, 100, 299], dtype=np.int32)
