@@ -55,9 +55,9 @@
 //
 // LDS stage: the latent as four 128-dim groups, each [32 rows][256 B], then
 // the rope rows [32][128 B]. The 16-byte chunks of a latent group's row r are
-// XOR-permuted by ((r & 3) << 2) | ((r >> 2) & 3) and those of rope row r by
-// (r >> 1) & 7, so the score waves' row reads and the value waves' transposed
-// reads are free of bank conflicts.
+// XOR-permuted by swl(r) and those of rope row r by (r >> 1) & 7 to keep the
+// score waves' row reads and the value waves' transposed reads off shared
+// banks.
 #include <mutex>
 
 #include "common.h"
@@ -77,11 +77,36 @@ constexpr int KEYS_LDS = DECODE_TOPK_MAX + DKT;   // a split's keys plus the res
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ int swl(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// 16-byte chunk permutation of latent row r (XOR of per-bit images 12, 1, 4, 2 of
+// r's low four bits), chosen by timing candidates on gfx950 for both read
+// patterns below: with it the 16x16x32 operand reads run at ~199 B/clk per CU,
+// against ~126 for ((r & 3) << 2) | ((r >> 2) & 3), and the transposed reads
+// are no slower.
+__device__ __forceinline__ int swl(int r) {
+  return ((r & 1) ? 12 : 0) ^ ((r & 2) ? 1 : 0) ^ ((r & 4) ? 4 : 0) ^ ((r & 8) ? 2 : 0);
+}
 __device__ __forceinline__ int swr(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ v4s read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+}
+
+// x[l] combined with x[l ^ 16] and with x[l ^ 32] (VALU lane swaps, no LDS round trip)
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
@@ -187,6 +212,10 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a, i
       const uint16_t* qp = (const uint16_t*)a.qlat + (hrow0 + hl) * DROW + 8 * kq;
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) qf[ks] = *(const bf16x8*)(qp + 32 * ks);
+      // from here on the query registers count as written (one wait here, none per tile
+      // behind the ring's loads)
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) __asm__ volatile("" : "+v"(qf[ks]));
     }
     // rope rows of tile kt: rows 8 s + lane / 8, physical chunk lane % 8
     auto issue_rope = [&](int kt, uint16_t* st) {
@@ -238,8 +267,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a, i
         float mx = z[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_xor32(max_xor16(mx));
         float f = 1.f;
         if (m == -INFINITY) m = mx;   // first live keys of this head: nothing accumulated yet
         else if (mx > m + LAZY) {     // rare: move the max, rescale what is accumulated
@@ -269,8 +297,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a, i
       cur = cur == 2 ? 0 : cur + 1;
     }
     // row sums over the four lanes of a head; log2-sum-exp of a run
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = sum_xor32(sum_xor16(l));
     if (lane < 16) {
       s_l[hl] = l;
       if (NS > 1) a.lse[(int64_t)j * a.R * a.H + hrow0 + hl] = l > 0.f ? m + __log2f(l) : -INFINITY;
