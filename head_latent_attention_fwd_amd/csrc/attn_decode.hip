@@ -28,8 +28,8 @@
 // 3-stage ring with two tiles in flight. A value wave reloads the 8 KB of the
 // stage that only it reads (its 128 dims of the 32 rows) as soon as its own
 // fragments of the tile are in registers; the score waves reload the rope
-// rows one tile later, after every score wave has read them. One barrier per
-// tile orders it all.
+// rows right after the next barrier, once every score wave has read them. One
+// barrier per tile orders it all.
 //
 // Softmax: the running max of a head stays at its first live tile's value
 // while later tiles add exp2(z - m) <= 2^LAZY. A tile whose max exceeds
@@ -230,6 +230,10 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a, i
     for (int i = 0; i <= nt; ++i) {
       wait_tile<1>(i + 1 < nt);
       barrier();
+      // rope rows of tile i + 2 into the stage tile i - 1 used: every score wave read
+      // them before this barrier, so they go out now, a whole tile ahead of their use
+      const int nx = cur == 0 ? 2 : cur - 1;
+      if (i + 2 < nt) issue_rope(i + 2, stages + nx * DSTAGE);
       uint16_t* st = stages + cur * DSTAGE;
       if (QLAT) {
         if (i < nt) quant_dequant_tile(st, tid);
@@ -291,9 +295,6 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a, i
         }
         if (lane < 16) fbuf[i & 1][hl] = f;
       }
-      // rope rows of tile i + 2 into the stage tile i - 1 used (every score wave read them before this tile's barrier)
-      const int nx = cur == 0 ? 2 : cur - 1;
-      if (i + 2 < nt) issue_rope(i + 2, stages + nx * DSTAGE);
       cur = cur == 2 ? 0 : cur + 1;
     }
     // row sums over the four lanes of a head; log2-sum-exp of a run
