@@ -221,8 +221,7 @@ __global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
         const float y0 = __uint_as_float(pk.x << 16), y1 = __uint_as_float(pk.x & 0xffff0000u);
         const float y2 = __uint_as_float(pk.y << 16), y3 = __uint_as_float(pk.y & 0xffff0000u);
         float amax = fmaxf(fmaxf(fabsf(y0), fabsf(y1)), fmaxf(fabsf(y2), fabsf(y3)));
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        amax = xor16_max(row16_max(amax));
         e4m3_quotients(amax, true, [&](const float s, auto quo) {
           uint32_t code = 0u;
           if (s != 0.f)
@@ -242,8 +241,7 @@ __global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
         const float y0 = __uint_as_float(pk.x << 16), y1 = __uint_as_float(pk.x & 0xffff0000u);
         const float y2 = __uint_as_float(pk.y << 16), y3 = __uint_as_float(pk.y & 0xffff0000u);
         float amax = fmaxf(fmaxf(fabsf(y0), fabsf(y1)), fmaxf(fabsf(y2), fabsf(y3)));
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        amax = xor16_max(row16_max(amax));
         e4m3_quotients(amax, true, [&](const float s, auto quo) {
           uint32_t code = 0u;
           if (s != 0.f)
@@ -331,8 +329,7 @@ __global__ __launch_bounds__(256) void silu_mul_quant_kernel(const void* gu, int
     y[e] = bf2f(f2bf(gf[e] / (1.0f + __builtin_amdgcn_exp2f(-gf[e] * 1.4426950408889634f)) * uf[e]));
     amax = fmaxf(amax, fabsf(y[e]));
   }
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  amax = row16_max(amax);
   e4m3_quotients(amax, true, [&](const float sc, auto quo) {
     uint2 code = make_uint2(0u, 0u);
     if (sc != 0.f) {
@@ -439,8 +436,7 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* a, int64_t
   float amax = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));   // within the 16 lanes
+  amax = row16_max(amax);   // within the 16 lanes
   e4m3_quotients(amax, dt != DT_F32, [&](const float s, auto quo) {
     uint2 code = make_uint2(0u, 0u);
     if (s != 0.f) {
