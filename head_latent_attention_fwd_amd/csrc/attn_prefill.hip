@@ -23,7 +23,10 @@
 //
 // Tiles move HBM -> LDS with gfx950's 16-byte direct-to-LDS loads into a
 // two-stage ring (one barrier per tile; the next tile's loads fly while the
-// current tile is consumed), 40 KB per stage, two workgroups per CU. The tile
+// current tile is consumed), 40 KB per stage, two workgroups per CU. The next
+// tile's ten loads per thread are issued one per two score MFMAs rather than
+// ahead of them: a wave issues in order, and a burst of loads held its first
+// MFMA back while the texture unit took in the workgroup's 40 KB. The tile
 // loop is unrolled over the two stages so every LDS address is a per-lane
 // base plus an immediate. Within a
 // 16-key block the K rows are stored with bits 2 and 3 of the key index
@@ -124,14 +127,15 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
       voff[i] = (dv * Tp + c * 8) * 2;
     }
   }
+  auto issue_one = [&](int stage, int k0, int i) {
+    auto* lds = (__attribute__((address_space(3))) void*)(smem + stage * STAGE + (4 * i + wv) * 512);
+    if (i < 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kn, lds, 16, voff[i], k0 * 256, 0, 0);
+    else if (i < 6) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kpe, lds, 16, voff[i], k0 * 128, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_vt, lds, 16, voff[i], k0 * 2, 0, 0);
+  };
   auto issue = [&](int stage, int k0) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      auto* lds = (__attribute__((address_space(3))) void*)(smem + stage * STAGE + (4 * i + wv) * 512);
-      if (i < 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kn, lds, 16, voff[i], k0 * 256, 0, 0);
-      else if (i < 6) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kpe, lds, 16, voff[i], k0 * 128, 0, 0);
-      else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_vt, lds, 16, voff[i], k0 * 2, 0, 0);
-    }
+    for (int i = 0; i < LOADS; ++i) issue_one(stage, k0, i);
   };
 
   // LDS operand offsets (elements), invariant over tiles
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
       __syncthreads();
       const uint32_t mw0 = nw0, mw1 = nw1;
       mask_words(kt + 1, nw0, nw1);
-      if (kt + 1 < ntiles) issue(cur ^ 1, k0 + BKV);
+      const bool more = kt + 1 < ntiles;   // wave-uniform
       // No early exit: a tile wholly after this wave's queries (k0 > pw) goes
       // through the masked path with every key dead, so O is updated on every
       // path and the compiler keeps it in place.
@@ -222,6 +226,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
 #pragma unroll
       for (int u = 0; u < 24; ++u) {
         if (u + 3 < 24) kf[u + 3] = kfrag(u + 3);
+        // the next tile's loads go out one per two MFMAs instead of ahead of them
+        if ((u & 1) == 0 && (u >> 1) < LOADS && more) issue_one(cur ^ 1, k0 + BKV, u >> 1);
         s[u & 1] = mfma32(kf[u], qf[u >> 1], s[u & 1]);
       }
       // s[kb][r] holds key k0 + 32kb + 16(r/8) + 8hi + r%8
