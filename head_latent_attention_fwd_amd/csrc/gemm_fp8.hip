@@ -176,48 +176,102 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmFp8Args g) {
 // multiply; two waves per SIMD hide each other's LDS and MFMA latencies.
 // K moves one 128-wide scale group per step through two LDS stages (64 KB
 // each: 256 A rows then 256 W rows of 128 bytes, 16-byte chunks swizzled by
-// (row >> 1) & 7) filled by 16-byte raw-buffer loads straight into LDS.
+// (row >> 1) & 7) filled by 16-byte loads straight into LDS.
 // Column tiles never straddle n_split (multiple of 128); output bf16 through
 // LDS (row-major or the k_nope / v^T split).
+//
+// Two forms of the K loop. With many groups (wo, q_a||kv_a) the loads are
+// raw-buffer builtins and the scales plain loads issued a step ahead. With
+// few groups per tile (kv_b: 4, q_b: 12) a tile's time is dominated by its
+// first groups' trips to HBM / MALL, so that form (PF) also
+//  - fetches group kg + 3's operand lines into L2 at the end of step kg
+//    (one dword per 128-byte line into a scratch LDS word), so the refill
+//    issued a step later hits L2;
+//  - during its last steps fetches the first groups of the tile that this
+//    XCD runs next in the same slot (t + CUs per XCD), so that tile's
+//    prologue hits L2 as well;
+//  - brings each group's block scales into the stage's tail with the refill
+//    (the scales of the following group, read a step before use).
+// All its direct-to-LDS loads are asm (m0 set in the same block), so the
+// compiler tracks none of them and orders no LDS read behind them; a refill
+// is always followed by one prefetch, so waiting for all but the newest load
+// at the end of a step covers every refill.
 constexpr int FB_BK = 128;                   // bytes of K per step (one scale group)
-constexpr int FB_STAGE = 512 * FB_BK;        // bytes per stage
+constexpr int FB_STAGE = 512 * FB_BK;        // operand bytes per stage
 constexpr int FB_CP = 256 + 8;               // bf16 C-tile pitch (elements)
 constexpr int FB_HALF = FB_STAGE > 128 * FB_CP * 2 ? FB_STAGE : 128 * FB_CP * 2;   // bytes per LDS array
 constexpr int FB_GROUP_M = 8;
+constexpr int FB_PF_MAX_GROUPS = 16;         // groups per tile up to which the PF form is used
+static_assert(FB_HALF >= FB_STAGE + 512 * 4, "a stage's tail holds its 512 scale slots");
 
 __device__ __forceinline__ int fb_sw(int row) { return (row >> 1) & 7; }
 constexpr int fb_wait(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8); }
 
-__global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int tiles_m, int tiles_n, int per_xcd) {
+__device__ __forceinline__ uint32_t fb_lds(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+// direct-to-LDS loads of 16 / 4 bytes per lane from base + off: lane l's bytes land at LDS byte
+// address lds + 16 l (4 l)
+__device__ __forceinline__ void fb_dma16(const void* base, uint32_t off, uint32_t lds) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(lds)
+                   : "memory", "m0");
+}
+__device__ __forceinline__ void fb_dma4(const void* base, uint32_t off, uint32_t lds) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" : : "v"(off), "s"(base), "s"(lds)
+                   : "memory", "m0");
+}
+
+struct FbTile {
+  int m0, n0, nbase, nend;
+  const uint8_t* Wb;     // row n0 of the tile's weight matrix
+  const float* wsc;      // that matrix's block scales
+};
+
+__device__ __forceinline__ FbTile fb_tile(const GemmFp8Args& g, int t, int tiles_m, int tiles_n) {
+  const int span = FB_GROUP_M * tiles_n, grp = t / span, first_m = grp * FB_GROUP_M;
+  const int gsz = min(tiles_m - first_m, FB_GROUP_M), r_in = t - grp * span;
+  const int tn = r_in / gsz;
+  const int nsp = g.W2 ? g.n_split : g.N, t1 = (nsp + 255) / 256;
+  const bool second = tn >= t1;
+  FbTile f;
+  f.m0 = (first_m + r_in % gsz) * 256;
+  f.nbase = second ? nsp : 0;                       // first row of this tile's weight matrix
+  f.n0 = second ? nsp + (tn - t1) * 256 : tn * 256;
+  f.nend = second ? g.N : nsp;
+  const uint8_t* w = g.W;
+  const float* ws = g.w_scale;
+  if (second) {
+    w = g.W2;
+    ws = g.w2_scale;
+  }
+  f.Wb = w + (int64_t)(f.n0 - f.nbase) * g.K;
+  f.wsc = ws;
+  return f;
+}
+
+template <bool PF>
+__global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int tiles_m, int tiles_n, int per_xcd,
+                                                              int slots) {
   __shared__ __attribute__((aligned(16))) uint8_t s0[FB_HALF];
   __shared__ __attribute__((aligned(16))) uint8_t s1[FB_HALF];
+  __shared__ __attribute__((aligned(16))) float sfirst[512];   // PF: the first group's scales
+  __shared__ __attribute__((aligned(16))) uint8_t spf[256];    // PF: where L2 prefetches land
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wv >> 1, wn = wv & 1;
   const int l32 = lane & 31, hi = lane >> 5;
   const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
   const int t = xcd * per_xcd + loc, ntile = tiles_m * tiles_n;
   if (loc >= per_xcd || t >= ntile) return;
-  const int span = FB_GROUP_M * tiles_n, grp = t / span, first_m = grp * FB_GROUP_M;
-  const int gsz = min(tiles_m - first_m, FB_GROUP_M), r_in = t - grp * span;
-  const int m0 = (first_m + r_in % gsz) * 256, tn = r_in / gsz;
-  const int M = g.M, N = g.N, K = g.K;
+  const FbTile tl = fb_tile(g, t, tiles_m, tiles_n);
+  const int m0 = tl.m0, n0 = tl.n0, nbase = tl.nbase, nend = tl.nend;
+  const uint8_t* Wb = tl.Wb;
+  const int M = g.M, K = g.K;
   // K groups [kg0, KG) of this workgroup's split (all of them without split-K)
   const int ns = max(g.k_splits, 1), per = (K / 128 + ns - 1) / ns, split = blockIdx.y;
   const int kg0 = split * per, KG = min(K / 128, kg0 + per);
-  const int nsp = g.W2 ? g.n_split : N, t1 = (nsp + 255) / 256;
-  const bool second = tn >= t1;
-  const int nbase = second ? nsp : 0;                          // first row of this tile's weight matrix
-  const int n0 = second ? nsp + (tn - t1) * 256 : tn * 256, nend = second ? N : nsp;
-  const uint8_t* Wb = (second ? g.W2 : g.W) + (int64_t)(n0 - nbase) * K;
-  const float* wsc = second ? g.w2_scale : g.w_scale;
   const int nblocks = (nend - nbase + 127) / 128;
   const int wblk = min((n0 - nbase) / 128 + wn, nblocks - 1);
-  const float* wsrow = wsc + (int64_t)wblk * (K / 128);   // scale rows hold every K group
 
-  const __amdgpu_buffer_rsrc_t rsA =
-      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (int)((int64_t)M * K), BUF_DW3);
-  const __amdgpu_buffer_rsrc_t rsW =
-      __builtin_amdgcn_make_buffer_rsrc((void*)Wb, (short)0, (int)((int64_t)(nend - n0) * K), BUF_DW3);
   // load i of wave w fills 1 KB block 8 i + w: blocks 0..31 are A rows, 32..63 W rows
   int voff[8];
 #pragma unroll
@@ -226,17 +280,6 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
     if (i < 4) voff[i] = min(m0 + r, M - 1) * K + c * 16;
     else voff[i] = (min(n0 + r - 256, nend - 1) - n0) * K + c * 16;
   }
-  auto issue = [&](uint8_t* st, int kg) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(i < 4 ? rsA : rsW,
-                                               (__attribute__((address_space(3))) void*)(st + (8 * i + wv) * 1024), 16,
-                                               voff[i], kg * FB_BK, 0, 0);
-  };
-
-  // activation scales of the lane's two output rows
-  const float* as0 = g.a_scale + (int64_t)min(m0 + wm * 64 + l32, M - 1) * (K / 128);
-  const float* as1 = g.a_scale + (int64_t)min(m0 + wm * 64 + 32 + l32, M - 1) * (K / 128);
 
   floatx16 acc[2][4];
 #pragma unroll
@@ -261,19 +304,21 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
   };
   const int ra = wm * 64 + l32, rw = 256 + wn * 128 + l32;
 
-  float sa0 = as0[kg0], sa1 = as1[kg0], sw = wsrow[kg0];
-  auto step = [&](const uint8_t* cur, uint8_t* refill, int kg) {
-    // promotion: keep the sum in units of this group's scale
+  // promotion: keep the sum in units of this group's scale (returns the factors for the
+  // lane's two rows' sums)
+  auto promote = [&](float sa0, float sa1, float sw) __attribute__((always_inline)) {
     const float n0s = sa0 * sw, n1s = sa1 * sw;
-    const float r0 = (n0s != 0.f && srun0 != 0.f) ? srun0 / n0s : 1.f;
-    const float r1 = (n1s != 0.f && srun1 != 0.f) ? srun1 / n1s : 1.f;
-    if (n0s != 0.f) srun0 = n0s;
-    if (n1s != 0.f) srun1 = n1s;
-    // next group's scales (clamped: the last group repeats)
-    const int kn = min(kg + 1, KG - 1);
-    sa0 = as0[kn];
-    sa1 = as1[kn];
-    sw = wsrow[kn];
+    // both quotients are formed unconditionally and selected (no branch in the wave)
+    const float q0 = srun0 / n0s, q1 = srun1 / n1s;
+    const float r0 = (n0s != 0.f && srun0 != 0.f) ? q0 : 1.f;
+    const float r1 = (n1s != 0.f && srun1 != 0.f) ? q1 : 1.f;
+    srun0 = n0s != 0.f ? n0s : srun0;
+    srun1 = n1s != 0.f ? n1s : srun1;
+    return make_float2(r0, r1);
+  };
+  // one group's MFMAs after the promotion factors r
+  auto group = [&](const uint8_t* cur, float2 r) __attribute__((always_inline)) {
+    const float r0 = r.x, r1 = r.y;
     // first k half: each 32x32 block is rescaled right before its MFMA, so the
     // 16 multiplies of the next block issue while the matrix core runs this
     // one; the second k half follows with no VALU work between MFMAs
@@ -296,24 +341,126 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
           acc[i][j] = mfma32_fp8(wf[j], af[i], acc[i][j]);
         }
     }
-    // every wave is done with `cur` and the other stage has landed
-    __builtin_amdgcn_s_waitcnt(fb_wait(0, 0));
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-    issue(refill, min(kg + 2, KG - 1));
   };
 
-  issue(s0, kg0);
-  issue(s1, min(kg0 + 1, KG - 1));
-  __builtin_amdgcn_s_waitcnt(fb_wait(8, 15));   // group 0 has landed
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-  int kg = kg0;
-  for (; kg + 1 < KG; kg += 2) {
-    step(s0, s0, kg);
-    step(s1, s1, kg + 1);
+  if constexpr (!PF) {
+    const __amdgpu_buffer_rsrc_t rsA =
+        __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (int)((int64_t)M * K), BUF_DW3);
+    const __amdgpu_buffer_rsrc_t rsW =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Wb, (short)0, (int)((int64_t)(nend - n0) * K), BUF_DW3);
+    auto issue = [&](uint8_t* st, int kg) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(i < 4 ? rsA : rsW,
+                                                 (__attribute__((address_space(3))) void*)(st + (8 * i + wv) * 1024),
+                                                 16, voff[i], kg * FB_BK, 0, 0);
+    };
+    // activation scales of the lane's two output rows, the wave's weight-block scales
+    const float* as0 = g.a_scale + (int64_t)min(m0 + wm * 64 + l32, M - 1) * (K / 128);
+    const float* as1 = g.a_scale + (int64_t)min(m0 + wm * 64 + 32 + l32, M - 1) * (K / 128);
+    const float* wsrow = tl.wsc + (int64_t)wblk * (K / 128);
+    float sa0 = as0[kg0], sa1 = as1[kg0], sw = wsrow[kg0];
+    auto step = [&](uint8_t* cur, int kg) {
+      const float2 r = promote(sa0, sa1, sw);
+      // next group's scales (clamped: the last group repeats)
+      const int kn = min(kg + 1, KG - 1);
+      sa0 = as0[kn];
+      sa1 = as1[kn];
+      sw = wsrow[kn];
+      group(cur, r);
+      // every wave is done with `cur` and the other stage has landed
+      __builtin_amdgcn_s_waitcnt(fb_wait(0, 0));
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+      issue(cur, min(kg + 2, KG - 1));
+    };
+    issue(s0, kg0);
+    issue(s1, min(kg0 + 1, KG - 1));
+    __builtin_amdgcn_s_waitcnt(fb_wait(8, 15));   // group 0 has landed
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    int kg = kg0;
+    for (; kg + 1 < KG; kg += 2) {
+      step(s0, kg);
+      step(s1, kg + 1);
+    }
+    if (kg < KG) step(s0, kg);
+  } else {
+    // the tile this XCD's slot runs next (same split)
+    const int ts = t + slots;
+    const bool has_succ = loc + slots < per_xcd && ts < ntile;
+    const FbTile sx = has_succ ? fb_tile(g, ts, tiles_m, tiles_n) : tl;
+    // block scales of a group: waves 0-3 fetch the 256 rows' activation scales (lane 2 j + e
+    // takes row 64 wv + j + 32 e, so a lane's two rows sit side by side), waves 4-7 the tile's
+    // two weight blocks' (lanes 0 and 1 of wave 4 are the ones read)
+    const float* sbase = g.a_scale;
+    if (wv >= 4) sbase = tl.wsc + 0;
+    const uint32_t soff = (uint32_t)((wv < 4 ? min(m0 + 64 * wv + (lane >> 1) + 32 * (lane & 1), M - 1)
+                                             : min((n0 - nbase) / 128 + (lane & 1), nblocks - 1)) *
+                                     (K / 128) * 4);
+    // L2 prefetch: this thread's row (A for waves 0-3, weights for 4-7) of this tile and of the next
+    const uint8_t* pb1 = g.A;
+    const uint8_t* pb2 = g.A;
+    if (wv >= 4) {
+      pb1 = Wb + 0;
+      pb2 = sx.Wb + 0;
+    }
+    const uint32_t pfo = (uint32_t)((wv < 4 ? min(m0 + tid, M - 1) : min(n0 + tid - 256, nend - 1) - n0) * K);
+    const uint32_t pfo2 =
+        (uint32_t)((wv < 4 ? min(sx.m0 + tid, M - 1) : min(sx.n0 + tid - 256, sx.nend - 1) - sx.n0) * K);
+    const uint32_t lpf = fb_lds(spf);
+    // group kg of this tile; past the last group, group kg - KG of the next tile (clamped)
+    auto pfetch = [&](int kg) __attribute__((always_inline)) {
+      if (kg < KG || !has_succ) fb_dma4(pb1 + min(kg, KG - 1) * FB_BK, pfo, lpf);
+      else fb_dma4(pb2 + min(kg0 + kg - KG, KG - 1) * FB_BK, pfo2, lpf);
+    };
+    // a stage holds the group's 512 x 128 operand bytes, then 512 scale slots with the
+    // following group's scales
+    auto issue = [&](uint8_t* st, int kg) __attribute__((always_inline)) {
+      const uint32_t lb = fb_lds(st);
+      const uint8_t* ab = g.A + kg * FB_BK;
+      const uint8_t* wb = Wb + kg * FB_BK;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) fb_dma16(i < 4 ? ab : wb, (uint32_t)voff[i], lb + (8 * i + wv) * 1024);
+      fb_dma4(sbase + min(kg + 1, KG - 1), soff, lb + FB_STAGE + 256 * wv);
+    };
+    struct Sc { float a0, a1, w; };
+    auto read_scales = [&](const float* sc, Sc& o) __attribute__((always_inline)) {
+      const float2 sa = *(const float2*)(sc + wm * 64 + 2 * l32);
+      o.a0 = sa.x;
+      o.a1 = sa.y;
+      o.w = sc[256 + wn];
+    };
+    Sc scA, scB;
+    auto step = [&](uint8_t* cur, const uint8_t* other, int kg, Sc& scl) __attribute__((always_inline)) {
+      group(cur, promote(scl.a0, scl.a1, scl.w));
+      // every wave is done with `cur`, and everything but the newest prefetch has landed
+      __builtin_amdgcn_s_waitcnt(fb_wait(1, 0));
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+      // `other` holds group kg + 1 and the scales of group kg + 2 (used two steps on)
+      if (kg + 2 < KG) read_scales((const float*)(other + FB_STAGE), scl);
+      __asm__ volatile("" ::: "memory");
+      if (kg + 2 < KG) issue(cur, kg + 2);
+      if (kg + 1 < KG) pfetch(kg + 3);
+      __asm__ volatile("" ::: "memory");
+    };
+    fb_dma4(sbase + kg0, soff, fb_lds(sfirst) + 256 * wv);
+    issue(s0, kg0);
+    issue(s1, min(kg0 + 1, KG - 1));
+    pfetch(kg0 + 2);
+    __builtin_amdgcn_s_waitcnt(fb_wait(10, 15));   // group 0 and the first scales have landed
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    read_scales(sfirst, scA);
+    read_scales((const float*)(s0 + FB_STAGE), scB);
+    int kg = kg0;
+    for (; kg + 1 < KG; kg += 2) {
+      step(s0, s1, kg, scA);
+      step(s1, s0, kg + 1, scB);
+    }
+    if (kg < KG) step(s0, s1, kg, scA);
   }
-  if (kg < KG) step(s0, s0, kg);
   __builtin_amdgcn_s_waitcnt(fb_wait(0, 0));
   __syncthreads();
 
@@ -436,6 +583,20 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
 }
 
 int fb_cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// workgroups of the big kernel one XCD runs at once (one per CU): the distance from a tile to
+// the one the same slot runs next
+int fb_slots_per_xcd() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 32;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+  const int slots = cus >= 8 ? cus / 8 : 1;
+  if (dev >= 0 && dev < 64) cached[dev] = slots;
+  return slots;
+}
 bool fp8_big_ok(const GemmFp8Args& g) {
   const int nsp = g.W2 ? g.n_split : g.N;
   return (g.c_dtype == DT_BF16 || (g.c_dtype == DT_F32 && g.epi == EPI_ROWMAJOR && (g.ldc & 3) == 0)) && g.M >= 256 && g.N >= 256 && g.K % 128 == 0 && (int64_t)g.M * g.K < (1LL << 31) &&
@@ -461,7 +622,12 @@ hipError_t launch_gemm_fp8(const GemmFp8Args& g, hipStream_t s) {
     const int nsp = g.W2 ? g.n_split : g.N;
     const int tm = fb_cdiv(g.M, 256), tn = g.W2 ? fb_cdiv(nsp, 256) + fb_cdiv(g.N - nsp, 256) : fb_cdiv(g.N, 256);
     const int per_xcd = fb_cdiv(tm * tn, 8);
-    gemm_fp8_big_kernel<<<dim3(8 * per_xcd, g.k_splits > 1 ? g.k_splits : 1), 512, 0, s>>>(g, tm, tn, per_xcd);
+    const dim3 grid(8 * per_xcd, g.k_splits > 1 ? g.k_splits : 1);
+    const int groups = fb_cdiv(g.K / 128, g.k_splits > 1 ? g.k_splits : 1);
+    if (groups <= FB_PF_MAX_GROUPS)
+      gemm_fp8_big_kernel<true><<<grid, 512, 0, s>>>(g, tm, tn, per_xcd, fb_slots_per_xcd());
+    else
+      gemm_fp8_big_kernel<false><<<grid, 512, 0, s>>>(g, tm, tn, per_xcd, 0);
     return hipGetLastError();
   }
   dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, 1);
