@@ -106,9 +106,10 @@ def test_gemm_fp8_blockscaled(M, N, K):
 @pytest.mark.parametrize("M,N,K,out", [(4352, 4096, 512, torch.bfloat16), (600, 2112, 1024, torch.float32),
                                        (1000, 1280, 2048, torch.bfloat16)])
 def test_gemm_fp8_blockscaled_many_tiles(M, N, K, out):
-    # more 256 x 256 tiles than CUs (a workgroup walks several, carrying the
-    # next tile's first K groups over), a ragged last row tile, a 64-wide last
-    # column tile (N = 2112), bf16 and fp32 outputs
+    # more 256 x 256 tiles than CUs (a second round, whose first K groups the
+    # first round's tiles fetch into L2 ahead of it), a ragged last row tile, a
+    # 64-wide last column tile (N = 2112), bf16 and fp32 outputs; all three
+    # take the short-K loop (at most 16 groups)
     rng = np.random.default_rng(M * 7 + N + K)
     a = synth.round_bf16(rng.standard_normal((M, K)))
     w = (rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
