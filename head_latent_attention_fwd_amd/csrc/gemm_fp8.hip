@@ -210,14 +210,23 @@ constexpr int fb_wait(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) |
 __device__ __forceinline__ uint32_t fb_lds(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
 }
-// direct-to-LDS loads of 16 / 4 bytes per lane from base + off: lane l's bytes land at LDS byte
-// address lds + 16 l (4 l)
+// a pointer that is the same in every lane, held in scalar registers
+__device__ __forceinline__ const void* fb_sgpr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+// direct-to-LDS loads of 16 / 4 bytes per lane from base + off (base the same in every
+// lane): lane l's bytes land at LDS byte address lds + 16 l (4 l)
 __device__ __forceinline__ void fb_dma16(const void* base, uint32_t off, uint32_t lds) {
-  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(lds)
+  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(fb_sgpr(base)),
+                   "s"(lds)
                    : "memory", "m0");
 }
 __device__ __forceinline__ void fb_dma4(const void* base, uint32_t off, uint32_t lds) {
-  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" : : "v"(off), "s"(base), "s"(lds)
+  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" : : "v"(off), "s"(fb_sgpr(base)),
+                   "s"(lds)
                    : "memory", "m0");
 }
 
@@ -344,10 +353,11 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(GemmFp8Args g, int
   };
 
   if constexpr (!PF) {
-    const __amdgpu_buffer_rsrc_t rsA =
-        __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (int)((int64_t)M * K), BUF_DW3);
-    const __amdgpu_buffer_rsrc_t rsW =
-        __builtin_amdgcn_make_buffer_rsrc((void*)Wb, (short)0, (int)((int64_t)(nend - n0) * K), BUF_DW3);
+    // (bases and sizes read from lane 0 so that the descriptors stay in scalar registers)
+    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)fb_sgpr(g.A), (short)0, __builtin_amdgcn_readfirstlane((int)((int64_t)M * K)), BUF_DW3);
+    const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)fb_sgpr(Wb), (short)0, __builtin_amdgcn_readfirstlane((int)((int64_t)(nend - n0) * K)), BUF_DW3);
     auto issue = [&](uint8_t* st, int kg) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
