@@ -121,34 +121,43 @@ __device__ __forceinline__ void dma16(const uint16_t* src, uint32_t base) {
                    : "memory", "m0");
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 // e4m3 view of a tile's latent (score waves, tid 0..255): thread (row r = tid / 8,
 // group g = (tid / 2) % 4, half hf = tid % 2) takes the 8 chunks 8 hf .. 8 hf + 7
-// of group g of row r; the two halves of a group are neighbouring lanes.
+// of group g of row r; the two halves of a group are neighbouring lanes. The group
+// maximum of |x| is taken on the bf16 bit patterns (16-bit integer maxima: for
+// finite values the order of |x| is that of its bits) and shared with the
+// neighbour by a quad permute.
 __device__ __forceinline__ void quant_dequant_tile(uint16_t* st, int tid) {
   const int r = tid >> 3, g = (tid >> 1) & 3, hf = tid & 1;
   uint16_t* row = st + g * DGRP + r * 128;
   uint4 v[8];
-  float amax = 0.f;
+  u16x2 am = {0, 0};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     v[i] = *(const uint4*)(row + (((8 * hf + i) ^ swl(r)) << 3));
     const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[e] << 16)), fabsf(__uint_as_float(w[e] & 0xffff0000u))));
+    for (int e = 0; e < 4; ++e) am = __builtin_elementwise_max(am, __builtin_bit_cast(u16x2, w[e] & 0x7fff7fffu));
   }
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  float amax = fmaxf(bf2f(am[0]), bf2f(am[1]));
+  amax = fmaxf(amax, dpp_mov<0xB1>(amax));
   e4m3_quotients(amax, true, [&](const float s, auto quo) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
       uint32_t o[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xffff0000u);
-        const int code = __builtin_amdgcn_cvt_pk_fp8_f32(quo(x0), quo(x1), 0, false);
-        const float2v d = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
-        o[e] = pack_bf16x2(d[0] * s, d[1] * s);
+      for (int e = 0; e < 4; e += 2) {   // four codes in one word: no register to clear per pair
+        int code = __builtin_amdgcn_cvt_pk_fp8_f32(quo(__uint_as_float(w[e] << 16)),
+                                                   quo(__uint_as_float(w[e] & 0xffff0000u)), 0, false);
+        code = __builtin_amdgcn_cvt_pk_fp8_f32(quo(__uint_as_float(w[e + 1] << 16)),
+                                               quo(__uint_as_float(w[e + 1] & 0xffff0000u)), code, true);
+        const float2v d0 = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
+        const float2v d1 = __builtin_amdgcn_cvt_pk_f32_fp8(code, true);
+        o[e] = pack_bf16x2(d0[0] * s, d0[1] * s);
+        o[e + 1] = pack_bf16x2(d1[0] * s, d1[1] * s);
       }
       *(uint4*)(row + (((8 * hf + i) ^ swl(r)) << 3)) = make_uint4(o[0], o[1], o[2], o[3]);
     }
