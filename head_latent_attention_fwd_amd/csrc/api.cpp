@@ -75,6 +75,8 @@ struct PrefillWs {
   void *cqkv, *cqn, *kvc, *q, *kn, *vt, *kpe, *attn, *mask, *aq, *as;
   float* part;      // split-K partials of the joint down-projection (or NULL)
   int qkv_splits;
+  float* kpe_part;  // e4m3: split-K partials of the k_pe columns [kpe_splits][M][64] (or NULL)
+  int kpe_splits;
 };
 
 int pad64(int T) { return (T + 63) & ~63; }
@@ -104,6 +106,24 @@ int prefill_qkv_splits(const mla_dims* d, int wdt, int adt, int M) {
   return mla::gemm_bf16_splits(qkv_args(d, adt, aligned, aligned, aligned, nullptr, M));
 }
 
+// e4m3 joint down-projection on the 256 x 256 e4m3 GEMM: its N = Dq + L + 64
+// columns make one tile column of 64 (the k_pe columns) per row of tiles, and
+// at M = 16384 those 64 narrow tiles are a whole third round on 8 of each XCD's
+// 32 CUs. Computing the k_pe columns as a separate product with its K cut into
+// KPE_SPLITS chunks (fp32 partials that the norm pass sums in chunk order) turns
+// that round into one of quarter-length tiles on every CU. Used where it
+// shortens the launch schedule (whole rounds of 256 workgroups).
+constexpr int KPE_SPLITS = 4, PREFILL_CUS = 256;
+int prefill_kpe_splits(const mla_dims* d, int wdt, int adt, int M) {
+  if (wdt != MLA_E4M3 || adt != MLA_BF16 || M < 256) return 0;
+  const int tm = (M + 255) / 256, tq = (d->q_lora_rank + 255) / 256;
+  const int full = tm * (tq + (d->kv_lora_rank + 64 + 255) / 256), main = tm * (tq + (d->kv_lora_rank + 255) / 256);
+  const double rounds_full = (full + PREFILL_CUS - 1) / PREFILL_CUS;
+  const double rounds_split = (main + PREFILL_CUS - 1) / PREFILL_CUS +
+                              (double)((tm * KPE_SPLITS + PREFILL_CUS - 1) / PREFILL_CUS) / KPE_SPLITS;
+  return rounds_split < rounds_full - 0.25 ? KPE_SPLITS : 0;
+}
+
 // Tk = keys per sequence (T, or start_pos + T with a cache)
 size_t prefill_layout(const mla_dims* d, int wdt, int adt, int B, int T, int Tk, int topk, bool own_kvc, void* ws,
                       PrefillWs* out) {
@@ -125,6 +145,8 @@ size_t prefill_layout(const mla_dims* d, int wdt, int adt, int B, int T, int Tk,
   // fp32 input of the norms: split-K partials (bf16), the whole product (e4m3)
   const size_t nparts = wdt == MLA_E4M3 ? 1 : p.qkv_splits > 1 ? p.qkv_splits : 0;
   p.part = nparts ? (float*)c.take(nparts * M * (Dq + L + 64) * 4) : nullptr;
+  p.kpe_splits = prefill_kpe_splits(d, wdt, adt, (int)M);
+  p.kpe_part = p.kpe_splits ? (float*)c.take((size_t)p.kpe_splits * M * 64 * 4) : nullptr;
   if (wdt == MLA_E4M3) {
     size_t kmax = d->dim;
     if (Dq > kmax) kmax = Dq;
@@ -433,14 +455,6 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t
   // move the normalised values that kv_b and q_b quantise again)
   const bool qkv_f32 = qkv_split || wdt == MLA_E4M3;
   const int qkv_nsplit = qkv_split ? p.qkv_splits : 1;
-  if (qkv_split) {
-    gq.k_splits = p.qkv_splits; gq.part = p.part;
-    LAUNCH(mla::launch_gemm_bf16(gq, s), "gemm_bf16(split-K q_a|kv_a)");
-  } else if ((rc = project(wdt, adt, x, dim, w->wq_a, w->wq_a_scale, w->wkv_a, w->wkv_a_scale, Dq,
-                           qkv_f32 ? (void*)p.part : p.cqkv, NQKV, M, NQKV, dim, &p, s, nullptr, nullptr, nullptr,
-                           qkv_f32 ? MLA_F32 : -1))) {
-    return rc;
-  }
   const size_t es = adt == MLA_F32 ? 4 : 2;
   // the norms read either the projection in the activation type or fp32 (partial) sums
   const void* qkv_in = qkv_f32 ? (const void*)p.part : p.cqkv;
@@ -469,6 +483,25 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t
       kv_codes = cq_codes + (size_t)M * Dq; kv_scales = cq_scales + (size_t)M * (Dq / 128);
       qa.kv_codes = kv_codes; qa.kv_scales = kv_scales;
     }
+  }
+  // e4m3 at large M: the k_pe columns as their own split-K product (prefill_kpe_splits)
+  const bool kpe_split = p.kpe_part && adt == MLA_BF16 && qkv_norm_ok(qa);
+  if (qkv_split) {
+    gq.k_splits = p.qkv_splits; gq.part = p.part;
+    LAUNCH(mla::launch_gemm_bf16(gq, s), "gemm_bf16(split-K q_a|kv_a)");
+  } else if ((rc = project(wdt, adt, x, dim, w->wq_a, w->wq_a_scale, w->wkv_a, w->wkv_a_scale, Dq,
+                           qkv_f32 ? (void*)p.part : p.cqkv, NQKV, M, kpe_split ? Dq + L : NQKV, dim, &p, s, nullptr,
+                           nullptr, nullptr, qkv_f32 ? MLA_F32 : -1))) {
+    return rc;
+  }
+  if (kpe_split) {   // rows L..L+63 of Wkv_a (block row L / 128 of its scales) on x's codes
+    mla::GemmFp8Args g{};
+    g.A = (const uint8_t*)p.aq; g.a_scale = (const float*)p.as;
+    g.W = (const uint8_t*)w->wkv_a + (int64_t)L * dim; g.w_scale = w->wkv_a_scale + (int64_t)(L / 128) * (dim / 128);
+    g.C = p.kpe_part; g.ldc = 64; g.c_dtype = MLA_F32; g.M = M; g.N = 64; g.K = dim; g.epi = mla::EPI_ROWMAJOR;
+    g.k_splits = p.kpe_splits; g.split_stride = (int64_t)M * 64;
+    LAUNCH(mla::launch_gemm_fp8(g, s), "gemm_fp8(k_pe columns, split-K)");
+    qa.kpe_in = p.kpe_part; qa.kpe_splits = p.kpe_splits; qa.kpe_split_stride = (int64_t)M * 64;
   }
   if (adt == MLA_BF16 && qkv_norm_ok(qa)) {
     LAUNCH(mla::launch_qkv_norm(qa, s), "qkv_norm");

@@ -609,7 +609,7 @@ int fb_slots_per_xcd() {
 }
 bool fp8_big_ok(const GemmFp8Args& g) {
   const int nsp = g.W2 ? g.n_split : g.N;
-  return (g.c_dtype == DT_BF16 || (g.c_dtype == DT_F32 && g.epi == EPI_ROWMAJOR && (g.ldc & 3) == 0)) && g.M >= 256 && g.N >= 256 && g.K % 128 == 0 && (int64_t)g.M * g.K < (1LL << 31) &&
+  return (g.c_dtype == DT_BF16 || (g.c_dtype == DT_F32 && g.epi == EPI_ROWMAJOR && (g.ldc & 3) == 0)) && g.M >= 256 && (g.N >= 256 || g.k_splits > 1) && g.K % 128 == 0 && (int64_t)g.M * g.K < (1LL << 31) &&
          (int64_t)g.N * g.K < (1LL << 31) && (!g.W2 || (nsp % 128 == 0 && nsp < g.N)) &&
          (g.epi != EPI_KV_SPLIT || g.N % 256 == 0) && (g.ldc & 7) == 0 && (((uintptr_t)g.C) & 15) == 0 &&
          (((uintptr_t)g.A | (uintptr_t)g.W | (uintptr_t)g.W2) & 15) == 0;

@@ -139,6 +139,10 @@ struct QkvNormArgs {
   uint8_t* q_codes; float* q_scales;
   // the same for the normalised latent (L % 128 == 0): codes [rows, L], scales [rows, L/128]
   uint8_t* kv_codes; float* kv_scales;
+  // optional separate source of the 64 k_pe inputs of each row: the sum of kpe_splits
+  // fp32 partials kpe_in[s * kpe_split_stride + m * 64 + j] (in split order) instead of
+  // the row's last 64 elements of `in`
+  const float* kpe_in; int kpe_splits; int64_t kpe_split_stride;
 };
 hipError_t launch_qkv_norm(const QkvNormArgs& a, hipStream_t s);
 hipError_t launch_rope_table(float* c, float* sn, int n_pos, float base, hipStream_t s);

@@ -10,6 +10,7 @@ import torch
 
 from head_latent_attention_fwd_amd import runner, synth
 from oracle import mla
+from oracle.fp8 import quant_weight_block128
 
 from helpers import BF16_TOL, F32_TOL, FP8_TOL, assert_parity, config, oracle_dims, small_cfg
 
@@ -87,8 +88,19 @@ def test_prefill_kimi_k2_bf16_full_size_sampled():
 
 def test_prefill_kimi_k2_fp8_full_size_sampled():
     cfg = config(2)
-    _check_prefill(cfg, synth.seed_of(2), rows=_sample_rows(cfg["T"], np.random.default_rng(2), 4),
-                   batches=[0, 3], tol=FP8_TOL, cos=0.999)
+    inp, run = _check_prefill(cfg, synth.seed_of(2), rows=_sample_rows(cfg["T"], np.random.default_rng(2), 4),
+                              batches=[0, 3], tol=FP8_TOL, cos=0.999)
+    # cache entries [c | k_pe] of one row in every 256-row tile of the B*T rows: at this
+    # size the k_pe columns of the joint down-projection are a separate split-K product
+    d = oracle_dims(cfg)
+    fp8 = {"wkv_a": quant_weight_block128(inp["w"]["wkv_a"])}
+    T, ntile = cfg["T"], cfg["B"] * cfg["T"] // 256
+    rows = [256 * k + (37 * k) % 256 for k in range(ntile)]
+    cache = run.kv_cache.float().cpu().numpy()
+    for b in range(cfg["B"]):
+        ts = np.array([m - b * T for m in rows if b * T <= m < (b + 1) * T])
+        entry = mla.latent_path(inp["x"][b][ts], inp["w"], d, ts, fp8=fp8)
+        assert_parity(cache[b][ts], entry, what=f"kv_cache_out rows of sequence {b}")
 
 
 def test_prefill_dsv32_sparse_full_size_sampled():
