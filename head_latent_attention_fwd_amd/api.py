@@ -67,6 +67,7 @@ _SIGS = {
     "gemm_bf16_decode": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, sz, vp]),
     "gemm_fp8_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, vp, sz, vp]),
     "mla_quant_e4m3_1x128": (ctypes.c_int, [vp, i64, i32, i32, i32, vp, vp, vp]),
+    "mla_latent_e4m3_view": (ctypes.c_int, [vp, i64, i64, i32, vp]),
     "mla_quant_e4m3_block128": (ctypes.c_int, [vp, i32, i32, vp, vp, vp]),
     "mla_topk_to_bitmask": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
     "mla_swiglu_workspace_size": (sz, [i32, i32]),
@@ -352,6 +353,14 @@ def mla_quant_e4m3_1x128(a, q=None, scales=None, stream=None):
     _check(lib().mla_quant_e4m3_1x128(_ptr(a), a.stride(0), _TORCH_DT[a.dtype], M, K, _ptr(q), _ptr(scales),
                                       _stream(stream)))
     return q, scales
+
+
+def mla_latent_e4m3_view(cache, kv_lora_rank, stream=None):
+    """In place: the latent part of every row of a [..., row] bf16 cache in its 1x128 e4m3 view."""
+    _need(cache, torch.bfloat16, "cache")
+    rows = cache.numel() // cache.shape[-1]
+    _check(lib().mla_latent_e4m3_view(_ptr(cache), rows, cache.stride(-2), kv_lora_rank, _stream(stream)))
+    return cache
 
 
 def mla_quant_e4m3_block128(w, stream=None):

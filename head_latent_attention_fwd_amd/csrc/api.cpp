@@ -479,6 +479,7 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t
   if (wdt == MLA_E4M3) {
     cq_codes = (uint8_t*)p.aq; cq_scales = (float*)p.as;
     qa.q_codes = cq_codes; qa.q_scales = cq_scales;
+    qa.kv_view = true;   // cache entries hold the latent as kv_b's quantiser sees it
     if (kv_fresh) {
       kv_codes = cq_codes + (size_t)M * Dq; kv_scales = cq_scales + (size_t)M * (Dq / 128);
       qa.kv_codes = kv_codes; qa.kv_scales = kv_scales;
@@ -505,8 +506,9 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t
   }
   if (adt == MLA_BF16 && qkv_norm_ok(qa)) {
     LAUNCH(mla::launch_qkv_norm(qa, s), "qkv_norm");
-  } else if (P > 0 || cache_bs != (int64_t)T * (L + 64)) {
-    return fail(MLA_UNSUPPORTED, "prefill over a cache needs bf16 activations and 16-byte aligned norm weights");
+  } else if (P > 0 || cache_bs != (int64_t)T * (L + 64) || wdt == MLA_E4M3) {
+    return fail(MLA_UNSUPPORTED, "prefill over a cache or with e4m3 weights needs bf16 activations and 16-byte "
+                                 "aligned norm weights and cache");
   } else {
     cq_codes = nullptr; kv_codes = nullptr;   // the separate norm passes quantise nothing
   {  // q_norm
@@ -676,7 +678,10 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
     a.q_out = p.cqn; a.ld_q = Dq;
     a.kv_out = kv_cache; a.ld_kv = (int64_t)max_len * (L + 64); a.kv_pos_stride = L + 64; a.kv_pos_max = max_len;
     a.cos_tab = rope_cos; a.sin_tab = rope_sin; a.rope_len = max_len; a.pos = cache_len;
-    if (fp8) { a.q_codes = aq; a.q_scales = as; }   // q_b's input, quantised in the same pass
+    if (fp8) {
+      a.q_codes = aq; a.q_scales = as;   // q_b's input, quantised in the same pass
+      a.kv_view = true;                  // the entry as kv_b's quantiser sees it
+    }
     if (!qkv_norm_ok(a)) return fail(MLA_UNSUPPORTED, "decode needs 16-byte aligned norm weights");
     LAUNCH(mla::launch_qkv_norm(a, s), "qkv_norm -> cache");
   }
@@ -705,7 +710,6 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t 
     a.splits = p.splits;
     if (p.splits == 1) a.olat = p.attn;
     else { a.part = p.attn; a.lse = p.lse; }
-    a.quant_latent = fp8;   // kv_b's e4m3 input: the dequantised 1x128 latent
     LAUNCH(mla::launch_decode_attn(a, s), "decode_attn");
   }
   {  // o[b, h] = W_UV_h . o_lat[b, h] (splits merged in order); e4m3: o leaves as wo's quantised input
@@ -1054,6 +1058,20 @@ int mla_rope_table(float* cos_tab, float* sin_tab, int32_t n_pos, float base, vo
   if (!cos_tab || !sin_tab) return fail(MLA_INVALID_ARG, "NULL table");
   if (n_pos <= 0 || !(base > 1.f)) return fail(MLA_INVALID_ARG, "bad n_pos/base");
   LAUNCH(mla::launch_rope_table(cos_tab, sin_tab, n_pos, base, (hipStream_t)stream), "rope_table");
+  return MLA_OK;
+}
+
+int mla_latent_e4m3_view(void* cache, int64_t rows, int64_t row_stride, int32_t kv_lora_rank, void* stream) {
+  g_err.clear();
+  if (!cache) return fail(MLA_INVALID_ARG, "NULL cache");
+  if (rows < 0 || kv_lora_rank <= 0 || row_stride < kv_lora_rank) return fail(MLA_INVALID_ARG, "bad sizes");
+  if (rows > (1LL << 40) / (kv_lora_rank / 128 > 0 ? kv_lora_rank / 128 : 1))
+    return fail(MLA_INVALID_ARG, "too many rows");
+  if (kv_lora_rank % 128) return fail(MLA_UNSUPPORTED, "kv_lora_rank must be a multiple of 128");
+  if (row_stride % 8 || ((uintptr_t)cache & 15))
+    return fail(MLA_UNSUPPORTED, "need row_stride % 8 == 0 and a 16-byte aligned cache");
+  LAUNCH(mla::launch_latent_e4m3_view(cache, rows, row_stride, kv_lora_rank, (hipStream_t)stream),
+         "latent_e4m3_view");
   return MLA_OK;
 }
 

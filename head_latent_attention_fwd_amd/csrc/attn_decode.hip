@@ -44,14 +44,11 @@
 // r loads cache row keys[k0 + r]. The same kernel serves a prefill in the
 // absorbed form, one query row per token.
 //
-// e4m3 weights (QLAT): kv_b is an e4m3 Linear whose input, the latent, is
-// quantised in dynamic 1x128 groups (Kimi K2 · Down projection,
-// quantization_config). The absorbed product therefore sees each latent as
-// its dequantised value: once a tile has landed, the score waves replace
-// every latent 128-group of the tile in LDS by scale * e4m3(x / scale)
-// (scale = amax / 448 in fp32, quotient from the correctly rounded reciprocal
-// plus one residual correction), rounded to bf16, before anyone reads it. The
-// rope key is not an input of kv_b and is used as cached.
+// e4m3 weights: kv_b is an e4m3 Linear whose input, the latent, is quantised
+// in dynamic 1x128 groups (Kimi K2 · Down projection, quantization_config);
+// with e4m3 weights the cache holds each latent in that quantised form (the
+// norm pass writes it so, and it is a fixed point of the quantiser), so the
+// same kernel serves both weight types. The rope key is not an input of kv_b.
 //
 // LDS stage: the latent as four 128-dim groups, each [32 rows][256 B], then
 // the rope rows [32][128 B]. The 16-byte chunks of a latent group's row r are
@@ -121,49 +118,6 @@ __device__ __forceinline__ void dma16(const uint16_t* src, uint32_t base) {
                    : "memory", "m0");
 }
 
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-// e4m3 view of a tile's latent (score waves, tid 0..255): thread (row r = tid / 8,
-// group g = (tid / 2) % 4, half hf = tid % 2) takes the 8 chunks 8 hf .. 8 hf + 7
-// of group g of row r; the two halves of a group are neighbouring lanes. The group
-// maximum of |x| is taken on the bf16 bit patterns (16-bit integer maxima: for
-// finite values the order of |x| is that of its bits) and shared with the
-// neighbour by a quad permute.
-__device__ __forceinline__ void quant_dequant_tile(uint16_t* st, int tid) {
-  const int r = tid >> 3, g = (tid >> 1) & 3, hf = tid & 1;
-  uint16_t* row = st + g * DGRP + r * 128;
-  uint4 v[8];
-  u16x2 am = {0, 0};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[i] = *(const uint4*)(row + (((8 * hf + i) ^ swl(r)) << 3));
-    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) am = __builtin_elementwise_max(am, __builtin_bit_cast(u16x2, w[e] & 0x7fff7fffu));
-  }
-  float amax = fmaxf(bf2f(am[0]), bf2f(am[1]));
-  amax = fmaxf(amax, dpp_mov<0xB1>(amax));
-  e4m3_quotients(amax, true, [&](const float s, auto quo) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-      uint32_t o[4];
-#pragma unroll
-      for (int e = 0; e < 4; e += 2) {   // four codes in one word: no register to clear per pair
-        int code = __builtin_amdgcn_cvt_pk_fp8_f32(quo(__uint_as_float(w[e] << 16)),
-                                                   quo(__uint_as_float(w[e] & 0xffff0000u)), 0, false);
-        code = __builtin_amdgcn_cvt_pk_fp8_f32(quo(__uint_as_float(w[e + 1] << 16)),
-                                               quo(__uint_as_float(w[e + 1] & 0xffff0000u)), code, true);
-        const float2v d0 = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
-        const float2v d1 = __builtin_amdgcn_cvt_pk_f32_fp8(code, true);
-        o[e] = pack_bf16x2(d0[0] * s, d0[1] * s);
-        o[e + 1] = pack_bf16x2(d1[0] * s, d1[1] * s);
-      }
-      *(uint4*)(row + (((8 * hf + i) ^ swl(r)) << 3)) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-  });
-}
-
 // LDS waits before a barrier: the wave's own LDS writes done and at most
 // `ahead` of its direct loads still in flight (their counts are wave-uniform).
 template <int N>
@@ -176,7 +130,7 @@ __device__ __forceinline__ void barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
-template <bool SPARSE, bool QLAT>
+template <bool SPARSE>
 __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a, int n_hg) {
   __shared__ __attribute__((aligned(16))) uint16_t stages[3 * DSTAGE];
   __shared__ __attribute__((aligned(16))) uint16_t pbuf[2][64 * DKT];   // P[h][t] bf16, per tile parity
@@ -244,11 +198,6 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a, i
       const int nx = cur == 0 ? 2 : cur - 1;
       if (i + 2 < nt) issue_rope(i + 2, stages + nx * DSTAGE);
       uint16_t* st = stages + cur * DSTAGE;
-      if (QLAT) {
-        if (i < nt) quant_dequant_tile(st, tid);
-        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        barrier();
-      }
       if (i < nt) {
         // A operand rows t = 16 tb + lane % 16, chunk 4 ks + kq of the 72 in a row
         auto afrag = [&](int tb, int ks) {
@@ -342,7 +291,6 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a, i
     for (int i = 0; i <= nt; ++i) {
       wait_tile<8>(i + 1 < nt);
       barrier();
-      if (QLAT) barrier();
       uint16_t* st = stages + prev * DSTAGE;
       if (i >= 1) {
         const uint16_t* pb = pbuf[(i - 1) & 1];
@@ -534,12 +482,10 @@ hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s) {
   const unsigned grid = 8u * (unsigned)((a.R + 7) / 8) * (unsigned)n_hg * (unsigned)a.splits;
   if (a.keys) {
     if (!a.nkeys || a.kstride < 0 || a.kstride > DECODE_TOPK_MAX) return hipErrorInvalidValue;
-    if (a.quant_latent) decode_attn_kernel<true, true><<<grid, 512, 0, s>>>(a, n_hg);
-    else decode_attn_kernel<true, false><<<grid, 512, 0, s>>>(a, n_hg);
+    decode_attn_kernel<true><<<grid, 512, 0, s>>>(a, n_hg);
   } else {
     if (a.rows_per_seq != 0) return hipErrorInvalidValue;
-    if (a.quant_latent) decode_attn_kernel<false, true><<<grid, 512, 0, s>>>(a, n_hg);
-    else decode_attn_kernel<false, false><<<grid, 512, 0, s>>>(a, n_hg);
+    decode_attn_kernel<false><<<grid, 512, 0, s>>>(a, n_hg);
   }
   return hipGetLastError();
 }

@@ -241,10 +241,9 @@ __global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
     } else if (c < nq + nkv && kv) {
       const int e = 4 * (c - nq);
       const float4 g = *(const float4*)&a.gkv[e];
-      const uint2 pk = make_uint2(pack_bf16x2(g.x * (v[j].x * rkv), g.y * (v[j].y * rkv)),
-                                  pack_bf16x2(g.z * (v[j].z * rkv), g.w * (v[j].w * rkv)));
-      *(uint2*)(kv + e) = pk;
-      if (a.kv_codes) {   // as for q: 32 consecutive lanes hold one 128-wide group
+      uint2 pk = make_uint2(pack_bf16x2(g.x * (v[j].x * rkv), g.y * (v[j].y * rkv)),
+                            pack_bf16x2(g.z * (v[j].z * rkv), g.w * (v[j].w * rkv)));
+      if (a.kv_codes || a.kv_view) {   // as for q: 32 consecutive lanes hold one 128-wide group
         const float y0 = __uint_as_float(pk.x << 16), y1 = __uint_as_float(pk.x & 0xffff0000u);
         const float y2 = __uint_as_float(pk.y << 16), y3 = __uint_as_float(pk.y & 0xffff0000u);
         float amax = fmaxf(fmaxf(fabsf(y0), fabsf(y1)), fmaxf(fabsf(y2), fabsf(y3)));
@@ -254,10 +253,18 @@ __global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
           if (s != 0.f)
             code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
                 quo(y2), quo(y3), __builtin_amdgcn_cvt_pk_fp8_f32(quo(y0), quo(y1), 0, false), true);
-          *(uint32_t*)(a.kv_codes + (int64_t)row * a.L + e) = code;
-          if (((c - nq) & 31) == 0) a.kv_scales[(int64_t)row * (a.L >> 7) + ((c - nq) >> 5)] = s;
+          if (a.kv_codes) {
+            *(uint32_t*)(a.kv_codes + (int64_t)row * a.L + e) = code;
+            if (((c - nq) & 31) == 0) a.kv_scales[(int64_t)row * (a.L >> 7) + ((c - nq) >> 5)] = s;
+          }
+          if (a.kv_view) {   // the entry holds the value kv_b's quantiser maps the latent to
+            const float2v d0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)code, false);
+            const float2v d1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)code, true);
+            pk = make_uint2(pack_bf16x2(d0[0] * s, d0[1] * s), pack_bf16x2(d1[0] * s, d1[1] * s));
+          }
         });
       }
+      *(uint2*)(kv + e) = pk;
     }
   }
   if (tid < 32) {
@@ -511,6 +518,46 @@ hipError_t launch_rmsnorm_rope(const NormRopeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Each 128-wide latent group of a cache row replaced, in place, by the value its
+// dynamic 1x128 e4m3 quantisation stands for (bf16 of code x scale): the input
+// kv_b's quantiser sees, and a fixed point of that quantiser. 16 lanes per
+// group, 8 values (16 bytes) per lane; the group maximum of |x| on the bf16 bit
+// patterns (for finite values their order is that of |x|).
+__global__ __launch_bounds__(256) void latent_view_kernel(uint16_t* __restrict__ cache, int64_t groups, int gpr,
+                                                          int64_t stride) {
+  const int64_t gid = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (gid >= groups) return;   // whole 16-lane rows leave together
+  const int64_t row = gid / gpr;
+  uint4* p = (uint4*)(cache + row * stride + (gid - row * gpr) * 128) + (threadIdx.x & 15);
+  const uint4 v = *p;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t am = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t m = w[e] & 0x7fff7fffu;
+    am = max(am, max(m & 0xffffu, m >> 16));
+  }
+  const float amax = row16_max(__uint_as_float(am << 16));
+  e4m3_quotients(amax, true, [&](const float s, auto quo) {
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      int code = 0;
+      if (s != 0.f)
+        code = __builtin_amdgcn_cvt_pk_fp8_f32(
+            quo(__uint_as_float(w[e + 1] << 16)), quo(__uint_as_float(w[e + 1] & 0xffff0000u)),
+            __builtin_amdgcn_cvt_pk_fp8_f32(quo(__uint_as_float(w[e] << 16)), quo(__uint_as_float(w[e] & 0xffff0000u)),
+                                            0, false),
+            true);
+      const float2v d0 = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
+      const float2v d1 = __builtin_amdgcn_cvt_pk_f32_fp8(code, true);
+      o[e] = pack_bf16x2(d0[0] * s, d0[1] * s);
+      o[e + 1] = pack_bf16x2(d1[0] * s, d1[1] * s);
+    }
+    *p = make_uint4(o[0], o[1], o[2], o[3]);
+  });
+}
+
 hipError_t launch_qkv_norm(const QkvNormArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   if ((a.Dq & 3) || (a.L & 3) || (a.ld_in & 3) || (a.Dq + a.L + 64) / 4 > 256 * QKV_CH ||
@@ -518,9 +565,18 @@ hipError_t launch_qkv_norm(const QkvNormArgs& a, hipStream_t s) {
       (a.ld_q & 3) || (a.ld_kv & 3) || (a.kv_pos_stride & 3) || a.in_splits < 1 || (!a.pos && a.pos_period <= 0) ||
       (a.q_codes && ((a.Dq & 127) || !a.q_scales || ((uintptr_t)a.q_codes & 3))) ||
       (a.kv_codes && ((a.Dq & 127) || (a.L & 127) || !a.kv_scales || ((uintptr_t)a.kv_codes & 3))) ||
-      (a.kpe_in && (a.kpe_splits < 1 || ((uintptr_t)a.kpe_in & 15) || (a.kpe_split_stride & 3))))
+      (a.kpe_in && (a.kpe_splits < 1 || ((uintptr_t)a.kpe_in & 15) || (a.kpe_split_stride & 3))) ||
+      (a.kv_view && ((a.Dq & 127) || (a.L & 127))))
     return hipErrorInvalidValue;
   qkv_norm_kernel<<<a.rows, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_latent_e4m3_view(void* cache, int64_t rows, int64_t stride, int L, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if ((L & 127) || L <= 0 || stride < L || (stride & 7) || ((uintptr_t)cache & 15)) return hipErrorInvalidValue;
+  const int64_t groups = rows * (L / 128);
+  latent_view_kernel<<<(unsigned)((groups + 15) / 16), 256, 0, s>>>((uint16_t*)cache, groups, L / 128, stride);
   return hipGetLastError();
 }
 

@@ -143,8 +143,14 @@ struct QkvNormArgs {
   // fp32 partials kpe_in[s * kpe_split_stride + m * 64 + j] (in split order) instead of
   // the row's last 64 elements of `in`
   const float* kpe_in; int kpe_splits; int64_t kpe_split_stride;
+  // e4m3 weights: each latent entry written as its 1x128 e4m3 view (bf16 of code x
+  // scale, the value kv_b's quantiser maps it to) instead of the bf16 latent
+  bool kv_view;
 };
 hipError_t launch_qkv_norm(const QkvNormArgs& a, hipStream_t s);
+// In place: the first L elements (L % 128 == 0) of each of `rows` bf16 rows, `stride`
+// elements apart, replaced by their 1x128 e4m3 view.
+hipError_t launch_latent_e4m3_view(void* cache, int64_t rows, int64_t stride, int L, hipStream_t s);
 hipError_t launch_rope_table(float* c, float* sn, int n_pos, float base, hipStream_t s);
 hipError_t launch_quant_1x128(const void* a, int64_t lda, int a_dtype, int M, int K,
                               uint8_t* q, float* scales, hipStream_t s);
@@ -216,8 +222,6 @@ struct DecodeAttnArgs {
   // [splits][R*H] its log2-sum-exp of the scaled scores (-inf for an empty run).
   int splits;
   void* olat; void* part; float* lse;
-  // e4m3 kv_b: every latent enters as its dequantised 1x128 e4m3 value
-  bool quant_latent;
 };
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s);
 // Splits that fill the chip for `rows` query rows of H heads over at most

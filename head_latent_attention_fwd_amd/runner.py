@@ -102,6 +102,8 @@ class Decode:
         self.w = device_weights(inp["w"], cfg.get("weight", "bf16"), device)
         self.weights = api.make_weights(self.w, self.wdt)
         self.cache0 = to_dev(inp["cache"], torch.bfloat16, device)
+        if self.wdt == api.MLA_E4M3:   # with e4m3 weights the cache holds each latent in its e4m3 view
+            api.mla_latent_e4m3_view(self.cache0, cfg["kv_lora_rank"])
         self.cache = self.cache0.clone()
         self.cache_len = to_dev(inp["cache_len"], torch.int32, device)
         max_len = self.cache.shape[1]

@@ -116,7 +116,9 @@ MLA_API size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t weight_d
  *            query must keep at least one live key (its own position suffices).
  *   out      [B, T, dim]   act_dtype
  *   kv_cache_out [B, T, kv_lora_rank + 64] bf16 (fp32 for MLA_F32) or NULL:
- *            receives the per-position [normalised latent | rotated k_pe].
+ *            receives the per-position [normalised latent | rotated k_pe];
+ *            with e4m3 weights the latent in its 1x128 e4m3 view (see
+ *            mla_latent_e4m3_view), the form kv_b's quantiser gives it.
  *   ws, ws_bytes  workspace of at least mla_prefill_workspace_size(...) bytes,
  *            256-byte aligned. */
 MLA_API int mla_prefill(const mla_dims* dims, const mla_weights* w, const void* x, int32_t act_dtype,
@@ -147,7 +149,9 @@ MLA_API size_t mla_prefill_cached_workspace_size(const mla_dims* dims, int32_t w
  *             for chunk row s iff t <= start_pos + s and (no topk_idx or t is
  *             listed in row (b, s)); -1 pads
  *   out       [B, T, dim] bf16
- * Weights bf16 or e4m3 (block-scaled, as for mla_prefill). */
+ * Weights bf16 or e4m3 (block-scaled, as for mla_prefill; the chunk's entries
+ * are then written in their e4m3 view, and cached latents in either form give
+ * the same result, since kv_b quantises them). */
 MLA_API int mla_prefill_cached(const mla_dims* dims, const mla_weights* w, const void* x, int32_t B, int32_t T,
                        int32_t start_pos, void* kv_cache, int32_t max_len, const float* rope_cos,
                        const float* rope_sin, int32_t rope_len, const int32_t* topk_idx, int32_t topk, void* out,
@@ -179,7 +183,11 @@ MLA_API size_t mla_decode_workspace_size(const mla_dims* dims, int32_t weight_dt
  * inputs of q_a|kv_a, q_b and wo are quantised in dynamic 1x128 groups, and
  * kv_b acts on each cached latent quantised in 1x128 groups; the absorbed
  * form reaches that result with the dequantised W_UK and W_UV and each
- * latent's dequantised 1x128 value. Needs kv_lora_rank = 512, n_heads a
+ * latent's dequantised 1x128 value. With e4m3 weights the cache holds every
+ * latent in that dequantised form (its e4m3 view, as mla_prefill,
+ * mla_prefill_cached and mla_decode write it with e4m3 weights, or as
+ * mla_latent_e4m3_view converts a cache of plain latents): the new entry is
+ * written so, and cached latents are read as they are. Needs kv_lora_rank = 512, n_heads a
  * multiple of 64, dim and q_lora_rank multiples of 128 for e4m3, and 16-byte
  * aligned x, out, cache and norm weights (MLA_UNSUPPORTED otherwise). The
  * key range of each sequence may be cut into several runs whose partial
@@ -291,6 +299,18 @@ MLA_API int mla_decode_attention(const void* q_lat, const void* cache, const int
 MLA_API int mla_decode_attention_noalloc(const void* q_lat, const void* cache, const int32_t* cache_len,
                                          void* o_lat, int32_t B, int32_t H, int32_t max_len, float scale,
                                          void* stream);
+
+/* e4m3 view of cached latents, in place (Kimi K2 · Down projection,
+ * quantization_config: kv_b is an e4m3 Linear whose input is quantised in
+ * dynamic 1x128 groups): the first kv_lora_rank bf16 elements of each of `rows`
+ * rows, row_stride elements apart, are replaced by the value their quantisation
+ * stands for, bf16(code x s) with s = amax / 448 and codes as in
+ * mla_quant_e4m3_1x128. The view is a fixed point of that quantisation, so kv_b
+ * gives the same product on it as on the plain latent; it is the cache form the
+ * e4m3 calls write and mla_decode reads. kv_lora_rank % 128 == 0, row_stride %
+ * 8 == 0 and a 16-byte aligned cache (MLA_UNSUPPORTED otherwise). */
+MLA_API int mla_latent_e4m3_view(void* cache, int64_t rows, int64_t row_stride, int32_t kv_lora_rank,
+                                 void* stream);
 
 /* cos/sin table for RoPE: cos_tab[p, d] = cos(p * base^(-d/32)), sin likewise,
  * for p < n_pos, d < 32, evaluated in fp64 and stored fp32. */

@@ -45,3 +45,14 @@ def oracle_dims(cfg):
 
 def config(i, **over):
     return synth.make_cfg(i, **over)
+
+
+def e4m3_entries(entries, L):
+    """Oracle cache entries in the form the e4m3 calls write them: the latent
+    part (first L values) replaced by the value its dynamic 1x128 e4m3
+    quantisation stands for (kv_b's input), the rotary part unchanged."""
+    from oracle import fp8
+    e = np.array(entries, dtype=np.float64, copy=True)
+    flat = e.reshape(-1, e.shape[-1])
+    flat[:, :L] = fp8.quant_dequant_act(flat[:, :L])
+    return flat.reshape(e.shape)

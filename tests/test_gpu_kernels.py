@@ -75,6 +75,26 @@ def test_quant_1x128_bit_exact(M, K):
     np.testing.assert_array_equal(q.cpu().numpy(), rq)
 
 
+def test_latent_e4m3_view():
+    """Each 128-group of a cache row's latent replaced by its 1x128 e4m3 value
+    (kv_b's quantised input); the rotary part untouched. The view quantises back
+    to the codes of the plain latent (a fixed point of the quantiser) and sits
+    within one bf16 step of code x scale."""
+    B, S, L = 3, 40, 512
+    lat = _act_with_edges(B * S, L, 7).reshape(B, S, L)
+    rope = synth.round_bf16(np.random.default_rng(8).standard_normal((B, S, 64)))
+    cache = dev(np.concatenate([lat, rope], axis=-1), torch.bfloat16)
+    api.mla_latent_e4m3_view(cache, L)
+    got = cache.float().cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(got[..., L:], rope)
+    ref = fp8.quant_dequant_act(lat.reshape(-1, L)).reshape(B, S, L)
+    assert (np.abs(got[..., :L] - ref) <= 2.0 ** -7 * np.abs(ref)).all()
+    q_view, s_view = fp8.quant_act_1x128(got[..., :L].reshape(-1, L), quotient="f32")
+    q_lat, s_lat = fp8.quant_act_1x128(lat.reshape(-1, L), quotient="f32")
+    np.testing.assert_array_equal(s_view, s_lat)
+    np.testing.assert_array_equal(q_view, q_lat)
+
+
 @pytest.mark.parametrize("N,K", [(576, 7168), (130, 200), (1536, 7168)])
 def test_quant_block128_bit_exact(N, K):
     rng = np.random.default_rng(N * K)
