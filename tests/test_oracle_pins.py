@@ -464,6 +464,28 @@ def test_fp8_decode_tracks_the_exact_decode():
     assert np.abs(e_got - e_exact).max() / np.abs(e_exact).max() < 0.3
 
 
+def test_e4m3_view_is_a_fixed_point_of_the_activation_quantiser():
+    """The value a 1x128 e4m3 quantisation stands for (code x group scale),
+    held in bf16, quantises back to the same scales and codes: storing a cached
+    latent in that form instead of its plain value leaves kv_b's input, and so
+    every product, unchanged. Checked on groups spanning 2^-30 to 2^30 in scale,
+    an all-zero group, one with a single huge element and one of 1e-30 values
+    (the quantiser's division branch)."""
+    rng = np.random.default_rng(91)
+    a = rng.standard_normal((96, 512)) * np.exp2(rng.uniform(-30, 30, (96, 4))).repeat(128, axis=1)
+    a[0, :128] = 0.0
+    a[1, 130] = 1e30
+    a[2, 256:384] = 1e-30 * rng.standard_normal(128)
+    a = fp8.round_bf16(a)
+    view = fp8.round_bf16(fp8.quant_dequant_act(a))
+    q0, s0 = fp8.quant_act_1x128(a.astype(np.float32), "f32")
+    q1, s1 = fp8.quant_act_1x128(view.astype(np.float32), "f32")
+    np.testing.assert_array_equal(s1, s0)
+    np.testing.assert_array_equal(q1, q0)
+    # the view is not the plain latent: most values moved
+    assert (view != a).mean() > 0.5
+
+
 def test_fp8_decode_quantises_the_cached_latents():
     """kv_b is an e4m3 Linear in the definition, so its input (each cached
     latent) is quantised in 1x128 groups: replacing every cached latent by its
