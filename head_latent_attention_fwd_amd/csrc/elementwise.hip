@@ -160,13 +160,16 @@ __global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
     if (c < nch) {
       const int64_t i = (int64_t)row * a.ld_in + 4 * c;
-      if (a.kpe_in && c >= nq + nkv) {   // k_pe from its own split-K partials
+      if (a.kpe_in && c >= nq + nkv) {   // k_pe from its own split-K partials (all loads first)
         const float* p = a.kpe_in + (int64_t)row * 64 + 4 * (c - nq - nkv);
-        x = *(const float4*)p;
-        for (int s = 1; s < a.kpe_splits; ++s) {
-          const float4 u = *(const float4*)(p + (int64_t)s * a.kpe_split_stride);
-          x.x += u.x; x.y += u.y; x.z += u.z; x.w += u.w;
-        }
+        float4 t[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          if (s < a.kpe_splits) t[s] = *(const float4*)(p + (int64_t)s * a.kpe_split_stride);
+        x = t[0];
+#pragma unroll
+        for (int s = 1; s < 8; ++s)
+          if (s < a.kpe_splits) { x.x += t[s].x; x.y += t[s].y; x.z += t[s].z; x.w += t[s].w; }
       } else if (a.in_dtype == DT_F32) {
         const float* p = (const float*)a.in + i;
         float4 t[8];
@@ -565,7 +568,7 @@ hipError_t launch_qkv_norm(const QkvNormArgs& a, hipStream_t s) {
       (a.ld_q & 3) || (a.ld_kv & 3) || (a.kv_pos_stride & 3) || a.in_splits < 1 || (!a.pos && a.pos_period <= 0) ||
       (a.q_codes && ((a.Dq & 127) || !a.q_scales || ((uintptr_t)a.q_codes & 3))) ||
       (a.kv_codes && ((a.Dq & 127) || (a.L & 127) || !a.kv_scales || ((uintptr_t)a.kv_codes & 3))) ||
-      (a.kpe_in && (a.kpe_splits < 1 || ((uintptr_t)a.kpe_in & 15) || (a.kpe_split_stride & 3))) ||
+      (a.kpe_in && (a.kpe_splits < 1 || a.kpe_splits > 8 || ((uintptr_t)a.kpe_in & 15) || (a.kpe_split_stride & 3))) ||
       (a.kv_view && ((a.Dq & 127) || (a.L & 127))))
     return hipErrorInvalidValue;
   qkv_norm_kernel<<<a.rows, 256, 0, s>>>(a);

@@ -139,7 +139,7 @@ struct QkvNormArgs {
   uint8_t* q_codes; float* q_scales;
   // the same for the normalised latent (L % 128 == 0): codes [rows, L], scales [rows, L/128]
   uint8_t* kv_codes; float* kv_scales;
-  // optional separate source of the 64 k_pe inputs of each row: the sum of kpe_splits
+  // optional separate source of the 64 k_pe inputs of each row: the sum of kpe_splits (<= 8)
   // fp32 partials kpe_in[s * kpe_split_stride + m * 64 + j] (in split order) instead of
   // the row's last 64 elements of `in`
   const float* kpe_in; int kpe_splits; int64_t kpe_split_stride;
