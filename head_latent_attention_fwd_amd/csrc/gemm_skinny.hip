@@ -286,16 +286,10 @@ __device__ __forceinline__ void gemm_skinny_fp8_body(const SkinnyArgs& g) {
                      : "memory");
     return a * w;
   };
-  float f = 0.f;
-  if (nk > 0) {
-    for (int s = 0; s < SK_ST; ++s)
-      if (s < nk) issue(s);
-    wait_ahead(min(nk, SK_ST) - 1);   // step 0 (and the staged scales) have landed
-    read(0);
-    f = scale(0);
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    floatx16 blk[FN];
+  // Software-pipelined over two block accumulators: step kt + 1's MFMAs are
+  // issued before step kt's block is added to the running sum, so those 16 FMAs
+  // per block run on the VALU while the matrix core works on the next step.
+  auto mfmas = [&](floatx16* blk) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       floatx16 zero;
@@ -304,19 +298,44 @@ __device__ __forceinline__ void gemm_skinny_fp8_body(const SkinnyArgs& g) {
       blk[j] = mfma32_fp8(wf[0][j], af[0], zero);
       blk[j] = mfma32_fp8(wf[1][j], af[1], blk[j]);
     }
-    const float fc = f;
-    // step kt + 1 has landed and every wave is done with stage kt, which is
-    // refilled; the next step's fragments are read while these MFMAs run
-    if (kt + 1 < nk) {
-      wait_ahead(min(nk - 2 - kt, 2));
-      if (kt + SK_ST < nk) issue(kt + SK_ST);
-      f = scale(kt + 1);
-      read(kt + 1);
-    }
+  };
+  auto promote = [&](const floatx16* blk, float fc) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][r] = fmaf(blk[j][r], fc, acc[j][r]);
+  };
+  float f = 0.f;
+  // step kt + 1 has landed and every wave is done with stage kt, which is
+  // refilled; then step kt + 1's fragments and scale are read
+  auto advance = [&](int kt) __attribute__((always_inline)) {
+    wait_ahead(min(nk - 2 - kt, 2));
+    if (kt + SK_ST < nk) issue(kt + SK_ST);
+    f = scale(kt + 1);
+    read(kt + 1);
+  };
+  if (nk > 0) {
+    for (int s = 0; s < SK_ST; ++s)
+      if (s < nk) issue(s);
+    wait_ahead(min(nk, SK_ST) - 1);   // step 0 (and the staged scales) have landed
+    read(0);
+    f = scale(0);
+    floatx16 b0[FN], b1[FN];
+    mfmas(b0);
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {   // b0 holds step kt's products, f its scale
+      float fc = f;
+      advance(kt);
+      mfmas(b1);
+      promote(b0, fc);
+      fc = f;
+      if (kt + 2 < nk) {
+        advance(kt + 1);
+        mfmas(b0);
+      }
+      promote(b1, fc);
+    }
+    if (kt < nk) promote(b0, f);
   }
 
   if (NT == 128 && g.qc) {
