@@ -113,9 +113,26 @@ int prefill_qkv_splits(const mla_dims* d, int wdt, int adt, int M) {
 // KPE_SPLITS chunks (fp32 partials that the norm pass sums in chunk order) turns
 // that round into one of quarter-length tiles on every CU. Used where it
 // shortens the launch schedule (whole rounds of 256 workgroups).
+// The bf16 joint down-projection (when it is not split-K as a whole) does the
+// same when the bf16 GEMM's schedule gains by it (its chunk count is then the
+// split-K plan of the 64-column product).
 constexpr int KPE_SPLITS = 4, PREFILL_CUS = 256;
 int prefill_kpe_splits(const mla_dims* d, int wdt, int adt, int M) {
-  if (wdt != MLA_E4M3 || adt != MLA_BF16 || M < 256) return 0;
+  if (adt != MLA_BF16 || M < 256) return 0;
+  if (wdt == MLA_BF16) {
+    if (prefill_qkv_splits(d, wdt, adt, M) > 1) return 0;
+    const void* al = (const void*)(uintptr_t)256;
+    const mla::GemmArgs full = qkv_args(d, adt, al, al, al, (void*)(uintptr_t)256, M);
+    mla::GemmArgs main = full;
+    main.N = d->q_lora_rank + d->kv_lora_rank;
+    const mla::GemmArgs tail = gemm_args(al, d->dim, al, d->dim, nullptr, 64, adt, M, 64, d->dim);
+    const int splits = mla::gemm_bf16_splits(tail);
+    if (splits < 2 || splits > 8) return 0;
+    const double c_full = mla::gemm_bf16_cost(full, false);
+    const double c_split = mla::gemm_bf16_cost(main, false) + mla::gemm_bf16_cost(tail, true);
+    return c_split < c_full - 0.25 ? splits : 0;
+  }
+  if (wdt != MLA_E4M3) return 0;
   const int tm = (M + 255) / 256, tq = (d->q_lora_rank + 255) / 256;
   const int full = tm * (tq + (d->kv_lora_rank + 64 + 255) / 256), main = tm * (tq + (d->kv_lora_rank + 255) / 256);
   const double rounds_full = (full + PREFILL_CUS - 1) / PREFILL_CUS;
@@ -495,7 +512,13 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const void* x, int32_t
                            nullptr, nullptr, qkv_f32 ? MLA_F32 : -1))) {
     return rc;
   }
-  if (kpe_split) {   // rows L..L+63 of Wkv_a (block row L / 128 of its scales) on x's codes
+  if (kpe_split && wdt == MLA_BF16) {   // rows L..L+63 of Wkv_a, split-K into fp32 partials
+    mla::GemmArgs g = gemm_args(x, dim, (const uint16_t*)w->wkv_a + (int64_t)L * dim, dim, nullptr, 64, adt, M, 64,
+                                dim);
+    g.k_splits = p.kpe_splits; g.part = p.kpe_part;
+    LAUNCH(mla::launch_gemm_bf16(g, s), "gemm_bf16(k_pe columns, split-K)");
+    qa.kpe_in = p.kpe_part; qa.kpe_splits = p.kpe_splits; qa.kpe_split_stride = (int64_t)M * 64;
+  } else if (kpe_split) {   // rows L..L+63 of Wkv_a (block row L / 128 of its scales) on x's codes
     mla::GemmFp8Args g{};
     g.A = (const uint8_t*)p.aq; g.a_scale = (const float*)p.as;
     g.W = (const uint8_t*)w->wkv_a + (int64_t)L * dim; g.w_scale = w->wkv_a_scale + (int64_t)(L / 128) * (dim / 128);

@@ -539,14 +539,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_swiglu_kernel(GemmArgs g, in
 
 namespace {
 // operand shapes the big-tile kernels take
-bool big_ok(const GemmArgs& g) {
+// (narrow: outputs of fewer than 256 columns too, for split-K products)
+bool big_ok(const GemmArgs& g, bool narrow = false) {
   // raw-buffer loads address each operand with 32-bit byte offsets
   const int64_t lim = (int64_t)1 << 31;
   const int nsp = g.W2 ? g.n_split : g.N;
   const bool fits = ((int64_t)(g.M - 1) * g.lda + g.K) * 2 < lim && ((int64_t)(nsp - 1) * g.ldw + g.K) * 2 < lim &&
                     (!g.W2 || (((int64_t)(g.N - nsp - 1) * g.ldw2 + g.K) * 2 < lim && (nsp & 7) == 0 && nsp < g.N &&
                                (g.ldw2 & 7) == 0 && ((uintptr_t)g.W2 & 15) == 0));
-  return !g.w_kn && g.M >= 256 && g.N >= 256 && g.K % GB_BK == 0 && (g.lda & 7) == 0 && (g.ldw & 7) == 0 && fits &&
+  return !g.w_kn && g.M >= 256 && (g.N >= 256 || (narrow && g.N >= 8)) && g.K % GB_BK == 0 && (g.lda & 7) == 0 && (g.ldw & 7) == 0 && fits &&
          (((uintptr_t)g.A | (uintptr_t)g.W) & 15) == 0;
 }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
@@ -583,7 +584,7 @@ hipError_t run_big(const GemmArgs& g, int bn, int ny, hipStream_t s) {
 struct SplitPlan { int bn, splits; };
 SplitPlan split_plan(const GemmArgs& g) {
   SplitPlan best{256, 1};
-  if (!big_ok(g) || g.batch != 1 || (g.N & 3) != 0 || g.epi == EPI_KV_SPLIT) return best;
+  if (!big_ok(g, true) || g.batch != 1 || (g.N & 3) != 0 || g.epi == EPI_KV_SPLIT) return best;
   const int tm = cdiv(g.M, 256), ksteps = g.K / GB_BK;
   double best_eff = 0;
   for (int bn : {256, 224, 192}) {
@@ -601,6 +602,16 @@ SplitPlan split_plan(const GemmArgs& g) {
 }  // namespace
 
 int gemm_bf16_splits(const GemmArgs& g) { return split_plan(g).splits; }
+
+double gemm_bf16_cost(const GemmArgs& g, bool split) {
+  if (split) {
+    const SplitPlan p = split_plan(g);
+    const int tiles = cdiv(g.M, 256) * big_tiles_n(g, p.bn) * p.splits;
+    return (double)cdiv(tiles, 256) * p.bn / 256.0 / p.splits;
+  }
+  const int bn = big_bn(g), tiles = cdiv(g.M, 256) * big_tiles_n(g, bn) * g.batch;
+  return (double)cdiv(tiles, 256) * bn / 256.0;
+}
 
 bool gemm_bf16_qrope_ok(const GemmArgs& g) {
   return big_ok(g) && !g.W2 && g.batch == 1 && g.k_splits <= 1 && g.c_dtype == DT_BF16 && g.N % 192 == 0 &&
@@ -627,7 +638,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
   }
   if (g.w_kn) return run<128, 128, 2, 2, true>(g, s);
   if (g.k_splits > 1) {   // the caller sized part[] from gemm_bf16_splits
-    if (!big_ok(g) || g.batch != 1 || !g.part || g.k_splits != gemm_bf16_splits(g)) return hipErrorInvalidValue;
+    if (!big_ok(g, true) || g.batch != 1 || !g.part || g.k_splits != gemm_bf16_splits(g)) return hipErrorInvalidValue;
     return run_big(g, split_plan(g).bn, g.k_splits, s);
   }
   // bf16 output, 16-byte aligned rows (the KV split needs N % 256 == 0, true for H*256)

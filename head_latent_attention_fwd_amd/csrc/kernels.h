@@ -50,6 +50,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
 // Number of K chunks the big-tile path would use for this shape (1 = no split;
 // a split is worth it when the output has too few 256x256 tiles to fill the chip).
 int gemm_bf16_splits(const GemmArgs& g);
+// launch length of g on the big-tile kernels in units of one round of 256 x 256
+// tiles on 256 CUs (split: as gemm_bf16_splits would run it)
+double gemm_bf16_cost(const GemmArgs& g, bool split);
 // whether launch_gemm_bf16 takes g with epi = EPI_QROPE / EPI_SWIGLU
 bool gemm_bf16_qrope_ok(const GemmArgs& g);
 bool gemm_bf16_swiglu_ok(const GemmArgs& g);

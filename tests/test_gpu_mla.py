@@ -86,27 +86,37 @@ def test_prefill_kimi_k2_bf16_full_size_sampled():
     _check_prefill(cfg, synth.seed_of(1), rows=_sample_rows(cfg["T"], np.random.default_rng(1)))
 
 
-def test_prefill_kimi_k2_fp8_full_size_sampled():
-    cfg = config(2)
-    inp, run = _check_prefill(cfg, synth.seed_of(2), rows=_sample_rows(cfg["T"], np.random.default_rng(2), 4),
-                              batches=[0, 3], tol=FP8_TOL, cos=0.999)
-    # cache entries [c | k_pe] of one row in every 256-row tile of the B*T rows: at this
-    # size the k_pe columns of the joint down-projection are a separate split-K product
+def _check_entries_every_row_tile(cfg, inp, run):
+    """Cache entries [c | k_pe] of one row in every 256-row tile of the B*T rows: at
+    the full sizes the k_pe columns of the joint down-projection are a separate
+    split-K product."""
     d = oracle_dims(cfg)
-    fp8 = {"wkv_a": quant_weight_block128(inp["w"]["wkv_a"])}
+    e4m3 = cfg["weight"] == "e4m3"
+    fp8 = {"wkv_a": quant_weight_block128(inp["w"]["wkv_a"])} if e4m3 else None
     T, ntile = cfg["T"], cfg["B"] * cfg["T"] // 256
     rows = [256 * k + (37 * k) % 256 for k in range(ntile)]
     cache = run.kv_cache.float().cpu().numpy()
     for b in range(cfg["B"]):
         ts = np.array([m - b * T for m in rows if b * T <= m < (b + 1) * T])
-        entry = e4m3_entries(mla.latent_path(inp["x"][b][ts], inp["w"], d, ts, fp8=fp8), cfg["kv_lora_rank"])
-        # fp8 bar: a latent whose fp32 and fp64 values round apart can land on a neighbouring e4m3 code
-        assert_parity(cache[b][ts], entry, tol=FP8_TOL, cos=0.999, what=f"kv_cache_out rows of sequence {b}")
+        entry = mla.latent_path(inp["x"][b][ts], inp["w"], d, ts, fp8=fp8)
+        if e4m3:   # fp8 bar: a latent whose fp32 and fp64 values round apart can land on a neighbouring code
+            assert_parity(cache[b][ts], e4m3_entries(entry, cfg["kv_lora_rank"]), tol=FP8_TOL, cos=0.999,
+                          what=f"kv_cache_out rows of sequence {b}")
+        else:
+            assert_parity(cache[b][ts], entry, what=f"kv_cache_out rows of sequence {b}")
+
+
+def test_prefill_kimi_k2_fp8_full_size_sampled():
+    cfg = config(2)
+    inp, run = _check_prefill(cfg, synth.seed_of(2), rows=_sample_rows(cfg["T"], np.random.default_rng(2), 4),
+                              batches=[0, 3], tol=FP8_TOL, cos=0.999)
+    _check_entries_every_row_tile(cfg, inp, run)
 
 
 def test_prefill_dsv32_sparse_full_size_sampled():
     cfg = config(3)
-    _check_prefill(cfg, synth.seed_of(3), rows=_sample_rows(cfg["T"], np.random.default_rng(3)))
+    inp, run = _check_prefill(cfg, synth.seed_of(3), rows=_sample_rows(cfg["T"], np.random.default_rng(3)))
+    _check_entries_every_row_tile(cfg, inp, run)
 
 
 def _check_decode(cfg, seed, cache_len=None, seqs=None, max_len=None):
