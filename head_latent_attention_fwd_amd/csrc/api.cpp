@@ -267,6 +267,8 @@ struct AbsorbedWs {
   float* part;
   int32_t *keys, *nkeys;   // compacted selections [M][topk], counts [M]
   int qkv_splits;
+  float* kpe_part;   // split-K partials of the k_pe columns (prefill_kpe_splits), or NULL
+  int kpe_splits;
 };
 
 size_t absorbed_layout(const mla_dims* d, int B, int T, int topk, bool own_kvc, void* ws, AbsorbedWs* out) {
@@ -283,6 +285,8 @@ size_t absorbed_layout(const mla_dims* d, int B, int T, int topk, bool own_kvc, 
   p.wukt = c.take(H * L * 128 * 2);
   p.qkv_splits = prefill_qkv_splits(d, MLA_BF16, MLA_BF16, (int)M);
   p.part = p.qkv_splits > 1 ? (float*)c.take((size_t)p.qkv_splits * M * (Dq + L + 64) * 4) : nullptr;
+  p.kpe_splits = prefill_kpe_splits(d, MLA_BF16, MLA_BF16, (int)M);
+  p.kpe_part = p.kpe_splits ? (float*)c.take((size_t)p.kpe_splits * M * 64 * 4) : nullptr;
   p.keys = (int32_t*)c.take(M * (size_t)topk * 4);
   p.nkeys = (int32_t*)c.take(M * 4);
   if (out) *out = p;
@@ -819,13 +823,22 @@ int mla_prefill_absorbed(const mla_dims* d, const mla_weights* w, const void* x,
   // [c_q | latent | k_pe] and the norms exactly as in prefill: the cache entries and c_q
   mla::GemmArgs gq = qkv_args(d, MLA_BF16, x, w->wq_a, w->wkv_a, p.cqkv, M);
   const bool qkv_split = p.qkv_splits > 1 && mla::gemm_bf16_splits(gq) == p.qkv_splits;
+  const bool kpe_split = !qkv_split && p.kpe_part;
   if (qkv_split) {
     gq.k_splits = p.qkv_splits; gq.part = p.part;
     LAUNCH(mla::launch_gemm_bf16(gq, s), "gemm_bf16(split-K q_a|kv_a)");
   } else {
+    if (kpe_split) gq.N = Dq + L;   // the k_pe columns follow as their own split-K product
     LAUNCH(mla::launch_gemm_bf16(gq, s), "gemm_bf16(q_a|kv_a)");
   }
+  if (kpe_split) {
+    mla::GemmArgs g = gemm_args(x, d->dim, (const uint16_t*)w->wkv_a + (int64_t)L * d->dim, d->dim, nullptr, 64,
+                                MLA_BF16, M, 64, d->dim);
+    g.k_splits = p.kpe_splits; g.part = p.kpe_part;
+    LAUNCH(mla::launch_gemm_bf16(g, s), "gemm_bf16(k_pe columns, split-K)");
+  }
   mla::QkvNormArgs qa{};
+  if (kpe_split) { qa.kpe_in = p.kpe_part; qa.kpe_splits = p.kpe_splits; qa.kpe_split_stride = (int64_t)M * 64; }
   qa.in = qkv_split ? (const void*)p.part : p.cqkv; qa.ld_in = NQKV; qa.in_dtype = qkv_split ? MLA_F32 : MLA_BF16;
   qa.in_splits = qkv_split ? p.qkv_splits : 1; qa.split_stride = (int64_t)M * NQKV;
   qa.rows = M; qa.Dq = Dq; qa.L = L; qa.gq = w->q_norm_w; qa.gkv = w->kv_norm_w; qa.eps = d->rms_eps;
