@@ -158,19 +158,9 @@ __global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
   for (int j = 0; j < QKV_CH; ++j) {
     const int c = tid + 256 * j;
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (c < nch) {
+    if (c < (a.kpe_in ? nq + nkv : nch)) {   // (k_pe from its own partials below)
       const int64_t i = (int64_t)row * a.ld_in + 4 * c;
-      if (a.kpe_in && c >= nq + nkv) {   // k_pe from its own split-K partials (all loads first)
-        const float* p = a.kpe_in + (int64_t)row * 64 + 4 * (c - nq - nkv);
-        float4 t[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-          if (s < a.kpe_splits) t[s] = *(const float4*)(p + (int64_t)s * a.kpe_split_stride);
-        x = t[0];
-#pragma unroll
-        for (int s = 1; s < 8; ++s)
-          if (s < a.kpe_splits) { x.x += t[s].x; x.y += t[s].y; x.z += t[s].z; x.w += t[s].w; }
-      } else if (a.in_dtype == DT_F32) {
+      if (a.in_dtype == DT_F32) {
         const float* p = (const float*)a.in + i;
         float4 t[8];
 #pragma unroll
@@ -195,6 +185,15 @@ __global__ __launch_bounds__(256) void qkv_norm_kernel(QkvNormArgs a) {
       else *(float4*)&kpe_s[4 * (c - nq - nkv)] = x;
     }
     v[j] = x;
+  }
+  if (a.kpe_in && tid < 16) {   // k_pe: the sum of its split-K partials, in split order
+    const float* p = a.kpe_in + (int64_t)row * 64 + 4 * tid;
+    float4 x = *(const float4*)p;
+    for (int s = 1; s < a.kpe_splits; ++s) {
+      const float4 u = *(const float4*)(p + (int64_t)s * a.kpe_split_stride);
+      x.x += u.x; x.y += u.y; x.z += u.z; x.w += u.w;
+    }
+    *(float4*)&kpe_s[4 * tid] = x;
   }
   sq = wave_sum(sq);
   skv = wave_sum(skv);
