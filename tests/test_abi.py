@@ -225,3 +225,14 @@ def test_widened_entry_point_argument_errors(hostonly):
     assert mlp(hidden=100) == api.MLA_UNSUPPORTED
     assert mlp(wsb=10) == api.MLA_INVALID_ARG
     assert lib.mla_swiglu_workspace_size(4, 128) >= 3 * 4 * 128 * 2
+
+
+def test_latent_view_argument_errors(hostonly):
+    lib = hostonly
+    assert lib.mla_latent_e4m3_view(None, 4, 576, 512, None) == api.MLA_INVALID_ARG
+    assert lib.mla_latent_e4m3_view(fake(), -1, 576, 512, None) == api.MLA_INVALID_ARG
+    assert lib.mla_latent_e4m3_view(fake(), 4, 500, 512, None) == api.MLA_INVALID_ARG      # stride < kv_lora_rank
+    assert lib.mla_latent_e4m3_view(fake(), 4, 576, 500, None) == api.MLA_UNSUPPORTED      # kv_lora_rank % 128
+    assert lib.mla_latent_e4m3_view(fake(), 4, 580, 512, None) == api.MLA_UNSUPPORTED      # row stride % 8
+    assert lib.mla_latent_e4m3_view(ctypes.c_void_p(0x1008), 4, 576, 512, None) == api.MLA_UNSUPPORTED   # alignment
+    assert lib.mla_latent_e4m3_view(fake(), 0, 576, 512, None) == api.MLA_OK                # nothing to do
