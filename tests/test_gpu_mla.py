@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from head_latent_attention_fwd_amd import runner, synth
+from head_latent_attention_fwd_amd import api, runner, synth
 from oracle import mla
 from oracle.fp8 import quant_weight_block128
 
@@ -513,3 +513,31 @@ def test_prefill_absorbed_repeated_positions():
     d = oracle_dims(cfg)
     ref = mla.mla_prefill(inp["x"], inp["w"], d, topk_idx=idx)
     assert_parity(run.out.float().cpu().numpy(), ref, what="absorbed prefill, repeated selection")
+
+
+def test_e4m3_prefill_cache_feeds_decode():
+    """With e4m3 weights the prefill writes each latent in its e4m3 view and the
+    decode reads the cache as it is: a decode step over the cache a prefill left
+    behind equals the oracle's e4m3 decode over the oracle's own plain cache
+    entries of the same tokens."""
+    cfg = small_cfg(B=2, T=40, dim=1024, q_lora_rank=256, kv_lora_rank=512, n_heads=64, weight="e4m3")
+    inp = synth.gen_prefill(cfg, 91)
+    pre = runner.Prefill(cfg, inp)
+    pre.run()
+    B, T, max_len = cfg["B"], cfg["T"], 48
+    cache = torch.zeros((B, max_len, 576), dtype=torch.bfloat16, device="cuda")
+    cache[:, :T] = pre.kv_cache
+    x_new = synth.round_bf16(np.random.default_rng(92).standard_normal((B, cfg["dim"])))
+    cos, sin = api.mla_rope_table(max_len)
+    out = torch.empty((B, cfg["dim"]), dtype=torch.bfloat16, device="cuda")
+    ws = api.workspace(api.mla_decode_workspace_size(pre.dims, pre.wdt, B, max_len), "cuda")
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    api.mla_decode(pre.dims, pre.weights, runner.to_dev(x_new, torch.bfloat16), cache, lens, cos, sin, out, ws)
+    torch.cuda.synchronize()
+    d = oracle_dims(cfg)
+    fp8 = {"wkv_a": quant_weight_block128(inp["w"]["wkv_a"])}
+    ref_cache = np.zeros((B, max_len, 576))
+    for b in range(B):
+        ref_cache[b, :T] = mla.latent_path(inp["x"][b], inp["w"], d, np.arange(T), fp8=fp8)
+    ref, _ = mla.mla_decode(x_new, inp["w"], d, ref_cache, np.full(B, T), fp8=True)
+    assert_parity(out.float().cpu().numpy(), ref, tol=FP8_TOL, cos=0.999, what="decode over an e4m3 prefill's cache")
