@@ -541,3 +541,15 @@ def test_e4m3_prefill_cache_feeds_decode():
         ref_cache[b, :T] = mla.latent_path(inp["x"][b], inp["w"], d, np.arange(T), fp8=fp8)
     ref, _ = mla.mla_decode(x_new, inp["w"], d, ref_cache, np.full(B, T), fp8=True)
     assert_parity(out.float().cpu().numpy(), ref, tol=FP8_TOL, cos=0.999, what="decode over an e4m3 prefill's cache")
+
+
+@pytest.mark.parametrize("weight,T,dim,q_lora", [("e4m3", 13300, 1024, 512), ("bf16", 8092, 7168, 1536)])
+def test_prefill_kpe_split_ragged_rows(weight, T, dim, q_lora):
+    """Row counts that are not a multiple of the 256-row tile, at sizes where the
+    k_pe columns of the joint down-projection run as their own split-K product
+    (the launch schedule decides it from the shapes): sampled rows and one
+    cache entry per row tile against the oracle."""
+    cfg = small_cfg(B=1, T=T, dim=dim, q_lora_rank=q_lora, kv_lora_rank=512, n_heads=2, weight=weight)
+    tol, cos = (FP8_TOL, 0.999) if weight == "e4m3" else (BF16_TOL, 0.9999)
+    inp, run = _check_prefill(cfg, 93, rows=_sample_rows(T, np.random.default_rng(93), 6), tol=tol, cos=cos)
+    _check_entries_every_row_tile(cfg, inp, run)
